@@ -1,0 +1,486 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these compares the oracle with itself: each check is a closed form,
+a worked example from the pages (tests/golden), a library routine doing the
+same step a different way, an invariant, or brute force on tiny inputs.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    rows = {}
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, *v = line.split()
+            rows.setdefault(k, []).append(v)
+    return rows
+
+
+# ------------------------------------------------------------------ P1 softmax
+def test_exp_spec_within_2ulp_of_libm():
+    xs = np.concatenate([np.linspace(-87.0, 0.0, 200001, dtype=np.float32),
+                         -np.logspace(-8, np.log10(87), 5000).astype(np.float32),
+                         np.array([0.0, -0.0, -87.0, -1e-30], np.float32)])
+    got = oracle.exp_spec(xs).astype(np.float64)
+    ref = np.exp(xs.astype(np.float64))
+    ulp = np.spacing(ref.astype(np.float32)).astype(np.float64)
+    assert np.max(np.abs(got - ref) / ulp) <= 2.0
+    assert oracle.exp_spec(np.float32(0.0)) == 1.0
+
+
+def test_softmax_matches_fp64_closed_form():
+    rng = np.random.default_rng(11)
+    for E in (1, 2, 3, 4, 7, 8, 64, 100, 256):
+        for scale in (0.01, 1.0, 10.0, 40.0):
+            l = (rng.standard_normal(E) * scale).astype(np.float32)
+            s, m, S = oracle.softmax_spec(l)
+            l64 = l.astype(np.float64)
+            ref = np.exp(l64 - l64.max())
+            ref /= ref.sum()
+            big = ref > 1e-30
+            # bound: a few ulp from exp/sum/divide plus the fp32 rounding of
+            # the shifted logit l - m, which moves exp(d) by |d| * 2^-24
+            dd = np.abs(l64 - l64.max())[big]
+            bound = (1e-6 + dd * 2.0**-23) * ref[big]
+            assert np.all(np.abs(s[big] - ref[big]) <= bound)
+            assert m == l.max()
+
+
+def test_softmax_bf16_roundoff_example_from_pages():
+    g = _golden("softmax_bf16_roundoff.txt")
+    logits = np.array([float(v) for v in g["logits_fp32"][0]], np.float32)
+    s32, _, _ = oracle.softmax_spec(logits)
+    assert abs(s32[0] - float(g["top_score_fp32_exact"][0][0])) <= 1e-6
+    # bf16 round-off of the logits (torch's RNE cast is the library routine)
+    lb = torch.tensor(logits).to(torch.bfloat16).float().numpy()
+    assert lb[0] == 128.0
+    sb, _, _ = oracle.softmax_spec(lb)
+    assert abs(sb[0] - float(g["top_score_bf16"][0][0])) <= 1e-7
+    rel = (s32[0] - sb[0]) / s32[0]
+    assert abs(rel - float(g["relative_error_exact"][0][0])) <= 1e-5
+    assert float(g["relative_error_page_lo"][0][0]) <= rel <= float(g["relative_error_page_hi"][0][0])
+
+
+def test_bf16_routing_flips_the_choice_fp32_does_not():
+    # same example with the 128.5 logit at index 3: fp32 routing picks 3,
+    # bf16-rounded logits tie at 128 and the tie goes to index 0.
+    l = np.full(10, 128.0, np.float32)
+    l[3] = 128.5
+    r32 = oracle.route(l[None], 1, 1, False)
+    lb = torch.tensor(l).to(torch.bfloat16).float().numpy()
+    rb = oracle.route(lb[None], 1, 1, False)
+    assert r32["cand_ids"][0, 0] == 3 and rb["cand_ids"][0, 0] == 0
+
+
+# ------------------------------------------------------------------ P2 top-k
+def _brute_topc(key, C):
+    """Ordered top-C by (key desc, index asc) via enumeration of subsets: the
+    chosen set dominates its complement, then it is ordered within."""
+    E = len(key)
+
+    def better(a, b):  # a ranks ahead of b
+        return key[a] > key[b] or (key[a] == key[b] and a < b)
+
+    for S in itertools.combinations(range(E), C):
+        rest = [e for e in range(E) if e not in S]
+        if all(better(a, b) for a in S for b in rest):
+            order = list(S)
+            # insertion order by pairwise `better`
+            out = []
+            for a in order:
+                i = 0
+                while i < len(out) and better(out[i], a):
+                    i += 1
+                out.insert(i, a)
+            return out
+    raise AssertionError("no dominant subset")
+
+
+def test_topk_matches_subset_enumeration_with_ties():
+    rng = np.random.default_rng(5)
+    for trial in range(300):
+        E = int(rng.integers(1, 7))
+        k = int(rng.integers(1, min(3, E) + 1))
+        C = k + (1 if (k < E and rng.random() < 0.5) else 0)
+        N = int(rng.integers(1, 9))
+        # few distinct values -> many ties, including -0/+0 style equal keys
+        l = rng.choice(np.array([-1.0, 0.0, 0.5, 2.0], np.float32), size=(N, E))
+        bias = None
+        if rng.random() < 0.5:
+            bias = rng.choice(np.array([0.0, -0.0, 0.25], np.float32), size=E)
+        r = oracle.route(l, k, C, bool(rng.random() < 0.5), bias)
+        for t in range(N):
+            s, _, _ = oracle.softmax_spec(l[t])
+            key = s + bias if bias is not None else s
+            assert list(r["cand_ids"][t]) == _brute_topc(key.astype(np.float32), C)
+            assert np.array_equal(r["cand_scores"][t], s[r["cand_ids"][t]])
+
+
+def test_renormalised_gates_equal_softmax_of_keeptopk():
+    # chiang97912 notes, "KeepTopK 策略": G = Softmax(KeepTopK(H, k)), other
+    # entries set to -inf. In fp64 that is the renormalised top-k softmax.
+    rng = np.random.default_rng(7)
+    for E, k in ((8, 2), (256, 8), (5, 3)):
+        l = (rng.standard_normal((50, E)) * 1.5).astype(np.float32)
+        r = oracle.route(l, k, k, True)
+        for t in range(50):
+            ids = r["cand_ids"][t]
+            v = np.full(E, -np.inf)
+            v[ids] = l[t, ids].astype(np.float64)
+            g = np.exp(v - v.max())
+            g /= g.sum()
+            assert np.allclose(r["gates"][t], g[ids], rtol=2e-6, atol=0)
+
+
+# ------------------------------------------------------------------ P3 gates
+def test_renormalised_gates_sum_to_one():
+    rng = np.random.default_rng(3)
+    for E, k in ((8, 2), (64, 8), (256, 8)):
+        l = (rng.standard_normal((200, E)) * 2).astype(np.float32)
+        r = oracle.route(l, k, k, True)
+        sums = r["gates"].astype(np.float64).sum(axis=1)
+        assert np.all(np.abs(sums - 1.0) <= k * 2.0**-23)
+
+
+# ------------------------------------------------------------------ P4 capacity
+def test_capacity_closed_forms():
+    # chiang97912 notes, "专家容量": capacity = tokens/experts x factor
+    assert W.C1.capacity == 80    # 256/4 * 1.25
+    assert W.C4.capacity == 256   # 16384/64 * 1.0
+    assert W.C2.capacity == -1 and W.C3.capacity == -1 and W.C5.capacity == -1
+    assert W.C1.with_(n_tokens=257).capacity == math.ceil(257 / 4 * 1.25)
+
+
+def test_collapse_onto_one_expert_keeps_first_cap_tokens():
+    N, E, cap = 256, 4, 80
+    cand = np.zeros((N, 1), np.int32)
+    cs = np.ones((N, 1), np.float32)
+    d = oracle.dispatch(cand, cs, cs.copy(), E, 1, oracle.DROP, cap)
+    assert d["counts_kept"].tolist() == [cap, 0, 0, 0]
+    kept = np.nonzero(d["row_of"][:, 0] >= 0)[0]
+    assert kept.tolist() == list(range(cap))
+    assert np.all(d["gates"][cap:] == 0)
+    assert d["R"] == N - (N - cap)
+    assert d["counts_kept"].sum() == N * 1 - np.sum(d["row_of"] < 0)
+
+
+def test_counts_sum_to_assignments_minus_dropped():
+    rng = np.random.default_rng(9)
+    for policy, k, C in ((oracle.DROP, 1, 1), (oracle.DROP, 2, 2), (oracle.REROUTE, 1, 2),
+                         (oracle.DROPLESS, 4, 4)):
+        N, E = 500, 16
+        l = (rng.standard_normal((N, E)) + np.linspace(2, 0, E)).astype(np.float32)
+        r = oracle.route(l, k, C, False)
+        cap = math.ceil(N / E * 1.0)
+        d = oracle.dispatch(r["cand_ids"], r["cand_scores"], r["gates"], E, k, policy, cap)
+        dropped = int(np.sum(d["row_of"] < 0))
+        assert d["counts_kept"].sum() == N * k - dropped == d["R"]
+        assert d["counts_routed"].sum() == N * k
+        if policy != oracle.DROPLESS:
+            assert np.all(d["counts_kept"] <= cap)
+        # rows form a permutation of 0..R-1 and perm_token inverts row_of
+        rows = d["row_of"][d["row_of"] >= 0]
+        assert sorted(rows.tolist()) == list(range(d["R"]))
+        for t in range(N):
+            for j in range(k):
+                if d["row_of"][t, j] >= 0:
+                    assert d["perm_token"][d["row_of"][t, j]] == t
+                    e = d["expert_of"][t, j]
+                    assert d["offsets"][e] <= d["row_of"][t, j] < d["offsets"][e + 1]
+
+
+# ------------------------------------------------------------------ P5 reroute
+def test_reroute_hand_example():
+    g = _golden("reroute_hand_example.txt")
+    cand = np.array([[int(v[1]), int(v[2])] for v in g["cand"]], np.int32)
+    cs = (np.arange(14, dtype=np.float32).reshape(7, 2) + 1) / 16
+    gates = cs[:, :1].copy()
+    d = oracle.dispatch(cand, cs, gates, 3, 1, oracle.REROUTE, 2)
+    for t, e, slot, row in ([int(a) for a in v] for v in g["expect"]):
+        assert d["expert_of"][t, 0] == e
+        assert d["row_of"][t, 0] == row
+        if e >= 0:
+            assert row - d["offsets"][e] == slot
+    assert d["counts_routed"].tolist() == [int(v) for v in g["counts_routed"][0]]
+    assert d["counts_kept"].tolist() == [int(v) for v in g["counts_kept"][0]]
+    assert d["offsets"].tolist() == [int(v) for v in g["offsets"][0]]
+    assert d["perm_token"].tolist() == [int(v) for v in g["perm_token"][0]]
+    # rerouted tokens take their second-choice score as gate; dropped get 0
+    assert d["gates"][2, 0] == cs[2, 1] and d["gates"][4, 0] == cs[4, 1]
+    assert d["gates"][0, 0] == cs[0, 0] and d["gates"][6, 0] == 0
+
+
+# ------------------------------------------------------------------ P6/P7 FFN, combine
+def _np_ffn(x, act, w1, w3, w2, b1=None, b2=None):
+    """numpy fp64 matmul version of one expert (library routine per step)."""
+    a = w1 @ x.T
+    if b1 is not None:
+        a = a + b1[:, None]
+    if act == oracle.RELU:
+        h = np.maximum(a, 0)
+    elif act == oracle.GELU:
+        from scipy.special import erf
+        h = 0.5 * a * (1 + erf(a / np.sqrt(2)))
+    else:
+        h = (a / (1 + np.exp(-a))) * (w3 @ x.T)
+    y = (w2 @ h).T
+    if b2 is not None:
+        y = y + b2[None, :]
+    return y
+
+
+@pytest.mark.parametrize("act", [oracle.RELU, oracle.GELU, oracle.SWIGLU])
+def test_expert_ffn_matches_numpy_matmul(act):
+    rng = np.random.default_rng(act)
+    n, d, f = 5, 48, 80
+    x = rng.standard_normal((n, d))
+    w1 = rng.standard_normal((f, d)).astype(np.float32) / 7
+    w3 = rng.standard_normal((f, d)).astype(np.float32) / 7
+    w2 = rng.standard_normal((d, f)).astype(np.float32) / 9
+    b1 = rng.standard_normal(f).astype(np.float32) if act != oracle.SWIGLU else None
+    b2 = rng.standard_normal(d).astype(np.float32) if act != oracle.SWIGLU else None
+    y = oracle.expert_ffn(x, act, oracle.F32, w1, w3 if act == oracle.SWIGLU else None, w2,
+                          b1, b2)
+    ref = _np_ffn(x, act, w1.astype(np.float64), w3.astype(np.float64),
+                  w2.astype(np.float64), None if b1 is None else b1.astype(np.float64),
+                  None if b2 is None else b2.astype(np.float64))
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_expert_ffn_special_cases():
+    d, f = 16, 32
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((3, d))
+    w2 = rng.standard_normal((d, f)).astype(np.float32)
+    b2 = rng.standard_normal(d).astype(np.float32)
+    zero = np.zeros((f, d), np.float32)
+    # zero W1, zero b1: relu(0)=0 -> y = b2
+    y = oracle.expert_ffn(x, oracle.RELU, oracle.F32, zero, None, w2, np.zeros(f, np.float32), b2)
+    assert np.array_equal(y, np.broadcast_to(b2.astype(np.float64), y.shape))
+    # GELU(0) = 0 and SwiGLU on zero input = 0
+    assert np.all(oracle.expert_ffn(np.zeros((2, d)), oracle.GELU, oracle.F32,
+                                     rng.standard_normal((f, d)).astype(np.float32), None,
+                                     w2) == 0)
+    w = rng.standard_normal((f, d)).astype(np.float32)
+    assert np.all(oracle.expert_ffn(np.zeros((2, d)), oracle.SWIGLU, oracle.F32, w, w, w2) == 0)
+
+
+def test_fp8_and_bf16_weights_decode_into_ffn():
+    rng = np.random.default_rng(2)
+    n, d, f = 3, 32, 64
+    x = rng.standard_normal((n, d))
+    w1 = torch.tensor(rng.standard_normal((f, d)), dtype=torch.float32) / 6
+    w3 = torch.tensor(rng.standard_normal((f, d)), dtype=torch.float32) / 6
+    w2 = torch.tensor(rng.standard_normal((d, f)), dtype=torch.float32) / 8
+    q1, s1 = W.quantize_e4m3_rows(w1)
+    q3, s3 = W.quantize_e4m3_rows(w3)
+    q2, s2 = W.quantize_e4m3_rows(w2)
+    y = oracle.expert_ffn(x, oracle.SWIGLU, oracle.FP8, q1.numpy(), q3.numpy(), q2.numpy(),
+                          s1=s1.numpy(), s3=s3.numpy(), s2=s2.numpy())
+    deq = lambda q, s: q.view(torch.float8_e4m3fn).double().numpy() * s.double().numpy()[:, None]
+    ref = _np_ffn(x, oracle.SWIGLU, deq(q1, s1), deq(q3, s3), deq(q2, s2))
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+    b1 = w1.to(torch.bfloat16)
+    b3 = w3.to(torch.bfloat16)
+    b2 = w2.to(torch.bfloat16)
+    yb = oracle.expert_ffn(x, oracle.SWIGLU, oracle.BF16, W.bits_u16(b1), W.bits_u16(b3),
+                           W.bits_u16(b2))
+    refb = _np_ffn(x, oracle.SWIGLU, b1.double().numpy(), b3.double().numpy(),
+                   b2.double().numpy())
+    assert np.allclose(yb, refb, rtol=1e-12, atol=1e-12)
+
+
+def _small_layer(cfg, seed_shift=0):
+    inp = W.make_inputs(cfg.with_(seed=cfg.seed + seed_shift), "cpu")
+    np_ = {k: (None if v is None else
+               (W.bits_u16(v) if v.dtype == torch.bfloat16 else v.numpy()))
+           for k, v in inp.items()}
+    return inp, np_
+
+
+def test_dense_masked_reference_equals_dispatch_combine():
+    # y_t = sum_e Gtilde_te FFN_e(x_t) with Gtilde zero off the kept set,
+    # computed without any permutation, against the oracle's dispatch/combine.
+    cfg = W.C1.with_(n_tokens=96, capacity_factor=1.0)
+    inp, a = _small_layer(cfg)
+    out = oracle.layer_forward(cfg, a["x"], cfg.x_dtype, a["w_gate"], oracle.ExpertSource(a))
+    d = out["dispatch"]
+    X = a["x"].astype(np.float64)
+    Gt = np.zeros((cfg.n_tokens, cfg.n_experts))
+    for t in range(cfg.n_tokens):
+        if d["row_of"][t, 0] >= 0:
+            Gt[t, d["expert_of"][t, 0]] = d["gates"][t, 0]
+    ref = np.zeros_like(X)
+    for e in range(cfg.n_experts):
+        ye = _np_ffn(X, oracle.RELU, a["w1"][e].astype(np.float64), None,
+                     a["w2"][e].astype(np.float64), a["b1"][e].astype(np.float64),
+                     a["b2"][e].astype(np.float64))
+        ref += Gt[:, e:e + 1] * ye
+    assert np.allclose(out["y"], ref, rtol=1e-12, atol=1e-12)
+    # dropped tokens output exactly 0 (skip the layer; residual is the caller's)
+    dropped = d["row_of"][:, 0] < 0
+    assert dropped.any() and np.all(out["y"][dropped] == 0)
+
+
+def test_identical_experts_reproduce_dense_ffn():
+    cfg = W.REDUCED["c3"].with_(n_tokens=40, d_model=64, n_experts=8, d_ff=64, shared_d_ff=64,
+                                select_bias=False)
+    inp, a = _small_layer(cfg)
+    for k in ("w1", "w3", "w2"):
+        a[k] = np.ascontiguousarray(np.broadcast_to(a[k][:1], a[k].shape))
+    out = oracle.layer_forward(cfg, a["x"], cfg.x_dtype, a["w_gate"], oracle.ExpertSource(a),
+                               oracle.ExpertSource({k[7:]: a[k] for k in a
+                                                    if k.startswith("shared_")}))
+    X = oracle.decode_rows(a["x"], cfg.x_dtype)
+    f = lambda w: oracle.bf16_to_f32(w).astype(np.float64)
+    dense = _np_ffn(X, oracle.SWIGLU, f(a["w1"][0]), f(a["w3"][0]), f(a["w2"][0]))
+    shared = _np_ffn(X, oracle.SWIGLU, f(a["shared_w1"][0]), f(a["shared_w3"][0]),
+                     f(a["shared_w2"][0]))
+    gsum = out["dispatch"]["gates"].astype(np.float64).sum(axis=1, keepdims=True)
+    assert np.all(np.abs(gsum - 1) <= cfg.top_k * 2.0**-23)
+    assert np.allclose(out["y"], dense * gsum + shared, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ P8-P11 stats
+def test_switch_aux_is_one_under_uniform_routing():
+    E, m = 8, 5
+    base = np.linspace(1.0, -1.0, E).astype(np.float32)
+    l = np.stack([np.roll(base, t % E) for t in range(m * E)])
+    r = oracle.route(l, 1, 1, False)
+    d = oracle.dispatch(r["cand_ids"], r["cand_scores"], r["gates"], E, 1, oracle.DROPLESS, -1)
+    st = oracle.balance_stats(1, d["counts_routed"], d["counts_kept"], r["s"], r["lse"])
+    assert np.allclose(st["f"], 1 / E, rtol=0, atol=0)
+    assert abs(st["switch_aux"] - 1.0) <= 1e-6
+    # collapse onto expert 0 with s_0 -> 1 gives aux -> E
+    lc = np.zeros((40, E), np.float32)
+    lc[:, 0] = 60.0
+    r = oracle.route(lc, 1, 1, False)
+    d = oracle.dispatch(r["cand_ids"], r["cand_scores"], r["gates"], E, 1, oracle.DROPLESS, -1)
+    st = oracle.balance_stats(1, d["counts_routed"], d["counts_kept"], r["s"], r["lse"])
+    assert abs(st["switch_aux"] - E) <= 1e-6 * E
+
+
+def test_importance_cv2_uniform_and_collapse():
+    E, N = 16, 64
+    r = oracle.route(np.zeros((N, E), np.float32), 2, 2, True)
+    st = oracle.balance_stats(2, np.full(E, N * 2 // E), np.full(E, N * 2 // E), r["s"], r["lse"])
+    assert st["importance_cv2"] == 0.0
+    assert abs(st["z_loss"] - math.log(E) ** 2) <= 1e-12  # z-loss of all-zero logits
+    lc = np.full((N, E), -200.0, np.float32)
+    lc[:, 0] = 0.0   # shifted logits below -87 contribute exactly 0
+    r = oracle.route(lc, 1, 1, False)
+    assert np.all(r["s"][:, 0] == 1.0)
+    st = oracle.balance_stats(1, np.array([N] + [0] * (E - 1)), np.array([N] + [0] * (E - 1)),
+                              r["s"], r["lse"])
+    assert abs(st["importance_cv2"] - (E - 1)) <= 1e-12
+
+
+def test_drop_rate_and_f_definition():
+    N, E, k = 10, 4, 2
+    s = np.full((N, E), 0.25, np.float32)
+    st = oracle.balance_stats(k, np.array([8, 4, 4, 4]), np.array([6, 4, 4, 4]), s,
+                              np.zeros(N))
+    assert np.allclose(st["f"], [0.4, 0.2, 0.2, 0.2])
+    assert abs(st["drop_rate"] - 2 / 20) <= 1e-15
+    assert abs(st["switch_aux"] - 1.0) <= 1e-7
+
+
+def test_bias_update_moves_against_load():
+    # ld246.com MoE Q3 item 2: over-used expert -> bias down, idle -> up.
+    N, k = 12, 2  # N k / E = 6 with E = 4
+    routed = np.array([9, 6, 3, 6], np.int32)
+    b = oracle.bias_update(N, k, routed, np.array([0.0, 0.5, -0.25, 1e-3], np.float32), 1e-3)
+    assert b[0] == np.float32(0.0) - np.float32(1e-3)
+    assert b[1] == np.float32(0.5)            # equal to mean: no change
+    assert b[2] == np.float32(-0.25) + np.float32(1e-3)
+    assert b[3] == np.float32(1e-3)
+
+
+# ------------------------------------------------------------------ P12 formats
+def test_e4m3_decode_all_256_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.e4m3_to_f64(codes)
+    ref = torch.tensor(codes).view(torch.float8_e4m3fn).double().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0**-9
+
+
+def test_e4m3_quantise_error_within_half_ulp():
+    rng = np.random.default_rng(4)
+    w = torch.tensor(rng.standard_normal((8, 300)), dtype=torch.float32)
+    q, s = W.quantize_e4m3_rows(w)
+    v = oracle.e4m3_to_f64(q.numpy()) * s.double().numpy()[:, None]
+    scaled = w.double().numpy() / s.double().numpy()[:, None]
+    a = np.abs(scaled)
+    # e4m3 spacing: 2^(floor(log2 a) - 3) for normal, 2^-9 below 2^-6
+    e = np.floor(np.log2(np.maximum(a, 2.0**-6)))
+    half_ulp = 2.0 ** (e - 3) / 2
+    assert np.all(np.abs(v / s.double().numpy()[:, None] - scaled) <= half_ulp * (1 + 1e-6))
+
+
+def test_bf16_decode_is_exact():
+    rng = np.random.default_rng(6)
+    t = torch.tensor(rng.standard_normal(1000), dtype=torch.float32).to(torch.bfloat16)
+    got = oracle.bf16_to_f32(W.bits_u16(t))
+    assert np.array_equal(got, t.float().numpy())
+
+
+# ------------------------------------------------------------------ P13 noise
+def test_splitmix64_published_vector():
+    # First output of SplitMix64 seeded with 0 (Steele, Lea & Flood 2014).
+    assert oracle.splitmix64(0) == 0xE220A8397B1DCDAF
+
+
+def test_hash_normal_moments_and_determinism():
+    z = oracle.hash_normal_grid(44, 4096, 256).astype(np.float64).ravel()
+    assert abs(z.mean()) < 0.005
+    assert abs(z.var() - 1.0) < 0.01
+    assert np.all(np.abs(z) <= 6.0)
+    assert oracle.hash_normal(44, 17, 3, 256) == z[17 * 256 + 3]
+    # z is a multiple of 2^-24 (sum of 24-bit integers, exact)
+    assert np.all(np.round(z * 2**24) == z * 2**24)
+
+
+def test_router_logits_match_numpy_fp64_gemm():
+    cfg = W.REDUCED["c4"].with_(n_tokens=64)
+    inp, a = _small_layer(cfg)
+    H, raw = oracle.router_logits(a["x"], cfg.x_dtype, a["w_gate"], a["logit_bias"],
+                                  a["w_noise"], cfg.noise_seed)
+    X = oracle.decode_rows(a["x"], cfg.x_dtype)
+    l64 = X @ a["w_gate"].astype(np.float64).T
+    l32 = l64.astype(np.float32) + a["logit_bias"][None, :]
+    ulp = np.spacing(np.abs(l32))
+    assert np.all(np.abs(raw - l32) <= ulp)
+    v = (X @ a["w_noise"].astype(np.float64).T).astype(np.float32).astype(np.float64)
+    sp = np.where(v > 20, v, np.log1p(np.exp(v)))
+    z = oracle.hash_normal_grid(cfg.noise_seed, cfg.n_tokens, cfg.n_experts).astype(np.float64)
+    Href = raw.astype(np.float64) + z * sp
+    assert np.allclose(H, Href, rtol=1e-6, atol=1e-6)
+
+
+def test_rank_major_capacity_order_hand_example():
+    g = _golden("rank_major_capacity_example.txt")
+    cand = np.array([[int(v[1]), int(v[2])] for v in g["cand"]], np.int32)
+    cs = np.full((3, 2), 0.5, np.float32)
+    d = oracle.dispatch(cand, cs, cs.copy(), 2, 2, oracle.DROP, 2)
+    for t, j, row in ([int(a) for a in v] for v in g["expect"]):
+        assert d["row_of"][t, j] == row
+        assert (d["gates"][t, j] == 0) == (row < 0)
+    assert d["counts_kept"].tolist() == [int(v) for v in g["counts_kept"][0]]
+    assert d["perm_token"].tolist() == [int(v) for v in g["perm_token"][0]]
