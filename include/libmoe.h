@@ -1,0 +1,260 @@
+/*
+ * libmoe.h -- C ABI of libmoe, the forward pass of one sparse
+ * Mixture-of-Experts FFN layer with every expert resident on one MI355X
+ * (gfx950) GPU.
+ *
+ * The layer, as the pages state it: a router scores each token against every
+ * expert (dot product with a learned per-expert vector, then a softmax), the
+ * token keeps its top-k experts, tokens are bucketed and packed by expert,
+ * each expert's FFN runs on its bucket (as one grouped GEMM), and the expert
+ * outputs are put back in token order weighted by the router's gate values.
+ * Sources: heavensheep.xyz MoE notes, "Routing Function"; mkbk-pku.cn
+ * "通信与并行" (router gives expert id and weight alpha, dispatch, bucketize,
+ * grouped GEMM, combine back to token order with alpha) and "MOE的优化"
+ * (grouped GEMM, bucketize + contiguous packing); chiang97912 MoE notes,
+ * "专家选择" (y = sum_i G(x)_i E_i(x)), "KeepTopK 策略", "专家容量".
+ *
+ * Conventions shared by every call
+ *  - All array arguments are DEVICE pointers to memory the caller allocated
+ *    and owns (e.g. torch tensors' data_ptr()). libmoe allocates no device
+ *    memory and keeps no state between calls; scratch space comes from the
+ *    caller's `workspace` (size from the matching *_workspace_bytes query,
+ *    alignment 256 bytes). Parameter structs are HOST memory, read during
+ *    the call only.
+ *  - Layouts are row-major and dense. bf16 is the upper half of an IEEE
+ *    binary32; fp8 is OCP E4M3FN (bias 7, max 448, no infinities).
+ *  - Every call enqueues its kernels on `hip_stream` (a hipStream_t; NULL is
+ *    the default stream) and returns without synchronising: routing counts
+ *    and offsets stay on the device.
+ *  - Arguments are validated on the host before anything is enqueued. On an
+ *    error nothing is enqueued and no output is touched; moe_last_error()
+ *    gives a message (per calling thread).
+ *      MOE_EINVAL        a required pointer is NULL or a size is out of range
+ *      MOE_EUNSUPPORTED  valid but not implemented (limits below)
+ *      MOE_EWORKSPACE    workspace NULL or smaller than required
+ *      MOE_EHIP          a kernel launch failed; faults inside kernels
+ *                        surface at the caller's next synchronisation
+ *  - Limits: 1 <= n_experts <= 256, 1 <= top_k <= 8, top_k <= n_experts,
+ *    n_tokens * n_cand < 2^31, d_model % 8 == 0 and d_ff % 8 == 0 (16-byte
+ *    rows); the bf16 tensor-core path needs d_model % 64 == 0 and
+ *    d_ff % 64 == 0. Non-finite inputs are not supported (garbage in).
+ *  - Results are deterministic: no atomics decide any value or order.
+ */
+#ifndef LIBMOE_H
+#define LIBMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,
+  MOE_EUNSUPPORTED = 2,
+  MOE_EWORKSPACE = 3,
+  MOE_EHIP = 4
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+
+/* Expert FFN activation: ReLU and GELU (exact erf form) apply to W1 x + b1;
+ * SwiGLU is silu(W1 x) * (W3 x) with w1 the gate and w3 the up projection. */
+typedef enum { MOE_RELU = 0, MOE_GELU = 1, MOE_SWIGLU = 2 } moe_act;
+
+/* What happens to an assignment beyond an expert's capacity
+ * (mkbk-pku.cn "负载均衡", overflow strategies; chiang97912 "专家容量"):
+ *  DROPLESS           no capacity limit;
+ *  DROP               the assignment is dropped (gate 0, contributes 0);
+ *  REROUTE_THEN_DROP  (top-1 with one spare candidate) after every token's
+ *                     first choice is placed, overflowed tokens in ascending
+ *                     order try their second candidate once, else drop. */
+typedef enum { MOE_DROPLESS = 0, MOE_DROP = 1, MOE_REROUTE_THEN_DROP = 2 } moe_overflow;
+
+/* ---------------------------------------------------------------------- */
+/* moe_router_topk                                                         */
+/* ---------------------------------------------------------------------- */
+/* Router: logits l = x . W_g^T (+ logit_bias); with w_noise, noisy top-k
+ * gating H = l + z * softplus(x . W_noise^T) (chiang97912 "KeepTopK 策略"),
+ * z a standard-normal draw from a counter hash of (noise_seed, token,
+ * expert); then an fp32 softmax (heavensheep "Training": exponentials need
+ * the higher precision) and top-k selection ("Routing Function"), keys =
+ * score + select_bias (ld246.com Q3: per-expert bias added to the softmax
+ * score before top-k). Gates: renormalize ? s_j / sum of the kept s (equal
+ * to softmax(KeepTopK(H,k))) : s_j.
+ *
+ * Numerics, fixed so that integer decisions are reproducible:
+ *  - softmax: m = max; d = l - m; u = 0 if d < -87 else exp(d) with a
+ *    Cody-Waite reduced, degree-7 Taylor fp32 exponential; S = halving-tree
+ *    sum of u padded to a power of two; s = u / S (IEEE divide);
+ *  - key ties go to the lower expert index; -0 counts as +0;
+ *  - renormalising sum in rank order, fp32.
+ */
+typedef struct {
+  int32_t n_tokens;     /* N >= 1 */
+  int32_t d_model;      /* d, % 8 == 0 */
+  int32_t n_experts;    /* E in [1, 256] */
+  int32_t top_k;        /* k in [1, min(8, E)] */
+  int32_t n_cand;       /* candidates kept per token: k, or k+1 for reroute */
+  int32_t renormalize;  /* 1: gates renormalised over the k; 0: gate = score */
+  const float* logit_bias;  /* [E] added to the logits, or NULL */
+  const float* select_bias; /* [E] added to scores for selection only, or NULL */
+  const float* w_noise;     /* [E][d] fp32 noise projection, or NULL */
+  uint64_t noise_seed;
+} moe_router_params;
+
+/*  x          [N][d] activations, x_dt = MOE_F32 or MOE_BF16
+ *  w_gate     [E][d] fp32 router weights (each expert's vector)
+ *  logits_in  [N][E] fp32 or NULL. When set, x, w_gate, logit_bias and
+ *             w_noise are ignored and these are the logits the softmax sees.
+ *  cand_ids   [N][n_cand] int32 out: experts by descending key
+ *  cand_scores[N][n_cand] fp32 out: their unbiased softmax scores
+ *  gates      [N][top_k]  fp32 out
+ *  logits_out [N][E] fp32 out (the logits the softmax saw), or NULL
+ *  score_sums [E+1] fp64 out, or NULL: [e] = sum over tokens of s_te,
+ *             [E] = sum over tokens of lse_t^2 (lse = m + ln S). Inputs of
+ *             moe_balance_stats. Summed in a fixed order. */
+moe_status moe_router_topk(const moe_router_params* p, const void* x, moe_dtype x_dt,
+                           const float* w_gate, const float* logits_in, int32_t* cand_ids,
+                           float* cand_scores, float* gates, float* logits_out,
+                           double* score_sums, void* workspace, size_t ws_bytes,
+                           void* hip_stream);
+size_t moe_router_workspace_bytes(int32_t n_tokens, int32_t n_experts, int32_t with_noise);
+
+/* ---------------------------------------------------------------------- */
+/* moe_dispatch                                                            */
+/* ---------------------------------------------------------------------- */
+/* Bucketize assignments by expert and pack each expert's tokens
+ * contiguously (mkbk-pku.cn "MOE的优化": bucketize + contiguous packing),
+ * applying the expert capacity (chiang97912 "专家容量").
+ * Order: assignments are taken rank-major -- every token's first choice in
+ * ascending token order, then every second choice, ... An assignment whose
+ * expert already holds `capacity` assignments overflows (policy above).
+ * Rows: offsets = exclusive prefix sum of counts_kept; the assignment's row
+ * is offsets[e] + its slot (its position among e's kept assignments).
+ *  cand_ids, cand_scores [N][n_cand] from moe_router_topk
+ *  gates       [N][top_k] in/out: rerouted -> second candidate's score,
+ *              dropped -> 0 (DROPLESS leaves it untouched)
+ *  capacity    -1 for DROPLESS, else >= 0 (see moe_capacity)
+ *  x           [N][d_model] (x_dt) rows to gather, or NULL with x_perm NULL
+ *  counts_routed [E] out: demand of the first top_k candidates (pre-capacity)
+ *  counts_kept   [E] out
+ *  offsets     [E+1] out, offsets[E] = R = kept assignments
+ *  row_of      [N][top_k] out: row in the packed order, -1 if dropped
+ *  expert_of   [N][top_k] out: expert actually used, -1 if dropped
+ *  perm_token  [N*top_k] out: token of each packed row (first R entries)
+ *  x_perm      [N*top_k][d_model] out (x_dt): x rows in packed order (first
+ *              R rows), or NULL to skip the gather.
+ * REROUTE_THEN_DROP needs top_k == 1 and n_cand == 2 (else EUNSUPPORTED). */
+moe_status moe_dispatch(int32_t n_tokens, int32_t n_experts, int32_t top_k, int32_t n_cand,
+                        moe_overflow policy, int32_t capacity, const int32_t* cand_ids,
+                        const float* cand_scores, float* gates, const void* x, moe_dtype x_dt,
+                        int32_t d_model, int32_t* counts_routed, int32_t* counts_kept,
+                        int32_t* offsets, int32_t* row_of, int32_t* expert_of,
+                        int32_t* perm_token, void* x_perm, void* workspace, size_t ws_bytes,
+                        void* hip_stream);
+size_t moe_dispatch_workspace_bytes(int32_t n_tokens, int32_t n_experts, int32_t top_k);
+
+/* capacity = ceil(n_tokens / n_experts * capacity_factor) (chiang97912
+ * "专家容量": tokens per batch / number of experts x capacity factor; the
+ * rounding up is this library's choice). Host function. */
+int32_t moe_capacity(int32_t n_tokens, int32_t n_experts, double capacity_factor);
+
+/* ---------------------------------------------------------------------- */
+/* moe_grouped_ffn                                                         */
+/* ---------------------------------------------------------------------- */
+/* Every expert's FFN on its packed rows, as one grouped GEMM pair
+ * (mkbk-pku.cn "MOE的优化", Grouped GEMM): rows offsets[e] .. offsets[e+1]
+ * of x_rows go through expert e:
+ *   ReLU/GELU: y = W2 act(W1 x + b1) + b2;  SwiGLU: y = W2 (silu(W1 x) * W3 x)
+ * The intermediate h is kept in bf16 (fp32 when act_dt is MOE_F32) in the
+ * workspace. fp8 weights carry one fp32 scale per output channel (row of
+ * W1/W3/W2), applied after the K sum; activations stay bf16 (W8A16).
+ * Shared always-on expert: the same call with n_experts = 1 and
+ * offsets = {0, N} on x.
+ * Supported: (act_dt, w_dt, y_dt) = (F32, F32, F32), (BF16, BF16, BF16|F32),
+ * (BF16, FP8_E4M3, BF16|F32); fp8 weights need SwiGLU or GELU and no bias. */
+typedef struct {
+  int32_t n_experts, d_model, d_ff;
+  moe_act act;
+  moe_dtype w_dt;
+  const void* w1; /* [E][d_ff][d_model] */
+  const void* w3; /* [E][d_ff][d_model], SwiGLU only, else NULL */
+  const void* w2; /* [E][d_model][d_ff] */
+  const float* b1; /* [E][d_ff] or NULL */
+  const float* b2; /* [E][d_model] or NULL */
+  const float* s1; /* [E][d_ff] fp8 scales, else NULL */
+  const float* s3; /* [E][d_ff] fp8 scales (SwiGLU), else NULL */
+  const float* s2; /* [E][d_model] fp8 scales, else NULL */
+} moe_ffn_weights;
+
+/*  x_rows   [max_rows][d_model] (act_dt), packed rows
+ *  offsets  [E+1] device int32 row offsets (from moe_dispatch); rows past
+ *           offsets[E] are not read or written
+ *  max_rows upper bound on offsets[E] used to size the launch (N*top_k)
+ *  y_rows   [max_rows][d_model] out (y_dt) */
+moe_status moe_grouped_ffn(const moe_ffn_weights* w, const void* x_rows, moe_dtype act_dt,
+                           const int32_t* offsets, int32_t max_rows, void* y_rows,
+                           moe_dtype y_dt, void* workspace, size_t ws_bytes,
+                           void* hip_stream);
+size_t moe_grouped_ffn_workspace_bytes(const moe_ffn_weights* w, moe_dtype act_dt,
+                                       int32_t max_rows);
+
+/* ---------------------------------------------------------------------- */
+/* moe_combine                                                             */
+/* ---------------------------------------------------------------------- */
+/* Back to token order, weighted by the gates (mkbk-pku.cn "通信与并行",
+ * combine with alpha; chiang97912 "专家选择": y = sum_i G(x)_i E_i(x)), plus
+ * the shared expert's output with gate 1 ("MoE" on ld246.com, Q4):
+ *   y[t] = sum over j < top_k with row_of[t][j] >= 0 of
+ *          gates[t][j] * y_rows[row_of[t][j]]  (+ y_shared[t]),
+ * accumulated in fp32 in rank order, rounded once. A token whose
+ * assignments were all dropped gets 0 (+ shared): it skips the layer, the
+ * residual add is the caller's.
+ *  y_rows [R][d_model] (y_dt), row_of/gates [N][top_k], y_shared [N][d_model]
+ *  (sh_dt) or NULL, y [N][d_model] out (out_dt). Dtypes: F32 or BF16. */
+moe_status moe_combine(int32_t n_tokens, int32_t d_model, int32_t top_k, const void* y_rows,
+                       moe_dtype y_dt, const int32_t* row_of, const float* gates,
+                       const void* y_shared, moe_dtype sh_dt, void* y, moe_dtype out_dt,
+                       void* hip_stream);
+
+/* ---------------------------------------------------------------------- */
+/* moe_balance_stats                                                       */
+/* ---------------------------------------------------------------------- */
+/* Load-balance statistics of one forward, computed in fp64:
+ *  f[e] = counts_routed[e] / (N k)   fraction of assignments sent to e, and
+ *  P[e] = score_sums[e] / N          mean router probability of e
+ *                                    (heavensheep "Training": f_i and P_i)
+ *  scalars[0] = E * sum_e f_e P_e    Switch aux loss, unscaled (1 when uniform)
+ *  scalars[1] = CV^2 of Importance = sum_t G(x_t) (population variance over
+ *               mean^2; chiang97912 "辅助损失")
+ *  scalars[2] = router z-loss = mean_t lse_t^2 ("[CS336-04]" section 4 names it)
+ *  scalars[3] = drop rate = (N k - sum counts_kept) / (N k)
+ * With select_bias non-NULL, the loss-free balancing step is applied in
+ * place: bias_e -= bias_rate * sign(counts_routed[e] - N k / E), sign(0) = 0
+ * (ld246.com Q3 item 2; heavensheep "Training", DeepSeek V3 bias).
+ *  counts_*: [E] int32; score_sums [E+1] fp64 from moe_router_topk;
+ *  f, P [E] fp32 out; scalars [4] fp32 out. */
+moe_status moe_balance_stats(int32_t n_tokens, int32_t n_experts, int32_t top_k,
+                             const int32_t* counts_routed, const int32_t* counts_kept,
+                             const double* score_sums, float* f, float* P, float* scalars,
+                             float* select_bias, float bias_rate, void* hip_stream);
+
+/* ---------------------------------------------------------------------- */
+/* Helpers                                                                 */
+/* ---------------------------------------------------------------------- */
+/* Largest workspace any call of one layer forward needs. */
+size_t moe_workspace_bytes(int32_t n_tokens, int32_t n_experts, int32_t top_k,
+                           int32_t d_model, int32_t d_ff);
+const char* moe_status_string(moe_status s);
+/* Message of the last error on the calling thread ("" if none). */
+const char* moe_last_error(void);
+/* Library version string. */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBMOE_H */

@@ -65,7 +65,7 @@ def lib():
             L.orc_hash_normal.argtypes = [u64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
             L.orc_hash_normal.restype = f32
             L.orc_hash_normal_grid.argtypes = [u64, i32, i32, P]
-            L.orc_router_logits.argtypes = [i32, i32, i32, P, i32, P, P, P, u64, P, P]
+            L.orc_router_logits.argtypes = [i32, i32, i32, P, i32, P, P, P, u64, P, P, P]
             L.orc_route.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, P]
             L.orc_dispatch.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P]
             L.orc_dispatch.restype = i32
@@ -140,8 +140,9 @@ def _x_arg(x: np.ndarray, x_dt: int):
     return _c(x, np.float32)
 
 
-def router_logits(x, x_dt, w_gate, logit_bias=None, w_noise=None, noise_seed=0):
-    """Returns (H, raw): logits the softmax sees, and the logits before noise."""
+def router_logits(x, x_dt, w_gate, logit_bias=None, w_noise=None, noise_seed=0, token_ids=None):
+    """Returns (H, raw): logits the softmax sees, and the logits before noise.
+    token_ids: each row's token index in the full batch (noise counter)."""
     x = _x_arg(x, x_dt)
     N, d = x.shape
     wg = _c(w_gate, np.float32)
@@ -149,7 +150,8 @@ def router_logits(x, x_dt, w_gate, logit_bias=None, w_noise=None, noise_seed=0):
     H = np.empty((N, E), np.float32)
     raw = np.empty((N, E), np.float32)
     lib().orc_router_logits(N, d, E, _p(x), x_dt, _p(wg), _p(_c(logit_bias, np.float32)),
-                            _p(_c(w_noise, np.float32)), int(noise_seed), _p(H), _p(raw))
+                            _p(_c(w_noise, np.float32)), int(noise_seed),
+                            _p(_c(token_ids, np.int32)), _p(H), _p(raw))
     return H, raw
 
 

@@ -202,30 +202,39 @@ void orc_hash_normal_grid(uint64_t seed, int N, int E, float* z) {
  *   v = fp32(sum x*Wn) in fp64;  sp = fp32(softplus(v)) computed in fp64
  *   (v itself when v > 20);  z = hash normal(seed, t, e);
  *   H = fma(z, sp, l) in fp32.
- * raw_out (optional) receives l before noise. */
+ * token_ids (optional) gives each row's index in the full batch (the noise
+ * counter); raw_out (optional) receives l before noise. */
 void orc_router_logits(int N, int d, int E, const void* x, int x_dt, const float* wg,
                        const float* logit_bias, const float* w_noise, uint64_t noise_seed,
-                       float* H_out, float* raw_out) {
-    #pragma omp parallel for schedule(static)
-    for (int t = 0; t < N; ++t) {
-        for (int e = 0; e < E; ++e) {
-            double acc = 0.0;
-            for (int i = 0; i < d; ++i)
-                acc += load_val(x, x_dt, (size_t)t * d + i) * (double)wg[(size_t)e * d + i];
-            float l = (float)acc;
-            if (logit_bias) l = l + logit_bias[e];
-            if (raw_out) raw_out[(size_t)t * E + e] = l;
-            if (w_noise) {
-                double av = 0.0;
-                for (int i = 0; i < d; ++i)
-                    av += load_val(x, x_dt, (size_t)t * d + i) * (double)w_noise[(size_t)e * d + i];
-                float v = (float)av;
-                float sp = (v > 20.0f) ? v : (float)log1p(exp((double)v));
-                float z = orc_hash_normal(noise_seed, t, e, E);
-                l = fmaf(z, sp, l);
+                       const int32_t* token_ids, float* H_out, float* raw_out) {
+    #pragma omp parallel
+    {
+        double* xr = (double*)malloc(sizeof(double) * (size_t)d);
+        #pragma omp for schedule(static)
+        for (int t = 0; t < N; ++t) {
+            /* token index for the noise counter: position in the full batch */
+            int64_t tok = token_ids ? (int64_t)token_ids[t] : (int64_t)t;
+            for (int i = 0; i < d; ++i) xr[i] = load_val(x, x_dt, (size_t)t * d + i);
+            for (int e = 0; e < E; ++e) {
+                double acc = 0.0;
+                const float* w = wg + (size_t)e * d;
+                for (int i = 0; i < d; ++i) acc += xr[i] * (double)w[i];
+                float l = (float)acc;
+                if (logit_bias) l = l + logit_bias[e];
+                if (raw_out) raw_out[(size_t)t * E + e] = l;
+                if (w_noise) {
+                    double av = 0.0;
+                    const float* wn = w_noise + (size_t)e * d;
+                    for (int i = 0; i < d; ++i) av += xr[i] * (double)wn[i];
+                    float v = (float)av;
+                    float sp = (v > 20.0f) ? v : (float)log1p(exp((double)v));
+                    float z = orc_hash_normal(noise_seed, tok, e, E);
+                    l = fmaf(z, sp, l);
+                }
+                H_out[(size_t)t * E + e] = l;
             }
-            H_out[(size_t)t * E + e] = l;
         }
+        free(xr);
     }
 }
 
@@ -384,34 +393,47 @@ void orc_expert_ffn(int n, int d, int f, int act, int w_dt, const double* X,
                     const float* b2, const float* s1, const float* s3, const float* s2,
                     double* Y) {
     double* H = (double*)malloc(sizeof(double) * (size_t)n * f);
-    #pragma omp parallel for collapse(2) schedule(static)
-    for (int r = 0; r < n; ++r) {
+    #pragma omp parallel
+    {
+        double* wa = (double*)malloc(sizeof(double) * (size_t)(d > f ? d : f));
+        double* wb = (double*)malloc(sizeof(double) * (size_t)d);
+        /* hidden layer: one output channel (row of W1, W3) at a time */
+        #pragma omp for schedule(static)
         for (int o = 0; o < f; ++o) {
-            const double* x = X + (size_t)r * d;
-            double a = 0.0;
-            for (int i = 0; i < d; ++i) a += load_val(w1, w_dt, (size_t)o * d + i) * x[i];
-            if (w_dt == ORC_FP8) a *= (double)s1[o];
-            if (b1) a += (double)b1[o];
-            if (act == ORC_SWIGLU) {
-                double g = 0.0;
-                for (int i = 0; i < d; ++i) g += load_val(w3, w_dt, (size_t)o * d + i) * x[i];
-                if (w_dt == ORC_FP8) g *= (double)s3[o];
-                H[(size_t)r * f + o] = silu_f64(a) * g;
-            } else {
-                H[(size_t)r * f + o] = act_f64(act, a);
+            for (int i = 0; i < d; ++i) wa[i] = load_val(w1, w_dt, (size_t)o * d + i);
+            if (act == ORC_SWIGLU)
+                for (int i = 0; i < d; ++i) wb[i] = load_val(w3, w_dt, (size_t)o * d + i);
+            for (int r = 0; r < n; ++r) {
+                const double* x = X + (size_t)r * d;
+                double a = 0.0;
+                for (int i = 0; i < d; ++i) a += wa[i] * x[i];
+                if (w_dt == ORC_FP8) a *= (double)s1[o];
+                if (b1) a += (double)b1[o];
+                if (act == ORC_SWIGLU) {
+                    double g = 0.0;
+                    for (int i = 0; i < d; ++i) g += wb[i] * x[i];
+                    if (w_dt == ORC_FP8) g *= (double)s3[o];
+                    H[(size_t)r * f + o] = silu_f64(a) * g;
+                } else {
+                    H[(size_t)r * f + o] = act_f64(act, a);
+                }
             }
         }
-    }
-    #pragma omp parallel for collapse(2) schedule(static)
-    for (int r = 0; r < n; ++r) {
+        /* output layer: one output channel (row of W2) at a time */
+        #pragma omp for schedule(static)
         for (int o = 0; o < d; ++o) {
-            const double* h = H + (size_t)r * f;
-            double a = 0.0;
-            for (int i = 0; i < f; ++i) a += load_val(w2, w_dt, (size_t)o * f + i) * h[i];
-            if (w_dt == ORC_FP8) a *= (double)s2[o];
-            if (b2) a += (double)b2[o];
-            Y[(size_t)r * d + o] = a;
+            for (int i = 0; i < f; ++i) wa[i] = load_val(w2, w_dt, (size_t)o * f + i);
+            for (int r = 0; r < n; ++r) {
+                const double* h = H + (size_t)r * f;
+                double a = 0.0;
+                for (int i = 0; i < f; ++i) a += wa[i] * h[i];
+                if (w_dt == ORC_FP8) a *= (double)s2[o];
+                if (b2) a += (double)b2[o];
+                Y[(size_t)r * d + o] = a;
+            }
         }
+        free(wa);
+        free(wb);
     }
     free(H);
 }

@@ -1,0 +1,342 @@
+"""Python binding of libmoe: the sparse MoE FFN layer forward on MI355X.
+
+Argument marshalling only. Each function takes torch tensors that already
+live on the GPU, checks dtype, shape and contiguity, and passes raw device
+pointers plus the current HIP stream to the C ABI in include/libmoe.h; every
+step of the layer runs in libmoe's HIP kernels. torch supplies device memory
+and streams, nothing else. There is no CPU fallback: if libmoe.so is not
+built, importing the binding raises.
+
+Calls (same names as the C ABI): moe_router_topk, moe_dispatch,
+moe_grouped_ffn, moe_combine, moe_balance_stats; MoELayer strings them
+together for one layer forward.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+RELU, GELU, SWIGLU = 0, 1, 2
+DROPLESS, DROP, REROUTE_THEN_DROP = 0, 1, 2
+_STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EUNSUPPORTED", 3: "MOE_EWORKSPACE",
+           4: "MOE_EHIP"}
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("%s: %s" % (_STATUS.get(status, status), msg))
+        self.status = status
+
+
+class RouterParams(ctypes.Structure):
+    _fields_ = [("n_tokens", ctypes.c_int32), ("d_model", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("n_cand", ctypes.c_int32), ("renormalize", ctypes.c_int32),
+                ("logit_bias", ctypes.c_void_p), ("select_bias", ctypes.c_void_p),
+                ("w_noise", ctypes.c_void_p), ("noise_seed", ctypes.c_uint64)]
+
+
+class FFNWeights(ctypes.Structure):
+    _fields_ = [("n_experts", ctypes.c_int32), ("d_model", ctypes.c_int32),
+                ("d_ff", ctypes.c_int32), ("act", ctypes.c_int32), ("w_dt", ctypes.c_int32),
+                ("w1", ctypes.c_void_p), ("w3", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("b1", ctypes.c_void_p), ("b2", ctypes.c_void_p), ("s1", ctypes.c_void_p),
+                ("s3", ctypes.c_void_p), ("s2", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libmoe.so is not built at %s; run "
+                          "`python -m sparse_mixture_experts_47_amd.build_lib`" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    L.moe_router_topk.argtypes = [ctypes.POINTER(RouterParams), P, i32, P, P, P, P, P, P, P, P,
+                                  sz, P]
+    L.moe_router_topk.restype = i32
+    L.moe_router_workspace_bytes.argtypes = [i32, i32, i32]
+    L.moe_router_workspace_bytes.restype = sz
+    L.moe_dispatch.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, i32, i32, P, P, P, P,
+                               P, P, P, P, sz, P]
+    L.moe_dispatch.restype = i32
+    L.moe_dispatch_workspace_bytes.argtypes = [i32, i32, i32]
+    L.moe_dispatch_workspace_bytes.restype = sz
+    L.moe_capacity.argtypes = [i32, i32, ctypes.c_double]
+    L.moe_capacity.restype = i32
+    L.moe_grouped_ffn.argtypes = [ctypes.POINTER(FFNWeights), P, i32, P, i32, P, i32, P, sz, P]
+    L.moe_grouped_ffn.restype = i32
+    L.moe_grouped_ffn_workspace_bytes.argtypes = [ctypes.POINTER(FFNWeights), i32, i32]
+    L.moe_grouped_ffn_workspace_bytes.restype = sz
+    L.moe_combine.argtypes = [i32, i32, i32, P, i32, P, P, P, i32, P, i32, P]
+    L.moe_combine.restype = i32
+    L.moe_balance_stats.argtypes = [i32, i32, i32, P, P, P, P, P, P, P, ctypes.c_float, P]
+    L.moe_balance_stats.restype = i32
+    L.moe_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.moe_workspace_bytes.restype = sz
+    L.moe_status_string.argtypes = [i32]
+    L.moe_status_string.restype = ctypes.c_char_p
+    L.moe_last_error.argtypes = []
+    L.moe_last_error.restype = ctypes.c_char_p
+    L.moe_version.argtypes = []
+    L.moe_version.restype = ctypes.c_char_p
+    return L
+
+
+lib = _load()
+
+
+def _check(status):
+    if status != 0:
+        raise MoEError(status, lib.moe_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("libmoe needs contiguous tensors")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return FP8_E4M3
+    raise TypeError("unsupported dtype %s" % t.dtype)
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev_check(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libmoe tensors must live on the GPU")
+
+
+def capacity(n_tokens: int, n_experts: int, capacity_factor: float) -> int:
+    return int(lib.moe_capacity(n_tokens, n_experts, capacity_factor))
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# --------------------------------------------------------------------- calls
+def moe_router_topk(x, w_gate, *, top_k, n_cand=None, renormalize=True, logit_bias=None,
+                    select_bias=None, w_noise=None, noise_seed=0, logits_in=None, cand_ids,
+                    cand_scores, gates, logits_out=None, score_sums=None, ws=None,
+                    stream=None):
+    """Router GEMM + fp32 softmax + top-k. Outputs are written in place."""
+    N, E = cand_ids.shape[0], (w_gate.shape[0] if logits_in is None else logits_in.shape[1])
+    d = x.shape[1] if x is not None else 0
+    n_cand = n_cand or top_k
+    _dev_check(x, w_gate, logits_in, cand_ids, cand_scores, gates, logits_out, score_sums)
+    p = RouterParams(N, d, E, top_k, n_cand, int(bool(renormalize)),
+                     _ptr(logit_bias), _ptr(select_bias), _ptr(w_noise), int(noise_seed))
+    if ws is None:
+        ws = workspace(lib.moe_router_workspace_bytes(N, E, int(w_noise is not None)),
+                       cand_ids.device)
+    _check(lib.moe_router_topk(ctypes.byref(p), _ptr(x), _dt(x) if x is not None else F32,
+                               _ptr(w_gate), _ptr(logits_in), _ptr(cand_ids), _ptr(cand_scores),
+                               _ptr(gates), _ptr(logits_out), _ptr(score_sums), _ptr(ws),
+                               ws.numel(), _stream(stream)))
+
+
+def moe_dispatch(cand_ids, cand_scores, gates, *, n_experts, top_k, policy=DROPLESS,
+                 capacity=-1, x=None, counts_routed, counts_kept, offsets, row_of, expert_of,
+                 perm_token, x_perm=None, ws=None, stream=None):
+    N, C = cand_ids.shape
+    _dev_check(cand_ids, cand_scores, gates, x, counts_routed, counts_kept, offsets, row_of,
+               expert_of, perm_token, x_perm)
+    if ws is None:
+        ws = workspace(lib.moe_dispatch_workspace_bytes(N, n_experts, top_k), cand_ids.device)
+    d = x.shape[1] if x is not None else 0
+    _check(lib.moe_dispatch(N, n_experts, top_k, C, policy, capacity, _ptr(cand_ids),
+                            _ptr(cand_scores), _ptr(gates), _ptr(x),
+                            _dt(x) if x is not None else F32, d, _ptr(counts_routed),
+                            _ptr(counts_kept), _ptr(offsets), _ptr(row_of), _ptr(expert_of),
+                            _ptr(perm_token), _ptr(x_perm), _ptr(ws), ws.numel(),
+                            _stream(stream)))
+
+
+def ffn_weights(w1, w2, w3=None, act=SWIGLU, b1=None, b2=None, s1=None, s3=None, s2=None):
+    E, F, d = w1.shape
+    return FFNWeights(E, d, F, act, _dt(w1), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(b1), _ptr(b2),
+                      _ptr(s1), _ptr(s3), _ptr(s2)), (w1, w2, w3, b1, b2, s1, s3, s2)
+
+
+def moe_grouped_ffn(weights: FFNWeights, x_rows, offsets, y_rows, *, max_rows=None, ws=None,
+                    stream=None):
+    _dev_check(x_rows, offsets, y_rows)
+    max_rows = max_rows or x_rows.shape[0]
+    if ws is None:
+        ws = workspace(lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(weights), _dt(x_rows),
+                                                           max_rows), x_rows.device)
+    _check(lib.moe_grouped_ffn(ctypes.byref(weights), _ptr(x_rows), _dt(x_rows), _ptr(offsets),
+                               max_rows, _ptr(y_rows), _dt(y_rows), _ptr(ws), ws.numel(),
+                               _stream(stream)))
+
+
+def moe_combine(y_rows, row_of, gates, y, *, y_shared=None, stream=None):
+    N, k = row_of.shape
+    _dev_check(y_rows, row_of, gates, y, y_shared)
+    _check(lib.moe_combine(N, y.shape[1], k, _ptr(y_rows), _dt(y_rows), _ptr(row_of),
+                           _ptr(gates), _ptr(y_shared),
+                           _dt(y_shared) if y_shared is not None else F32, _ptr(y), _dt(y),
+                           _stream(stream)))
+
+
+def moe_balance_stats(n_tokens, top_k, counts_routed, counts_kept, score_sums, f, P, scalars,
+                      *, select_bias=None, bias_rate=0.0, stream=None):
+    E = counts_routed.shape[0]
+    _dev_check(counts_routed, counts_kept, score_sums, f, P, scalars, select_bias)
+    _check(lib.moe_balance_stats(n_tokens, E, top_k, _ptr(counts_routed), _ptr(counts_kept),
+                                 _ptr(score_sums), _ptr(f), _ptr(P), _ptr(scalars),
+                                 _ptr(select_bias), float(bias_rate), _stream(stream)))
+
+
+# --------------------------------------------------------------------- layer
+@dataclass
+class LayerSpec:
+    n_tokens: int
+    d_model: int
+    n_experts: int
+    d_ff: int
+    top_k: int
+    act: int
+    renormalize: bool
+    overflow: int = DROPLESS
+    capacity: int = -1
+    n_cand: int = 0
+    noise_seed: int = 0
+    bias_rate: float = 1e-3
+    shared_d_ff: int = 0
+
+
+class MoELayer:
+    """One MoE FFN layer forward through libmoe. Holds device weights and
+    preallocated outputs/workspaces so repeated forwards allocate nothing.
+
+    weights: dict with w_gate, logit_bias, select_bias, w_noise, w1, w3, w2,
+    b1, b2, s1, s3, s2 and shared_{w1,w3,w2,s1,s3,s2} (device tensors/None).
+    """
+
+    def __init__(self, spec: LayerSpec, weights: dict, x_dtype=torch.bfloat16, device="cuda",
+                 out_dtype=None):
+        self.spec = s = spec
+        self.w = weights
+        self.dev = torch.device(device)
+        N, E, k = s.n_tokens, s.n_experts, s.top_k
+        C = s.n_cand or k
+        self.C = C
+        dev = self.dev
+        i32 = dict(dtype=torch.int32, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.cand_ids = torch.empty((N, C), **i32)
+        self.cand_scores = torch.empty((N, C), **f32)
+        self.gates = torch.empty((N, k), **f32)
+        self.logits = torch.empty((N, E), **f32)
+        self.score_sums = torch.empty(E + 1, dtype=torch.float64, device=dev)
+        self.counts_routed = torch.empty(E, **i32)
+        self.counts_kept = torch.empty(E, **i32)
+        self.offsets = torch.empty(E + 1, **i32)
+        self.row_of = torch.empty((N, k), **i32)
+        self.expert_of = torch.empty((N, k), **i32)
+        self.perm_token = torch.empty(N * k, **i32)
+        self.x_perm = torch.empty((N * k, s.d_model), dtype=x_dtype, device=dev)
+        # Expert outputs and the layer output stay fp32: the only bf16
+        # rounding on the path is the intermediate h inside the grouped FFN.
+        ydt = torch.float32
+        self.y_rows = torch.empty((N * k, s.d_model), dtype=ydt, device=dev)
+        self.out_dtype = out_dtype or torch.float32
+        self.y = torch.empty((N, s.d_model), dtype=self.out_dtype, device=dev)
+        self.f = torch.empty(E, **f32)
+        self.P = torch.empty(E, **f32)
+        self.scalars = torch.empty(4, **f32)
+        self.ffn, self._keep = ffn_weights(weights["w1"], weights["w2"], weights.get("w3"),
+                                           s.act, weights.get("b1"), weights.get("b2"),
+                                           weights.get("s1"), weights.get("s3"),
+                                           weights.get("s2"))
+        self.shared = None
+        if weights.get("shared_w1") is not None:
+            self.shared, self._keep_sh = ffn_weights(
+                weights["shared_w1"], weights["shared_w2"], weights.get("shared_w3"), s.act,
+                None, None, weights.get("shared_s1"), weights.get("shared_s3"),
+                weights.get("shared_s2"))
+            self.sh_offsets = torch.tensor([0, N], **i32)
+            self.y_shared = torch.empty((N, s.d_model), dtype=ydt, device=dev)
+        xdt = _dt(torch.empty(0, dtype=x_dtype))
+        noise = int(weights.get("w_noise") is not None)
+        self.ws_router = workspace(lib.moe_router_workspace_bytes(N, E, noise), dev)
+        self.ws_dispatch = workspace(lib.moe_dispatch_workspace_bytes(N, E, k), dev)
+        self.ws_ffn = workspace(lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(self.ffn), xdt,
+                                                                    N * k), dev)
+        if self.shared is not None:
+            self.ws_shared = workspace(lib.moe_grouped_ffn_workspace_bytes(
+                ctypes.byref(self.shared), xdt, N), dev)
+
+    def route(self, x, logits_in=None, stream=None):
+        s, w = self.spec, self.w
+        moe_router_topk(x, w["w_gate"], top_k=s.top_k, n_cand=self.C,
+                        renormalize=s.renormalize, logit_bias=w.get("logit_bias"),
+                        select_bias=w.get("select_bias"), w_noise=w.get("w_noise"),
+                        noise_seed=s.noise_seed, logits_in=logits_in, cand_ids=self.cand_ids,
+                        cand_scores=self.cand_scores, gates=self.gates, logits_out=self.logits,
+                        score_sums=self.score_sums, ws=self.ws_router, stream=stream)
+
+    def dispatch(self, x, stream=None):
+        s = self.spec
+        moe_dispatch(self.cand_ids, self.cand_scores, self.gates, n_experts=s.n_experts,
+                     top_k=s.top_k, policy=s.overflow, capacity=s.capacity, x=x,
+                     counts_routed=self.counts_routed, counts_kept=self.counts_kept,
+                     offsets=self.offsets, row_of=self.row_of, expert_of=self.expert_of,
+                     perm_token=self.perm_token, x_perm=self.x_perm, ws=self.ws_dispatch,
+                     stream=stream)
+
+    def experts(self, x, stream=None):
+        moe_grouped_ffn(self.ffn, self.x_perm, self.offsets, self.y_rows,
+                        max_rows=self.spec.n_tokens * self.spec.top_k, ws=self.ws_ffn,
+                        stream=stream)
+        if self.shared is not None:
+            moe_grouped_ffn(self.shared, x, self.sh_offsets, self.y_shared,
+                            max_rows=self.spec.n_tokens, ws=self.ws_shared, stream=stream)
+
+    def combine(self, stream=None):
+        moe_combine(self.y_rows, self.row_of, self.gates, self.y,
+                    y_shared=self.y_shared if self.shared is not None else None, stream=stream)
+
+    def stats(self, update_bias=False, stream=None):
+        s = self.spec
+        moe_balance_stats(s.n_tokens, s.top_k, self.counts_routed, self.counts_kept,
+                          self.score_sums, self.f, self.P, self.scalars,
+                          select_bias=self.w.get("select_bias") if update_bias else None,
+                          bias_rate=s.bias_rate, stream=stream)
+
+    def forward(self, x, logits_in=None, stats=True, update_bias=False, stream=None):
+        self.route(x, logits_in, stream)
+        self.dispatch(x, stream)
+        self.experts(x, stream)
+        self.combine(stream)
+        if stats:
+            self.stats(update_bias, stream)
+        return self.y
+
+
+def spec_from_config(cfg) -> LayerSpec:
+    """LayerSpec from a workload config object (duck-typed)."""
+    return LayerSpec(cfg.n_tokens, cfg.d_model, cfg.n_experts, cfg.d_ff, cfg.top_k, cfg.act,
+                     cfg.renormalize, cfg.overflow, cfg.capacity, cfg.n_cand, cfg.noise_seed,
+                     1e-3, cfg.shared_d_ff)

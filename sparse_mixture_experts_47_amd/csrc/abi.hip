@@ -1,0 +1,259 @@
+// abi.hip -- libmoe's C entry points: host-side validation, workspace
+// layout, and the launches on the caller's stream.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "moe_device.h"
+
+namespace moe_host {
+
+size_t router_workspace_bytes(int N, int E, int with_noise);
+moe_status router_launch(const moe_router_params* p, const void* x, moe_dtype x_dt,
+                         const float* w_gate, const float* logits_in, int32_t* cand_ids,
+                         float* cand_scores, float* gates, float* logits_out,
+                         double* score_sums, void* workspace, hipStream_t st);
+size_t dispatch_workspace_bytes(int N, int E, int k);
+moe_status dispatch_launch(int N, int E, int k, int C, moe_overflow policy, int cap,
+                           const int32_t* cand, const float* cand_s, float* gates,
+                           const void* x, moe_dtype x_dt, int d, int32_t* counts_routed,
+                           int32_t* counts_kept, int32_t* offsets, int32_t* row_of,
+                           int32_t* expert_of, int32_t* perm_token, void* x_perm,
+                           void* workspace, hipStream_t st);
+size_t grouped_ffn_workspace_bytes(const moe_ffn_weights* w, moe_dtype act_dt, int max_rows);
+moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_dtype act_dt,
+                              const int32_t* offsets, int max_rows, void* y_rows,
+                              moe_dtype y_dt, void* workspace, hipStream_t st);
+moe_status combine_launch(int N, int d, int k, const void* y_rows, moe_dtype y_dt,
+                          const int32_t* row_of, const float* gates, const void* y_shared,
+                          moe_dtype sh_dt, void* y, moe_dtype out_dt, hipStream_t st);
+moe_status balance_stats_launch(int N, int E, int k, const int32_t* routed, const int32_t* kept,
+                                const double* sums, float* f, float* P, float* scalars,
+                                float* bias, float rate, hipStream_t st);
+
+static thread_local char g_err[512];
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+moe_status launch_status(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("%s: kernel launch failed: %s", what, hipGetErrorString(e));
+    return MOE_EHIP;
+  }
+  return MOE_OK;
+}
+
+}  // namespace moe_host
+
+using namespace moe_host;
+
+#define CHECK(cond, code, ...)      \
+  do {                              \
+    if (!(cond)) {                  \
+      set_error(__VA_ARGS__);       \
+      return code;                  \
+    }                               \
+  } while (0)
+
+static moe_status check_ws(void* ws, size_t have, size_t need, const char* who) {
+  CHECK(need == 0 || (ws != nullptr && have >= need), MOE_EWORKSPACE,
+        "%s: workspace of %zu bytes needed, %zu given%s", who, need, have,
+        ws ? "" : " (NULL)");
+  CHECK(((uintptr_t)ws & 255) == 0, MOE_EINVAL, "%s: workspace must be 256-byte aligned", who);
+  return MOE_OK;
+}
+
+extern "C" {
+
+const char* moe_version(void) { return "libmoe 0.1 gfx950"; }
+
+const char* moe_last_error(void) { return g_err; }
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_EINVAL: return "MOE_EINVAL";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED";
+    case MOE_EWORKSPACE: return "MOE_EWORKSPACE";
+    case MOE_EHIP: return "MOE_EHIP";
+  }
+  return "MOE_UNKNOWN";
+}
+
+int32_t moe_capacity(int32_t n_tokens, int32_t n_experts, double capacity_factor) {
+  if (n_tokens <= 0 || n_experts <= 0 || !(capacity_factor >= 0.0)) return -1;
+  const double c = (double)n_tokens / (double)n_experts * capacity_factor;
+  return (int32_t)ceil(c - 1e-9);
+}
+
+size_t moe_router_workspace_bytes(int32_t n_tokens, int32_t n_experts, int32_t with_noise) {
+  if (n_tokens <= 0 || n_experts <= 0) return 0;
+  return router_workspace_bytes(n_tokens, n_experts, with_noise);
+}
+
+size_t moe_dispatch_workspace_bytes(int32_t n_tokens, int32_t n_experts, int32_t top_k) {
+  if (n_tokens <= 0 || n_experts <= 0 || top_k <= 0) return 0;
+  return dispatch_workspace_bytes(n_tokens, n_experts, top_k);
+}
+
+size_t moe_grouped_ffn_workspace_bytes(const moe_ffn_weights* w, moe_dtype act_dt,
+                                       int32_t max_rows) {
+  if (!w || max_rows <= 0) return 0;
+  return grouped_ffn_workspace_bytes(w, act_dt, max_rows);
+}
+
+size_t moe_workspace_bytes(int32_t n_tokens, int32_t n_experts, int32_t top_k, int32_t d_model,
+                           int32_t d_ff) {
+  if (n_tokens <= 0 || n_experts <= 0 || top_k <= 0) return 0;
+  size_t a = router_workspace_bytes(n_tokens, n_experts, 1);
+  size_t b = dispatch_workspace_bytes(n_tokens, n_experts, top_k);
+  moe_ffn_weights w = {};
+  w.n_experts = n_experts;
+  w.d_model = d_model;
+  w.d_ff = d_ff;
+  size_t c = grouped_ffn_workspace_bytes(&w, MOE_F32, n_tokens * top_k);
+  size_t m = a > b ? a : b;
+  return m > c ? m : c;
+}
+
+moe_status moe_router_topk(const moe_router_params* p, const void* x, moe_dtype x_dt,
+                           const float* w_gate, const float* logits_in, int32_t* cand_ids,
+                           float* cand_scores, float* gates, float* logits_out,
+                           double* score_sums, void* workspace, size_t ws_bytes,
+                           void* hip_stream) {
+  CHECK(p, MOE_EINVAL, "moe_router_topk: params is NULL");
+  const int N = p->n_tokens, d = p->d_model, E = p->n_experts, k = p->top_k, C = p->n_cand;
+  CHECK(N >= 1 && E >= 1 && k >= 1, MOE_EINVAL, "moe_router_topk: N=%d E=%d k=%d must be >= 1",
+        N, E, k);
+  CHECK(k <= E, MOE_EINVAL, "moe_router_topk: top_k %d > n_experts %d", k, E);
+  CHECK(C == k || C == k + 1, MOE_EINVAL, "moe_router_topk: n_cand %d must be k or k+1", C);
+  CHECK(C <= E, MOE_EINVAL, "moe_router_topk: n_cand %d > n_experts %d", C, E);
+  CHECK((long long)N * C < (1ll << 31), MOE_EINVAL, "moe_router_topk: N*n_cand too large");
+  CHECK(cand_ids && cand_scores && gates, MOE_EINVAL, "moe_router_topk: NULL output");
+  CHECK(E <= 256, MOE_EUNSUPPORTED, "moe_router_topk: n_experts %d > 256", E);
+  CHECK(k <= 8, MOE_EUNSUPPORTED, "moe_router_topk: top_k %d > 8", k);
+  if (!logits_in) {
+    CHECK(x && w_gate, MOE_EINVAL, "moe_router_topk: x and w_gate needed without logits_in");
+    CHECK(d >= 1, MOE_EINVAL, "moe_router_topk: d_model %d", d);
+    CHECK(x_dt == MOE_F32 || x_dt == MOE_BF16, MOE_EUNSUPPORTED,
+          "moe_router_topk: x dtype must be F32 or BF16");
+  }
+  const int noise = (!logits_in && p->w_noise) ? 1 : 0;
+  moe_status s = check_ws(workspace, ws_bytes, router_workspace_bytes(N, E, noise),
+                          "moe_router_topk");
+  if (s != MOE_OK) return s;
+  return router_launch(p, x, x_dt, w_gate, logits_in, cand_ids, cand_scores, gates, logits_out,
+                       score_sums, workspace, (hipStream_t)hip_stream);
+}
+
+moe_status moe_dispatch(int32_t n_tokens, int32_t n_experts, int32_t top_k, int32_t n_cand,
+                        moe_overflow policy, int32_t capacity, const int32_t* cand_ids,
+                        const float* cand_scores, float* gates, const void* x, moe_dtype x_dt,
+                        int32_t d_model, int32_t* counts_routed, int32_t* counts_kept,
+                        int32_t* offsets, int32_t* row_of, int32_t* expert_of,
+                        int32_t* perm_token, void* x_perm, void* workspace, size_t ws_bytes,
+                        void* hip_stream) {
+  const int N = n_tokens, E = n_experts, k = top_k, C = n_cand;
+  CHECK(N >= 1 && E >= 1 && k >= 1 && k <= E, MOE_EINVAL,
+        "moe_dispatch: N=%d E=%d k=%d out of range", N, E, k);
+  CHECK(C == k || C == k + 1, MOE_EINVAL, "moe_dispatch: n_cand %d must be k or k+1", C);
+  CHECK((long long)N * C < (1ll << 31), MOE_EINVAL, "moe_dispatch: N*n_cand too large");
+  CHECK(policy == MOE_DROPLESS || policy == MOE_DROP || policy == MOE_REROUTE_THEN_DROP,
+        MOE_EINVAL, "moe_dispatch: unknown overflow policy %d", (int)policy);
+  CHECK(policy == MOE_DROPLESS || capacity >= 0, MOE_EINVAL,
+        "moe_dispatch: capacity %d must be >= 0 with a dropping policy", capacity);
+  CHECK(capacity >= -1, MOE_EINVAL, "moe_dispatch: capacity %d < -1", capacity);
+  CHECK(cand_ids && cand_scores && gates && counts_routed && counts_kept && offsets && row_of &&
+            expert_of && perm_token,
+        MOE_EINVAL, "moe_dispatch: NULL argument");
+  CHECK(E <= 256, MOE_EUNSUPPORTED, "moe_dispatch: n_experts %d > 256", E);
+  CHECK(policy != MOE_REROUTE_THEN_DROP || (k == 1 && C == 2), MOE_EUNSUPPORTED,
+        "moe_dispatch: reroute needs top_k == 1 and n_cand == 2");
+  if (x_perm) {
+    CHECK(x, MOE_EINVAL, "moe_dispatch: x_perm given without x");
+    CHECK(x_dt == MOE_F32 || x_dt == MOE_BF16, MOE_EUNSUPPORTED, "moe_dispatch: x dtype");
+    CHECK(d_model >= 8 && d_model % 8 == 0, MOE_EUNSUPPORTED,
+          "moe_dispatch: d_model %d must be a multiple of 8", d_model);
+  }
+  moe_status s = check_ws(workspace, ws_bytes, dispatch_workspace_bytes(N, E, k), "moe_dispatch");
+  if (s != MOE_OK) return s;
+  return dispatch_launch(N, E, k, C, policy, capacity, cand_ids, cand_scores, gates, x, x_dt,
+                         d_model, counts_routed, counts_kept, offsets, row_of, expert_of,
+                         perm_token, x_perm, workspace, (hipStream_t)hip_stream);
+}
+
+moe_status moe_grouped_ffn(const moe_ffn_weights* w, const void* x_rows, moe_dtype act_dt,
+                           const int32_t* offsets, int32_t max_rows, void* y_rows,
+                           moe_dtype y_dt, void* workspace, size_t ws_bytes, void* hip_stream) {
+  CHECK(w, MOE_EINVAL, "moe_grouped_ffn: weights is NULL");
+  const int E = w->n_experts, d = w->d_model, F = w->d_ff;
+  CHECK(E >= 1 && d >= 1 && F >= 1 && max_rows >= 1, MOE_EINVAL,
+        "moe_grouped_ffn: E=%d d=%d d_ff=%d max_rows=%d out of range", E, d, F, max_rows);
+  CHECK(x_rows && offsets && y_rows && w->w1 && w->w2, MOE_EINVAL, "moe_grouped_ffn: NULL argument");
+  CHECK(w->act == MOE_RELU || w->act == MOE_GELU || w->act == MOE_SWIGLU, MOE_EINVAL,
+        "moe_grouped_ffn: unknown activation %d", (int)w->act);
+  CHECK(w->act != MOE_SWIGLU || w->w3, MOE_EINVAL, "moe_grouped_ffn: SwiGLU needs w3");
+  CHECK((long long)max_rows * (d > F ? d : F) < (1ll << 40), MOE_EINVAL,
+        "moe_grouped_ffn: max_rows too large");
+  CHECK(E <= 256, MOE_EUNSUPPORTED, "moe_grouped_ffn: n_experts %d > 256", E);
+  if (act_dt == MOE_F32) {
+    CHECK(w->w_dt == MOE_F32 && y_dt == MOE_F32, MOE_EUNSUPPORTED,
+          "moe_grouped_ffn: fp32 activations need fp32 weights and output");
+  } else if (act_dt == MOE_BF16) {
+    CHECK(w->w_dt == MOE_BF16 || w->w_dt == MOE_FP8_E4M3, MOE_EUNSUPPORTED,
+          "moe_grouped_ffn: bf16 activations need bf16 or fp8 weights");
+    CHECK(y_dt == MOE_BF16 || y_dt == MOE_F32, MOE_EUNSUPPORTED, "moe_grouped_ffn: output dtype");
+    CHECK(d % 64 == 0 && F % 64 == 0, MOE_EUNSUPPORTED,
+          "moe_grouped_ffn: d_model %d and d_ff %d must be multiples of 64", d, F);
+    if (w->w_dt == MOE_FP8_E4M3) {
+      CHECK(w->act != MOE_RELU, MOE_EUNSUPPORTED, "moe_grouped_ffn: fp8 needs SwiGLU or GELU");
+      CHECK(!w->b1 && !w->b2, MOE_EUNSUPPORTED, "moe_grouped_ffn: fp8 path has no biases");
+      CHECK(w->s1 && w->s2 && (w->act != MOE_SWIGLU || w->s3), MOE_EINVAL,
+            "moe_grouped_ffn: fp8 weights need their scales");
+    }
+  } else {
+    CHECK(0, MOE_EUNSUPPORTED, "moe_grouped_ffn: activation dtype %d", (int)act_dt);
+  }
+  moe_status s = check_ws(workspace, ws_bytes, grouped_ffn_workspace_bytes(w, act_dt, max_rows),
+                          "moe_grouped_ffn");
+  if (s != MOE_OK) return s;
+  return grouped_ffn_launch(w, x_rows, act_dt, offsets, max_rows, y_rows, y_dt, workspace,
+                            (hipStream_t)hip_stream);
+}
+
+moe_status moe_combine(int32_t n_tokens, int32_t d_model, int32_t top_k, const void* y_rows,
+                       moe_dtype y_dt, const int32_t* row_of, const float* gates,
+                       const void* y_shared, moe_dtype sh_dt, void* y, moe_dtype out_dt,
+                       void* hip_stream) {
+  CHECK(n_tokens >= 1 && d_model >= 1 && top_k >= 1, MOE_EINVAL,
+        "moe_combine: N=%d d=%d k=%d out of range", n_tokens, d_model, top_k);
+  CHECK(y_rows && row_of && gates && y, MOE_EINVAL, "moe_combine: NULL argument");
+  CHECK(top_k <= 8, MOE_EUNSUPPORTED, "moe_combine: top_k %d > 8", top_k);
+  CHECK(d_model % 8 == 0, MOE_EUNSUPPORTED, "moe_combine: d_model %d not a multiple of 8", d_model);
+  CHECK((y_dt == MOE_F32 || y_dt == MOE_BF16) && (out_dt == MOE_F32 || out_dt == MOE_BF16) &&
+            (!y_shared || sh_dt == MOE_F32 || sh_dt == MOE_BF16),
+        MOE_EUNSUPPORTED, "moe_combine: dtypes must be F32 or BF16");
+  return combine_launch(n_tokens, d_model, top_k, y_rows, y_dt, row_of, gates, y_shared, sh_dt, y,
+                        out_dt, (hipStream_t)hip_stream);
+}
+
+moe_status moe_balance_stats(int32_t n_tokens, int32_t n_experts, int32_t top_k,
+                             const int32_t* counts_routed, const int32_t* counts_kept,
+                             const double* score_sums, float* f, float* P, float* scalars,
+                             float* select_bias, float bias_rate, void* hip_stream) {
+  CHECK(n_tokens >= 1 && n_experts >= 1 && top_k >= 1, MOE_EINVAL,
+        "moe_balance_stats: N=%d E=%d k=%d out of range", n_tokens, n_experts, top_k);
+  CHECK(counts_routed && counts_kept && score_sums && f && P && scalars, MOE_EINVAL,
+        "moe_balance_stats: NULL argument");
+  CHECK(n_experts <= 256, MOE_EUNSUPPORTED, "moe_balance_stats: n_experts %d > 256", n_experts);
+  return balance_stats_launch(n_tokens, n_experts, top_k, counts_routed, counts_kept, score_sums,
+                              f, P, scalars, select_bias, bias_rate, (hipStream_t)hip_stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+// combine.hip -- gate-weighted combine back to token order (gfx950).
+//
+// mkbk-pku.cn, "通信与并行": expert outputs go back to each token's original
+// position, weighted by the router's alpha; chiang97912 MoE notes, "专家选择":
+// y = sum_i G(x)_i E_i(x). The shared always-on expert ("MoE" on ld246.com,
+// Q4) adds its output with gate 1. A dropped assignment adds nothing
+// (mkbk-pku.cn "负载均衡": the overflowed token's output is zero).
+#include "moe_device.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename T>
+struct Vec8;
+template <>
+struct Vec8<float> {
+  __device__ static void load(const float* p, float v[8]) {
+    const f32x4_t a = *(const f32x4_t*)p, b = *(const f32x4_t*)(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+  }
+  __device__ static void store(float* p, const float v[8]) {
+    *(f32x4_t*)p = f32x4_t{v[0], v[1], v[2], v[3]};
+    *(f32x4_t*)(p + 4) = f32x4_t{v[4], v[5], v[6], v[7]};
+  }
+};
+template <>
+struct Vec8<uint16_t> {
+  __device__ static void load(const uint16_t* p, float v[8]) {
+    const u32x4_t a = *(const u32x4_t*)p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(a[i] << 16);
+      v[2 * i + 1] = __uint_as_float(a[i] & 0xFFFF0000u);
+    }
+  }
+  __device__ static void store(uint16_t* p, const float v[8]) {
+    u32x4_t a;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = moe::pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    *(u32x4_t*)p = a;
+  }
+};
+
+// One block per token; each thread owns 8 consecutive features per pass.
+template <typename YT, typename ST, typename OT>
+__global__ __launch_bounds__(kThreads) void combine_kernel(int d, int k,
+                                                           const YT* __restrict__ y_rows,
+                                                           const int32_t* __restrict__ row_of,
+                                                           const float* __restrict__ gates,
+                                                           const ST* __restrict__ ysh,
+                                                           OT* __restrict__ y) {
+  const int t = blockIdx.x;
+  int rows[8];
+  float g[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    rows[j] = j < k ? row_of[(size_t)t * k + j] : -1;
+    g[j] = j < k ? gates[(size_t)t * k + j] : 0.f;
+  }
+  for (int c = threadIdx.x * 8; c < d; c += kThreads * 8) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (rows[j] < 0) continue;
+      float v[8];
+      Vec8<YT>::load(y_rows + (size_t)rows[j] * d + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(g[j], v[i], acc[i]);
+    }
+    if (ysh) {
+      float v[8];
+      Vec8<ST>::load(ysh + (size_t)t * d + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    Vec8<OT>::store(y + (size_t)t * d + c, acc);
+  }
+}
+
+template <typename YT, typename ST>
+moe_status dispatch_out(int N, int d, int k, const void* yr, const int32_t* row_of,
+                        const float* gates, const void* ysh, void* y, moe_dtype out_dt,
+                        hipStream_t st) {
+  if (out_dt == MOE_BF16)
+    combine_kernel<YT, ST, uint16_t><<<N, kThreads, 0, st>>>(d, k, (const YT*)yr, row_of, gates,
+                                                             (const ST*)ysh, (uint16_t*)y);
+  else
+    combine_kernel<YT, ST, float><<<N, kThreads, 0, st>>>(d, k, (const YT*)yr, row_of, gates,
+                                                          (const ST*)ysh, (float*)y);
+  return moe_host::launch_status("combine");
+}
+
+}  // namespace
+
+namespace moe_host {
+
+moe_status combine_launch(int N, int d, int k, const void* y_rows, moe_dtype y_dt,
+                          const int32_t* row_of, const float* gates, const void* y_shared,
+                          moe_dtype sh_dt, void* y, moe_dtype out_dt, hipStream_t st) {
+  const bool ybf = y_dt == MOE_BF16, sbf = sh_dt == MOE_BF16;
+  if (ybf && sbf) return dispatch_out<uint16_t, uint16_t>(N, d, k, y_rows, row_of, gates, y_shared, y, out_dt, st);
+  if (ybf) return dispatch_out<uint16_t, float>(N, d, k, y_rows, row_of, gates, y_shared, y, out_dt, st);
+  if (sbf) return dispatch_out<float, uint16_t>(N, d, k, y_rows, row_of, gates, y_shared, y, out_dt, st);
+  return dispatch_out<float, float>(N, d, k, y_rows, row_of, gates, y_shared, y, out_dt, st);
+}
+
+}  // namespace moe_host

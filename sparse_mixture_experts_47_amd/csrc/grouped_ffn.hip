@@ -1,0 +1,462 @@
+// grouped_ffn.hip -- every expert's FFN as one ragged grouped GEMM pair.
+//
+// mkbk-pku.cn, "MOE的优化" / Grouped GEMM: instead of two GEMMs per expert,
+// one grouped launch over the bucketed, contiguously packed tokens. Rows
+// offsets[e] .. offsets[e+1] go through expert e. GEMM 1 computes W1 x (and
+// W3 x for SwiGLU) with the activation fused into its epilogue; GEMM 2
+// computes W2 h. Both operands are K-contiguous (x rows, weight rows), so
+// C = A . B^T with 16-byte loads along K on both sides.
+//
+// Paths:
+//  - bf16 x bf16 -> fp32 on gfx950 MFMA (v_mfma_f32_32x32x16_bf16), LDS
+//    tiles with an XOR swizzle, M tiles from a device-built tile table so no
+//    host sync is needed;
+//  - fp32 (small layers) on plain fp32 FMA;
+//  - fp8 e4m3 weights with bf16 activations for few rows per expert
+//    (decode): weights streamed once from HBM, converted to bf16 in
+//    registers, v_mfma_f32_16x16x32_bf16, per-output-channel scale after
+//    the K sum.
+#include <math.h>
+
+#include "moe_device.h"
+
+namespace {
+
+enum { MODE_ACT = 0, MODE_GLU = 1, MODE_OUT = 2 };
+
+__device__ __forceinline__ float act_fn(int act, float v) {
+  if (act == MOE_RELU) return fmaxf(v, 0.f);
+  // GELU, exact erf form
+  return 0.5f * v * (1.f + erff(v * 0.70710678118654752f));
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.f + __expf(-g)); }
+
+// tile_start[e] = sum over e' < e of ceil(count_e' / bm); tile_start[E] = total.
+__global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restrict__ offsets,
+                                                         int E, int bm,
+                                                         int32_t* __restrict__ tile_start) {
+  __shared__ int sc[256];
+  const int e = threadIdx.x;
+  int n = 0;
+  if (e < E) n = (offsets[e + 1] - offsets[e] + bm - 1) / bm;
+  sc[e] = n;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    int v = e >= o ? sc[e - o] : 0;
+    __syncthreads();
+    sc[e] += v;
+    __syncthreads();
+  }
+  if (e < E) tile_start[e] = sc[e] - n;
+  if (e == E - 1) tile_start[E] = sc[e];
+}
+
+struct GemmArgs {
+  const void* A;          // [rows][K]
+  const void* B0;         // [E][Nout][K]
+  const void* B1;         // [E][Nout][K] (GLU) or null
+  const float* bias;      // [E][Nout] or null
+  void* C;                // [rows][Nout]
+  int K, Nout, E, max_mt, act;
+  const int32_t* offsets;
+  const int32_t* tile_start;
+};
+
+// Expert of M tile `mt`: tile_start[e] <= mt < tile_start[e+1].
+__device__ __forceinline__ int tile_expert(const int32_t* ts, int E, int mt) {
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (ts[mid] <= mt) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------------- bf16 MFMA
+// LDS tile rows are BK bf16 (BK/8 16-byte chunks); chunk c of row r is stored
+// at chunk position c ^ ((r >> 1) & (BK/8 - 1)), so the 16 lanes that read a
+// 16x16-byte column slice of rows r..r+15 hit distinct banks.
+template <int BK>
+__device__ __forceinline__ int swz(int r, int c) {
+  return r * BK + ((c ^ ((r >> 1) & (BK / 8 - 1))) << 3);
+}
+
+template <int BM, int BN, int BK, int WGM, int WGN, int MODE, bool OUT_BF16>
+__global__ __launch_bounds__(WGM * WGN * 64) void ggemm_bf16_kernel(GemmArgs g) {
+  constexpr int NT = WGM * WGN * 64;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int FM = WM / 32, FN = WN / 32;
+  constexpr int NB = MODE == MODE_GLU ? 2 : 1;
+  constexpr int CPR = BK / 8;
+  static_assert(FM >= 1 && FN >= 1, "wave tile");
+  static_assert((BM * CPR) % NT == 0 && (BN * CPR) % NT == 0, "load split");
+  __shared__ __attribute__((aligned(16))) uint16_t lds_a[BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_b[NB][BN * BK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int mt = blockIdx.x % g.max_mt, nt = blockIdx.x / g.max_mt;
+  if (mt >= g.tile_start[g.E]) return;
+  const int e = tile_expert(g.tile_start, g.E, mt);
+  const int row0 = g.offsets[e] + (mt - g.tile_start[e]) * BM;
+  const int row_end = g.offsets[e + 1];
+  const int n0 = nt * BN;
+  const int K = g.K;
+
+  const uint16_t* A = (const uint16_t*)g.A;
+  const uint16_t* Bm[2];
+  Bm[0] = (const uint16_t*)g.B0 + ((size_t)e * g.Nout + n0) * K;
+  Bm[1] = NB == 2 ? (const uint16_t*)g.B1 + ((size_t)e * g.Nout + n0) * K : nullptr;
+
+  f32x16_t acc[NB][FM][FN];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[b][i][j][r] = 0.f;
+
+  for (int k0 = 0; k0 < K; k0 += BK) {
+#pragma unroll
+    for (int it = 0; it < (BM * CPR) / NT; ++it) {
+      const int q = tid + it * NT;
+      const int r = q / CPR, c = q % CPR;
+      int row = row0 + r;
+      row = row < row_end ? row : row_end - 1;
+      const u32x4_t v = *(const u32x4_t*)(A + (size_t)row * K + k0 + c * 8);
+      *(u32x4_t*)(lds_a + swz<BK>(r, c)) = v;
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int it = 0; it < (BN * CPR) / NT; ++it) {
+        const int q = tid + it * NT;
+        const int r = q / CPR, c = q % CPR;
+        const u32x4_t v = *(const u32x4_t*)(Bm[b] + (size_t)r * K + k0 + c * 8);
+        *(u32x4_t*)(lds_b[b] + swz<BK>(r, c)) = v;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int c = kk * 2 + (lane >> 5);
+      bf16x8_t af[FM];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = *(const bf16x8_t*)(lds_a + swz<BK>(wm * WM + i * 32 + (lane & 31), c));
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const bf16x8_t bfr =
+              *(const bf16x8_t*)(lds_b[b] + swz<BK>(wn * WN + j * 32 + (lane & 31), c));
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+            acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr, acc[b][i][j], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // Epilogue. 32x32 accumulator layout: register r of lane l holds
+  // row (r & 3) + 4 * (l >> 5) + 8 * (r >> 2), column l & 31.
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = n0 + wn * WN + j * 32 + (lane & 31);
+      const float bv = (MODE != MODE_GLU && g.bias) ? g.bias[(size_t)e * g.Nout + col] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = row0 + wm * WM + i * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
+        if (row >= row_end) continue;
+        float v;
+        if (MODE == MODE_GLU) {
+          v = silu(acc[0][i][j][r]) * acc[NB - 1][i][j][r];
+        } else if (MODE == MODE_ACT) {
+          v = act_fn(g.act, acc[0][i][j][r] + bv);
+        } else {
+          v = acc[0][i][j][r] + bv;
+        }
+        const size_t o = (size_t)row * g.Nout + col;
+        if (OUT_BF16)
+          ((uint16_t*)g.C)[o] = moe::f32_to_bf16_bits(v);
+        else
+          ((float*)g.C)[o] = v;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- fp32 SIMT
+template <int MODE>
+__global__ __launch_bounds__(256) void ggemm_f32_kernel(GemmArgs g) {
+  constexpr int BM = 64, BN = 64, BK = 16, TM = 4, TN = 4;
+  constexpr int NB = MODE == MODE_GLU ? 2 : 1;
+  __shared__ float As[BK][BM + 4];
+  __shared__ float Bs[NB][BK][BN + 4];
+  const int tid = threadIdx.x;
+  const int tx = tid % (BN / TN), ty = tid / (BN / TN);
+  const int mt = blockIdx.x % g.max_mt, nt = blockIdx.x / g.max_mt;
+  if (mt >= g.tile_start[g.E]) return;
+  const int e = tile_expert(g.tile_start, g.E, mt);
+  const int row0 = g.offsets[e] + (mt - g.tile_start[e]) * BM;
+  const int row_end = g.offsets[e + 1];
+  const int n0 = nt * BN;
+  const int K = g.K, Nout = g.Nout;
+  const float* A = (const float*)g.A;
+  const float* Bp[2] = {(const float*)g.B0 + (size_t)e * Nout * K,
+                        NB == 2 ? (const float*)g.B1 + (size_t)e * Nout * K : nullptr};
+  float acc[NB][TM][TN];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[b][i][j] = 0.f;
+  for (int k0 = 0; k0 < K; k0 += BK) {
+    for (int i = tid; i < BM * BK; i += 256) {
+      const int m = i / BK, kk = i % BK;
+      const int row = row0 + m, k = k0 + kk;
+      As[kk][m] = (row < row_end && k < K) ? A[(size_t)row * K + k] : 0.f;
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      for (int i = tid; i < BN * BK; i += 256) {
+        const int n = i / BK, kk = i % BK;
+        const int col = n0 + n, k = k0 + kk;
+        Bs[b][kk][n] = (col < Nout && k < K) ? Bp[b][(size_t)col * K + k] : 0.f;
+      }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk) {
+      float a[TM];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) a[i] = As[kk][ty * TM + i];
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const float bv = Bs[b][kk][tx * TN + j];
+#pragma unroll
+          for (int i = 0; i < TM; ++i) acc[b][i][j] = __builtin_fmaf(a[i], bv, acc[b][i][j]);
+        }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int row = row0 + ty * TM + i;
+    if (row >= row_end) continue;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + tx * TN + j;
+      if (col >= Nout) continue;
+      float v;
+      if (MODE == MODE_GLU) {
+        v = silu(acc[0][i][j]) * acc[NB - 1][i][j];
+      } else {
+        const float bv = g.bias ? g.bias[(size_t)e * Nout + col] : 0.f;
+        v = acc[0][i][j] + bv;
+        if (MODE == MODE_ACT) v = act_fn(g.act, v);
+      }
+      ((float*)g.C)[(size_t)row * Nout + col] = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- fp8 decode
+struct Fp8Args {
+  const uint16_t* A;   // [rows][K] bf16
+  const uint8_t* B0;   // [E][Nout][K] e4m3
+  const uint8_t* B1;   // GLU partner or null
+  const float* s0;     // [E][Nout]
+  const float* s1;     // [E][Nout] or null
+  void* C;             // [rows][Nout]
+  int K, Nout, E, act;
+  const int32_t* offsets;
+};
+
+// 8 e4m3 codes (two dwords) -> 8 bf16, exactly (e4m3 values are bf16 values).
+__device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  bf16x8_t r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+// Block: 4 waves, 64 output columns (16 per wave) of one expert
+// (blockIdx.y). Rows are processed in groups of 64 (four 16-row MFMA
+// tiles); a lane loads 16 consecutive K bytes of one weight row and feeds
+// them to two 16x16x32 MFMAs together with the matching 8+8 activations.
+template <int MODE, bool OUT_BF16>
+__global__ __launch_bounds__(256) void ffn_fp8_kernel(Fp8Args g) {
+  constexpr int NB = MODE == MODE_GLU ? 2 : 1;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e = blockIdx.y;
+  const int r_begin = g.offsets[e], r_end = g.offsets[e + 1];
+  if (r_begin >= r_end) return;
+  const int n = blockIdx.x * 64 + wave * 16 + (lane & 15);
+  const int grp = lane >> 4;
+  const int K = g.K;
+  const uint8_t* Bp[2];
+  Bp[0] = g.B0 + ((size_t)e * g.Nout + n) * K;
+  Bp[1] = NB == 2 ? g.B1 + ((size_t)e * g.Nout + n) * K : nullptr;
+
+  for (int rb = r_begin; rb < r_end; rb += 64) {
+    const int nchunk = min(4, (r_end - rb + 15) >> 4);
+    f32x4_t acc[NB][4];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc[b][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int k0 = 0; k0 < K; k0 += 64) {
+      const int kl = k0 + grp * 16;
+      bf16x8_t wlo[NB], whi[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const u32x4_t w = *(const u32x4_t*)(Bp[b] + kl);
+        wlo[b] = e4m3x8_to_bf16(w[0], w[1]);
+        whi[b] = e4m3x8_to_bf16(w[2], w[3]);
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        if (m >= nchunk) break;
+        const int row = rb + m * 16 + (lane & 15);
+        u32x4_t alo = {0u, 0u, 0u, 0u}, ahi = {0u, 0u, 0u, 0u};
+        if (row < r_end) {
+          const u32x4_t* ap = (const u32x4_t*)(g.A + (size_t)row * K + kl);
+          alo = ap[0];
+          ahi = ap[1];
+        }
+        const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, alo);
+        const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, ahi);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          acc[b][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, wlo[b], acc[b][m], 0, 0, 0);
+          acc[b][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, whi[b], acc[b][m], 0, 0, 0);
+        }
+      }
+    }
+    // 16x16 accumulator layout: register r of lane l holds row 4*(l>>4)+r,
+    // column l & 15.
+    const float sc0 = g.s0[(size_t)e * g.Nout + n];
+    const float sc1 = NB == 2 ? g.s1[(size_t)e * g.Nout + n] : 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      if (m >= nchunk) break;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = rb + m * 16 + 4 * grp + r;
+        if (row >= r_end) continue;
+        float v;
+        if (MODE == MODE_GLU)
+          v = silu(acc[0][m][r] * sc0) * (acc[NB - 1][m][r] * sc1);
+        else if (MODE == MODE_ACT)
+          v = act_fn(g.act, acc[0][m][r] * sc0);
+        else
+          v = acc[0][m][r] * sc0;
+        const size_t o = (size_t)row * g.Nout + n;
+        if (OUT_BF16)
+          ((uint16_t*)g.C)[o] = moe::f32_to_bf16_bits(v);
+        else
+          ((float*)g.C)[o] = v;
+      }
+    }
+  }
+}
+
+// bf16 MFMA tile configuration
+constexpr int kBM = 128, kBK = 64;
+
+template <int MODE, bool OUT_BF16>
+moe_status launch_bf16(const GemmArgs& g, hipStream_t st) {
+  if (g.Nout % 128 == 0) {
+    const int grid = g.max_mt * (g.Nout / 128);
+    ggemm_bf16_kernel<kBM, 128, kBK, 2, 2, MODE, OUT_BF16><<<grid, 256, 0, st>>>(g);
+  } else {
+    const int grid = g.max_mt * (g.Nout / 64);
+    ggemm_bf16_kernel<kBM, 64, kBK, 2, 2, MODE, OUT_BF16><<<grid, 256, 0, st>>>(g);
+  }
+  return moe_host::launch_status("grouped GEMM (bf16 MFMA)");
+}
+
+}  // namespace
+
+namespace moe_host {
+
+static size_t h_bytes(const moe_ffn_weights* w, moe_dtype act_dt, int max_rows) {
+  const size_t es = act_dt == MOE_F32 ? 4 : 2;
+  return align256((size_t)max_rows * w->d_ff * es);
+}
+
+size_t grouped_ffn_workspace_bytes(const moe_ffn_weights* w, moe_dtype act_dt, int max_rows) {
+  return h_bytes(w, act_dt, max_rows) + align256((size_t)(w->n_experts + 1) * sizeof(int32_t));
+}
+
+moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_dtype act_dt,
+                              const int32_t* offsets, int max_rows, void* y_rows,
+                              moe_dtype y_dt, void* workspace, hipStream_t st) {
+  const int E = w->n_experts, d = w->d_model, F = w->d_ff;
+  char* ws = (char*)workspace;
+  void* h = ws;
+  int32_t* tile_start = (int32_t*)(ws + h_bytes(w, act_dt, max_rows));
+  const bool glu = w->act == MOE_SWIGLU;
+  moe_status s;
+
+  if (w->w_dt == MOE_FP8_E4M3) {
+    Fp8Args a1{(const uint16_t*)x_rows, (const uint8_t*)w->w1, (const uint8_t*)w->w3,
+               w->s1, w->s3, h, d, F, E, (int)w->act, offsets};
+    dim3 g1(F / 64, E);
+    if (glu)
+      ffn_fp8_kernel<MODE_GLU, true><<<g1, 256, 0, st>>>(a1);
+    else
+      ffn_fp8_kernel<MODE_ACT, true><<<g1, 256, 0, st>>>(a1);
+    s = launch_status("grouped FFN fp8 GEMM 1");
+    if (s != MOE_OK) return s;
+    Fp8Args a2{(const uint16_t*)h, (const uint8_t*)w->w2, nullptr, w->s2, nullptr, y_rows,
+               F, d, E, (int)w->act, offsets};
+    dim3 g2(d / 64, E);
+    if (y_dt == MOE_BF16)
+      ffn_fp8_kernel<MODE_OUT, true><<<g2, 256, 0, st>>>(a2);
+    else
+      ffn_fp8_kernel<MODE_OUT, false><<<g2, 256, 0, st>>>(a2);
+    return launch_status("grouped FFN fp8 GEMM 2");
+  }
+
+  const int bm = act_dt == MOE_F32 ? 64 : kBM;
+  tile_table_kernel<<<1, 256, 0, st>>>(offsets, E, bm, tile_start);
+  s = launch_status("tile table");
+  if (s != MOE_OK) return s;
+  const int max_mt = (max_rows + bm - 1) / bm + E;
+
+  GemmArgs a1{x_rows, w->w1, w->w3, w->b1, h, d, F, E, max_mt, (int)w->act, offsets,
+              tile_start};
+  GemmArgs a2{h, w->w2, nullptr, w->b2, y_rows, F, d, E, max_mt, (int)w->act, offsets,
+              tile_start};
+
+  if (act_dt == MOE_F32) {
+    const int g1 = max_mt * ((F + 63) / 64), g2 = max_mt * ((d + 63) / 64);
+    if (glu)
+      ggemm_f32_kernel<MODE_GLU><<<g1, 256, 0, st>>>(a1);
+    else
+      ggemm_f32_kernel<MODE_ACT><<<g1, 256, 0, st>>>(a1);
+    ggemm_f32_kernel<MODE_OUT><<<g2, 256, 0, st>>>(a2);
+    return launch_status("grouped FFN fp32");
+  }
+  s = glu ? launch_bf16<MODE_GLU, true>(a1, st) : launch_bf16<MODE_ACT, true>(a1, st);
+  if (s != MOE_OK) return s;
+  return y_dt == MOE_BF16 ? launch_bf16<MODE_OUT, true>(a2, st)
+                          : launch_bf16<MODE_OUT, false>(a2, st);
+}
+
+}  // namespace moe_host

@@ -1,0 +1,329 @@
+// router.hip -- router GEMM, fp32 softmax and wave-level top-k for gfx950.
+//
+// The router scores every token against every expert's learned vector,
+// applies a softmax, and keeps the top-k experts (heavensheep.xyz MoE notes,
+// "Routing Function"; "MoE" on ld246.com, Q1: router = FFN + softmax).
+// Noisy gating H = x.W_g + N(0,1) * softplus(x.W_noise) follows the
+// chiang97912 MoE notes, "KeepTopK 策略". The selection key adds a
+// per-expert bias to the softmax score before top-k (ld246.com Q3, item 2).
+#include <math.h>
+
+#include "moe_device.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTokPerWave = 4;
+constexpr int kTokPerBlock = kTokPerWave * (kThreads / MOE_WAVE);
+
+// ---------------------------------------------------------------- GEMM
+// out[t][c] = sum_k x[t][k] * W[c][k] with W = [w_gate ; w_noise] (E or 2E
+// rows), fp32 accumulation. Tiles: BM tokens x BN router columns, BK = 16,
+// each thread a 4x4 register block. x is bf16 or fp32.
+template <int BM, int BN, bool XBF16>
+__global__ __launch_bounds__(kThreads) void router_gemm_kernel(
+    const void* __restrict__ xv, const float* __restrict__ wg, const float* __restrict__ wn,
+    float* __restrict__ out, int N, int d, int E, int E2) {
+  constexpr int BK = 16, TM = 4, TN = 4;
+  static_assert((BM / TM) * (BN / TN) == kThreads, "tile");
+  __shared__ float As[BK][BM + 4];
+  __shared__ float Bs[BK][BN + 4];
+  const int tid = threadIdx.x;
+  const int tx = tid % (BN / TN), ty = tid / (BN / TN);
+  const int t0 = blockIdx.x * BM, c0 = blockIdx.y * BN;
+  float acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = 0.f;
+
+  for (int k0 = 0; k0 < d; k0 += BK) {
+    for (int i = tid; i < BM * BK; i += kThreads) {
+      int m = i / BK, kk = i % BK;
+      int t = t0 + m, k = k0 + kk;
+      float v = 0.f;
+      if (t < N && k < d) {
+        size_t off = (size_t)t * d + k;
+        v = XBF16 ? moe::bf16_bits_to_f32(((const uint16_t*)xv)[off]) : ((const float*)xv)[off];
+      }
+      As[kk][m] = v;
+    }
+    for (int i = tid; i < BN * BK; i += kThreads) {
+      int n = i / BK, kk = i % BK;
+      int c = c0 + n, k = k0 + kk;
+      float v = 0.f;
+      if (c < E2 && k < d) v = (c < E) ? wg[(size_t)c * d + k] : wn[(size_t)(c - E) * d + k];
+      Bs[kk][n] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk) {
+      float a[TM], b[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) a[i] = As[kk][ty * TM + i];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) b[j] = Bs[kk][tx * TN + j];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    int t = t0 + ty * TM + i;
+    if (t >= N) continue;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      int c = c0 + tx * TN + j;
+      if (c < E2) out[(size_t)t * E2 + c] = acc[i][j];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- select
+struct SelectArgs {
+  int N, E, k, C, renorm;
+  const float* src;  // [N][stride]: logits, then (if noise) E noise columns
+  int stride;
+  int from_gemm;     // 1: apply logit_bias and noise to src; 0: src is logits_in
+  int noise;
+  const float* logit_bias;
+  const float* select_bias;
+  uint64_t seed;
+  int32_t* cand;
+  float* cand_s;
+  float* gates;
+  float* logits_out;
+  double* partials;  // [gridDim.x][E+1] or null
+};
+
+__device__ __forceinline__ float pick(const float* v, int slot, int n) {
+  float r = v[0];
+#pragma unroll
+  for (int s = 1; s < 4; ++s)
+    if (s < n && slot == s) r = v[s];
+  return r;
+}
+
+// One wave per token; expert e lives in lane e % 64, register slot e / 64.
+// Softmax tree: the zero-padded 256-wide halving tree equals the tree padded
+// to the next power of two (adding +0 changes nothing), so in-lane slot
+// sums (0+2, 1+3, then the two) are the h = 128 and h = 64 levels and the
+// wave butterfly does h = 32 .. 1.
+template <int SLOTS>
+__global__ __launch_bounds__(kThreads) void router_select_kernel(SelectArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ double red[kThreads / MOE_WAVE][257];
+  double acc[SLOTS];
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) acc[s] = 0.0;
+  double lse2 = 0.0;
+  const int E = a.E;
+
+  for (int i = 0; i < kTokPerWave; ++i) {
+    const int t = blockIdx.x * kTokPerBlock + wave * kTokPerWave + i;
+    if (t >= a.N) break;
+    const float* row = a.src + (size_t)t * a.stride;
+    float l[SLOTS];
+    bool valid[SLOTS];
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+      const int e = lane + 64 * s;
+      valid[s] = e < E;
+      float v = -INFINITY;
+      if (valid[s]) {
+        v = row[e];
+        if (a.from_gemm) {
+          if (a.logit_bias) v = v + a.logit_bias[e];
+          if (a.noise) {
+            float nv = row[E + e];
+            float sp = nv > 20.f ? nv : (float)log1p(exp((double)nv));
+            float z = moe::noise_normal(a.seed, (uint32_t)t, (uint32_t)e, (uint32_t)E);
+            v = __builtin_fmaf(z, sp, v);
+          }
+        }
+        if (a.logits_out) a.logits_out[(size_t)t * E + e] = v;
+      }
+      l[s] = v;
+    }
+    float m = l[0];
+#pragma unroll
+    for (int s = 1; s < SLOTS; ++s) m = fmaxf(m, l[s]);
+    m = moe::wave_max(m);
+
+    float u[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+      float dlt = l[s] - m;
+      u[s] = (valid[s] && !(dlt < -87.0f)) ? moe::softmax_exp(dlt) : 0.f;
+    }
+    float part;
+    {
+#pragma clang fp contract(off)
+      float a0 = u[0] + u[2];
+      float a1 = u[1] + u[3];
+      part = a0 + a1;
+    }
+    const float S = moe::wave_tree_sum(part);
+
+    float sc[4] = {0.f, 0.f, 0.f, 0.f};
+    uint64_t key[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+      const int e = lane + 64 * s;
+      if (valid[s]) {
+        sc[s] = u[s] / S;
+        float kv = a.select_bias ? sc[s] + a.select_bias[e] : sc[s];
+        if (kv == 0.0f) kv = 0.0f;
+        key[s] = ((uint64_t)moe::orderable(kv) << 32) | (uint32_t)(0xFFFFu - (uint32_t)e);
+        acc[s] += (double)sc[s];
+      }
+    }
+    if (lane == 0) {
+      double lse = (double)m + log((double)S);
+      lse2 += lse * lse;
+    }
+
+    // top-C: C rounds of a wave-wide max over each lane's best remaining key
+    uint64_t best = key[0];
+#pragma unroll
+    for (int s = 1; s < SLOTS; ++s) best = key[s] > best ? key[s] : best;
+    int my_c = 0;
+    float my_cs = 0.f;
+    for (int j = 0; j < a.C; ++j) {
+      const uint64_t w = moe::wave_max_u64(best);
+      const int ew = (int)(0xFFFFu - (uint32_t)(w & 0xFFFFu));
+      const int owner = ew & 63, slot = ew >> 6;
+      const float sw = __shfl(pick(sc, slot, SLOTS), owner, MOE_WAVE);
+      if (lane == j) {
+        my_c = ew;
+        my_cs = sw;
+      }
+      if (lane == owner) {
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s)
+          if (s == slot) key[s] = 0;
+        best = key[0];
+#pragma unroll
+        for (int s = 1; s < SLOTS; ++s) best = key[s] > best ? key[s] : best;
+      }
+    }
+    if (lane < a.C) {
+      a.cand[(size_t)t * a.C + lane] = my_c;
+      a.cand_s[(size_t)t * a.C + lane] = my_cs;
+    }
+    float Sk = __shfl(my_cs, 0, MOE_WAVE);
+    for (int j = 1; j < a.k; ++j) {
+#pragma clang fp contract(off)
+      Sk = Sk + __shfl(my_cs, j, MOE_WAVE);
+    }
+    if (lane < a.k) a.gates[(size_t)t * a.k + lane] = a.renorm ? my_cs / Sk : my_cs;
+  }
+
+  if (a.partials) {
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+      const int e = lane + 64 * s;
+      if (e < E) red[wave][e] = acc[s];
+    }
+    if (lane == 0) red[wave][E] = lse2;
+    __syncthreads();
+    for (int e = threadIdx.x; e <= E; e += kThreads) {
+      double v = red[0][e];
+#pragma unroll
+      for (int w = 1; w < kThreads / MOE_WAVE; ++w) v += red[w][e];
+      a.partials[(size_t)blockIdx.x * (E + 1) + e] = v;
+    }
+  }
+}
+
+// score_sums[e] = sum over blocks b (in order) of partials[b][e].
+__global__ __launch_bounds__(kThreads) void router_sum_partials_kernel(
+    const double* __restrict__ partials, int nblk, int width, double* __restrict__ out) {
+  for (int e = threadIdx.x; e < width; e += kThreads) {
+    double v = 0.0;
+    for (int b = 0; b < nblk; ++b) v += partials[(size_t)b * width + e];
+    out[e] = v;
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- host side
+namespace moe_host {
+
+size_t router_workspace_bytes(int N, int E, int with_noise) {
+  const int E2 = with_noise ? 2 * E : E;
+  const size_t nblk = (size_t)(N + kTokPerBlock - 1) / kTokPerBlock;
+  return align256((size_t)N * E2 * sizeof(float)) + align256(nblk * (E + 1) * sizeof(double));
+}
+
+moe_status router_launch(const moe_router_params* p, const void* x, moe_dtype x_dt,
+                         const float* w_gate, const float* logits_in, int32_t* cand_ids,
+                         float* cand_scores, float* gates, float* logits_out,
+                         double* score_sums, void* workspace, hipStream_t st) {
+  const int N = p->n_tokens, d = p->d_model, E = p->n_experts;
+  const int noise = (!logits_in && p->w_noise) ? 1 : 0;
+  const int E2 = noise ? 2 * E : E;
+  const int nblk = (N + kTokPerBlock - 1) / kTokPerBlock;
+  char* ws = (char*)workspace;
+  float* raw = (float*)ws;
+  double* partials = (double*)(ws + align256((size_t)N * E2 * sizeof(float)));
+
+  const float* src = logits_in;
+  int stride = E;
+  if (!logits_in) {
+    if (E2 <= 16) {
+      dim3 grid((N + 255) / 256, 1);
+      if (x_dt == MOE_BF16)
+        router_gemm_kernel<256, 16, true><<<grid, kThreads, 0, st>>>(x, w_gate, p->w_noise, raw, N, d, E, E2);
+      else
+        router_gemm_kernel<256, 16, false><<<grid, kThreads, 0, st>>>(x, w_gate, p->w_noise, raw, N, d, E, E2);
+    } else {
+      dim3 grid((N + 63) / 64, (E2 + 63) / 64);
+      if (x_dt == MOE_BF16)
+        router_gemm_kernel<64, 64, true><<<grid, kThreads, 0, st>>>(x, w_gate, p->w_noise, raw, N, d, E, E2);
+      else
+        router_gemm_kernel<64, 64, false><<<grid, kThreads, 0, st>>>(x, w_gate, p->w_noise, raw, N, d, E, E2);
+    }
+    moe_status s = launch_status("router_gemm");
+    if (s != MOE_OK) return s;
+    src = raw;
+    stride = E2;
+  }
+  SelectArgs a;
+  a.N = N;
+  a.E = E;
+  a.k = p->top_k;
+  a.C = p->n_cand;
+  a.renorm = p->renormalize;
+  a.src = src;
+  a.stride = stride;
+  a.from_gemm = logits_in ? 0 : 1;
+  a.noise = noise;
+  a.logit_bias = logits_in ? nullptr : p->logit_bias;
+  a.select_bias = p->select_bias;
+  a.seed = p->noise_seed;
+  a.cand = cand_ids;
+  a.cand_s = cand_scores;
+  a.gates = gates;
+  a.logits_out = logits_out;
+  a.partials = score_sums ? partials : nullptr;
+  if (E <= 64)
+    router_select_kernel<1><<<nblk, kThreads, 0, st>>>(a);
+  else if (E <= 128)
+    router_select_kernel<2><<<nblk, kThreads, 0, st>>>(a);
+  else
+    router_select_kernel<4><<<nblk, kThreads, 0, st>>>(a);
+  moe_status s = launch_status("router_select");
+  if (s != MOE_OK) return s;
+  if (score_sums) {
+    router_sum_partials_kernel<<<1, kThreads, 0, st>>>(partials, nblk, E + 1, score_sums);
+    s = launch_status("router_sum_partials");
+  }
+  return s;
+}
+
+}  // namespace moe_host

@@ -1,0 +1,101 @@
+"""Helpers for GPU-vs-oracle parity tests (no test functions here)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+# Output tolerances: max |y - y_ref| / RMS(y_ref).
+TOL_BF16 = 2e-2
+TOL_FP8 = 6e-2
+TOL_F32 = 1e-5
+# scores, losses and statistics: relative
+TOL_REL = 1e-5
+# id comparison skips tokens whose k-th / (k+1)-th key margin is below this
+MARGIN = 1e-3
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def out_tol(cfg):
+    if cfg.w_dtype == W.FP8_E4M3:
+        return TOL_FP8
+    if cfg.x_dtype == W.F32:
+        return TOL_F32
+    return TOL_BF16
+
+
+def host_view(t):
+    """torch tensor -> numpy in the oracle's storage form."""
+    if t is None:
+        return None
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
+    return t.numpy()
+
+
+def host_inputs(inp):
+    return {k: host_view(v) for k, v in inp.items()}
+
+
+def to_device(inp, device="cuda"):
+    return {k: (None if v is None else v.to(device)) for k, v in inp.items()}
+
+
+def rel_err(y, ref):
+    y = np.asarray(y, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = np.sqrt(np.mean(ref * ref))
+    if rms == 0:
+        return float(np.max(np.abs(y)))
+    return float(np.max(np.abs(y - ref)) / rms)
+
+
+def to_np(t):
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return t.numpy()
+
+
+class DeviceExperts(oracle.ExpertSource):
+    """Fetch one expert's weights from device tensors on demand."""
+
+    def __init__(self, dev_inputs, prefix=""):
+        self.d = dev_inputs
+        self.prefix = prefix
+        self.cache = {}
+
+    def get(self, e):
+        if e not in self.cache:
+            out = {}
+            for k in ("w1", "w3", "w2", "b1", "b2", "s1", "s3", "s2"):
+                v = self.d.get(self.prefix + k)
+                out[k] = None if v is None else host_view(v[e])
+            self.cache[e] = out
+        return self.cache[e]
+
+
+def experts_of(host, prefix=""):
+    return oracle.ExpertSource({k[len(prefix):]: v for k, v in host.items()
+                                if k.startswith(prefix) and v is not None})
+
+
+def margins(keys, k):
+    """k-th minus (k+1)-th largest key per token (inf when E == k)."""
+    s = -np.sort(-keys.astype(np.float64), axis=1)
+    if s.shape[1] <= k:
+        return np.full(s.shape[0], np.inf)
+    return s[:, k - 1] - s[:, k]
+
+
+def oracle_keys(route, select_bias):
+    s = route["s"]
+    return s + select_bias[None, :] if select_bias is not None else s

@@ -1,0 +1,86 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (MoELayer.forward). Routing and dispatch are compared over
+all tokens (bit-exact at level 1); layer outputs on a sample of tokens that
+the fp64 oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from parity_utils import (MARGIN, TOL_REL, DeviceExperts, host_view, margins, oracle_keys,
+                          out_tol, rel_err, require_gpu, to_np)
+
+pytestmark = pytest.mark.gpu
+
+SAMPLES = {"c1": 256, "c2": 12, "c3": 4, "c4": 24, "c5": 4}
+
+
+@pytest.fixture(scope="module")
+def moe():
+    require_gpu()
+    import sparse_mixture_experts_47_amd as m
+    return m
+
+
+@pytest.mark.parametrize("key", ["c1", "c2", "c3", "c4", "c5"])
+def test_full_size_parity(moe, key):
+    cfg = W.CONFIGS[key]
+    print("full-size", key, cfg.name, flush=True)
+    torch.manual_seed(0)
+    dev = W.make_inputs(cfg, "cuda")
+    torch.cuda.synchronize()
+    hx = host_view(dev["x"])
+    hwg = host_view(dev["w_gate"])
+    hb = {k: host_view(dev[k]) for k in ("logit_bias", "select_bias", "w_noise")}
+    H, _ = oracle.router_logits(hx, cfg.x_dtype, hwg, hb["logit_bias"], hb["w_noise"],
+                                cfg.noise_seed)
+    print("  oracle logits done", flush=True)
+    xdt = torch.float32 if cfg.x_dtype == W.F32 else torch.bfloat16
+    layer = moe.MoELayer(moe.spec_from_config(cfg), dev, x_dtype=xdt)
+
+    # ---- level 1: oracle logits in, bit-exact routing, sampled outputs
+    y = layer.forward(dev["x"], logits_in=torch.from_numpy(H).cuda()).clone()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(len(key))
+    N = cfg.n_tokens
+    sample = np.arange(N) if SAMPLES[key] >= N else np.sort(
+        rng.choice(N, SAMPLES[key], replace=False))
+    shared = DeviceExperts(dev, "shared_") if cfg.shared_d_ff else None
+    ref = oracle.layer_forward(cfg, hx, cfg.x_dtype, hwg, DeviceExperts(dev), shared,
+                               hb["logit_bias"], hb["select_bias"], hb["w_noise"], logits=H,
+                               tokens=sample)
+    r, d = ref["route"], ref["dispatch"]
+    assert np.array_equal(to_np(layer.cand_ids), r["cand_ids"])
+    assert np.array_equal(to_np(layer.gates).view(np.uint32), d["gates"].view(np.uint32))
+    for name in ("counts_routed", "counts_kept", "offsets", "row_of", "expert_of"):
+        assert np.array_equal(to_np(getattr(layer, name)), d[name]), name
+    assert np.array_equal(to_np(layer.perm_token)[:d["R"]], d["perm_token"])
+    err = rel_err(to_np(y)[sample], ref["y"])
+    print("  level-1 sampled max|dy|/rms =", err, " R =", d["R"], flush=True)
+    assert err <= out_tol(cfg)
+    st = ref["stats"]
+    torch.cuda.synchronize()
+    assert np.allclose(to_np(layer.P), st["P"], rtol=TOL_REL, atol=1e-12)
+    sc = to_np(layer.scalars)
+    for i, name in enumerate(("switch_aux", "importance_cv2", "z_loss", "drop_rate")):
+        assert abs(sc[i] - st[name]) <= TOL_REL * abs(st[name]) + 1e-7, name
+
+    # ---- level 2: the GPU's own router GEMM
+    y2 = layer.forward(dev["x"]).clone()
+    torch.cuda.synchronize()
+    lerr = rel_err(to_np(layer.logits), H)
+    print("  level-2 logits max|dl|/rms =", lerr, flush=True)
+    assert lerr <= TOL_REL
+    mg = margins(oracle_keys(r, hb["select_bias"]), cfg.top_k)
+    ok = mg >= MARGIN
+    gid = np.sort(to_np(layer.cand_ids)[:, :cfg.top_k], axis=1)
+    rid = np.sort(r["cand_ids"][:, :cfg.top_k], axis=1)
+    same = np.all(gid == rid, axis=1)
+    assert np.all(same[ok])
+    ge = np.sort(to_np(layer.expert_of)[sample], axis=1)
+    re = np.sort(d["expert_of"][sample], axis=1)
+    alike = np.all(ge == re, axis=1)
+    if alike.any():
+        assert rel_err(to_np(y2)[sample][alike], ref["y"][alike]) <= out_tol(cfg)
