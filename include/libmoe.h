@@ -121,7 +121,8 @@ moe_status moe_router_topk(const moe_router_params* p, const void* x, moe_dtype 
                            float* cand_scores, float* gates, float* logits_out,
                            double* score_sums, void* workspace, size_t ws_bytes,
                            void* hip_stream);
-size_t moe_router_workspace_bytes(int32_t n_tokens, int32_t n_experts, int32_t with_noise);
+size_t moe_router_workspace_bytes(int32_t n_tokens, int32_t d_model, int32_t n_experts,
+                                  int32_t with_noise);
 
 /* ---------------------------------------------------------------------- */
 /* moe_dispatch                                                            */
@@ -169,8 +170,8 @@ int32_t moe_capacity(int32_t n_tokens, int32_t n_experts, double capacity_factor
  * (mkbk-pku.cn "MOE的优化", Grouped GEMM): rows offsets[e] .. offsets[e+1]
  * of x_rows go through expert e:
  *   ReLU/GELU: y = W2 act(W1 x + b1) + b2;  SwiGLU: y = W2 (silu(W1 x) * W3 x)
- * The intermediate h is kept in bf16 (fp32 when act_dt is MOE_F32) in the
- * workspace. fp8 weights carry one fp32 scale per output channel (row of
+ * The intermediate h is kept in the workspace in bf16, or fp32 when
+ * act_dt is MOE_F32 or h_fp32 is set. fp8 weights carry one fp32 scale per output channel (row of
  * W1/W3/W2), applied after the K sum; activations stay bf16 (W8A16).
  * Shared always-on expert: the same call with n_experts = 1 and
  * offsets = {0, N} on x.
@@ -188,6 +189,12 @@ typedef struct {
   const float* s1; /* [E][d_ff] fp8 scales, else NULL */
   const float* s3; /* [E][d_ff] fp8 scales (SwiGLU), else NULL */
   const float* s2; /* [E][d_model] fp8 scales, else NULL */
+  /* Precision of the intermediate h between the two GEMMs (bf16 paths):
+   * 0 = bf16; 1 = fp32, with GEMM 2 run as two bf16 MFMA passes over the
+   * high and low bf16 parts of h (twice the GEMM 2 MFMA work, about 16 more
+   * bits of h). Meant for layers bound by weight traffic, where MFMA time is
+   * spare. Ignored for the fp32 path (h is fp32 there). */
+  int32_t h_fp32;
 } moe_ffn_weights;
 
 /*  x_rows   [max_rows][d_model] (act_dt), packed rows

@@ -21,7 +21,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe.so")
+# LIBMOE_PATH selects another build of the same sources (tile-tuning builds)
+LIB_PATH = os.environ.get("LIBMOE_PATH") or os.path.join(_HERE, "libmoe.so")
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 RELU, GELU, SWIGLU = 0, 1, 2
@@ -49,7 +50,7 @@ class FFNWeights(ctypes.Structure):
                 ("d_ff", ctypes.c_int32), ("act", ctypes.c_int32), ("w_dt", ctypes.c_int32),
                 ("w1", ctypes.c_void_p), ("w3", ctypes.c_void_p), ("w2", ctypes.c_void_p),
                 ("b1", ctypes.c_void_p), ("b2", ctypes.c_void_p), ("s1", ctypes.c_void_p),
-                ("s3", ctypes.c_void_p), ("s2", ctypes.c_void_p)]
+                ("s3", ctypes.c_void_p), ("s2", ctypes.c_void_p), ("h_fp32", ctypes.c_int32)]
 
 
 def _load():
@@ -61,7 +62,7 @@ def _load():
     L.moe_router_topk.argtypes = [ctypes.POINTER(RouterParams), P, i32, P, P, P, P, P, P, P, P,
                                   sz, P]
     L.moe_router_topk.restype = i32
-    L.moe_router_workspace_bytes.argtypes = [i32, i32, i32]
+    L.moe_router_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.moe_router_workspace_bytes.restype = sz
     L.moe_dispatch.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, i32, i32, P, P, P, P,
                                P, P, P, P, sz, P]
@@ -147,7 +148,7 @@ def moe_router_topk(x, w_gate, *, top_k, n_cand=None, renormalize=True, logit_bi
     p = RouterParams(N, d, E, top_k, n_cand, int(bool(renormalize)),
                      _ptr(logit_bias), _ptr(select_bias), _ptr(w_noise), int(noise_seed))
     if ws is None:
-        ws = workspace(lib.moe_router_workspace_bytes(N, E, int(w_noise is not None)),
+        ws = workspace(lib.moe_router_workspace_bytes(N, d, E, int(w_noise is not None)),
                        cand_ids.device)
     _check(lib.moe_router_topk(ctypes.byref(p), _ptr(x), _dt(x) if x is not None else F32,
                                _ptr(w_gate), _ptr(logits_in), _ptr(cand_ids), _ptr(cand_scores),
@@ -172,10 +173,12 @@ def moe_dispatch(cand_ids, cand_scores, gates, *, n_experts, top_k, policy=DROPL
                             _stream(stream)))
 
 
-def ffn_weights(w1, w2, w3=None, act=SWIGLU, b1=None, b2=None, s1=None, s3=None, s2=None):
+def ffn_weights(w1, w2, w3=None, act=SWIGLU, b1=None, b2=None, s1=None, s3=None, s2=None,
+                h_fp32=False):
     E, F, d = w1.shape
     return FFNWeights(E, d, F, act, _dt(w1), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(b1), _ptr(b2),
-                      _ptr(s1), _ptr(s3), _ptr(s2)), (w1, w2, w3, b1, b2, s1, s3, s2)
+                      _ptr(s1), _ptr(s3), _ptr(s2), int(bool(h_fp32))), \
+        (w1, w2, w3, b1, b2, s1, s3, s2)
 
 
 def moe_grouped_ffn(weights: FFNWeights, x_rows, offsets, y_rows, *, max_rows=None, ws=None,
@@ -224,6 +227,7 @@ class LayerSpec:
     noise_seed: int = 0
     bias_rate: float = 1e-3
     shared_d_ff: int = 0
+    h_fp32: bool = False
 
 
 class MoELayer:
@@ -269,18 +273,18 @@ class MoELayer:
         self.ffn, self._keep = ffn_weights(weights["w1"], weights["w2"], weights.get("w3"),
                                            s.act, weights.get("b1"), weights.get("b2"),
                                            weights.get("s1"), weights.get("s3"),
-                                           weights.get("s2"))
+                                           weights.get("s2"), s.h_fp32)
         self.shared = None
         if weights.get("shared_w1") is not None:
             self.shared, self._keep_sh = ffn_weights(
                 weights["shared_w1"], weights["shared_w2"], weights.get("shared_w3"), s.act,
                 None, None, weights.get("shared_s1"), weights.get("shared_s3"),
-                weights.get("shared_s2"))
+                weights.get("shared_s2"), s.h_fp32)
             self.sh_offsets = torch.tensor([0, N], **i32)
             self.y_shared = torch.empty((N, s.d_model), dtype=ydt, device=dev)
         xdt = _dt(torch.empty(0, dtype=x_dtype))
         noise = int(weights.get("w_noise") is not None)
-        self.ws_router = workspace(lib.moe_router_workspace_bytes(N, E, noise), dev)
+        self.ws_router = workspace(lib.moe_router_workspace_bytes(N, s.d_model, E, noise), dev)
         self.ws_dispatch = workspace(lib.moe_dispatch_workspace_bytes(N, E, k), dev)
         self.ws_ffn = workspace(lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(self.ffn), xdt,
                                                                     N * k), dev)
@@ -339,4 +343,4 @@ def spec_from_config(cfg) -> LayerSpec:
     """LayerSpec from a workload config object (duck-typed)."""
     return LayerSpec(cfg.n_tokens, cfg.d_model, cfg.n_experts, cfg.d_ff, cfg.top_k, cfg.act,
                      cfg.renormalize, cfg.overflow, cfg.capacity, cfg.n_cand, cfg.noise_seed,
-                     1e-3, cfg.shared_d_ff)
+                     1e-3, cfg.shared_d_ff, bool(getattr(cfg, "h_fp32", False)))

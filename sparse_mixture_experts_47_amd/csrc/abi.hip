@@ -8,7 +8,7 @@
 
 namespace moe_host {
 
-size_t router_workspace_bytes(int N, int E, int with_noise);
+size_t router_workspace_bytes(int N, int d, int E, int with_noise);
 moe_status router_launch(const moe_router_params* p, const void* x, moe_dtype x_dt,
                          const float* w_gate, const float* logits_in, int32_t* cand_ids,
                          float* cand_scores, float* gates, float* logits_out,
@@ -92,9 +92,10 @@ int32_t moe_capacity(int32_t n_tokens, int32_t n_experts, double capacity_factor
   return (int32_t)ceil(c - 1e-9);
 }
 
-size_t moe_router_workspace_bytes(int32_t n_tokens, int32_t n_experts, int32_t with_noise) {
-  if (n_tokens <= 0 || n_experts <= 0) return 0;
-  return router_workspace_bytes(n_tokens, n_experts, with_noise);
+size_t moe_router_workspace_bytes(int32_t n_tokens, int32_t d_model, int32_t n_experts,
+                                  int32_t with_noise) {
+  if (n_tokens <= 0 || n_experts <= 0 || d_model < 0) return 0;
+  return router_workspace_bytes(n_tokens, d_model, n_experts, with_noise);
 }
 
 size_t moe_dispatch_workspace_bytes(int32_t n_tokens, int32_t n_experts, int32_t top_k) {
@@ -111,7 +112,7 @@ size_t moe_grouped_ffn_workspace_bytes(const moe_ffn_weights* w, moe_dtype act_d
 size_t moe_workspace_bytes(int32_t n_tokens, int32_t n_experts, int32_t top_k, int32_t d_model,
                            int32_t d_ff) {
   if (n_tokens <= 0 || n_experts <= 0 || top_k <= 0) return 0;
-  size_t a = router_workspace_bytes(n_tokens, n_experts, 1);
+  size_t a = router_workspace_bytes(n_tokens, d_model, n_experts, 1);
   size_t b = dispatch_workspace_bytes(n_tokens, n_experts, top_k);
   moe_ffn_weights w = {};
   w.n_experts = n_experts;
@@ -145,7 +146,7 @@ moe_status moe_router_topk(const moe_router_params* p, const void* x, moe_dtype 
           "moe_router_topk: x dtype must be F32 or BF16");
   }
   const int noise = (!logits_in && p->w_noise) ? 1 : 0;
-  moe_status s = check_ws(workspace, ws_bytes, router_workspace_bytes(N, E, noise),
+  moe_status s = check_ws(workspace, ws_bytes, router_workspace_bytes(N, logits_in ? 0 : d, E, noise),
                           "moe_router_topk");
   if (s != MOE_OK) return s;
   return router_launch(p, x, x_dt, w_gate, logits_in, cand_ids, cand_scores, gates, logits_out,

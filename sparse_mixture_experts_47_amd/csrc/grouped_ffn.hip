@@ -18,6 +18,7 @@
 //    the K sum.
 #include <math.h>
 
+#include "gemm_bf16.h"
 #include "moe_device.h"
 
 namespace {
@@ -71,125 +72,6 @@ __device__ __forceinline__ int tile_expert(const int32_t* ts, int E, int mt) {
     if (ts[mid] <= mt) lo = mid; else hi = mid;
   }
   return lo;
-}
-
-// ---------------------------------------------------------------- bf16 MFMA
-// LDS tile rows are BK bf16 (BK/8 16-byte chunks); chunk c of row r is stored
-// at chunk position c ^ ((r >> 1) & (BK/8 - 1)), so the 16 lanes that read a
-// 16x16-byte column slice of rows r..r+15 hit distinct banks.
-template <int BK>
-__device__ __forceinline__ int swz(int r, int c) {
-  return r * BK + ((c ^ ((r >> 1) & (BK / 8 - 1))) << 3);
-}
-
-template <int BM, int BN, int BK, int WGM, int WGN, int MODE, bool OUT_BF16>
-__global__ __launch_bounds__(WGM * WGN * 64) void ggemm_bf16_kernel(GemmArgs g) {
-  constexpr int NT = WGM * WGN * 64;
-  constexpr int WM = BM / WGM, WN = BN / WGN;
-  constexpr int FM = WM / 32, FN = WN / 32;
-  constexpr int NB = MODE == MODE_GLU ? 2 : 1;
-  constexpr int CPR = BK / 8;
-  static_assert(FM >= 1 && FN >= 1, "wave tile");
-  static_assert((BM * CPR) % NT == 0 && (BN * CPR) % NT == 0, "load split");
-  __shared__ __attribute__((aligned(16))) uint16_t lds_a[BM * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_b[NB][BN * BK];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WGN, wn = wave % WGN;
-  const int mt = blockIdx.x % g.max_mt, nt = blockIdx.x / g.max_mt;
-  if (mt >= g.tile_start[g.E]) return;
-  const int e = tile_expert(g.tile_start, g.E, mt);
-  const int row0 = g.offsets[e] + (mt - g.tile_start[e]) * BM;
-  const int row_end = g.offsets[e + 1];
-  const int n0 = nt * BN;
-  const int K = g.K;
-
-  const uint16_t* A = (const uint16_t*)g.A;
-  const uint16_t* Bm[2];
-  Bm[0] = (const uint16_t*)g.B0 + ((size_t)e * g.Nout + n0) * K;
-  Bm[1] = NB == 2 ? (const uint16_t*)g.B1 + ((size_t)e * g.Nout + n0) * K : nullptr;
-
-  f32x16_t acc[NB][FM][FN];
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[b][i][j][r] = 0.f;
-
-  for (int k0 = 0; k0 < K; k0 += BK) {
-#pragma unroll
-    for (int it = 0; it < (BM * CPR) / NT; ++it) {
-      const int q = tid + it * NT;
-      const int r = q / CPR, c = q % CPR;
-      int row = row0 + r;
-      row = row < row_end ? row : row_end - 1;
-      const u32x4_t v = *(const u32x4_t*)(A + (size_t)row * K + k0 + c * 8);
-      *(u32x4_t*)(lds_a + swz<BK>(r, c)) = v;
-    }
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-#pragma unroll
-      for (int it = 0; it < (BN * CPR) / NT; ++it) {
-        const int q = tid + it * NT;
-        const int r = q / CPR, c = q % CPR;
-        const u32x4_t v = *(const u32x4_t*)(Bm[b] + (size_t)r * K + k0 + c * 8);
-        *(u32x4_t*)(lds_b[b] + swz<BK>(r, c)) = v;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int c = kk * 2 + (lane >> 5);
-      bf16x8_t af[FM];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *(const bf16x8_t*)(lds_a + swz<BK>(wm * WM + i * 32 + (lane & 31), c));
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const bf16x8_t bfr =
-              *(const bf16x8_t*)(lds_b[b] + swz<BK>(wn * WN + j * 32 + (lane & 31), c));
-#pragma unroll
-          for (int i = 0; i < FM; ++i)
-            acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr, acc[b][i][j], 0, 0, 0);
-        }
-      }
-    }
-    __syncthreads();
-  }
-
-  // Epilogue. 32x32 accumulator layout: register r of lane l holds
-  // row (r & 3) + 4 * (l >> 5) + 8 * (r >> 2), column l & 31.
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int col = n0 + wn * WN + j * 32 + (lane & 31);
-      const float bv = (MODE != MODE_GLU && g.bias) ? g.bias[(size_t)e * g.Nout + col] : 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row0 + wm * WM + i * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
-        if (row >= row_end) continue;
-        float v;
-        if (MODE == MODE_GLU) {
-          v = silu(acc[0][i][j][r]) * acc[NB - 1][i][j][r];
-        } else if (MODE == MODE_ACT) {
-          v = act_fn(g.act, acc[0][i][j][r] + bv);
-        } else {
-          v = acc[0][i][j][r] + bv;
-        }
-        const size_t o = (size_t)row * g.Nout + col;
-        if (OUT_BF16)
-          ((uint16_t*)g.C)[o] = moe::f32_to_bf16_bits(v);
-        else
-          ((float*)g.C)[o] = v;
-      }
-    }
-  }
 }
 
 // ---------------------------------------------------------------- fp32 SIMT
@@ -375,19 +257,51 @@ __global__ __launch_bounds__(256) void ffn_fp8_kernel(Fp8Args g) {
   }
 }
 
-// bf16 MFMA tile configuration
-constexpr int kBM = 128, kBK = 64;
+// bf16 MFMA tile configurations (BM, BN, BK, waves along M, waves along N).
+// GEMM 1 (gate/up): 256 rows x 128 output columns of both W1 and W3.
+// GEMM 2 (down): 256 x 128.
+#ifndef MOE_G1_WGN
+#define MOE_G1_WGN 2
+#endif
+#ifndef MOE_G2_BN
+#define MOE_G2_BN 128
+#endif
+#ifndef MOE_GROUP_N
+#define MOE_GROUP_N 8
+#endif
+constexpr int kBM = 256, kBK = 64;
 
-template <int MODE, bool OUT_BF16>
-moe_status launch_bf16(const GemmArgs& g, hipStream_t st) {
-  if (g.Nout % 128 == 0) {
-    const int grid = g.max_mt * (g.Nout / 128);
-    ggemm_bf16_kernel<kBM, 128, kBK, 2, 2, MODE, OUT_BF16><<<grid, 256, 0, st>>>(g);
-  } else {
-    const int grid = g.max_mt * (g.Nout / 64);
-    ggemm_bf16_kernel<kBM, 64, kBK, 2, 2, MODE, OUT_BF16><<<grid, 256, 0, st>>>(g);
+moe_status gemm_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) {
+    moe_host::set_error("%s: launch failed: %s", what, hipGetErrorString(e));
+    return MOE_EHIP;
   }
-  return moe_host::launch_status("grouped GEMM (bf16 MFMA)");
+  return MOE_OK;
+}
+
+moe_gemm::Args base_args(const void* A, const void* B0, const void* B1, const float* bias,
+                         void* C, int K, int Nrows, int E, int max_mt, int act,
+                         const int32_t* offsets, const int32_t* tile_start) {
+  moe_gemm::Args g{};
+  g.A = A;
+  g.B[0] = (const uint16_t*)B0;
+  g.B[1] = (const uint16_t*)B1;
+  g.B[2] = nullptr;
+  g.bias = bias;
+  g.C = C;
+  g.K = K;
+  g.Nrows = Nrows;
+  g.n_valid = Nrows;
+  g.ldc = Nrows;
+  g.c_split = 0;
+  g.k_chunk = K;
+  g.E = E;
+  g.max_mt = max_mt;
+  g.act = act;
+  g.group_n = MOE_GROUP_N;
+  g.offsets = offsets;
+  g.tile_start = tile_start;
+  return g;
 }
 
 }  // namespace
@@ -395,7 +309,7 @@ moe_status launch_bf16(const GemmArgs& g, hipStream_t st) {
 namespace moe_host {
 
 static size_t h_bytes(const moe_ffn_weights* w, moe_dtype act_dt, int max_rows) {
-  const size_t es = act_dt == MOE_F32 ? 4 : 2;
+  const size_t es = (act_dt == MOE_F32 || w->h_fp32) ? 4 : 2;
   return align256((size_t)max_rows * w->d_ff * es);
 }
 
@@ -439,12 +353,11 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
   if (s != MOE_OK) return s;
   const int max_mt = (max_rows + bm - 1) / bm + E;
 
-  GemmArgs a1{x_rows, w->w1, w->w3, w->b1, h, d, F, E, max_mt, (int)w->act, offsets,
-              tile_start};
-  GemmArgs a2{h, w->w2, nullptr, w->b2, y_rows, F, d, E, max_mt, (int)w->act, offsets,
-              tile_start};
-
   if (act_dt == MOE_F32) {
+    GemmArgs a1{x_rows, w->w1, w->w3, w->b1, h, d, F, E, max_mt, (int)w->act, offsets,
+                tile_start};
+    GemmArgs a2{h, w->w2, nullptr, w->b2, y_rows, F, d, E, max_mt, (int)w->act, offsets,
+                tile_start};
     const int g1 = max_mt * ((F + 63) / 64), g2 = max_mt * ((d + 63) / 64);
     if (glu)
       ggemm_f32_kernel<MODE_GLU><<<g1, 256, 0, st>>>(a1);
@@ -453,10 +366,42 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
     ggemm_f32_kernel<MODE_OUT><<<g2, 256, 0, st>>>(a2);
     return launch_status("grouped FFN fp32");
   }
-  s = glu ? launch_bf16<MODE_GLU, true>(a1, st) : launch_bf16<MODE_ACT, true>(a1, st);
+
+  using namespace moe_gemm;
+  const bool h32 = w->h_fp32 != 0;
+  Args g1 = base_args(x_rows, w->w1, w->w3, w->b1, h, d, F, E, max_mt, (int)w->act, offsets,
+                      tile_start);
+  hipError_t err;
+  if (F % 128 != 0) {  // d_ff a multiple of 64 only: 64-column tiles
+    if (glu)
+      err = h32 ? launch<kBM, 64, kBK, 2, 2, 1, 2, EPI_GLU, false>(g1, 1, st)
+                : launch<kBM, 64, kBK, 2, 2, 1, 2, EPI_GLU, true>(g1, 1, st);
+    else
+      err = h32 ? launch<kBM, 64, kBK, 2, 2, 1, 1, EPI_ACT, false>(g1, 1, st)
+                : launch<kBM, 64, kBK, 2, 2, 1, 1, EPI_ACT, true>(g1, 1, st);
+  } else if (glu) {
+    err = h32 ? launch<kBM, 128, kBK, 2, MOE_G1_WGN, 1, 2, EPI_GLU, false>(g1, 1, st)
+              : launch<kBM, 128, kBK, 2, MOE_G1_WGN, 1, 2, EPI_GLU, true>(g1, 1, st);
+  } else {
+    err = h32 ? launch<kBM, 128, kBK, 2, 2, 1, 1, EPI_ACT, false>(g1, 1, st)
+              : launch<kBM, 128, kBK, 2, 2, 1, 1, EPI_ACT, true>(g1, 1, st);
+  }
+  s = gemm_status(err, "grouped FFN GEMM 1");
   if (s != MOE_OK) return s;
-  return y_dt == MOE_BF16 ? launch_bf16<MODE_OUT, true>(a2, st)
-                          : launch_bf16<MODE_OUT, false>(a2, st);
+  Args g2 = base_args(h, w->w2, nullptr, w->b2, y_rows, F, d, E, max_mt, (int)w->act, offsets,
+                      tile_start);
+  const bool ybf = y_dt == MOE_BF16;
+  if (h32) {  // two A planes: 64-column tiles keep LDS at 144 KB
+    err = ybf ? launch<kBM, 64, kBK, 2, 2, 2, 1, EPI_OUT, true>(g2, 1, st)
+              : launch<kBM, 64, kBK, 2, 2, 2, 1, EPI_OUT, false>(g2, 1, st);
+  } else if (d % MOE_G2_BN != 0) {
+    err = ybf ? launch<kBM, 64, kBK, 2, 2, 1, 1, EPI_OUT, true>(g2, 1, st)
+              : launch<kBM, 64, kBK, 2, 2, 1, 1, EPI_OUT, false>(g2, 1, st);
+  } else {
+    err = ybf ? launch<kBM, MOE_G2_BN, kBK, 2, 2, 1, 1, EPI_OUT, true>(g2, 1, st)
+              : launch<kBM, MOE_G2_BN, kBK, 2, 2, 1, 1, EPI_OUT, false>(g2, 1, st);
+  }
+  return gemm_status(err, "grouped FFN GEMM 2");
 }
 
 }  // namespace moe_host

@@ -8,6 +8,7 @@
 // per-expert bias to the softmax score before top-k (ld246.com Q3, item 2).
 #include <math.h>
 
+#include "gemm_bf16.h"
 #include "moe_device.h"
 
 namespace {
@@ -85,8 +86,10 @@ __global__ __launch_bounds__(kThreads) void router_gemm_kernel(
 // ---------------------------------------------------------------- select
 struct SelectArgs {
   int N, E, k, C, renorm;
-  const float* src;  // [N][stride]: logits, then (if noise) E noise columns
+  const float* src;  // [nsplit][N][stride]: logits, then (if noise) E noise columns
   int stride;
+  int nsplit;        // K-split partials summed in order s = 0 .. nsplit-1
+  long long split_stride;
   int from_gemm;     // 1: apply logit_bias and noise to src; 0: src is logits_in
   int noise;
   const float* logit_bias;
@@ -135,10 +138,12 @@ __global__ __launch_bounds__(kThreads) void router_select_kernel(SelectArgs a) {
       float v = -INFINITY;
       if (valid[s]) {
         v = row[e];
+        for (int q = 1; q < a.nsplit; ++q) v = v + row[q * a.split_stride + e];
         if (a.from_gemm) {
           if (a.logit_bias) v = v + a.logit_bias[e];
           if (a.noise) {
             float nv = row[E + e];
+            for (int q = 1; q < a.nsplit; ++q) nv = nv + row[q * a.split_stride + E + e];
             float sp = nv > 20.f ? nv : (float)log1p(exp((double)nv));
             float z = moe::noise_normal(a.seed, (uint32_t)t, (uint32_t)e, (uint32_t)E);
             v = __builtin_fmaf(z, sp, v);
@@ -239,6 +244,40 @@ __global__ __launch_bounds__(kThreads) void router_select_kernel(SelectArgs a) {
   }
 }
 
+// The router weights as three bf16 planes whose sum is the fp32 value:
+// hi = bf16(w), mid = bf16(w - hi), lo = bf16(w - hi - mid) (each step
+// exact in fp32). Rows: w_gate 0..E-1, w_noise E..2E-1, zero padding.
+// x is bf16, so x . W runs on bf16 MFMA with every product exact.
+__global__ __launch_bounds__(kThreads) void router_split_weights_kernel(
+    const float* __restrict__ wg, const float* __restrict__ wn, int E, int E2, int E2pad, int d,
+    uint16_t* __restrict__ planes) {
+  const size_t n = (size_t)E2pad * d;
+  for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * kThreads) {
+    const int c = (int)(i / d), k = (int)(i % d);
+    float w = 0.f;
+    if (c < E) w = wg[(size_t)c * d + k];
+    else if (c < E2) w = wn[(size_t)(c - E) * d + k];
+    const uint16_t hi = moe::f32_to_bf16_bits(w);
+    const float r1 = w - moe::bf16_bits_to_f32(hi);
+    const uint16_t mid = moe::f32_to_bf16_bits(r1);
+    const float r2 = r1 - moe::bf16_bits_to_f32(mid);
+    planes[i] = hi;
+    planes[n + i] = mid;
+    planes[2 * n + i] = moe::f32_to_bf16_bits(r2);
+  }
+}
+
+// One group of N rows: offsets = {0, N}, tile_start = {0, ceil(N / bm)}.
+__global__ void router_group_table_kernel(int N, int bm, int32_t* offsets, int32_t* tile_start) {
+  if (threadIdx.x == 0) {
+    offsets[0] = 0;
+    offsets[1] = N;
+    tile_start[0] = 0;
+    tile_start[1] = (N + bm - 1) / bm;
+  }
+}
+
 // score_sums[e] = sum over blocks b (in order) of partials[b][e].
 __global__ __launch_bounds__(kThreads) void router_sum_partials_kernel(
     const double* __restrict__ partials, int nblk, int width, double* __restrict__ out) {
@@ -254,10 +293,51 @@ __global__ __launch_bounds__(kThreads) void router_sum_partials_kernel(
 // ---------------------------------------------------------------- host side
 namespace moe_host {
 
-size_t router_workspace_bytes(int N, int E, int with_noise) {
-  const int E2 = with_noise ? 2 * E : E;
+namespace {
+constexpr int kRouterBM = 128;
+
+struct RouterPlan {
+  bool mfma;
+  int E2, E2pad, bn, nsplit, k_chunk;
+  size_t planes_bytes, raw_bytes, table_bytes, stat_bytes;
+};
+
+RouterPlan plan_router(int N, int d, int E, int with_noise, bool x_bf16) {
+  RouterPlan p{};
+  p.E2 = with_noise ? 2 * E : E;
+  p.mfma = x_bf16 && d > 0 && d % 64 == 0;
+  p.nsplit = 1;
+  p.k_chunk = d;
+  if (p.mfma) {
+    p.bn = p.E2 <= 32 ? 32 : 64;
+    p.E2pad = (p.E2 + p.bn - 1) / p.bn * p.bn;
+    const int tiles = ((N + kRouterBM - 1) / kRouterBM) * (p.E2pad / p.bn);
+    const int KT = d / 64;
+    int want = (512 + tiles - 1) / tiles;
+    want = want < 1 ? 1 : (want > KT ? KT : want);
+    const int steps = (KT + want - 1) / want;
+    p.k_chunk = steps * 64;
+    p.nsplit = (KT + steps - 1) / steps;
+    p.planes_bytes = align256((size_t)3 * p.E2pad * d * sizeof(uint16_t));
+  } else {
+    p.bn = 0;
+    p.E2pad = p.E2;
+  }
+  p.raw_bytes = align256((size_t)p.nsplit * N * p.E2pad * sizeof(float));
+  p.table_bytes = 256;
   const size_t nblk = (size_t)(N + kTokPerBlock - 1) / kTokPerBlock;
-  return align256((size_t)N * E2 * sizeof(float)) + align256(nblk * (E + 1) * sizeof(double));
+  p.stat_bytes = align256(nblk * (E + 1) * sizeof(double));
+  return p;
+}
+}  // namespace
+
+size_t router_workspace_bytes(int N, int d, int E, int with_noise) {
+  // the larger of the two plans (x dtype is not known at query time)
+  RouterPlan a = plan_router(N, d, E, with_noise, true);
+  RouterPlan b = plan_router(N, d, E, with_noise, false);
+  size_t sa = a.planes_bytes + a.raw_bytes + a.table_bytes + a.stat_bytes;
+  size_t sb = b.planes_bytes + b.raw_bytes + b.table_bytes + b.stat_bytes;
+  return sa > sb ? sa : sb;
 }
 
 moe_status router_launch(const moe_router_params* p, const void* x, moe_dtype x_dt,
@@ -266,32 +346,76 @@ moe_status router_launch(const moe_router_params* p, const void* x, moe_dtype x_
                          double* score_sums, void* workspace, hipStream_t st) {
   const int N = p->n_tokens, d = p->d_model, E = p->n_experts;
   const int noise = (!logits_in && p->w_noise) ? 1 : 0;
-  const int E2 = noise ? 2 * E : E;
+  // same effective d as the workspace check: no GEMM when logits come in
+  const RouterPlan pl = plan_router(N, logits_in ? 0 : d, E, noise, x_dt == MOE_BF16);
   const int nblk = (N + kTokPerBlock - 1) / kTokPerBlock;
   char* ws = (char*)workspace;
-  float* raw = (float*)ws;
-  double* partials = (double*)(ws + align256((size_t)N * E2 * sizeof(float)));
+  uint16_t* planes = (uint16_t*)ws;
+  float* raw = (float*)(ws + pl.planes_bytes);
+  int32_t* table = (int32_t*)(ws + pl.planes_bytes + pl.raw_bytes);
+  double* partials = (double*)(ws + pl.planes_bytes + pl.raw_bytes + pl.table_bytes);
 
   const float* src = logits_in;
-  int stride = E;
+  int stride = E, nsplit = 1;
   if (!logits_in) {
-    if (E2 <= 16) {
-      dim3 grid((N + 255) / 256, 1);
-      if (x_dt == MOE_BF16)
-        router_gemm_kernel<256, 16, true><<<grid, kThreads, 0, st>>>(x, w_gate, p->w_noise, raw, N, d, E, E2);
-      else
-        router_gemm_kernel<256, 16, false><<<grid, kThreads, 0, st>>>(x, w_gate, p->w_noise, raw, N, d, E, E2);
+    const int E2 = pl.E2;
+    if (pl.mfma) {
+      const size_t n = (size_t)pl.E2pad * d;
+      const int sgrid = (int)((n + kThreads - 1) / kThreads < 2048 ? (n + kThreads - 1) / kThreads : 2048);
+      router_split_weights_kernel<<<sgrid, kThreads, 0, st>>>(w_gate, p->w_noise, E, E2,
+                                                              pl.E2pad, d, planes);
+      router_group_table_kernel<<<1, 64, 0, st>>>(N, kRouterBM, table, table + 2);
+      moe_status s = launch_status("router weight split");
+      if (s != MOE_OK) return s;
+      using namespace moe_gemm;
+      Args g{};
+      g.A = x;
+      g.B[0] = planes;
+      g.B[1] = planes + n;
+      g.B[2] = planes + 2 * n;
+      g.bias = nullptr;
+      g.C = raw;
+      g.K = d;
+      g.Nrows = pl.E2pad;
+      g.n_valid = E2;
+      g.ldc = pl.E2pad;
+      g.c_split = (long long)N * pl.E2pad;
+      g.k_chunk = pl.k_chunk;
+      g.E = 1;
+      g.max_mt = (N + kRouterBM - 1) / kRouterBM;
+      g.act = 0;
+      g.group_n = 8;
+      g.offsets = table;
+      g.tile_start = table + 2;
+      hipError_t err =
+          pl.bn == 32
+              ? launch<kRouterBM, 32, 64, 4, 1, 1, 3, EPI_SUM, false>(g, pl.nsplit, st)
+              : launch<kRouterBM, 64, 64, 2, 2, 1, 3, EPI_SUM, false>(g, pl.nsplit, st);
+      if (err != hipSuccess) {
+        set_error("router GEMM: launch failed: %s", hipGetErrorString(err));
+        return MOE_EHIP;
+      }
+      stride = pl.E2pad;
+      nsplit = pl.nsplit;
     } else {
-      dim3 grid((N + 63) / 64, (E2 + 63) / 64);
-      if (x_dt == MOE_BF16)
-        router_gemm_kernel<64, 64, true><<<grid, kThreads, 0, st>>>(x, w_gate, p->w_noise, raw, N, d, E, E2);
-      else
-        router_gemm_kernel<64, 64, false><<<grid, kThreads, 0, st>>>(x, w_gate, p->w_noise, raw, N, d, E, E2);
+      if (E2 <= 16) {
+        dim3 grid((N + 255) / 256, 1);
+        if (x_dt == MOE_BF16)
+          router_gemm_kernel<256, 16, true><<<grid, kThreads, 0, st>>>(x, w_gate, p->w_noise, raw, N, d, E, E2);
+        else
+          router_gemm_kernel<256, 16, false><<<grid, kThreads, 0, st>>>(x, w_gate, p->w_noise, raw, N, d, E, E2);
+      } else {
+        dim3 grid((N + 63) / 64, (E2 + 63) / 64);
+        if (x_dt == MOE_BF16)
+          router_gemm_kernel<64, 64, true><<<grid, kThreads, 0, st>>>(x, w_gate, p->w_noise, raw, N, d, E, E2);
+        else
+          router_gemm_kernel<64, 64, false><<<grid, kThreads, 0, st>>>(x, w_gate, p->w_noise, raw, N, d, E, E2);
+      }
+      moe_status s = launch_status("router_gemm");
+      if (s != MOE_OK) return s;
+      stride = E2;
     }
-    moe_status s = launch_status("router_gemm");
-    if (s != MOE_OK) return s;
     src = raw;
-    stride = E2;
   }
   SelectArgs a;
   a.N = N;
@@ -301,6 +425,8 @@ moe_status router_launch(const moe_router_params* p, const void* x, moe_dtype x_
   a.renorm = p->renormalize;
   a.src = src;
   a.stride = stride;
+  a.nsplit = nsplit;
+  a.split_stride = (long long)N * stride;
   a.from_gemm = logits_in ? 0 : 1;
   a.noise = noise;
   a.logit_bias = logits_in ? nullptr : p->logit_bias;

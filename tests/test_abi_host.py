@@ -33,7 +33,7 @@ def test_capacity_and_workspace_queries(lib):
     assert lib.capacity(256, 4, 1.25) == 80
     assert lib.capacity(16384, 64, 1.0) == 256
     assert lib.capacity(10, 3, 1.0) == 4
-    assert lib.lib.moe_router_workspace_bytes(4096, 8, 0) > 4096 * 8 * 4
+    assert lib.lib.moe_router_workspace_bytes(4096, 4096, 8, 0) > 4096 * 8 * 4
     assert lib.lib.moe_dispatch_workspace_bytes(8192, 256, 8) > 0
     assert lib.lib.moe_workspace_bytes(4096, 8, 2, 4096, 14336) >= 8192 * 14336 * 2
 
@@ -57,7 +57,7 @@ def test_validation_errors_before_any_launch(lib):
     # workspace too small
     assert L.moe_dispatch(16, 4, 1, 1, 0, -1, fake, fake, fake, None, 1, 0, fake, fake, fake,
                           fake, fake, fake, None, fake, 8, None) == 3
-    w = lib.FFNWeights(8, 4096, 100, 2, 1, 4096, 4096, 4096, None, None, None, None, None)
+    w = lib.FFNWeights(8, 4096, 100, 2, 1, 4096, 4096, 4096, None, None, None, None, None, 0)
     assert L.moe_grouped_ffn(ctypes.byref(w), fake, 1, fake, 10, fake, 1, fake, 1 << 30,
                              None) == 2
     assert L.moe_status_string(3) == b"MOE_EWORKSPACE"

@@ -328,3 +328,31 @@ def test_abi_errors_leave_outputs_untouched(moe):
     assert ei.value.status == 3
     torch.cuda.synchronize()
     assert torch.all(cand == -5) and torch.all(gates == -5.0)
+
+
+def test_grouped_ffn_fp32_intermediate_is_tighter(moe):
+    """With h kept in fp32 (GEMM 2 as hi + lo bf16 passes) the grouped FFN
+    error falls well below the bf16-h error (about 2^-9 relative per h
+    element), down to the fp32 accumulation level."""
+    cfg = W.REDUCED["c4"]
+    inp = W.make_inputs(cfg, "cpu")
+    host = host_inputs(inp)
+    dev = to_device(inp)
+    E = cfg.n_experts
+    counts = np.full(E, 37)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offs[-1])
+    tok = np.arange(R) % cfg.n_tokens
+    x = dev["x"][torch.from_numpy(tok).cuda()].contiguous()
+    X64 = oracle.decode_rows(host["x"][tok], cfg.x_dtype)
+    ref = oracle.ffn_for_assignments(np.arange(R), np.repeat(np.arange(E), counts), X64,
+                                     cfg.act, cfg.w_dtype, experts_of(host))
+    errs = {}
+    for h32 in (False, True):
+        y = torch.empty((R, cfg.d_model), dtype=torch.float32, device="cuda")
+        w, keep = moe.ffn_weights(dev["w1"], dev["w2"], dev["w3"], cfg.act, h_fp32=h32)
+        moe.moe_grouped_ffn(w, x, torch.from_numpy(offs).cuda(), y, max_rows=R)
+        torch.cuda.synchronize()
+        errs[h32] = rel_err(to_np(y), ref)
+    print("bf16 h:", errs[False], " fp32 h:", errs[True])
+    assert errs[True] <= 1e-3 and errs[True] < errs[False] / 8

@@ -60,6 +60,9 @@ class MoEConfig:
     weight_seed: Optional[int] = None  # seed for expert weights (C5 reuses C3's)
     noise_seed: int = 0
     router_std: float = 0.02
+    # keep the FFN intermediate h in fp32 (GEMM 2 as hi+lo bf16 passes); used
+    # where the layer is bound by weight reads and MFMA time is spare
+    h_fp32: bool = False
 
     @property
     def n_cand(self) -> int:
@@ -89,7 +92,7 @@ C3 = MoEConfig("deepseek_prefill_top8_shared", 8192, 7168, 256, 2048, 8, ACT_SWI
                BF16, True, shared_d_ff=2048, select_bias=True, seed=3)
 C4 = MoEConfig("switch_skewed_top1_capacity", 16384, 1024, 64, 4096, 1, ACT_GELU, BF16, BF16,
                False, overflow=REROUTE_THEN_DROP, capacity_factor=1.0, zipf_s=1.1,
-               noisy=True, seed=4, noise_seed=44)
+               noisy=True, seed=4, noise_seed=44, h_fp32=True)
 C5 = MoEConfig("deepseek_decode_fp8", 64, 7168, 256, 2048, 8, ACT_SWIGLU, BF16, FP8_E4M3,
                True, shared_d_ff=2048, seed=5, weight_seed=3)
 
