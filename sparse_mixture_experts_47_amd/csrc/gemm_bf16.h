@@ -6,19 +6,15 @@
 // device-built tile table (no host sync on the group sizes).
 //
 // Operand planes: an operand may be given as several bf16 planes whose sum
-// is the value (NA planes of A, NB planes of B). NA = 2 takes fp32 A and
-// splits every element into hi = bf16(a), lo = bf16(a - hi) while staging;
-// NB = 3 takes three bf16 planes of an fp32 matrix (hi, mid, lo). All plane
+// is the value (NA planes of A, NB planes of B): NA = 2 is an fp32 operand
+// held as hi = bf16(a), lo = bf16(a - hi); NB = 3 holds an fp32 matrix as
+// three bf16 planes (hi, mid, lo). All plane
 // products go into one accumulator, except for the gated (GLU) epilogue
 // where B plane 0 (gate) and plane 1 (up) keep separate accumulators.
 //
-// Pipeline: double-buffered LDS. While the MFMAs consume K tile t from one
-// buffer, the global loads of tile t+1 are in flight into registers; they are
-// written to the other buffer after the compute, then one barrier.
-// LDS rows are BK bf16 = BK/8 16-byte chunks; chunk c of row r sits at chunk
-// position c ^ (r & 7), so the 8 rows that one 128-byte LDS cycle serves
-// (for the MFMA operand reads: 8 lanes, 8 consecutive rows, one chunk each)
-// fall on distinct banks.
+// Pipeline: operands go from global memory straight into a ring of LDS
+// stages (see the direct-to-LDS kernel below), several K tiles ahead of the
+// MFMAs.
 //
 // Tile order: workgroups are dealt round-robin to the 8 XCDs, so block b is
 // remapped to a logical tile such that each XCD walks one contiguous range
@@ -43,6 +39,8 @@ struct Args {
   int n_valid;           // columns to store (<= Nrows)
   int ldc;
   long long c_split;     // element offset between K-split outputs
+  long long a_plane;     // element offset between A planes (direct-LDS kernel)
+  long long c_plane;     // element offset of the lo plane of a bf16 pair output
   int k_chunk;           // K per split (multiple of BK)
   int E, max_mt, act;
   int n_tiles_n;         // Nrows / BN
@@ -67,52 +65,55 @@ __device__ __forceinline__ int tile_expert(const int32_t* ts, int E, int mt) {
   return lo;
 }
 
-template <int BK>
-__device__ __forceinline__ int lds_off(int r, int c) {
-  return r * BK + ((c ^ (r & 7)) << 3);
+// ---------------------------------------------------------------------------
+// Direct-to-LDS variant (bf16 A only): every 16-byte chunk goes from global
+// memory straight into LDS with global_load_lds_dwordx4, so no staging
+// registers are needed and NS LDS stages let the loads run NS-1 K steps ahead
+// of the MFMAs. One such instruction writes 1 KB of LDS: lane l's 16 bytes
+// land at l*16. With BK = 32 (64-byte LDS rows, 4 chunks) a 1 KB segment is
+// 16 rows; lane l of segment j covers row 16j + l/4, physical chunk l%4, and
+// fetches the logical chunk that the swizzle places there:
+// c = (l%4) ^ ((row >> 2) & 3). The same swizzle serves the MFMA reads: a
+// 16-byte LDS read serves 16 lanes (16 consecutive rows, one logical chunk)
+// per cycle over 64 four-byte banks; rows r, r+4, r+8, r+12 share bank
+// group r%4, and the swizzle gives them four different chunks.
+__device__ __forceinline__ int dlds_off(int r, int c) {  // bf16 elements, BK = 32
+  return r * 32 + ((c ^ ((r >> 2) & 3)) << 3);
 }
 
-__device__ __forceinline__ u32x4_t split_hi_lo(const f32x4_t& a, const f32x4_t& b, u32x4_t& lo) {
-  u32x4_t hi;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const float x0 = a[2 * i], x1 = a[2 * i + 1];
-    const uint16_t h0 = moe::f32_to_bf16_bits(x0), h1 = moe::f32_to_bf16_bits(x1);
-    hi[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-    lo[i] = moe::pack_bf16x2(x0 - moe::bf16_bits_to_f32(h0), x1 - moe::bf16_bits_to_f32(h1));
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const float x0 = b[2 * i], x1 = b[2 * i + 1];
-    const uint16_t h0 = moe::f32_to_bf16_bits(x0), h1 = moe::f32_to_bf16_bits(x1);
-    hi[2 + i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-    lo[2 + i] = moe::pack_bf16x2(x0 - moe::bf16_bits_to_f32(h0), x1 - moe::bf16_bits_to_f32(h1));
-  }
-  return hi;
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  // s_waitcnt with only the vector-memory counter limited to N
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int NA, int NB, int EPI, bool OUT_BF16>
-__global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(Args g) {
-  constexpr int NT = WGM * WGN * 64;
+// Output kinds of the direct-LDS kernel.
+enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_BF16_PAIR = 2 };
+
+// NA A planes (bf16, plane p at A + p * a_plane elements): NA = 2 is an fp32
+// operand kept as hi + lo bf16 parts. OUT_BF16_PAIR writes the result the
+// same way: hi = bf16(v) at C, lo = bf16(v - hi) at C + c_plane.
+template <int BM, int BN, int NS, int WGM, int WGN, int NA, int NB, int EPI, int OUTK>
+__global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args g) {
+  constexpr int BK = 32;
+  constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int NACC = EPI == EPI_GLU ? 2 : 1;
-  constexpr int CPR = BK / 8;                    // 16-byte chunks per LDS row
-  constexpr int A_IT = BM * CPR / NT;            // staging chunks per thread (A)
-  constexpr int B_IT = BN * CPR / NT;            // per B plane
+  constexpr int A_SEG = BM / 16, B_SEG = BN / 16;  // 1 KB segments per plane
+  constexpr int A_IT = A_SEG / NW, B_IT = B_SEG / NW;
+  constexpr int LPT = NA * A_IT + NB * B_IT;      // load instructions per stage
   constexpr int A_PLANE = BM * BK, B_PLANE = BN * BK;
-  constexpr int STAGE = NA * A_PLANE + NB * B_PLANE;  // bf16 elements per buffer
+  constexpr int STAGE = NA * A_PLANE + NB * B_PLANE;  // bf16 elements
   static_assert(FM >= 1 && FN >= 1, "wave tile too small");
-  static_assert(A_IT * NT == BM * CPR && B_IT * NT == BN * CPR, "staging split");
+  static_assert(A_IT * NW == A_SEG && B_IT * NW == B_SEG, "segments per wave");
+  static_assert(LPT * (NS - 1) < 64, "vmcnt range");
   static_assert(EPI != EPI_GLU || (NB == 2 && NA == 1), "GLU takes gate and up planes");
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
-
-  // ---- tile of this block (XCD-aware order, GN N-tiles fastest)
-  const int total_blocks = gridDim.x;
-  const int per_xcd = total_blocks >> 3;  // grid is a multiple of 8
+  const int per_xcd = gridDim.x >> 3;
   const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   const int span = g.max_mt * g.group_n;
   const int ng = logical / span, rem = logical - ng * span;
@@ -128,61 +129,49 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(Args g) {
   const int k_end = min(K, k_begin + g.k_chunk);
   const int KT = (k_end - k_begin) / BK;
 
-  // ---- staging: which (row, chunk) each thread moves
-  const uint16_t* Bp[NB];
+  // per-lane global source pointers (at k = k_begin) for each segment
+  const int lr = lane >> 2;
+  const uint16_t* asrc[NA][A_IT];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) Bp[b] = g.B[b] + ((size_t)e * g.Nrows + n0) * K;
-
-  u32x4_t ra[A_IT][NA == 2 ? 2 : 1];
-  u32x4_t rb[NB][B_IT];
-
-  auto load_tile = [&](int k0) {
+  for (int i = 0; i < A_IT; ++i) {
+    const int r = (wave + i * NW) * 16 + lr;
+    int row = row0 + r;
+    row = row < row_end ? row : row_end - 1;
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
 #pragma unroll
-    for (int it = 0; it < A_IT; ++it) {
-      const int q = tid + it * NT;
-      const int r = q / CPR, c = q % CPR;
-      int row = row0 + r;
-      row = row < row_end ? row : row_end - 1;
-      if (NA == 1) {
-        ra[it][0] = *(const u32x4_t*)((const uint16_t*)g.A + (size_t)row * K + k0 + c * 8);
-      } else {
-        const float* ap = (const float*)g.A + (size_t)row * K + k0 + c * 8;
-        ra[it][0] = *(const u32x4_t*)ap;
-        ra[it][NA == 2 ? 1 : 0] = *(const u32x4_t*)(ap + 4);
-      }
+    for (int p = 0; p < NA; ++p)
+      asrc[p][i] = (const uint16_t*)g.A + (size_t)p * g.a_plane + (size_t)row * K + k_begin + c * 8;
+  }
+  const uint16_t* bsrc[NB][B_IT];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int i = 0; i < B_IT; ++i) {
+      const int r = (wave + i * NW) * 16 + lr;
+      const int c = (lane & 3) ^ ((r >> 2) & 3);
+      bsrc[b][i] = g.B[b] + ((size_t)e * g.Nrows + n0 + r) * K + k_begin + c * 8;
     }
+
+  auto issue = [&](int kt, int stage) {
+    uint16_t* base = smem + stage * STAGE;
+    const int koff = kt * BK;
+#pragma unroll
+    for (int p = 0; p < NA; ++p)
+#pragma unroll
+      for (int i = 0; i < A_IT; ++i)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(asrc[p][i] + koff),
+            (__attribute__((address_space(3))) void*)(base + p * A_PLANE + (wave + i * NW) * 512),
+            16, 0, 0);
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int it = 0; it < B_IT; ++it) {
-        const int q = tid + it * NT;
-        const int r = q / CPR, c = q % CPR;
-        rb[b][it] = *(const u32x4_t*)(Bp[b] + (size_t)r * K + k0 + c * 8);
-      }
-  };
-  auto store_tile = [&](uint16_t* buf) {
-#pragma unroll
-    for (int it = 0; it < A_IT; ++it) {
-      const int q = tid + it * NT;
-      const int r = q / CPR, c = q % CPR;
-      if (NA == 1) {
-        *(u32x4_t*)(buf + lds_off<BK>(r, c)) = ra[it][0];
-      } else {
-        u32x4_t lo;
-        const u32x4_t hi = split_hi_lo(__builtin_bit_cast(f32x4_t, ra[it][0]),
-                                       __builtin_bit_cast(f32x4_t, ra[it][NA == 2 ? 1 : 0]), lo);
-        *(u32x4_t*)(buf + lds_off<BK>(r, c)) = hi;
-        *(u32x4_t*)(buf + A_PLANE + lds_off<BK>(r, c)) = lo;
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int it = 0; it < B_IT; ++it) {
-        const int q = tid + it * NT;
-        const int r = q / CPR, c = q % CPR;
-        *(u32x4_t*)(buf + NA * A_PLANE + b * B_PLANE + lds_off<BK>(r, c)) = rb[b][it];
-      }
+      for (int i = 0; i < B_IT; ++i)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(bsrc[b][i] + koff),
+            (__attribute__((address_space(3))) void*)(base + NA * A_PLANE + b * B_PLANE +
+                                                       (wave + i * NW) * 512),
+            16, 0, 0);
   };
 
   f32x16_t acc[NACC][FM][FN];
@@ -195,47 +184,77 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(Args g) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[a][i][j][r] = 0.f;
 
+  // MFMA operand fragments of one 16-wide K half of a stage
+  struct Frags {
+    bf16x8_t a[NA][FM];
+    bf16x8_t b[NB][FN];
+  };
+  auto read_frags = [&](Frags& f, int stage, int kk) {
+    const uint16_t* cur = smem + stage * STAGE;
+    const int c = kk * 2 + (lane >> 5);
+#pragma unroll
+    for (int p = 0; p < NA; ++p)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        f.a[p][i] = *(const bf16x8_t*)(cur + p * A_PLANE +
+                                       dlds_off(wm * WM + i * 32 + (lane & 31), c));
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        f.b[b][j] = *(const bf16x8_t*)(cur + NA * A_PLANE + b * B_PLANE +
+                                       dlds_off(wn * WN + j * 32 + (lane & 31), c));
+  };
+  auto mfma = [&](const Frags& f) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int p = 0; p < NA; ++p)
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            f32x16_t& d = acc[EPI == EPI_GLU ? b : 0][i][j];
+            d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[p][i], f.b[b][j], d, 0, 0, 0);
+          }
+  };
+
+  // Schedule per K tile kt (stage kt % NS), in two 16-wide halves:
+  //   read half 1 of tile kt; MFMAs on half 0;
+  //   wait for this wave's LDS reads and for tile kt+1's loads; barrier
+  //   (now no wave reads stage kt % NS any more, and tile kt+1 is visible);
+  //   issue the loads of tile kt+NS into stage kt % NS;
+  //   read half 0 of tile kt+1; MFMAs on half 1 of tile kt.
+  // LDS reads always run under the previous half's MFMAs, and the global
+  // loads run NS-1 to NS tiles ahead. sched_barrier keeps the compiler from
+  // moving MFMAs across the waits.
+#pragma unroll
+  for (int j = 0; j < NS; ++j)
+    if (j < KT) issue(j, j);
+  Frags f0, f1;
   if (KT > 0) {
-    load_tile(k_begin);
-    store_tile(smem);
+    if (KT > NS - 1) wait_vmcnt<(NS - 1) * LPT>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    read_frags(f0, 0, 0);
   }
-  __syncthreads();
   for (int kt = 0; kt < KT; ++kt) {
-    uint16_t* cur = smem + (kt & 1) * STAGE;
-    if (kt + 1 < KT) load_tile(k_begin + (kt + 1) * BK);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int c = kk * 2 + (lane >> 5);
-      bf16x8_t af[NA][FM];
-#pragma unroll
-      for (int p = 0; p < NA; ++p)
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-          af[p][i] = *(const bf16x8_t*)(cur + p * A_PLANE +
-                                        lds_off<BK>(wm * WM + i * 32 + (lane & 31), c));
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const bf16x8_t bfr = *(const bf16x8_t*)(cur + NA * A_PLANE + b * B_PLANE +
-                                                  lds_off<BK>(wn * WN + j * 32 + (lane & 31), c));
-#pragma unroll
-          for (int p = 0; p < NA; ++p)
-#pragma unroll
-            for (int i = 0; i < FM; ++i) {
-              f32x16_t& d = acc[EPI == EPI_GLU ? b : 0][i][j];
-              d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[p][i], bfr, d, 0, 0, 0);
-            }
-        }
-      }
-    }
-    if (kt + 1 < KT) store_tile(smem + ((kt + 1) & 1) * STAGE);
-    __syncthreads();
+    read_frags(f1, kt % NS, 1);
+    mfma(f0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+    if (kt + NS - 1 < KT) wait_vmcnt<(NS - 2) * LPT>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + NS < KT) issue(kt + NS, kt % NS);
+    if (kt + 1 < KT) read_frags(f0, (kt + 1) % NS, 0);
+    mfma(f1);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- epilogue. 32x32 accumulator: register r of lane l is
-  // row (r & 3) + 4 (l >> 5) + 8 (r >> 2), column l & 31.
-  char* Cb = (char*)g.C + (size_t)blockIdx.y * g.c_split * (OUT_BF16 ? 2 : 4);
+  constexpr int OB = OUTK == OUT_F32 ? 4 : 2;
+  char* Cb = (char*)g.C + (size_t)blockIdx.y * g.c_split * OB;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -256,22 +275,24 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(Args g) {
         else
           v = acc[0][i][j][r] + bv;
         const size_t o = (size_t)row * g.ldc + col;
-        if (OUT_BF16)
-          ((uint16_t*)Cb)[o] = moe::f32_to_bf16_bits(v);
-        else
+        if (OUTK == OUT_F32) {
           ((float*)Cb)[o] = v;
+        } else {
+          const uint16_t hi = moe::f32_to_bf16_bits(v);
+          ((uint16_t*)Cb)[o] = hi;
+          if (OUTK == OUT_BF16_PAIR)
+            ((uint16_t*)Cb)[g.c_plane + o] = moe::f32_to_bf16_bits(v - moe::bf16_bits_to_f32(hi));
+        }
       }
     }
   }
 }
 
-// Launch helper: grid = 8-aligned count of (max_mt x n_tiles_n) tiles, times
-// the K splits in grid.y. Dynamic LDS = 2 stages.
-template <int BM, int BN, int BK, int WGM, int WGN, int NA, int NB, int EPI, bool OUT_BF16>
-inline hipError_t launch(Args g, int k_splits, hipStream_t st) {
-  constexpr int STAGE = NA * BM * BK + NB * BN * BK;
-  constexpr size_t lds = 2 * STAGE * sizeof(uint16_t);
-  auto kern = grouped_gemm_kernel<BM, BN, BK, WGM, WGN, NA, NB, EPI, OUT_BF16>;
+template <int BM, int BN, int NS, int WGM, int WGN, int NA, int NB, int EPI, int OUTK>
+inline hipError_t launch_dlds(Args g, int k_splits, hipStream_t st) {
+  constexpr size_t lds = (size_t)NS * (NA * BM + NB * BN) * 32 * sizeof(uint16_t);
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  auto kern = grouped_gemm_dlds_kernel<BM, BN, NS, WGM, WGN, NA, NB, EPI, OUTK>;
   static bool configured = false;
   if (!configured) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -286,6 +307,24 @@ inline hipError_t launch(Args g, int k_splits, hipStream_t st) {
   dim3 grid(grid_x, k_splits);
   kern<<<grid, WGM * WGN * 64, lds, st>>>(g);
   return hipGetLastError();
+}
+
+// LDS stages for a tile: as many as fit in 144 KB (at most 8), bounded so
+// that (stages - 1) x loads-per-stage fits the 6-bit vmcnt (4 waves).
+template <int BM, int BN, int NA, int NB>
+constexpr int pick_stages() {
+  constexpr int stage_bytes = (NA * BM + NB * BN) * 32 * 2;
+  constexpr int lpt = NA * (BM / 64) + NB * (BN / 64);
+  int ns = 147456 / stage_bytes;
+  if (ns > 8) ns = 8;
+  while (ns > 2 && (ns - 1) * lpt >= 64) --ns;
+  return ns;
+}
+
+template <int BM, int BN, int NA, int NB, int EPI, int OUTK>
+inline hipError_t run_gemm(const Args& g, int k_splits, hipStream_t st) {
+  return launch_dlds<BM, BN, pick_stages<BM, BN, NA, NB>(), 2, 2, NA, NB, EPI, OUTK>(g, k_splits,
+                                                                                       st);
 }
 
 }  // namespace moe_gemm

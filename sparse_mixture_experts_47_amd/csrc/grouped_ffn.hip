@@ -179,6 +179,11 @@ __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
 // (blockIdx.y). Rows are processed in groups of 64 (four 16-row MFMA
 // tiles); a lane loads 16 consecutive K bytes of one weight row and feeds
 // them to two 16x16x32 MFMAs together with the matching 8+8 activations.
+// The K loop is unrolled by kU steps of 64 and all weight loads of a group
+// are issued before any is used, so each lane keeps kU*NB 16-byte loads in
+// flight (the kernel is bound by streaming the weights once).
+constexpr int kU = 4;
+
 template <int MODE, bool OUT_BF16>
 __global__ __launch_bounds__(256) void ffn_fp8_kernel(Fp8Args g) {
   constexpr int NB = MODE == MODE_GLU ? 2 : 1;
@@ -190,8 +195,8 @@ __global__ __launch_bounds__(256) void ffn_fp8_kernel(Fp8Args g) {
   const int grp = lane >> 4;
   const int K = g.K;
   const uint8_t* Bp[2];
-  Bp[0] = g.B0 + ((size_t)e * g.Nout + n) * K;
-  Bp[1] = NB == 2 ? g.B1 + ((size_t)e * g.Nout + n) * K : nullptr;
+  Bp[0] = g.B0 + ((size_t)e * g.Nout + n) * K + grp * 16;
+  Bp[1] = NB == 2 ? g.B1 + ((size_t)e * g.Nout + n) * K + grp * 16 : nullptr;
 
   for (int rb = r_begin; rb < r_end; rb += 64) {
     const int nchunk = min(4, (r_end - rb + 15) >> 4);
@@ -201,15 +206,14 @@ __global__ __launch_bounds__(256) void ffn_fp8_kernel(Fp8Args g) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) acc[b][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    for (int k0 = 0; k0 < K; k0 += 64) {
-      const int kl = k0 + grp * 16;
+    auto step = [&](int k0, const u32x4_t (&w)[NB]) {
       bf16x8_t wlo[NB], whi[NB];
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const u32x4_t w = *(const u32x4_t*)(Bp[b] + kl);
-        wlo[b] = e4m3x8_to_bf16(w[0], w[1]);
-        whi[b] = e4m3x8_to_bf16(w[2], w[3]);
+        wlo[b] = e4m3x8_to_bf16(w[b][0], w[b][1]);
+        whi[b] = e4m3x8_to_bf16(w[b][2], w[b][3]);
       }
+      const int kl = k0 + grp * 16;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         if (m >= nchunk) break;
@@ -228,6 +232,23 @@ __global__ __launch_bounds__(256) void ffn_fp8_kernel(Fp8Args g) {
           acc[b][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, whi[b], acc[b][m], 0, 0, 0);
         }
       }
+    };
+
+    int k0 = 0;
+    for (; k0 + kU * 64 <= K; k0 += kU * 64) {
+      u32x4_t w[kU][NB];
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) w[u][b] = *(const u32x4_t*)(Bp[b] + k0 + u * 64);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) step(k0 + u * 64, w[u]);
+    }
+    for (; k0 < K; k0 += 64) {
+      u32x4_t w[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) w[b] = *(const u32x4_t*)(Bp[b] + k0);
+      step(k0, w);
     }
     // 16x16 accumulator layout: register r of lane l holds row 4*(l>>4)+r,
     // column l & 15.
@@ -257,19 +278,9 @@ __global__ __launch_bounds__(256) void ffn_fp8_kernel(Fp8Args g) {
   }
 }
 
-// bf16 MFMA tile configurations (BM, BN, BK, waves along M, waves along N).
-// GEMM 1 (gate/up): 256 rows x 128 output columns of both W1 and W3.
-// GEMM 2 (down): 256 x 128.
-#ifndef MOE_G1_WGN
-#define MOE_G1_WGN 2
-#endif
-#ifndef MOE_G2_BN
-#define MOE_G2_BN 128
-#endif
 #ifndef MOE_GROUP_N
-#define MOE_GROUP_N 8
+#define MOE_GROUP_N 4
 #endif
-constexpr int kBM = 256, kBK = 64;
 
 moe_status gemm_status(hipError_t e, const char* what) {
   if (e != hipSuccess) {
@@ -277,6 +288,49 @@ moe_status gemm_status(hipError_t e, const char* what) {
     return MOE_EHIP;
   }
   return MOE_OK;
+}
+
+// GEMM 1 then GEMM 2 of the bf16 path for M tiles of BM rows. 128-column N
+// tiles (GEMM 1: 128 columns of both W1 and W3), 64 when the width is not
+// a multiple of 128.
+template <int BM>
+hipError_t launch_ffn(bool glu, bool pair, bool ybf, const moe_gemm::Args& g1,
+                      const moe_gemm::Args& g2, hipStream_t st) {
+  using namespace moe_gemm;
+  const bool n1 = g1.Nrows % 128 == 0, n2 = g2.Nrows % 128 == 0;
+  hipError_t e;
+  if (glu) {
+    if (n1)
+      e = pair ? run_gemm<BM, 128, 1, 2, EPI_GLU, OUT_BF16_PAIR>(g1, 1, st)
+               : run_gemm<BM, 128, 1, 2, EPI_GLU, OUT_BF16>(g1, 1, st);
+    else
+      e = pair ? run_gemm<BM, 64, 1, 2, EPI_GLU, OUT_BF16_PAIR>(g1, 1, st)
+               : run_gemm<BM, 64, 1, 2, EPI_GLU, OUT_BF16>(g1, 1, st);
+  } else {
+    if (n1)
+      e = pair ? run_gemm<BM, 128, 1, 1, EPI_ACT, OUT_BF16_PAIR>(g1, 1, st)
+               : run_gemm<BM, 128, 1, 1, EPI_ACT, OUT_BF16>(g1, 1, st);
+    else
+      e = pair ? run_gemm<BM, 64, 1, 1, EPI_ACT, OUT_BF16_PAIR>(g1, 1, st)
+               : run_gemm<BM, 64, 1, 1, EPI_ACT, OUT_BF16>(g1, 1, st);
+  }
+  if (e != hipSuccess) return e;
+  if (pair) {
+    if (n2)
+      e = ybf ? run_gemm<BM, 128, 2, 1, EPI_OUT, OUT_BF16>(g2, 1, st)
+              : run_gemm<BM, 128, 2, 1, EPI_OUT, OUT_F32>(g2, 1, st);
+    else
+      e = ybf ? run_gemm<BM, 64, 2, 1, EPI_OUT, OUT_BF16>(g2, 1, st)
+              : run_gemm<BM, 64, 2, 1, EPI_OUT, OUT_F32>(g2, 1, st);
+  } else {
+    if (n2)
+      e = ybf ? run_gemm<BM, 128, 1, 1, EPI_OUT, OUT_BF16>(g2, 1, st)
+              : run_gemm<BM, 128, 1, 1, EPI_OUT, OUT_F32>(g2, 1, st);
+    else
+      e = ybf ? run_gemm<BM, 64, 1, 1, EPI_OUT, OUT_BF16>(g2, 1, st)
+              : run_gemm<BM, 64, 1, 1, EPI_OUT, OUT_F32>(g2, 1, st);
+  }
+  return e;
 }
 
 moe_gemm::Args base_args(const void* A, const void* B0, const void* B1, const float* bias,
@@ -347,7 +401,9 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
     return launch_status("grouped FFN fp8 GEMM 2");
   }
 
-  const int bm = act_dt == MOE_F32 ? 64 : kBM;
+  // 256-row M tiles when experts average at least 512 rows, else 128 rows
+  // (less padding in partly filled tiles)
+  const int bm = act_dt == MOE_F32 ? 64 : (max_rows / E >= 512 ? 256 : 128);
   tile_table_kernel<<<1, 256, 0, st>>>(offsets, E, bm, tile_start);
   s = launch_status("tile table");
   if (s != MOE_OK) return s;
@@ -368,40 +424,16 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
   }
 
   using namespace moe_gemm;
-  const bool h32 = w->h_fp32 != 0;
+  const bool pair = w->h_fp32 != 0;
   Args g1 = base_args(x_rows, w->w1, w->w3, w->b1, h, d, F, E, max_mt, (int)w->act, offsets,
                       tile_start);
-  hipError_t err;
-  if (F % 128 != 0) {  // d_ff a multiple of 64 only: 64-column tiles
-    if (glu)
-      err = h32 ? launch<kBM, 64, kBK, 2, 2, 1, 2, EPI_GLU, false>(g1, 1, st)
-                : launch<kBM, 64, kBK, 2, 2, 1, 2, EPI_GLU, true>(g1, 1, st);
-    else
-      err = h32 ? launch<kBM, 64, kBK, 2, 2, 1, 1, EPI_ACT, false>(g1, 1, st)
-                : launch<kBM, 64, kBK, 2, 2, 1, 1, EPI_ACT, true>(g1, 1, st);
-  } else if (glu) {
-    err = h32 ? launch<kBM, 128, kBK, 2, MOE_G1_WGN, 1, 2, EPI_GLU, false>(g1, 1, st)
-              : launch<kBM, 128, kBK, 2, MOE_G1_WGN, 1, 2, EPI_GLU, true>(g1, 1, st);
-  } else {
-    err = h32 ? launch<kBM, 128, kBK, 2, 2, 1, 1, EPI_ACT, false>(g1, 1, st)
-              : launch<kBM, 128, kBK, 2, 2, 1, 1, EPI_ACT, true>(g1, 1, st);
-  }
-  s = gemm_status(err, "grouped FFN GEMM 1");
-  if (s != MOE_OK) return s;
   Args g2 = base_args(h, w->w2, nullptr, w->b2, y_rows, F, d, E, max_mt, (int)w->act, offsets,
                       tile_start);
-  const bool ybf = y_dt == MOE_BF16;
-  if (h32) {  // two A planes: 64-column tiles keep LDS at 144 KB
-    err = ybf ? launch<kBM, 64, kBK, 2, 2, 2, 1, EPI_OUT, true>(g2, 1, st)
-              : launch<kBM, 64, kBK, 2, 2, 2, 1, EPI_OUT, false>(g2, 1, st);
-  } else if (d % MOE_G2_BN != 0) {
-    err = ybf ? launch<kBM, 64, kBK, 2, 2, 1, 1, EPI_OUT, true>(g2, 1, st)
-              : launch<kBM, 64, kBK, 2, 2, 1, 1, EPI_OUT, false>(g2, 1, st);
-  } else {
-    err = ybf ? launch<kBM, MOE_G2_BN, kBK, 2, 2, 1, 1, EPI_OUT, true>(g2, 1, st)
-              : launch<kBM, MOE_G2_BN, kBK, 2, 2, 1, 1, EPI_OUT, false>(g2, 1, st);
-  }
-  return gemm_status(err, "grouped FFN GEMM 2");
+  g1.c_plane = (long long)max_rows * F;  // lo plane of the bf16 pair h
+  g2.a_plane = (long long)max_rows * F;
+  const hipError_t err = bm == 256 ? launch_ffn<256>(glu, pair, y_dt == MOE_BF16, g1, g2, st)
+                                   : launch_ffn<128>(glu, pair, y_dt == MOE_BF16, g1, g2, st);
+  return gemm_status(err, "grouped FFN GEMM");
 }
 
 }  // namespace moe_host

@@ -278,14 +278,23 @@ __global__ void router_group_table_kernel(int N, int bm, int32_t* offsets, int32
   }
 }
 
-// score_sums[e] = sum over blocks b (in order) of partials[b][e].
+// score_sums[e] = sum over blocks b of partials[b][e]: one workgroup per
+// column; thread i adds rows i, i + 256, ... in order, then a fixed halving
+// tree over the 256 threads. The order never changes, so the sum is
+// reproducible bit for bit.
 __global__ __launch_bounds__(kThreads) void router_sum_partials_kernel(
     const double* __restrict__ partials, int nblk, int width, double* __restrict__ out) {
-  for (int e = threadIdx.x; e < width; e += kThreads) {
-    double v = 0.0;
-    for (int b = 0; b < nblk; ++b) v += partials[(size_t)b * width + e];
-    out[e] = v;
+  __shared__ double buf[kThreads];
+  const int e = blockIdx.x;
+  double v = 0.0;
+  for (int b = threadIdx.x; b < nblk; b += kThreads) v += partials[(size_t)b * width + e];
+  buf[threadIdx.x] = v;
+  __syncthreads();
+  for (int h = kThreads / 2; h >= 1; h >>= 1) {
+    if ((int)threadIdx.x < h) buf[threadIdx.x] += buf[threadIdx.x + h];
+    __syncthreads();
   }
+  if (threadIdx.x == 0) out[e] = buf[0];
 }
 
 }  // namespace
@@ -309,12 +318,15 @@ RouterPlan plan_router(int N, int d, int E, int with_noise, bool x_bf16) {
   p.nsplit = 1;
   p.k_chunk = d;
   if (p.mfma) {
-    p.bn = p.E2 <= 32 ? 32 : 64;
+    p.bn = 64;
     p.E2pad = (p.E2 + p.bn - 1) / p.bn * p.bn;
     const int tiles = ((N + kRouterBM - 1) / kRouterBM) * (p.E2pad / p.bn);
     const int KT = d / 64;
+    // enough K splits for ~512 workgroups, at most 8 (the select kernel sums
+    // the split partials of every logit in order)
     int want = (512 + tiles - 1) / tiles;
-    want = want < 1 ? 1 : (want > KT ? KT : want);
+    want = want < 1 ? 1 : (want > 8 ? 8 : want);
+    want = want > KT ? KT : want;
     const int steps = (KT + want - 1) / want;
     p.k_chunk = steps * 64;
     p.nsplit = (KT + steps - 1) / steps;
@@ -387,10 +399,7 @@ moe_status router_launch(const moe_router_params* p, const void* x, moe_dtype x_
       g.group_n = 8;
       g.offsets = table;
       g.tile_start = table + 2;
-      hipError_t err =
-          pl.bn == 32
-              ? launch<kRouterBM, 32, 64, 4, 1, 1, 3, EPI_SUM, false>(g, pl.nsplit, st)
-              : launch<kRouterBM, 64, 64, 2, 2, 1, 3, EPI_SUM, false>(g, pl.nsplit, st);
+      hipError_t err = run_gemm<kRouterBM, 64, 1, 3, EPI_SUM, OUT_F32>(g, pl.nsplit, st);
       if (err != hipSuccess) {
         set_error("router GEMM: launch failed: %s", hipGetErrorString(err));
         return MOE_EHIP;
@@ -446,7 +455,7 @@ moe_status router_launch(const moe_router_params* p, const void* x, moe_dtype x_
   moe_status s = launch_status("router_select");
   if (s != MOE_OK) return s;
   if (score_sums) {
-    router_sum_partials_kernel<<<1, kThreads, 0, st>>>(partials, nblk, E + 1, score_sums);
+    router_sum_partials_kernel<<<E + 1, kThreads, 0, st>>>(partials, nblk, E + 1, score_sums);
     s = launch_status("router_sum_partials");
   }
   return s;
