@@ -282,6 +282,12 @@ class MoELayer:
                 weights.get("shared_s2"), s.h_fp32)
             self.sh_offsets = torch.tensor([0, N], **i32)
             self.y_shared = torch.empty((N, s.d_model), dtype=ydt, device=dev)
+            # the always-on expert depends only on x: it runs on a side stream
+            # (default priority) next to routing, dispatch and the routed FFN
+            self.side = torch.cuda.Stream(device=dev)
+            self.ev_x = torch.cuda.Event()
+            self.ev_shared = torch.cuda.Event()
+            self._shared_pending = False
         xdt = _dt(torch.empty(0, dtype=x_dtype))
         noise = int(weights.get("w_noise") is not None)
         self.ws_router = workspace(lib.moe_router_workspace_bytes(N, s.d_model, E, noise), dev)
@@ -310,15 +316,29 @@ class MoELayer:
                      perm_token=self.perm_token, x_perm=self.x_perm, ws=self.ws_dispatch,
                      stream=stream)
 
+    def start_shared(self, x, stream=None):
+        """Launch the shared expert's FFN on the side stream once x is ready
+        on `stream`; combine() waits for it."""
+        if self.shared is None or self._shared_pending:
+            return
+        main = stream or torch.cuda.current_stream()
+        self.ev_x.record(main)
+        self.side.wait_event(self.ev_x)
+        moe_grouped_ffn(self.shared, x, self.sh_offsets, self.y_shared,
+                        max_rows=self.spec.n_tokens, ws=self.ws_shared, stream=self.side)
+        self.ev_shared.record(self.side)
+        self._shared_pending = True
+
     def experts(self, x, stream=None):
         moe_grouped_ffn(self.ffn, self.x_perm, self.offsets, self.y_rows,
                         max_rows=self.spec.n_tokens * self.spec.top_k, ws=self.ws_ffn,
                         stream=stream)
-        if self.shared is not None:
-            moe_grouped_ffn(self.shared, x, self.sh_offsets, self.y_shared,
-                            max_rows=self.spec.n_tokens, ws=self.ws_shared, stream=stream)
+        self.start_shared(x, stream)
 
     def combine(self, stream=None):
+        if self.shared is not None:
+            (stream or torch.cuda.current_stream()).wait_event(self.ev_shared)
+            self._shared_pending = False
         moe_combine(self.y_rows, self.row_of, self.gates, self.y,
                     y_shared=self.y_shared if self.shared is not None else None, stream=stream)
 
@@ -330,6 +350,7 @@ class MoELayer:
                           bias_rate=s.bias_rate, stream=stream)
 
     def forward(self, x, logits_in=None, stats=True, update_bias=False, stream=None):
+        self.start_shared(x, stream)
         self.route(x, logits_in, stream)
         self.dispatch(x, stream)
         self.experts(x, stream)

@@ -314,17 +314,17 @@ inline hipError_t launch_dlds(Args g, int k_splits, hipStream_t st) {
 template <int BM, int BN, int NA, int NB>
 constexpr int pick_stages() {
   constexpr int stage_bytes = (NA * BM + NB * BN) * 32 * 2;
-  constexpr int lpt = NA * (BM / 64) + NB * (BN / 64);
+  constexpr int lpt = NA * (BM / 64) + NB * (BN / 64);  // with 4 waves (fewer with 8)
   int ns = 147456 / stage_bytes;
   if (ns > 8) ns = 8;
   while (ns > 2 && (ns - 1) * lpt >= 64) --ns;
   return ns;
 }
 
-template <int BM, int BN, int NA, int NB, int EPI, int OUTK>
+template <int BM, int BN, int NA, int NB, int EPI, int OUTK, int WGN = 2>
 inline hipError_t run_gemm(const Args& g, int k_splits, hipStream_t st) {
-  return launch_dlds<BM, BN, pick_stages<BM, BN, NA, NB>(), 2, 2, NA, NB, EPI, OUTK>(g, k_splits,
-                                                                                       st);
+  return launch_dlds<BM, BN, pick_stages<BM, BN, NA, NB>(), 2, WGN, NA, NB, EPI, OUTK>(
+      g, k_splits, st);
 }
 
 }  // namespace moe_gemm

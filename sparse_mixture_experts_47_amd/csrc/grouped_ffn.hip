@@ -281,6 +281,14 @@ __global__ __launch_bounds__(256) void ffn_fp8_kernel(Fp8Args g) {
 #ifndef MOE_GROUP_N
 #define MOE_GROUP_N 4
 #endif
+// GEMM 1 (SwiGLU, 256-row tiles) runs 8 waves (2 per SIMD); GEMM 2 uses
+// 256x256 tiles when the width allows (16 MFMAs per wave per half K step)
+#ifndef MOE_G1_WGN
+#define MOE_G1_WGN 4
+#endif
+#ifndef MOE_G2_WIDE
+#define MOE_G2_WIDE 1
+#endif
 
 moe_status gemm_status(hipError_t e, const char* what) {
   if (e != hipSuccess) {
@@ -302,7 +310,7 @@ hipError_t launch_ffn(bool glu, bool pair, bool ybf, const moe_gemm::Args& g1,
   if (glu) {
     if (n1)
       e = pair ? run_gemm<BM, 128, 1, 2, EPI_GLU, OUT_BF16_PAIR>(g1, 1, st)
-               : run_gemm<BM, 128, 1, 2, EPI_GLU, OUT_BF16>(g1, 1, st);
+               : run_gemm<BM, 128, 1, 2, EPI_GLU, OUT_BF16, MOE_G1_WGN>(g1, 1, st);
     else
       e = pair ? run_gemm<BM, 64, 1, 2, EPI_GLU, OUT_BF16_PAIR>(g1, 1, st)
                : run_gemm<BM, 64, 1, 2, EPI_GLU, OUT_BF16>(g1, 1, st);
@@ -323,7 +331,10 @@ hipError_t launch_ffn(bool glu, bool pair, bool ybf, const moe_gemm::Args& g1,
       e = ybf ? run_gemm<BM, 64, 2, 1, EPI_OUT, OUT_BF16>(g2, 1, st)
               : run_gemm<BM, 64, 2, 1, EPI_OUT, OUT_F32>(g2, 1, st);
   } else {
-    if (n2)
+    if (MOE_G2_WIDE && BM == 256 && g2.Nrows % 256 == 0)
+      e = ybf ? run_gemm<BM, 256, 1, 1, EPI_OUT, OUT_BF16>(g2, 1, st)
+              : run_gemm<BM, 256, 1, 1, EPI_OUT, OUT_F32>(g2, 1, st);
+    else if (n2)
       e = ybf ? run_gemm<BM, 128, 1, 1, EPI_OUT, OUT_BF16>(g2, 1, st)
               : run_gemm<BM, 128, 1, 1, EPI_OUT, OUT_F32>(g2, 1, st);
     else
