@@ -173,8 +173,8 @@ int32_t moe_capacity(int32_t n_tokens, int32_t n_experts, double capacity_factor
  * The intermediate h is kept in the workspace in bf16, or fp32 when
  * act_dt is MOE_F32 or h_fp32 is set. fp8 weights carry one fp32 scale per output channel (row of
  * W1/W3/W2), applied after the K sum; activations stay bf16 (W8A16).
- * Shared always-on expert: the same call with n_experts = 1 and
- * offsets = {0, N} on x.
+ * Shared always-on expert: the same call with n_experts = 1,
+ * offsets = {0, N}, row_index NULL, on x.
  * Supported: (act_dt, w_dt, y_dt) = (F32, F32, F32), (BF16, BF16, BF16|F32),
  * (BF16, FP8_E4M3, BF16|F32); fp8 weights need SwiGLU or GELU and no bias. */
 typedef struct {
@@ -197,14 +197,21 @@ typedef struct {
   int32_t h_fp32;
 } moe_ffn_weights;
 
-/*  x_rows   [max_rows][d_model] (act_dt), packed rows
- *  offsets  [E+1] device int32 row offsets (from moe_dispatch); rows past
- *           offsets[E] are not read or written
- *  max_rows upper bound on offsets[E] used to size the launch (N*top_k)
- *  y_rows   [max_rows][d_model] out (y_dt) */
+/*  x_rows    activations (act_dt), row-major with d_model columns: the
+ *            packed rows [max_rows][d_model] when row_index is NULL, or any
+ *            row set (e.g. the token rows x [N][d_model]) when row_index is
+ *            given
+ *  row_index [max_rows] device int32 or NULL: packed row r reads
+ *            x_rows[row_index[r]] -- pass perm_token from moe_dispatch to
+ *            fuse the token gather into GEMM 1's operand loads (the fused
+ *            dispatch + GEMM of mkbk-pku.cn "MOE的优化", Fused MoE kernel)
+ *  offsets   [E+1] device int32 row offsets (from moe_dispatch); rows past
+ *            offsets[E] are not read or written
+ *  max_rows  upper bound on offsets[E] used to size the launch (N*top_k)
+ *  y_rows    [max_rows][d_model] out (y_dt), in packed row order */
 moe_status moe_grouped_ffn(const moe_ffn_weights* w, const void* x_rows, moe_dtype act_dt,
-                           const int32_t* offsets, int32_t max_rows, void* y_rows,
-                           moe_dtype y_dt, void* workspace, size_t ws_bytes,
+                           const int32_t* row_index, const int32_t* offsets, int32_t max_rows,
+                           void* y_rows, moe_dtype y_dt, void* workspace, size_t ws_bytes,
                            void* hip_stream);
 size_t moe_grouped_ffn_workspace_bytes(const moe_ffn_weights* w, moe_dtype act_dt,
                                        int32_t max_rows);

@@ -71,7 +71,8 @@ def _load():
     L.moe_dispatch_workspace_bytes.restype = sz
     L.moe_capacity.argtypes = [i32, i32, ctypes.c_double]
     L.moe_capacity.restype = i32
-    L.moe_grouped_ffn.argtypes = [ctypes.POINTER(FFNWeights), P, i32, P, i32, P, i32, P, sz, P]
+    L.moe_grouped_ffn.argtypes = [ctypes.POINTER(FFNWeights), P, i32, P, P, i32, P, i32, P, sz,
+                                  P]
     L.moe_grouped_ffn.restype = i32
     L.moe_grouped_ffn_workspace_bytes.argtypes = [ctypes.POINTER(FFNWeights), i32, i32]
     L.moe_grouped_ffn_workspace_bytes.restype = sz
@@ -181,16 +182,18 @@ def ffn_weights(w1, w2, w3=None, act=SWIGLU, b1=None, b2=None, s1=None, s3=None,
         (w1, w2, w3, b1, b2, s1, s3, s2)
 
 
-def moe_grouped_ffn(weights: FFNWeights, x_rows, offsets, y_rows, *, max_rows=None, ws=None,
-                    stream=None):
-    _dev_check(x_rows, offsets, y_rows)
-    max_rows = max_rows or x_rows.shape[0]
+def moe_grouped_ffn(weights: FFNWeights, x_rows, offsets, y_rows, *, row_index=None,
+                    max_rows=None, ws=None, stream=None):
+    """Grouped expert FFN. row_index (e.g. perm_token) makes packed row r read
+    x_rows[row_index[r]], so x_rows can be the unpermuted token rows."""
+    _dev_check(x_rows, offsets, y_rows, row_index)
+    max_rows = max_rows or (row_index.shape[0] if row_index is not None else x_rows.shape[0])
     if ws is None:
         ws = workspace(lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(weights), _dt(x_rows),
                                                            max_rows), x_rows.device)
-    _check(lib.moe_grouped_ffn(ctypes.byref(weights), _ptr(x_rows), _dt(x_rows), _ptr(offsets),
-                               max_rows, _ptr(y_rows), _dt(y_rows), _ptr(ws), ws.numel(),
-                               _stream(stream)))
+    _check(lib.moe_grouped_ffn(ctypes.byref(weights), _ptr(x_rows), _dt(x_rows),
+                               _ptr(row_index), _ptr(offsets), max_rows, _ptr(y_rows),
+                               _dt(y_rows), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def moe_combine(y_rows, row_of, gates, y, *, y_shared=None, stream=None):
@@ -239,7 +242,7 @@ class MoELayer:
     """
 
     def __init__(self, spec: LayerSpec, weights: dict, x_dtype=torch.bfloat16, device="cuda",
-                 out_dtype=None):
+                 out_dtype=None, fused_gather=True):
         self.spec = s = spec
         self.w = weights
         self.dev = torch.device(device)
@@ -260,7 +263,11 @@ class MoELayer:
         self.row_of = torch.empty((N, k), **i32)
         self.expert_of = torch.empty((N, k), **i32)
         self.perm_token = torch.empty(N * k, **i32)
-        self.x_perm = torch.empty((N * k, s.d_model), dtype=x_dtype, device=dev)
+        # fused_gather: GEMM 1 reads token rows through perm_token, so no
+        # packed copy of x is made; otherwise dispatch gathers x_perm first
+        self.fused_gather = fused_gather
+        self.x_perm = (None if fused_gather else
+                       torch.empty((N * k, s.d_model), dtype=x_dtype, device=dev))
         # Expert outputs and the layer output stay fp32: the only bf16
         # rounding on the path is the intermediate h inside the grouped FFN.
         ydt = torch.float32
@@ -316,6 +323,9 @@ class MoELayer:
                      perm_token=self.perm_token, x_perm=self.x_perm, ws=self.ws_dispatch,
                      stream=stream)
 
+    def _packed_rows(self, x):
+        return (x, self.perm_token) if self.fused_gather else (self.x_perm, None)
+
     def start_shared(self, x, stream=None):
         """Launch the shared expert's FFN on the side stream once x is ready
         on `stream`; combine() waits for it."""
@@ -330,7 +340,8 @@ class MoELayer:
         self._shared_pending = True
 
     def experts(self, x, stream=None):
-        moe_grouped_ffn(self.ffn, self.x_perm, self.offsets, self.y_rows,
+        rows, index = self._packed_rows(x)
+        moe_grouped_ffn(self.ffn, rows, self.offsets, self.y_rows, row_index=index,
                         max_rows=self.spec.n_tokens * self.spec.top_k, ws=self.ws_ffn,
                         stream=stream)
         self.start_shared(x, stream)

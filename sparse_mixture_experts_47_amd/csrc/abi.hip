@@ -22,8 +22,8 @@ moe_status dispatch_launch(int N, int E, int k, int C, moe_overflow policy, int 
                            void* workspace, hipStream_t st);
 size_t grouped_ffn_workspace_bytes(const moe_ffn_weights* w, moe_dtype act_dt, int max_rows);
 moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_dtype act_dt,
-                              const int32_t* offsets, int max_rows, void* y_rows,
-                              moe_dtype y_dt, void* workspace, hipStream_t st);
+                              const int32_t* row_index, const int32_t* offsets, int max_rows,
+                              void* y_rows, moe_dtype y_dt, void* workspace, hipStream_t st);
 moe_status combine_launch(int N, int d, int k, const void* y_rows, moe_dtype y_dt,
                           const int32_t* row_of, const float* gates, const void* y_shared,
                           moe_dtype sh_dt, void* y, moe_dtype out_dt, hipStream_t st);
@@ -190,8 +190,9 @@ moe_status moe_dispatch(int32_t n_tokens, int32_t n_experts, int32_t top_k, int3
 }
 
 moe_status moe_grouped_ffn(const moe_ffn_weights* w, const void* x_rows, moe_dtype act_dt,
-                           const int32_t* offsets, int32_t max_rows, void* y_rows,
-                           moe_dtype y_dt, void* workspace, size_t ws_bytes, void* hip_stream) {
+                           const int32_t* row_index, const int32_t* offsets, int32_t max_rows,
+                           void* y_rows, moe_dtype y_dt, void* workspace, size_t ws_bytes,
+                           void* hip_stream) {
   CHECK(w, MOE_EINVAL, "moe_grouped_ffn: weights is NULL");
   const int E = w->n_experts, d = w->d_model, F = w->d_ff;
   CHECK(E >= 1 && d >= 1 && F >= 1 && max_rows >= 1, MOE_EINVAL,
@@ -224,8 +225,8 @@ moe_status moe_grouped_ffn(const moe_ffn_weights* w, const void* x_rows, moe_dty
   moe_status s = check_ws(workspace, ws_bytes, grouped_ffn_workspace_bytes(w, act_dt, max_rows),
                           "moe_grouped_ffn");
   if (s != MOE_OK) return s;
-  return grouped_ffn_launch(w, x_rows, act_dt, offsets, max_rows, y_rows, y_dt, workspace,
-                            (hipStream_t)hip_stream);
+  return grouped_ffn_launch(w, x_rows, act_dt, row_index, offsets, max_rows, y_rows, y_dt,
+                            workspace, (hipStream_t)hip_stream);
 }
 
 moe_status moe_combine(int32_t n_tokens, int32_t d_model, int32_t top_k, const void* y_rows,

@@ -1,9 +1,12 @@
 // gemm_bf16.h -- ragged grouped GEMM C = A . B^T on gfx950 bf16 MFMA.
 //
 // A [rows][K] and every B [E][Nrows][K] are K-contiguous, so both operands
-// load as 16-byte row chunks. Rows offsets[e] .. offsets[e+1] of A belong to
-// group (expert) e and multiply that group's B. M tiles come from a
-// device-built tile table (no host sync on the group sizes).
+// load as 16-byte row chunks. Rows offsets[e] .. offsets[e+1] of the product
+// belong to group (expert) e and multiply that group's B; product row r
+// reads A row r, or A row a_rows[r] when a row map is given (the token
+// gather of dispatch fused into the operand load, as a fused MoE kernel
+// does). M tiles come from a device-built tile table (no host sync on the
+// group sizes).
 //
 // Operand planes: an operand may be given as several bf16 planes whose sum
 // is the value (NA planes of A, NB planes of B): NA = 2 is an fp32 operand
@@ -47,6 +50,7 @@ struct Args {
   int group_n;           // GN
   const int32_t* offsets;     // [E+1]
   const int32_t* tile_start;  // [E+1]
+  const int32_t* a_rows;      // row r of the product reads A row a_rows[r] (or r if null)
 };
 
 __device__ __forceinline__ float act_fn(int act, float v) {
@@ -77,8 +81,24 @@ __device__ __forceinline__ int tile_expert(const int32_t* ts, int E, int mt) {
 // 16-byte LDS read serves 16 lanes (16 consecutive rows, one logical chunk)
 // per cycle over 64 four-byte banks; rows r, r+4, r+8, r+12 share bank
 // group r%4, and the swizzle gives them four different chunks.
-__device__ __forceinline__ int dlds_off(int r, int c) {  // bf16 elements, BK = 32
-  return r * 32 + ((c ^ ((r >> 2) & 3)) << 3);
+#ifndef MOE_MFMA_PRIO
+#define MOE_MFMA_PRIO 0
+#endif
+#ifndef MOE_SCHED_GROUPS
+#define MOE_SCHED_GROUPS 0
+#endif
+
+// LDS element offset of logical 16-byte chunk c of row r. BK = 32: 64-byte
+// rows, chunk ^ ((r >> 2) & 3); BK = 64: 128-byte rows, chunk ^ ((r >> 1) & 7).
+// Either way the 16 consecutive rows read in one LDS cycle at one logical
+// chunk land on 16 distinct 16-byte bank groups.
+template <int BK>
+__device__ __forceinline__ int chunk_swz(int r) {
+  return BK == 32 ? ((r >> 2) & 3) : ((r >> 1) & 7);
+}
+template <int BK>
+__device__ __forceinline__ int dlds_off(int r, int c) {
+  return r * BK + ((c ^ chunk_swz<BK>(r)) << 3);
 }
 
 template <int N>
@@ -93,19 +113,22 @@ enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_BF16_PAIR = 2 };
 // NA A planes (bf16, plane p at A + p * a_plane elements): NA = 2 is an fp32
 // operand kept as hi + lo bf16 parts. OUT_BF16_PAIR writes the result the
 // same way: hi = bf16(v) at C, lo = bf16(v - hi) at C + c_plane.
-template <int BM, int BN, int NS, int WGM, int WGN, int NA, int NB, int EPI, int OUTK>
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, int NA, int NB, int EPI, int OUTK>
 __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args g) {
-  constexpr int BK = 32;
+  constexpr int KK = BK / 16;                     // MFMA K steps per stage (even)
+  constexpr int CPR = BK / 8;                     // 16-byte chunks per LDS row
+  constexpr int SEG_ROWS = 1024 / (BK * 2);       // rows per 1 KB segment
   constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int NACC = EPI == EPI_GLU ? 2 : 1;
-  constexpr int A_SEG = BM / 16, B_SEG = BN / 16;  // 1 KB segments per plane
+  constexpr int A_SEG = BM / SEG_ROWS, B_SEG = BN / SEG_ROWS;  // 1 KB segments per plane
   constexpr int A_IT = A_SEG / NW, B_IT = B_SEG / NW;
   constexpr int LPT = NA * A_IT + NB * B_IT;      // load instructions per stage
   constexpr int A_PLANE = BM * BK, B_PLANE = BN * BK;
   constexpr int STAGE = NA * A_PLANE + NB * B_PLANE;  // bf16 elements
   static_assert(FM >= 1 && FN >= 1, "wave tile too small");
+  static_assert(KK % 2 == 0, "fragment sets alternate over an even number of K steps");
   static_assert(A_IT * NW == A_SEG && B_IT * NW == B_SEG, "segments per wave");
   static_assert(LPT * (NS - 1) < 64, "vmcnt range");
   static_assert(EPI != EPI_GLU || (NB == 2 && NA == 1), "GLU takes gate and up planes");
@@ -129,15 +152,18 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
   const int k_end = min(K, k_begin + g.k_chunk);
   const int KT = (k_end - k_begin) / BK;
 
-  // per-lane global source pointers (at k = k_begin) for each segment
-  const int lr = lane >> 2;
+  // per-lane global source pointers (at k = k_begin) for each segment: lane
+  // l of a segment lands at byte l*16, i.e. row l / CPR, physical chunk
+  // l % CPR, and fetches the logical chunk the swizzle puts there
+  const int lr = lane / CPR;
   const uint16_t* asrc[NA][A_IT];
 #pragma unroll
   for (int i = 0; i < A_IT; ++i) {
-    const int r = (wave + i * NW) * 16 + lr;
+    const int r = (wave + i * NW) * SEG_ROWS + lr;
     int row = row0 + r;
     row = row < row_end ? row : row_end - 1;
-    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    if (g.a_rows) row = g.a_rows[row];  // gather fused into the operand load
+    const int c = (lane % CPR) ^ chunk_swz<BK>(r);
 #pragma unroll
     for (int p = 0; p < NA; ++p)
       asrc[p][i] = (const uint16_t*)g.A + (size_t)p * g.a_plane + (size_t)row * K + k_begin + c * 8;
@@ -147,8 +173,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
   for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int i = 0; i < B_IT; ++i) {
-      const int r = (wave + i * NW) * 16 + lr;
-      const int c = (lane & 3) ^ ((r >> 2) & 3);
+      const int r = (wave + i * NW) * SEG_ROWS + lr;
+      const int c = (lane % CPR) ^ chunk_swz<BK>(r);
       bsrc[b][i] = g.B[b] + ((size_t)e * g.Nrows + n0 + r) * K + k_begin + c * 8;
     }
 
@@ -191,21 +217,24 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
   };
   auto read_frags = [&](Frags& f, int stage, int kk) {
     const uint16_t* cur = smem + stage * STAGE;
-    const int c = kk * 2 + (lane >> 5);
+    const int c = kk * 2 + (lane >> 5);  // chunk of this lane's 8 K values
 #pragma unroll
     for (int p = 0; p < NA; ++p)
 #pragma unroll
       for (int i = 0; i < FM; ++i)
         f.a[p][i] = *(const bf16x8_t*)(cur + p * A_PLANE +
-                                       dlds_off(wm * WM + i * 32 + (lane & 31), c));
+                                       dlds_off<BK>(wm * WM + i * 32 + (lane & 31), c));
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
         f.b[b][j] = *(const bf16x8_t*)(cur + NA * A_PLANE + b * B_PLANE +
-                                       dlds_off(wn * WN + j * 32 + (lane & 31), c));
+                                       dlds_off<BK>(wn * WN + j * 32 + (lane & 31), c));
   };
   auto mfma = [&](const Frags& f) {
+#if MOE_MFMA_PRIO
+    __builtin_amdgcn_s_setprio(1);
+#endif
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -217,6 +246,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
             f32x16_t& d = acc[EPI == EPI_GLU ? b : 0][i][j];
             d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[p][i], f.b[b][j], d, 0, 0, 0);
           }
+#if MOE_MFMA_PRIO
+    __builtin_amdgcn_s_setprio(0);
+#endif
   };
 
   // Schedule per K tile kt (stage kt % NS), in two 16-wide halves:
@@ -231,25 +263,40 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
 #pragma unroll
   for (int j = 0; j < NS; ++j)
     if (j < KT) issue(j, j);
-  Frags f0, f1;
+  Frags fr[2];
   if (KT > 0) {
     if (KT > NS - 1) wait_vmcnt<(NS - 1) * LPT>();
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    read_frags(f0, 0, 0);
+    read_frags(fr[0], 0, 0);
   }
   for (int kt = 0; kt < KT; ++kt) {
-    read_frags(f1, kt % NS, 1);
-    mfma(f0);
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk + 1 < KK; ++kk) {
+      read_frags(fr[(kk + 1) & 1], kt % NS, kk + 1);
+      mfma(fr[kk & 1]);
+#if MOE_SCHED_GROUPS
+      // all LDS reads of the next step go out before this step's MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, NA * FM + NB * FN, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NA * NB * FM * FN, 0);
+#endif
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // this wave's LDS reads of tile kt are done; tile kt+1 may still be
+    // followed by up to NS-2 younger tiles in flight
     __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
     if (kt + NS - 1 < KT) wait_vmcnt<(NS - 2) * LPT>();
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     if (kt + NS < KT) issue(kt + NS, kt % NS);
-    if (kt + 1 < KT) read_frags(f0, (kt + 1) % NS, 0);
-    mfma(f1);
+    if (kt + 1 < KT) read_frags(fr[KK & 1], (kt + 1) % NS, 0);
+    mfma(fr[(KK - 1) & 1]);
+#if MOE_SCHED_GROUPS
+    __builtin_amdgcn_sched_group_barrier(0x020, LPT, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, NA * FM + NB * FN, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NA * NB * FM * FN, 0);
+#endif
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -288,11 +335,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
   }
 }
 
-template <int BM, int BN, int NS, int WGM, int WGN, int NA, int NB, int EPI, int OUTK>
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, int NA, int NB, int EPI, int OUTK>
 inline hipError_t launch_dlds(Args g, int k_splits, hipStream_t st) {
-  constexpr size_t lds = (size_t)NS * (NA * BM + NB * BN) * 32 * sizeof(uint16_t);
+  constexpr size_t lds = (size_t)NS * (NA * BM + NB * BN) * BK * sizeof(uint16_t);
   static_assert(lds <= 160 * 1024, "LDS budget");
-  auto kern = grouped_gemm_dlds_kernel<BM, BN, NS, WGM, WGN, NA, NB, EPI, OUTK>;
+  auto kern = grouped_gemm_dlds_kernel<BM, BN, BK, NS, WGM, WGN, NA, NB, EPI, OUTK>;
   static bool configured = false;
   if (!configured) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -309,22 +356,34 @@ inline hipError_t launch_dlds(Args g, int k_splits, hipStream_t st) {
   return hipGetLastError();
 }
 
+#ifndef MOE_GEMM_BK
+#define MOE_GEMM_BK 64
+#endif
+
 // LDS stages for a tile: as many as fit in 144 KB (at most 8), bounded so
 // that (stages - 1) x loads-per-stage fits the 6-bit vmcnt (4 waves).
-template <int BM, int BN, int NA, int NB>
+template <int BM, int BN, int BK, int NA, int NB>
 constexpr int pick_stages() {
-  constexpr int stage_bytes = (NA * BM + NB * BN) * 32 * 2;
-  constexpr int lpt = NA * (BM / 64) + NB * (BN / 64);  // with 4 waves (fewer with 8)
+  constexpr int stage_bytes = (NA * BM + NB * BN) * BK * 2;
+  constexpr int lpt = (NA * BM + NB * BN) * BK * 2 / 1024 / 4;  // with 4 waves
   int ns = 147456 / stage_bytes;
   if (ns > 8) ns = 8;
   while (ns > 2 && (ns - 1) * lpt >= 64) --ns;
   return ns;
 }
 
-template <int BM, int BN, int NA, int NB, int EPI, int OUTK, int WGN = 2>
+// K width of a stage: the preferred one if two stages of it fit, else 32.
+template <int BM, int BN, int NA, int NB, int BKP>
+constexpr int pick_bk() {
+  return pick_stages<BM, BN, BKP, NA, NB>() >= 2 ? BKP : 32;
+}
+
+template <int BM, int BN, int NA, int NB, int EPI, int OUTK, int WGN = 2, int BKP = MOE_GEMM_BK>
 inline hipError_t run_gemm(const Args& g, int k_splits, hipStream_t st) {
-  return launch_dlds<BM, BN, pick_stages<BM, BN, NA, NB>(), 2, WGN, NA, NB, EPI, OUTK>(
-      g, k_splits, st);
+  constexpr int bk = pick_bk<BM, BN, NA, NB, BKP>();
+  constexpr int ns = pick_stages<BM, BN, bk, NA, NB>();
+  static_assert(ns >= 2, "tile too large for two LDS stages");
+  return launch_dlds<BM, BN, bk, ns, 2, WGN, NA, NB, EPI, OUTK>(g, k_splits, st);
 }
 
 }  // namespace moe_gemm

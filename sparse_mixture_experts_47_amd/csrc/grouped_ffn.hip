@@ -62,6 +62,7 @@ struct GemmArgs {
   int K, Nout, E, max_mt, act;
   const int32_t* offsets;
   const int32_t* tile_start;
+  const int32_t* a_rows;  // product row r reads A row a_rows[r], or r if null
 };
 
 // Expert of M tile `mt`: tile_start[e] <= mt < tile_start[e+1].
@@ -104,7 +105,8 @@ __global__ __launch_bounds__(256) void ggemm_f32_kernel(GemmArgs g) {
     for (int i = tid; i < BM * BK; i += 256) {
       const int m = i / BK, kk = i % BK;
       const int row = row0 + m, k = k0 + kk;
-      As[kk][m] = (row < row_end && k < K) ? A[(size_t)row * K + k] : 0.f;
+      const int arow = (row < row_end && g.a_rows) ? g.a_rows[row] : row;
+      As[kk][m] = (row < row_end && k < K) ? A[(size_t)arow * K + k] : 0.f;
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -161,6 +163,7 @@ struct Fp8Args {
   void* C;             // [rows][Nout]
   int K, Nout, E, act;
   const int32_t* offsets;
+  const int32_t* a_rows;  // product row r reads A row a_rows[r], or r if null
 };
 
 // 8 e4m3 codes (two dwords) -> 8 bf16, exactly (e4m3 values are bf16 values).
@@ -220,7 +223,8 @@ __global__ __launch_bounds__(256) void ffn_fp8_kernel(Fp8Args g) {
         const int row = rb + m * 16 + (lane & 15);
         u32x4_t alo = {0u, 0u, 0u, 0u}, ahi = {0u, 0u, 0u, 0u};
         if (row < r_end) {
-          const u32x4_t* ap = (const u32x4_t*)(g.A + (size_t)row * K + kl);
+          const int arow = g.a_rows ? g.a_rows[row] : row;
+          const u32x4_t* ap = (const u32x4_t*)(g.A + (size_t)arow * K + kl);
           alo = ap[0];
           ahi = ap[1];
         }
@@ -282,12 +286,15 @@ __global__ __launch_bounds__(256) void ffn_fp8_kernel(Fp8Args g) {
 #define MOE_GROUP_N 4
 #endif
 // GEMM 1 (SwiGLU, 256-row tiles) runs 8 waves (2 per SIMD); GEMM 2 uses
-// 256x256 tiles when the width allows (16 MFMAs per wave per half K step)
+// 256x128 tiles (MOE_G2_WIDE=1: 256x256)
 #ifndef MOE_G1_WGN
 #define MOE_G1_WGN 4
 #endif
 #ifndef MOE_G2_WIDE
-#define MOE_G2_WIDE 1
+#define MOE_G2_WIDE 0
+#endif
+#ifndef MOE_G2_WGN
+#define MOE_G2_WGN 4
 #endif
 
 moe_status gemm_status(hipError_t e, const char* what) {
@@ -335,8 +342,8 @@ hipError_t launch_ffn(bool glu, bool pair, bool ybf, const moe_gemm::Args& g1,
       e = ybf ? run_gemm<BM, 256, 1, 1, EPI_OUT, OUT_BF16>(g2, 1, st)
               : run_gemm<BM, 256, 1, 1, EPI_OUT, OUT_F32>(g2, 1, st);
     else if (n2)
-      e = ybf ? run_gemm<BM, 128, 1, 1, EPI_OUT, OUT_BF16>(g2, 1, st)
-              : run_gemm<BM, 128, 1, 1, EPI_OUT, OUT_F32>(g2, 1, st);
+      e = ybf ? run_gemm<BM, 128, 1, 1, EPI_OUT, OUT_BF16, MOE_G2_WGN>(g2, 1, st)
+              : run_gemm<BM, 128, 1, 1, EPI_OUT, OUT_F32, MOE_G2_WGN>(g2, 1, st);
     else
       e = ybf ? run_gemm<BM, 64, 1, 1, EPI_OUT, OUT_BF16>(g2, 1, st)
               : run_gemm<BM, 64, 1, 1, EPI_OUT, OUT_F32>(g2, 1, st);
@@ -383,8 +390,8 @@ size_t grouped_ffn_workspace_bytes(const moe_ffn_weights* w, moe_dtype act_dt, i
 }
 
 moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_dtype act_dt,
-                              const int32_t* offsets, int max_rows, void* y_rows,
-                              moe_dtype y_dt, void* workspace, hipStream_t st) {
+                              const int32_t* row_index, const int32_t* offsets, int max_rows,
+                              void* y_rows, moe_dtype y_dt, void* workspace, hipStream_t st) {
   const int E = w->n_experts, d = w->d_model, F = w->d_ff;
   char* ws = (char*)workspace;
   void* h = ws;
@@ -394,7 +401,7 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
 
   if (w->w_dt == MOE_FP8_E4M3) {
     Fp8Args a1{(const uint16_t*)x_rows, (const uint8_t*)w->w1, (const uint8_t*)w->w3,
-               w->s1, w->s3, h, d, F, E, (int)w->act, offsets};
+               w->s1, w->s3, h, d, F, E, (int)w->act, offsets, row_index};
     dim3 g1(F / 64, E);
     if (glu)
       ffn_fp8_kernel<MODE_GLU, true><<<g1, 256, 0, st>>>(a1);
@@ -403,7 +410,7 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
     s = launch_status("grouped FFN fp8 GEMM 1");
     if (s != MOE_OK) return s;
     Fp8Args a2{(const uint16_t*)h, (const uint8_t*)w->w2, nullptr, w->s2, nullptr, y_rows,
-               F, d, E, (int)w->act, offsets};
+               F, d, E, (int)w->act, offsets, nullptr};
     dim3 g2(d / 64, E);
     if (y_dt == MOE_BF16)
       ffn_fp8_kernel<MODE_OUT, true><<<g2, 256, 0, st>>>(a2);
@@ -422,9 +429,9 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
 
   if (act_dt == MOE_F32) {
     GemmArgs a1{x_rows, w->w1, w->w3, w->b1, h, d, F, E, max_mt, (int)w->act, offsets,
-                tile_start};
+                tile_start, row_index};
     GemmArgs a2{h, w->w2, nullptr, w->b2, y_rows, F, d, E, max_mt, (int)w->act, offsets,
-                tile_start};
+                tile_start, nullptr};
     const int g1 = max_mt * ((F + 63) / 64), g2 = max_mt * ((d + 63) / 64);
     if (glu)
       ggemm_f32_kernel<MODE_GLU><<<g1, 256, 0, st>>>(a1);
@@ -438,6 +445,7 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
   const bool pair = w->h_fp32 != 0;
   Args g1 = base_args(x_rows, w->w1, w->w3, w->b1, h, d, F, E, max_mt, (int)w->act, offsets,
                       tile_start);
+  g1.a_rows = row_index;
   Args g2 = base_args(h, w->w2, nullptr, w->b2, y_rows, F, d, E, max_mt, (int)w->act, offsets,
                       tile_start);
   g1.c_plane = (long long)max_rows * F;  // lo plane of the bf16 pair h

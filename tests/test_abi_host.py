@@ -58,6 +58,6 @@ def test_validation_errors_before_any_launch(lib):
     assert L.moe_dispatch(16, 4, 1, 1, 0, -1, fake, fake, fake, None, 1, 0, fake, fake, fake,
                           fake, fake, fake, None, fake, 8, None) == 3
     w = lib.FFNWeights(8, 4096, 100, 2, 1, 4096, 4096, 4096, None, None, None, None, None, 0)
-    assert L.moe_grouped_ffn(ctypes.byref(w), fake, 1, fake, 10, fake, 1, fake, 1 << 30,
+    assert L.moe_grouped_ffn(ctypes.byref(w), fake, 1, None, fake, 10, fake, 1, fake, 1 << 30,
                              None) == 2
     assert L.moe_status_string(3) == b"MOE_EWORKSPACE"

@@ -74,10 +74,10 @@ def test_level1_routing_bit_exact_and_outputs(moe, key):
     assert np.array_equal(to_np(layer.expert_of), d["expert_of"])
     R = d["R"]
     assert np.array_equal(to_np(layer.perm_token)[:R], d["perm_token"])
-    # gathered rows are exact copies
-    xp = to_np(layer.x_perm.float() if layer.x_perm.dtype == torch.bfloat16 else layer.x_perm)
-    xs = to_np(dev["x"].float())
-    assert np.array_equal(xp[:R], xs[d["perm_token"]])
+    if layer.x_perm is not None:  # explicit gather path: rows are exact copies
+        xp = to_np(layer.x_perm.float() if layer.x_perm.dtype == torch.bfloat16 else layer.x_perm)
+        xs = to_np(dev["x"].float())
+        assert np.array_equal(xp[:R], xs[d["perm_token"]])
     err = rel_err(to_np(y), ref["y"])
     print("  max|dy|/rms =", err)
     assert err <= out_tol(cfg)
@@ -356,3 +356,18 @@ def test_grouped_ffn_fp32_intermediate_is_tighter(moe):
         errs[h32] = rel_err(to_np(y), ref)
     print("bf16 h:", errs[False], " fp32 h:", errs[True])
     assert errs[True] <= 1e-3 and errs[True] < errs[False] / 8
+
+
+@pytest.mark.parametrize("key", ["c2", "c4", "c5", "c1"])
+def test_fused_gather_matches_explicit_gather(moe, key):
+    """GEMM 1 reading token rows through perm_token gives bit-identical
+    outputs to gathering x_perm first in dispatch."""
+    cfg = W.REDUCED[key]
+    dev = to_device(W.make_inputs(cfg, "cpu"))
+    xdt = torch.float32 if cfg.x_dtype == W.F32 else torch.bfloat16
+    outs = []
+    for fused in (False, True):
+        layer = moe.MoELayer(moe.spec_from_config(cfg), dev, x_dtype=xdt, fused_gather=fused)
+        outs.append(layer.forward(dev["x"]).clone())
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
