@@ -282,6 +282,242 @@ __global__ __launch_bounds__(256) void ffn_fp8_kernel(Fp8Args g) {
   }
 }
 
+// ------------------------------------------------------- fp8 decode, streamed
+// With a few rows per expert the FFN is a pure weight stream, so this path
+// is built around keeping HBM reads in flight without interruption.
+// Persistent blocks of NW waves walk work units: one 16-row tile of one
+// expert (tile table with 16-row tiles) x 16*NW output columns, column tiles
+// of a row tile being consecutive units. Every unit streams its K dimension
+// through one LDS ring of NS stages of SK K values, filled by direct-to-LDS
+// loads (global_load_lds): each wave brings its own 16 weight rows (SK
+// contiguous e4m3 bytes per row and matrix), the first waves bring the
+// unit's 16 activation rows (SK bf16 each), and every wave re-fetches its
+// 16 (GLU: 2 x 16) per-channel scales so the epilogue reads them from the
+// stage it finishes on. The ring runs across unit boundaries: the loads of
+// the next unit start while the current one is still being multiplied, and
+// all unit metadata (tile table, offsets, gather rows) sits in LDS so that
+// setting up a unit never waits on the vector-memory counter. A wave waits
+// only for its own loads of the stage it is about to use (s_waitcnt vmcnt
+// with the count of loads issued after it), then one barrier makes every
+// wave's part of the stage visible and frees the slot consumed one step
+// earlier.
+//
+// LDS row layouts use an XOR swizzle of the 16-byte chunk index so that the
+// 16 lanes reading 16 consecutive rows at one logical chunk hit 16 distinct
+// bank groups: 64-byte rows ^((r>>2)&3), 128-byte rows ^((r>>1)&7),
+// 256-byte rows ^(r&15).
+template <int RB>
+__device__ __forceinline__ int stream_swz(int r) {
+  return RB == 64 ? ((r >> 2) & 3) : RB == 128 ? ((r >> 1) & 7) : (r & 15);
+}
+
+template <int SK, int NW, int NB>
+struct StreamLayout {
+  static constexpr int A_ROW = SK * 2;              // bytes of one bf16 activation row
+  static constexpr int A_BYTES = 16 * A_ROW;
+  static constexpr int A_LOADS = A_BYTES / 1024;    // one per wave, waves 0..A_LOADS-1
+  static constexpr int W_ROW = SK;                  // bytes of one e4m3 weight row
+  static constexpr int W_BYTES = 16 * W_ROW;        // one wave, one matrix
+  static constexpr int W_LOADS = W_BYTES / 1024;
+  static constexpr int S_BYTES = 256;               // scales: 64 lanes x 4 bytes per wave
+  static constexpr int STAGE = A_BYTES + NW * NB * W_BYTES + NW * S_BYTES;
+  static_assert(A_LOADS >= 1 && A_LOADS <= NW && W_LOADS >= 1, "stream stage shape");
+};
+
+template <int MODE, int SK, int NW, int NS>
+constexpr int stream_lds_bytes(int E, int rows_cap) {
+  return NS * StreamLayout<SK, NW, MODE == MODE_GLU ? 2 : 1>::STAGE +
+         ((2 * (E + 1) + rows_cap) * 4 + 15) / 16 * 16;
+}
+
+template <int MODE, bool OUT_BF16, int SK, int NW, int NS>
+__global__ __launch_bounds__(NW * 64) void ffn_fp8_stream_kernel(Fp8Args g,
+                                                                  const int32_t* __restrict__ tile_start,
+                                                                  int rows_cap) {
+  constexpr int NB = MODE == MODE_GLU ? 2 : 1;
+  using L = StreamLayout<SK, NW, NB>;
+  constexpr int BN = 16 * NW;
+  constexpr int LPW = NB * L::W_LOADS + 1;  // loads per stage of a wave without A
+  static_assert((NS - 2) * (LPW + 1) <= 63, "vmcnt range");
+  extern __shared__ __align__(16) uint8_t smem[];
+  int32_t* s_ts = (int32_t*)(smem + NS * L::STAGE);
+  int32_t* s_off = s_ts + (g.E + 1);
+  int32_t* s_arow = s_off + (g.E + 1);
+
+  const int lane = threadIdx.x & 63, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int E = g.E, K = g.K, Nout = g.Nout;
+  for (int i = threadIdx.x; i <= E; i += NW * 64) {
+    s_ts[i] = tile_start[i];
+    s_off[i] = g.offsets[i];
+  }
+  if (g.a_rows) {
+    const int R = min(g.offsets[E], rows_cap);
+    for (int i = threadIdx.x; i < R; i += NW * 64) s_arow[i] = g.a_rows[i];
+  }
+  __syncthreads();
+  const int NT = Nout / BN, KT = K / SK;
+  const int n_units = s_ts[E] * NT;
+  const int G = gridDim.x, bid = blockIdx.x;
+  const int my_units = n_units > bid ? (n_units - 1 - bid) / G + 1 : 0;
+  const int Q = my_units * KT;  // stages streamed by this block
+  if (Q == 0) return;
+
+  // unit j of this block -> expert, row range [rb, re) (at most 16 rows), n0
+  struct Unit {
+    int e, rb, re, n0;
+  };
+  auto unit_of = [&](int j) {
+    const int u = bid + j * G;
+    const int mt = u / NT;
+    int lo = 0, hi = E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_ts[mid] <= mt) lo = mid; else hi = mid;
+    }
+    Unit t;
+    t.e = __builtin_amdgcn_readfirstlane(lo);
+    const int rb = s_off[t.e] + (mt - s_ts[t.e]) * 16;
+    t.rb = __builtin_amdgcn_readfirstlane(rb);
+    t.re = __builtin_amdgcn_readfirstlane(min(s_off[t.e + 1], rb + 16));
+    t.n0 = __builtin_amdgcn_readfirstlane((u - mt * NT) * BN);
+    return t;
+  };
+
+  // ---- loader: per-lane global sources of the unit being fetched
+  const uint8_t* wsrc[NB][L::W_LOADS];
+  const uint8_t* asrc = nullptr;
+  const float* ssrc = nullptr;
+  int lj = 0, lkt = 0;
+  auto set_sources = [&](int j) {
+    const Unit t = unit_of(j);
+    constexpr int CPR = L::W_ROW / 16;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int i = 0; i < L::W_LOADS; ++i) {
+        const int r = i * (64 / CPR) + lane / CPR;
+        const int c = (lane % CPR) ^ stream_swz<L::W_ROW>(r);
+        const uint8_t* B = b == 0 ? g.B0 : g.B1;
+        wsrc[b][i] = B + ((size_t)t.e * Nout + t.n0 + wave * 16 + r) * K + c * 16;
+      }
+    if (wave < L::A_LOADS) {
+      constexpr int ACPR = L::A_ROW / 16;
+      const int r = wave * (64 / ACPR) + lane / ACPR;
+      const int c = (lane % ACPR) ^ stream_swz<L::A_ROW>(r);
+      const int row = min(t.rb + r, t.re - 1);  // pad rows repeat the last row
+      const int arow = g.a_rows ? s_arow[min(row, rows_cap - 1)] : row;
+      asrc = (const uint8_t*)g.A + (size_t)arow * K * 2 + c * 16;
+    }
+    const int sb = NB == 2 ? (lane >> 4) & 1 : 0;
+    ssrc = (sb ? g.s1 : g.s0) + (size_t)t.e * Nout + t.n0 + wave * 16 + (lane & 15);
+  };
+  auto issue = [&](int slot) {
+    uint8_t* base = smem + slot * L::STAGE;
+    if (wave < L::A_LOADS)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(asrc + (size_t)lkt * SK * 2),
+          (__attribute__((address_space(3))) void*)(base + wave * 1024), 16, 0, 0);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int i = 0; i < L::W_LOADS; ++i)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(wsrc[b][i] + (size_t)lkt * SK),
+            (__attribute__((address_space(3))) void*)(base + L::A_BYTES +
+                                                       ((wave * NB + b) * L::W_LOADS + i) * 1024),
+            16, 0, 0);
+    __builtin_amdgcn_global_load_lds(
+        (const void*)ssrc,
+        (__attribute__((address_space(3))) void*)(base + L::A_BYTES + NW * NB * L::W_BYTES +
+                                                   wave * L::S_BYTES),
+        4, 0, 0);
+    if (++lkt == KT) {
+      lkt = 0;
+      if (++lj < my_units) set_sources(lj);
+    }
+  };
+
+  set_sources(0);
+  for (int s = 0; s < NS - 1 && s < Q; ++s) issue(s);
+
+  f32x4_t acc[NB];
+  int ckt = 0, cj = 0;
+  for (int q = 0; q < Q; ++q) {
+    const int slot = q % NS;
+    // this wave's loads of stage q are done when at most the loads of the
+    // NS-2 later stages are outstanding
+    if (q + NS - 2 < Q) {
+      if (wave < L::A_LOADS) moe_gemm::wait_vmcnt<(NS - 2) * (LPW + 1)>();
+      else moe_gemm::wait_vmcnt<(NS - 2) * LPW>();
+    } else {
+      moe_gemm::wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (q + NS - 1 < Q) issue((q + NS - 1) % NS);
+
+    if (ckt == 0) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    const uint8_t* base = smem + slot * L::STAGE;
+    const int rl = lane & 15;
+#pragma unroll
+    for (int s = 0; s < SK / 64; ++s) {
+      const int ca = s * 8 + grp * 2;
+      const uint8_t* arow = base + rl * L::A_ROW;
+      const u32x4_t alo = *(const u32x4_t*)(arow + ((ca ^ stream_swz<L::A_ROW>(rl)) << 4));
+      const u32x4_t ahi = *(const u32x4_t*)(arow + (((ca + 1) ^ stream_swz<L::A_ROW>(rl)) << 4));
+      const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, alo);
+      const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, ahi);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const uint8_t* wrow = base + L::A_BYTES + (wave * NB + b) * L::W_BYTES + rl * L::W_ROW;
+        const int cw = s * 4 + grp;
+        const u32x4_t w = *(const u32x4_t*)(wrow + ((cw ^ stream_swz<L::W_ROW>(rl)) << 4));
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, e4m3x8_to_bf16(w[0], w[1]), acc[b],
+                                                         0, 0, 0);
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, e4m3x8_to_bf16(w[2], w[3]), acc[b],
+                                                         0, 0, 0);
+      }
+    }
+
+    if (ckt == KT - 1) {
+      const Unit t = unit_of(cj);
+      const float* sc = (const float*)(base + L::A_BYTES + NW * NB * L::W_BYTES +
+                                       wave * L::S_BYTES);
+      const float sc0 = sc[rl];
+      const float sc1 = NB == 2 ? sc[16 + rl] : 0.f;
+      const int n = t.n0 + wave * 16 + rl;
+      // 16x16 accumulator layout: register r of lane l holds row 4*(l>>4)+r,
+      // column l & 15
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = t.rb + 4 * grp + r;
+        if (row >= t.re) continue;
+        float v;
+        if (MODE == MODE_GLU)
+          v = silu(acc[0][r] * sc0) * (acc[NB - 1][r] * sc1);
+        else if (MODE == MODE_ACT)
+          v = act_fn(g.act, acc[0][r] * sc0);
+        else
+          v = acc[0][r] * sc0;
+        const size_t o = (size_t)row * Nout + n;
+        if (OUT_BF16)
+          ((uint16_t*)g.C)[o] = moe::f32_to_bf16_bits(v);
+        else
+          ((float*)g.C)[o] = v;
+      }
+    }
+    if (++ckt == KT) {
+      ckt = 0;
+      ++cj;
+    }
+  }
+}
+
 #ifndef MOE_GROUP_N
 #define MOE_GROUP_N 4
 #endif
@@ -303,6 +539,56 @@ moe_status gemm_status(hipError_t e, const char* what) {
     return MOE_EHIP;
   }
   return MOE_OK;
+}
+
+// fp8 streaming path: 128 K values per stage, 4 waves (64 output columns)
+// per block, two blocks per CU (each ring stays under 80 KB of LDS).
+#ifndef MOE_FP8_STREAM
+#define MOE_FP8_STREAM 1
+#endif
+constexpr int kStreamSK = 128, kStreamNW = 4;
+constexpr int kStreamNsGlu = 3;  // two-matrix stages (21 KB)
+constexpr int kStreamNs1 = 5;    // one-matrix stages (13 KB)
+constexpr int kStreamMaxRows = 2048;
+
+// The streaming kernel re-reads an expert's weights once per 16-row tile,
+// so it serves layers averaging at most 8 rows per expert (decode); its
+// shapes need K and the output width to be multiples of 128 and 64.
+bool use_fp8_stream(int E, int d, int F, int max_rows) {
+  return MOE_FP8_STREAM && max_rows <= 8 * E && max_rows <= kStreamMaxRows &&
+         d % kStreamSK == 0 && F % kStreamSK == 0 && d % (16 * kStreamNW) == 0 &&
+         F % (16 * kStreamNW) == 0;
+}
+
+int device_cu_count() {
+  static int cached_dev = -1, cached_n = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev != cached_dev) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached_dev = dev;
+    cached_n = n;
+  }
+  return cached_n;
+}
+
+template <int MODE, bool OUT_BF16, int NS>
+hipError_t launch_stream(const Fp8Args& a, const int32_t* tile_start, int rows_cap,
+                         hipStream_t st) {
+  auto kern = ffn_fp8_stream_kernel<MODE, OUT_BF16, kStreamSK, kStreamNW, NS>;
+  const int lds = stream_lds_bytes<MODE, kStreamSK, kStreamNW, NS>(a.E, rows_cap);
+  static int configured = 0;
+  if (lds > configured) {
+    const hipError_t e =
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    configured = lds;
+  }
+  kern<<<2 * device_cu_count(), kStreamNW * 64, lds, st>>>(a, tile_start, max(rows_cap, 1));
+  return hipGetLastError();
 }
 
 // GEMM 1 then GEMM 2 of the bf16 path for M tiles of BM rows. 128-column N
@@ -402,6 +688,20 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
   if (w->w_dt == MOE_FP8_E4M3) {
     Fp8Args a1{(const uint16_t*)x_rows, (const uint8_t*)w->w1, (const uint8_t*)w->w3,
                w->s1, w->s3, h, d, F, E, (int)w->act, offsets, row_index};
+    Fp8Args a2{(const uint16_t*)h, (const uint8_t*)w->w2, nullptr, w->s2, nullptr, y_rows,
+               F, d, E, (int)w->act, offsets, nullptr};
+    if (use_fp8_stream(E, d, F, max_rows)) {
+      tile_table_kernel<<<1, 256, 0, st>>>(offsets, E, 16, tile_start);
+      s = launch_status("tile table");
+      if (s != MOE_OK) return s;
+      const int cap1 = row_index ? max_rows : 0;
+      hipError_t e = glu ? launch_stream<MODE_GLU, true, kStreamNsGlu>(a1, tile_start, cap1, st)
+                         : launch_stream<MODE_ACT, true, kStreamNs1>(a1, tile_start, cap1, st);
+      if (e != hipSuccess) return gemm_status(e, "grouped FFN fp8 stream GEMM 1");
+      e = y_dt == MOE_BF16 ? launch_stream<MODE_OUT, true, kStreamNs1>(a2, tile_start, 0, st)
+                           : launch_stream<MODE_OUT, false, kStreamNs1>(a2, tile_start, 0, st);
+      return gemm_status(e, "grouped FFN fp8 stream GEMM 2");
+    }
     dim3 g1(F / 64, E);
     if (glu)
       ffn_fp8_kernel<MODE_GLU, true><<<g1, 256, 0, st>>>(a1);
@@ -409,8 +709,6 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
       ffn_fp8_kernel<MODE_ACT, true><<<g1, 256, 0, st>>>(a1);
     s = launch_status("grouped FFN fp8 GEMM 1");
     if (s != MOE_OK) return s;
-    Fp8Args a2{(const uint16_t*)h, (const uint8_t*)w->w2, nullptr, w->s2, nullptr, y_rows,
-               F, d, E, (int)w->act, offsets, nullptr};
     dim3 g2(d / 64, E);
     if (y_dt == MOE_BF16)
       ffn_fp8_kernel<MODE_OUT, true><<<g2, 256, 0, st>>>(a2);

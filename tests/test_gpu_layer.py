@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import workloads as W
-from parity_utils import (MARGIN, TOL_REL, DeviceExperts, experts_of, host_inputs, margins,
+from parity_utils import (MARGIN, TOL_FP8, TOL_REL, DeviceExperts, experts_of, host_inputs, margins,
                           oracle_keys, out_tol, rel_err, require_gpu, to_device, to_np)
 
 pytestmark = pytest.mark.gpu
@@ -370,4 +370,53 @@ def test_fused_gather_matches_explicit_gather(moe, key):
         layer = moe.MoELayer(moe.spec_from_config(cfg), dev, x_dtype=xdt, fused_gather=fused)
         outs.append(layer.forward(dev["x"]).clone())
     torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("gather", [False, True])
+def test_fp8_stream_and_row_group_paths(moe, gather):
+    """fp8 weights, few rows per expert: the streaming path (16-row tiles,
+    chosen while max_rows <= 8 per expert) and the 64-row-group path (forced
+    by a larger max_rows) on the same ragged counts, including experts that
+    span one, two and three 16-row tiles. Both match the oracle, agree
+    bitwise with each other (same MFMA accumulation order), and leave rows
+    past offsets[E] untouched."""
+    cfg = W.REDUCED["c5"]
+    inp = W.make_inputs(cfg, "cpu")
+    host = host_inputs(inp)
+    dev = to_device(inp)
+    E, d = cfg.n_experts, cfg.d_model
+    rng = np.random.default_rng(11)
+    counts = rng.integers(0, 9, size=E)
+    counts[0] = 0
+    counts[-1] = 0
+    counts[1], counts[2], counts[3], counts[4] = 1, 16, 17, 40
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offs[-1])
+    assert R <= 8 * E
+    tok = rng.integers(0, cfg.n_tokens, size=R)
+    w, keep = moe.ffn_weights(dev["w1"], dev["w2"], dev["w3"], cfg.act, None, None,
+                              dev["s1"], dev["s3"], dev["s2"])
+    X64 = oracle.decode_rows(host["x"][tok], cfg.x_dtype)
+    experts = np.repeat(np.arange(E), counts)
+    ref = oracle.ffn_for_assignments(np.arange(R), experts, X64, cfg.act, cfg.w_dtype,
+                                     experts_of(host))
+    outs = []
+    for max_rows in (R, 8 * E + 1):
+        idx = np.zeros(max_rows, np.int32)
+        idx[:R] = tok
+        if gather:
+            x_rows = dev["x"]
+            row_index = torch.from_numpy(idx).cuda()
+        else:
+            x_rows = dev["x"][torch.from_numpy(idx).long().cuda()].contiguous()
+            row_index = None
+        y = torch.full((max_rows, d), 7.0, dtype=torch.float32, device="cuda")
+        moe.moe_grouped_ffn(w, x_rows, torch.from_numpy(offs).cuda(), y, row_index=row_index,
+                            max_rows=max_rows)
+        torch.cuda.synchronize()
+        got = to_np(y)
+        assert rel_err(got[:R], ref) <= TOL_FP8, max_rows
+        assert np.all(got[R:] == 7.0)
+        outs.append(y[:R].clone())
     assert torch.equal(outs[0], outs[1])
