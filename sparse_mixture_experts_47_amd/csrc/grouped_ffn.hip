@@ -541,21 +541,43 @@ moe_status gemm_status(hipError_t e, const char* what) {
   return MOE_OK;
 }
 
-// fp8 streaming path: 128 K values per stage, 4 waves (64 output columns)
-// per block, two blocks per CU (each ring stays under 80 KB of LDS).
+// fp8 streaming path: 128 K values per stage, 8 waves (128 output columns)
+// per block, one block per CU; 3 two-matrix stages (38 KB each) or 6
+// one-matrix stages (22 KB each). Measured on the 256-expert decode layer:
+// 4 waves per CU (in one or two blocks) or 64-value stages stream slower,
+// deeper rings change nothing.
 #ifndef MOE_FP8_STREAM
 #define MOE_FP8_STREAM 1
 #endif
-constexpr int kStreamSK = 128, kStreamNW = 4;
-constexpr int kStreamNsGlu = 3;  // two-matrix stages (21 KB)
-constexpr int kStreamNs1 = 5;    // one-matrix stages (13 KB)
+#ifndef MOE_STREAM_SK
+#define MOE_STREAM_SK 128
+#endif
+#ifndef MOE_STREAM_NW
+#define MOE_STREAM_NW 8
+#endif
+#ifndef MOE_STREAM_NS_GLU
+#define MOE_STREAM_NS_GLU 3
+#endif
+#ifndef MOE_STREAM_NS1
+#define MOE_STREAM_NS1 6
+#endif
+#ifndef MOE_STREAM_BPC
+#define MOE_STREAM_BPC 1  // resident blocks per CU
+#endif
+constexpr int kStreamSK = MOE_STREAM_SK, kStreamNW = MOE_STREAM_NW;
+constexpr int kStreamNsGlu = MOE_STREAM_NS_GLU;
+constexpr int kStreamNs1 = MOE_STREAM_NS1;
 constexpr int kStreamMaxRows = 2048;
 
 // The streaming kernel re-reads an expert's weights once per 16-row tile,
-// so it serves layers averaging at most 8 rows per expert (decode); its
-// shapes need K and the output width to be multiples of 128 and 64.
+// so it serves layers averaging at most 8 rows per expert (decode), and any
+// call of at most 64 rows (a decode batch through the shared expert: four
+// passes over a small weight set, spread over the whole chip instead of one
+// workgroup per 64 columns); its shapes need K and the output width to be
+// multiples of 128.
 bool use_fp8_stream(int E, int d, int F, int max_rows) {
-  return MOE_FP8_STREAM && max_rows <= 8 * E && max_rows <= kStreamMaxRows &&
+  return MOE_FP8_STREAM && (max_rows <= 8 * E || max_rows <= 64) &&
+         max_rows <= kStreamMaxRows &&
          d % kStreamSK == 0 && F % kStreamSK == 0 && d % (16 * kStreamNW) == 0 &&
          F % (16 * kStreamNW) == 0;
 }
@@ -587,7 +609,8 @@ hipError_t launch_stream(const Fp8Args& a, const int32_t* tile_start, int rows_c
     if (e != hipSuccess) return e;
     configured = lds;
   }
-  kern<<<2 * device_cu_count(), kStreamNW * 64, lds, st>>>(a, tile_start, max(rows_cap, 1));
+  kern<<<MOE_STREAM_BPC * device_cu_count(), kStreamNW * 64, lds, st>>>(a, tile_start,
+                                                                        max(rows_cap, 1));
   return hipGetLastError();
 }
 

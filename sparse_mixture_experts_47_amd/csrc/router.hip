@@ -14,8 +14,17 @@
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTokPerWave = 4;
-constexpr int kTokPerBlock = kTokPerWave * (kThreads / MOE_WAVE);
+constexpr int kWaves = kThreads / MOE_WAVE;
+
+// Tokens per wave in the select kernel: one while that leaves the GPU
+// short of waves (few tokens: the kernel is latency bound), four for large
+// batches (fewer per-block score partials to sum afterwards).
+inline int select_tok_per_wave(int N) { return N >= 2048 ? 4 : 1; }
+constexpr int kMaxSplits = 8;  // K splits of the router GEMM (partials summed in order)
+inline int select_blocks(int N) {
+  const int per_block = select_tok_per_wave(N) * kWaves;
+  return (N + per_block - 1) / per_block;
+}
 
 // ---------------------------------------------------------------- GEMM
 // out[t][c] = sum_k x[t][k] * W[c][k] with W = [w_gate ; w_noise] (E or 2E
@@ -100,6 +109,7 @@ struct SelectArgs {
   float* gates;
   float* logits_out;
   double* partials;  // [gridDim.x][E+1] or null
+  int tok_per_wave;
 };
 
 __device__ __forceinline__ float pick(const float* v, int slot, int n) {
@@ -110,7 +120,8 @@ __device__ __forceinline__ float pick(const float* v, int slot, int n) {
   return r;
 }
 
-// One wave per token; expert e lives in lane e % 64, register slot e / 64.
+// One wave per token (tok_per_wave tokens in turn); expert e lives in lane
+// e % 64, register slot e / 64.
 // Softmax tree: the zero-padded 256-wide halving tree equals the tree padded
 // to the next power of two (adding +0 changes nothing), so in-lane slot
 // sums (0+2, 1+3, then the two) are the h = 128 and h = 64 levels and the
@@ -125,8 +136,9 @@ __global__ __launch_bounds__(kThreads) void router_select_kernel(SelectArgs a) {
   double lse2 = 0.0;
   const int E = a.E;
 
-  for (int i = 0; i < kTokPerWave; ++i) {
-    const int t = blockIdx.x * kTokPerBlock + wave * kTokPerWave + i;
+  const int tpw = a.tok_per_wave;
+  for (int i = 0; i < tpw; ++i) {
+    const int t = (blockIdx.x * kWaves + wave) * tpw + i;
     if (t >= a.N) break;
     const float* row = a.src + (size_t)t * a.stride;
     float l[SLOTS];
@@ -137,13 +149,25 @@ __global__ __launch_bounds__(kThreads) void router_select_kernel(SelectArgs a) {
       valid[s] = e < E;
       float v = -INFINITY;
       if (valid[s]) {
-        v = row[e];
-        for (int q = 1; q < a.nsplit; ++q) v = v + row[q * a.split_stride + e];
+        // all split partials are loaded before the in-order sum
+        float pv[kMaxSplits];
+#pragma unroll
+        for (int q = 0; q < kMaxSplits; ++q)
+          pv[q] = q < a.nsplit ? row[q * a.split_stride + e] : 0.f;
+        v = pv[0];
+#pragma unroll
+        for (int q = 1; q < kMaxSplits; ++q)
+          if (q < a.nsplit) v = v + pv[q];
         if (a.from_gemm) {
           if (a.logit_bias) v = v + a.logit_bias[e];
           if (a.noise) {
-            float nv = row[E + e];
-            for (int q = 1; q < a.nsplit; ++q) nv = nv + row[q * a.split_stride + E + e];
+#pragma unroll
+            for (int q = 0; q < kMaxSplits; ++q)
+              pv[q] = q < a.nsplit ? row[q * a.split_stride + E + e] : 0.f;
+            float nv = pv[0];
+#pragma unroll
+            for (int q = 1; q < kMaxSplits; ++q)
+              if (q < a.nsplit) nv = nv + pv[q];
             float sp = nv > 20.f ? nv : (float)log1p(exp((double)nv));
             float z = moe::noise_normal(a.seed, (uint32_t)t, (uint32_t)e, (uint32_t)E);
             v = __builtin_fmaf(z, sp, v);
@@ -247,34 +271,42 @@ __global__ __launch_bounds__(kThreads) void router_select_kernel(SelectArgs a) {
 // The router weights as three bf16 planes whose sum is the fp32 value:
 // hi = bf16(w), mid = bf16(w - hi), lo = bf16(w - hi - mid) (each step
 // exact in fp32). Rows: w_gate 0..E-1, w_noise E..2E-1, zero padding.
-// x is bf16, so x . W runs on bf16 MFMA with every product exact.
+// x is bf16, so x . W runs on bf16 MFMA with every product exact. Four
+// consecutive k per thread (d is a multiple of 64 on this path). The first
+// thread also writes the one-group tile table of the GEMM over N token
+// rows: offsets = {0, N}, tile_start = {0, ceil(N / bm)}.
 __global__ __launch_bounds__(kThreads) void router_split_weights_kernel(
     const float* __restrict__ wg, const float* __restrict__ wn, int E, int E2, int E2pad, int d,
-    uint16_t* __restrict__ planes) {
-  const size_t n = (size_t)E2pad * d;
-  for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n;
-       i += (size_t)gridDim.x * kThreads) {
-    const int c = (int)(i / d), k = (int)(i % d);
-    float w = 0.f;
-    if (c < E) w = wg[(size_t)c * d + k];
-    else if (c < E2) w = wn[(size_t)(c - E) * d + k];
-    const uint16_t hi = moe::f32_to_bf16_bits(w);
-    const float r1 = w - moe::bf16_bits_to_f32(hi);
-    const uint16_t mid = moe::f32_to_bf16_bits(r1);
-    const float r2 = r1 - moe::bf16_bits_to_f32(mid);
-    planes[i] = hi;
-    planes[n + i] = mid;
-    planes[2 * n + i] = moe::f32_to_bf16_bits(r2);
+    uint16_t* __restrict__ planes, int N, int bm, int32_t* __restrict__ table) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    table[0] = 0;
+    table[1] = N;
+    table[2] = 0;
+    table[3] = (N + bm - 1) / bm;
   }
-}
-
-// One group of N rows: offsets = {0, N}, tile_start = {0, ceil(N / bm)}.
-__global__ void router_group_table_kernel(int N, int bm, int32_t* offsets, int32_t* tile_start) {
-  if (threadIdx.x == 0) {
-    offsets[0] = 0;
-    offsets[1] = N;
-    tile_start[0] = 0;
-    tile_start[1] = (N + bm - 1) / bm;
+  const size_t n = (size_t)E2pad * d, n4 = n / 4;
+  for (size_t i4 = (size_t)blockIdx.x * kThreads + threadIdx.x; i4 < n4;
+       i4 += (size_t)gridDim.x * kThreads) {
+    const size_t i = i4 * 4;
+    const int c = (int)(i / d), k = (int)(i % d);
+    f32x4_t w = {0.f, 0.f, 0.f, 0.f};
+    if (c < E) w = *(const f32x4_t*)(wg + (size_t)c * d + k);
+    else if (c < E2) w = *(const f32x4_t*)(wn + (size_t)(c - E) * d + k);
+    uint16_t hi[4], mid[4], lo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      hi[j] = moe::f32_to_bf16_bits(w[j]);
+      const float r1 = w[j] - moe::bf16_bits_to_f32(hi[j]);
+      mid[j] = moe::f32_to_bf16_bits(r1);
+      lo[j] = moe::f32_to_bf16_bits(r1 - moe::bf16_bits_to_f32(mid[j]));
+    }
+    auto pack = [](const uint16_t* v) {
+      return make_uint2((uint32_t)v[0] | ((uint32_t)v[1] << 16),
+                        (uint32_t)v[2] | ((uint32_t)v[3] << 16));
+    };
+    *(uint2*)(planes + i) = pack(hi);
+    *(uint2*)(planes + n + i) = pack(mid);
+    *(uint2*)(planes + 2 * n + i) = pack(lo);
   }
 }
 
@@ -325,7 +357,7 @@ RouterPlan plan_router(int N, int d, int E, int with_noise, bool x_bf16) {
     // enough K splits for ~512 workgroups, at most 8 (the select kernel sums
     // the split partials of every logit in order)
     int want = (512 + tiles - 1) / tiles;
-    want = want < 1 ? 1 : (want > 8 ? 8 : want);
+    want = want < 1 ? 1 : (want > kMaxSplits ? kMaxSplits : want);
     want = want > KT ? KT : want;
     const int steps = (KT + want - 1) / want;
     p.k_chunk = steps * 64;
@@ -337,7 +369,7 @@ RouterPlan plan_router(int N, int d, int E, int with_noise, bool x_bf16) {
   }
   p.raw_bytes = align256((size_t)p.nsplit * N * p.E2pad * sizeof(float));
   p.table_bytes = 256;
-  const size_t nblk = (size_t)(N + kTokPerBlock - 1) / kTokPerBlock;
+  const size_t nblk = (size_t)select_blocks(N);
   p.stat_bytes = align256(nblk * (E + 1) * sizeof(double));
   return p;
 }
@@ -360,7 +392,7 @@ moe_status router_launch(const moe_router_params* p, const void* x, moe_dtype x_
   const int noise = (!logits_in && p->w_noise) ? 1 : 0;
   // same effective d as the workspace check: no GEMM when logits come in
   const RouterPlan pl = plan_router(N, logits_in ? 0 : d, E, noise, x_dt == MOE_BF16);
-  const int nblk = (N + kTokPerBlock - 1) / kTokPerBlock;
+  const int nblk = select_blocks(N);
   char* ws = (char*)workspace;
   uint16_t* planes = (uint16_t*)ws;
   float* raw = (float*)(ws + pl.planes_bytes);
@@ -373,10 +405,11 @@ moe_status router_launch(const moe_router_params* p, const void* x, moe_dtype x_
     const int E2 = pl.E2;
     if (pl.mfma) {
       const size_t n = (size_t)pl.E2pad * d;
-      const int sgrid = (int)((n + kThreads - 1) / kThreads < 2048 ? (n + kThreads - 1) / kThreads : 2048);
+      const size_t sblk = (n / 4 + kThreads - 1) / kThreads;
+      const int sgrid = (int)(sblk < 2048 ? sblk : 2048);
       router_split_weights_kernel<<<sgrid, kThreads, 0, st>>>(w_gate, p->w_noise, E, E2,
-                                                              pl.E2pad, d, planes);
-      router_group_table_kernel<<<1, 64, 0, st>>>(N, kRouterBM, table, table + 2);
+                                                              pl.E2pad, d, planes, N, kRouterBM,
+                                                              table);
       moe_status s = launch_status("router weight split");
       if (s != MOE_OK) return s;
       using namespace moe_gemm;
@@ -446,6 +479,7 @@ moe_status router_launch(const moe_router_params* p, const void* x, moe_dtype x_
   a.gates = gates;
   a.logits_out = logits_out;
   a.partials = score_sums ? partials : nullptr;
+  a.tok_per_wave = select_tok_per_wave(N);
   if (E <= 64)
     router_select_kernel<1><<<nblk, kThreads, 0, st>>>(a);
   else if (E <= 128)
