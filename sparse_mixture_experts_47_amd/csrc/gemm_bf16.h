@@ -51,6 +51,12 @@ struct Args {
   const int32_t* offsets;     // [E+1]
   const int32_t* tile_start;  // [E+1]
   const int32_t* a_rows;      // row r of the product reads A row a_rows[r] (or r if null)
+  // rows of group e covered by this launch: [seg_begin[e], seg_end[e]), or
+  // [offsets[e], offsets[e+1]) when null; tile_e[mt] = group of M tile mt
+  // (binary search over tile_start when null)
+  const int32_t* seg_begin;
+  const int32_t* seg_end;
+  const int32_t* tile_e;
 };
 
 __device__ __forceinline__ float act_fn(int act, float v) {
@@ -86,6 +92,16 @@ __device__ __forceinline__ int tile_expert(const int32_t* ts, int E, int mt) {
 #endif
 #ifndef MOE_SCHED_GROUPS
 #define MOE_SCHED_GROUPS 0
+#endif
+#ifndef MOE_MFMA_ORDER
+#define MOE_MFMA_ORDER 0
+#endif
+#ifndef MOE_PINGPONG
+#define MOE_PINGPONG 0
+#endif
+// LDS bytes the stages of one tile may take
+#ifndef MOE_LDS_BUDGET
+#define MOE_LDS_BUDGET 147456
 #endif
 
 // LDS element offset of logical 16-byte chunk c of row r. BK = 32: 64-byte
@@ -143,9 +159,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
   const int mt = rem / g.group_n;
   const int nt = ng * g.group_n + (rem - mt * g.group_n);
   if (nt >= g.n_tiles_n || mt >= g.tile_start[g.E]) return;
-  const int e = tile_expert(g.tile_start, g.E, mt);
-  const int row0 = g.offsets[e] + (mt - g.tile_start[e]) * BM;
-  const int row_end = g.offsets[e + 1];
+  const int e = g.tile_e ? g.tile_e[mt] : tile_expert(g.tile_start, g.E, mt);
+  const int row0 = (g.seg_begin ? g.seg_begin[e] : g.offsets[e]) + (mt - g.tile_start[e]) * BM;
+  const int row_end = g.seg_end ? g.seg_end[e] : g.offsets[e + 1];
   const int n0 = nt * BN;
   const int K = g.K;
   const int k_begin = blockIdx.y * g.k_chunk;
@@ -235,6 +251,20 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
 #if MOE_MFMA_PRIO
     __builtin_amdgcn_s_setprio(1);
 #endif
+#if MOE_MFMA_ORDER
+    // A-fragment major: consecutive MFMAs share their A operand
+#pragma unroll
+    for (int p = 0; p < NA; ++p)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            f32x16_t& d = acc[EPI == EPI_GLU ? b : 0][i][j];
+            d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[p][i], f.b[b][j], d, 0, 0, 0);
+          }
+#else
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -246,58 +276,122 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
             f32x16_t& d = acc[EPI == EPI_GLU ? b : 0][i][j];
             d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[p][i], f.b[b][j], d, 0, 0, 0);
           }
+#endif
 #if MOE_MFMA_PRIO
     __builtin_amdgcn_s_setprio(0);
 #endif
   };
 
-  // Schedule per K tile kt (stage kt % NS), in two 16-wide halves:
-  //   read half 1 of tile kt; MFMAs on half 0;
-  //   wait for this wave's LDS reads and for tile kt+1's loads; barrier
-  //   (now no wave reads stage kt % NS any more, and tile kt+1 is visible);
-  //   issue the loads of tile kt+NS into stage kt % NS;
-  //   read half 0 of tile kt+1; MFMAs on half 1 of tile kt.
-  // LDS reads always run under the previous half's MFMAs, and the global
-  // loads run NS-1 to NS tiles ahead. sched_barrier keeps the compiler from
-  // moving MFMAs across the waits.
+  if constexpr (MOE_PINGPONG && NW == 8) {
+    if (KT > 0) {
+    // Ping-pong schedule. The 8 waves form two groups of four (one wave of
+    // each per SIMD) that run one phase apart: while one group issues the
+    // MFMAs of a cluster (CS K steps), the other reads the fragments of its
+    // next cluster from LDS and issues global loads, and every phase ends
+    // with a workgroup barrier. A SIMD's MFMA pipe is thus fed by one of its
+    // two waves in every phase, and a barrier costs only its own latency.
+    // Group 1 starts with an idle phase; cluster c of group q is read in
+    // phase 2c+q and multiplied in phase 2c+q+1.
+    // Stage rules: tile t+NS-1 is loaded into stage (t-1)%NS at the first
+    // read phase of tile t (every wave finished reading tile t-1 one phase
+    // earlier: reads end with lgkmcnt(0) before their phase barrier); each
+    // wave waits for its own loads of tile t+1 at the end of the phase just
+    // before group 0 first reads tile t+1 (group 0: its last multiply phase
+    // of tile t, group 1: its last read phase of tile t).
+    constexpr int CS = 2;                // K steps per cluster
+    static_assert(KK % CS == 0, "clusters per tile");
+    constexpr int CPT = KK / CS;
+    const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
+    Frags cf[CS];
 #pragma unroll
-  for (int j = 0; j < NS; ++j)
-    if (j < KT) issue(j, j);
-  Frags fr[2];
-  if (KT > 0) {
-    if (KT > NS - 1) wait_vmcnt<(NS - 1) * LPT>();
+    for (int j = 0; j < NS - 1; ++j)
+      if (j < KT) issue(j, j);
+    if (KT > NS - 2) wait_vmcnt<(NS - 2) * LPT>();
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    read_frags(fr[0], 0, 0);
-  }
-  for (int kt = 0; kt < KT; ++kt) {
+    if (grp == 1) __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    const int NC = KT * CPT;
+    for (int c = 0; c < NC; ++c) {
+      const int t = c / CPT, h = c - t * CPT;
+      // ---- read phase
+      if (h == 0 && t + NS - 1 < KT) issue(t + NS - 1, (t + NS - 1) % NS);
 #pragma unroll
-    for (int kk = 0; kk + 1 < KK; ++kk) {
-      read_frags(fr[(kk + 1) & 1], kt % NS, kk + 1);
-      mfma(fr[kk & 1]);
+      for (int s = 0; s < CS; ++s) read_frags(cf[s], t % NS, h * CS + s);
+      __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+      if (grp == 1 && h == CPT - 1 && t + 1 < KT) {
+        if (t + NS - 1 < KT) wait_vmcnt<(NS - 2) * LPT>();
+        else wait_vmcnt<0>();
+      }
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- multiply phase
+#if MOE_MFMA_PRIO
+      __builtin_amdgcn_s_setprio(1);
+#endif
+#pragma unroll
+      for (int s = 0; s < CS; ++s) mfma(cf[s]);
+#if MOE_MFMA_PRIO
+      __builtin_amdgcn_s_setprio(0);
+#endif
+      __builtin_amdgcn_sched_barrier(0);
+      if (grp == 0 && h == CPT - 1 && t + 1 < KT) {
+        if (t + NS - 1 < KT) wait_vmcnt<(NS - 2) * LPT>();
+        else wait_vmcnt<0>();
+      }
+      if (grp == 0 || c + 1 < NC) __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    }
+  } else {
+    // Schedule per K tile kt (stage kt % NS), in two 16-wide halves:
+    //   read half 1 of tile kt; MFMAs on half 0;
+    //   wait for this wave's LDS reads and for tile kt+1's loads; barrier
+    //   (now no wave reads stage kt % NS any more, and tile kt+1 is visible);
+    //   issue the loads of tile kt+NS into stage kt % NS;
+    //   read half 0 of tile kt+1; MFMAs on half 1 of tile kt.
+    // LDS reads always run under the previous half's MFMAs, and the global
+    // loads run NS-1 to NS tiles ahead. sched_barrier keeps the compiler from
+    // moving MFMAs across the waits.
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+      if (j < KT) issue(j, j);
+    Frags fr[2];
+    if (KT > 0) {
+      if (KT > NS - 1) wait_vmcnt<(NS - 1) * LPT>();
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      read_frags(fr[0], 0, 0);
+    }
+    for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+      for (int kk = 0; kk + 1 < KK; ++kk) {
+        read_frags(fr[(kk + 1) & 1], kt % NS, kk + 1);
+        mfma(fr[kk & 1]);
 #if MOE_SCHED_GROUPS
-      // all LDS reads of the next step go out before this step's MFMAs
+        // all LDS reads of the next step go out before this step's MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, NA * FM + NB * FN, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, NA * NB * FM * FN, 0);
+#endif
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // this wave's LDS reads of tile kt are done; tile kt+1 may still be
+      // followed by up to NS-2 younger tiles in flight
+      __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+      if (kt + NS - 1 < KT) wait_vmcnt<(NS - 2) * LPT>();
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + NS < KT) issue(kt + NS, kt % NS);
+      if (kt + 1 < KT) read_frags(fr[KK & 1], (kt + 1) % NS, 0);
+      mfma(fr[(KK - 1) & 1]);
+#if MOE_SCHED_GROUPS
+      __builtin_amdgcn_sched_group_barrier(0x020, LPT, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, NA * FM + NB * FN, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, NA * NB * FM * FN, 0);
 #endif
       __builtin_amdgcn_sched_barrier(0);
     }
-    // this wave's LDS reads of tile kt are done; tile kt+1 may still be
-    // followed by up to NS-2 younger tiles in flight
-    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
-    if (kt + NS - 1 < KT) wait_vmcnt<(NS - 2) * LPT>();
-    else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    if (kt + NS < KT) issue(kt + NS, kt % NS);
-    if (kt + 1 < KT) read_frags(fr[KK & 1], (kt + 1) % NS, 0);
-    mfma(fr[(KK - 1) & 1]);
-#if MOE_SCHED_GROUPS
-    __builtin_amdgcn_sched_group_barrier(0x020, LPT, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, NA * FM + NB * FN, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, NA * NB * FM * FN, 0);
-#endif
-    __builtin_amdgcn_sched_barrier(0);
   }
 
   constexpr int OB = OUTK == OUT_F32 ? 4 : 2;
@@ -366,7 +460,7 @@ template <int BM, int BN, int BK, int NA, int NB>
 constexpr int pick_stages() {
   constexpr int stage_bytes = (NA * BM + NB * BN) * BK * 2;
   constexpr int lpt = (NA * BM + NB * BN) * BK * 2 / 1024 / 4;  // with 4 waves
-  int ns = 147456 / stage_bytes;
+  int ns = MOE_LDS_BUDGET / stage_bytes;
   if (ns > 8) ns = 8;
   while (ns > 2 && (ns - 1) * lpt >= 64) --ns;
   return ns;
@@ -378,12 +472,13 @@ constexpr int pick_bk() {
   return pick_stages<BM, BN, BKP, NA, NB>() >= 2 ? BKP : 32;
 }
 
-template <int BM, int BN, int NA, int NB, int EPI, int OUTK, int WGN = 2, int BKP = MOE_GEMM_BK>
+template <int BM, int BN, int NA, int NB, int EPI, int OUTK, int WGN = 2, int BKP = MOE_GEMM_BK,
+          int WGM = 2>
 inline hipError_t run_gemm(const Args& g, int k_splits, hipStream_t st) {
   constexpr int bk = pick_bk<BM, BN, NA, NB, BKP>();
   constexpr int ns = pick_stages<BM, BN, bk, NA, NB>();
   static_assert(ns >= 2, "tile too large for two LDS stages");
-  return launch_dlds<BM, BN, bk, ns, 2, WGN, NA, NB, EPI, OUTK>(g, k_splits, st);
+  return launch_dlds<BM, BN, bk, ns, WGM, WGN, NA, NB, EPI, OUTK>(g, k_splits, st);
 }
 
 }  // namespace moe_gemm

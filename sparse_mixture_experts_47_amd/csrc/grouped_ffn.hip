@@ -33,24 +33,62 @@ __device__ __forceinline__ float act_fn(int act, float v) {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.f + __expf(-g)); }
 
-// tile_start[e] = sum over e' < e of ceil(count_e' / bm); tile_start[E] = total.
-__global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restrict__ offsets,
-                                                         int E, int bm,
-                                                         int32_t* __restrict__ tile_start) {
-  __shared__ int sc[256];
+// M tile tables. Expert e's rows [offsets[e], offsets[e+1]) are cut into
+// bm-row tiles: tile_start[e] = number of tiles of experts before e,
+// tile_start[E] = total. With split, the rows past an expert's last full
+// bm-row tile (split == 1), or only such a tail of at most bm/2 rows
+// (split == 2), go to a second table of bm/2-row tiles, so that an expert
+// just over a multiple of bm does not pay for a nearly empty bm-row tile.
+// Optional outputs (null to skip): seg_* = row range of each expert per
+// table, te* = expert of each tile (saves the per-block search).
+__global__ __launch_bounds__(256) void tile_table_kernel(
+    const int32_t* __restrict__ offsets, int E, int bm, int split, int32_t* __restrict__ ts,
+    int32_t* __restrict__ ts_r, int32_t* __restrict__ sb, int32_t* __restrict__ se,
+    int32_t* __restrict__ sb_r, int32_t* __restrict__ se_r, int32_t* __restrict__ te,
+    int32_t* __restrict__ te_r) {
+  __shared__ int sc[2][256];
   const int e = threadIdx.x;
-  int n = 0;
-  if (e < E) n = (offsets[e + 1] - offsets[e] + bm - 1) / bm;
-  sc[e] = n;
+  int n = 0, nr = 0, beg = 0, mid = 0, end = 0;
+  if (e < E) {
+    beg = offsets[e];
+    end = offsets[e + 1];
+    const int cnt = end - beg;
+    if (split) {
+      n = cnt / bm;
+      // split == 2: only a tail of at most bm/2 rows leaves the main table
+      if (split == 2 && cnt - n * bm > bm / 2) ++n;
+      mid = min(beg + n * bm, end);
+      nr = (end - mid + bm / 2 - 1) / (bm / 2);
+    } else {
+      n = (cnt + bm - 1) / bm;
+      mid = end;
+    }
+  }
+  sc[0][e] = n;
+  sc[1][e] = nr;
   __syncthreads();
   for (int o = 1; o < 256; o <<= 1) {
-    int v = e >= o ? sc[e - o] : 0;
+    const int v0 = e >= o ? sc[0][e - o] : 0, v1 = e >= o ? sc[1][e - o] : 0;
     __syncthreads();
-    sc[e] += v;
+    sc[0][e] += v0;
+    sc[1][e] += v1;
     __syncthreads();
   }
-  if (e < E) tile_start[e] = sc[e] - n;
-  if (e == E - 1) tile_start[E] = sc[e];
+  if (e < E) {
+    const int t0 = sc[0][e] - n, t1 = sc[1][e] - nr;
+    ts[e] = t0;
+    if (e == E - 1) ts[E] = sc[0][e];
+    if (ts_r) {
+      ts_r[e] = t1;
+      if (e == E - 1) ts_r[E] = sc[1][e];
+    }
+    if (sb) { sb[e] = beg; se[e] = mid; }
+    if (sb_r) { sb_r[e] = mid; se_r[e] = end; }
+    if (te)
+      for (int t = 0; t < n; ++t) te[t0 + t] = e;
+    if (te_r)
+      for (int t = 0; t < nr; ++t) te_r[t1 + t] = e;
+  }
 }
 
 struct GemmArgs {
@@ -518,19 +556,41 @@ __global__ __launch_bounds__(NW * 64) void ffn_fp8_stream_kernel(Fp8Args g,
   }
 }
 
+// N tiles per group of the XCD-aware tile order (measured on the Mixtral
+// shape: 2 and 4 tie for GEMM 1, 2 is best for GEMM 2)
 #ifndef MOE_GROUP_N
-#define MOE_GROUP_N 4
+#define MOE_GROUP_N 2
 #endif
-// GEMM 1 (SwiGLU, 256-row tiles) runs 8 waves (2 per SIMD); GEMM 2 uses
-// 256x128 tiles (MOE_G2_WIDE=1: 256x256)
+// average rows per expert from which 256-row M tiles are used
+#ifndef MOE_BM256_ROWS
+#define MOE_BM256_ROWS 512
+#endif
+// 256-row tiling: 1 = every expert's rows past its last full tile run as
+// 128-row tiles of a second launch, 2 = only tails of at most 128 rows do
+// (measured on the Mixtral shape: 2 is fastest, 1 slower than no split)
+#ifndef MOE_SPLIT_TAIL
+#define MOE_SPLIT_TAIL 2
+#endif
+// GEMM 1 (SwiGLU, 256-row tiles) runs 8 waves (2 per SIMD); GEMM 2 with
+// 256-row tiles uses 256x256 tiles on 8 waves (128x64 per wave): fewer LDS
+// fragment reads per MFMA than 256x128, faster than 4 waves of 128x128
 #ifndef MOE_G1_WGN
 #define MOE_G1_WGN 4
 #endif
 #ifndef MOE_G2_WIDE
-#define MOE_G2_WIDE 0
+#define MOE_G2_WIDE 1
 #endif
 #ifndef MOE_G2_WGN
 #define MOE_G2_WGN 4
+#endif
+#ifndef MOE_G2_WIDE_WGN
+#define MOE_G2_WIDE_WGN 4
+#endif
+#ifndef MOE_G2_WIDE_WGM
+#define MOE_G2_WIDE_WGM 2
+#endif
+#ifndef MOE_G1_WGM
+#define MOE_G1_WGM 2
 #endif
 
 moe_status gemm_status(hipError_t e, const char* what) {
@@ -614,50 +674,49 @@ hipError_t launch_stream(const Fp8Args& a, const int32_t* tile_start, int rows_c
   return hipGetLastError();
 }
 
-// GEMM 1 then GEMM 2 of the bf16 path for M tiles of BM rows. 128-column N
+// GEMM 1 and GEMM 2 of the bf16 path for M tiles of BM rows. 128-column N
 // tiles (GEMM 1: 128 columns of both W1 and W3), 64 when the width is not
-// a multiple of 128.
+// a multiple of 128; GEMM 2 with 256-row tiles takes 256-column tiles.
 template <int BM>
-hipError_t launch_ffn(bool glu, bool pair, bool ybf, const moe_gemm::Args& g1,
-                      const moe_gemm::Args& g2, hipStream_t st) {
+hipError_t launch_g1(bool glu, bool pair, const moe_gemm::Args& g1, hipStream_t st) {
   using namespace moe_gemm;
-  const bool n1 = g1.Nrows % 128 == 0, n2 = g2.Nrows % 128 == 0;
-  hipError_t e;
+  const bool n1 = g1.Nrows % 128 == 0;
   if (glu) {
     if (n1)
-      e = pair ? run_gemm<BM, 128, 1, 2, EPI_GLU, OUT_BF16_PAIR>(g1, 1, st)
-               : run_gemm<BM, 128, 1, 2, EPI_GLU, OUT_BF16, MOE_G1_WGN>(g1, 1, st);
-    else
-      e = pair ? run_gemm<BM, 64, 1, 2, EPI_GLU, OUT_BF16_PAIR>(g1, 1, st)
-               : run_gemm<BM, 64, 1, 2, EPI_GLU, OUT_BF16>(g1, 1, st);
-  } else {
-    if (n1)
-      e = pair ? run_gemm<BM, 128, 1, 1, EPI_ACT, OUT_BF16_PAIR>(g1, 1, st)
-               : run_gemm<BM, 128, 1, 1, EPI_ACT, OUT_BF16>(g1, 1, st);
-    else
-      e = pair ? run_gemm<BM, 64, 1, 1, EPI_ACT, OUT_BF16_PAIR>(g1, 1, st)
-               : run_gemm<BM, 64, 1, 1, EPI_ACT, OUT_BF16>(g1, 1, st);
+      return pair ? run_gemm<BM, 128, 1, 2, EPI_GLU, OUT_BF16_PAIR>(g1, 1, st)
+                  : run_gemm<BM, 128, 1, 2, EPI_GLU, OUT_BF16, MOE_G1_WGN, MOE_GEMM_BK,
+                             MOE_G1_WGM>(g1, 1, st);
+    return pair ? run_gemm<BM, 64, 1, 2, EPI_GLU, OUT_BF16_PAIR>(g1, 1, st)
+                : run_gemm<BM, 64, 1, 2, EPI_GLU, OUT_BF16>(g1, 1, st);
   }
-  if (e != hipSuccess) return e;
+  if (n1)
+    return pair ? run_gemm<BM, 128, 1, 1, EPI_ACT, OUT_BF16_PAIR>(g1, 1, st)
+                : run_gemm<BM, 128, 1, 1, EPI_ACT, OUT_BF16>(g1, 1, st);
+  return pair ? run_gemm<BM, 64, 1, 1, EPI_ACT, OUT_BF16_PAIR>(g1, 1, st)
+              : run_gemm<BM, 64, 1, 1, EPI_ACT, OUT_BF16>(g1, 1, st);
+}
+
+template <int BM>
+hipError_t launch_g2(bool pair, bool ybf, const moe_gemm::Args& g2, hipStream_t st) {
+  using namespace moe_gemm;
+  const bool n2 = g2.Nrows % 128 == 0;
   if (pair) {
     if (n2)
-      e = ybf ? run_gemm<BM, 128, 2, 1, EPI_OUT, OUT_BF16>(g2, 1, st)
-              : run_gemm<BM, 128, 2, 1, EPI_OUT, OUT_F32>(g2, 1, st);
-    else
-      e = ybf ? run_gemm<BM, 64, 2, 1, EPI_OUT, OUT_BF16>(g2, 1, st)
-              : run_gemm<BM, 64, 2, 1, EPI_OUT, OUT_F32>(g2, 1, st);
-  } else {
-    if (MOE_G2_WIDE && BM == 256 && g2.Nrows % 256 == 0)
-      e = ybf ? run_gemm<BM, 256, 1, 1, EPI_OUT, OUT_BF16>(g2, 1, st)
-              : run_gemm<BM, 256, 1, 1, EPI_OUT, OUT_F32>(g2, 1, st);
-    else if (n2)
-      e = ybf ? run_gemm<BM, 128, 1, 1, EPI_OUT, OUT_BF16, MOE_G2_WGN>(g2, 1, st)
-              : run_gemm<BM, 128, 1, 1, EPI_OUT, OUT_F32, MOE_G2_WGN>(g2, 1, st);
-    else
-      e = ybf ? run_gemm<BM, 64, 1, 1, EPI_OUT, OUT_BF16>(g2, 1, st)
-              : run_gemm<BM, 64, 1, 1, EPI_OUT, OUT_F32>(g2, 1, st);
+      return ybf ? run_gemm<BM, 128, 2, 1, EPI_OUT, OUT_BF16>(g2, 1, st)
+                 : run_gemm<BM, 128, 2, 1, EPI_OUT, OUT_F32>(g2, 1, st);
+    return ybf ? run_gemm<BM, 64, 2, 1, EPI_OUT, OUT_BF16>(g2, 1, st)
+               : run_gemm<BM, 64, 2, 1, EPI_OUT, OUT_F32>(g2, 1, st);
   }
-  return e;
+  if (MOE_G2_WIDE && BM == 256 && g2.Nrows % 256 == 0)
+    return ybf ? run_gemm<BM, 256, 1, 1, EPI_OUT, OUT_BF16, MOE_G2_WIDE_WGN, MOE_GEMM_BK,
+                          MOE_G2_WIDE_WGM>(g2, 1, st)
+               : run_gemm<BM, 256, 1, 1, EPI_OUT, OUT_F32, MOE_G2_WIDE_WGN, MOE_GEMM_BK,
+                          MOE_G2_WIDE_WGM>(g2, 1, st);
+  if (n2)
+    return ybf ? run_gemm<BM, 128, 1, 1, EPI_OUT, OUT_BF16, MOE_G2_WGN>(g2, 1, st)
+               : run_gemm<BM, 128, 1, 1, EPI_OUT, OUT_F32, MOE_G2_WGN>(g2, 1, st);
+  return ybf ? run_gemm<BM, 64, 1, 1, EPI_OUT, OUT_BF16>(g2, 1, st)
+             : run_gemm<BM, 64, 1, 1, EPI_OUT, OUT_F32>(g2, 1, st);
 }
 
 moe_gemm::Args base_args(const void* A, const void* B0, const void* B1, const float* bias,
@@ -694,8 +753,32 @@ static size_t h_bytes(const moe_ffn_weights* w, moe_dtype act_dt, int max_rows) 
   return align256((size_t)max_rows * w->d_ff * es);
 }
 
+// Tile tables after h (int32): tile_start and split-remainder tile_start
+// [E+1] each, segment bounds of both [E] x 4, then the tile -> expert maps
+// (main: at most max_rows/128 + E tiles, remainder: at most 2E).
+struct TileTables {
+  int32_t *ts, *ts_r, *sb, *se, *sb_r, *se_r, *te, *te_r;
+};
+static size_t table_ints(int E, int max_rows) {
+  return (size_t)6 * E + 2 + (size_t)(max_rows / 128 + E + 1) + 2 * (size_t)E;
+}
+static TileTables tile_tables(char* base, int E, int max_rows) {
+  int32_t* p = (int32_t*)base;
+  TileTables t;
+  t.ts = p;
+  t.ts_r = p + (E + 1);
+  t.sb = p + 2 * (E + 1);
+  t.se = t.sb + E;
+  t.sb_r = t.se + E;
+  t.se_r = t.sb_r + E;
+  t.te = t.se_r + E;
+  t.te_r = t.te + (max_rows / 128 + E + 1);
+  return t;
+}
+
 size_t grouped_ffn_workspace_bytes(const moe_ffn_weights* w, moe_dtype act_dt, int max_rows) {
-  return h_bytes(w, act_dt, max_rows) + align256((size_t)(w->n_experts + 1) * sizeof(int32_t));
+  return h_bytes(w, act_dt, max_rows) +
+         align256(table_ints(w->n_experts, max_rows) * sizeof(int32_t));
 }
 
 moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_dtype act_dt,
@@ -704,7 +787,8 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
   const int E = w->n_experts, d = w->d_model, F = w->d_ff;
   char* ws = (char*)workspace;
   void* h = ws;
-  int32_t* tile_start = (int32_t*)(ws + h_bytes(w, act_dt, max_rows));
+  const TileTables tt = tile_tables(ws + h_bytes(w, act_dt, max_rows), E, max_rows);
+  int32_t* tile_start = tt.ts;
   const bool glu = w->act == MOE_SWIGLU;
   moe_status s;
 
@@ -714,7 +798,8 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
     Fp8Args a2{(const uint16_t*)h, (const uint8_t*)w->w2, nullptr, w->s2, nullptr, y_rows,
                F, d, E, (int)w->act, offsets, nullptr};
     if (use_fp8_stream(E, d, F, max_rows)) {
-      tile_table_kernel<<<1, 256, 0, st>>>(offsets, E, 16, tile_start);
+      tile_table_kernel<<<1, 256, 0, st>>>(offsets, E, 16, 0, tile_start, nullptr, nullptr,
+                                           nullptr, nullptr, nullptr, nullptr, nullptr);
       s = launch_status("tile table");
       if (s != MOE_OK) return s;
       const int cap1 = row_index ? max_rows : 0;
@@ -741,9 +826,16 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
   }
 
   // 256-row M tiles when experts average at least 512 rows, else 128 rows
-  // (less padding in partly filled tiles)
-  const int bm = act_dt == MOE_F32 ? 64 : (max_rows / E >= 512 ? 256 : 128);
-  tile_table_kernel<<<1, 256, 0, st>>>(offsets, E, bm, tile_start);
+  // (less padding in partly filled tiles). With 256-row tiles, short tails
+  // of the experts run as a second launch of 128-row tiles.
+  const int bm = act_dt == MOE_F32 ? 64 : (max_rows / E >= MOE_BM256_ROWS ? 256 : 128);
+  const bool split = bm == 256 && MOE_SPLIT_TAIL;
+  if (act_dt == MOE_F32)
+    tile_table_kernel<<<1, 256, 0, st>>>(offsets, E, bm, 0, tt.ts, nullptr, nullptr, nullptr,
+                                         nullptr, nullptr, nullptr, nullptr);
+  else
+    tile_table_kernel<<<1, 256, 0, st>>>(offsets, E, bm, split ? MOE_SPLIT_TAIL : 0, tt.ts, tt.ts_r, tt.sb,
+                                         tt.se, tt.sb_r, tt.se_r, tt.te, tt.te_r);
   s = launch_status("tile table");
   if (s != MOE_OK) return s;
   const int max_mt = (max_rows + bm - 1) / bm + E;
@@ -764,15 +856,37 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
 
   using namespace moe_gemm;
   const bool pair = w->h_fp32 != 0;
+  const bool ybf = y_dt == MOE_BF16;
   Args g1 = base_args(x_rows, w->w1, w->w3, w->b1, h, d, F, E, max_mt, (int)w->act, offsets,
-                      tile_start);
+                      tt.ts);
   g1.a_rows = row_index;
+  g1.seg_begin = tt.sb;
+  g1.seg_end = tt.se;
+  g1.tile_e = tt.te;
   Args g2 = base_args(h, w->w2, nullptr, w->b2, y_rows, F, d, E, max_mt, (int)w->act, offsets,
-                      tile_start);
+                      tt.ts);
+  g2.seg_begin = tt.sb;
+  g2.seg_end = tt.se;
+  g2.tile_e = tt.te;
   g1.c_plane = (long long)max_rows * F;  // lo plane of the bf16 pair h
   g2.a_plane = (long long)max_rows * F;
-  const hipError_t err = bm == 256 ? launch_ffn<256>(glu, pair, y_dt == MOE_BF16, g1, g2, st)
-                                   : launch_ffn<128>(glu, pair, y_dt == MOE_BF16, g1, g2, st);
+  // remainder launches: same operands, the second table, 128-row tiles
+  Args g1r = g1, g2r = g2;
+  g1r.tile_start = g2r.tile_start = tt.ts_r;
+  g1r.seg_begin = g2r.seg_begin = tt.sb_r;
+  g1r.seg_end = g2r.seg_end = tt.se_r;
+  g1r.tile_e = g2r.tile_e = tt.te_r;
+  g1r.max_mt = g2r.max_mt = 2 * E;
+  hipError_t err;
+  if (bm == 256) {
+    err = launch_g1<256>(glu, pair, g1, st);
+    if (err == hipSuccess && split) err = launch_g1<128>(glu, pair, g1r, st);
+    if (err == hipSuccess) err = launch_g2<256>(pair, ybf, g2, st);
+    if (err == hipSuccess && split) err = launch_g2<128>(pair, ybf, g2r, st);
+  } else {
+    err = launch_g1<128>(glu, pair, g1, st);
+    if (err == hipSuccess) err = launch_g2<128>(pair, ybf, g2, st);
+  }
   return gemm_status(err, "grouped FFN GEMM");
 }
 

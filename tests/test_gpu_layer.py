@@ -420,3 +420,33 @@ def test_fp8_stream_and_row_group_paths(moe, gather):
         assert np.all(got[R:] == 7.0)
         outs.append(y[:R].clone())
     assert torch.equal(outs[0], outs[1])
+
+
+def test_grouped_ffn_256_row_tiles_with_tails(moe):
+    """Experts averaging over 512 rows take 256-row M tiles for their full
+    tiles and 128-row tiles for the rest; counts cover a multiple of 256 (no
+    tail), a 1-row tail, a tail of one and of two 128-row tiles, an expert
+    smaller than one tile and an empty one."""
+    cfg = W.REDUCED["c2"]
+    inp = W.make_inputs(cfg, "cpu")
+    host = host_inputs(inp)
+    dev = to_device(inp)
+    E = cfg.n_experts
+    counts = np.array([0, 768, 513, 1100, 700, 520, 1, 600])
+    assert len(counts) == E and counts.sum() >= 512 * E
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offs[-1])
+    rng = np.random.default_rng(5)
+    tok = rng.integers(0, cfg.n_tokens, size=R)
+    w, keep = moe.ffn_weights(dev["w1"], dev["w2"], dev["w3"], cfg.act, None, None)
+    y = torch.full((R + 3, cfg.d_model), 7.0, dtype=torch.float32, device="cuda")
+    moe.moe_grouped_ffn(w, dev["x"], torch.from_numpy(offs).cuda(), y,
+                        row_index=torch.from_numpy(tok.astype(np.int32)).cuda(), max_rows=R)
+    torch.cuda.synchronize()
+    X64 = oracle.decode_rows(host["x"][tok], cfg.x_dtype)
+    experts = np.repeat(np.arange(E), counts)
+    ref = oracle.ffn_for_assignments(np.arange(R), experts, X64, cfg.act, cfg.w_dtype,
+                                     experts_of(host))
+    got = to_np(y)
+    assert rel_err(got[:R], ref) <= out_tol(cfg)
+    assert np.all(got[R:] == 7.0)
