@@ -825,10 +825,15 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
     return launch_status("grouped FFN fp8 GEMM 2");
   }
 
-  // 256-row M tiles when experts average at least 512 rows, else 128 rows
-  // (less padding in partly filled tiles). With 256-row tiles, short tails
-  // of the experts run as a second launch of 128-row tiles.
-  const int bm = act_dt == MOE_F32 ? 64 : (max_rows / E >= MOE_BM256_ROWS ? 256 : 128);
+  // 256-row M tiles when experts average at least 512 rows, or at least 256
+  // with a long K (d_model >= 4096: each M tile streams the expert's weights,
+  // so fewer tiles per expert pay off), else 128 rows (less padding in
+  // partly filled tiles; measured faster with d_model = 1024). With 256-row
+  // tiles, short tails of the experts run as a second launch of 128-row tiles.
+  const int avg_rows = max_rows / E;
+  const int bm = act_dt == MOE_F32 ? 64
+                 : (avg_rows >= MOE_BM256_ROWS || (avg_rows >= 256 && d >= 4096)) ? 256
+                                                                                  : 128;
   const bool split = bm == 256 && MOE_SPLIT_TAIL;
   if (act_dt == MOE_F32)
     tile_table_kernel<<<1, 256, 0, st>>>(offsets, E, bm, 0, tt.ts, nullptr, nullptr, nullptr,
