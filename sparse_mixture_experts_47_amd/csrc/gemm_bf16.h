@@ -64,7 +64,12 @@ __device__ __forceinline__ float act_fn(int act, float v) {
   return 0.5f * v * (1.f + erff(v * 0.70710678118654752f));
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.f + __expf(-g)); }
+// silu(g) = g * sigmoid(g) with the hardware reciprocal (about 1 ulp): the
+// result is rounded to bf16 (or a bf16 hi/lo pair), so the correctly rounded
+// division this library is built with for its softmax is not needed here
+__device__ __forceinline__ float silu(float g) {
+  return g * __builtin_amdgcn_rcpf(1.f + __expf(-g));
+}
 
 __device__ __forceinline__ int tile_expert(const int32_t* ts, int E, int mt) {
   int lo = 0, hi = E;
