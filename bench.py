@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0,
                     help="tokens in the oracle's timed sample (0: choose by workload)")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="extra steps timed one by one after writing a 512 MiB buffer "
+                         "(evicts the 256 MB Infinity Cache); reported beside the warm run")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB read + 1 GiB write streaming kernel (torch.neg) "
                          "to calibrate the HBM byte counters")
@@ -140,7 +143,18 @@ def cpu_baseline(cfg, dev, sample_tokens):
     cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
     return {"value": S / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": "oracle layer forward (fp32 routing, fp64 FFN/combine) on the first %d "
-                      "tokens of the workload as one batch; %.1f s" % (S, dt)}
+                      "tokens of the workload as one batch; %.1f s; CPU: %s" % (S, dt, cpu_model())}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -191,8 +205,42 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    per = {n: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
-           for i, n in enumerate(names)}
+    samples = {n: [ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]
+               for i, n in enumerate(names)}
+    per = {n: float(np.mean(v)) for n, v in samples.items()}
+    layer_ev = [ev[s][0].elapsed_time(ev[s][len(names)]) for s in range(args.steps)]
+
+    # cold-cache steps: a 512 MiB write before each step evicts the 256 MB
+    # Infinity Cache; each step is timed on its own with events
+    cold = None
+    if args.cold_steps > 0:
+        evict = torch.empty(1 << 27, dtype=torch.float32, device="cuda")
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+               for _ in range(args.cold_steps)]
+        for s in range(args.cold_steps):
+            evict.fill_(float(s))
+            e = cev[s]
+            e[0].record(stream)
+            layer.start_shared(x)
+            layer.route(x)
+            e[1].record(stream)
+            layer.dispatch(x)
+            e[2].record(stream)
+            layer.experts(x)
+            e[3].record(stream)
+            layer.combine()
+            e[4].record(stream)
+            layer.stats()
+            e[5].record(stream)
+            torch.cuda.synchronize()
+        csamp = {n: [cev[s][i].elapsed_time(cev[s][i + 1]) for s in range(args.cold_steps)]
+                 for i, n in enumerate(names)}
+        clayer = [cev[s][0].elapsed_time(cev[s][len(names)]) for s in range(args.cold_steps)]
+        cold = {"steps": args.cold_steps, "evict_bytes": 4 << 27,
+                "ms_per_step_median": round(float(np.median(clayer)), 4),
+                "ms_per_step_min": round(float(np.min(clayer)), 4),
+                "per_call_ms_median": {k: round(float(np.median(v)), 4) for k, v in csamp.items()}}
+        del evict
     ms_step = elapsed * 1e3 / args.steps
     flops, wbytes, act_bytes = ffn_work(cfg, counts, touched)
     ffn_ms = per["grouped_ffn"]
@@ -231,6 +279,11 @@ def main():
                    "parallelism": "single-gpu"},
         "roofline": roof,
         "per_call_ms": {k: round(v, 4) for k, v in per.items()},
+        "per_call_ms_median": {k: round(float(np.median(v)), 4) for k, v in samples.items()},
+        "per_call_ms_min": {k: round(float(np.min(v)), 4) for k, v in samples.items()},
+        "layer_ms_events_median": round(float(np.median(layer_ev)), 4),
+        "layer_ms_events_min": round(float(np.min(layer_ev)), 4),
+        "cold_cache": cold,
         "grouped_ffn_tflops": round(tflops, 1),
         "layer_weight_gbs": round(layer_weight_bytes(cfg, touched) / (ms_step * 1e-3) / 1e9, 1),
         "layer_weight_frac_hbm": round(layer_weight_bytes(cfg, touched) / (ms_step * 1e-3) / 1e9
