@@ -26,6 +26,8 @@
 // share a few A row panels and B weight panels in that XCD's L2.
 #pragma once
 
+#include <type_traits>
+
 #include "moe_device.h"
 
 namespace moe_gemm {
@@ -101,6 +103,9 @@ __device__ __forceinline__ int tile_expert(const int32_t* ts, int E, int mt) {
 #ifndef MOE_MFMA_ORDER
 #define MOE_MFMA_ORDER 0
 #endif
+#ifndef MOE_SKIP_EMPTY
+#define MOE_SKIP_EMPTY 1
+#endif
 #ifndef MOE_PINGPONG
 #define MOE_PINGPONG 0
 #endif
@@ -169,6 +174,15 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
   const int row_end = g.seg_end ? g.seg_end[e] : g.offsets[e + 1];
   const int n0 = nt * BN;
   const int K = g.K;
+  // 32-row blocks of this wave's rows that hold at least one row of the
+  // group: the rest of a partly filled M tile needs no fragment reads and
+  // no MFMAs (uniform per wave)
+  // (256-row tiles only: with 128-row tiles the checked loop measured slower
+  // than computing the padding)
+  int nfm = FM;
+  if constexpr (MOE_SKIP_EMPTY && BM == 256)
+    nfm = __builtin_amdgcn_readfirstlane(
+        max(0, min(FM, (row_end - row0 - wm * WM + 31) / 32)));
   const int k_begin = blockIdx.y * g.k_chunk;
   const int k_end = min(K, k_begin + g.k_chunk);
   const int KT = (k_end - k_begin) / BK;
@@ -236,15 +250,18 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
     bf16x8_t a[NA][FM];
     bf16x8_t b[NB][FN];
   };
-  auto read_frags = [&](Frags& f, int stage, int kk) {
+  // `full`: std::true_type when every 32-row block of the wave is in use
+  // (no per-block checks in the generated loop)
+  auto read_frags = [&](Frags& f, int stage, int kk, auto full) {
     const uint16_t* cur = smem + stage * STAGE;
     const int c = kk * 2 + (lane >> 5);  // chunk of this lane's 8 K values
 #pragma unroll
     for (int p = 0; p < NA; ++p)
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        f.a[p][i] = *(const bf16x8_t*)(cur + p * A_PLANE +
-                                       dlds_off<BK>(wm * WM + i * 32 + (lane & 31), c));
+        if (decltype(full)::value || i < nfm)
+          f.a[p][i] = *(const bf16x8_t*)(cur + p * A_PLANE +
+                                         dlds_off<BK>(wm * WM + i * 32 + (lane & 31), c));
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -252,7 +269,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
         f.b[b][j] = *(const bf16x8_t*)(cur + NA * A_PLANE + b * B_PLANE +
                                        dlds_off<BK>(wn * WN + j * 32 + (lane & 31), c));
   };
-  auto mfma = [&](const Frags& f) {
+  auto mfma = [&](const Frags& f, auto full) {
 #if MOE_MFMA_PRIO
     __builtin_amdgcn_s_setprio(1);
 #endif
@@ -266,6 +283,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
         for (int b = 0; b < NB; ++b)
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
+            if (!decltype(full)::value && i >= nfm) continue;
             f32x16_t& d = acc[EPI == EPI_GLU ? b : 0][i][j];
             d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[p][i], f.b[b][j], d, 0, 0, 0);
           }
@@ -278,6 +296,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
         for (int p = 0; p < NA; ++p)
 #pragma unroll
           for (int i = 0; i < FM; ++i) {
+            if (!decltype(full)::value && i >= nfm) continue;
             f32x16_t& d = acc[EPI == EPI_GLU ? b : 0][i][j];
             d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[p][i], f.b[b][j], d, 0, 0, 0);
           }
@@ -322,7 +341,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
       // ---- read phase
       if (h == 0 && t + NS - 1 < KT) issue(t + NS - 1, (t + NS - 1) % NS);
 #pragma unroll
-      for (int s = 0; s < CS; ++s) read_frags(cf[s], t % NS, h * CS + s);
+      for (int s = 0; s < CS; ++s) read_frags(cf[s], t % NS, h * CS + s, std::true_type{});
       __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
       if (grp == 1 && h == CPT - 1 && t + 1 < KT) {
         if (t + NS - 1 < KT) wait_vmcnt<(NS - 2) * LPT>();
@@ -335,7 +354,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
       __builtin_amdgcn_s_setprio(1);
 #endif
 #pragma unroll
-      for (int s = 0; s < CS; ++s) mfma(cf[s]);
+      for (int s = 0; s < CS; ++s) mfma(cf[s], std::true_type{});
 #if MOE_MFMA_PRIO
       __builtin_amdgcn_s_setprio(0);
 #endif
@@ -358,45 +377,52 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
     // LDS reads always run under the previous half's MFMAs, and the global
     // loads run NS-1 to NS tiles ahead. sched_barrier keeps the compiler from
     // moving MFMAs across the waits.
+    // one instance for waves whose 32-row blocks are all in use, one with
+    // per-block checks (only the last M tile of a group can need it); both
+    // run the same barriers
+    auto k_loop = [&](auto full) {
 #pragma unroll
-    for (int j = 0; j < NS; ++j)
-      if (j < KT) issue(j, j);
-    Frags fr[2];
-    if (KT > 0) {
-      if (KT > NS - 1) wait_vmcnt<(NS - 1) * LPT>();
-      else wait_vmcnt<0>();
-      __builtin_amdgcn_s_barrier();
-      read_frags(fr[0], 0, 0);
-    }
-    for (int kt = 0; kt < KT; ++kt) {
+      for (int j = 0; j < NS; ++j)
+        if (j < KT) issue(j, j);
+      Frags fr[2];
+      if (KT > 0) {
+        if (KT > NS - 1) wait_vmcnt<(NS - 1) * LPT>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        read_frags(fr[0], 0, 0, full);
+      }
+      for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
-      for (int kk = 0; kk + 1 < KK; ++kk) {
-        read_frags(fr[(kk + 1) & 1], kt % NS, kk + 1);
-        mfma(fr[kk & 1]);
+        for (int kk = 0; kk + 1 < KK; ++kk) {
+          read_frags(fr[(kk + 1) & 1], kt % NS, kk + 1, full);
+          mfma(fr[kk & 1], full);
 #if MOE_SCHED_GROUPS
-        // all LDS reads of the next step go out before this step's MFMAs
+          // all LDS reads of the next step go out before this step's MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x100, NA * FM + NB * FN, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, NA * NB * FM * FN, 0);
+#endif
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // this wave's LDS reads of tile kt are done; tile kt+1 may still be
+        // followed by up to NS-2 younger tiles in flight
+        __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+        if (kt + NS - 1 < KT) wait_vmcnt<(NS - 2) * LPT>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + NS < KT) issue(kt + NS, kt % NS);
+        if (kt + 1 < KT) read_frags(fr[KK & 1], (kt + 1) % NS, 0, full);
+        mfma(fr[(KK - 1) & 1], full);
+#if MOE_SCHED_GROUPS
+        __builtin_amdgcn_sched_group_barrier(0x020, LPT, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, NA * FM + NB * FN, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, NA * NB * FM * FN, 0);
 #endif
         __builtin_amdgcn_sched_barrier(0);
       }
-      // this wave's LDS reads of tile kt are done; tile kt+1 may still be
-      // followed by up to NS-2 younger tiles in flight
-      __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
-      if (kt + NS - 1 < KT) wait_vmcnt<(NS - 2) * LPT>();
-      else wait_vmcnt<0>();
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      if (kt + NS < KT) issue(kt + NS, kt % NS);
-      if (kt + 1 < KT) read_frags(fr[KK & 1], (kt + 1) % NS, 0);
-      mfma(fr[(KK - 1) & 1]);
-#if MOE_SCHED_GROUPS
-      __builtin_amdgcn_sched_group_barrier(0x020, LPT, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, NA * FM + NB * FN, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, NA * NB * FM * FN, 0);
-#endif
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+    if (nfm == FM) k_loop(std::true_type{});
+    else k_loop(std::false_type{});
   }
 
   constexpr int OB = OUTK == OUT_F32 ? 4 : 2;

@@ -450,3 +450,33 @@ def test_grouped_ffn_256_row_tiles_with_tails(moe):
     got = to_np(y)
     assert rel_err(got[:R], ref) <= out_tol(cfg)
     assert np.all(got[R:] == 7.0)
+
+
+def test_grouped_ffn_256_row_tiles_partial_blocks(moe):
+    """Long-K experts averaging 256-511 rows run 256-row tiles without a
+    tail launch; the last tile's unused 32-row blocks skip their MFMAs.
+    Tails of 44, 1 and 254 rows, one expert of exactly 256, one empty."""
+    cfg = W.REDUCED["c2"].with_(name="long_k_256", n_tokens=600, d_model=4096, d_ff=256,
+                                n_experts=5)
+    inp = W.make_inputs(cfg, "cpu")
+    host = host_inputs(inp)
+    dev = to_device(inp)
+    E = cfg.n_experts
+    counts = np.array([300, 257, 0, 510, 256])
+    assert 256 <= counts.sum() // E < 512
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offs[-1])
+    rng = np.random.default_rng(9)
+    tok = rng.integers(0, cfg.n_tokens, size=R)
+    w, keep = moe.ffn_weights(dev["w1"], dev["w2"], dev["w3"], cfg.act, None, None)
+    y = torch.full((R + 3, cfg.d_model), 7.0, dtype=torch.float32, device="cuda")
+    moe.moe_grouped_ffn(w, dev["x"], torch.from_numpy(offs).cuda(), y,
+                        row_index=torch.from_numpy(tok.astype(np.int32)).cuda(), max_rows=R)
+    torch.cuda.synchronize()
+    X64 = oracle.decode_rows(host["x"][tok], cfg.x_dtype)
+    experts = np.repeat(np.arange(E), counts)
+    ref = oracle.ffn_for_assignments(np.arange(R), experts, X64, cfg.act, cfg.w_dtype,
+                                     experts_of(host))
+    got = to_np(y)
+    assert rel_err(got[:R], ref) <= out_tol(cfg)
+    assert np.all(got[R:] == 7.0)
