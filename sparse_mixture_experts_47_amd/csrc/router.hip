@@ -335,10 +335,15 @@ __global__ __launch_bounds__(kThreads) void router_sum_partials_kernel(
 namespace moe_host {
 
 namespace {
+// Router GEMM: 128-row M tiles, 64 columns of each of the three weight
+// planes, 4 waves, two 40 KB LDS stages so that two workgroups share a CU
+// (measured: 3 stages with one workgroup per CU, or 256-row tiles on 8
+// waves, are 1.2-1.6x slower for the DeepSeek-shaped router)
 constexpr int kRouterBM = 128;
 
 struct RouterPlan {
   bool mfma;
+  int bm;
   int E2, E2pad, bn, nsplit, k_chunk;
   size_t planes_bytes, raw_bytes, table_bytes, stat_bytes;
 };
@@ -349,10 +354,11 @@ RouterPlan plan_router(int N, int d, int E, int with_noise, bool x_bf16) {
   p.mfma = x_bf16 && d > 0 && d % 64 == 0;
   p.nsplit = 1;
   p.k_chunk = d;
+  p.bm = kRouterBM;
   if (p.mfma) {
     p.bn = 64;
     p.E2pad = (p.E2 + p.bn - 1) / p.bn * p.bn;
-    const int tiles = ((N + kRouterBM - 1) / kRouterBM) * (p.E2pad / p.bn);
+    const int tiles = ((N + p.bm - 1) / p.bm) * (p.E2pad / p.bn);
     const int KT = d / 64;
     // enough K splits for ~512 workgroups, at most 8 (the select kernel sums
     // the split partials of every logit in order)
@@ -408,7 +414,7 @@ moe_status router_launch(const moe_router_params* p, const void* x, moe_dtype x_
       const size_t sblk = (n / 4 + kThreads - 1) / kThreads;
       const int sgrid = (int)(sblk < 2048 ? sblk : 2048);
       router_split_weights_kernel<<<sgrid, kThreads, 0, st>>>(w_gate, p->w_noise, E, E2,
-                                                              pl.E2pad, d, planes, N, kRouterBM,
+                                                              pl.E2pad, d, planes, N, pl.bm,
                                                               table);
       moe_status s = launch_status("router weight split");
       if (s != MOE_OK) return s;
@@ -427,12 +433,13 @@ moe_status router_launch(const moe_router_params* p, const void* x, moe_dtype x_
       g.c_split = (long long)N * pl.E2pad;
       g.k_chunk = pl.k_chunk;
       g.E = 1;
-      g.max_mt = (N + kRouterBM - 1) / kRouterBM;
+      g.max_mt = (N + pl.bm - 1) / pl.bm;
       g.act = 0;
       g.group_n = 8;
       g.offsets = table;
       g.tile_start = table + 2;
-      hipError_t err = run_gemm<kRouterBM, 64, 1, 3, EPI_SUM, OUT_F32>(g, pl.nsplit, st);
+      const hipError_t err =
+          launch_dlds<kRouterBM, 64, 64, 2, 2, 2, 1, 3, EPI_SUM, OUT_F32>(g, pl.nsplit, st);
       if (err != hipSuccess) {
         set_error("router GEMM: launch failed: %s", hipGetErrorString(err));
         return MOE_EHIP;
