@@ -43,19 +43,34 @@ __global__ __launch_bounds__(kThreads) void disp_count_kernel(KeyArgs g, int E,
   for (int e = threadIdx.x; e < E; e += kThreads) blockcnt[(size_t)blockIdx.x * E + e] = hist[e];
 }
 
-// Exclusive scan over blocks for each expert, in block order.
+// Exclusive scan over blocks for each expert, in block order: one workgroup
+// per expert; thread t owns a contiguous run of blocks, the per-thread sums
+// are scanned across the workgroup, then each thread writes its run's
+// prefixes. Integer sums, so the order of additions does not matter.
 __global__ __launch_bounds__(kThreads) void disp_scan_kernel(int nblk, int E,
                                                              const int32_t* __restrict__ blockcnt,
                                                              int32_t* __restrict__ blockbase,
                                                              int32_t* __restrict__ total) {
-  for (int e = threadIdx.x; e < E; e += kThreads) {
-    int run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      blockbase[(size_t)b * E + e] = run;
-      run += blockcnt[(size_t)b * E + e];
-    }
-    total[e] = run;
+  __shared__ int sums[kThreads];
+  const int e = blockIdx.x, t = threadIdx.x;
+  const int chunk = (nblk + kThreads - 1) / kThreads;
+  const int b0 = t * chunk, b1 = min(nblk, b0 + chunk);
+  int local = 0;
+  for (int b = b0; b < b1; ++b) local += blockcnt[(size_t)b * E + e];
+  sums[t] = local;
+  __syncthreads();
+  for (int o = 1; o < kThreads; o <<= 1) {
+    const int v = t >= o ? sums[t - o] : 0;
+    __syncthreads();
+    sums[t] += v;
+    __syncthreads();
   }
+  int run = sums[t] - local;  // exclusive prefix of this thread's run
+  for (int b = b0; b < b1; ++b) {
+    blockbase[(size_t)b * E + e] = run;
+    run += blockcnt[(size_t)b * E + e];
+  }
+  if (t == kThreads - 1) total[e] = sums[t];
 }
 
 // Position of each item among the items with the same key, in item order,
@@ -228,7 +243,7 @@ moe_status dispatch_launch(int N, int E, int k, int C, moe_overflow policy, int 
 
   KeyArgs g1{N, k, C, 0, cand, nullptr, A};
   disp_count_kernel<<<nb, kThreads, 0, st>>>(g1, E, blockcnt);
-  disp_scan_kernel<<<1, kThreads, 0, st>>>(nb, E, blockcnt, blockbase, routed);
+  disp_scan_kernel<<<E, kThreads, 0, st>>>(nb, E, blockcnt, blockbase, routed);
   disp_rank_kernel<<<nb, kThreads, 0, st>>>(g1, E, ecap, blockbase, nullptr, slot1);
   moe_status s = launch_status("dispatch phase 1");
   if (s != MOE_OK) return s;
@@ -238,7 +253,7 @@ moe_status dispatch_launch(int N, int E, int k, int C, moe_overflow policy, int 
     KeyArgs g2{N, k, C, 1, cand, slot1, N};
     disp_kept1_kernel<<<1, kThreads, 0, st>>>(E, cap, routed, kept1);
     disp_count_kernel<<<nb2, kThreads, 0, st>>>(g2, E, blockcnt);
-    disp_scan_kernel<<<1, kThreads, 0, st>>>(nb2, E, blockcnt, blockbase, demand2);
+    disp_scan_kernel<<<E, kThreads, 0, st>>>(nb2, E, blockcnt, blockbase, demand2);
     disp_rank_kernel<<<nb2, kThreads, 0, st>>>(g2, E, cap, blockbase, kept1, slot2);
     s = launch_status("dispatch reroute phase");
     if (s != MOE_OK) return s;
