@@ -170,6 +170,32 @@ def route(logits, top_k, n_cand, renormalize, select_bias=None):
     return dict(s=s, cand_ids=cand, cand_scores=cand_s, gates=gates, lse=lse)
 
 
+def expert_choice(s, capacity):
+    """Expert-choice routing (heavensheep "Routing Function": experts choose
+    tokens, which balances the load by construction; "[CS336-04] Mixture of
+    Experts" section 3: the routing can be reversed so that experts select
+    tokens). Plain definition: expert e takes the min(capacity, N) tokens
+    with the largest router score s[t][e], ties to the lower token index; its
+    rows list those tokens in token order; the gate of a chosen (token,
+    expert) pair is s[t][e]. Returns dict(offsets [E+1], perm_token [E*cap],
+    row_of [N][E] (-1 = not chosen), gates [N][E] (0 = not chosen))."""
+    s = np.asarray(s, np.float32)
+    N, E = s.shape
+    cap = min(int(capacity), N)
+    offsets = (np.arange(E + 1) * cap).astype(np.int32)
+    perm = np.empty(E * cap, np.int32)
+    row_of = np.full((N, E), -1, np.int32)
+    gates = np.zeros((N, E), np.float32)
+    tok = np.arange(N)
+    for e in range(E):
+        order = np.lexsort((tok, -s[:, e].astype(np.float64)))  # score desc, then token asc
+        chosen = np.sort(order[:cap])
+        perm[e * cap:(e + 1) * cap] = chosen
+        row_of[chosen, e] = e * cap + np.arange(cap)
+        gates[chosen, e] = s[chosen, e]
+    return dict(offsets=offsets, perm_token=perm, row_of=row_of, gates=gates, capacity=cap)
+
+
 def dispatch(cand_ids, cand_scores, gates, n_experts, top_k, policy, capacity):
     cand = _c(cand_ids, np.int32)
     cs = _c(cand_scores, np.float32)
@@ -290,6 +316,8 @@ def layer_forward(cfg, x, x_dt, w_gate, experts: ExpertSource, shared: ExpertSou
         H, raw = router_logits(x, x_dt, w_gate, logit_bias, w_noise, cfg.noise_seed)
     else:
         H, raw = np.ascontiguousarray(logits, np.float32), None
+    if getattr(cfg, "expert_choice", False):
+        return _expert_choice_forward(cfg, x, x_dt, H, raw, experts, shared, tokens)
     r = route(H, cfg.top_k, cfg.n_cand, cfg.renormalize, select_bias)
     dsp = dispatch(r["cand_ids"], r["cand_scores"], r["gates"], cfg.n_experts, cfg.top_k,
                    cfg.overflow, cfg.capacity)
@@ -313,4 +341,33 @@ def layer_forward(cfg, x, x_dt, w_gate, experts: ExpertSource, shared: ExpertSou
                                   cfg.act, cfg.w_dtype, shared)
     y = combine(row_of, gates, Yexp, Ysh)
     return dict(logits=H, raw_logits=raw, route=r, dispatch=dsp, stats=st, y=y, rows=rows,
+                Yexp=Yexp, Ysh=Ysh)
+
+
+def _expert_choice_forward(cfg, x, x_dt, H, raw, experts, shared, tokens):
+    """Layer forward with expert-choice routing: softmax scores as for token
+    choice, every expert takes its `cfg.ec_capacity` top tokens, the FFNs run
+    on those rows, and a token's output sums gate x expert output over the
+    experts that chose it (in expert order), plus the shared expert."""
+    r = route(H, 1, 1, False)  # the full score matrix s; its top-1 is unused
+    ec = expert_choice(r["s"], cfg.ec_capacity)
+    E = cfg.n_experts
+    N = H.shape[0]
+    rows = np.arange(N) if tokens is None else np.asarray(tokens)
+    X64 = decode_rows(np.asarray(x)[rows], x_dt)
+    row_of = ec["row_of"][rows]
+    gates = ec["gates"][rows]
+    local_t, local_e = np.nonzero(row_of >= 0)
+    Yexp = np.zeros((len(rows), E, X64.shape[1]), np.float64)
+    if len(local_t):
+        Yexp[local_t, local_e] = ffn_for_assignments(local_t, local_e, X64, cfg.act,
+                                                     cfg.w_dtype, experts)
+    Ysh = None
+    if shared is not None:
+        Ysh = ffn_for_assignments(np.arange(len(rows)), np.zeros(len(rows), np.int64), X64,
+                                  cfg.act, cfg.w_dtype, shared)
+    y = combine(row_of, gates, Yexp, Ysh)
+    counts = np.full(E, ec["capacity"], np.int32)
+    st = balance_stats(cfg.top_k, counts, counts, r["s"], r["lse"])
+    return dict(logits=H, raw_logits=raw, route=r, ec=ec, stats=st, y=y, rows=rows,
                 Yexp=Yexp, Ysh=Ysh)

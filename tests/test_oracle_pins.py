@@ -484,3 +484,61 @@ def test_rank_major_capacity_order_hand_example():
         assert (d["gates"][t, j] == 0) == (row < 0)
     assert d["counts_kept"].tolist() == [int(v) for v in g["counts_kept"][0]]
     assert d["perm_token"].tolist() == [int(v) for v in g["perm_token"][0]]
+
+
+# ------------------------------------------------------------------ expert choice
+def _ec_rank_definition(s, cap):
+    """Chosen iff fewer than cap tokens beat it (higher score, or equal score
+    and lower index): the definition written out, no sorting."""
+    N, E = s.shape
+    chosen = np.zeros((N, E), bool)
+    for e in range(E):
+        for t in range(N):
+            better = sum(1 for u in range(N)
+                         if s[u, e] > s[t, e] or (s[u, e] == s[t, e] and u < t))
+            chosen[t, e] = better < cap
+    return chosen
+
+
+def test_expert_choice_matches_rank_definition_with_ties():
+    rng = np.random.default_rng(21)
+    for N, E, cap in [(7, 3, 2), (9, 2, 4), (5, 4, 5), (6, 3, 9), (8, 1, 1)]:
+        s = rng.integers(0, 3, size=(N, E)).astype(np.float32) / 4  # many ties
+        ec = oracle.expert_choice(s, cap)
+        want = _ec_rank_definition(s, min(cap, N))
+        assert np.array_equal(ec["row_of"] >= 0, want)
+        c = min(cap, N)
+        for e in range(E):
+            toks = np.nonzero(want[:, e])[0]  # token order
+            assert ec["perm_token"][e * c:(e + 1) * c].tolist() == toks.tolist()
+            assert ec["row_of"][toks, e].tolist() == list(range(e * c, (e + 1) * c))
+            assert np.array_equal(ec["gates"][toks, e], s[toks, e])
+        assert np.all(ec["gates"][~want] == 0)
+        assert ec["offsets"].tolist() == [e * c for e in range(E + 1)]
+
+
+def test_expert_choice_takes_every_token_when_capacity_reaches_n():
+    s = np.random.default_rng(2).random((10, 4)).astype(np.float32)
+    ec = oracle.expert_choice(s, 10)
+    assert np.all(ec["row_of"] >= 0) and np.array_equal(ec["gates"], s)
+
+
+def test_expert_choice_layer_equals_dense_masked_formula():
+    # y_t = sum_e [e chose t] s_te FFN_e(x_t), with the top-cap sets taken
+    # from a numpy argsort of the scores and FFNs from numpy matmuls
+    cfg = W.REDUCED["c6"].with_(n_tokens=48, d_model=64, d_ff=64)
+    inp, a = _small_layer(cfg)
+    out = oracle.layer_forward(cfg, a["x"], cfg.x_dtype, a["w_gate"], oracle.ExpertSource(a))
+    s = out["route"]["s"].astype(np.float64)
+    cap = cfg.ec_capacity
+    X = oracle.decode_rows(a["x"], cfg.x_dtype)
+    f = lambda w: oracle.bf16_to_f32(w).astype(np.float64)
+    ref = np.zeros_like(X)
+    for e in range(cfg.n_experts):
+        order = sorted(range(cfg.n_tokens), key=lambda t: (-s[t, e], t))[:cap]
+        G = np.zeros(cfg.n_tokens)
+        G[order] = s[order, e]
+        ref += G[:, None] * _np_ffn(X, oracle.SWIGLU, f(a["w1"][e]), f(a["w3"][e]), f(a["w2"][e]))
+    assert np.allclose(out["y"], ref, rtol=1e-12, atol=1e-12)
+    # balanced by construction: every expert holds exactly cap rows
+    assert np.all(np.diff(out["ec"]["offsets"]) == cap)

@@ -63,6 +63,9 @@ class MoEConfig:
     # keep the FFN intermediate h in fp32 (GEMM 2 as hi+lo bf16 passes); used
     # where the layer is bound by weight reads and MFMA time is spare
     h_fp32: bool = False
+    # expert-choice routing: every expert takes its top ec_capacity tokens
+    # (top_k then only sets the average, N * top_k = E * ec_capacity)
+    expert_choice: bool = False
 
     @property
     def n_cand(self) -> int:
@@ -77,6 +80,11 @@ class MoEConfig:
         if self.overflow == DROPLESS or self.capacity_factor is None:
             return -1
         return int(math.ceil(self.n_tokens * self.capacity_factor / self.n_experts - 1e-9))
+
+    @property
+    def ec_capacity(self) -> int:
+        """Tokens per expert under expert choice: ceil(N * top_k / E)."""
+        return -(-self.n_tokens * self.top_k // self.n_experts)
 
     def with_(self, **kw) -> "MoEConfig":
         return dataclasses.replace(self, **kw)
@@ -96,7 +104,11 @@ C4 = MoEConfig("switch_skewed_top1_capacity", 16384, 1024, 64, 4096, 1, ACT_GELU
 C5 = MoEConfig("deepseek_decode_fp8", 64, 7168, 256, 2048, 8, ACT_SWIGLU, BF16, FP8_E4M3,
                True, shared_d_ff=2048, seed=5, weight_seed=3)
 
-CONFIGS = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5}
+# Expert-choice variant of the Mixtral-shaped prefill: same shapes, every
+# expert takes N * 2 / 8 = 1024 tokens.
+C6 = C2.with_(name="mixtral_prefill_expert_choice", expert_choice=True, seed=6)
+
+CONFIGS = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5, "c6": C6}
 
 # Reduced shapes of the same recipes: small enough for the fp64 oracle to run
 # in seconds, large enough to span several GEMM tiles with ragged tails.
@@ -109,6 +121,7 @@ REDUCED = {
                    d_ff=512),
     "c5": C5.with_(name="deepseek_decode_reduced", n_tokens=24, d_model=512, n_experts=64,
                    d_ff=256, shared_d_ff=256),
+    "c6": C6.with_(name="expert_choice_reduced", n_tokens=600, d_model=512, d_ff=1024),
 }
 
 # tensor ids used to derive per-tensor seeds
