@@ -1,6 +1,6 @@
 """Benchmark: one MoE FFN layer forward per step on one MI355X, through libmoe.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4|c5]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4|c5|c6]
 
 A step is one pass of the whole layer: router GEMM + fp32 softmax + top-k,
 dispatch (capacity, packing, row gather), the grouped expert FFN (+ shared
@@ -34,7 +34,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "c6"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0,
                     help="tokens in the oracle's timed sample (0: choose by workload)")
@@ -276,6 +276,7 @@ def main():
                    "n_experts": cfg.n_experts, "d_ff": cfg.d_ff, "top_k": cfg.top_k,
                    "act": ["relu", "gelu", "swiglu"][cfg.act],
                    "shared_d_ff": cfg.shared_d_ff, "capacity": cfg.capacity,
+                   "routing": "expert_choice" if cfg.expert_choice else "token_choice",
                    "parallelism": "single-gpu"},
         "roofline": roof,
         "per_call_ms": {k: round(v, 4) for k, v in per.items()},
@@ -303,7 +304,8 @@ def main():
         out["copy_calibration_bytes"] = 4 * n
         del a, b
     if not args.no_cpu_baseline:
-        S = args.cpu_sample or {"c1": 256, "c2": 1024, "c3": 64, "c4": 4096, "c5": 64}[args.workload]
+        S = args.cpu_sample or {"c1": 256, "c2": 1024, "c3": 64, "c4": 4096, "c5": 64,
+                                  "c6": 1024}[args.workload]
         out["cpu_baseline"] = cpu_baseline(cfg, dev, S)
     print(json.dumps(out), flush=True)
 

@@ -103,6 +103,9 @@ typedef struct {
   const float* select_bias; /* [E] added to scores for selection only, or NULL */
   const float* w_noise;     /* [E][d] fp32 noise projection, or NULL */
   uint64_t noise_seed;
+  float* scores_out;        /* [N][E] fp32 out: every softmax score s_te (the
+                               values cand_scores takes them from), or NULL;
+                               the input of moe_expert_choice */
 } moe_router_params;
 
 /*  x          [N][d] activations, x_dt = MOE_F32 or MOE_BF16
@@ -162,6 +165,32 @@ size_t moe_dispatch_workspace_bytes(int32_t n_tokens, int32_t n_experts, int32_t
  * "专家容量": tokens per batch / number of experts x capacity factor; the
  * rounding up is this library's choice). Host function. */
 int32_t moe_capacity(int32_t n_tokens, int32_t n_experts, double capacity_factor);
+
+/* ---------------------------------------------------------------------- */
+/* moe_expert_choice                                                       */
+/* ---------------------------------------------------------------------- */
+/* Expert-choice routing: instead of every token picking its top-k experts,
+ * every expert picks its tokens, which balances the load by construction
+ * (heavensheep.xyz MoE notes, "Routing Function"; "[CS336-04] Mixture of
+ * Experts", section 3). Expert e takes cap = min(capacity, N) tokens: the
+ * ones with the largest score s_te, ties to the lower token index; its rows
+ * are those tokens in token order, rows e*cap .. e*cap+cap-1. The gate of a
+ * chosen (token, expert) pair is s_te; a token no expert chose gets 0 from
+ * the combine (the residual is the caller's).
+ *  scores     [N][E] fp32 (moe_router_params.scores_out)
+ *  offsets    [E+1] int32 out: e * cap
+ *  perm_token [E*cap] int32 out: token of each row (row_index of
+ *             moe_grouped_ffn)
+ *  row_of     [N][E] int32 out: row of (t, e), or -1 (moe_combine with
+ *             top_k = E)
+ *  gates      [N][E] fp32 out: s_te where chosen, else 0
+ *  counts     [E] int32 out (cap each), or NULL
+ * Errors: EINVAL for N < 1, capacity < 1, E outside [1, 256], N*E or E*cap
+ * of 2^31 or more, or a NULL required pointer. No workspace. */
+moe_status moe_expert_choice(int32_t n_tokens, int32_t n_experts, int32_t capacity,
+                             const float* scores, int32_t* offsets, int32_t* perm_token,
+                             int32_t* row_of, float* gates, int32_t* counts,
+                             void* hip_stream);
 
 /* ---------------------------------------------------------------------- */
 /* moe_grouped_ffn                                                         */
@@ -228,7 +257,9 @@ size_t moe_grouped_ffn_workspace_bytes(const moe_ffn_weights* w, moe_dtype act_d
  * assignments were all dropped gets 0 (+ shared): it skips the layer, the
  * residual add is the caller's.
  *  y_rows [R][d_model] (y_dt), row_of/gates [N][top_k], y_shared [N][d_model]
- *  (sh_dt) or NULL, y [N][d_model] out (out_dt). Dtypes: F32 or BF16. */
+ *  (sh_dt) or NULL, y [N][d_model] out (out_dt). Dtypes: F32 or BF16.
+ *  top_k in [1, 256]: up to 8 for token choice, up to E with the [N][E]
+ *  row_of/gates of moe_expert_choice (rows still summed in j order). */
 moe_status moe_combine(int32_t n_tokens, int32_t d_model, int32_t top_k, const void* y_rows,
                        moe_dtype y_dt, const int32_t* row_of, const float* gates,
                        const void* y_shared, moe_dtype sh_dt, void* y, moe_dtype out_dt,

@@ -42,7 +42,8 @@ class RouterParams(ctypes.Structure):
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("n_cand", ctypes.c_int32), ("renormalize", ctypes.c_int32),
                 ("logit_bias", ctypes.c_void_p), ("select_bias", ctypes.c_void_p),
-                ("w_noise", ctypes.c_void_p), ("noise_seed", ctypes.c_uint64)]
+                ("w_noise", ctypes.c_void_p), ("noise_seed", ctypes.c_uint64),
+                ("scores_out", ctypes.c_void_p)]
 
 
 class FFNWeights(ctypes.Structure):
@@ -78,6 +79,8 @@ def _load():
     L.moe_grouped_ffn_workspace_bytes.restype = sz
     L.moe_combine.argtypes = [i32, i32, i32, P, i32, P, P, P, i32, P, i32, P]
     L.moe_combine.restype = i32
+    L.moe_expert_choice.argtypes = [i32, i32, i32, P, P, P, P, P, P, P]
+    L.moe_expert_choice.restype = i32
     L.moe_balance_stats.argtypes = [i32, i32, i32, P, P, P, P, P, P, P, ctypes.c_float, P]
     L.moe_balance_stats.restype = i32
     L.moe_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
@@ -139,15 +142,18 @@ def workspace(nbytes: int, device) -> torch.Tensor:
 # --------------------------------------------------------------------- calls
 def moe_router_topk(x, w_gate, *, top_k, n_cand=None, renormalize=True, logit_bias=None,
                     select_bias=None, w_noise=None, noise_seed=0, logits_in=None, cand_ids,
-                    cand_scores, gates, logits_out=None, score_sums=None, ws=None,
-                    stream=None):
-    """Router GEMM + fp32 softmax + top-k. Outputs are written in place."""
+                    cand_scores, gates, logits_out=None, score_sums=None, scores_out=None,
+                    ws=None, stream=None):
+    """Router GEMM + fp32 softmax + top-k. Outputs are written in place;
+    scores_out [N][E] fp32 (optional) receives every softmax score."""
     N, E = cand_ids.shape[0], (w_gate.shape[0] if logits_in is None else logits_in.shape[1])
     d = x.shape[1] if x is not None else 0
     n_cand = n_cand or top_k
-    _dev_check(x, w_gate, logits_in, cand_ids, cand_scores, gates, logits_out, score_sums)
+    _dev_check(x, w_gate, logits_in, cand_ids, cand_scores, gates, logits_out, score_sums,
+               scores_out)
     p = RouterParams(N, d, E, top_k, n_cand, int(bool(renormalize)),
-                     _ptr(logit_bias), _ptr(select_bias), _ptr(w_noise), int(noise_seed))
+                     _ptr(logit_bias), _ptr(select_bias), _ptr(w_noise), int(noise_seed),
+                     _ptr(scores_out))
     if ws is None:
         ws = workspace(lib.moe_router_workspace_bytes(N, d, E, int(w_noise is not None)),
                        cand_ids.device)
@@ -172,6 +178,17 @@ def moe_dispatch(cand_ids, cand_scores, gates, *, n_experts, top_k, policy=DROPL
                             _ptr(counts_kept), _ptr(offsets), _ptr(row_of), _ptr(expert_of),
                             _ptr(perm_token), _ptr(x_perm), _ptr(ws), ws.numel(),
                             _stream(stream)))
+
+
+def moe_expert_choice(scores, capacity, *, offsets, perm_token, row_of, gates, counts=None,
+                      stream=None):
+    """Expert-choice selection: every expert takes its min(capacity, N)
+    top-scoring tokens, listed in token order."""
+    N, E = scores.shape
+    _dev_check(scores, offsets, perm_token, row_of, gates, counts)
+    _check(lib.moe_expert_choice(N, E, int(capacity), _ptr(scores), _ptr(offsets),
+                                 _ptr(perm_token), _ptr(row_of), _ptr(gates), _ptr(counts),
+                                 _stream(stream)))
 
 
 def ffn_weights(w1, w2, w3=None, act=SWIGLU, b1=None, b2=None, s1=None, s3=None, s2=None,
@@ -231,6 +248,8 @@ class LayerSpec:
     bias_rate: float = 1e-3
     shared_d_ff: int = 0
     h_fp32: bool = False
+    expert_choice: bool = False  # experts pick their ec_capacity top tokens
+    ec_capacity: int = 0
 
 
 class MoELayer:
@@ -239,6 +258,11 @@ class MoELayer:
 
     weights: dict with w_gate, logit_bias, select_bias, w_noise, w1, w3, w2,
     b1, b2, s1, s3, s2 and shared_{w1,w3,w2,s1,s3,s2} (device tensors/None).
+
+    With spec.expert_choice the router's full score matrix feeds
+    moe_expert_choice instead of moe_dispatch: every expert gets exactly
+    cap = min(ec_capacity, N) rows and a token sums over the experts that
+    chose it (combine with k = E).
     """
 
     def __init__(self, spec: LayerSpec, weights: dict, x_dtype=torch.bfloat16, device="cuda",
@@ -247,8 +271,17 @@ class MoELayer:
         self.w = weights
         self.dev = torch.device(device)
         N, E, k = s.n_tokens, s.n_experts, s.top_k
-        C = s.n_cand or k
+        self.ec = bool(s.expert_choice)
+        if self.ec:
+            if s.ec_capacity < 1:
+                raise ValueError("expert choice needs ec_capacity >= 1")
+            k = 1  # the router's own top-k is unused; its scores_out feeds the selection
+            self.cap = min(s.ec_capacity, N)
+        C = 1 if self.ec else (s.n_cand or k)
         self.C = C
+        # packed rows: N*k assignments (token choice) or E*cap (expert choice)
+        R = E * self.cap if self.ec else N * k
+        self.R = R
         dev = self.dev
         i32 = dict(dtype=torch.int32, device=dev)
         f32 = dict(dtype=torch.float32, device=dev)
@@ -260,18 +293,21 @@ class MoELayer:
         self.counts_routed = torch.empty(E, **i32)
         self.counts_kept = torch.empty(E, **i32)
         self.offsets = torch.empty(E + 1, **i32)
-        self.row_of = torch.empty((N, k), **i32)
-        self.expert_of = torch.empty((N, k), **i32)
-        self.perm_token = torch.empty(N * k, **i32)
+        self.row_of = torch.empty((N, E if self.ec else k), **i32)
+        self.expert_of = None if self.ec else torch.empty((N, k), **i32)
+        self.perm_token = torch.empty(R, **i32)
+        self.scores = torch.empty((N, E), **f32) if self.ec else None
+        self.ec_gates = torch.empty((N, E), **f32) if self.ec else None
         # fused_gather: GEMM 1 reads token rows through perm_token, so no
         # packed copy of x is made; otherwise dispatch gathers x_perm first
-        self.fused_gather = fused_gather
-        self.x_perm = (None if fused_gather else
-                       torch.empty((N * k, s.d_model), dtype=x_dtype, device=dev))
+        # (expert choice always reads through perm_token)
+        self.fused_gather = fused_gather or self.ec
+        self.x_perm = (None if self.fused_gather else
+                       torch.empty((R, s.d_model), dtype=x_dtype, device=dev))
         # Expert outputs and the layer output stay fp32: the only bf16
         # rounding on the path is the intermediate h inside the grouped FFN.
         ydt = torch.float32
-        self.y_rows = torch.empty((N * k, s.d_model), dtype=ydt, device=dev)
+        self.y_rows = torch.empty((R, s.d_model), dtype=ydt, device=dev)
         self.out_dtype = out_dtype or torch.float32
         self.y = torch.empty((N, s.d_model), dtype=self.out_dtype, device=dev)
         self.f = torch.empty(E, **f32)
@@ -300,22 +336,29 @@ class MoELayer:
         self.ws_router = workspace(lib.moe_router_workspace_bytes(N, s.d_model, E, noise), dev)
         self.ws_dispatch = workspace(lib.moe_dispatch_workspace_bytes(N, E, k), dev)
         self.ws_ffn = workspace(lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(self.ffn), xdt,
-                                                                    N * k), dev)
+                                                                    R), dev)
         if self.shared is not None:
             self.ws_shared = workspace(lib.moe_grouped_ffn_workspace_bytes(
                 ctypes.byref(self.shared), xdt, N), dev)
 
     def route(self, x, logits_in=None, stream=None):
         s, w = self.spec, self.w
-        moe_router_topk(x, w["w_gate"], top_k=s.top_k, n_cand=self.C,
-                        renormalize=s.renormalize, logit_bias=w.get("logit_bias"),
-                        select_bias=w.get("select_bias"), w_noise=w.get("w_noise"),
-                        noise_seed=s.noise_seed, logits_in=logits_in, cand_ids=self.cand_ids,
-                        cand_scores=self.cand_scores, gates=self.gates, logits_out=self.logits,
-                        score_sums=self.score_sums, ws=self.ws_router, stream=stream)
+        moe_router_topk(x, w["w_gate"], top_k=1 if self.ec else s.top_k, n_cand=self.C,
+                        renormalize=s.renormalize and not self.ec,
+                        logit_bias=w.get("logit_bias"),
+                        select_bias=None if self.ec else w.get("select_bias"),
+                        w_noise=w.get("w_noise"), noise_seed=s.noise_seed, logits_in=logits_in,
+                        cand_ids=self.cand_ids, cand_scores=self.cand_scores, gates=self.gates,
+                        logits_out=self.logits, score_sums=self.score_sums,
+                        scores_out=self.scores, ws=self.ws_router, stream=stream)
 
     def dispatch(self, x, stream=None):
         s = self.spec
+        if self.ec:
+            moe_expert_choice(self.scores, self.cap, offsets=self.offsets,
+                              perm_token=self.perm_token, row_of=self.row_of,
+                              gates=self.ec_gates, counts=self.counts_kept, stream=stream)
+            return
         moe_dispatch(self.cand_ids, self.cand_scores, self.gates, n_experts=s.n_experts,
                      top_k=s.top_k, policy=s.overflow, capacity=s.capacity, x=x,
                      counts_routed=self.counts_routed, counts_kept=self.counts_kept,
@@ -342,20 +385,21 @@ class MoELayer:
     def experts(self, x, stream=None):
         rows, index = self._packed_rows(x)
         moe_grouped_ffn(self.ffn, rows, self.offsets, self.y_rows, row_index=index,
-                        max_rows=self.spec.n_tokens * self.spec.top_k, ws=self.ws_ffn,
-                        stream=stream)
+                        max_rows=self.R, ws=self.ws_ffn, stream=stream)
         self.start_shared(x, stream)
 
     def combine(self, stream=None):
         if self.shared is not None:
             (stream or torch.cuda.current_stream()).wait_event(self.ev_shared)
             self._shared_pending = False
-        moe_combine(self.y_rows, self.row_of, self.gates, self.y,
+        moe_combine(self.y_rows, self.row_of, self.ec_gates if self.ec else self.gates, self.y,
                     y_shared=self.y_shared if self.shared is not None else None, stream=stream)
 
     def stats(self, update_bias=False, stream=None):
         s = self.spec
-        moe_balance_stats(s.n_tokens, s.top_k, self.counts_routed, self.counts_kept,
+        # expert choice: every expert is routed and keeps exactly cap rows
+        routed = self.counts_kept if self.ec else self.counts_routed
+        moe_balance_stats(s.n_tokens, s.top_k, routed, self.counts_kept,
                           self.score_sums, self.f, self.P, self.scalars,
                           select_bias=self.w.get("select_bias") if update_bias else None,
                           bias_rate=s.bias_rate, stream=stream)
@@ -375,4 +419,6 @@ def spec_from_config(cfg) -> LayerSpec:
     """LayerSpec from a workload config object (duck-typed)."""
     return LayerSpec(cfg.n_tokens, cfg.d_model, cfg.n_experts, cfg.d_ff, cfg.top_k, cfg.act,
                      cfg.renormalize, cfg.overflow, cfg.capacity, cfg.n_cand, cfg.noise_seed,
-                     1e-3, cfg.shared_d_ff, bool(getattr(cfg, "h_fp32", False)))
+                     1e-3, cfg.shared_d_ff, bool(getattr(cfg, "h_fp32", False)),
+                     bool(getattr(cfg, "expert_choice", False)),
+                     int(cfg.ec_capacity) if getattr(cfg, "expert_choice", False) else 0)

@@ -27,6 +27,9 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
 moe_status combine_launch(int N, int d, int k, const void* y_rows, moe_dtype y_dt,
                           const int32_t* row_of, const float* gates, const void* y_shared,
                           moe_dtype sh_dt, void* y, moe_dtype out_dt, hipStream_t st);
+moe_status expert_choice_launch(int N, int E, int capacity, const float* scores,
+                                int32_t* offsets, int32_t* perm_token, int32_t* row_of,
+                                float* gates, int32_t* counts, hipStream_t st);
 moe_status balance_stats_launch(int N, int E, int k, const int32_t* routed, const int32_t* kept,
                                 const double* sums, float* f, float* P, float* scalars,
                                 float* bias, float rate, hipStream_t st);
@@ -236,13 +239,29 @@ moe_status moe_combine(int32_t n_tokens, int32_t d_model, int32_t top_k, const v
   CHECK(n_tokens >= 1 && d_model >= 1 && top_k >= 1, MOE_EINVAL,
         "moe_combine: N=%d d=%d k=%d out of range", n_tokens, d_model, top_k);
   CHECK(y_rows && row_of && gates && y, MOE_EINVAL, "moe_combine: NULL argument");
-  CHECK(top_k <= 8, MOE_EUNSUPPORTED, "moe_combine: top_k %d > 8", top_k);
+  CHECK(top_k <= 256, MOE_EUNSUPPORTED, "moe_combine: top_k %d > 256", top_k);
   CHECK(d_model % 8 == 0, MOE_EUNSUPPORTED, "moe_combine: d_model %d not a multiple of 8", d_model);
   CHECK((y_dt == MOE_F32 || y_dt == MOE_BF16) && (out_dt == MOE_F32 || out_dt == MOE_BF16) &&
             (!y_shared || sh_dt == MOE_F32 || sh_dt == MOE_BF16),
         MOE_EUNSUPPORTED, "moe_combine: dtypes must be F32 or BF16");
   return combine_launch(n_tokens, d_model, top_k, y_rows, y_dt, row_of, gates, y_shared, sh_dt, y,
                         out_dt, (hipStream_t)hip_stream);
+}
+
+moe_status moe_expert_choice(int32_t n_tokens, int32_t n_experts, int32_t capacity,
+                             const float* scores, int32_t* offsets, int32_t* perm_token,
+                             int32_t* row_of, float* gates, int32_t* counts, void* hip_stream) {
+  CHECK(n_tokens >= 1 && capacity >= 1, MOE_EINVAL,
+        "moe_expert_choice: N=%d capacity=%d out of range", n_tokens, capacity);
+  CHECK(n_experts >= 1 && n_experts <= 256, MOE_EINVAL,
+        "moe_expert_choice: n_experts %d outside [1, 256]", n_experts);
+  const long long cap = capacity < n_tokens ? capacity : n_tokens;
+  CHECK((long long)n_tokens * n_experts < (1ll << 31) && cap * n_experts < (1ll << 31),
+        MOE_EINVAL, "moe_expert_choice: N*E or E*capacity too large");
+  CHECK(scores && offsets && perm_token && row_of && gates, MOE_EINVAL,
+        "moe_expert_choice: NULL argument");
+  return expert_choice_launch(n_tokens, n_experts, capacity, scores, offsets, perm_token, row_of,
+                              gates, counts, (hipStream_t)hip_stream);
 }
 
 moe_status moe_balance_stats(int32_t n_tokens, int32_t n_experts, int32_t top_k,

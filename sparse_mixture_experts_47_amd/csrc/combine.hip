@@ -43,7 +43,8 @@ struct Vec8<uint16_t> {
   }
 };
 
-// One block per token; each thread owns 8 consecutive features per pass.
+// One block per token; each thread owns 8 consecutive features per pass
+// (k <= 8: the token's rows and gates sit in registers).
 template <typename YT, typename ST, typename OT>
 __global__ __launch_bounds__(kThreads) void combine_kernel(int d, int k,
                                                            const YT* __restrict__ y_rows,
@@ -79,16 +80,75 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(int d, int k,
   }
 }
 
+// Wide form for k > 8 (expert-choice routing makes k = n_experts): the block
+// first packs the token's kept (row, gate) pairs into LDS in slot order, so
+// each feature chunk loops over kept rows only, with the same fma order as
+// combine_kernel.
+template <typename YT, typename ST, typename OT>
+__global__ __launch_bounds__(kThreads) void combine_wide_kernel(int d, int k,
+                                                                const YT* __restrict__ y_rows,
+                                                                const int32_t* __restrict__ row_of,
+                                                                const float* __restrict__ gates,
+                                                                const ST* __restrict__ ysh,
+                                                                OT* __restrict__ y) {
+  __shared__ int s_row[kThreads];
+  __shared__ float s_g[kThreads];
+  __shared__ int s_wave[kThreads / 64];
+  const int t = blockIdx.x, j = threadIdx.x, wave = j >> 6;
+  const int r = j < k ? row_of[(size_t)t * k + j] : -1;
+  const float gj = j < k ? gates[(size_t)t * k + j] : 0.f;
+  const uint64_t kept = __ballot(r >= 0);
+  if ((j & 63) == 0) s_wave[wave] = __popcll(kept);
+  __syncthreads();
+  int base = 0, n = 0;
+  for (int w = 0; w < kThreads / 64; ++w) {
+    base += w < wave ? s_wave[w] : 0;
+    n += s_wave[w];
+  }
+  if (r >= 0) {
+    const int pos = base + __popcll(kept & moe::lanemask_lt());
+    s_row[pos] = r;
+    s_g[pos] = gj;
+  }
+  __syncthreads();
+  for (int c = threadIdx.x * 8; c < d; c += kThreads * 8) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < n; ++q) {
+      float v[8];
+      Vec8<YT>::load(y_rows + (size_t)s_row[q] * d + c, v);
+      const float g = s_g[q];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(g, v[i], acc[i]);
+    }
+    if (ysh) {
+      float v[8];
+      Vec8<ST>::load(ysh + (size_t)t * d + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    Vec8<OT>::store(y + (size_t)t * d + c, acc);
+  }
+}
+
+template <typename YT, typename ST, typename OT>
+void launch_combine(int N, int d, int k, const void* yr, const int32_t* row_of,
+                    const float* gates, const void* ysh, void* y, hipStream_t st) {
+  if (k <= 8)
+    combine_kernel<YT, ST, OT><<<N, kThreads, 0, st>>>(d, k, (const YT*)yr, row_of, gates,
+                                                       (const ST*)ysh, (OT*)y);
+  else
+    combine_wide_kernel<YT, ST, OT><<<N, kThreads, 0, st>>>(d, k, (const YT*)yr, row_of, gates,
+                                                            (const ST*)ysh, (OT*)y);
+}
+
 template <typename YT, typename ST>
 moe_status dispatch_out(int N, int d, int k, const void* yr, const int32_t* row_of,
                         const float* gates, const void* ysh, void* y, moe_dtype out_dt,
                         hipStream_t st) {
   if (out_dt == MOE_BF16)
-    combine_kernel<YT, ST, uint16_t><<<N, kThreads, 0, st>>>(d, k, (const YT*)yr, row_of, gates,
-                                                             (const ST*)ysh, (uint16_t*)y);
+    launch_combine<YT, ST, uint16_t>(N, d, k, yr, row_of, gates, ysh, y, st);
   else
-    combine_kernel<YT, ST, float><<<N, kThreads, 0, st>>>(d, k, (const YT*)yr, row_of, gates,
-                                                          (const ST*)ysh, (float*)y);
+    launch_combine<YT, ST, float>(N, d, k, yr, row_of, gates, ysh, y, st);
   return moe_host::launch_status("combine");
 }
 

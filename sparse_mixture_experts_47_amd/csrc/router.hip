@@ -108,6 +108,7 @@ struct SelectArgs {
   float* cand_s;
   float* gates;
   float* logits_out;
+  float* scores_out;  // [N][E] softmax scores, or null
   double* partials;  // [gridDim.x][E+1] or null
   int tok_per_wave;
 };
@@ -204,6 +205,7 @@ __global__ __launch_bounds__(kThreads) void router_select_kernel(SelectArgs a) {
       const int e = lane + 64 * s;
       if (valid[s]) {
         sc[s] = u[s] / S;
+        if (a.scores_out) a.scores_out[(size_t)t * E + e] = sc[s];
         float kv = a.select_bias ? sc[s] + a.select_bias[e] : sc[s];
         if (kv == 0.0f) kv = 0.0f;
         key[s] = ((uint64_t)moe::orderable(kv) << 32) | (uint32_t)(0xFFFFu - (uint32_t)e);
@@ -485,6 +487,7 @@ moe_status router_launch(const moe_router_params* p, const void* x, moe_dtype x_
   a.cand_s = cand_scores;
   a.gates = gates;
   a.logits_out = logits_out;
+  a.scores_out = p->scores_out;
   a.partials = score_sums ? partials : nullptr;
   a.tok_per_wave = select_tok_per_wave(N);
   if (E <= 64)

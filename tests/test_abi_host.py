@@ -61,3 +61,19 @@ def test_validation_errors_before_any_launch(lib):
     assert L.moe_grouped_ffn(ctypes.byref(w), fake, 1, None, fake, 10, fake, 1, fake, 1 << 30,
                              None) == 2
     assert L.moe_status_string(3) == b"MOE_EWORKSPACE"
+
+
+def test_expert_choice_and_combine_validation(lib):
+    L = lib.lib
+    fake = ctypes.c_void_p(4096)
+    # capacity < 1, N < 1, E outside [1, 256], NULL required pointer
+    assert L.moe_expert_choice(16, 4, 0, fake, fake, fake, fake, fake, None, None) == 1
+    assert L.moe_expert_choice(0, 4, 2, fake, fake, fake, fake, fake, None, None) == 1
+    assert L.moe_expert_choice(16, 257, 2, fake, fake, fake, fake, fake, None, None) == 1
+    assert b"256" in L.moe_last_error()
+    assert L.moe_expert_choice(16, 4, 2, fake, fake, None, fake, fake, None, None) == 1
+    # N*E of 2^31 or more
+    assert L.moe_expert_choice(1 << 24, 256, 2, fake, fake, fake, fake, fake, None, None) == 1
+    # combine takes k up to 256 (expert choice combines over all experts)
+    assert L.moe_combine(4, 64, 257, fake, 1, fake, fake, None, 0, fake, 0, None) == 2
+    assert b"256" in L.moe_last_error()

@@ -84,3 +84,48 @@ def test_full_size_parity(moe, key):
     alike = np.all(ge == re, axis=1)
     if alike.any():
         assert rel_err(to_np(y2)[sample][alike], ref["y"][alike]) <= out_tol(cfg)
+
+
+def test_full_size_expert_choice(moe):
+    """Mixtral-shaped prefill with expert-choice routing: selection bit-exact
+    over all tokens from the oracle's logits, sampled outputs, statistics."""
+    cfg = W.CONFIGS["c6"]
+    print("full-size c6", cfg.name, flush=True)
+    torch.manual_seed(0)
+    dev = W.make_inputs(cfg, "cuda")
+    torch.cuda.synchronize()
+    hx = host_view(dev["x"])
+    hwg = host_view(dev["w_gate"])
+    hb = {k: host_view(dev[k]) for k in ("logit_bias", "select_bias", "w_noise")}
+    H, _ = oracle.router_logits(hx, cfg.x_dtype, hwg, hb["logit_bias"], hb["w_noise"],
+                                cfg.noise_seed)
+    layer = moe.MoELayer(moe.spec_from_config(cfg), dev, x_dtype=torch.bfloat16)
+    y = layer.forward(dev["x"], logits_in=torch.from_numpy(H).cuda()).clone()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    sample = np.sort(rng.choice(cfg.n_tokens, 12, replace=False))
+    ref = oracle.layer_forward(cfg, hx, cfg.x_dtype, hwg, DeviceExperts(dev), None,
+                               hb["logit_bias"], hb["select_bias"], hb["w_noise"], logits=H,
+                               tokens=sample)
+    ec = ref["ec"]
+    assert np.array_equal(to_np(layer.scores).view(np.uint32), ref["route"]["s"].view(np.uint32))
+    assert np.array_equal(to_np(layer.offsets), ec["offsets"])
+    assert np.array_equal(to_np(layer.perm_token), ec["perm_token"])
+    assert np.array_equal(to_np(layer.row_of), ec["row_of"])
+    assert np.array_equal(to_np(layer.ec_gates).view(np.uint32), ec["gates"].view(np.uint32))
+    err = rel_err(to_np(y)[sample], ref["y"])
+    print("  level-1 sampled max|dy|/rms =", err, " cap =", ec["capacity"], flush=True)
+    assert err <= out_tol(cfg)
+    st = ref["stats"]
+    assert np.allclose(to_np(layer.P), st["P"], rtol=TOL_REL, atol=1e-12)
+    sc = to_np(layer.scalars)
+    for i, name in enumerate(("switch_aux", "importance_cv2", "z_loss", "drop_rate")):
+        assert abs(sc[i] - st[name]) <= TOL_REL * abs(st[name]) + 1e-7, name
+    # level 2: the GPU's own router GEMM; pairs away from the thresholds agree
+    layer.forward(dev["x"])
+    torch.cuda.synchronize()
+    assert rel_err(to_np(layer.logits), H) <= TOL_REL
+    s = ref["route"]["s"].astype(np.float64)
+    thr = np.sort(s, axis=0)[::-1][ec["capacity"] - 1]
+    far = np.abs(s - thr[None, :]) >= MARGIN * thr[None, :]
+    assert np.all((to_np(layer.row_of) >= 0)[far] == (ec["row_of"] >= 0)[far])
