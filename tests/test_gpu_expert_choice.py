@@ -47,8 +47,9 @@ def _ec_gpu(moe, s, cap):
                                           (600, 8, 150, True), (1000, 64, 40, False),
                                           (3000, 8, 5000, False), (2049, 4, 2049, True),
                                           (65, 256, 1, False), (8192, 8, 2048, False),
-                                          (5000, 3, 1667, True)])
+                                          (5000, 3, 1667, True), (40000, 4, 10000, True)])
 def test_expert_choice_selection_bit_exact(moe, N, E, cap, ties):
+    # N = 40000 takes the kernel form that reads scores from global memory
     print("ec select", N, E, cap, ties, flush=True)
     s = _softmax_scores(N, E, N + E, ties)
     ref = oracle.expert_choice(s, cap)
