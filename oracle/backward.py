@@ -1,0 +1,195 @@
+"""CPU oracle for the backward pass of the MoE FFN layer -- TEST INFRASTRUCTURE.
+
+Only the tests and the benchmark's `cpu_baseline` leg may import this
+module; the product library never does and shares no code with it.
+
+What it differentiates. The layer forward of `oracle.layer_forward` with the
+discrete decisions (which experts a token selects, which assignments a
+capacity drops) held fixed, and the scalar
+
+    L = sum_t <dy_t, y_t> + alpha * switch_aux + beta * z_loss
+
+where dy is the upstream gradient, switch_aux = E * sum_e f_e * P_e with
+f_e = routed_e / (N k) a count (no gradient) and P_e = (1/N) sum_t s_te, and
+z_loss = (1/N) sum_t lse_t^2 over the logits the softmax sees.
+
+Passages. heavensheep.xyz MoE notes, section "Training": with top-k
+selection the experts a token did not select get zero gradient from the main
+loss, and the auxiliary loss of f_i and P_i is what gives the router of an
+unselected expert a gradient. mkbk-pku.cn, "通信与并行", step 5: the
+backward pass sends gradients back along the same routing path (expert
+output -> expert -> the token's position). chiang97912 MoE notes, "专家选择":
+y = sum_i G(x)_i E_i(x), so the gate and the expert output each take the
+other as the factor of their gradient. CS336 notes section 4: the z-loss.
+
+Everything here is plain fp64 numpy, written from the chain rule in the
+order the forward runs backwards:
+  combine -> (gate gradient, expert-output gradient)
+  expert FFN: W2, activation, W1/W3 (and biases) -> token-row gradient
+  gates -> scores (renormalisation Jacobian, or the Switch identity)
+  + auxiliary-loss term on the scores
+  softmax -> logits, + z-loss term on the logits
+  (noise: logits of the softmax -> raw logits and W_noise)
+  router GEMM -> W_g, logit bias and the token rows.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import (BF16, F32, FP8, GELU, RELU, SWIGLU, decode_rows, hash_normal_grid)
+
+
+def decode_weight(w, w_dt):
+    """Weights in storage form (fp32, or bf16 bits as uint16) -> fp64."""
+    if w is None:
+        return None
+    if w_dt == BF16:
+        return decode_rows(w, BF16)
+    if w_dt == F32:
+        return np.asarray(w, np.float32).astype(np.float64)
+    raise ValueError("the backward oracle covers fp32 and bf16 weights (fp8 is inference-only)")
+
+
+def _phi(a):
+    return np.exp(-0.5 * a * a) / np.sqrt(2.0 * np.pi)
+
+
+def _Phi(a):
+    from scipy.special import erf
+    return 0.5 * (1.0 + erf(a / np.sqrt(2.0)))
+
+
+def expert_backward(X, dO, act, w1, w3, w2, b1=None, b2=None):
+    """One expert on rows X [n][d] (fp64) with output gradient dO [n][d].
+    Forward: a = X W1^T (+b1); SwiGLU: u = X W3^T, h = silu(a) * u; ReLU /
+    GELU: h = act(a); o = h W2^T (+b2).
+    Returns dict(dX, dW1, dW3, dW2, db1, db2) in fp64 (dW3 None unless SwiGLU)."""
+    a = X @ w1.T
+    if b1 is not None:
+        a = a + b1
+    if act == SWIGLU:
+        sig = 1.0 / (1.0 + np.exp(-a))
+        u = X @ w3.T
+        h = a * sig * u
+    elif act == RELU:
+        h = np.maximum(a, 0.0)
+    else:  # GELU, exact erf form
+        h = a * _Phi(a)
+    dh = dO @ w2              # o = h W2^T  ->  dh = dO W2
+    dW2 = dO.T @ h            # dW2[c][f] = sum_rows dO[c] h[f]
+    db2 = dO.sum(axis=0) if b2 is not None else None
+    dW3 = None
+    if act == SWIGLU:
+        # h = silu(a) u: dh/da = u silu'(a), silu'(a) = sig (1 + a (1 - sig)); dh/du = silu(a)
+        da = dh * u * sig * (1.0 + a * (1.0 - sig))
+        du = dh * a * sig
+        dW3 = du.T @ X
+        dX = da @ w1 + du @ w3
+    elif act == RELU:
+        da = dh * (a > 0.0)
+        dX = da @ w1
+    else:
+        da = dh * (_Phi(a) + a * _phi(a))
+        dX = da @ w1
+    dW1 = da.T @ X
+    db1 = da.sum(axis=0) if b1 is not None else None
+    return dict(dX=dX, dW1=dW1, dW3=dW3, dW2=dW2, db1=db1, db2=db2)
+
+
+def layer_backward(cfg, x, x_dt, w_gate, experts, fwd, dy, alpha=0.0, beta=0.0,
+                   shared=None, logit_bias=None, w_noise=None):
+    """Gradients of L (module docstring) for a token-choice layer.
+
+    cfg, x, x_dt, w_gate, experts (an ExpertSource), shared, logit_bias and
+    w_noise are the forward's inputs; fwd is `oracle.layer_forward`'s result
+    over all tokens (its routing, dispatch and statistics are reused as the
+    fixed discrete decisions); dy [N][d] is the upstream gradient.
+    Returns dict with dx [N][d], dw_gate [E][d], dlogit_bias [E] (or None),
+    dw_noise [E][d] (or None), dl [N][E] (gradient of the logits the softmax
+    sees), dg [N][k] (gate gradients), ds [N][E] (score gradients) and, per
+    expert e, dW1/dW3/dW2/db1/db2 [E][...] (zeros for experts with no rows),
+    and the shared expert's dW (shared_dW1, ...)."""
+    if getattr(cfg, "expert_choice", False):
+        raise ValueError("the backward oracle covers token-choice routing")
+    X = decode_rows(x, x_dt)
+    N, d = X.shape
+    E, k = cfg.n_experts, cfg.top_k
+    dy = np.asarray(dy, np.float64)
+    r, dsp = fwd["route"], fwd["dispatch"]
+    row_of, exp_of = dsp["row_of"], dsp["expert_of"]
+    gates_used = dsp["gates"]   # the gate each kept assignment was scaled by
+    Yexp = fwd["Yexp"]          # [N][k][d] fp64 expert outputs (0 where dropped)
+
+    # ---- combine: y_t = sum_j g_tj o_tj (+ shared); kept slots only
+    kept = row_of >= 0
+    dg = np.where(kept, np.einsum("td,tjd->tj", dy, Yexp), 0.0)
+
+    # ---- experts (routed), grouped by expert
+    dX = np.zeros((N, d))
+    grads = {n: [] for n in ("dW1", "dW3", "dW2", "db1", "db2")}
+    for e in range(E):
+        tt, jj = np.nonzero(kept & (exp_of == e))
+        w = experts.get(e)
+        w1 = decode_weight(w["w1"], cfg.w_dtype)
+        w3 = decode_weight(w["w3"], cfg.w_dtype)
+        w2 = decode_weight(w["w2"], cfg.w_dtype)
+        b1 = None if w["b1"] is None else np.asarray(w["b1"], np.float64)
+        b2 = None if w["b2"] is None else np.asarray(w["b2"], np.float64)
+        dO = gates_used[tt, jj].astype(np.float64)[:, None] * dy[tt]
+        g = expert_backward(X[tt], dO, cfg.act, w1, w3, w2, b1, b2)
+        np.add.at(dX, tt, g["dX"])
+        for n in grads:
+            grads[n].append(g[n])
+    out = {n: (None if grads[n][0] is None else np.stack(grads[n])) for n in grads}
+
+    # ---- shared expert: gate 1 on every token
+    if shared is not None:
+        w = shared.get(0)
+        g = expert_backward(X, dy, cfg.act, decode_weight(w["w1"], cfg.w_dtype),
+                            decode_weight(w["w3"], cfg.w_dtype),
+                            decode_weight(w["w2"], cfg.w_dtype))
+        dX += g["dX"]
+        for n in ("dW1", "dW3", "dW2"):
+            out["shared_" + n] = g[n]
+
+    # ---- gates -> scores
+    s = r["s"].astype(np.float64)
+    ds = np.zeros((N, E))
+    if cfg.renormalize:
+        # g_j = s_{c_j} / S, S = sum over the k selected candidates:
+        # dL/ds_{c_i} = (dg_i - sum_j dg_j g_j) / S
+        cand = r["cand_ids"][:, :k]
+        sel = np.take_along_axis(s, cand, axis=1)
+        S = sel.sum(axis=1, keepdims=True)
+        gk = sel / S
+        ds_sel = (dg - (dg * gk).sum(axis=1, keepdims=True)) / S
+        np.put_along_axis(ds, cand, ds_sel, axis=1)
+    else:
+        # Switch gate: g = s of the expert actually used (after a reroute)
+        for j in range(k):
+            np.add.at(ds, (np.arange(N), exp_of[:, j]), np.where(kept[:, j], dg[:, j], 0.0))
+    # auxiliary loss: d(alpha E sum_e f_e P_e)/ds_te = alpha E f_e / N
+    f = dsp["counts_routed"].astype(np.float64) / (N * k)
+    ds += alpha * E * f[None, :] / N
+
+    # ---- softmax -> logits (+ z-loss: d(lse_t^2 / N)/dl_te = 2 lse_t s_te / N)
+    dl = s * (ds - (s * ds).sum(axis=1, keepdims=True))
+    dl += beta * 2.0 * r["lse"][:, None] * s / N
+
+    # ---- noise: H = l + z * softplus(v); dH/dl = 1, dH/dv = z * sigmoid(v)
+    wg = np.asarray(w_gate, np.float32).astype(np.float64)
+    dw_noise = None
+    dl_raw = dl
+    if w_noise is not None:
+        wn = np.asarray(w_noise, np.float32).astype(np.float64)
+        v = X @ wn.T
+        z = hash_normal_grid(cfg.noise_seed, N, E).astype(np.float64)
+        dv = dl * z / (1.0 + np.exp(-v))
+        dw_noise = dv.T @ X
+        dX += dv @ wn
+    # ---- router GEMM l = X W_g^T (+ b)
+    dX += dl_raw @ wg
+    out.update(dx=dX, dw_gate=dl_raw.T @ X,
+               dlogit_bias=None if logit_bias is None else dl_raw.sum(axis=0),
+               dw_noise=dw_noise, dl=dl, dg=dg, ds=ds)
+    return out
