@@ -63,7 +63,8 @@ def expert_backward(X, dO, act, w1, w3, w2, b1=None, b2=None):
     """One expert on rows X [n][d] (fp64) with output gradient dO [n][d].
     Forward: a = X W1^T (+b1); SwiGLU: u = X W3^T, h = silu(a) * u; ReLU /
     GELU: h = act(a); o = h W2^T (+b2).
-    Returns dict(dX, dW1, dW3, dW2, db1, db2) in fp64 (dW3 None unless SwiGLU)."""
+    Returns dict(dX, dW1, dW3, dW2, db1, db2) in fp64 (dW3 None unless SwiGLU)
+    and the intermediates a, u, h, dh, da, du (u, du None unless SwiGLU)."""
     a = X @ w1.T
     if b1 is not None:
         a = a + b1
@@ -72,13 +73,15 @@ def expert_backward(X, dO, act, w1, w3, w2, b1=None, b2=None):
         u = X @ w3.T
         h = a * sig * u
     elif act == RELU:
+        u = None
         h = np.maximum(a, 0.0)
     else:  # GELU, exact erf form
+        u = None
         h = a * _Phi(a)
     dh = dO @ w2              # o = h W2^T  ->  dh = dO W2
     dW2 = dO.T @ h            # dW2[c][f] = sum_rows dO[c] h[f]
     db2 = dO.sum(axis=0) if b2 is not None else None
-    dW3 = None
+    dW3 = du = None
     if act == SWIGLU:
         # h = silu(a) u: dh/da = u silu'(a), silu'(a) = sig (1 + a (1 - sig)); dh/du = silu(a)
         da = dh * u * sig * (1.0 + a * (1.0 - sig))
@@ -93,11 +96,12 @@ def expert_backward(X, dO, act, w1, w3, w2, b1=None, b2=None):
         dX = da @ w1
     dW1 = da.T @ X
     db1 = da.sum(axis=0) if b1 is not None else None
-    return dict(dX=dX, dW1=dW1, dW3=dW3, dW2=dW2, db1=db1, db2=db2)
+    return dict(dX=dX, dW1=dW1, dW3=dW3, dW2=dW2, db1=db1, db2=db2, a=a, u=u, h=h, dh=dh, da=da,
+                du=du)
 
 
 def layer_backward(cfg, x, x_dt, w_gate, experts, fwd, dy, alpha=0.0, beta=0.0,
-                   shared=None, logit_bias=None, w_noise=None):
+                   shared=None, logit_bias=None, w_noise=None, keep_terms=False):
     """Gradients of L (module docstring) for a token-choice layer.
 
     cfg, x, x_dt, w_gate, experts (an ExpertSource), shared, logit_bias and
@@ -108,7 +112,9 @@ def layer_backward(cfg, x, x_dt, w_gate, experts, fwd, dy, alpha=0.0, beta=0.0,
     dw_noise [E][d] (or None), dl [N][E] (gradient of the logits the softmax
     sees), dg [N][k] (gate gradients), ds [N][E] (score gradients) and, per
     expert e, dW1/dW3/dW2/db1/db2 [E][...] (zeros for experts with no rows),
-    and the shared expert's dW (shared_dW1, ...)."""
+    and the shared expert's dW (shared_dW1, ...). keep_terms: also
+    `terms`, per expert dict(tokens, slots, X, dO, w1, w3, w2, a, u, h, dh,
+    da, du): its rows' token and slot indices and fp64 intermediates."""
     if getattr(cfg, "expert_choice", False):
         raise ValueError("the backward oracle covers token-choice routing")
     X = decode_rows(x, x_dt)
@@ -127,6 +133,7 @@ def layer_backward(cfg, x, x_dt, w_gate, experts, fwd, dy, alpha=0.0, beta=0.0,
     # ---- experts (routed), grouped by expert
     dX = np.zeros((N, d))
     grads = {n: [] for n in ("dW1", "dW3", "dW2", "db1", "db2")}
+    terms = []
     for e in range(E):
         tt, jj = np.nonzero(kept & (exp_of == e))
         w = experts.get(e)
@@ -140,7 +147,12 @@ def layer_backward(cfg, x, x_dt, w_gate, experts, fwd, dy, alpha=0.0, beta=0.0,
         np.add.at(dX, tt, g["dX"])
         for n in grads:
             grads[n].append(g[n])
+        if keep_terms:
+            terms.append(dict(tokens=tt, slots=jj, X=X[tt], dO=dO, w1=w1, w3=w3, w2=w2,
+                              **{n: g[n] for n in ("a", "u", "h", "dh", "da", "du")}))
     out = {n: (None if grads[n][0] is None else np.stack(grads[n])) for n in grads}
+    if keep_terms:
+        out["terms"] = terms
 
     # ---- shared expert: gate 1 on every token
     if shared is not None:
@@ -152,7 +164,28 @@ def layer_backward(cfg, x, x_dt, w_gate, experts, fwd, dy, alpha=0.0, beta=0.0,
         for n in ("dW1", "dW3", "dW2"):
             out["shared_" + n] = g[n]
 
-    # ---- gates -> scores
+    rb = router_backward(cfg, X, w_gate, fwd, dg, alpha, beta, logit_bias, w_noise)
+    dX += rb.pop("dx")
+    out.update(rb)
+    out["dx"] = dX
+    out["dg"] = dg
+    return out
+
+
+def router_backward(cfg, X, w_gate, fwd, dg, alpha=0.0, beta=0.0, logit_bias=None,
+                    w_noise=None):
+    """Router part of the backward pass for given gate gradients dg [N][k]
+    (fp64; 0 for dropped slots): gates -> scores (+ auxiliary loss) ->
+    logits (+ z-loss) -> (noise) -> W_g, logit bias and the token rows X
+    (fp64 [N][d]). fwd gives the forward's route (s, lse, cand_ids) and
+    dispatch (expert_of, row_of, counts_routed). Returns dict(ds, dl, dw_gate,
+    dlogit_bias, dw_noise, dx) with dx the router's share of the token
+    gradient."""
+    r, dsp = fwd["route"], fwd["dispatch"]
+    N, E, k = X.shape[0], cfg.n_experts, cfg.top_k
+    kept = dsp["row_of"] >= 0
+    exp_of = dsp["expert_of"]
+    dg = np.where(kept, np.asarray(dg, np.float64), 0.0)
     s = r["s"].astype(np.float64)
     ds = np.zeros((N, E))
     if cfg.renormalize:
@@ -167,29 +200,28 @@ def layer_backward(cfg, x, x_dt, w_gate, experts, fwd, dy, alpha=0.0, beta=0.0,
     else:
         # Switch gate: g = s of the expert actually used (after a reroute)
         for j in range(k):
-            np.add.at(ds, (np.arange(N), exp_of[:, j]), np.where(kept[:, j], dg[:, j], 0.0))
+            np.add.at(ds, (np.arange(N), np.maximum(exp_of[:, j], 0)), dg[:, j])
     # auxiliary loss: d(alpha E sum_e f_e P_e)/ds_te = alpha E f_e / N
     f = dsp["counts_routed"].astype(np.float64) / (N * k)
     ds += alpha * E * f[None, :] / N
 
-    # ---- softmax -> logits (+ z-loss: d(lse_t^2 / N)/dl_te = 2 lse_t s_te / N)
+    # softmax -> logits (+ z-loss: d(lse_t^2 / N)/dl_te = 2 lse_t s_te / N)
     dl = s * (ds - (s * ds).sum(axis=1, keepdims=True))
     dl += beta * 2.0 * r["lse"][:, None] * s / N
 
-    # ---- noise: H = l + z * softplus(v); dH/dl = 1, dH/dv = z * sigmoid(v)
+    # noise: H = l + z * softplus(v); dH/dl = 1, dH/dv = z * sigmoid(v)
     wg = np.asarray(w_gate, np.float32).astype(np.float64)
+    dx = np.zeros_like(X)
     dw_noise = None
-    dl_raw = dl
     if w_noise is not None:
         wn = np.asarray(w_noise, np.float32).astype(np.float64)
         v = X @ wn.T
         z = hash_normal_grid(cfg.noise_seed, N, E).astype(np.float64)
         dv = dl * z / (1.0 + np.exp(-v))
         dw_noise = dv.T @ X
-        dX += dv @ wn
-    # ---- router GEMM l = X W_g^T (+ b)
-    dX += dl_raw @ wg
-    out.update(dx=dX, dw_gate=dl_raw.T @ X,
-               dlogit_bias=None if logit_bias is None else dl_raw.sum(axis=0),
-               dw_noise=dw_noise, dl=dl, dg=dg, ds=ds)
-    return out
+        dx += dv @ wn
+    # router GEMM l = X W_g^T (+ b)
+    dx += dl @ wg
+    return dict(ds=ds, dl=dl, dw_gate=dl.T @ X,
+                dlogit_bias=None if logit_bias is None else dl.sum(axis=0),
+                dw_noise=dw_noise, dx=dx)

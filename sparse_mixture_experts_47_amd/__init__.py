@@ -81,6 +81,21 @@ def _load():
     L.moe_combine.restype = i32
     L.moe_expert_choice.argtypes = [i32, i32, i32, P, P, P, P, P, P, P]
     L.moe_expert_choice.restype = i32
+    L.moe_grouped_ffn_train.argtypes = [ctypes.POINTER(FFNWeights), P, P, P, i32, P, i32, P, P,
+                                        P, sz, P]
+    L.moe_grouped_ffn_train.restype = i32
+    L.moe_grouped_ffn_backward_workspace_bytes.argtypes = [ctypes.POINTER(FFNWeights), i32, i32]
+    L.moe_grouped_ffn_backward_workspace_bytes.restype = sz
+    L.moe_grouped_ffn_backward.argtypes = [ctypes.POINTER(FFNWeights), P, P, P, i32, P, P, P, P,
+                                           P, P, P, P, sz, P]
+    L.moe_grouped_ffn_backward.restype = i32
+    L.moe_combine_backward.argtypes = [i32, i32, i32, P, P, i32, P, P, P, P, P]
+    L.moe_combine_backward.restype = i32
+    L.moe_router_backward_workspace_bytes.argtypes = [i32, i32, i32]
+    L.moe_router_backward_workspace_bytes.restype = sz
+    L.moe_router_backward.argtypes = [ctypes.POINTER(RouterParams), P, i32, P, P, P, P, P, P, P,
+                                      ctypes.c_float, ctypes.c_float, P, P, P, P, P, P, sz, P]
+    L.moe_router_backward.restype = i32
     L.moe_balance_stats.argtypes = [i32, i32, i32, P, P, P, P, P, P, P, ctypes.c_float, P]
     L.moe_balance_stats.restype = i32
     L.moe_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
@@ -231,6 +246,63 @@ def moe_balance_stats(n_tokens, top_k, counts_routed, counts_kept, score_sums, f
                                  _ptr(select_bias), float(bias_rate), _stream(stream)))
 
 
+# ------------------------------------------------------------------ training
+def moe_grouped_ffn_train(weights: FFNWeights, x_rows, offsets, y_rows, preact, h, *,
+                          row_index=None, max_rows=None, ws=None, stream=None):
+    """Grouped FFN forward that also saves the pre-activations [R][2 d_ff]
+    and h [R][d_ff] (bf16) for the backward pass."""
+    _dev_check(x_rows, offsets, y_rows, preact, h, row_index)
+    max_rows = max_rows or (row_index.shape[0] if row_index is not None else x_rows.shape[0])
+    if ws is None:
+        ws = workspace(lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(weights), BF16,
+                                                           max_rows), x_rows.device)
+    _check(lib.moe_grouped_ffn_train(ctypes.byref(weights), _ptr(x_rows), _ptr(row_index),
+                                     _ptr(offsets), max_rows, _ptr(y_rows), _dt(y_rows),
+                                     _ptr(preact), _ptr(h), _ptr(ws), ws.numel(),
+                                     _stream(stream)))
+
+
+def moe_combine_backward(dy, y_rows, row_of, gates, d_rows, dgates, *, stream=None):
+    N, k = row_of.shape
+    _dev_check(dy, y_rows, row_of, gates, d_rows, dgates)
+    _check(lib.moe_combine_backward(N, dy.shape[1], k, _ptr(dy), _ptr(y_rows), _dt(y_rows),
+                                    _ptr(row_of), _ptr(gates), _ptr(d_rows), _ptr(dgates),
+                                    _stream(stream)))
+
+
+def moe_grouped_ffn_backward(weights: FFNWeights, x_rows, offsets, preact, h, d_rows, dx_rows,
+                             dw1, dw3, dw2, *, row_index=None, max_rows=None, ws=None,
+                             stream=None):
+    _dev_check(x_rows, offsets, preact, h, d_rows, dx_rows, dw1, dw3, dw2, row_index)
+    max_rows = max_rows or d_rows.shape[0]
+    if ws is None:
+        ws = workspace(lib.moe_grouped_ffn_backward_workspace_bytes(
+            ctypes.byref(weights), max_rows, int(row_index is not None)), x_rows.device)
+    _check(lib.moe_grouped_ffn_backward(ctypes.byref(weights), _ptr(x_rows), _ptr(row_index),
+                                        _ptr(offsets), max_rows, _ptr(preact), _ptr(h),
+                                        _ptr(d_rows), _ptr(dx_rows), _ptr(dw1), _ptr(dw3),
+                                        _ptr(dw2), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def moe_router_backward(x, w_gate, logits, cand_ids, expert_of, row_of, dgates, counts_routed,
+                        dlogits, dw_gate, dx, *, top_k, renormalize, alpha=0.0, beta=0.0,
+                        dx_rows=None, dlogit_bias=None, ws=None, stream=None):
+    N, E = logits.shape
+    d = x.shape[1]
+    _dev_check(x, w_gate, logits, cand_ids, expert_of, row_of, dgates, counts_routed, dlogits,
+               dw_gate, dx, dx_rows, dlogit_bias)
+    p = RouterParams(N, d, E, top_k, cand_ids.shape[1], int(bool(renormalize)), None, None,
+                     None, 0, None)
+    if ws is None:
+        ws = workspace(lib.moe_router_backward_workspace_bytes(N, d, E), x.device)
+    _check(lib.moe_router_backward(ctypes.byref(p), _ptr(x), _dt(x), _ptr(w_gate), _ptr(logits),
+                                   _ptr(cand_ids), _ptr(expert_of), _ptr(row_of), _ptr(dgates),
+                                   _ptr(counts_routed), float(alpha), float(beta),
+                                   _ptr(dx_rows), _ptr(dlogits), _ptr(dw_gate),
+                                   _ptr(dlogit_bias), _ptr(dx), _ptr(ws), ws.numel(),
+                                   _stream(stream)))
+
+
 # --------------------------------------------------------------------- layer
 @dataclass
 class LayerSpec:
@@ -266,7 +338,7 @@ class MoELayer:
     """
 
     def __init__(self, spec: LayerSpec, weights: dict, x_dtype=torch.bfloat16, device="cuda",
-                 out_dtype=None, fused_gather=True):
+                 out_dtype=None, fused_gather=True, train=False):
         self.spec = s = spec
         self.w = weights
         self.dev = torch.device(device)
@@ -340,6 +412,16 @@ class MoELayer:
         if self.shared is not None:
             self.ws_shared = workspace(lib.moe_grouped_ffn_workspace_bytes(
                 ctypes.byref(self.shared), xdt, N), dev)
+        # training: the experts' forward keeps its pre-activations and h
+        self.train = bool(train)
+        if self.train:
+            if self.ec or self.shared is not None or weights.get("w_noise") is not None:
+                raise ValueError("the backward pass covers token choice without noise or a "
+                                 "shared expert")
+            bf = dict(dtype=torch.bfloat16, device=dev)
+            self.preact = torch.empty((R, 2 * s.d_ff), **bf)
+            self.h = torch.empty((R, s.d_ff), **bf)
+            self._bwd = None
 
     def route(self, x, logits_in=None, stream=None):
         s, w = self.spec, self.w
@@ -384,8 +466,13 @@ class MoELayer:
 
     def experts(self, x, stream=None):
         rows, index = self._packed_rows(x)
-        moe_grouped_ffn(self.ffn, rows, self.offsets, self.y_rows, row_index=index,
-                        max_rows=self.R, ws=self.ws_ffn, stream=stream)
+        if self.train:
+            moe_grouped_ffn_train(self.ffn, rows, self.offsets, self.y_rows, self.preact, self.h,
+                                  row_index=index, max_rows=self.R, ws=self.ws_ffn,
+                                  stream=stream)
+        else:
+            moe_grouped_ffn(self.ffn, rows, self.offsets, self.y_rows, row_index=index,
+                            max_rows=self.R, ws=self.ws_ffn, stream=stream)
         self.start_shared(x, stream)
 
     def combine(self, stream=None):
@@ -413,6 +500,47 @@ class MoELayer:
         if stats:
             self.stats(update_bias, stream)
         return self.y
+
+
+def _backward_buffers(layer):
+    s, dev = layer.spec, layer.dev
+    E, d, F, N, R = s.n_experts, s.d_model, s.d_ff, s.n_tokens, layer.R
+    f32 = dict(dtype=torch.float32, device=dev)
+    b = dict(d_rows=torch.empty((R, d), dtype=torch.bfloat16, device=dev),
+             dgates=torch.empty((N, s.top_k), **f32), dx_rows=torch.empty((R, d), **f32),
+             dw1=torch.empty((E, F, d), **f32), dw3=torch.empty((E, F, d), **f32),
+             dw2=torch.empty((E, d, F), **f32), dlogits=torch.empty((N, E), **f32),
+             dw_gate=torch.empty((E, d), **f32), dx=torch.empty((N, d), **f32),
+             dlogit_bias=torch.empty(E, **f32) if layer.w.get("logit_bias") is not None else None)
+    ws_f = workspace(lib.moe_grouped_ffn_backward_workspace_bytes(
+        ctypes.byref(layer.ffn), R, int(layer.fused_gather)), dev)
+    ws_r = workspace(lib.moe_router_backward_workspace_bytes(N, d, E), dev)
+    return b, ws_f, ws_r
+
+
+def layer_backward(layer, x, dy, alpha=0.0, beta=0.0, stream=None):
+    """Backward of the last `layer.forward` (the layer built with train=True):
+    L = <dy, y> + alpha * Switch aux + beta * z-loss. Returns a dict of fp32
+    device tensors: dx, dw_gate, dlogit_bias (or None), dw1, dw3, dw2,
+    dlogits, dgates (buffers reused by the next call)."""
+    if not layer.train:
+        raise ValueError("build the layer with train=True to run its backward pass")
+    if layer._bwd is None:
+        layer._bwd = _backward_buffers(layer)
+    b, ws_f, ws_r = layer._bwd
+    s, w = layer.spec, layer.w
+    moe_combine_backward(dy, layer.y_rows, layer.row_of, layer.gates, b["d_rows"], b["dgates"],
+                         stream=stream)
+    rows, index = layer._packed_rows(x)
+    moe_grouped_ffn_backward(layer.ffn, rows, layer.offsets, layer.preact, layer.h, b["d_rows"],
+                             b["dx_rows"], b["dw1"], b["dw3"], b["dw2"], row_index=index,
+                             max_rows=layer.R, ws=ws_f, stream=stream)
+    moe_router_backward(x, w["w_gate"], layer.logits, layer.cand_ids, layer.expert_of,
+                        layer.row_of, b["dgates"], layer.counts_routed, b["dlogits"],
+                        b["dw_gate"], b["dx"], top_k=s.top_k, renormalize=s.renormalize,
+                        alpha=alpha, beta=beta, dx_rows=b["dx_rows"],
+                        dlogit_bias=b["dlogit_bias"], ws=ws_r, stream=stream)
+    return b
 
 
 def spec_from_config(cfg) -> LayerSpec:

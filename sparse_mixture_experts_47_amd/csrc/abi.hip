@@ -23,7 +23,27 @@ moe_status dispatch_launch(int N, int E, int k, int C, moe_overflow policy, int 
 size_t grouped_ffn_workspace_bytes(const moe_ffn_weights* w, moe_dtype act_dt, int max_rows);
 moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_dtype act_dt,
                               const int32_t* row_index, const int32_t* offsets, int max_rows,
-                              void* y_rows, moe_dtype y_dt, void* workspace, hipStream_t st);
+                              void* y_rows, moe_dtype y_dt, void* workspace, hipStream_t st,
+                              uint16_t* preact = nullptr, uint16_t* h_out = nullptr);
+size_t grouped_ffn_backward_workspace_bytes(const moe_ffn_weights* w, int max_rows,
+                                            bool gather);
+moe_status grouped_ffn_backward_launch(const moe_ffn_weights* w, const void* x_rows,
+                                       const int32_t* row_index, const int32_t* offsets,
+                                       int max_rows, const uint16_t* preact, const uint16_t* h,
+                                       const uint16_t* d_out, float* dx_rows, float* dw1,
+                                       float* dw3, float* dw2, void* workspace, hipStream_t st);
+moe_status combine_backward_launch(int N, int d, int k, const float* dy, const void* y_rows,
+                                   moe_dtype y_dt, const int32_t* row_of, const float* gates,
+                                   uint16_t* d_rows, float* dgates, hipStream_t st);
+size_t router_backward_workspace_bytes(int N, int d, int E);
+moe_status router_backward_launch(int N, int d, int E, int k, int C, int renormalize,
+                                  const void* x, moe_dtype x_dt, const float* w_gate,
+                                  const float* logits, const int32_t* cand_ids,
+                                  const int32_t* expert_of, const int32_t* row_of,
+                                  const float* dgates, const int32_t* counts_routed, float alpha,
+                                  float beta, const float* dx_rows, float* dlogits,
+                                  float* dw_gate, float* dlogit_bias, float* dx, void* workspace,
+                                  hipStream_t st);
 moe_status combine_launch(int N, int d, int k, const void* y_rows, moe_dtype y_dt,
                           const int32_t* row_of, const float* gates, const void* y_shared,
                           moe_dtype sh_dt, void* y, moe_dtype out_dt, hipStream_t st);
@@ -230,6 +250,116 @@ moe_status moe_grouped_ffn(const moe_ffn_weights* w, const void* x_rows, moe_dty
   if (s != MOE_OK) return s;
   return grouped_ffn_launch(w, x_rows, act_dt, row_index, offsets, max_rows, y_rows, y_dt,
                             workspace, (hipStream_t)hip_stream);
+}
+
+// ------------------------------------------------------------ training
+static moe_status check_train_weights(const moe_ffn_weights* w, const char* who) {
+  CHECK(w, MOE_EINVAL, "%s: weights is NULL", who);
+  const int E = w->n_experts, d = w->d_model, F = w->d_ff;
+  CHECK(E >= 1 && E <= 256 && d >= 1 && F >= 1, MOE_EINVAL, "%s: E=%d d=%d d_ff=%d out of range",
+        who, E, d, F);
+  CHECK(w->w1 && w->w2 && w->w3, MOE_EINVAL, "%s: NULL weight", who);
+  CHECK(w->act == MOE_SWIGLU && w->w_dt == MOE_BF16 && !w->b1 && !w->b2 && !w->h_fp32,
+        MOE_EUNSUPPORTED, "%s: training covers bf16 SwiGLU experts without biases", who);
+  CHECK(d % 256 == 0 && F % 256 == 0, MOE_EUNSUPPORTED,
+        "%s: d_model %d and d_ff %d must be multiples of 256", who, d, F);
+  return MOE_OK;
+}
+
+moe_status moe_grouped_ffn_train(const moe_ffn_weights* w, const void* x_rows,
+                                 const int32_t* row_index, const int32_t* offsets,
+                                 int32_t max_rows, void* y_rows, moe_dtype y_dt,
+                                 uint16_t* preact, uint16_t* h, void* workspace, size_t ws_bytes,
+                                 void* hip_stream) {
+  moe_status s = check_train_weights(w, "moe_grouped_ffn_train");
+  if (s != MOE_OK) return s;
+  CHECK(max_rows >= 1 && (long long)max_rows * 2 * w->d_ff < (1ll << 40), MOE_EINVAL,
+        "moe_grouped_ffn_train: max_rows %d out of range", max_rows);
+  CHECK(x_rows && offsets && y_rows && preact && h, MOE_EINVAL,
+        "moe_grouped_ffn_train: NULL argument");
+  CHECK(y_dt == MOE_BF16 || y_dt == MOE_F32, MOE_EUNSUPPORTED,
+        "moe_grouped_ffn_train: output dtype");
+  s = check_ws(workspace, ws_bytes, grouped_ffn_workspace_bytes(w, MOE_BF16, max_rows),
+               "moe_grouped_ffn_train");
+  if (s != MOE_OK) return s;
+  return grouped_ffn_launch(w, x_rows, MOE_BF16, row_index, offsets, max_rows, y_rows, y_dt,
+                            workspace, (hipStream_t)hip_stream, preact, h);
+}
+
+size_t moe_grouped_ffn_backward_workspace_bytes(const moe_ffn_weights* w, int32_t max_rows,
+                                                int32_t gather) {
+  if (!w || max_rows <= 0) return 0;
+  return grouped_ffn_backward_workspace_bytes(w, max_rows, gather != 0);
+}
+
+moe_status moe_grouped_ffn_backward(const moe_ffn_weights* w, const void* x_rows,
+                                    const int32_t* row_index, const int32_t* offsets,
+                                    int32_t max_rows, const uint16_t* preact, const uint16_t* h,
+                                    const uint16_t* d_rows, float* dx_rows, float* dw1,
+                                    float* dw3, float* dw2, void* workspace, size_t ws_bytes,
+                                    void* hip_stream) {
+  moe_status s = check_train_weights(w, "moe_grouped_ffn_backward");
+  if (s != MOE_OK) return s;
+  CHECK(max_rows >= 1 && (long long)max_rows * 2 * w->d_ff < (1ll << 40), MOE_EINVAL,
+        "moe_grouped_ffn_backward: max_rows %d out of range", max_rows);
+  CHECK(x_rows && offsets && preact && h && d_rows && dx_rows && dw1 && dw3 && dw2, MOE_EINVAL,
+        "moe_grouped_ffn_backward: NULL argument");
+  s = check_ws(workspace, ws_bytes,
+               grouped_ffn_backward_workspace_bytes(w, max_rows, row_index != nullptr),
+               "moe_grouped_ffn_backward");
+  if (s != MOE_OK) return s;
+  return grouped_ffn_backward_launch(w, x_rows, row_index, offsets, max_rows, preact, h, d_rows,
+                                     dx_rows, dw1, dw3, dw2, workspace,
+                                     (hipStream_t)hip_stream);
+}
+
+moe_status moe_combine_backward(int32_t n_tokens, int32_t d_model, int32_t top_k,
+                                const float* dy, const void* y_rows, moe_dtype y_dt,
+                                const int32_t* row_of, const float* gates, uint16_t* d_rows,
+                                float* dgates, void* hip_stream) {
+  CHECK(n_tokens >= 1 && d_model >= 1 && top_k >= 1 && top_k <= 256, MOE_EINVAL,
+        "moe_combine_backward: N=%d d=%d k=%d out of range", n_tokens, d_model, top_k);
+  CHECK(dy && y_rows && row_of && gates && d_rows && dgates, MOE_EINVAL,
+        "moe_combine_backward: NULL argument");
+  CHECK(d_model % 8 == 0, MOE_EUNSUPPORTED, "moe_combine_backward: d_model %d not a multiple of 8",
+        d_model);
+  CHECK(y_dt == MOE_F32 || y_dt == MOE_BF16, MOE_EUNSUPPORTED,
+        "moe_combine_backward: y_rows dtype must be F32 or BF16");
+  return combine_backward_launch(n_tokens, d_model, top_k, dy, y_rows, y_dt, row_of, gates,
+                                 d_rows, dgates, (hipStream_t)hip_stream);
+}
+
+size_t moe_router_backward_workspace_bytes(int32_t n_tokens, int32_t d_model,
+                                           int32_t n_experts) {
+  if (n_tokens <= 0 || d_model <= 0 || n_experts <= 0) return 0;
+  return router_backward_workspace_bytes(n_tokens, d_model, n_experts);
+}
+
+moe_status moe_router_backward(const moe_router_params* p, const void* x, moe_dtype x_dt,
+                               const float* w_gate, const float* logits, const int32_t* cand_ids,
+                               const int32_t* expert_of, const int32_t* row_of,
+                               const float* dgates, const int32_t* counts_routed, float alpha,
+                               float beta, const float* dx_rows, float* dlogits, float* dw_gate,
+                               float* dlogit_bias, float* dx, void* workspace, size_t ws_bytes,
+                               void* hip_stream) {
+  CHECK(p, MOE_EINVAL, "moe_router_backward: params is NULL");
+  const int N = p->n_tokens, d = p->d_model, E = p->n_experts, k = p->top_k, C = p->n_cand;
+  CHECK(N >= 1 && d >= 1 && E >= 1 && k >= 1 && C >= k && k <= E, MOE_EINVAL,
+        "moe_router_backward: N=%d d=%d E=%d k=%d n_cand=%d out of range", N, d, E, k, C);
+  CHECK(E <= 256, MOE_EUNSUPPORTED, "moe_router_backward: n_experts %d > 256", E);
+  CHECK(!p->w_noise, MOE_EUNSUPPORTED, "moe_router_backward: noisy gating has no backward here");
+  CHECK(x && w_gate && logits && cand_ids && expert_of && row_of && dgates && counts_routed &&
+            dlogits && dw_gate && dx,
+        MOE_EINVAL, "moe_router_backward: NULL argument");
+  CHECK(x_dt == MOE_F32 || x_dt == MOE_BF16, MOE_EUNSUPPORTED, "moe_router_backward: x dtype");
+  CHECK((long long)N * (d > E ? d : E) < (1ll << 40), MOE_EINVAL, "moe_router_backward: too large");
+  moe_status s = check_ws(workspace, ws_bytes, router_backward_workspace_bytes(N, d, E),
+                          "moe_router_backward");
+  if (s != MOE_OK) return s;
+  return router_backward_launch(N, d, E, k, C, p->renormalize, x, x_dt, w_gate, logits, cand_ids,
+                                expert_of, row_of, dgates, counts_routed, alpha, beta, dx_rows,
+                                dlogits, dw_gate, dlogit_bias, dx, workspace,
+                                (hipStream_t)hip_stream);
 }
 
 moe_status moe_combine(int32_t n_tokens, int32_t d_model, int32_t top_k, const void* y_rows,

@@ -152,9 +152,66 @@ moe_status dispatch_out(int N, int d, int k, const void* yr, const int32_t* row_
   return moe_host::launch_status("combine");
 }
 
+// Backward of the combine, one block per token. y_t = sum_j g_tj o_tj:
+// dO_r = g_tj * dy_t (bf16, the data operand of the experts' backward GEMMs)
+// for the row r = row_of[t][j] of each kept slot, and dg_tj = <dy_t, o_r>
+// (fp32, summed per thread in feature order, then over the block's threads
+// in a fixed tree: deterministic). A dropped slot gets dg = 0.
+template <typename YT>
+__global__ __launch_bounds__(kThreads) void combine_backward_kernel(
+    int d, int k, const float* __restrict__ dy, const YT* __restrict__ y_rows,
+    const int32_t* __restrict__ row_of, const float* __restrict__ gates,
+    uint16_t* __restrict__ d_rows, float* __restrict__ dgates) {
+  __shared__ float red[kThreads / 64];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  for (int j = 0; j < k; ++j) {
+    const int r = row_of[(size_t)t * k + j];
+    if (r < 0) {
+      if (tid == 0) dgates[(size_t)t * k + j] = 0.f;
+      continue;
+    }
+    const float g = gates[(size_t)t * k + j];
+    float dot = 0.f;
+    for (int c = tid * 8; c < d; c += kThreads * 8) {
+      float v[8], o[8];
+      Vec8<float>::load(dy + (size_t)t * d + c, v);
+      Vec8<YT>::load(y_rows + (size_t)r * d + c, o);
+      float s[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        dot = __builtin_fmaf(v[i], o[i], dot);
+        s[i] = g * v[i];
+      }
+      Vec8<uint16_t>::store(d_rows + (size_t)r * d + c, s);
+    }
+    dot = moe::wave_tree_sum(dot);
+    if ((tid & 63) == 0) red[tid >> 6] = dot;
+    __syncthreads();
+    if (tid == 0) {
+      float sum = 0.f;
+      for (int w = 0; w < kThreads / 64; ++w) sum += red[w];
+      dgates[(size_t)t * k + j] = sum;
+    }
+    __syncthreads();
+  }
+}
+
 }  // namespace
 
 namespace moe_host {
+
+moe_status combine_backward_launch(int N, int d, int k, const float* dy, const void* y_rows,
+                                   moe_dtype y_dt, const int32_t* row_of, const float* gates,
+                                   uint16_t* d_rows, float* dgates, hipStream_t st) {
+  if (y_dt == MOE_BF16)
+    combine_backward_kernel<uint16_t><<<N, kThreads, 0, st>>>(
+        d, k, dy, (const uint16_t*)y_rows, row_of, gates, d_rows, dgates);
+  else
+    combine_backward_kernel<float><<<N, kThreads, 0, st>>>(d, k, dy, (const float*)y_rows,
+                                                            row_of, gates, d_rows, dgates);
+  return launch_status("combine backward");
+}
+
 
 moe_status combine_launch(int N, int d, int k, const void* y_rows, moe_dtype y_dt,
                           const int32_t* row_of, const float* gates, const void* y_shared,

@@ -59,6 +59,9 @@ struct Args {
   const int32_t* seg_begin;
   const int32_t* seg_end;
   const int32_t* tile_e;
+  // GLU only, or null: the pre-activations are also stored, bf16, as rows
+  // of 2 * Nrows (gate | up) -- the state the backward pass differentiates
+  uint16_t* pre;
 };
 
 __device__ __forceinline__ float act_fn(int act, float v) {
@@ -440,8 +443,14 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
         const int row = row0 + wm * WM + i * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
         if (row >= row_end) continue;
         float v;
-        if (EPI == EPI_GLU)
+        if (EPI == EPI_GLU) {
           v = silu(acc[0][i][j][r]) * acc[NACC - 1][i][j][r];
+          if (g.pre) {
+            const size_t po = (size_t)row * 2 * g.Nrows + col;
+            g.pre[po] = moe::f32_to_bf16_bits(acc[0][i][j][r]);
+            g.pre[po + g.Nrows] = moe::f32_to_bf16_bits(acc[NACC - 1][i][j][r]);
+          }
+        }
         else if (EPI == EPI_ACT)
           v = act_fn(g.act, acc[0][i][j][r] + bv);
         else

@@ -1,0 +1,307 @@
+// gemm_bwd.h -- bf16 MFMA grouped GEMMs of the expert FFN's backward pass on
+// gfx950: products whose operands have the contraction index as their slow
+// (row) dimension in memory.
+//
+// The forward GEMMs multiply token rows by weights stored with K contiguous
+// (both operands K-major). Backward needs the other layouts:
+//   data gradient   dH[r][n]  = sum_k dO[r][k] * W[k][n]       (W is K-slow)
+//   weight gradient dW_e[m][n] = sum_{rows r of e} A[r][m] B[r][n]  (both K-slow)
+// A K-slow tile is staged into LDS exactly as it lies in memory, [BK][cols]
+// with cols contiguous (16-byte chunks straight from global memory with
+// global_load_lds), and the MFMA fragment, which wants 8 consecutive K
+// values per lane, is read with gfx950's transposing LDS read
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane 4p+c supplies the
+// address of 4 consecutive columns (8 bytes) of LDS row p, and lane j
+// receives column j's 4 values of the 4 rows. Two such reads (rows k..k+3
+// and k+4..k+7) give a lane its 8 K values of one column.
+//
+// K-slow LDS rows are swizzled in 16-byte chunks: physical chunk = logical
+// chunk ^ ((row & 3) << 2), so the four rows one transposing read touches
+// fall on four different 64-byte bank groups. K-contiguous tiles use the
+// forward GEMM's layout ([rows][BK], chunk ^ ((row >> 1) & 7)).
+//
+// Two tile spaces:
+//   ROWS  (data gradient): M = packed rows grouped by expert (ragged, tile
+//         table as in the forward), A = rows [R][K] K-contiguous, B = the
+//         expert's weight [K][N] K-slow, optionally as two K segments
+//         (k < kseg from B0, else B1: W1 then W3 for SwiGLU's gate and up).
+//   DENSE (weight gradient): per expert a full M x N output; K = the
+//         expert's row count (ragged, masked in the last K tile); A = rows
+//         [R][M] and B = rows [R][N], both K-slow; the output rows m < mseg
+//         go to C0, the rest to C1 (dW1 and dW3 from one launch).
+#pragma once
+
+#include "gemm_bf16.h"
+#include "moe_device.h"
+
+namespace moe_bwd {
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+enum { MODE_ROWS = 0, MODE_DENSE = 1 };
+enum { BEPI_F32 = 0, BEPI_DSWIGLU = 1 };
+
+struct BwdArgs {
+  const uint16_t* A;   // ROWS: [R][lda] rows, K-contiguous. DENSE: [R][lda] rows (K = row)
+  const uint16_t* B0;  // ROWS: weights [E][K][ldb]. DENSE: [R][ldb] rows
+  const uint16_t* B1;  // ROWS: second K segment (k >= kseg), or null
+  float* C0;           // F32 output: ROWS [R][ldc]; DENSE [E][mseg][ldc] (m < mseg)
+  float* C1;           // DENSE: [E][M - mseg][ldc] (m >= mseg), or null
+  const uint16_t* pre; // DSWIGLU: saved pre-activations [R][2 N] (gate | up)
+  uint16_t* dpre;      // DSWIGLU: out [R][2 N] (d gate | d up)
+  int M, N, K;         // DENSE: M, N; ROWS: N (columns), K (contraction)
+  int lda, ldb, ldc;
+  int kseg, mseg;
+  long long b_expert;  // ROWS: elements between experts' weights
+  int E, max_mt, n_tiles_n, group_n;
+  const int32_t* offsets;     // [E+1] rows of each expert
+  const int32_t* tile_start;  // ROWS: [E+1] first M tile of each expert
+};
+
+__device__ __forceinline__ int ks_phys(int row, int chunk) { return chunk ^ ((row & 3) << 2); }
+
+// MFMA fragment (32 columns x 16 K) of a K-slow LDS tile [BK][BC] at column
+// block cb and K step kk. kvalid < BK zeroes the K values past it.
+template <int BC>
+__device__ __forceinline__ bf16x8_t frag_kslow(const uint16_t* tile, int cb, int kk, int lane,
+                                               int kvalid) {
+  const int G = lane >> 4, s = lane & 15, p = s >> 2, c4 = s & 3;
+  const int row = kk * 16 + 8 * (G >> 1) + p;
+  const int col = cb + 16 * (G & 1) + 4 * c4;
+  const int off0 = row * BC + (ks_phys(row, col >> 3) << 3) + (col & 7);
+  const int off1 = off0 + 4 * BC;  // row + 4: same (row & 3), same swizzle
+  s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(tile + off0));
+  s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(tile + off1));
+  if (kvalid < 64) {
+    // this lane holds K = kk*16 + 8*(lane>>5) + 0..7 of column (lane & 31)
+    const int k0 = kk * 16 + 8 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (k0 + i >= kvalid) lo[i] = 0;
+      if (k0 + 4 + i >= kvalid) hi[i] = 0;
+    }
+  }
+  union {
+    s16x4_t h[2];
+    bf16x8_t v;
+  } u;
+  u.h[0] = lo;
+  u.h[1] = hi;
+  return u.v;
+}
+
+// BM x BN tile, BK = 64, NS LDS stages, WGM x WGN waves.
+template <int MODE, int BEPI, int BM, int BN, int NS, int WGM, int WGN>
+__global__ __launch_bounds__(WGM * WGN * 64) void gemm_bwd_kernel(BwdArgs g) {
+  constexpr int BK = 64;
+  constexpr int KK = BK / 16;
+  constexpr int NW = WGM * WGN;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int FM = WM / 32, FN = WN / 32;
+  constexpr int A_ELEMS = BM * BK, B_ELEMS = BN * BK;
+  constexpr int STAGE = A_ELEMS + B_ELEMS;
+  // 1 KB segments: K-contiguous [rows][64] = 8 rows; K-slow [64][cols] = 512/cols rows
+  constexpr int A_SEG_ROWS = MODE == MODE_ROWS ? 8 : 512 / BM;
+  constexpr int B_SEG_ROWS = 512 / BN;
+  constexpr int A_SEGS = (MODE == MODE_ROWS ? BM : BK) / A_SEG_ROWS;
+  constexpr int B_SEGS = BK / B_SEG_ROWS;
+  constexpr int A_IT = A_SEGS / NW, B_IT = B_SEGS / NW;
+  constexpr int LPT = A_IT + B_IT;
+  static_assert(A_IT * NW == A_SEGS && B_IT * NW == B_SEGS, "segments per wave");
+  static_assert(BN >= 128 && (MODE == MODE_ROWS || BM >= 128), "K-slow tiles need >= 16 chunks");
+  static_assert(FM >= 1 && FN >= 1, "wave tile");
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+
+  // ---- tile -> (expert, M tile, N tile); XCD-aware as in the forward GEMM
+  const int per_xcd = gridDim.x >> 3;
+  const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  int e, mt, nt, row0 = 0, row_end = 0, kbeg = 0, kcount = 0;
+  if constexpr (MODE == MODE_ROWS) {
+    const int span = g.max_mt * g.group_n;
+    const int ng = logical / span, rem = logical - ng * span;
+    mt = rem / g.group_n;
+    nt = ng * g.group_n + (rem - mt * g.group_n);
+    if (nt >= g.n_tiles_n || mt >= g.tile_start[g.E]) return;
+    e = moe_gemm::tile_expert(g.tile_start, g.E, mt);
+    row0 = g.offsets[e] + (mt - g.tile_start[e]) * BM;
+    row_end = g.offsets[e + 1];
+    kcount = g.K;
+  } else {
+    const int mtiles = g.M / BM;
+    const int span = mtiles * g.group_n;
+    const int per_e = span * ((g.n_tiles_n + g.group_n - 1) / g.group_n);
+    e = logical / per_e;
+    const int rest = logical - e * per_e;
+    const int ng = rest / span, rem = rest - ng * span;
+    mt = rem / g.group_n;
+    nt = ng * g.group_n + (rem - mt * g.group_n);
+    if (e >= g.E || nt >= g.n_tiles_n) return;
+    kbeg = g.offsets[e];
+    kcount = g.offsets[e + 1] - kbeg;
+  }
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int KT = (kcount + BK - 1) / BK;
+
+  // ---- one stage of loads: A then B segments, 16 bytes per lane each
+  auto issue = [&](int kt, int stage) {
+    uint16_t* base = smem + stage * STAGE;
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < A_IT; ++i) {
+      const int seg = wave + i * NW;
+      const uint16_t* src;
+      if constexpr (MODE == MODE_ROWS) {
+        const int r = seg * 8 + (lane >> 3);
+        int row = row0 + r;
+        row = row < row_end ? row : row_end - 1;
+        const int c = (lane & 7) ^ moe_gemm::chunk_swz<64>(r);
+        src = g.A + (size_t)row * g.lda + k0 + c * 8;
+      } else {
+        constexpr int CPR = BM / 8;
+        const int r = seg * A_SEG_ROWS + lane / CPR;
+        const int kr = min(k0 + r, kcount - 1);
+        const int c = ks_phys(r, lane % CPR);
+        src = g.A + (size_t)(kbeg + kr) * g.lda + m0 + c * 8;
+      }
+      __builtin_amdgcn_global_load_lds(
+          (const void*)src, (__attribute__((address_space(3))) void*)(base + seg * 512), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < B_IT; ++i) {
+      const int seg = wave + i * NW;
+      constexpr int CPR = BN / 8;
+      const int r = seg * B_SEG_ROWS + lane / CPR;
+      const int c = ks_phys(r, lane % CPR);
+      const uint16_t* src;
+      if constexpr (MODE == MODE_ROWS) {
+        const int k = k0 + r;
+        const uint16_t* w = (g.B1 && k >= g.kseg) ? g.B1 + (size_t)(k - g.kseg) * g.ldb
+                                                  : g.B0 + (size_t)k * g.ldb;
+        src = w + (size_t)e * g.b_expert + n0 + c * 8;
+      } else {
+        const int kr = min(k0 + r, kcount - 1);
+        src = g.B0 + (size_t)(kbeg + kr) * g.ldb + n0 + c * 8;
+      }
+      __builtin_amdgcn_global_load_lds(
+          (const void*)src,
+          (__attribute__((address_space(3))) void*)(base + A_ELEMS + seg * 512), 16, 0, 0);
+    }
+  };
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  struct Frags {
+    bf16x8_t a[FM];
+    bf16x8_t b[FN];
+  };
+  auto read_frags = [&](Frags& f, int stage, int kk, int kvalid) {
+    const uint16_t* cur = smem + stage * STAGE;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      if constexpr (MODE == MODE_ROWS)
+        f.a[i] = *(const bf16x8_t*)(cur + moe_gemm::dlds_off<64>(wm * WM + i * 32 + (lane & 31),
+                                                                  kk * 2 + (lane >> 5)));
+      else
+        f.a[i] = frag_kslow<BM>(cur, wm * WM + i * 32, kk, lane, kvalid);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      f.b[j] = frag_kslow<BN>(cur + A_ELEMS, wn * WN + j * 32, kk, lane, 64);
+  };
+  auto mfma = [&](const Frags& f) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+  };
+
+  // ---- main loop: NS-stage ring, loads run NS-1 tiles ahead
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < KT) issue(j, j);
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt + NS - 2 < KT) moe_gemm::wait_vmcnt<(NS - 2) * LPT>();
+    else moe_gemm::wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();  // tile kt visible; every wave is done with tile kt-1
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + NS - 1 < KT) issue(kt + NS - 1, (kt + NS - 1) % NS);
+    const int st = kt % NS;
+    // only the A operand of a DENSE tile is masked: rows past the expert's
+    // count repeat its last row (finite), so a zero A gives a zero product
+    const int kvalid = MODE == MODE_DENSE ? min(BK, kcount - kt * BK) : BK;
+    Frags fr[2];
+    read_frags(fr[0], st, 0, kvalid);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      if (kk + 1 < KK) read_frags(fr[(kk + 1) & 1], st, kk + 1, kvalid);
+      mfma(fr[kk & 1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // ---- epilogue
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = n0 + wn * WN + j * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int lr = wm * WM + i * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
+        const float v = acc[i][j][r];
+        if constexpr (MODE == MODE_ROWS) {
+          const int row = row0 + lr;
+          if (row >= row_end) continue;
+          if constexpr (BEPI == BEPI_DSWIGLU) {
+            // h = silu(a) * u; dh = v: da = v u silu'(a), du = v silu(a),
+            // silu'(a) = sig (1 + a (1 - sig))
+            const size_t o = (size_t)row * 2 * g.N + col;
+            const float a = moe::bf16_bits_to_f32(g.pre[o]);
+            const float u = moe::bf16_bits_to_f32(g.pre[o + g.N]);
+            const float sig = __builtin_amdgcn_rcpf(1.f + __expf(-a));
+            g.dpre[o] = moe::f32_to_bf16_bits(v * u * sig * (1.f + a * (1.f - sig)));
+            g.dpre[o + g.N] = moe::f32_to_bf16_bits(v * a * sig);
+          } else {
+            g.C0[(size_t)row * g.ldc + col] = v;
+          }
+        } else {
+          const int m = m0 + lr;
+          float* C = m < g.mseg ? g.C0 + ((size_t)e * g.mseg + m) * g.ldc
+                                : g.C1 + ((size_t)e * (g.M - g.mseg) + (m - g.mseg)) * g.ldc;
+          C[col] = v;
+        }
+      }
+    }
+  }
+}
+
+template <int MODE, int BEPI, int BM, int BN, int NS, int WGM, int WGN>
+inline hipError_t launch_bwd(BwdArgs g, long long tiles, hipStream_t st) {
+  constexpr size_t lds = (size_t)NS * (BM + BN) * 64 * sizeof(uint16_t);
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  auto kern = gemm_bwd_kernel<MODE, BEPI, BM, BN, NS, WGM, WGN>;
+  static bool configured = false;
+  if (!configured) {
+    hipError_t err = hipFuncSetAttribute((const void*)kern,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+    configured = true;
+  }
+  const int grid = (int)((tiles + 7) / 8 * 8);
+  kern<<<grid, WGM * WGN * 64, lds, st>>>(g);
+  return hipGetLastError();
+}
+
+}  // namespace moe_bwd

@@ -791,10 +791,13 @@ size_t grouped_ffn_workspace_bytes(const moe_ffn_weights* w, moe_dtype act_dt, i
 
 moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_dtype act_dt,
                               const int32_t* row_index, const int32_t* offsets, int max_rows,
-                              void* y_rows, moe_dtype y_dt, void* workspace, hipStream_t st) {
+                              void* y_rows, moe_dtype y_dt, void* workspace, hipStream_t st,
+                              uint16_t* preact, uint16_t* h_out) {
   const int E = w->n_experts, d = w->d_model, F = w->d_ff;
   char* ws = (char*)workspace;
-  void* h = ws;
+  // training: h goes to the caller's buffer (it is an operand of the weight
+  // gradient of W2) and GEMM 1 also stores the pre-activations
+  void* h = h_out ? (void*)h_out : (void*)ws;
   const TileTables tt = tile_tables(ws + h_bytes(w, act_dt, max_rows), E, max_rows);
   int32_t* tile_start = tt.ts;
   const bool glu = w->act == MOE_SWIGLU;
@@ -873,6 +876,7 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
   Args g1 = base_args(x_rows, w->w1, w->w3, w->b1, h, d, F, E, max_mt, (int)w->act, offsets,
                       tt.ts);
   g1.a_rows = row_index;
+  g1.pre = preact;
   g1.seg_begin = tt.sb;
   g1.seg_end = tt.se;
   g1.tile_e = tt.te;

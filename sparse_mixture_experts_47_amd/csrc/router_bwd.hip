@@ -1,0 +1,208 @@
+// router_bwd.hip -- backward pass of the router on gfx950: gates -> scores
+// -> logits (with the auxiliary and z-loss terms) -> W_g, the logit bias and
+// the token rows, plus the sum of the experts' row gradients back to tokens.
+//
+// heavensheep.xyz MoE notes, "Training": the main loss reaches only the
+// selected experts' scores (top-k passes no gradient to the rest), and the
+// Switch auxiliary loss E * sum_i f_i P_i is what gives every expert's
+// router weights a gradient; CS336 notes section 4: the z-loss
+// (1/N) sum_t lse_t^2. chiang97912 MoE notes, "KeepTopK 策略": the gates
+// are the softmax renormalised over the kept k (G = Softmax(KeepTopK(H,k))).
+// Per token t (s = softmax(l), lse = log sum exp l):
+//   renormalised: g_j = s_{c_j} / S, S = sum_j s_{c_j}:
+//                 dL/ds_{c_j} = (dg_j - sum_i dg_i g_i) / S
+//   Switch:       g = s_e of the expert used: dL/ds_e = dg
+//   auxiliary:    dL/ds_te += alpha E f_e / N, f_e = routed_e / (N k)
+//   softmax:      dl_te = s_te (ds_te - sum_e' s_te' ds_te')
+//   z-loss:       dl_te += beta 2 lse_t s_te / N
+//   router GEMM:  dW_g = dl^T x,  d(logit bias) = sum_t dl_t,  dx_t += dl_t W_g
+// dx_t also sums the token's kept expert-row gradients in slot order.
+#include "moe_device.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunkTokens = 256;  // tokens per partial sum of dW_g
+
+// one wave per token
+__global__ __launch_bounds__(kThreads) void router_bwd_token_kernel(
+    int N, int E, int k, int C, int renormalize, const float* __restrict__ logits,
+    const int32_t* __restrict__ cand_ids, const int32_t* __restrict__ expert_of,
+    const int32_t* __restrict__ row_of, const float* __restrict__ dgates,
+    const int32_t* __restrict__ counts_routed, float alpha, float beta,
+    float* __restrict__ dlogits) {
+  __shared__ float s_sh[kThreads / 64][256];
+  __shared__ float ds_sh[kThreads / 64][256];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kThreads / 64) + wave;
+  if (t >= N) return;  // whole waves leave together; no block barrier below
+  float* S_ = s_sh[wave];
+  float* D_ = ds_sh[wave];
+  const float* l = logits + (size_t)t * E;
+  float m = -INFINITY;
+  for (int e = lane; e < E; e += 64) m = fmaxf(m, l[e]);
+  m = moe::wave_max(m);
+  float part = 0.f;
+  for (int e = lane; e < E; e += 64) {
+    const float u = __expf(l[e] - m);
+    S_[e] = u;
+    part += u;
+  }
+  const float S = moe::wave_tree_sum(part);
+  const float lse = m + __logf(S);
+  const float invNk = 1.f / ((float)N * (float)k);
+  for (int e = lane; e < E; e += 64) {
+    S_[e] = S_[e] / S;
+    D_[e] = alpha * (float)E * ((float)counts_routed[e] * invNk) / (float)N;
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  if (lane == 0) {
+    const float* dg = dgates + (size_t)t * k;
+    if (renormalize) {
+      const int32_t* c = cand_ids + (size_t)t * C;
+      float Ssel = 0.f;
+      for (int j = 0; j < k; ++j) Ssel += S_[c[j]];
+      float dot = 0.f;
+      for (int j = 0; j < k; ++j) dot += dg[j] * (S_[c[j]] / Ssel);
+      for (int j = 0; j < k; ++j) D_[c[j]] += (dg[j] - dot) / Ssel;
+    } else {
+      for (int j = 0; j < k; ++j) {
+        const int e = expert_of[(size_t)t * k + j];
+        if (row_of[(size_t)t * k + j] >= 0 && e >= 0) D_[e] += dg[j];
+      }
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  float sd = 0.f;
+  for (int e = lane; e < E; e += 64) sd += S_[e] * D_[e];
+  sd = moe::wave_tree_sum(sd);
+  const float zc = beta * 2.f * lse / (float)N;
+  for (int e = lane; e < E; e += 64) {
+    const float s = S_[e];
+    dlogits[(size_t)t * E + e] = s * (D_[e] - sd) + zc * s;
+  }
+}
+
+// dx_t = sum_j dx_rows[row_of[t][j]] (kept slots in order) + sum_e dl_te W_g[e]
+__global__ __launch_bounds__(kThreads) void router_bwd_dx_kernel(
+    int d, int E, int k, const float* __restrict__ dl, const float* __restrict__ w_gate,
+    const int32_t* __restrict__ row_of, const float* __restrict__ dx_rows,
+    float* __restrict__ dx) {
+  __shared__ float dls[256];
+  const int t = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += kThreads) dls[e] = dl[(size_t)t * E + e];
+  __syncthreads();
+  for (int c = threadIdx.x; c < d; c += kThreads) {
+    float acc = 0.f;
+    if (dx_rows)
+      for (int j = 0; j < k; ++j) {
+        const int r = row_of[(size_t)t * k + j];
+        if (r >= 0) acc += dx_rows[(size_t)r * d + c];
+      }
+    for (int e = 0; e < E; ++e) acc = __builtin_fmaf(dls[e], w_gate[(size_t)e * d + c], acc);
+    dx[(size_t)t * d + c] = acc;
+  }
+}
+
+// partial[chunk][e][c] = sum over the chunk's tokens of dl[t][e] x[t][c]
+template <typename XT>
+__global__ __launch_bounds__(kThreads) void router_bwd_wg_partial_kernel(
+    int N, int d, int E, const float* __restrict__ dl, const XT* __restrict__ x,
+    float* __restrict__ partial) {
+  const int c = blockIdx.x * kThreads + threadIdx.x;
+  const int e0 = blockIdx.y * 8, chunk = blockIdx.z;
+  if (c >= d) return;
+  const int t0 = chunk * kChunkTokens, t1 = min(N, t0 + kChunkTokens);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int t = t0; t < t1; ++t) {
+    float xv;
+    if constexpr (sizeof(XT) == 2) xv = moe::bf16_bits_to_f32(x[(size_t)t * d + c]);
+    else xv = x[(size_t)t * d + c];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (e0 + i < E) acc[i] = __builtin_fmaf(dl[(size_t)t * E + e0 + i], xv, acc[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (e0 + i < E) partial[((size_t)chunk * E + e0 + i) * d + c] = acc[i];
+}
+
+// dW_g[e][c] = sum of the partials in chunk order
+__global__ __launch_bounds__(kThreads) void router_bwd_wg_reduce_kernel(
+    int d, int E, int chunks, const float* __restrict__ partial, float* __restrict__ dw) {
+  const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= (size_t)E * d) return;
+  float acc = 0.f;
+  for (int ch = 0; ch < chunks; ++ch) acc += partial[(size_t)ch * E * d + i];
+  dw[i] = acc;
+}
+
+// d(logit bias)[e] = sum_t dl[t][e]: one block per expert, fixed tree
+__global__ __launch_bounds__(kThreads) void router_bwd_bias_kernel(int N, int E,
+                                                                   const float* __restrict__ dl,
+                                                                   float* __restrict__ db) {
+  __shared__ float red[kThreads / 64];
+  const int e = blockIdx.x;
+  float acc = 0.f;
+  for (int t = threadIdx.x; t < N; t += kThreads) acc += dl[(size_t)t * E + e];
+  acc = moe::wave_tree_sum(acc);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float s = 0.f;
+    for (int w = 0; w < kThreads / 64; ++w) s += red[w];
+    db[e] = s;
+  }
+}
+
+}  // namespace
+
+namespace moe_host {
+
+size_t router_backward_workspace_bytes(int N, int d, int E) {
+  const int chunks = (N + kChunkTokens - 1) / kChunkTokens;
+  return align256((size_t)chunks * E * d * 4);
+}
+
+moe_status router_backward_launch(int N, int d, int E, int k, int C, int renormalize,
+                                  const void* x, moe_dtype x_dt, const float* w_gate,
+                                  const float* logits, const int32_t* cand_ids,
+                                  const int32_t* expert_of, const int32_t* row_of,
+                                  const float* dgates, const int32_t* counts_routed, float alpha,
+                                  float beta, const float* dx_rows, float* dlogits,
+                                  float* dw_gate, float* dlogit_bias, float* dx, void* workspace,
+                                  hipStream_t st) {
+  const int per_block = kThreads / 64;
+  router_bwd_token_kernel<<<(N + per_block - 1) / per_block, kThreads, 0, st>>>(
+      N, E, k, C, renormalize, logits, cand_ids, expert_of, row_of, dgates, counts_routed, alpha,
+      beta, dlogits);
+  moe_status s = launch_status("router backward (scores)");
+  if (s != MOE_OK) return s;
+  router_bwd_dx_kernel<<<N, kThreads, 0, st>>>(d, E, k, dlogits, w_gate, row_of, dx_rows, dx);
+  s = launch_status("router backward (dx)");
+  if (s != MOE_OK) return s;
+  const int chunks = (N + kChunkTokens - 1) / kChunkTokens;
+  float* partial = (float*)workspace;
+  dim3 grid((d + kThreads - 1) / kThreads, (E + 7) / 8, chunks);
+  if (x_dt == MOE_BF16)
+    router_bwd_wg_partial_kernel<uint16_t><<<grid, kThreads, 0, st>>>(
+        N, d, E, dlogits, (const uint16_t*)x, partial);
+  else
+    router_bwd_wg_partial_kernel<float><<<grid, kThreads, 0, st>>>(N, d, E, dlogits,
+                                                                   (const float*)x, partial);
+  s = launch_status("router backward (dW_g partials)");
+  if (s != MOE_OK) return s;
+  router_bwd_wg_reduce_kernel<<<(int)(((size_t)E * d + kThreads - 1) / kThreads), kThreads, 0,
+                                st>>>(d, E, chunks, partial, dw_gate);
+  s = launch_status("router backward (dW_g)");
+  if (s != MOE_OK) return s;
+  if (dlogit_bias) {
+    router_bwd_bias_kernel<<<E, kThreads, 0, st>>>(N, E, dlogits, dlogit_bias);
+    s = launch_status("router backward (logit bias)");
+  }
+  return s;
+}
+
+}  // namespace moe_host

@@ -1,0 +1,251 @@
+"""GPU parity of the layer's backward pass against the fp64 backward oracle.
+
+The GPU runs the training forward (which keeps the experts' pre-activations
+and h) from the oracle's logits, so every routing decision is identical
+(checked bit-exactly), then the backward of
+L = <dy, y> + alpha * Switch aux + beta * z-loss for a seeded dy.
+
+Tolerances, element by element. The GPU rounds to bf16 (unit roundoff
+u = 2^-8) the saved pre-activations a and u, h, dO = g * dy and the
+intermediates da and du, and sums in fp32. Each gradient's error is bounded
+by first-order propagation of those roundings through the sums of absolute
+terms (the running error bound of Higham, "Accuracy and Stability of
+Numerical Algorithms", ch. 3), times 3 for second-order terms, fp32
+rounding and the hardware exp and reciprocal. With A = |dO| |W2| (absolute
+terms of dh = dO W2) and A_o = |h| |W2|^T (absolute terms of o = h W2^T):
+  dW2 = dO^T h:   |err| <= 3u |dO|^T |h|
+  M_a = |u silu'(a)| A + |dh| |u| (|silu'(a)| + |a|) + |da|   (first-order error of da, /u)
+  M_u = |silu(a)| A + |dh| (|silu'(a)| |a| + |silu(a)|) + |du|
+  dW1 = da^T x:   3u M_a^T |x|;   dW3 = du^T x:   3u M_u^T |x|
+  dX rows:        3u (M_a |W1| + M_u |W3|)
+  dg_tj = <dy_t, o_r>:  B_g = 3 * 2u |dy_t| . A_o[r]     (o carries h's rounding)
+  ds (renormalised):   B_s[c_j] = (B_g_j + sum_i B_g_i g_i) / S;  Switch: B_s[e] = B_g
+  dl = s (ds - s.ds):  B_l = s (B_s + s.B_s) + 1e-5 (|dl| + s (|ds| + s.|ds|))  (fp32 softmax)
+  dW_g = dl^T x:  B_l^T |x|;  d logit bias: sum_t B_l;  dx = sum_j dX rows + dl W_g.
+These worst-case bounds are loose where many terms of mixed sign cancel, so
+the router-side gradients must also meet the layer output's normwise bf16
+bar, max |g - g_ref| / RMS(g_ref) <= 2e-2, and the router's backward alone
+(fp32 arithmetic only) is checked to 1e-5 relative.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from oracle import backward as OB
+from parity_utils import (TOL_BF16, experts_of, host_inputs, rel_err, require_gpu, to_device,
+                          to_np)
+
+pytestmark = pytest.mark.gpu
+
+ALPHA, BETA = 0.1, 0.01
+
+
+@pytest.fixture(scope="module")
+def moe():
+    require_gpu()
+    import sparse_mixture_experts_47_amd as m
+    return m
+
+
+def _bf16_bits(a):
+    """fp32 -> bf16 bits, round to nearest even (finite values)."""
+    u = np.ascontiguousarray(a, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def test_combine_backward_matches_definition(moe):
+    rng = np.random.default_rng(21)
+    N, d, k = 70, 264, 3
+    R = N * k
+    row_of = rng.permutation(R).astype(np.int32).reshape(N, k)
+    row_of[rng.random((N, k)) < 0.2] = -1
+    row_of[4] = -1
+    gates = rng.random((N, k)).astype(np.float32)
+    dy = rng.standard_normal((N, d)).astype(np.float32)
+    yr = rng.standard_normal((R, d)).astype(np.float32)
+    d_rows = torch.full((R, d), 7, dtype=torch.bfloat16, device="cuda")
+    dg = torch.full((N, k), 9.0, device="cuda")
+    moe.moe_combine_backward(torch.from_numpy(dy).cuda(), torch.from_numpy(yr).cuda(),
+                             torch.from_numpy(row_of).cuda(), torch.from_numpy(gates).cuda(),
+                             d_rows, dg)
+    torch.cuda.synchronize()
+    got_rows = d_rows.view(torch.int16).cpu().numpy().view(np.uint16)
+    kept = row_of >= 0
+    for t, j in zip(*np.nonzero(kept)):
+        # the product g * dy rounds once in fp32, then to bf16
+        want = _bf16_bits(gates[t, j] * dy[t])
+        assert np.array_equal(got_rows[row_of[t, j]], want)
+    ref = np.where(kept, np.einsum("td,tjd->tj", dy.astype(np.float64),
+                                   yr.astype(np.float64)[np.maximum(row_of, 0)]), 0.0)
+    assert np.all(to_np(dg)[~kept] == 0.0)
+    assert np.max(np.abs(to_np(dg) - ref)) <= 1e-5 * np.max(np.abs(ref))
+
+
+CASES = {
+    "mixtral_reduced": W.REDUCED["c2"],
+    # Switch gate, top-1, capacity drops (SwiGLU bf16 experts)
+    "switch_drop_reduced": W.REDUCED["c2"].with_(name="switch_drop_reduced", top_k=1,
+                                                  renormalize=False, overflow=W.DROP,
+                                                  capacity_factor=1.0, n_tokens=512),
+}
+
+
+def _dy(cfg):
+    g = torch.Generator().manual_seed(1000 + cfg.seed)
+    return torch.randn((cfg.n_tokens, cfg.d_model), generator=g)
+
+
+@pytest.mark.parametrize("key", list(CASES))
+def test_layer_backward_matches_oracle(moe, key):
+    cfg = CASES[key]
+    print("backward", key, cfg, flush=True)
+    inp = W.make_inputs(cfg, "cpu")
+    host = host_inputs(inp)
+    experts = experts_of(host)
+    fwd = oracle.layer_forward(cfg, host["x"], cfg.x_dtype, host["w_gate"], experts, None,
+                               host["logit_bias"], host["select_bias"], host["w_noise"])
+    dy = _dy(cfg)
+    ref = OB.layer_backward(cfg, host["x"], cfg.x_dtype, host["w_gate"], experts, fwd,
+                            dy.numpy().astype(np.float64), ALPHA, BETA,
+                            logit_bias=host["logit_bias"], keep_terms=True)
+    dev = to_device(inp)
+    layer = moe.MoELayer(moe.spec_from_config(cfg), dev, x_dtype=torch.bfloat16, train=True)
+    layer_eval = moe.MoELayer(moe.spec_from_config(cfg), dev, x_dtype=torch.bfloat16)
+    logits = torch.from_numpy(fwd["logits"]).cuda()
+    y = layer.forward(dev["x"], logits_in=logits).clone()
+    y_eval = layer_eval.forward(dev["x"], logits_in=logits)
+    torch.cuda.synchronize()
+    # the training forward computes the same layer output bit for bit
+    assert torch.equal(y, y_eval)
+    d = fwd["dispatch"]
+    for name in ("row_of", "expert_of", "counts_routed", "offsets"):
+        assert np.array_equal(to_np(getattr(layer, name)), d[name]), name
+    g = moe.layer_backward(layer, dev["x"], dy.cuda(), ALPHA, BETA)
+    torch.cuda.synchronize()
+    _check_bounds(g, ref, fwd, dy.numpy().astype(np.float64), host, cfg)
+    # the router-side gradients also meet the layer output's normwise bf16 bar
+    for name, gname in (("dgates", "dg"), ("dlogits", "dl"), ("dw_gate", "dw_gate")):
+        assert rel_err(to_np(g[name]), ref[gname]) <= TOL_BF16, name
+
+
+def _check_bounds(g, ref, fwd, dy, host, cfg):
+    u = 2.0 ** -8
+    N, E, k = cfg.n_tokens, cfg.n_experts, cfg.top_k
+    d = dy.shape[1]
+    r, dsp = fwd["route"], fwd["dispatch"]
+    bounds, refs, gots = {}, {}, {}
+    Bg = np.zeros((N, k))
+    Bdx = np.zeros((N, d))
+    dx_rows_gpu = to_np(g["dx_rows"]).astype(np.float64)
+    for e, T in enumerate(ref["terms"]):
+        tt, jj = T["tokens"], T["slots"]
+        a, uu, dh = T["a"], T["u"], T["dh"]
+        sig = 1.0 / (1.0 + np.exp(-a))
+        silu, dsilu = a * sig, sig * (1.0 + a * (1.0 - sig))
+        A = np.abs(T["dO"]) @ np.abs(T["w2"])
+        Ma = np.abs(uu * dsilu) * A + np.abs(dh * uu) * (np.abs(dsilu) + np.abs(a)) + np.abs(T["da"])
+        Mu = np.abs(silu) * A + np.abs(dh) * (np.abs(dsilu * a) + np.abs(silu)) + np.abs(T["du"])
+        X = np.abs(T["X"])
+        for name, B, R in (("dw2", np.abs(T["dO"]).T @ np.abs(T["h"]), ref["dW2"][e]),
+                           ("dw1", Ma.T @ X, ref["dW1"][e]), ("dw3", Mu.T @ X, ref["dW3"][e])):
+            bounds.setdefault(name, []).append(3 * u * B)
+            refs.setdefault(name, []).append(R)
+            gots.setdefault(name, []).append(to_np(g[name][e]))
+        # expert part of dx: per packed row (rows are identical: row_of is bit-exact)
+        Brow = 3 * u * (Ma @ np.abs(T["w1"]) + Mu @ np.abs(T["w3"]))
+        rows = dsp["row_of"][tt, jj]
+        ref_rows = T["da"] @ T["w1"] + T["du"] @ T["w3"]
+        bounds.setdefault("dx_rows", []).append(Brow)
+        refs.setdefault("dx_rows", []).append(ref_rows)
+        gots.setdefault("dx_rows", []).append(dx_rows_gpu[rows])
+        np.add.at(Bdx, tt, Brow)
+        Ao = np.abs(T["h"]) @ np.abs(T["w2"]).T
+        Bg[tt, jj] = 3 * 2 * u * np.sum(np.abs(dy[tt]) * Ao, axis=1)
+    s = r["s"].astype(np.float64)
+    Bs = np.zeros((N, E))
+    if cfg.renormalize:
+        cand = r["cand_ids"][:, :k]
+        sel = np.take_along_axis(s, cand, axis=1)
+        S = sel.sum(axis=1, keepdims=True)
+        np.put_along_axis(Bs, cand, (Bg + (Bg * sel / S).sum(axis=1, keepdims=True)) / S, axis=1)
+    else:
+        for j in range(k):
+            np.add.at(Bs, (np.arange(N), np.maximum(dsp["expert_of"][:, j], 0)), Bg[:, j])
+    ads = np.abs(ref["ds"])
+    Bl = s * (Bs + (s * Bs).sum(axis=1, keepdims=True)) + 1e-5 * (
+        np.abs(ref["dl"]) + s * (ads + (s * ads).sum(axis=1, keepdims=True)))
+    xa = np.abs(oracle.decode_rows(host["x"], cfg.x_dtype))
+    wga = np.abs(host["w_gate"].astype(np.float64))
+    one = {"dgates": (Bg, ref["dg"]), "dlogits": (Bl, ref["dl"]),
+           "dw_gate": (Bl.T @ xa + 1e-5 * np.abs(ref["dl"]).T @ xa, ref["dw_gate"]),
+           "dx": (Bdx + Bl @ wga + 1e-5 * np.abs(ref["dl"]) @ wga, ref["dx"])}
+    if g["dlogit_bias"] is not None:
+        one["dlogit_bias"] = (Bl.sum(axis=0), ref["dlogit_bias"])
+    for name, (B, R) in one.items():
+        bounds[name], refs[name], gots[name] = [B], [R], [to_np(g[name])]
+    worst = {}
+    for name in bounds:
+        for B, R, G in zip(bounds[name], refs[name], gots[name]):
+            err = np.abs(np.asarray(G, np.float64) - R)
+            assert np.all(err <= B), (name, float(np.max(err - B)))
+            if B.size:
+                worst[name] = max(worst.get(name, 0.0), float(np.max(err / np.maximum(B, 1e-300))))
+    print("  max error / bound:", {kk: round(v, 3) for kk, v in worst.items()}, flush=True)
+
+
+ROUTER_CASES = {
+    "c1": W.REDUCED["c1"],                                   # Switch, fp32 x, capacity drops
+    "c2": W.REDUCED["c2"],                                   # renormalised top-2
+    "c3": W.REDUCED["c3"],                                   # E = 64, top-8, selection bias
+    "c4_no_noise": W.REDUCED["c4"].with_(name="c4_reduced_no_noise", noisy=False),  # reroute
+}
+
+
+@pytest.mark.parametrize("key", list(ROUTER_CASES))
+def test_router_backward_fp32_against_oracle(moe, key):
+    """The router's backward alone for random gate gradients: fp32 arithmetic
+    only, so the fp32 bar (1e-5 relative) applies element by element."""
+    cfg = ROUTER_CASES[key]
+    print("router backward", key, flush=True)
+    inp = W.make_inputs(cfg, "cpu")
+    host = host_inputs(inp)
+    fwd = oracle.layer_forward(cfg, host["x"], cfg.x_dtype, host["w_gate"], experts_of(host),
+                               None, host["logit_bias"], host["select_bias"], host["w_noise"],
+                               tokens=np.arange(0))
+    rng = np.random.default_rng(cfg.seed + 77)
+    N, E, k, d = cfg.n_tokens, cfg.n_experts, cfg.top_k, cfg.d_model
+    dsp = fwd["dispatch"]
+    dg = np.where(dsp["row_of"] >= 0, rng.standard_normal((N, k)), 0.0).astype(np.float32)
+    X = oracle.decode_rows(host["x"], cfg.x_dtype)
+    ref = OB.router_backward(cfg, X, host["w_gate"], fwd, dg, 0.3, 0.05, host["logit_bias"])
+    c = lambda a, dt=None: torch.from_numpy(np.ascontiguousarray(a if dt is None else a.astype(dt))).cuda()
+    f32 = dict(dtype=torch.float32, device="cuda")
+    out = dict(dlogits=torch.full((N, E), 7.0, **f32), dw_gate=torch.full((E, d), 7.0, **f32),
+               dx=torch.full((N, d), 7.0, **f32),
+               dlogit_bias=None if host["logit_bias"] is None else torch.full((E,), 7.0, **f32))
+    moe.moe_router_backward(dev_x(inp), c(host["w_gate"]), c(fwd["logits"]),
+                            c(fwd["route"]["cand_ids"]), c(dsp["expert_of"]), c(dsp["row_of"]),
+                            c(dg), c(dsp["counts_routed"]), out["dlogits"], out["dw_gate"],
+                            out["dx"], top_k=k, renormalize=cfg.renormalize, alpha=0.3,
+                            beta=0.05, dlogit_bias=out["dlogit_bias"])
+    torch.cuda.synchronize()
+    dl = ref["dl"]
+    got = to_np(out["dlogits"])
+    assert np.max(np.abs(got - dl)) <= 1e-5 * np.max(np.abs(dl))
+    # each dl is within e_l = 1e-5 max|dl|; the sums over it add their fp32 rounding
+    adl, ax = np.abs(dl), np.abs(X)
+    e_l = 1e-5 * np.max(adl)
+    wga = np.abs(host["w_gate"].astype(np.float64))
+    checks = {"dw_gate": (ref["dw_gate"], e_l * ax.sum(axis=0)[None, :] + 1e-5 * (adl.T @ ax)),
+              "dx": (ref["dx"], e_l * wga.sum(axis=0)[None, :] + 1e-5 * (adl @ wga))}
+    if out["dlogit_bias"] is not None:
+        checks["dlogit_bias"] = (ref["dlogit_bias"], e_l * N + 1e-5 * adl.sum(axis=0))
+    for name, (R, B) in checks.items():
+        err = np.abs(to_np(out[name]).astype(np.float64) - R)
+        assert np.all(err <= B), (name, float(np.max(err / B)))
+
+
+def dev_x(inp):
+    return inp["x"].cuda()
