@@ -1,6 +1,7 @@
 """Benchmark: one MoE FFN layer forward per step on one MI355X, through libmoe.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4|c5|c6]
+                [--backward]
 
 A step is one pass of the whole layer: router GEMM + fp32 softmax + top-k,
 dispatch (capacity, packing, row gather), the grouped expert FFN (+ shared
@@ -14,6 +15,13 @@ gate/up with fused SwiGLU + GEMM 2 down) is the dominant kernel group; its
 duration is measured with HIP events on the launch stream inside the timed
 region. cpu_baseline: the CPU oracle (fp64 FFNs) timed on a bounded sample of
 the same workload on this host's cores.
+
+--backward: a step is one training pass of the layer instead: the training
+forward (which keeps the experts' pre-activations) and the backward pass of
+L = <dy, y> + 0.01 Switch aux + 0.001 z-loss (combine backward, grouped FFN
+backward, router backward). The dominant kernel group is the grouped FFN
+backward (four bf16 MFMA GEMMs: data and weight gradients of both expert
+GEMMs, 12 d d_ff FLOPs per kept assignment).
 """
 import argparse
 import json
@@ -41,6 +49,8 @@ def parse():
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="extra steps timed one by one after writing a 512 MiB buffer "
                          "(evicts the 256 MB Infinity Cache); reported beside the warm run")
+    ap.add_argument("--backward", action="store_true",
+                    help="time a training step (forward + backward) instead of the forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB read + 1 GiB write streaming kernel (torch.neg) "
                          "to calibrate the HBM byte counters")
@@ -157,12 +167,146 @@ def cpu_model():
     return "unknown"
 
 
+def cpu_baseline_backward(cfg, dev, sample_tokens, alpha, beta):
+    """Time the CPU oracle's layer forward + backward on the first
+    `sample_tokens` tokens of the workload as their own batch."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from oracle import backward as OB
+
+    def host(t):
+        if t is None:
+            return None
+        t = t.detach().contiguous().cpu()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16)
+        return t.numpy()
+
+    S = min(sample_tokens, cfg.n_tokens)
+    scfg = cfg.with_(n_tokens=S)
+    h = {k: host(v) for k, v in dev.items() if k != "x"}
+    hx = host(dev["x"][:S])
+    experts = oracle.ExpertSource(h)
+    dy = np.random.default_rng(0).standard_normal((S, cfg.d_model))
+    oracle.lib()
+    t0 = time.perf_counter()
+    fwd = oracle.layer_forward(scfg, hx, cfg.x_dtype, h["w_gate"], experts, None,
+                               h.get("logit_bias"), h.get("select_bias"), h.get("w_noise"))
+    OB.layer_backward(scfg, hx, cfg.x_dtype, h["w_gate"], experts, fwd, dy, alpha, beta,
+                      logit_bias=h.get("logit_bias"))
+    dt = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    return {"value": S / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "oracle layer forward + backward (fp32 routing, fp64 FFNs and gradients) "
+                      "on the first %d tokens of the workload as one batch; %.1f s; CPU: %s"
+                      % (S, dt, cpu_model())}
+
+
+def bench_backward(args):
+    import numpy as np
+    import torch
+
+    import sparse_mixture_experts_47_amd as moe
+    import workloads as W
+
+    alpha, beta = 0.01, 0.001
+    cfg = W.CONFIGS[args.workload]
+    torch.cuda.set_device(0)
+    dev = W.make_inputs(cfg, "cuda")
+    xdt = torch.float32 if cfg.x_dtype == W.F32 else torch.bfloat16
+    layer = moe.MoELayer(moe.spec_from_config(cfg), dev, x_dtype=xdt, train=True)
+    x = dev["x"]
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    dy = torch.randn((cfg.n_tokens, cfg.d_model), generator=g, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(e=None):
+        if e is not None:
+            e[0].record(stream)
+        layer.forward(x, stats=False)
+        if e is not None:
+            e[1].record(stream)
+        b = layer._bwd
+        moe.moe_combine_backward(dy, layer.y_rows, layer.row_of, layer.gates, b[0]["d_rows"],
+                                 b[0]["dgates"])
+        if e is not None:
+            e[2].record(stream)
+        rows, index = layer._packed_rows(x)
+        moe.moe_grouped_ffn_backward(layer.ffn, rows, layer.offsets, layer.preact, layer.h,
+                                     b[0]["d_rows"], b[0]["dx_rows"], b[0]["dw1"], b[0]["dw3"],
+                                     b[0]["dw2"], row_index=index, max_rows=layer.R, ws=b[1])
+        if e is not None:
+            e[3].record(stream)
+        moe.moe_router_backward(x, dev["w_gate"], layer.logits, layer.cand_ids, layer.expert_of,
+                                layer.row_of, b[0]["dgates"], layer.counts_routed,
+                                b[0]["dlogits"], b[0]["dw_gate"], b[0]["dx"],
+                                top_k=cfg.top_k, renormalize=cfg.renormalize, alpha=alpha,
+                                beta=beta, dx_rows=b[0]["dx_rows"],
+                                dlogit_bias=b[0]["dlogit_bias"], ws=b[2])
+        if e is not None:
+            e[4].record(stream)
+
+    moe.layer_backward(layer, x, dy, alpha, beta)  # allocates the backward buffers
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    names = ["forward_train", "combine_backward", "grouped_ffn_backward", "router_backward"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        step(ev[s_])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    samples = {n: [ev[s_][i].elapsed_time(ev[s_][i + 1]) for s_ in range(args.steps)]
+               for i, n in enumerate(names)}
+    counts = layer.counts_kept.cpu().numpy()
+    touched = int((counts > 0).sum())
+    R = int(counts.sum())
+    d, F = cfg.d_model, cfg.d_ff
+    flops = 12.0 * d * F * R
+    ms_bwd_ffn = float(np.median(samples["grouped_ffn_backward"]))
+    tflops = flops / (ms_bwd_ffn * 1e-3) / 1e12
+    ms_step = elapsed * 1e3 / args.steps
+    out = {
+        "metric": "MoE-layer training-step tokens/sec (forward + backward) + grouped-GEMM "
+                  "backward % MFMA peak, 1 MI355X",
+        "value": round(cfg.n_tokens / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name + "_training_step", "n_tokens": cfg.n_tokens,
+                   "d_model": d, "n_experts": cfg.n_experts, "d_ff": F, "top_k": cfg.top_k,
+                   "act": ["relu", "gelu", "swiglu"][cfg.act], "loss": "<dy,y> + 0.01 aux + "
+                   "0.001 z", "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": "moe_grouped_ffn_backward (data and weight gradients of both "
+                               "expert GEMMs, SwiGLU backward fused)",
+                     "per_launch": {"flops": flops, "avg_ms": round(ms_bwd_ffn, 4),
+                                    "kept_assignments": R, "touched_experts": touched}},
+        "per_call_ms_median": {k: round(float(np.median(v)), 4) for k, v in samples.items()},
+        "per_call_ms_min": {k: round(float(np.min(v)), 4) for k, v in samples.items()},
+    }
+    if not args.no_cpu_baseline:
+        S = args.cpu_sample or 256
+        out["cpu_baseline"] = cpu_baseline_backward(cfg, dev, S, alpha, beta)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.backward:
+        return bench_backward(args)
     import numpy as np
     import torch
 

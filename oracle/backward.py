@@ -172,26 +172,53 @@ def layer_backward(cfg, x, x_dt, w_gate, experts, fwd, dy, alpha=0.0, beta=0.0,
     return out
 
 
+def weight_grad_features(X, dO, w1, w3, w2, fs, want_dW=True):
+    """One SwiGLU expert's weight gradients restricted to the features fs
+    (indices into d_ff): rows fs of dW1 and dW3 ([len(fs)][d]) and columns fs
+    of dW2 ([d][len(fs)]), from its rows X [n][d] and output gradients dO
+    [n][d] (fp64). The same definitions as expert_backward, evaluated only
+    where asked, so full-size layers can be sampled. Also returns the
+    intermediates a, u, h, dh, da, du [n][len(fs)] (only these when
+    want_dW is false)."""
+    fs = np.asarray(fs)
+    a = X @ w1[fs].T
+    u = X @ w3[fs].T
+    sig = 1.0 / (1.0 + np.exp(-a))
+    h = a * sig * u
+    dh = dO @ w2[:, fs]
+    da = dh * u * sig * (1.0 + a * (1.0 - sig))
+    du = dh * a * sig
+    out = dict(a=a, u=u, h=h, dh=dh, da=da, du=du)
+    if want_dW:
+        out.update(dW1=da.T @ X, dW3=du.T @ X, dW2=dO.T @ h)
+    return out
+
+
 def router_backward(cfg, X, w_gate, fwd, dg, alpha=0.0, beta=0.0, logit_bias=None,
-                    w_noise=None):
+                    w_noise=None, rows=None, n_total=None):
     """Router part of the backward pass for given gate gradients dg [N][k]
     (fp64; 0 for dropped slots): gates -> scores (+ auxiliary loss) ->
     logits (+ z-loss) -> (noise) -> W_g, logit bias and the token rows X
     (fp64 [N][d]). fwd gives the forward's route (s, lse, cand_ids) and
     dispatch (expert_of, row_of, counts_routed). Returns dict(ds, dl, dw_gate,
     dlogit_bias, dw_noise, dx) with dx the router's share of the token
-    gradient."""
+    gradient. rows (optional): X and dg hold only these tokens of the batch
+    (its size n_total sets the 1/N of the auxiliary and z-loss terms and of
+    f_e); the per-token formulas are evaluated for them alone."""
     r, dsp = fwd["route"], fwd["dispatch"]
-    N, E, k = X.shape[0], cfg.n_experts, cfg.top_k
-    kept = dsp["row_of"] >= 0
-    exp_of = dsp["expert_of"]
+    rows = np.arange(X.shape[0]) if rows is None else np.asarray(rows)
+    N = X.shape[0] if n_total is None else int(n_total)
+    E, k = cfg.n_experts, cfg.top_k
+    kept = dsp["row_of"][rows] >= 0
+    exp_of = dsp["expert_of"][rows]
     dg = np.where(kept, np.asarray(dg, np.float64), 0.0)
-    s = r["s"].astype(np.float64)
-    ds = np.zeros((N, E))
+    s = r["s"][rows].astype(np.float64)
+    n = len(rows)
+    ds = np.zeros((n, E))
     if cfg.renormalize:
         # g_j = s_{c_j} / S, S = sum over the k selected candidates:
         # dL/ds_{c_i} = (dg_i - sum_j dg_j g_j) / S
-        cand = r["cand_ids"][:, :k]
+        cand = r["cand_ids"][rows][:, :k]
         sel = np.take_along_axis(s, cand, axis=1)
         S = sel.sum(axis=1, keepdims=True)
         gk = sel / S
@@ -200,14 +227,14 @@ def router_backward(cfg, X, w_gate, fwd, dg, alpha=0.0, beta=0.0, logit_bias=Non
     else:
         # Switch gate: g = s of the expert actually used (after a reroute)
         for j in range(k):
-            np.add.at(ds, (np.arange(N), np.maximum(exp_of[:, j], 0)), dg[:, j])
+            np.add.at(ds, (np.arange(n), np.maximum(exp_of[:, j], 0)), dg[:, j])
     # auxiliary loss: d(alpha E sum_e f_e P_e)/ds_te = alpha E f_e / N
     f = dsp["counts_routed"].astype(np.float64) / (N * k)
     ds += alpha * E * f[None, :] / N
 
     # softmax -> logits (+ z-loss: d(lse_t^2 / N)/dl_te = 2 lse_t s_te / N)
     dl = s * (ds - (s * ds).sum(axis=1, keepdims=True))
-    dl += beta * 2.0 * r["lse"][:, None] * s / N
+    dl += beta * 2.0 * r["lse"][rows][:, None] * s / N
 
     # noise: H = l + z * softplus(v); dH/dl = 1, dH/dv = z * sigmoid(v)
     wg = np.asarray(w_gate, np.float32).astype(np.float64)
@@ -216,7 +243,7 @@ def router_backward(cfg, X, w_gate, fwd, dg, alpha=0.0, beta=0.0, logit_bias=Non
     if w_noise is not None:
         wn = np.asarray(w_noise, np.float32).astype(np.float64)
         v = X @ wn.T
-        z = hash_normal_grid(cfg.noise_seed, N, E).astype(np.float64)
+        z = hash_normal_grid(cfg.noise_seed, N, E)[rows].astype(np.float64)
         dv = dl * z / (1.0 + np.exp(-v))
         dw_noise = dv.T @ X
         dx += dv @ wn

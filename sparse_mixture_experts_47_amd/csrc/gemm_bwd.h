@@ -147,45 +147,77 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bwd_kernel(BwdArgs g) {
   const int m0 = mt * BM, n0 = nt * BN;
   const int KT = (kcount + BK - 1) / BK;
 
-  // ---- one stage of loads: A then B segments, 16 bytes per lane each
+  // ---- per-lane source pointers at k = 0 for each 1 KB segment (16 bytes a
+  // lane); a K tile then adds a uniform offset. K-slow rows past an
+  // expert's count (DENSE tail tile) are clamped to its last row.
+  const uint16_t* asrc[A_IT];
+  int arow[A_IT];
+#pragma unroll
+  for (int i = 0; i < A_IT; ++i) {
+    const int seg = wave + i * NW;
+    if constexpr (MODE == MODE_ROWS) {
+      const int r = seg * 8 + (lane >> 3);
+      int row = row0 + r;
+      row = row < row_end ? row : row_end - 1;
+      const int c = (lane & 7) ^ moe_gemm::chunk_swz<64>(r);
+      asrc[i] = g.A + (size_t)row * g.lda + c * 8;
+      arow[i] = r;
+    } else {
+      constexpr int CPR = BM / 8;
+      const int r = seg * A_SEG_ROWS + lane / CPR;
+      const int c = ks_phys(r, lane % CPR);
+      asrc[i] = g.A + (size_t)kbeg * g.lda + m0 + c * 8;
+      arow[i] = r;
+    }
+  }
+  const uint16_t* bsrc0[B_IT];
+  const uint16_t* bsrc1[B_IT];
+  int brow[B_IT];
+#pragma unroll
+  for (int i = 0; i < B_IT; ++i) {
+    const int seg = wave + i * NW;
+    constexpr int CPR = BN / 8;
+    const int r = seg * B_SEG_ROWS + lane / CPR;
+    const int c = ks_phys(r, lane % CPR);
+    brow[i] = r;
+    if constexpr (MODE == MODE_ROWS) {
+      const size_t col = (size_t)e * g.b_expert + n0 + c * 8;
+      bsrc0[i] = g.B0 + col + (size_t)r * g.ldb;
+      bsrc1[i] = g.B1 ? g.B1 + col + (size_t)r * g.ldb : nullptr;
+    } else {
+      bsrc0[i] = g.B0 + (size_t)kbeg * g.ldb + n0 + c * 8;
+      bsrc1[i] = nullptr;
+    }
+  }
+
   auto issue = [&](int kt, int stage) {
     uint16_t* base = smem + stage * STAGE;
     const int k0 = kt * BK;
+    const bool tail = MODE == MODE_DENSE && k0 + BK > kcount;
 #pragma unroll
     for (int i = 0; i < A_IT; ++i) {
       const int seg = wave + i * NW;
       const uint16_t* src;
       if constexpr (MODE == MODE_ROWS) {
-        const int r = seg * 8 + (lane >> 3);
-        int row = row0 + r;
-        row = row < row_end ? row : row_end - 1;
-        const int c = (lane & 7) ^ moe_gemm::chunk_swz<64>(r);
-        src = g.A + (size_t)row * g.lda + k0 + c * 8;
+        src = asrc[i] + k0;
       } else {
-        constexpr int CPR = BM / 8;
-        const int r = seg * A_SEG_ROWS + lane / CPR;
-        const int kr = min(k0 + r, kcount - 1);
-        const int c = ks_phys(r, lane % CPR);
-        src = g.A + (size_t)(kbeg + kr) * g.lda + m0 + c * 8;
+        const int kr = tail ? min(k0 + arow[i], kcount - 1) : k0 + arow[i];
+        src = asrc[i] + (size_t)kr * g.lda;
       }
       __builtin_amdgcn_global_load_lds(
           (const void*)src, (__attribute__((address_space(3))) void*)(base + seg * 512), 16, 0, 0);
     }
+    const bool second = MODE == MODE_ROWS && g.B1 && k0 >= g.kseg;
+    const size_t kofs = (size_t)(second ? k0 - g.kseg : k0) * g.ldb;
 #pragma unroll
     for (int i = 0; i < B_IT; ++i) {
       const int seg = wave + i * NW;
-      constexpr int CPR = BN / 8;
-      const int r = seg * B_SEG_ROWS + lane / CPR;
-      const int c = ks_phys(r, lane % CPR);
       const uint16_t* src;
       if constexpr (MODE == MODE_ROWS) {
-        const int k = k0 + r;
-        const uint16_t* w = (g.B1 && k >= g.kseg) ? g.B1 + (size_t)(k - g.kseg) * g.ldb
-                                                  : g.B0 + (size_t)k * g.ldb;
-        src = w + (size_t)e * g.b_expert + n0 + c * 8;
+        src = (second ? bsrc1[i] : bsrc0[i]) + kofs;
       } else {
-        const int kr = min(k0 + r, kcount - 1);
-        src = g.B0 + (size_t)(kbeg + kr) * g.ldb + n0 + c * 8;
+        const int kr = tail ? min(k0 + brow[i], kcount - 1) : k0 + brow[i];
+        src = bsrc0[i] + (size_t)kr * g.ldb;
       }
       __builtin_amdgcn_global_load_lds(
           (const void*)src,
@@ -227,27 +259,44 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bwd_kernel(BwdArgs g) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
   };
 
-  // ---- main loop: NS-stage ring, loads run NS-1 tiles ahead
+  // ---- main loop: NS-stage ring. Per K tile kt (stage kt % NS): the MFMAs
+  // of each 16-wide K step run while the next step's fragments are read;
+  // after the last step's reads, wait for this wave's reads and for tile
+  // kt+1's loads, barrier (no wave reads stage kt % NS any more), issue the
+  // loads of tile kt+NS into it, read the first fragments of tile kt+1, and
+  // only then run the last MFMAs of tile kt, so the barrier and the first
+  // LDS reads of the next tile hide under MFMAs and NS tiles stay in flight.
+  // Only the A operand of a DENSE tile is masked: rows past the expert's
+  // count repeat its last row (finite), so a zero A gives a zero product.
+  auto kvalid_of = [&](int kt) { return MODE == MODE_DENSE ? min(BK, kcount - kt * BK) : BK; };
 #pragma unroll
-  for (int j = 0; j < NS - 1; ++j)
+  for (int j = 0; j < NS; ++j)
     if (j < KT) issue(j, j);
-  for (int kt = 0; kt < KT; ++kt) {
-    if (kt + NS - 2 < KT) moe_gemm::wait_vmcnt<(NS - 2) * LPT>();
+  Frags fr[2];
+  if (KT > 0) {
+    if (KT > NS - 1) moe_gemm::wait_vmcnt<(NS - 1) * LPT>();
     else moe_gemm::wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();  // tile kt visible; every wave is done with tile kt-1
+    __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    if (kt + NS - 1 < KT) issue(kt + NS - 1, (kt + NS - 1) % NS);
+    read_frags(fr[0], 0, 0, kvalid_of(0));
+  }
+  for (int kt = 0; kt < KT; ++kt) {
     const int st = kt % NS;
-    // only the A operand of a DENSE tile is masked: rows past the expert's
-    // count repeat its last row (finite), so a zero A gives a zero product
-    const int kvalid = MODE == MODE_DENSE ? min(BK, kcount - kt * BK) : BK;
-    Frags fr[2];
-    read_frags(fr[0], st, 0, kvalid);
+    const int kv = kvalid_of(kt);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      if (kk + 1 < KK) read_frags(fr[(kk + 1) & 1], st, kk + 1, kvalid);
+    for (int kk = 0; kk + 1 < KK; ++kk) {
+      read_frags(fr[(kk + 1) & 1], st, kk + 1, kv);
       mfma(fr[kk & 1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+    if (kt + NS - 1 < KT) moe_gemm::wait_vmcnt<(NS - 2) * LPT>();
+    else moe_gemm::wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + NS < KT) issue(kt + NS, st);
+    if (kt + 1 < KT) read_frags(fr[KK & 1], (kt + 1) % NS, 0, kvalid_of(kt + 1));
+    mfma(fr[(KK - 1) & 1]);
     __builtin_amdgcn_sched_barrier(0);
   }
 

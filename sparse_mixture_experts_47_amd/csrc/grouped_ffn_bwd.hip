@@ -16,9 +16,32 @@
 // sums it back to tokens.
 #include "gemm_bwd.h"
 
+// Tile shapes: 256-row M tiles; N tile width and the wave grid per tile space
+#ifndef MOE_BWD_ROWS_BN
+#define MOE_BWD_ROWS_BN 256
+#endif
+#ifndef MOE_BWD_ROWS_WGM
+#define MOE_BWD_ROWS_WGM 4
+#endif
+#ifndef MOE_BWD_DENSE_BN
+#define MOE_BWD_DENSE_BN 256
+#endif
+#ifndef MOE_BWD_DENSE_WGM
+#define MOE_BWD_DENSE_WGM 4
+#endif
+// N tiles that run side by side over consecutive M tiles (L2 reuse of both operands)
+#ifndef MOE_BWD_ROWS_GN
+#define MOE_BWD_ROWS_GN 2
+#endif
+#ifndef MOE_BWD_DENSE_GN
+#define MOE_BWD_DENSE_GN 16
+#endif
+
 namespace {
 
 constexpr int kBwdBM = 256;
+constexpr int kRowsBN = MOE_BWD_ROWS_BN, kDenseBN = MOE_BWD_DENSE_BN;
+constexpr int kRowsWGM = MOE_BWD_ROWS_WGM, kDenseWGM = MOE_BWD_DENSE_WGM;
 
 // tile_start[e] = sum over e' < e of ceil(rows_e' / bm)
 __global__ __launch_bounds__(256) void bwd_tile_table_kernel(const int32_t* __restrict__ offsets,
@@ -106,9 +129,9 @@ moe_status grouped_ffn_backward_launch(const moe_ffn_weights* w, const void* x_r
   g.E = E;
   g.offsets = offsets;
   g.tile_start = ts;
-  g.group_n = 2;
   g.max_mt = max_mt;
   BwdArgs d2 = g;
+  d2.group_n = MOE_BWD_ROWS_GN;
   d2.A = d_out;
   d2.lda = d;
   d2.B0 = (const uint16_t*)w->w2;  // [E][d][F]: row k = feature of d
@@ -116,15 +139,16 @@ moe_status grouped_ffn_backward_launch(const moe_ffn_weights* w, const void* x_r
   d2.b_expert = (long long)d * F;
   d2.N = F;
   d2.K = d;
-  d2.n_tiles_n = F / 256;
+  d2.n_tiles_n = F / kRowsBN;
   d2.pre = preact;
   d2.dpre = dpre;
-  hipError_t err = launch_bwd<MODE_ROWS, BEPI_DSWIGLU, 256, 256, 2, 4, 2>(
-      d2, (long long)max_mt * ((d2.n_tiles_n + 1) / 2 * 2), st);
+  hipError_t err = launch_bwd<MODE_ROWS, BEPI_DSWIGLU, 256, kRowsBN, 2, kRowsWGM, 8 / kRowsWGM>(
+      d2, (long long)max_mt * ((d2.n_tiles_n + d2.group_n - 1) / d2.group_n * d2.group_n), st);
   if (err != hipSuccess) return bwd_status(err, "backward data gradient of GEMM 2");
 
   // weight gradient of GEMM 2: dW2[e][c][f] = sum_r dO[r][c] h[r][f]
   BwdArgs w2 = g;
+  w2.group_n = MOE_BWD_DENSE_GN;
   w2.A = d_out;
   w2.lda = d;
   w2.B0 = h;
@@ -134,13 +158,14 @@ moe_status grouped_ffn_backward_launch(const moe_ffn_weights* w, const void* x_r
   w2.mseg = d;
   w2.C0 = dw2;
   w2.ldc = F;
-  w2.n_tiles_n = F / 256;
-  err = launch_bwd<MODE_DENSE, BEPI_F32, 256, 256, 2, 4, 2>(
-      w2, (long long)E * (d / 256) * ((w2.n_tiles_n + 1) / 2 * 2), st);
+  w2.n_tiles_n = F / kDenseBN;
+  err = launch_bwd<MODE_DENSE, BEPI_F32, 256, kDenseBN, 2, kDenseWGM, 8 / kDenseWGM>(
+      w2, (long long)E * (d / 256) * ((w2.n_tiles_n + w2.group_n - 1) / w2.group_n * w2.group_n), st);
   if (err != hipSuccess) return bwd_status(err, "backward weight gradient of GEMM 2");
 
   // data gradient of GEMM 1: dX = [da | du] [W1 ; W3], K = 2F
   BwdArgs d1 = g;
+  d1.group_n = MOE_BWD_ROWS_GN;
   d1.A = dpre;
   d1.lda = 2 * F;
   d1.B0 = (const uint16_t*)w->w1;  // [E][F][d]
@@ -150,15 +175,16 @@ moe_status grouped_ffn_backward_launch(const moe_ffn_weights* w, const void* x_r
   d1.b_expert = (long long)F * d;
   d1.N = d;
   d1.K = 2 * F;
-  d1.n_tiles_n = d / 256;
+  d1.n_tiles_n = d / kRowsBN;
   d1.C0 = dx_rows;
   d1.ldc = d;
-  err = launch_bwd<MODE_ROWS, BEPI_F32, 256, 256, 2, 4, 2>(
-      d1, (long long)max_mt * ((d1.n_tiles_n + 1) / 2 * 2), st);
+  err = launch_bwd<MODE_ROWS, BEPI_F32, 256, kRowsBN, 2, kRowsWGM, 8 / kRowsWGM>(
+      d1, (long long)max_mt * ((d1.n_tiles_n + d1.group_n - 1) / d1.group_n * d1.group_n), st);
   if (err != hipSuccess) return bwd_status(err, "backward data gradient of GEMM 1");
 
   // weight gradients of GEMM 1: rows m < F of [da | du]^T x -> dW1, the rest -> dW3
   BwdArgs w1 = g;
+  w1.group_n = MOE_BWD_DENSE_GN;
   w1.A = dpre;
   w1.lda = 2 * F;
   w1.B0 = xp;
@@ -169,9 +195,9 @@ moe_status grouped_ffn_backward_launch(const moe_ffn_weights* w, const void* x_r
   w1.C0 = dw1;
   w1.C1 = dw3;
   w1.ldc = d;
-  w1.n_tiles_n = d / 256;
-  err = launch_bwd<MODE_DENSE, BEPI_F32, 256, 256, 2, 4, 2>(
-      w1, (long long)E * (2 * F / 256) * ((w1.n_tiles_n + 1) / 2 * 2), st);
+  w1.n_tiles_n = d / kDenseBN;
+  err = launch_bwd<MODE_DENSE, BEPI_F32, 256, kDenseBN, 2, kDenseWGM, 8 / kDenseWGM>(
+      w1, (long long)E * (2 * F / 256) * ((w1.n_tiles_n + w1.group_n - 1) / w1.group_n * w1.group_n), st);
   return bwd_status(err, "backward weight gradient of GEMM 1");
 }
 

@@ -129,3 +129,117 @@ def test_full_size_expert_choice(moe):
     thr = np.sort(s, axis=0)[::-1][ec["capacity"] - 1]
     far = np.abs(s - thr[None, :]) >= MARGIN * thr[None, :]
     assert np.all((to_np(layer.row_of) >= 0)[far] == (ec["row_of"] >= 0)[far])
+
+
+def test_full_size_backward_sampled():
+    """Mixtral-shaped training step (4096 tokens, 8 experts of 14336): the
+    GPU's backward from the oracle's logits, checked on sampled entries the
+    fp64 oracle computes one by one -- gate gradients and token gradients of
+    sampled tokens, and sampled features of every expert's weight gradients
+    -- each within the first-order bf16 error bound times 3 (u = 2^-8; the
+    bounds are those of the reduced-size backward test)."""
+    import sparse_mixture_experts_47_amd as moe
+    from oracle import backward as OB
+    require_gpu()
+    cfg = W.CONFIGS["c2"]
+    print("full-size backward c2", flush=True)
+    dev = W.make_inputs(cfg, "cuda")
+    torch.cuda.synchronize()
+    hx = host_view(dev["x"])
+    hwg = host_view(dev["w_gate"])
+    H, _ = oracle.router_logits(hx, cfg.x_dtype, hwg, None, None, 0)
+    fwd = oracle.layer_forward(cfg, hx, cfg.x_dtype, hwg, DeviceExperts(dev), None, None, None,
+                               None, logits=H, tokens=np.arange(0))
+    layer = moe.MoELayer(moe.spec_from_config(cfg), dev, x_dtype=torch.bfloat16, train=True)
+    layer.forward(dev["x"], logits_in=torch.from_numpy(H).cuda())
+    g = torch.Generator(device="cuda").manual_seed(99)
+    dy = torch.randn((cfg.n_tokens, cfg.d_model), generator=g, device="cuda")
+    alpha, beta = 0.01, 0.001
+    grads = moe.layer_backward(layer, dev["x"], dy, alpha, beta)
+    torch.cuda.synchronize()
+    dsp = fwd["dispatch"]
+    for name in ("row_of", "expert_of", "counts_routed"):
+        assert np.array_equal(to_np(getattr(layer, name)), dsp[name]), name
+    u = 2.0 ** -8
+    X = oracle.decode_rows(hx, cfg.x_dtype)
+    dyh = to_np(dy).astype(np.float64)
+    gates = dsp["gates"].astype(np.float64)
+    experts = DeviceExperts(dev)
+    wts = {}
+
+    def weights(e):
+        if e not in wts:
+            w = experts.get(e)
+            wts[e] = tuple(OB.decode_weight(w[n], cfg.w_dtype) for n in ("w1", "w3", "w2"))
+        return wts[e]
+
+    def bound_terms(Xr, dO, w1, w3, w2, fs=None):
+        """the oracle's intermediates and the first-order error terms (/u) of da, du"""
+        want = fs is not None
+        if fs is None:
+            fs = np.arange(w1.shape[0])
+        p = OB.weight_grad_features(Xr, dO, w1, w3, w2, fs, want_dW=want)
+        a, uu, dh = p["a"], p["u"], p["dh"]
+        sig = 1.0 / (1.0 + np.exp(-a))
+        silu, dsilu = a * sig, sig * (1.0 + a * (1.0 - sig))
+        A = np.abs(dO) @ np.abs(w2[:, fs])
+        Ma = np.abs(uu * dsilu) * A + np.abs(dh * uu) * (np.abs(dsilu) + np.abs(a)) + np.abs(p["da"])
+        Mu = np.abs(silu) * A + np.abs(dh) * (np.abs(dsilu * a) + np.abs(silu)) + np.abs(p["du"])
+        return p, Ma, Mu
+
+    rng = np.random.default_rng(2)
+    # ---- sampled features of every expert's weight gradients
+    for e in range(cfg.n_experts):
+        tt, jj = np.nonzero((dsp["row_of"] >= 0) & (dsp["expert_of"] == e))
+        w1, w3, w2 = weights(e)
+        dO = gates[tt, jj][:, None] * dyh[tt]
+        fs = np.sort(rng.choice(cfg.d_ff, 3, replace=False))
+        p, Ma, Mu = bound_terms(X[tt], dO, w1, w3, w2, fs)
+        Xa = np.abs(X[tt])
+        for name, got, ref, B in (
+                ("dw1", to_np(grads["dw1"][e][fs]), p["dW1"], 3 * u * Ma.T @ Xa),
+                ("dw3", to_np(grads["dw3"][e][fs]), p["dW3"], 3 * u * Mu.T @ Xa),
+                ("dw2", to_np(grads["dw2"][e][:, fs]), p["dW2"],
+                 3 * u * np.abs(dO).T @ np.abs(p["h"]))):
+            err = np.abs(got.astype(np.float64) - ref)
+            assert np.all(err <= B), (name, e, float(np.max(err / B)))
+    # ---- sampled tokens: gate gradients and token gradients
+    sample = np.sort(rng.choice(cfg.n_tokens, 6, replace=False))
+    k = cfg.top_k
+    dg = np.zeros((len(sample), k))
+    Bg = np.zeros((len(sample), k))
+    dx_exp = np.zeros((len(sample), cfg.d_model))
+    Bdx = np.zeros((len(sample), cfg.d_model))
+    for i, t in enumerate(sample):
+        for j in range(k):
+            if dsp["row_of"][t, j] < 0:
+                continue
+            e = int(dsp["expert_of"][t, j])
+            w1, w3, w2 = weights(e)
+            dO = gates[t, j] * dyh[t:t + 1]
+            p, Ma, Mu = bound_terms(X[t:t + 1], dO, w1, w3, w2)
+            o = p["h"] @ w2.T
+            dg[i, j] = float(dyh[t] @ o[0])
+            Bg[i, j] = 3 * 2 * u * float(np.abs(dyh[t]) @ (np.abs(p["h"]) @ np.abs(w2).T)[0])
+            dx_exp[i] += (p["da"] @ w1 + p["du"] @ w3)[0]
+            Bdx[i] += 3 * u * (Ma @ np.abs(w1) + Mu @ np.abs(w3))[0]
+    err = np.abs(to_np(grads["dgates"])[sample] - dg)
+    assert np.all(err <= Bg), float(np.max(err / np.maximum(Bg, 1e-300)))
+    rb = OB.router_backward(cfg, X[sample], hwg, fwd, dg, alpha, beta, rows=sample,
+                            n_total=cfg.n_tokens)
+    s = fwd["route"]["s"][sample].astype(np.float64)
+    cand = fwd["route"]["cand_ids"][sample][:, :k]
+    sel = np.take_along_axis(s, cand, axis=1)
+    S = sel.sum(axis=1, keepdims=True)
+    Bs = np.zeros_like(s)
+    np.put_along_axis(Bs, cand, (Bg + (Bg * sel / S).sum(axis=1, keepdims=True)) / S, axis=1)
+    ads = np.abs(rb["ds"])
+    Bl = s * (Bs + (s * Bs).sum(axis=1, keepdims=True)) + 1e-5 * (
+        np.abs(rb["dl"]) + s * (ads + (s * ads).sum(axis=1, keepdims=True)))
+    wga = np.abs(hwg.astype(np.float64))
+    err = np.abs(to_np(grads["dlogits"])[sample] - rb["dl"])
+    assert np.all(err <= Bl), float(np.max(err / Bl))
+    ref_dx = dx_exp + rb["dx"]
+    Bx = Bdx + Bl @ wga + 1e-5 * np.abs(rb["dl"]) @ wga
+    err = np.abs(to_np(grads["dx"])[sample] - ref_dx)
+    assert np.all(err <= Bx), float(np.max(err / Bx))

@@ -189,3 +189,27 @@ def test_renormalised_gate_gradient_is_orthogonal_to_scores():
     s = fwd["route"]["s"].astype(np.float64)
     dots = (s * got["ds"]).sum(axis=1)
     assert np.max(np.abs(dots)) < 1e-12 * np.max(np.abs(got["ds"]))
+
+
+def test_sampled_evaluations_equal_full_ones():
+    """The sampled forms used at full size (features of one expert, tokens of
+    the router part) agree with the full computations pinned above."""
+    cfg, x, w, wg, lb, wn, dy = _tiny(k=2, E=4, N=30)
+    fwd, got = _run(cfg, x, w, wg, lb, wn, dy, 0.2, 0.03)
+    X = x.astype(np.float64)
+    dsp = fwd["dispatch"]
+    e = int(np.argmax(dsp["counts_kept"]))
+    tt, jj = np.nonzero((dsp["row_of"] >= 0) & (dsp["expert_of"] == e))
+    dO = dsp["gates"][tt, jj].astype(np.float64)[:, None] * dy[tt]
+    fs = np.array([0, 5, 11])
+    part = B.weight_grad_features(X[tt], dO, w["w1"][e].astype(np.float64),
+                                  w["w3"][e].astype(np.float64), w["w2"][e].astype(np.float64), fs)
+    assert np.allclose(part["dW1"], got["dW1"][e][fs], rtol=1e-12, atol=1e-14)
+    assert np.allclose(part["dW3"], got["dW3"][e][fs], rtol=1e-12, atol=1e-14)
+    assert np.allclose(part["dW2"], got["dW2"][e][:, fs], rtol=1e-12, atol=1e-14)
+    rows = np.array([3, 17, 29])
+    sub = B.router_backward(cfg, X[rows], wg, fwd, got["dg"][rows], 0.2, 0.03, lb, rows=rows,
+                            n_total=cfg.n_tokens)
+    full = B.router_backward(cfg, X, wg, fwd, got["dg"], 0.2, 0.03, lb)
+    for name in ("dl", "ds", "dx"):
+        assert np.allclose(sub[name], full[name][rows], rtol=1e-12, atol=1e-15), name
