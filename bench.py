@@ -229,14 +229,20 @@ def bench_backward(args):
         if e is not None:
             e[1].record(stream)
         b = layer._bwd
+        sh = layer.shared is not None
         moe.moe_combine_backward(dy, layer.y_rows, layer.row_of, layer.gates, b[0]["d_rows"],
-                                 b[0]["dgates"])
+                                 b[0]["dgates"], d_shared=b[0]["d_shared"] if sh else None)
         if e is not None:
             e[2].record(stream)
         rows, index = layer._packed_rows(x)
         moe.moe_grouped_ffn_backward(layer.ffn, rows, layer.offsets, layer.preact, layer.h,
                                      b[0]["d_rows"], b[0]["dx_rows"], b[0]["dw1"], b[0]["dw3"],
                                      b[0]["dw2"], row_index=index, max_rows=layer.R, ws=b[1])
+        if sh:
+            moe.moe_grouped_ffn_backward(layer.shared, x, layer.sh_offsets, layer.preact_sh,
+                                         layer.h_sh, b[0]["d_shared"], b[0]["dx_shared"],
+                                         b[0]["shared_dw1"], b[0]["shared_dw3"],
+                                         b[0]["shared_dw2"], max_rows=cfg.n_tokens, ws=b[1])
         if e is not None:
             e[3].record(stream)
         moe.moe_router_backward(x, dev["w_gate"], layer.logits, layer.cand_ids, layer.expert_of,
@@ -244,6 +250,7 @@ def bench_backward(args):
                                 b[0]["dlogits"], b[0]["dw_gate"], b[0]["dx"],
                                 top_k=cfg.top_k, renormalize=cfg.renormalize, alpha=alpha,
                                 beta=beta, dx_rows=b[0]["dx_rows"],
+                                dx_shared=b[0]["dx_shared"] if sh else None,
                                 dlogit_bias=b[0]["dlogit_bias"], ws=b[2])
         if e is not None:
             e[4].record(stream)
@@ -266,7 +273,7 @@ def bench_backward(args):
     touched = int((counts > 0).sum())
     R = int(counts.sum())
     d, F = cfg.d_model, cfg.d_ff
-    flops = 12.0 * d * F * R
+    flops = 12.0 * d * F * R + 12.0 * d * cfg.shared_d_ff * cfg.n_tokens
     ms_bwd_ffn = float(np.median(samples["grouped_ffn_backward"]))
     tflops = flops / (ms_bwd_ffn * 1e-3) / 1e12
     ms_step = elapsed * 1e3 / args.steps
@@ -287,7 +294,7 @@ def bench_backward(args):
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": None,
                      "kernel": "moe_grouped_ffn_backward (data and weight gradients of both "
-                               "expert GEMMs, SwiGLU backward fused)",
+                               "expert GEMMs, SwiGLU backward fused; routed + shared experts)",
                      "per_launch": {"flops": flops, "avg_ms": round(ms_bwd_ffn, 4),
                                     "kept_assignments": R, "touched_experts": touched}},
         "per_call_ms_median": {k: round(float(np.median(v)), 4) for k, v in samples.items()},

@@ -299,9 +299,9 @@ moe_status moe_balance_stats(int32_t n_tokens, int32_t n_experts, int32_t top_k,
  * auxiliary loss gives the router a gradient for every expert;
  * mkbk-pku.cn "通信与并行", step 5: gradients go back along the forward's
  * routing path. Order of the calls: moe_combine_backward ->
- * moe_grouped_ffn_backward -> moe_router_backward. Scope: token-choice
- * routing without noise; bf16 SwiGLU experts without biases; d_model and
- * d_ff multiples of 256. Gradients come out in fp32 and overwrite their
+ * moe_grouped_ffn_backward (routed experts, and the shared expert if any) ->
+ * moe_router_backward. Scope: token-choice routing without noise; bf16
+ * SwiGLU experts without biases; d_model and d_ff multiples of 256. Gradients come out in fp32 and overwrite their
  * buffers (no accumulation). */
 
 /* Forward of the routed (or shared) experts that also keeps what the
@@ -316,20 +316,25 @@ moe_status moe_grouped_ffn_train(const moe_ffn_weights* w, const void* x_rows,
                                  uint16_t* preact, uint16_t* h, void* workspace, size_t ws_bytes,
                                  void* hip_stream);
 
-/* Backward of the gate-weighted combine y_t = sum_j g_tj o_{row_of[t][j]}:
+/* Backward of the gate-weighted combine y_t = sum_j g_tj o_{row_of[t][j]}
+ * (+ the shared expert's output with gate 1):
  *  dy     [N][d] fp32 upstream gradient
  *  y_rows [R][d] (y_dt F32 or BF16) the expert outputs o of the forward
  *  row_of, gates [N][k] as given to moe_combine
  *  d_rows [R][d] bf16 out: g_tj * dy_t on the row of each kept slot
  *  dgates [N][k] fp32 out: <dy_t, o_row>, 0 for a dropped slot
+ *  d_shared [N][d] bf16 out (dy rounded: the shared expert's output
+ *           gradient) or NULL without a shared expert
  * Deterministic (fixed reduction order). */
 moe_status moe_combine_backward(int32_t n_tokens, int32_t d_model, int32_t top_k,
                                 const float* dy, const void* y_rows, moe_dtype y_dt,
                                 const int32_t* row_of, const float* gates, uint16_t* d_rows,
-                                float* dgates, void* hip_stream);
+                                float* dgates, uint16_t* d_shared, void* hip_stream);
 
-/* Backward of the grouped SwiGLU FFN (per expert e over its packed rows:
- * a = x W1^T, u = x W3^T, h = silu(a) u, o = h W2^T):
+/* Backward of the grouped SwiGLU FFN. The shared expert is the same call
+ * with one expert, offsets {0, N}, row_index NULL and d_rows =
+ * moe_combine_backward's d_shared. Per expert e over its packed rows
+ * (a = x W1^T, u = x W3^T, h = silu(a) u, o = h W2^T):
  *  dh = dO W2; da = dh u silu'(a); du = dh silu(a); dX = da W1 + du W3;
  *  dW2_e = sum_r dO_r^T h_r; dW1_e = sum_r da_r^T x_r; dW3_e = sum_r du_r^T x_r.
  *  x_rows, row_index, offsets, max_rows: as given to moe_grouped_ffn_train
@@ -352,20 +357,22 @@ moe_status moe_grouped_ffn_backward(const moe_ffn_weights* w, const void* x_rows
                                     void* hip_stream);
 
 /* Backward of the router (chiang97912 "KeepTopK 策略": gates renormalised
- * over the kept k; "[CS336-04]" section 4: z-loss). Per token, with s the
+ * over the kept k; "[CS336-04]" section 4: z-loss); it also assembles the
+ * token gradient dx. Per token, with s the
  * softmax of the logits the forward's softmax saw:
  *  renormalised gates: ds_{c_j} = (dg_j - sum_i dg_i g_i) / sum_i s_{c_i}
  *  Switch gate (renormalize = 0): ds_e += dg_j for the expert used
  *  auxiliary: ds_te += alpha E f_e / N, f_e = counts_routed[e] / (N k)
  *  dl_te = s_te (ds_te - sum_e s_te ds_te) + beta 2 lse_t s_te / N
- *  dW_g = dl^T x; dlogit_bias = sum_t dl_t; dx_t = dl_t W_g + sum over the
- *  token's kept slots j (in order) of dx_rows[row_of[t][j]].
+ *  dW_g = dl^T x; dlogit_bias = sum_t dl_t; dx_t = sum over the token's
+ *  kept slots j (in order) of dx_rows[row_of[t][j]] + dx_shared[t] + dl_t W_g.
  *  p: n_tokens, d_model, n_experts, top_k, n_cand, renormalize as in the
  *     forward (w_noise must be NULL)
  *  logits [N][E] fp32: the forward's logits_out; cand_ids [N][n_cand],
  *  expert_of, row_of [N][k], counts_routed [E]: the forward's
  *  dgates [N][k] from moe_combine_backward; dx_rows from
- *  moe_grouped_ffn_backward or NULL (router part only)
+ *  moe_grouped_ffn_backward or NULL (router part only); dx_shared [N][d]
+ *  fp32 (the shared expert's moe_grouped_ffn_backward) or NULL
  *  dlogits [N][E], dw_gate [E][d], dlogit_bias [E] (or NULL), dx [N][d]:
  *  fp32 out. Deterministic. Workspace: moe_router_backward_workspace_bytes. */
 size_t moe_router_backward_workspace_bytes(int32_t n_tokens, int32_t d_model,
@@ -374,9 +381,9 @@ moe_status moe_router_backward(const moe_router_params* p, const void* x, moe_dt
                                const float* w_gate, const float* logits, const int32_t* cand_ids,
                                const int32_t* expert_of, const int32_t* row_of,
                                const float* dgates, const int32_t* counts_routed, float alpha,
-                               float beta, const float* dx_rows, float* dlogits, float* dw_gate,
-                               float* dlogit_bias, float* dx, void* workspace, size_t ws_bytes,
-                               void* hip_stream);
+                               float beta, const float* dx_rows, const float* dx_shared,
+                               float* dlogits, float* dw_gate, float* dlogit_bias, float* dx,
+                               void* workspace, size_t ws_bytes, void* hip_stream);
 
 /* ---------------------------------------------------------------------- */
 /* Helpers                                                                 */

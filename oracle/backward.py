@@ -114,7 +114,8 @@ def layer_backward(cfg, x, x_dt, w_gate, experts, fwd, dy, alpha=0.0, beta=0.0,
     expert e, dW1/dW3/dW2/db1/db2 [E][...] (zeros for experts with no rows),
     and the shared expert's dW (shared_dW1, ...). keep_terms: also
     `terms`, per expert dict(tokens, slots, X, dO, w1, w3, w2, a, u, h, dh,
-    da, du): its rows' token and slot indices and fp64 intermediates."""
+    da, du): its rows' token and slot indices and fp64 intermediates (and
+    `shared_terms` for the shared expert, every token with gate 1)."""
     if getattr(cfg, "expert_choice", False):
         raise ValueError("the backward oracle covers token-choice routing")
     X = decode_rows(x, x_dt)
@@ -163,6 +164,10 @@ def layer_backward(cfg, x, x_dt, w_gate, experts, fwd, dy, alpha=0.0, beta=0.0,
         dX += g["dX"]
         for n in ("dW1", "dW3", "dW2"):
             out["shared_" + n] = g[n]
+        if keep_terms:
+            w1s, w3s, w2s = (decode_weight(w[n], cfg.w_dtype) for n in ("w1", "w3", "w2"))
+            out["shared_terms"] = dict(tokens=np.arange(N), X=X, dO=dy, w1=w1s, w3=w3s, w2=w2s,
+                                       **{n: g[n] for n in ("a", "u", "h", "dh", "da", "du")})
 
     rb = router_backward(cfg, X, w_gate, fwd, dg, alpha, beta, logit_bias, w_noise)
     dX += rb.pop("dx")

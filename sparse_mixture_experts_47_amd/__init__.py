@@ -89,12 +89,12 @@ def _load():
     L.moe_grouped_ffn_backward.argtypes = [ctypes.POINTER(FFNWeights), P, P, P, i32, P, P, P, P,
                                            P, P, P, P, sz, P]
     L.moe_grouped_ffn_backward.restype = i32
-    L.moe_combine_backward.argtypes = [i32, i32, i32, P, P, i32, P, P, P, P, P]
+    L.moe_combine_backward.argtypes = [i32, i32, i32, P, P, i32, P, P, P, P, P, P]
     L.moe_combine_backward.restype = i32
     L.moe_router_backward_workspace_bytes.argtypes = [i32, i32, i32]
     L.moe_router_backward_workspace_bytes.restype = sz
     L.moe_router_backward.argtypes = [ctypes.POINTER(RouterParams), P, i32, P, P, P, P, P, P, P,
-                                      ctypes.c_float, ctypes.c_float, P, P, P, P, P, P, sz, P]
+                                      ctypes.c_float, ctypes.c_float, P, P, P, P, P, P, P, sz, P]
     L.moe_router_backward.restype = i32
     L.moe_balance_stats.argtypes = [i32, i32, i32, P, P, P, P, P, P, P, ctypes.c_float, P]
     L.moe_balance_stats.restype = i32
@@ -262,12 +262,13 @@ def moe_grouped_ffn_train(weights: FFNWeights, x_rows, offsets, y_rows, preact, 
                                      _stream(stream)))
 
 
-def moe_combine_backward(dy, y_rows, row_of, gates, d_rows, dgates, *, stream=None):
+def moe_combine_backward(dy, y_rows, row_of, gates, d_rows, dgates, *, d_shared=None,
+                         stream=None):
     N, k = row_of.shape
-    _dev_check(dy, y_rows, row_of, gates, d_rows, dgates)
+    _dev_check(dy, y_rows, row_of, gates, d_rows, dgates, d_shared)
     _check(lib.moe_combine_backward(N, dy.shape[1], k, _ptr(dy), _ptr(y_rows), _dt(y_rows),
                                     _ptr(row_of), _ptr(gates), _ptr(d_rows), _ptr(dgates),
-                                    _stream(stream)))
+                                    _ptr(d_shared), _stream(stream)))
 
 
 def moe_grouped_ffn_backward(weights: FFNWeights, x_rows, offsets, preact, h, d_rows, dx_rows,
@@ -286,11 +287,11 @@ def moe_grouped_ffn_backward(weights: FFNWeights, x_rows, offsets, preact, h, d_
 
 def moe_router_backward(x, w_gate, logits, cand_ids, expert_of, row_of, dgates, counts_routed,
                         dlogits, dw_gate, dx, *, top_k, renormalize, alpha=0.0, beta=0.0,
-                        dx_rows=None, dlogit_bias=None, ws=None, stream=None):
+                        dx_rows=None, dx_shared=None, dlogit_bias=None, ws=None, stream=None):
     N, E = logits.shape
     d = x.shape[1]
     _dev_check(x, w_gate, logits, cand_ids, expert_of, row_of, dgates, counts_routed, dlogits,
-               dw_gate, dx, dx_rows, dlogit_bias)
+               dw_gate, dx, dx_rows, dx_shared, dlogit_bias)
     p = RouterParams(N, d, E, top_k, cand_ids.shape[1], int(bool(renormalize)), None, None,
                      None, 0, None)
     if ws is None:
@@ -298,7 +299,7 @@ def moe_router_backward(x, w_gate, logits, cand_ids, expert_of, row_of, dgates, 
     _check(lib.moe_router_backward(ctypes.byref(p), _ptr(x), _dt(x), _ptr(w_gate), _ptr(logits),
                                    _ptr(cand_ids), _ptr(expert_of), _ptr(row_of), _ptr(dgates),
                                    _ptr(counts_routed), float(alpha), float(beta),
-                                   _ptr(dx_rows), _ptr(dlogits), _ptr(dw_gate),
+                                   _ptr(dx_rows), _ptr(dx_shared), _ptr(dlogits), _ptr(dw_gate),
                                    _ptr(dlogit_bias), _ptr(dx), _ptr(ws), ws.numel(),
                                    _stream(stream)))
 
@@ -415,12 +416,14 @@ class MoELayer:
         # training: the experts' forward keeps its pre-activations and h
         self.train = bool(train)
         if self.train:
-            if self.ec or self.shared is not None or weights.get("w_noise") is not None:
-                raise ValueError("the backward pass covers token choice without noise or a "
-                                 "shared expert")
+            if self.ec or weights.get("w_noise") is not None:
+                raise ValueError("the backward pass covers token choice without noise")
             bf = dict(dtype=torch.bfloat16, device=dev)
             self.preact = torch.empty((R, 2 * s.d_ff), **bf)
             self.h = torch.empty((R, s.d_ff), **bf)
+            if self.shared is not None:
+                self.preact_sh = torch.empty((N, 2 * s.shared_d_ff), **bf)
+                self.h_sh = torch.empty((N, s.shared_d_ff), **bf)
             self._bwd = None
 
     def route(self, x, logits_in=None, stream=None):
@@ -459,8 +462,13 @@ class MoELayer:
         main = stream or torch.cuda.current_stream()
         self.ev_x.record(main)
         self.side.wait_event(self.ev_x)
-        moe_grouped_ffn(self.shared, x, self.sh_offsets, self.y_shared,
-                        max_rows=self.spec.n_tokens, ws=self.ws_shared, stream=self.side)
+        if self.train:
+            moe_grouped_ffn_train(self.shared, x, self.sh_offsets, self.y_shared, self.preact_sh,
+                                  self.h_sh, max_rows=self.spec.n_tokens, ws=self.ws_shared,
+                                  stream=self.side)
+        else:
+            moe_grouped_ffn(self.shared, x, self.sh_offsets, self.y_shared,
+                            max_rows=self.spec.n_tokens, ws=self.ws_shared, stream=self.side)
         self.ev_shared.record(self.side)
         self._shared_pending = True
 
@@ -514,6 +522,15 @@ def _backward_buffers(layer):
              dlogit_bias=torch.empty(E, **f32) if layer.w.get("logit_bias") is not None else None)
     ws_f = workspace(lib.moe_grouped_ffn_backward_workspace_bytes(
         ctypes.byref(layer.ffn), R, int(layer.fused_gather)), dev)
+    if layer.shared is not None:
+        Fs = s.shared_d_ff
+        b.update(d_shared=torch.empty((N, d), dtype=torch.bfloat16, device=dev),
+                 dx_shared=torch.empty((N, d), **f32), shared_dw1=torch.empty((1, Fs, d), **f32),
+                 shared_dw3=torch.empty((1, Fs, d), **f32),
+                 shared_dw2=torch.empty((1, d, Fs), **f32))
+        ws_s = workspace(lib.moe_grouped_ffn_backward_workspace_bytes(
+            ctypes.byref(layer.shared), N, 0), dev)
+        ws_f = workspace(max(ws_f.numel(), ws_s.numel()), dev)
     ws_r = workspace(lib.moe_router_backward_workspace_bytes(N, d, E), dev)
     return b, ws_f, ws_r
 
@@ -522,23 +539,32 @@ def layer_backward(layer, x, dy, alpha=0.0, beta=0.0, stream=None):
     """Backward of the last `layer.forward` (the layer built with train=True):
     L = <dy, y> + alpha * Switch aux + beta * z-loss. Returns a dict of fp32
     device tensors: dx, dw_gate, dlogit_bias (or None), dw1, dw3, dw2,
-    dlogits, dgates (buffers reused by the next call)."""
+    dlogits, dgates, and with a shared expert shared_dw1/3/2 [1][...] (buffers
+    reused by the next call)."""
     if not layer.train:
         raise ValueError("build the layer with train=True to run its backward pass")
     if layer._bwd is None:
         layer._bwd = _backward_buffers(layer)
     b, ws_f, ws_r = layer._bwd
     s, w = layer.spec, layer.w
+    sh = layer.shared is not None
     moe_combine_backward(dy, layer.y_rows, layer.row_of, layer.gates, b["d_rows"], b["dgates"],
-                         stream=stream)
+                         d_shared=b["d_shared"] if sh else None, stream=stream)
     rows, index = layer._packed_rows(x)
     moe_grouped_ffn_backward(layer.ffn, rows, layer.offsets, layer.preact, layer.h, b["d_rows"],
                              b["dx_rows"], b["dw1"], b["dw3"], b["dw2"], row_index=index,
                              max_rows=layer.R, ws=ws_f, stream=stream)
+    if sh:
+        # one expert over every token with gate 1 (the workspace is reused in stream order)
+        moe_grouped_ffn_backward(layer.shared, x, layer.sh_offsets, layer.preact_sh, layer.h_sh,
+                                 b["d_shared"], b["dx_shared"], b["shared_dw1"],
+                                 b["shared_dw3"], b["shared_dw2"], max_rows=s.n_tokens, ws=ws_f,
+                                 stream=stream)
     moe_router_backward(x, w["w_gate"], layer.logits, layer.cand_ids, layer.expert_of,
                         layer.row_of, b["dgates"], layer.counts_routed, b["dlogits"],
                         b["dw_gate"], b["dx"], top_k=s.top_k, renormalize=s.renormalize,
                         alpha=alpha, beta=beta, dx_rows=b["dx_rows"],
+                        dx_shared=b["dx_shared"] if sh else None,
                         dlogit_bias=b["dlogit_bias"], ws=ws_r, stream=stream)
     return b
 

@@ -34,16 +34,17 @@ moe_status grouped_ffn_backward_launch(const moe_ffn_weights* w, const void* x_r
                                        float* dw3, float* dw2, void* workspace, hipStream_t st);
 moe_status combine_backward_launch(int N, int d, int k, const float* dy, const void* y_rows,
                                    moe_dtype y_dt, const int32_t* row_of, const float* gates,
-                                   uint16_t* d_rows, float* dgates, hipStream_t st);
+                                   uint16_t* d_rows, float* dgates, uint16_t* d_shared,
+                                   hipStream_t st);
 size_t router_backward_workspace_bytes(int N, int d, int E);
 moe_status router_backward_launch(int N, int d, int E, int k, int C, int renormalize,
                                   const void* x, moe_dtype x_dt, const float* w_gate,
                                   const float* logits, const int32_t* cand_ids,
                                   const int32_t* expert_of, const int32_t* row_of,
                                   const float* dgates, const int32_t* counts_routed, float alpha,
-                                  float beta, const float* dx_rows, float* dlogits,
-                                  float* dw_gate, float* dlogit_bias, float* dx, void* workspace,
-                                  hipStream_t st);
+                                  float beta, const float* dx_rows, const float* dx_shared,
+                                  float* dlogits, float* dw_gate, float* dlogit_bias, float* dx,
+                                  void* workspace, hipStream_t st);
 moe_status combine_launch(int N, int d, int k, const void* y_rows, moe_dtype y_dt,
                           const int32_t* row_of, const float* gates, const void* y_shared,
                           moe_dtype sh_dt, void* y, moe_dtype out_dt, hipStream_t st);
@@ -316,7 +317,7 @@ moe_status moe_grouped_ffn_backward(const moe_ffn_weights* w, const void* x_rows
 moe_status moe_combine_backward(int32_t n_tokens, int32_t d_model, int32_t top_k,
                                 const float* dy, const void* y_rows, moe_dtype y_dt,
                                 const int32_t* row_of, const float* gates, uint16_t* d_rows,
-                                float* dgates, void* hip_stream) {
+                                float* dgates, uint16_t* d_shared, void* hip_stream) {
   CHECK(n_tokens >= 1 && d_model >= 1 && top_k >= 1 && top_k <= 256, MOE_EINVAL,
         "moe_combine_backward: N=%d d=%d k=%d out of range", n_tokens, d_model, top_k);
   CHECK(dy && y_rows && row_of && gates && d_rows && dgates, MOE_EINVAL,
@@ -326,7 +327,7 @@ moe_status moe_combine_backward(int32_t n_tokens, int32_t d_model, int32_t top_k
   CHECK(y_dt == MOE_F32 || y_dt == MOE_BF16, MOE_EUNSUPPORTED,
         "moe_combine_backward: y_rows dtype must be F32 or BF16");
   return combine_backward_launch(n_tokens, d_model, top_k, dy, y_rows, y_dt, row_of, gates,
-                                 d_rows, dgates, (hipStream_t)hip_stream);
+                                 d_rows, dgates, d_shared, (hipStream_t)hip_stream);
 }
 
 size_t moe_router_backward_workspace_bytes(int32_t n_tokens, int32_t d_model,
@@ -339,9 +340,9 @@ moe_status moe_router_backward(const moe_router_params* p, const void* x, moe_dt
                                const float* w_gate, const float* logits, const int32_t* cand_ids,
                                const int32_t* expert_of, const int32_t* row_of,
                                const float* dgates, const int32_t* counts_routed, float alpha,
-                               float beta, const float* dx_rows, float* dlogits, float* dw_gate,
-                               float* dlogit_bias, float* dx, void* workspace, size_t ws_bytes,
-                               void* hip_stream) {
+                               float beta, const float* dx_rows, const float* dx_shared,
+                               float* dlogits, float* dw_gate, float* dlogit_bias, float* dx,
+                               void* workspace, size_t ws_bytes, void* hip_stream) {
   CHECK(p, MOE_EINVAL, "moe_router_backward: params is NULL");
   const int N = p->n_tokens, d = p->d_model, E = p->n_experts, k = p->top_k, C = p->n_cand;
   CHECK(N >= 1 && d >= 1 && E >= 1 && k >= 1 && C >= k && k <= E, MOE_EINVAL,
@@ -358,7 +359,7 @@ moe_status moe_router_backward(const moe_router_params* p, const void* x, moe_dt
   if (s != MOE_OK) return s;
   return router_backward_launch(N, d, E, k, C, p->renormalize, x, x_dt, w_gate, logits, cand_ids,
                                 expert_of, row_of, dgates, counts_routed, alpha, beta, dx_rows,
-                                dlogits, dw_gate, dlogit_bias, dx, workspace,
+                                dx_shared, dlogits, dw_gate, dlogit_bias, dx, workspace,
                                 (hipStream_t)hip_stream);
 }
 

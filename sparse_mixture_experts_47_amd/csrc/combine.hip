@@ -156,14 +156,21 @@ moe_status dispatch_out(int N, int d, int k, const void* yr, const int32_t* row_
 // dO_r = g_tj * dy_t (bf16, the data operand of the experts' backward GEMMs)
 // for the row r = row_of[t][j] of each kept slot, and dg_tj = <dy_t, o_r>
 // (fp32, summed per thread in feature order, then over the block's threads
-// in a fixed tree: deterministic). A dropped slot gets dg = 0.
+// in a fixed tree: deterministic). A dropped slot gets dg = 0. With a shared
+// expert (gate 1) its output gradient is dy itself, written as bf16 rows.
 template <typename YT>
 __global__ __launch_bounds__(kThreads) void combine_backward_kernel(
     int d, int k, const float* __restrict__ dy, const YT* __restrict__ y_rows,
     const int32_t* __restrict__ row_of, const float* __restrict__ gates,
-    uint16_t* __restrict__ d_rows, float* __restrict__ dgates) {
+    uint16_t* __restrict__ d_rows, float* __restrict__ dgates, uint16_t* __restrict__ d_shared) {
   __shared__ float red[kThreads / 64];
   const int t = blockIdx.x, tid = threadIdx.x;
+  if (d_shared)
+    for (int c = tid * 8; c < d; c += kThreads * 8) {
+      float v[8];
+      Vec8<float>::load(dy + (size_t)t * d + c, v);
+      Vec8<uint16_t>::store(d_shared + (size_t)t * d + c, v);
+    }
   for (int j = 0; j < k; ++j) {
     const int r = row_of[(size_t)t * k + j];
     if (r < 0) {
@@ -202,13 +209,14 @@ namespace moe_host {
 
 moe_status combine_backward_launch(int N, int d, int k, const float* dy, const void* y_rows,
                                    moe_dtype y_dt, const int32_t* row_of, const float* gates,
-                                   uint16_t* d_rows, float* dgates, hipStream_t st) {
+                                   uint16_t* d_rows, float* dgates, uint16_t* d_shared,
+                                   hipStream_t st) {
   if (y_dt == MOE_BF16)
     combine_backward_kernel<uint16_t><<<N, kThreads, 0, st>>>(
-        d, k, dy, (const uint16_t*)y_rows, row_of, gates, d_rows, dgates);
+        d, k, dy, (const uint16_t*)y_rows, row_of, gates, d_rows, dgates, d_shared);
   else
-    combine_backward_kernel<float><<<N, kThreads, 0, st>>>(d, k, dy, (const float*)y_rows,
-                                                            row_of, gates, d_rows, dgates);
+    combine_backward_kernel<float><<<N, kThreads, 0, st>>>(
+        d, k, dy, (const float*)y_rows, row_of, gates, d_rows, dgates, d_shared);
   return launch_status("combine backward");
 }
 

@@ -16,7 +16,8 @@
 //   softmax:      dl_te = s_te (ds_te - sum_e' s_te' ds_te')
 //   z-loss:       dl_te += beta 2 lse_t s_te / N
 //   router GEMM:  dW_g = dl^T x,  d(logit bias) = sum_t dl_t,  dx_t += dl_t W_g
-// dx_t also sums the token's kept expert-row gradients in slot order.
+// dx_t also sums the token's kept expert-row gradients in slot order and the
+// shared expert's token-row gradient.
 #include "moe_device.h"
 
 namespace {
@@ -85,11 +86,12 @@ __global__ __launch_bounds__(kThreads) void router_bwd_token_kernel(
   }
 }
 
-// dx_t = sum_j dx_rows[row_of[t][j]] (kept slots in order) + sum_e dl_te W_g[e]
+// dx_t = sum_j dx_rows[row_of[t][j]] (kept slots in order) + dx_shared[t]
+//        + sum_e dl_te W_g[e]
 __global__ __launch_bounds__(kThreads) void router_bwd_dx_kernel(
     int d, int E, int k, const float* __restrict__ dl, const float* __restrict__ w_gate,
     const int32_t* __restrict__ row_of, const float* __restrict__ dx_rows,
-    float* __restrict__ dx) {
+    const float* __restrict__ dx_shared, float* __restrict__ dx) {
   __shared__ float dls[256];
   const int t = blockIdx.x;
   for (int e = threadIdx.x; e < E; e += kThreads) dls[e] = dl[(size_t)t * E + e];
@@ -101,6 +103,7 @@ __global__ __launch_bounds__(kThreads) void router_bwd_dx_kernel(
         const int r = row_of[(size_t)t * k + j];
         if (r >= 0) acc += dx_rows[(size_t)r * d + c];
       }
+    if (dx_shared) acc += dx_shared[(size_t)t * d + c];
     for (int e = 0; e < E; ++e) acc = __builtin_fmaf(dls[e], w_gate[(size_t)e * d + c], acc);
     dx[(size_t)t * d + c] = acc;
   }
@@ -171,16 +174,17 @@ moe_status router_backward_launch(int N, int d, int E, int k, int C, int renorma
                                   const float* logits, const int32_t* cand_ids,
                                   const int32_t* expert_of, const int32_t* row_of,
                                   const float* dgates, const int32_t* counts_routed, float alpha,
-                                  float beta, const float* dx_rows, float* dlogits,
-                                  float* dw_gate, float* dlogit_bias, float* dx, void* workspace,
-                                  hipStream_t st) {
+                                  float beta, const float* dx_rows, const float* dx_shared,
+                                  float* dlogits, float* dw_gate, float* dlogit_bias, float* dx,
+                                  void* workspace, hipStream_t st) {
   const int per_block = kThreads / 64;
   router_bwd_token_kernel<<<(N + per_block - 1) / per_block, kThreads, 0, st>>>(
       N, E, k, C, renormalize, logits, cand_ids, expert_of, row_of, dgates, counts_routed, alpha,
       beta, dlogits);
   moe_status s = launch_status("router backward (scores)");
   if (s != MOE_OK) return s;
-  router_bwd_dx_kernel<<<N, kThreads, 0, st>>>(d, E, k, dlogits, w_gate, row_of, dx_rows, dx);
+  router_bwd_dx_kernel<<<N, kThreads, 0, st>>>(d, E, k, dlogits, w_gate, row_of, dx_rows,
+                                               dx_shared, dx);
   s = launch_status("router backward (dx)");
   if (s != MOE_OK) return s;
   const int chunks = (N + kChunkTokens - 1) / kChunkTokens;

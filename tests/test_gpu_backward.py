@@ -22,10 +22,11 @@ terms of dh = dO W2) and A_o = |h| |W2|^T (absolute terms of o = h W2^T):
   ds (renormalised):   B_s[c_j] = (B_g_j + sum_i B_g_i g_i) / S;  Switch: B_s[e] = B_g
   dl = s (ds - s.ds):  B_l = s (B_s + s.B_s) + 1e-5 (|dl| + s (|ds| + s.|ds|))  (fp32 softmax)
   dW_g = dl^T x:  B_l^T |x|;  d logit bias: sum_t B_l;  dx = sum_j dX rows + dl W_g.
-These worst-case bounds are loose where many terms of mixed sign cancel, so
-the router-side gradients must also meet the layer output's normwise bf16
-bar, max |g - g_ref| / RMS(g_ref) <= 2e-2, and the router's backward alone
-(fp32 arithmetic only) is checked to 1e-5 relative.
+These worst-case bounds are loose where many terms of mixed sign cancel,
+so the router-side gradients (dg, dl, dW_g, d logit bias) are also held to a
+statistical bound (7 standard deviations of the propagated rounding error;
+see _check_router_statistical), and the router's backward alone (fp32
+arithmetic only) is checked to 1e-5 relative.
 """
 import numpy as np
 import pytest
@@ -34,7 +35,7 @@ import torch
 import oracle
 import workloads as W
 from oracle import backward as OB
-from parity_utils import (TOL_BF16, experts_of, host_inputs, rel_err, require_gpu, to_device,
+from parity_utils import (experts_of, host_inputs, require_gpu, to_device,
                           to_np)
 
 pytestmark = pytest.mark.gpu
@@ -89,6 +90,8 @@ CASES = {
     "switch_drop_reduced": W.REDUCED["c2"].with_(name="switch_drop_reduced", top_k=1,
                                                   renormalize=False, overflow=W.DROP,
                                                   capacity_factor=1.0, n_tokens=512),
+    # 64 experts, top-8 with a selection bias, plus a shared expert
+    "deepseek_reduced": W.REDUCED["c3"],
 }
 
 
@@ -104,11 +107,12 @@ def test_layer_backward_matches_oracle(moe, key):
     inp = W.make_inputs(cfg, "cpu")
     host = host_inputs(inp)
     experts = experts_of(host)
-    fwd = oracle.layer_forward(cfg, host["x"], cfg.x_dtype, host["w_gate"], experts, None,
+    shared = experts_of(host, "shared_") if cfg.shared_d_ff else None
+    fwd = oracle.layer_forward(cfg, host["x"], cfg.x_dtype, host["w_gate"], experts, shared,
                                host["logit_bias"], host["select_bias"], host["w_noise"])
     dy = _dy(cfg)
     ref = OB.layer_backward(cfg, host["x"], cfg.x_dtype, host["w_gate"], experts, fwd,
-                            dy.numpy().astype(np.float64), ALPHA, BETA,
+                            dy.numpy().astype(np.float64), ALPHA, BETA, shared=shared,
                             logit_bias=host["logit_bias"], keep_terms=True)
     dev = to_device(inp)
     layer = moe.MoELayer(moe.spec_from_config(cfg), dev, x_dtype=torch.bfloat16, train=True)
@@ -125,9 +129,75 @@ def test_layer_backward_matches_oracle(moe, key):
     g = moe.layer_backward(layer, dev["x"], dy.cuda(), ALPHA, BETA)
     torch.cuda.synchronize()
     _check_bounds(g, ref, fwd, dy.numpy().astype(np.float64), host, cfg)
-    # the router-side gradients also meet the layer output's normwise bf16 bar
-    for name, gname in (("dgates", "dg"), ("dlogits", "dl"), ("dw_gate", "dw_gate")):
-        assert rel_err(to_np(g[name]), ref[gname]) <= TOL_BF16, name
+    _check_router_statistical(g, ref, fwd, dy.numpy().astype(np.float64), host, cfg)
+
+
+def _check_router_statistical(g, ref, fwd, dy, host, cfg):
+    """Tight check of the router-side gradients: the rounding errors of h
+    (relative, uniform in +-u: variance u^2/3, independent) reach a gate
+    gradient as dg_err = sum_f delta_f h_f (dy W2)_f, so its standard
+    deviation is sigma_g = (u/sqrt 3) ||h * (dy W2)||_2; dl, dW_g, the logit
+    bias and dx's router share are linear in dg (matrices M = J R: softmax
+    Jacobian times the renormalisation's), so their sigmas follow exactly
+    for independent slots. Each entry must lie within 7 sigma (a false
+    alarm has odds below 3e-12 per entry) plus 1e-5 of the fp32 terms
+    (for renormalised gates, of dg itself: ds = (dg_i - sum dg g) / S
+    cancels)."""
+    u = 2.0 ** -8
+    N, E, k = cfg.n_tokens, cfg.n_experts, cfg.top_k
+    r, dsp = fwd["route"], fwd["dispatch"]
+    sg = np.zeros((N, k))
+    for T in ref["terms"]:
+        tt, jj = T["tokens"], T["slots"]
+        sg[tt, jj] = u / np.sqrt(3.0) * np.sqrt(np.sum((T["h"] * (dy[tt] @ T["w2"])) ** 2, axis=1))
+    s = r["s"].astype(np.float64)
+    M = np.zeros((N, E, k))  # d dl_te / d dg_tj
+    if cfg.renormalize:
+        cand = r["cand_ids"][:, :k]
+        sel = np.take_along_axis(s, cand, axis=1)
+        S = sel.sum(axis=1)
+        gk = sel / S[:, None]
+        Rm = np.zeros((N, E, k))  # d ds_te / d dg_tj
+        for i in range(k):
+            for j in range(k):
+                Rm[np.arange(N), cand[:, i], j] += ((i == j) - gk[:, j]) / S
+    else:
+        Rm = np.zeros((N, E, k))
+        for j in range(k):
+            Rm[np.arange(N), np.maximum(dsp["expert_of"][:, j], 0), j] += dsp["row_of"][:, j] >= 0
+    # J[e][e'] = s_e (delta - s_e')
+    M = s[:, :, None] * (Rm - np.einsum("te,tej->tj", s, Rm)[:, None, :])
+    sl = np.sqrt(np.einsum("tej,tj->te", M ** 2, sg ** 2))
+    X = oracle.decode_rows(host["x"], cfg.x_dtype)
+    wg = host["w_gate"].astype(np.float64)
+    fp = lambda a: 1e-5 * np.abs(a)
+    # fp32 terms of ds before the renormalisation's cancellation (dg_i - sum dg g)
+    ads = np.abs(ref["ds"])
+    if cfg.renormalize:
+        adg = np.abs(ref["dg"])
+        np.put_along_axis(ads, cand, np.take_along_axis(ads, cand, axis=1) + (
+            adg + (adg * gk).sum(axis=1, keepdims=True)) / S[:, None], axis=1)
+    # fp32 rounding of the GPU's softmax recomputation and score gradients
+    Fdl = 1e-5 * (np.abs(ref["dl"]) + s * (ads + (s * ads).sum(axis=1, keepdims=True)))
+    checks = {
+        "dgates": (ref["dg"], 7 * sg + fp(ref["dg"])),
+        "dlogits": (ref["dl"], 7 * sl + Fdl),
+        "dw_gate": (ref["dw_gate"], 7 * np.sqrt((sl ** 2).T @ X ** 2)
+                    + (Fdl + 1e-5 * np.abs(ref["dl"])).T @ np.abs(X)),
+    }
+    if g["dlogit_bias"] is not None:
+        checks["dlogit_bias"] = (ref["dlogit_bias"], 7 * np.sqrt((sl ** 2).sum(axis=0))
+                                 + (Fdl + 1e-5 * np.abs(ref["dl"])).sum(axis=0))
+    worst = {}
+    for name, (R, B) in checks.items():
+        G = to_np(g[name]).astype(np.float64)
+        err = np.abs(G - R)
+        ratio = err / np.maximum(B, 1e-300)
+        i = np.unravel_index(np.argmax(ratio), ratio.shape)
+        assert np.all(err <= B), (name, float(ratio[i]), i, float(G[i]), float(R[i]), float(B[i]))
+        worst[name] = float(ratio[i])
+    print("  router-side error / (7 sigma + fp32):", {kk: round(v, 3) for kk, v in worst.items()},
+          flush=True)
 
 
 def _check_bounds(g, ref, fwd, dy, host, cfg):
@@ -139,8 +209,11 @@ def _check_bounds(g, ref, fwd, dy, host, cfg):
     Bg = np.zeros((N, k))
     Bdx = np.zeros((N, d))
     dx_rows_gpu = to_np(g["dx_rows"]).astype(np.float64)
-    for e, T in enumerate(ref["terms"]):
-        tt, jj = T["tokens"], T["slots"]
+    blocks = [(e, T) for e, T in enumerate(ref["terms"])]
+    if "shared_terms" in ref:
+        blocks.append(("shared", ref["shared_terms"]))
+    for e, T in blocks:
+        tt = T["tokens"]
         a, uu, dh = T["a"], T["u"], T["dh"]
         sig = 1.0 / (1.0 + np.exp(-a))
         silu, dsilu = a * sig, sig * (1.0 + a * (1.0 - sig))
@@ -148,19 +221,23 @@ def _check_bounds(g, ref, fwd, dy, host, cfg):
         Ma = np.abs(uu * dsilu) * A + np.abs(dh * uu) * (np.abs(dsilu) + np.abs(a)) + np.abs(T["da"])
         Mu = np.abs(silu) * A + np.abs(dh) * (np.abs(dsilu * a) + np.abs(silu)) + np.abs(T["du"])
         X = np.abs(T["X"])
-        for name, B, R in (("dw2", np.abs(T["dO"]).T @ np.abs(T["h"]), ref["dW2"][e]),
-                           ("dw1", Ma.T @ X, ref["dW1"][e]), ("dw3", Mu.T @ X, ref["dW3"][e])):
-            bounds.setdefault(name, []).append(3 * u * B)
-            refs.setdefault(name, []).append(R)
-            gots.setdefault(name, []).append(to_np(g[name][e]))
-        # expert part of dx: per packed row (rows are identical: row_of is bit-exact)
+        pre, idx = ("shared_", 0) if e == "shared" else ("", e)
+        for name, B, R in (("dw2", np.abs(T["dO"]).T @ np.abs(T["h"]), ref[pre + "dW2"]),
+                           ("dw1", Ma.T @ X, ref[pre + "dW1"]), ("dw3", Mu.T @ X, ref[pre + "dW3"])):
+            bounds.setdefault(pre + name, []).append(3 * u * B)
+            refs.setdefault(pre + name, []).append(R if e == "shared" else R[e])
+            gots.setdefault(pre + name, []).append(to_np(g[pre + name][idx]))
         Brow = 3 * u * (Ma @ np.abs(T["w1"]) + Mu @ np.abs(T["w3"]))
+        np.add.at(Bdx, tt, Brow)
+        if e == "shared":
+            continue
+        # expert part of dx: per packed row (rows are identical: row_of is bit-exact)
+        jj = T["slots"]
         rows = dsp["row_of"][tt, jj]
         ref_rows = T["da"] @ T["w1"] + T["du"] @ T["w3"]
         bounds.setdefault("dx_rows", []).append(Brow)
         refs.setdefault("dx_rows", []).append(ref_rows)
         gots.setdefault("dx_rows", []).append(dx_rows_gpu[rows])
-        np.add.at(Bdx, tt, Brow)
         Ao = np.abs(T["h"]) @ np.abs(T["w2"]).T
         Bg[tt, jj] = 3 * 2 * u * np.sum(np.abs(dy[tt]) * Ao, axis=1)
     s = r["s"].astype(np.float64)

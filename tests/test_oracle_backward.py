@@ -14,7 +14,7 @@ from oracle import backward as B
 
 
 def _tiny(act=W.ACT_SWIGLU, w_dt=W.F32, renorm=True, k=2, E=4, overflow=W.DROPLESS, cf=None,
-          noise=False, N=24, d=16, F=12, seed=7):
+          noise=False, N=24, d=16, F=12, seed=7, shared=False):
     cfg = W.C2.with_(name="bwd_tiny", n_tokens=N, d_model=d, n_experts=E, d_ff=F, top_k=k,
                      act=act, w_dtype=w_dt, x_dtype=W.F32 if w_dt == W.F32 else W.BF16,
                      renormalize=renorm, overflow=overflow, capacity_factor=cf, seed=seed,
@@ -33,6 +33,10 @@ def _tiny(act=W.ACT_SWIGLU, w_dt=W.F32, renorm=True, k=2, E=4, overflow=W.DROPLE
     lb = (rng.standard_normal(E) * 0.1).astype(np.float32)
     wn = (rng.standard_normal((E, d)) * 0.3).astype(np.float32) if noise else None
     dy = rng.standard_normal((N, d))
+    if shared:  # one always-on SwiGLU expert, gate 1
+        w["shared"] = dict(w1=(rng.standard_normal((1, F, d)) / np.sqrt(d)).astype(np.float32),
+                           w3=(rng.standard_normal((1, F, d)) / np.sqrt(d)).astype(np.float32),
+                           w2=(rng.standard_normal((1, d, F)) / np.sqrt(F)).astype(np.float32))
     return cfg, x, w, wg, lb, wn, dy
 
 
@@ -77,6 +81,9 @@ def _autograd(cfg, x, w, wg, lb, wn, fwd, dy, alpha, beta):
                 h = torch.nn.functional.gelu(a)
             o = W2[e] @ h + (B2[e] if B2 is not None else 0)
             y[t] = y[t] + g[t, j] * o
+    if "shared" in w:
+        S1, S3, S2 = (T(w["shared"][n][0]) for n in ("w1", "w3", "w2"))
+        y = y + (torch.nn.functional.silu(X @ S1.T) * (X @ S3.T)) @ S2.T
     f = torch.tensor(dsp["counts_routed"].astype(np.float64) / (N * k))
     aux = E * (f * s.mean(dim=0)).sum()
     zl = (lse ** 2).mean()
@@ -89,14 +96,17 @@ def _autograd(cfg, x, w, wg, lb, wn, fwd, dy, alpha, beta):
         out["db1"], out["db2"] = B1.grad, B2.grad
     if Wn is not None:
         out["dw_noise"] = Wn.grad
+    if "shared" in w:
+        out.update(shared_dW1=S1.grad, shared_dW3=S3.grad, shared_dW2=S2.grad)
     return {n: v.numpy() for n, v in out.items()}
 
 
 def _run(cfg, x, w, wg, lb, wn, dy, alpha, beta):
     experts = oracle.ExpertSource(w)
-    fwd = oracle.layer_forward(cfg, x, cfg.x_dtype, wg, experts, None, lb, None, wn)
+    shared = oracle.ExpertSource(w["shared"]) if "shared" in w else None
+    fwd = oracle.layer_forward(cfg, x, cfg.x_dtype, wg, experts, shared, lb, None, wn)
     got = B.layer_backward(cfg, x, cfg.x_dtype, wg, experts, fwd, dy, alpha, beta,
-                           logit_bias=lb, w_noise=wn)
+                           shared=shared, logit_bias=lb, w_noise=wn)
     return fwd, got
 
 
@@ -106,13 +116,14 @@ def _rel(a, b):
 
 
 @pytest.mark.parametrize("case", ["swiglu_renorm", "relu_switch_drop", "gelu_switch_noise",
-                                  "swiglu_top1_reroute"])
+                                  "swiglu_top1_reroute", "swiglu_top2_shared"])
 def test_backward_matches_autograd(case):
     kw = dict(swiglu_renorm={}, relu_switch_drop=dict(act=W.ACT_RELU, renorm=False, k=1,
                                                       overflow=W.DROP, cf=0.75),
               gelu_switch_noise=dict(act=W.ACT_GELU, renorm=False, k=1, noise=True),
               swiglu_top1_reroute=dict(renorm=False, k=1, overflow=W.REROUTE_THEN_DROP,
-                                       cf=0.5))[case]
+                                       cf=0.5),
+              swiglu_top2_shared=dict(shared=True))[case]
     cfg, x, w, wg, lb, wn, dy = _tiny(**kw)
     alpha, beta = 0.3, 0.05
     fwd, got = _run(cfg, x, w, wg, lb, wn, dy, alpha, beta)
