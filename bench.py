@@ -51,6 +51,8 @@ def parse():
                          "(evicts the 256 MB Infinity Cache); reported beside the warm run")
     ap.add_argument("--backward", action="store_true",
                     help="time a training step (forward + backward) instead of the forward")
+    ap.add_argument("--dw-bf16", action="store_true",
+                    help="with --backward: expert weight gradients in bf16 instead of fp32")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB read + 1 GiB write streaming kernel (torch.neg) "
                          "to calibrate the HBM byte counters")
@@ -255,7 +257,11 @@ def bench_backward(args):
         if e is not None:
             e[4].record(stream)
 
-    moe.layer_backward(layer, x, dy, alpha, beta)  # allocates the backward buffers
+    dw_dtype = torch.bfloat16 if args.dw_bf16 else torch.float32
+    # one full step allocates the backward buffers (the forward first: the
+    # backward reads its routing and saved activations)
+    layer.forward(x, stats=False)
+    moe.layer_backward(layer, x, dy, alpha, beta, dw_dtype)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -289,7 +295,8 @@ def bench_backward(args):
         "config": {"workload": cfg.name + "_training_step", "n_tokens": cfg.n_tokens,
                    "d_model": d, "n_experts": cfg.n_experts, "d_ff": F, "top_k": cfg.top_k,
                    "act": ["relu", "gelu", "swiglu"][cfg.act], "loss": "<dy,y> + 0.01 aux + "
-                   "0.001 z", "parallelism": "single-gpu"},
+                   "0.001 z", "weight_grad_dtype": "bf16" if args.dw_bf16 else "f32",
+                   "parallelism": "single-gpu"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": None,

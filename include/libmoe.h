@@ -301,8 +301,9 @@ moe_status moe_balance_stats(int32_t n_tokens, int32_t n_experts, int32_t top_k,
  * routing path. Order of the calls: moe_combine_backward ->
  * moe_grouped_ffn_backward (routed experts, and the shared expert if any) ->
  * moe_router_backward. Scope: token-choice routing without noise; bf16
- * SwiGLU experts without biases; d_model and d_ff multiples of 256. Gradients come out in fp32 and overwrite their
- * buffers (no accumulation). */
+ * SwiGLU experts without biases; d_model and d_ff multiples of 256.
+ * Gradients come out in fp32 (expert weight gradients optionally bf16) and
+ * overwrite their buffers (no accumulation). */
 
 /* Forward of the routed (or shared) experts that also keeps what the
  * backward needs: as moe_grouped_ffn (bf16 activations), plus
@@ -342,8 +343,9 @@ moe_status moe_combine_backward(int32_t n_tokens, int32_t d_model, int32_t top_k
  *  d_rows [R][d] bf16: dO (moe_combine_backward's d_rows)
  *  dx_rows [max_rows][d] fp32 out: dX per packed row (rows >= offsets[E]
  *          untouched)
- *  dw1, dw3 [E][d_ff][d], dw2 [E][d][d_ff] fp32 out (every element written;
- *          zero for an expert without rows)
+ *  dw1, dw3 [E][d_ff][d], dw2 [E][d][d_ff] out in dw_dt (F32, or BF16:
+ *          the fp32 sums rounded once; every element written, zero for an
+ *          expert without rows)
  * Workspace: moe_grouped_ffn_backward_workspace_bytes(w, max_rows,
  * row_index != NULL). bf16 MFMA products with fp32 accumulation; the
  * intermediate da, du are bf16. */
@@ -352,8 +354,8 @@ size_t moe_grouped_ffn_backward_workspace_bytes(const moe_ffn_weights* w, int32_
 moe_status moe_grouped_ffn_backward(const moe_ffn_weights* w, const void* x_rows,
                                     const int32_t* row_index, const int32_t* offsets,
                                     int32_t max_rows, const uint16_t* preact, const uint16_t* h,
-                                    const uint16_t* d_rows, float* dx_rows, float* dw1,
-                                    float* dw3, float* dw2, void* workspace, size_t ws_bytes,
+                                    const uint16_t* d_rows, float* dx_rows, void* dw1, void* dw3,
+                                    void* dw2, moe_dtype dw_dt, void* workspace, size_t ws_bytes,
                                     void* hip_stream);
 
 /* Backward of the router (chiang97912 "KeepTopK 策略": gates renormalised

@@ -87,7 +87,7 @@ def _load():
     L.moe_grouped_ffn_backward_workspace_bytes.argtypes = [ctypes.POINTER(FFNWeights), i32, i32]
     L.moe_grouped_ffn_backward_workspace_bytes.restype = sz
     L.moe_grouped_ffn_backward.argtypes = [ctypes.POINTER(FFNWeights), P, P, P, i32, P, P, P, P,
-                                           P, P, P, P, sz, P]
+                                           P, P, P, i32, P, sz, P]
     L.moe_grouped_ffn_backward.restype = i32
     L.moe_combine_backward.argtypes = [i32, i32, i32, P, P, i32, P, P, P, P, P, P]
     L.moe_combine_backward.restype = i32
@@ -282,7 +282,8 @@ def moe_grouped_ffn_backward(weights: FFNWeights, x_rows, offsets, preact, h, d_
     _check(lib.moe_grouped_ffn_backward(ctypes.byref(weights), _ptr(x_rows), _ptr(row_index),
                                         _ptr(offsets), max_rows, _ptr(preact), _ptr(h),
                                         _ptr(d_rows), _ptr(dx_rows), _ptr(dw1), _ptr(dw3),
-                                        _ptr(dw2), _ptr(ws), ws.numel(), _stream(stream)))
+                                        _ptr(dw2), _dt(dw1), _ptr(ws), ws.numel(),
+                                        _stream(stream)))
 
 
 def moe_router_backward(x, w_gate, logits, cand_ids, expert_of, row_of, dgates, counts_routed,
@@ -425,6 +426,7 @@ class MoELayer:
                 self.preact_sh = torch.empty((N, 2 * s.shared_d_ff), **bf)
                 self.h_sh = torch.empty((N, s.shared_d_ff), **bf)
             self._bwd = None
+        self._forward_done = False
 
     def route(self, x, logits_in=None, stream=None):
         s, w = self.spec, self.w
@@ -507,17 +509,19 @@ class MoELayer:
         self.combine(stream)
         if stats:
             self.stats(update_bias, stream)
+        self._forward_done = True
         return self.y
 
 
-def _backward_buffers(layer):
+def _backward_buffers(layer, dw_dtype=torch.float32):
     s, dev = layer.spec, layer.dev
     E, d, F, N, R = s.n_experts, s.d_model, s.d_ff, s.n_tokens, layer.R
     f32 = dict(dtype=torch.float32, device=dev)
+    wdt = dict(dtype=dw_dtype, device=dev)
     b = dict(d_rows=torch.empty((R, d), dtype=torch.bfloat16, device=dev),
              dgates=torch.empty((N, s.top_k), **f32), dx_rows=torch.empty((R, d), **f32),
-             dw1=torch.empty((E, F, d), **f32), dw3=torch.empty((E, F, d), **f32),
-             dw2=torch.empty((E, d, F), **f32), dlogits=torch.empty((N, E), **f32),
+             dw1=torch.empty((E, F, d), **wdt), dw3=torch.empty((E, F, d), **wdt),
+             dw2=torch.empty((E, d, F), **wdt), dlogits=torch.empty((N, E), **f32),
              dw_gate=torch.empty((E, d), **f32), dx=torch.empty((N, d), **f32),
              dlogit_bias=torch.empty(E, **f32) if layer.w.get("logit_bias") is not None else None)
     ws_f = workspace(lib.moe_grouped_ffn_backward_workspace_bytes(
@@ -525,9 +529,9 @@ def _backward_buffers(layer):
     if layer.shared is not None:
         Fs = s.shared_d_ff
         b.update(d_shared=torch.empty((N, d), dtype=torch.bfloat16, device=dev),
-                 dx_shared=torch.empty((N, d), **f32), shared_dw1=torch.empty((1, Fs, d), **f32),
-                 shared_dw3=torch.empty((1, Fs, d), **f32),
-                 shared_dw2=torch.empty((1, d, Fs), **f32))
+                 dx_shared=torch.empty((N, d), **f32), shared_dw1=torch.empty((1, Fs, d), **wdt),
+                 shared_dw3=torch.empty((1, Fs, d), **wdt),
+                 shared_dw2=torch.empty((1, d, Fs), **wdt))
         ws_s = workspace(lib.moe_grouped_ffn_backward_workspace_bytes(
             ctypes.byref(layer.shared), N, 0), dev)
         ws_f = workspace(max(ws_f.numel(), ws_s.numel()), dev)
@@ -535,16 +539,20 @@ def _backward_buffers(layer):
     return b, ws_f, ws_r
 
 
-def layer_backward(layer, x, dy, alpha=0.0, beta=0.0, stream=None):
+def layer_backward(layer, x, dy, alpha=0.0, beta=0.0, dw_dtype=torch.float32, stream=None):
     """Backward of the last `layer.forward` (the layer built with train=True):
     L = <dy, y> + alpha * Switch aux + beta * z-loss. Returns a dict of fp32
     device tensors: dx, dw_gate, dlogit_bias (or None), dw1, dw3, dw2,
     dlogits, dgates, and with a shared expert shared_dw1/3/2 [1][...] (buffers
-    reused by the next call)."""
+    reused by the next call). dw_dtype: float32, or bfloat16 for the expert
+    weight gradients."""
     if not layer.train:
         raise ValueError("build the layer with train=True to run its backward pass")
-    if layer._bwd is None:
-        layer._bwd = _backward_buffers(layer)
+    if not layer._forward_done:
+        # the backward reads the forward's routing and saved activations
+        raise ValueError("run the layer's forward before its backward pass")
+    if layer._bwd is None or layer._bwd[0]["dw1"].dtype != dw_dtype:
+        layer._bwd = _backward_buffers(layer, dw_dtype)
     b, ws_f, ws_r = layer._bwd
     s, w = layer.spec, layer.w
     sh = layer.shared is not None

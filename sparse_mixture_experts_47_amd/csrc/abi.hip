@@ -30,8 +30,9 @@ size_t grouped_ffn_backward_workspace_bytes(const moe_ffn_weights* w, int max_ro
 moe_status grouped_ffn_backward_launch(const moe_ffn_weights* w, const void* x_rows,
                                        const int32_t* row_index, const int32_t* offsets,
                                        int max_rows, const uint16_t* preact, const uint16_t* h,
-                                       const uint16_t* d_out, float* dx_rows, float* dw1,
-                                       float* dw3, float* dw2, void* workspace, hipStream_t st);
+                                       const uint16_t* d_out, float* dx_rows, void* dw1,
+                                       void* dw3, void* dw2, moe_dtype dw_dt, void* workspace,
+                                       hipStream_t st);
 moe_status combine_backward_launch(int N, int d, int k, const float* dy, const void* y_rows,
                                    moe_dtype y_dt, const int32_t* row_of, const float* gates,
                                    uint16_t* d_rows, float* dgates, uint16_t* d_shared,
@@ -296,8 +297,8 @@ size_t moe_grouped_ffn_backward_workspace_bytes(const moe_ffn_weights* w, int32_
 moe_status moe_grouped_ffn_backward(const moe_ffn_weights* w, const void* x_rows,
                                     const int32_t* row_index, const int32_t* offsets,
                                     int32_t max_rows, const uint16_t* preact, const uint16_t* h,
-                                    const uint16_t* d_rows, float* dx_rows, float* dw1,
-                                    float* dw3, float* dw2, void* workspace, size_t ws_bytes,
+                                    const uint16_t* d_rows, float* dx_rows, void* dw1, void* dw3,
+                                    void* dw2, moe_dtype dw_dt, void* workspace, size_t ws_bytes,
                                     void* hip_stream) {
   moe_status s = check_train_weights(w, "moe_grouped_ffn_backward");
   if (s != MOE_OK) return s;
@@ -305,12 +306,14 @@ moe_status moe_grouped_ffn_backward(const moe_ffn_weights* w, const void* x_rows
         "moe_grouped_ffn_backward: max_rows %d out of range", max_rows);
   CHECK(x_rows && offsets && preact && h && d_rows && dx_rows && dw1 && dw3 && dw2, MOE_EINVAL,
         "moe_grouped_ffn_backward: NULL argument");
+  CHECK(dw_dt == MOE_F32 || dw_dt == MOE_BF16, MOE_EUNSUPPORTED,
+        "moe_grouped_ffn_backward: weight gradients are F32 or BF16");
   s = check_ws(workspace, ws_bytes,
                grouped_ffn_backward_workspace_bytes(w, max_rows, row_index != nullptr),
                "moe_grouped_ffn_backward");
   if (s != MOE_OK) return s;
   return grouped_ffn_backward_launch(w, x_rows, row_index, offsets, max_rows, preact, h, d_rows,
-                                     dx_rows, dw1, dw3, dw2, workspace,
+                                     dx_rows, dw1, dw3, dw2, dw_dt, workspace,
                                      (hipStream_t)hip_stream);
 }
 

@@ -45,8 +45,9 @@ struct BwdArgs {
   const uint16_t* A;   // ROWS: [R][lda] rows, K-contiguous. DENSE: [R][lda] rows (K = row)
   const uint16_t* B0;  // ROWS: weights [E][K][ldb]. DENSE: [R][ldb] rows
   const uint16_t* B1;  // ROWS: second K segment (k >= kseg), or null
-  float* C0;           // F32 output: ROWS [R][ldc]; DENSE [E][mseg][ldc] (m < mseg)
-  float* C1;           // DENSE: [E][M - mseg][ldc] (m >= mseg), or null
+  void* C0;            // output: ROWS [R][ldc] fp32; DENSE [E][mseg][ldc] (m < mseg)
+  void* C1;            // DENSE: [E][M - mseg][ldc] (m >= mseg), or null
+  int c_bf16;          // DENSE: outputs rounded to bf16 instead of fp32
   const uint16_t* pre; // DSWIGLU: saved pre-activations [R][2 N] (gate | up)
   uint16_t* dpre;      // DSWIGLU: out [R][2 N] (d gate | d up)
   int M, N, K;         // DENSE: M, N; ROWS: N (columns), K (contraction)
@@ -323,13 +324,15 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bwd_kernel(BwdArgs g) {
             g.dpre[o] = moe::f32_to_bf16_bits(v * u * sig * (1.f + a * (1.f - sig)));
             g.dpre[o + g.N] = moe::f32_to_bf16_bits(v * a * sig);
           } else {
-            g.C0[(size_t)row * g.ldc + col] = v;
+            ((float*)g.C0)[(size_t)row * g.ldc + col] = v;
           }
         } else {
           const int m = m0 + lr;
-          float* C = m < g.mseg ? g.C0 + ((size_t)e * g.mseg + m) * g.ldc
-                                : g.C1 + ((size_t)e * (g.M - g.mseg) + (m - g.mseg)) * g.ldc;
-          C[col] = v;
+          const size_t o = m < g.mseg ? ((size_t)e * g.mseg + m) * g.ldc + col
+                                      : ((size_t)e * (g.M - g.mseg) + (m - g.mseg)) * g.ldc + col;
+          void* C = m < g.mseg ? g.C0 : g.C1;
+          if (g.c_bf16) ((uint16_t*)C)[o] = moe::f32_to_bf16_bits(v);
+          else ((float*)C)[o] = v;
         }
       }
     }

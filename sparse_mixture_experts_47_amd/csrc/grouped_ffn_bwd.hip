@@ -102,8 +102,9 @@ size_t grouped_ffn_backward_workspace_bytes(const moe_ffn_weights* w, int max_ro
 moe_status grouped_ffn_backward_launch(const moe_ffn_weights* w, const void* x_rows,
                                        const int32_t* row_index, const int32_t* offsets,
                                        int max_rows, const uint16_t* preact, const uint16_t* h,
-                                       const uint16_t* d_out, float* dx_rows, float* dw1,
-                                       float* dw3, float* dw2, void* workspace, hipStream_t st) {
+                                       const uint16_t* d_out, float* dx_rows, void* dw1,
+                                       void* dw3, void* dw2, moe_dtype dw_dt, void* workspace,
+                                       hipStream_t st) {
   using namespace moe_bwd;
   const int E = w->n_experts, d = w->d_model, F = w->d_ff;
   char* ws = (char*)workspace;
@@ -157,6 +158,7 @@ moe_status grouped_ffn_backward_launch(const moe_ffn_weights* w, const void* x_r
   w2.N = F;
   w2.mseg = d;
   w2.C0 = dw2;
+  w2.c_bf16 = dw_dt == MOE_BF16;
   w2.ldc = F;
   w2.n_tiles_n = F / kDenseBN;
   err = launch_bwd<MODE_DENSE, BEPI_F32, 256, kDenseBN, 2, kDenseWGM, 8 / kDenseWGM>(
@@ -194,6 +196,7 @@ moe_status grouped_ffn_backward_launch(const moe_ffn_weights* w, const void* x_r
   w1.mseg = F;
   w1.C0 = dw1;
   w1.C1 = dw3;
+  w1.c_bf16 = dw_dt == MOE_BF16;
   w1.ldc = d;
   w1.n_tiles_n = d / kDenseBN;
   err = launch_bwd<MODE_DENSE, BEPI_F32, 256, kDenseBN, 2, kDenseWGM, 8 / kDenseWGM>(

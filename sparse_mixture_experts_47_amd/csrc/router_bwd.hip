@@ -87,49 +87,89 @@ __global__ __launch_bounds__(kThreads) void router_bwd_token_kernel(
 }
 
 // dx_t = sum_j dx_rows[row_of[t][j]] (kept slots in order) + dx_shared[t]
-//        + sum_e dl_te W_g[e]
+//        + sum_e dl_te W_g[e] (e ascending). A block takes kDxTokens tokens x
+// 256 columns: their dl rows sit in LDS and every W_g element read serves
+// all of the block's tokens.
+constexpr int kDxTokens = 16;
 __global__ __launch_bounds__(kThreads) void router_bwd_dx_kernel(
-    int d, int E, int k, const float* __restrict__ dl, const float* __restrict__ w_gate,
+    int N, int d, int E, int k, const float* __restrict__ dl, const float* __restrict__ w_gate,
     const int32_t* __restrict__ row_of, const float* __restrict__ dx_rows,
     const float* __restrict__ dx_shared, float* __restrict__ dx) {
-  __shared__ float dls[256];
-  const int t = blockIdx.x;
-  for (int e = threadIdx.x; e < E; e += kThreads) dls[e] = dl[(size_t)t * E + e];
-  __syncthreads();
-  for (int c = threadIdx.x; c < d; c += kThreads) {
-    float acc = 0.f;
-    if (dx_rows)
-      for (int j = 0; j < k; ++j) {
-        const int r = row_of[(size_t)t * k + j];
-        if (r >= 0) acc += dx_rows[(size_t)r * d + c];
-      }
-    if (dx_shared) acc += dx_shared[(size_t)t * d + c];
-    for (int e = 0; e < E; ++e) acc = __builtin_fmaf(dls[e], w_gate[(size_t)e * d + c], acc);
-    dx[(size_t)t * d + c] = acc;
+  __shared__ __align__(16) float dls[kDxTokens][256];
+  const int t0 = blockIdx.x * kDxTokens, c = blockIdx.y * kThreads + threadIdx.x;
+  const int nt = min(kDxTokens, N - t0);
+  const int E4 = (E + 3) & ~3;  // dl columns past E are zero
+  for (int i = threadIdx.x; i < kDxTokens * E4; i += kThreads) {
+    const int tt = i / E4, e = i - tt * E4;
+    dls[tt][e] = (tt < nt && e < E) ? dl[(size_t)(t0 + tt) * E + e] : 0.f;
   }
+  __syncthreads();
+  if (c >= d) return;
+  float acc[kDxTokens];
+#pragma unroll
+  for (int tt = 0; tt < kDxTokens; ++tt) {
+    float a = 0.f;
+    if (tt < nt) {
+      const int t = t0 + tt;
+      if (dx_rows)
+        for (int j = 0; j < k; ++j) {
+          const int r = row_of[(size_t)t * k + j];
+          if (r >= 0) a += dx_rows[(size_t)r * d + c];
+        }
+      if (dx_shared) a += dx_shared[(size_t)t * d + c];
+    }
+    acc[tt] = a;
+  }
+  for (int e = 0; e < E4; e += 4) {
+    float w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = e + i < E ? w_gate[(size_t)(e + i) * d + c] : 0.f;
+#pragma unroll
+    for (int tt = 0; tt < kDxTokens; ++tt) {
+      const f32x4_t v = *(const f32x4_t*)&dls[tt][e];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[tt] = __builtin_fmaf(v[i], w[i], acc[tt]);
+    }
+  }
+#pragma unroll
+  for (int tt = 0; tt < kDxTokens; ++tt)
+    if (tt < nt) dx[(size_t)(t0 + tt) * d + c] = acc[tt];
 }
 
-// partial[chunk][e][c] = sum over the chunk's tokens of dl[t][e] x[t][c]
+// partial[chunk][e][c] = sum over the chunk's tokens (ascending) of
+// dl[t][e] x[t][c]; a block takes 256 columns x kWgExperts experts, with the
+// chunk's dl columns in LDS, so x is read once per expert group
+constexpr int kWgExperts = 32;
 template <typename XT>
 __global__ __launch_bounds__(kThreads) void router_bwd_wg_partial_kernel(
     int N, int d, int E, const float* __restrict__ dl, const XT* __restrict__ x,
     float* __restrict__ partial) {
+  __shared__ __align__(16) float dls[kChunkTokens][kWgExperts];
   const int c = blockIdx.x * kThreads + threadIdx.x;
-  const int e0 = blockIdx.y * 8, chunk = blockIdx.z;
-  if (c >= d) return;
+  const int e0 = blockIdx.y * kWgExperts, chunk = blockIdx.z;
   const int t0 = chunk * kChunkTokens, t1 = min(N, t0 + kChunkTokens);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int ne = min(kWgExperts, E - e0);
+  for (int i = threadIdx.x; i < kChunkTokens * kWgExperts; i += kThreads) {
+    const int tt = i / kWgExperts, ei = i - tt * kWgExperts;
+    dls[tt][ei] = (t0 + tt < t1 && ei < ne) ? dl[(size_t)(t0 + tt) * E + e0 + ei] : 0.f;
+  }
+  __syncthreads();
+  if (c >= d) return;
+  float acc[kWgExperts];
+#pragma unroll
+  for (int i = 0; i < kWgExperts; ++i) acc[i] = 0.f;
   for (int t = t0; t < t1; ++t) {
     float xv;
     if constexpr (sizeof(XT) == 2) xv = moe::bf16_bits_to_f32(x[(size_t)t * d + c]);
     else xv = x[(size_t)t * d + c];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (e0 + i < E) acc[i] = __builtin_fmaf(dl[(size_t)t * E + e0 + i], xv, acc[i]);
-  }
+    for (int i = 0; i < kWgExperts; i += 4) {
+      const f32x4_t v = *(const f32x4_t*)&dls[t - t0][i];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    if (e0 + i < E) partial[((size_t)chunk * E + e0 + i) * d + c] = acc[i];
+      for (int q = 0; q < 4; ++q) acc[i + q] = __builtin_fmaf(v[q], xv, acc[i + q]);
+    }
+  }
+  for (int i = 0; i < ne; ++i) partial[((size_t)chunk * E + e0 + i) * d + c] = acc[i];
 }
 
 // dW_g[e][c] = sum of the partials in chunk order
@@ -183,13 +223,14 @@ moe_status router_backward_launch(int N, int d, int E, int k, int C, int renorma
       beta, dlogits);
   moe_status s = launch_status("router backward (scores)");
   if (s != MOE_OK) return s;
-  router_bwd_dx_kernel<<<N, kThreads, 0, st>>>(d, E, k, dlogits, w_gate, row_of, dx_rows,
-                                               dx_shared, dx);
+  dim3 gdx((N + kDxTokens - 1) / kDxTokens, (d + kThreads - 1) / kThreads);
+  router_bwd_dx_kernel<<<gdx, kThreads, 0, st>>>(N, d, E, k, dlogits, w_gate, row_of, dx_rows,
+                                                 dx_shared, dx);
   s = launch_status("router backward (dx)");
   if (s != MOE_OK) return s;
   const int chunks = (N + kChunkTokens - 1) / kChunkTokens;
   float* partial = (float*)workspace;
-  dim3 grid((d + kThreads - 1) / kThreads, (E + 7) / 8, chunks);
+  dim3 grid((d + kThreads - 1) / kThreads, (E + kWgExperts - 1) / kWgExperts, chunks);
   if (x_dt == MOE_BF16)
     router_bwd_wg_partial_kernel<uint16_t><<<grid, kThreads, 0, st>>>(
         N, d, E, dlogits, (const uint16_t*)x, partial);

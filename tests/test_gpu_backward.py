@@ -326,3 +326,24 @@ def test_router_backward_fp32_against_oracle(moe, key):
 
 def dev_x(inp):
     return inp["x"].cuda()
+
+
+def test_bf16_weight_gradients_are_the_fp32_ones_rounded(moe):
+    """The bf16 weight-gradient output is the same fp32 sum rounded once to
+    nearest even (same kernels, deterministic order)."""
+    cfg = CASES["mixtral_reduced"]
+    inp = W.make_inputs(cfg, "cpu")
+    dev = to_device(inp)
+    layer = moe.MoELayer(moe.spec_from_config(cfg), dev, x_dtype=torch.bfloat16, train=True)
+    layer.forward(dev["x"])
+    dy = _dy(cfg).cuda()
+    g32 = {k: v.clone() for k, v in moe.layer_backward(layer, dev["x"], dy, ALPHA, BETA).items()
+           if v is not None}
+    g16 = moe.layer_backward(layer, dev["x"], dy, ALPHA, BETA, dw_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    for name in ("dw1", "dw3", "dw2"):
+        want = _bf16_bits(to_np(g32[name]))
+        got = g16[name].view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, want), name
+    for name in ("dx", "dw_gate", "dlogits"):
+        assert torch.equal(g32[name], g16[name]), name
