@@ -145,8 +145,17 @@ def _check_ec(layer, ec):
     assert np.array_equal(to_np(layer.ec_gates).view(np.uint32), ec["gates"].view(np.uint32))
 
 
-def test_expert_choice_layer_level1(moe):
-    cfg = W.REDUCED["c6"]
+EC_LAYERS = {
+    "c6": W.REDUCED["c6"],
+    # fine-grained experts (64, capacity ceil(320*8/64) = 40) plus a shared expert
+    "c3_expert_choice": W.REDUCED["c3"].with_(name="deepseek_reduced_expert_choice",
+                                              expert_choice=True, select_bias=False),
+}
+
+
+@pytest.mark.parametrize("key", list(EC_LAYERS))
+def test_expert_choice_layer_level1(moe, key):
+    cfg = EC_LAYERS[key]
     print("ec level1", cfg, flush=True)
     inp = W.make_inputs(cfg, "cpu")
     host = host_inputs(inp)
