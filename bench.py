@@ -21,7 +21,7 @@ forward (which keeps the experts' pre-activations) and the backward pass of
 L = <dy, y> + 0.01 Switch aux + 0.001 z-loss (combine backward, grouped FFN
 backward, router backward). The dominant kernel group is the grouped FFN
 backward (four bf16 MFMA GEMMs: data and weight gradients of both expert
-GEMMs, 12 d d_ff FLOPs per kept assignment).
+GEMMs, 4 d d_ff FLOPs per weight matrix per kept assignment).
 """
 import argparse
 import json
@@ -218,7 +218,9 @@ def bench_backward(args):
     torch.cuda.set_device(0)
     dev = W.make_inputs(cfg, "cuda")
     xdt = torch.float32 if cfg.x_dtype == W.F32 else torch.bfloat16
-    layer = moe.MoELayer(moe.spec_from_config(cfg), dev, x_dtype=xdt, train=True)
+    spec = moe.spec_from_config(cfg)
+    spec.h_fp32 = False  # training keeps h in bf16
+    layer = moe.MoELayer(spec, dev, x_dtype=xdt, train=True)
     x = dev["x"]
     g = torch.Generator(device="cuda").manual_seed(1234)
     dy = torch.randn((cfg.n_tokens, cfg.d_model), generator=g, device="cuda")
@@ -253,7 +255,9 @@ def bench_backward(args):
                                 top_k=cfg.top_k, renormalize=cfg.renormalize, alpha=alpha,
                                 beta=beta, dx_rows=b[0]["dx_rows"],
                                 dx_shared=b[0]["dx_shared"] if sh else None,
-                                dlogit_bias=b[0]["dlogit_bias"], ws=b[2])
+                                dlogit_bias=b[0]["dlogit_bias"], w_noise=dev.get("w_noise"),
+                                noise_seed=cfg.noise_seed, noise_v=layer.noise_v,
+                                dw_noise=b[0]["dw_noise"], ws=b[2])
         if e is not None:
             e[4].record(stream)
 
@@ -279,9 +283,36 @@ def bench_backward(args):
     touched = int((counts > 0).sum())
     R = int(counts.sum())
     d, F = cfg.d_model, cfg.d_ff
-    flops = 12.0 * d * F * R + 12.0 * d * cfg.shared_d_ff * cfg.n_tokens
+    nmat = 3 if cfg.act == 2 else 2  # weight matrices per expert
+    flops = 4.0 * nmat * d * (F * R + cfg.shared_d_ff * cfg.n_tokens)
     ms_bwd_ffn = float(np.median(samples["grouped_ffn_backward"]))
     tflops = flops / (ms_bwd_ffn * 1e-3) / 1e12
+    # algorithmic bytes of the expert backward: the data gradients read every
+    # touched weight once (bf16); every expert's weight gradients are written
+    # once; activations at their minimum (dO read twice, the saved pre-
+    # activations and h once, dpre written once and read twice, x rows read
+    # once, dX rows written once in fp32)
+    gb = 2 if args.dw_bf16 else 4
+    P = (2 if nmat == 3 else 1) * F
+    wbytes = nmat * d * F * 2 * touched + nmat * d * F * gb * cfg.n_experts
+    abytes = R * (2 * d * 2 + P * 2 + F * 2 + 3 * P * 2 + d * 2 + d * 4)
+    if cfg.shared_d_ff:
+        Fs, Ps = cfg.shared_d_ff, (2 if nmat == 3 else 1) * cfg.shared_d_ff
+        wbytes += nmat * d * Fs * (2 + gb)
+        abytes += cfg.n_tokens * (2 * d * 2 + Ps * 2 + Fs * 2 + 3 * Ps * 2 + d * 2 + d * 4)
+    gbs = (wbytes + abytes) / (ms_bwd_ffn * 1e-3) / 1e9
+    if args.workload in ("c3", "c4"):  # weight-bound shapes, as for the forward
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
+    roof.update(traffic=None,
+                kernel="moe_grouped_ffn_backward (data and weight gradients of both expert "
+                       "GEMMs, activation backward fused; routed + shared experts)",
+                per_launch={"flops": flops, "weight_bytes": wbytes, "activation_bytes": abytes,
+                            "avg_ms": round(ms_bwd_ffn, 4), "kept_assignments": R,
+                            "touched_experts": touched})
     ms_step = elapsed * 1e3 / args.steps
     out = {
         "metric": "MoE-layer training-step tokens/sec (forward + backward) + grouped-GEMM "
@@ -297,13 +328,9 @@ def bench_backward(args):
                    "act": ["relu", "gelu", "swiglu"][cfg.act], "loss": "<dy,y> + 0.01 aux + "
                    "0.001 z", "weight_grad_dtype": "bf16" if args.dw_bf16 else "f32",
                    "parallelism": "single-gpu"},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None,
-                     "kernel": "moe_grouped_ffn_backward (data and weight gradients of both "
-                               "expert GEMMs, SwiGLU backward fused; routed + shared experts)",
-                     "per_launch": {"flops": flops, "avg_ms": round(ms_bwd_ffn, 4),
-                                    "kept_assignments": R, "touched_experts": touched}},
+        "roofline": roof,
+        "grouped_ffn_backward_tflops": round(tflops, 1),
+        "grouped_ffn_backward_gbs": round(gbs, 1),
         "per_call_ms_median": {k: round(float(np.median(v)), 4) for k, v in samples.items()},
         "per_call_ms_min": {k: round(float(np.min(v)), 4) for k, v in samples.items()},
     }

@@ -106,6 +106,10 @@ typedef struct {
   float* scores_out;        /* [N][E] fp32 out: every softmax score s_te (the
                                values cand_scores takes them from), or NULL;
                                the input of moe_expert_choice */
+  float* noise_out;         /* [N][E] fp32 out with w_noise: v = x.W_noise^T
+                               before the softplus (the backward pass's
+                               input), or NULL. Not written when logits_in
+                               is given (the router computes no logits) */
 } moe_router_params;
 
 /*  x          [N][d] activations, x_dt = MOE_F32 or MOE_BF16
@@ -300,16 +304,20 @@ moe_status moe_balance_stats(int32_t n_tokens, int32_t n_experts, int32_t top_k,
  * mkbk-pku.cn "通信与并行", step 5: gradients go back along the forward's
  * routing path. Order of the calls: moe_combine_backward ->
  * moe_grouped_ffn_backward (routed experts, and the shared expert if any) ->
- * moe_router_backward. Scope: token-choice routing without noise; bf16
- * SwiGLU experts without biases; d_model and d_ff multiples of 256.
+ * moe_router_backward. Scope: token-choice routing (with or without noisy
+ * gating, capacity and reroute); bf16 SwiGLU, ReLU or
+ * GELU experts without biases (h kept in bf16); d_model and d_ff multiples
+ * of 256.
  * Gradients come out in fp32 (expert weight gradients optionally bf16) and
  * overwrite their buffers (no accumulation). */
 
 /* Forward of the routed (or shared) experts that also keeps what the
  * backward needs: as moe_grouped_ffn (bf16 activations), plus
- *  preact [max_rows][2 d_ff] bf16 out: per packed row the gate
- *         pre-activation a = x W1^T then the up projection u = x W3^T
- *  h      [max_rows][d_ff] bf16 out: silu(a) * u, the operand of GEMM 2
+ *  preact [max_rows][2 d_ff] bf16 out (SwiGLU: per packed row the gate
+ *         pre-activation a = x W1^T then the up projection u = x W3^T), or
+ *         [max_rows][d_ff] (ReLU / GELU: a)
+ *  h      [max_rows][d_ff] bf16 out: silu(a) * u or act(a), the operand of
+ *         GEMM 2
  * Rows past offsets[E] are untouched. Workspace: moe_grouped_ffn's. */
 moe_status moe_grouped_ffn_train(const moe_ffn_weights* w, const void* x_rows,
                                  const int32_t* row_index, const int32_t* offsets,
@@ -332,12 +340,14 @@ moe_status moe_combine_backward(int32_t n_tokens, int32_t d_model, int32_t top_k
                                 const int32_t* row_of, const float* gates, uint16_t* d_rows,
                                 float* dgates, uint16_t* d_shared, void* hip_stream);
 
-/* Backward of the grouped SwiGLU FFN. The shared expert is the same call
+/* Backward of the grouped expert FFN. The shared expert is the same call
  * with one expert, offsets {0, N}, row_index NULL and d_rows =
  * moe_combine_backward's d_shared. Per expert e over its packed rows
  * (a = x W1^T, u = x W3^T, h = silu(a) u, o = h W2^T):
  *  dh = dO W2; da = dh u silu'(a); du = dh silu(a); dX = da W1 + du W3;
  *  dW2_e = sum_r dO_r^T h_r; dW1_e = sum_r da_r^T x_r; dW3_e = sum_r du_r^T x_r.
+ *  ReLU / GELU (h = act(a)): da = dh act'(a), dX = da W1, no dW3 (dw3 may be
+ *  NULL); GELU' = Phi(a) + a phi(a) (exact erf form).
  *  x_rows, row_index, offsets, max_rows: as given to moe_grouped_ffn_train
  *  preact, h: what moe_grouped_ffn_train saved
  *  d_rows [R][d] bf16: dO (moe_combine_backward's d_rows)
@@ -359,24 +369,29 @@ moe_status moe_grouped_ffn_backward(const moe_ffn_weights* w, const void* x_rows
                                     void* hip_stream);
 
 /* Backward of the router (chiang97912 "KeepTopK 策略": gates renormalised
- * over the kept k; "[CS336-04]" section 4: z-loss); it also assembles the
- * token gradient dx. Per token, with s the
- * softmax of the logits the forward's softmax saw:
+ * over the kept k, noisy logits H(x); "[CS336-04]" section 4: z-loss); it
+ * also assembles the token gradient dx. Per token, with s the softmax of
+ * the logits the forward's softmax saw:
  *  renormalised gates: ds_{c_j} = (dg_j - sum_i dg_i g_i) / sum_i s_{c_i}
  *  Switch gate (renormalize = 0): ds_e += dg_j for the expert used
  *  auxiliary: ds_te += alpha E f_e / N, f_e = counts_routed[e] / (N k)
  *  dl_te = s_te (ds_te - sum_e s_te ds_te) + beta 2 lse_t s_te / N
+ *  noise (p->w_noise set): dv_te = dl_te z_te sigmoid(v_te) (1 for v > 20),
+ *  dW_noise = dv^T x
  *  dW_g = dl^T x; dlogit_bias = sum_t dl_t; dx_t = sum over the token's
- *  kept slots j (in order) of dx_rows[row_of[t][j]] + dx_shared[t] + dl_t W_g.
- *  p: n_tokens, d_model, n_experts, top_k, n_cand, renormalize as in the
- *     forward (w_noise must be NULL)
+ *  kept slots j (in order) of dx_rows[row_of[t][j]] + dx_shared[t]
+ *  + dl_t W_g + dv_t W_noise.
+ *  p: n_tokens, d_model, n_experts, top_k, n_cand, renormalize, w_noise and
+ *     noise_seed as in the forward
  *  logits [N][E] fp32: the forward's logits_out; cand_ids [N][n_cand],
  *  expert_of, row_of [N][k], counts_routed [E]: the forward's
  *  dgates [N][k] from moe_combine_backward; dx_rows from
  *  moe_grouped_ffn_backward or NULL (router part only); dx_shared [N][d]
- *  fp32 (the shared expert's moe_grouped_ffn_backward) or NULL
- *  dlogits [N][E], dw_gate [E][d], dlogit_bias [E] (or NULL), dx [N][d]:
- *  fp32 out. Deterministic. Workspace: moe_router_backward_workspace_bytes. */
+ *  fp32 (the shared expert's moe_grouped_ffn_backward) or NULL; noise_v
+ *  [N][E] fp32 (the forward's noise_out) with noise, else NULL
+ *  dlogits [N][E], dw_gate [E][d], dlogit_bias [E] (or NULL), dw_noise
+ *  [E][d] (with noise, else NULL), dx [N][d]: fp32 out. Deterministic.
+ *  Workspace: moe_router_backward_workspace_bytes. */
 size_t moe_router_backward_workspace_bytes(int32_t n_tokens, int32_t d_model,
                                            int32_t n_experts);
 moe_status moe_router_backward(const moe_router_params* p, const void* x, moe_dtype x_dt,
@@ -384,8 +399,9 @@ moe_status moe_router_backward(const moe_router_params* p, const void* x, moe_dt
                                const int32_t* expert_of, const int32_t* row_of,
                                const float* dgates, const int32_t* counts_routed, float alpha,
                                float beta, const float* dx_rows, const float* dx_shared,
-                               float* dlogits, float* dw_gate, float* dlogit_bias, float* dx,
-                               void* workspace, size_t ws_bytes, void* hip_stream);
+                               const float* noise_v, float* dlogits, float* dw_gate,
+                               float* dlogit_bias, float* dw_noise, float* dx, void* workspace,
+                               size_t ws_bytes, void* hip_stream);
 
 /* ---------------------------------------------------------------------- */
 /* Helpers                                                                 */

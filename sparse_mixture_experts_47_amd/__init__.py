@@ -43,7 +43,7 @@ class RouterParams(ctypes.Structure):
                 ("n_cand", ctypes.c_int32), ("renormalize", ctypes.c_int32),
                 ("logit_bias", ctypes.c_void_p), ("select_bias", ctypes.c_void_p),
                 ("w_noise", ctypes.c_void_p), ("noise_seed", ctypes.c_uint64),
-                ("scores_out", ctypes.c_void_p)]
+                ("scores_out", ctypes.c_void_p), ("noise_out", ctypes.c_void_p)]
 
 
 class FFNWeights(ctypes.Structure):
@@ -94,7 +94,8 @@ def _load():
     L.moe_router_backward_workspace_bytes.argtypes = [i32, i32, i32]
     L.moe_router_backward_workspace_bytes.restype = sz
     L.moe_router_backward.argtypes = [ctypes.POINTER(RouterParams), P, i32, P, P, P, P, P, P, P,
-                                      ctypes.c_float, ctypes.c_float, P, P, P, P, P, P, P, sz, P]
+                                      ctypes.c_float, ctypes.c_float, P, P, P, P, P, P, P, P, P,
+                                      sz, P]
     L.moe_router_backward.restype = i32
     L.moe_balance_stats.argtypes = [i32, i32, i32, P, P, P, P, P, P, P, ctypes.c_float, P]
     L.moe_balance_stats.restype = i32
@@ -158,17 +159,17 @@ def workspace(nbytes: int, device) -> torch.Tensor:
 def moe_router_topk(x, w_gate, *, top_k, n_cand=None, renormalize=True, logit_bias=None,
                     select_bias=None, w_noise=None, noise_seed=0, logits_in=None, cand_ids,
                     cand_scores, gates, logits_out=None, score_sums=None, scores_out=None,
-                    ws=None, stream=None):
+                    noise_out=None, ws=None, stream=None):
     """Router GEMM + fp32 softmax + top-k. Outputs are written in place;
     scores_out [N][E] fp32 (optional) receives every softmax score."""
     N, E = cand_ids.shape[0], (w_gate.shape[0] if logits_in is None else logits_in.shape[1])
     d = x.shape[1] if x is not None else 0
     n_cand = n_cand or top_k
     _dev_check(x, w_gate, logits_in, cand_ids, cand_scores, gates, logits_out, score_sums,
-               scores_out)
+               scores_out, noise_out)
     p = RouterParams(N, d, E, top_k, n_cand, int(bool(renormalize)),
                      _ptr(logit_bias), _ptr(select_bias), _ptr(w_noise), int(noise_seed),
-                     _ptr(scores_out))
+                     _ptr(scores_out), _ptr(noise_out))
     if ws is None:
         ws = workspace(lib.moe_router_workspace_bytes(N, d, E, int(w_noise is not None)),
                        cand_ids.device)
@@ -288,21 +289,22 @@ def moe_grouped_ffn_backward(weights: FFNWeights, x_rows, offsets, preact, h, d_
 
 def moe_router_backward(x, w_gate, logits, cand_ids, expert_of, row_of, dgates, counts_routed,
                         dlogits, dw_gate, dx, *, top_k, renormalize, alpha=0.0, beta=0.0,
-                        dx_rows=None, dx_shared=None, dlogit_bias=None, ws=None, stream=None):
+                        dx_rows=None, dx_shared=None, dlogit_bias=None, w_noise=None,
+                        noise_seed=0, noise_v=None, dw_noise=None, ws=None, stream=None):
     N, E = logits.shape
     d = x.shape[1]
     _dev_check(x, w_gate, logits, cand_ids, expert_of, row_of, dgates, counts_routed, dlogits,
-               dw_gate, dx, dx_rows, dx_shared, dlogit_bias)
+               dw_gate, dx, dx_rows, dx_shared, dlogit_bias, w_noise, noise_v, dw_noise)
     p = RouterParams(N, d, E, top_k, cand_ids.shape[1], int(bool(renormalize)), None, None,
-                     None, 0, None)
+                     _ptr(w_noise), int(noise_seed), None, None)
     if ws is None:
         ws = workspace(lib.moe_router_backward_workspace_bytes(N, d, E), x.device)
     _check(lib.moe_router_backward(ctypes.byref(p), _ptr(x), _dt(x), _ptr(w_gate), _ptr(logits),
                                    _ptr(cand_ids), _ptr(expert_of), _ptr(row_of), _ptr(dgates),
                                    _ptr(counts_routed), float(alpha), float(beta),
-                                   _ptr(dx_rows), _ptr(dx_shared), _ptr(dlogits), _ptr(dw_gate),
-                                   _ptr(dlogit_bias), _ptr(dx), _ptr(ws), ws.numel(),
-                                   _stream(stream)))
+                                   _ptr(dx_rows), _ptr(dx_shared), _ptr(noise_v), _ptr(dlogits),
+                                   _ptr(dw_gate), _ptr(dlogit_bias), _ptr(dw_noise), _ptr(dx),
+                                   _ptr(ws), ws.numel(), _stream(stream)))
 
 
 # --------------------------------------------------------------------- layer
@@ -417,19 +419,32 @@ class MoELayer:
         # training: the experts' forward keeps its pre-activations and h
         self.train = bool(train)
         if self.train:
-            if self.ec or weights.get("w_noise") is not None:
-                raise ValueError("the backward pass covers token choice without noise")
+            if self.ec:
+                raise ValueError("the backward pass covers token-choice routing")
+            if s.h_fp32:
+                raise ValueError("training keeps h in bf16 (build the spec with h_fp32=False)")
             bf = dict(dtype=torch.bfloat16, device=dev)
-            self.preact = torch.empty((R, 2 * s.d_ff), **bf)
+            glu = s.act == SWIGLU
+            self.preact = torch.empty((R, (2 if glu else 1) * s.d_ff), **bf)
+            self.noise_v = (torch.empty((N, E), **f32) if weights.get("w_noise") is not None
+                            else None)
             self.h = torch.empty((R, s.d_ff), **bf)
             if self.shared is not None:
-                self.preact_sh = torch.empty((N, 2 * s.shared_d_ff), **bf)
+                self.preact_sh = torch.empty((N, (2 if glu else 1) * s.shared_d_ff), **bf)
                 self.h_sh = torch.empty((N, s.shared_d_ff), **bf)
             self._bwd = None
         self._forward_done = False
 
-    def route(self, x, logits_in=None, stream=None):
+    def route(self, x, logits_in=None, stream=None, noise_in=None):
+        """noise_in (training with noisy gating and logits_in only): the noise
+        pre-activations v = x W_noise^T that produced logits_in, kept for the
+        backward pass (the router computes none when given logits)."""
         s, w = self.spec, self.w
+        if self.train and self.noise_v is not None:
+            if logits_in is not None:
+                if noise_in is None:
+                    raise ValueError("noisy gating with logits_in needs noise_in for training")
+                self.noise_v.copy_(noise_in)
         moe_router_topk(x, w["w_gate"], top_k=1 if self.ec else s.top_k, n_cand=self.C,
                         renormalize=s.renormalize and not self.ec,
                         logit_bias=w.get("logit_bias"),
@@ -437,7 +452,9 @@ class MoELayer:
                         w_noise=w.get("w_noise"), noise_seed=s.noise_seed, logits_in=logits_in,
                         cand_ids=self.cand_ids, cand_scores=self.cand_scores, gates=self.gates,
                         logits_out=self.logits, score_sums=self.score_sums,
-                        scores_out=self.scores, ws=self.ws_router, stream=stream)
+                        scores_out=self.scores,
+                        noise_out=self.noise_v if self.train else None, ws=self.ws_router,
+                        stream=stream)
 
     def dispatch(self, x, stream=None):
         s = self.spec
@@ -501,9 +518,10 @@ class MoELayer:
                           select_bias=self.w.get("select_bias") if update_bias else None,
                           bias_rate=s.bias_rate, stream=stream)
 
-    def forward(self, x, logits_in=None, stats=True, update_bias=False, stream=None):
+    def forward(self, x, logits_in=None, stats=True, update_bias=False, stream=None,
+                noise_in=None):
         self.start_shared(x, stream)
-        self.route(x, logits_in, stream)
+        self.route(x, logits_in, stream, noise_in)
         self.dispatch(x, stream)
         self.experts(x, stream)
         self.combine(stream)
@@ -520,9 +538,11 @@ def _backward_buffers(layer, dw_dtype=torch.float32):
     wdt = dict(dtype=dw_dtype, device=dev)
     b = dict(d_rows=torch.empty((R, d), dtype=torch.bfloat16, device=dev),
              dgates=torch.empty((N, s.top_k), **f32), dx_rows=torch.empty((R, d), **f32),
-             dw1=torch.empty((E, F, d), **wdt), dw3=torch.empty((E, F, d), **wdt),
+             dw1=torch.empty((E, F, d), **wdt),
+             dw3=torch.empty((E, F, d), **wdt) if s.act == SWIGLU else None,
              dw2=torch.empty((E, d, F), **wdt), dlogits=torch.empty((N, E), **f32),
              dw_gate=torch.empty((E, d), **f32), dx=torch.empty((N, d), **f32),
+             dw_noise=torch.empty((E, d), **f32) if layer.noise_v is not None else None,
              dlogit_bias=torch.empty(E, **f32) if layer.w.get("logit_bias") is not None else None)
     ws_f = workspace(lib.moe_grouped_ffn_backward_workspace_bytes(
         ctypes.byref(layer.ffn), R, int(layer.fused_gather)), dev)
@@ -530,7 +550,7 @@ def _backward_buffers(layer, dw_dtype=torch.float32):
         Fs = s.shared_d_ff
         b.update(d_shared=torch.empty((N, d), dtype=torch.bfloat16, device=dev),
                  dx_shared=torch.empty((N, d), **f32), shared_dw1=torch.empty((1, Fs, d), **wdt),
-                 shared_dw3=torch.empty((1, Fs, d), **wdt),
+                 shared_dw3=torch.empty((1, Fs, d), **wdt) if s.act == SWIGLU else None,
                  shared_dw2=torch.empty((1, d, Fs), **wdt))
         ws_s = workspace(lib.moe_grouped_ffn_backward_workspace_bytes(
             ctypes.byref(layer.shared), N, 0), dev)
@@ -542,7 +562,8 @@ def _backward_buffers(layer, dw_dtype=torch.float32):
 def layer_backward(layer, x, dy, alpha=0.0, beta=0.0, dw_dtype=torch.float32, stream=None):
     """Backward of the last `layer.forward` (the layer built with train=True):
     L = <dy, y> + alpha * Switch aux + beta * z-loss. Returns a dict of fp32
-    device tensors: dx, dw_gate, dlogit_bias (or None), dw1, dw3, dw2,
+    device tensors: dx, dw_gate, dlogit_bias (or None), dw_noise (or None),
+    dw1, dw3 (None unless SwiGLU), dw2,
     dlogits, dgates, and with a shared expert shared_dw1/3/2 [1][...] (buffers
     reused by the next call). dw_dtype: float32, or bfloat16 for the expert
     weight gradients."""
@@ -573,7 +594,9 @@ def layer_backward(layer, x, dy, alpha=0.0, beta=0.0, dw_dtype=torch.float32, st
                         b["dw_gate"], b["dx"], top_k=s.top_k, renormalize=s.renormalize,
                         alpha=alpha, beta=beta, dx_rows=b["dx_rows"],
                         dx_shared=b["dx_shared"] if sh else None,
-                        dlogit_bias=b["dlogit_bias"], ws=ws_r, stream=stream)
+                        dlogit_bias=b["dlogit_bias"], w_noise=w.get("w_noise"),
+                        noise_seed=s.noise_seed, noise_v=layer.noise_v, dw_noise=b["dw_noise"],
+                        ws=ws_r, stream=stream)
     return b
 
 

@@ -44,8 +44,9 @@ moe_status router_backward_launch(int N, int d, int E, int k, int C, int renorma
                                   const int32_t* expert_of, const int32_t* row_of,
                                   const float* dgates, const int32_t* counts_routed, float alpha,
                                   float beta, const float* dx_rows, const float* dx_shared,
-                                  float* dlogits, float* dw_gate, float* dlogit_bias, float* dx,
-                                  void* workspace, hipStream_t st);
+                                  const float* w_noise, const float* noise_v, uint64_t seed,
+                                  float* dlogits, float* dw_gate, float* dlogit_bias,
+                                  float* dw_noise, float* dx, void* workspace, hipStream_t st);
 moe_status combine_launch(int N, int d, int k, const void* y_rows, moe_dtype y_dt,
                           const int32_t* row_of, const float* gates, const void* y_shared,
                           moe_dtype sh_dt, void* y, moe_dtype out_dt, hipStream_t st);
@@ -260,9 +261,11 @@ static moe_status check_train_weights(const moe_ffn_weights* w, const char* who)
   const int E = w->n_experts, d = w->d_model, F = w->d_ff;
   CHECK(E >= 1 && E <= 256 && d >= 1 && F >= 1, MOE_EINVAL, "%s: E=%d d=%d d_ff=%d out of range",
         who, E, d, F);
-  CHECK(w->w1 && w->w2 && w->w3, MOE_EINVAL, "%s: NULL weight", who);
-  CHECK(w->act == MOE_SWIGLU && w->w_dt == MOE_BF16 && !w->b1 && !w->b2 && !w->h_fp32,
-        MOE_EUNSUPPORTED, "%s: training covers bf16 SwiGLU experts without biases", who);
+  CHECK(w->act == MOE_RELU || w->act == MOE_GELU || w->act == MOE_SWIGLU, MOE_EINVAL,
+        "%s: unknown activation %d", who, (int)w->act);
+  CHECK(w->w1 && w->w2 && (w->act != MOE_SWIGLU || w->w3), MOE_EINVAL, "%s: NULL weight", who);
+  CHECK(w->w_dt == MOE_BF16 && !w->b1 && !w->b2 && !w->h_fp32, MOE_EUNSUPPORTED,
+        "%s: training covers bf16 experts without biases and with bf16 h", who);
   CHECK(d % 256 == 0 && F % 256 == 0, MOE_EUNSUPPORTED,
         "%s: d_model %d and d_ff %d must be multiples of 256", who, d, F);
   return MOE_OK;
@@ -304,8 +307,9 @@ moe_status moe_grouped_ffn_backward(const moe_ffn_weights* w, const void* x_rows
   if (s != MOE_OK) return s;
   CHECK(max_rows >= 1 && (long long)max_rows * 2 * w->d_ff < (1ll << 40), MOE_EINVAL,
         "moe_grouped_ffn_backward: max_rows %d out of range", max_rows);
-  CHECK(x_rows && offsets && preact && h && d_rows && dx_rows && dw1 && dw3 && dw2, MOE_EINVAL,
-        "moe_grouped_ffn_backward: NULL argument");
+  CHECK(x_rows && offsets && preact && h && d_rows && dx_rows && dw1 && dw2 &&
+            (w->act != MOE_SWIGLU || dw3),
+        MOE_EINVAL, "moe_grouped_ffn_backward: NULL argument");
   CHECK(dw_dt == MOE_F32 || dw_dt == MOE_BF16, MOE_EUNSUPPORTED,
         "moe_grouped_ffn_backward: weight gradients are F32 or BF16");
   s = check_ws(workspace, ws_bytes,
@@ -344,14 +348,16 @@ moe_status moe_router_backward(const moe_router_params* p, const void* x, moe_dt
                                const int32_t* expert_of, const int32_t* row_of,
                                const float* dgates, const int32_t* counts_routed, float alpha,
                                float beta, const float* dx_rows, const float* dx_shared,
-                               float* dlogits, float* dw_gate, float* dlogit_bias, float* dx,
-                               void* workspace, size_t ws_bytes, void* hip_stream) {
+                               const float* noise_v, float* dlogits, float* dw_gate,
+                               float* dlogit_bias, float* dw_noise, float* dx, void* workspace,
+                               size_t ws_bytes, void* hip_stream) {
   CHECK(p, MOE_EINVAL, "moe_router_backward: params is NULL");
   const int N = p->n_tokens, d = p->d_model, E = p->n_experts, k = p->top_k, C = p->n_cand;
   CHECK(N >= 1 && d >= 1 && E >= 1 && k >= 1 && C >= k && k <= E, MOE_EINVAL,
         "moe_router_backward: N=%d d=%d E=%d k=%d n_cand=%d out of range", N, d, E, k, C);
   CHECK(E <= 256, MOE_EUNSUPPORTED, "moe_router_backward: n_experts %d > 256", E);
-  CHECK(!p->w_noise, MOE_EUNSUPPORTED, "moe_router_backward: noisy gating has no backward here");
+  CHECK(!p->w_noise || (noise_v && dw_noise), MOE_EINVAL,
+        "moe_router_backward: noisy gating needs noise_v and dw_noise");
   CHECK(x && w_gate && logits && cand_ids && expert_of && row_of && dgates && counts_routed &&
             dlogits && dw_gate && dx,
         MOE_EINVAL, "moe_router_backward: NULL argument");
@@ -362,8 +368,8 @@ moe_status moe_router_backward(const moe_router_params* p, const void* x, moe_dt
   if (s != MOE_OK) return s;
   return router_backward_launch(N, d, E, k, C, p->renormalize, x, x_dt, w_gate, logits, cand_ids,
                                 expert_of, row_of, dgates, counts_routed, alpha, beta, dx_rows,
-                                dx_shared, dlogits, dw_gate, dlogit_bias, dx, workspace,
-                                (hipStream_t)hip_stream);
+                                dx_shared, p->w_noise, noise_v, p->noise_seed, dlogits, dw_gate,
+                                dlogit_bias, dw_noise, dx, workspace, (hipStream_t)hip_stream);
 }
 
 moe_status moe_combine(int32_t n_tokens, int32_t d_model, int32_t top_k, const void* y_rows,

@@ -59,8 +59,9 @@ struct Args {
   const int32_t* seg_begin;
   const int32_t* seg_end;
   const int32_t* tile_e;
-  // GLU only, or null: the pre-activations are also stored, bf16, as rows
-  // of 2 * Nrows (gate | up) -- the state the backward pass differentiates
+  // GLU / ACT, or null: the pre-activations are also stored, bf16, as rows
+  // of 2 * Nrows (gate | up) or Nrows -- the state the backward pass
+  // differentiates
   uint16_t* pre;
 };
 
@@ -451,8 +452,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
             g.pre[po + g.Nrows] = moe::f32_to_bf16_bits(acc[NACC - 1][i][j][r]);
           }
         }
-        else if (EPI == EPI_ACT)
+        else if (EPI == EPI_ACT) {
           v = act_fn(g.act, acc[0][i][j][r] + bv);
+          if (g.pre) g.pre[(size_t)row * g.Nrows + col] = moe::f32_to_bf16_bits(acc[0][i][j][r] + bv);
+        }
         else
           v = acc[0][i][j][r] + bv;
         const size_t o = (size_t)row * g.ldc + col;

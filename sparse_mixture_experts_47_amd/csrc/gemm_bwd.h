@@ -39,7 +39,7 @@ namespace moe_bwd {
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 enum { MODE_ROWS = 0, MODE_DENSE = 1 };
-enum { BEPI_F32 = 0, BEPI_DSWIGLU = 1 };
+enum { BEPI_F32 = 0, BEPI_DSWIGLU = 1, BEPI_DACT = 2 };
 
 struct BwdArgs {
   const uint16_t* A;   // ROWS: [R][lda] rows, K-contiguous. DENSE: [R][lda] rows (K = row)
@@ -48,8 +48,9 @@ struct BwdArgs {
   void* C0;            // output: ROWS [R][ldc] fp32; DENSE [E][mseg][ldc] (m < mseg)
   void* C1;            // DENSE: [E][M - mseg][ldc] (m >= mseg), or null
   int c_bf16;          // DENSE: outputs rounded to bf16 instead of fp32
-  const uint16_t* pre; // DSWIGLU: saved pre-activations [R][2 N] (gate | up)
-  uint16_t* dpre;      // DSWIGLU: out [R][2 N] (d gate | d up)
+  const uint16_t* pre; // DSWIGLU: saved pre-activations [R][2 N] (gate | up); DACT: [R][N]
+  uint16_t* dpre;      // DSWIGLU: out [R][2 N] (d gate | d up); DACT: out [R][N]
+  int act;             // DACT: MOE_RELU or MOE_GELU
   int M, N, K;         // DENSE: M, N; ROWS: N (columns), K (contraction)
   int lda, ldb, ldc;
   int kseg, mseg;
@@ -314,7 +315,19 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bwd_kernel(BwdArgs g) {
         if constexpr (MODE == MODE_ROWS) {
           const int row = row0 + lr;
           if (row >= row_end) continue;
-          if constexpr (BEPI == BEPI_DSWIGLU) {
+          if constexpr (BEPI == BEPI_DACT) {
+            // h = act(a): da = v act'(a); ReLU' = [a > 0], GELU' = Phi(a) + a phi(a)
+            const size_t o = (size_t)row * g.N + col;
+            const float a = moe::bf16_bits_to_f32(g.pre[o]);
+            float dact;
+            if (g.act == MOE_RELU) {
+              dact = a > 0.f ? 1.f : 0.f;
+            } else {
+              const float Phi = 0.5f * (1.f + erff(a * 0.70710678118654752f));
+              dact = Phi + a * 0.39894228040143268f * __expf(-0.5f * a * a);
+            }
+            g.dpre[o] = moe::f32_to_bf16_bits(v * dact);
+          } else if constexpr (BEPI == BEPI_DSWIGLU) {
             // h = silu(a) * u; dh = v: da = v u silu'(a), du = v silu(a),
             // silu'(a) = sig (1 + a (1 - sig))
             const size_t o = (size_t)row * 2 * g.N + col;

@@ -1,5 +1,5 @@
-// grouped_ffn_bwd.hip -- backward pass of the grouped SwiGLU expert FFN on
-// gfx950 (bf16 MFMA, fp32 accumulation).
+// grouped_ffn_bwd.hip -- backward pass of the grouped expert FFN (SwiGLU,
+// or ReLU / GELU) on gfx950 (bf16 MFMA, fp32 accumulation).
 //
 // heavensheep.xyz MoE notes, "Training": an expert receives gradient only
 // from the tokens routed to it; mkbk-pku.cn "通信与并行", step 5: the
@@ -13,7 +13,8 @@
 //   dW1 = sum_r da_r^T x_r, dW3 = sum_r du_r^T x_r   (one launch)
 // The forward's training call saved a and u (bf16) and h (bf16, the exact
 // operand GEMM 2 used). dX stays in packed row order; the router's backward
-// sums it back to tokens.
+// sums it back to tokens. ReLU / GELU experts (h = act(a)) have one gate
+// plane: da = dh act'(a), dX = da W1, dW1 = sum_r da_r^T x_r.
 #include "gemm_bwd.h"
 
 // Tile shapes: 256-row M tiles; N tile width and the wave grid per tile space
@@ -107,6 +108,8 @@ moe_status grouped_ffn_backward_launch(const moe_ffn_weights* w, const void* x_r
                                        hipStream_t st) {
   using namespace moe_bwd;
   const int E = w->n_experts, d = w->d_model, F = w->d_ff;
+  const bool glu = w->act == MOE_SWIGLU;
+  const int P = glu ? 2 * F : F;  // columns of the saved pre-activations and of dpre
   char* ws = (char*)workspace;
   int32_t* ts = (int32_t*)ws;
   ws += align256((size_t)(E + 1) * 4);
@@ -143,8 +146,14 @@ moe_status grouped_ffn_backward_launch(const moe_ffn_weights* w, const void* x_r
   d2.n_tiles_n = F / kRowsBN;
   d2.pre = preact;
   d2.dpre = dpre;
-  hipError_t err = launch_bwd<MODE_ROWS, BEPI_DSWIGLU, 256, kRowsBN, 2, kRowsWGM, 8 / kRowsWGM>(
-      d2, (long long)max_mt * ((d2.n_tiles_n + d2.group_n - 1) / d2.group_n * d2.group_n), st);
+  d2.act = (int)w->act;
+  const long long d2_tiles =
+      (long long)max_mt * ((d2.n_tiles_n + d2.group_n - 1) / d2.group_n * d2.group_n);
+  hipError_t err =
+      glu ? launch_bwd<MODE_ROWS, BEPI_DSWIGLU, 256, kRowsBN, 2, kRowsWGM, 8 / kRowsWGM>(
+                d2, d2_tiles, st)
+          : launch_bwd<MODE_ROWS, BEPI_DACT, 256, kRowsBN, 2, kRowsWGM, 8 / kRowsWGM>(
+                d2, d2_tiles, st);
   if (err != hipSuccess) return bwd_status(err, "backward data gradient of GEMM 2");
 
   // weight gradient of GEMM 2: dW2[e][c][f] = sum_r dO[r][c] h[r][f]
@@ -169,14 +178,14 @@ moe_status grouped_ffn_backward_launch(const moe_ffn_weights* w, const void* x_r
   BwdArgs d1 = g;
   d1.group_n = MOE_BWD_ROWS_GN;
   d1.A = dpre;
-  d1.lda = 2 * F;
+  d1.lda = P;
   d1.B0 = (const uint16_t*)w->w1;  // [E][F][d]
-  d1.B1 = (const uint16_t*)w->w3;
+  d1.B1 = glu ? (const uint16_t*)w->w3 : nullptr;
   d1.kseg = F;
   d1.ldb = d;
   d1.b_expert = (long long)F * d;
   d1.N = d;
-  d1.K = 2 * F;
+  d1.K = P;
   d1.n_tiles_n = d / kRowsBN;
   d1.C0 = dx_rows;
   d1.ldc = d;
@@ -188,19 +197,19 @@ moe_status grouped_ffn_backward_launch(const moe_ffn_weights* w, const void* x_r
   BwdArgs w1 = g;
   w1.group_n = MOE_BWD_DENSE_GN;
   w1.A = dpre;
-  w1.lda = 2 * F;
+  w1.lda = P;
   w1.B0 = xp;
   w1.ldb = d;
-  w1.M = 2 * F;
+  w1.M = P;
   w1.N = d;
   w1.mseg = F;
   w1.C0 = dw1;
-  w1.C1 = dw3;
+  w1.C1 = glu ? dw3 : nullptr;
   w1.c_bf16 = dw_dt == MOE_BF16;
   w1.ldc = d;
   w1.n_tiles_n = d / kDenseBN;
   err = launch_bwd<MODE_DENSE, BEPI_F32, 256, kDenseBN, 2, kDenseWGM, 8 / kDenseWGM>(
-      w1, (long long)E * (2 * F / 256) * ((w1.n_tiles_n + w1.group_n - 1) / w1.group_n * w1.group_n), st);
+      w1, (long long)E * (P / 256) * ((w1.n_tiles_n + w1.group_n - 1) / w1.group_n * w1.group_n), st);
   return bwd_status(err, "backward weight gradient of GEMM 1");
 }
 

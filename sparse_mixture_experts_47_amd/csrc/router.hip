@@ -109,6 +109,7 @@ struct SelectArgs {
   float* gates;
   float* logits_out;
   float* scores_out;  // [N][E] softmax scores, or null
+  float* noise_out;   // [N][E] noise pre-activations v, or null
   double* partials;  // [gridDim.x][E+1] or null
   int tok_per_wave;
 };
@@ -169,6 +170,7 @@ __global__ __launch_bounds__(kThreads) void router_select_kernel(SelectArgs a) {
 #pragma unroll
             for (int q = 1; q < kMaxSplits; ++q)
               if (q < a.nsplit) nv = nv + pv[q];
+            if (a.noise_out) a.noise_out[(size_t)t * E + e] = nv;
             float sp = nv > 20.f ? nv : (float)log1p(exp((double)nv));
             float z = moe::noise_normal(a.seed, (uint32_t)t, (uint32_t)e, (uint32_t)E);
             v = __builtin_fmaf(z, sp, v);
@@ -488,6 +490,7 @@ moe_status router_launch(const moe_router_params* p, const void* x, moe_dtype x_
   a.gates = gates;
   a.logits_out = logits_out;
   a.scores_out = p->scores_out;
+  a.noise_out = p->noise_out;
   a.partials = score_sums ? partials : nullptr;
   a.tok_per_wave = select_tok_per_wave(N);
   if (E <= 64)

@@ -15,6 +15,9 @@
 //   auxiliary:    dL/ds_te += alpha E f_e / N, f_e = routed_e / (N k)
 //   softmax:      dl_te = s_te (ds_te - sum_e' s_te' ds_te')
 //   z-loss:       dl_te += beta 2 lse_t s_te / N
+//   noise (chiang97912 "KeepTopK 策略": H = x W_g + z softplus(x W_noise)):
+//                 dv_te = dl_te z_te sigmoid(v_te) (1 where softplus is v, v > 20),
+//                 dW_noise = dv^T x,  dx_t += dv_t W_noise
 //   router GEMM:  dW_g = dl^T x,  d(logit bias) = sum_t dl_t,  dx_t += dl_t W_g
 // dx_t also sums the token's kept expert-row gradients in slot order and the
 // shared expert's token-row gradient.
@@ -31,7 +34,8 @@ __global__ __launch_bounds__(kThreads) void router_bwd_token_kernel(
     const int32_t* __restrict__ cand_ids, const int32_t* __restrict__ expert_of,
     const int32_t* __restrict__ row_of, const float* __restrict__ dgates,
     const int32_t* __restrict__ counts_routed, float alpha, float beta,
-    float* __restrict__ dlogits) {
+    float* __restrict__ dlogits, const float* __restrict__ noise_v, uint64_t seed,
+    float* __restrict__ dv) {
   __shared__ float s_sh[kThreads / 64][256];
   __shared__ float ds_sh[kThreads / 64][256];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -82,26 +86,37 @@ __global__ __launch_bounds__(kThreads) void router_bwd_token_kernel(
   const float zc = beta * 2.f * lse / (float)N;
   for (int e = lane; e < E; e += 64) {
     const float s = S_[e];
-    dlogits[(size_t)t * E + e] = s * (D_[e] - sd) + zc * s;
+    const float g = s * (D_[e] - sd) + zc * s;
+    dlogits[(size_t)t * E + e] = g;
+    if (noise_v) {
+      const float v = noise_v[(size_t)t * E + e];
+      const float z = moe::noise_normal(seed, (uint32_t)t, (uint32_t)e, (uint32_t)E);
+      const float sig = v > 20.f ? 1.f : 1.f / (1.f + __expf(-v));
+      dv[(size_t)t * E + e] = g * z * sig;
+    }
   }
 }
 
 // dx_t = sum_j dx_rows[row_of[t][j]] (kept slots in order) + dx_shared[t]
-//        + sum_e dl_te W_g[e] (e ascending). A block takes kDxTokens tokens x
+//        + sum_e dl_te W_g[e] (e ascending) + sum_e dv_te W_noise[e] (with
+//        noise). A block takes kDxTokens tokens x
 // 256 columns: their dl rows sit in LDS and every W_g element read serves
 // all of the block's tokens.
 constexpr int kDxTokens = 16;
 __global__ __launch_bounds__(kThreads) void router_bwd_dx_kernel(
     int N, int d, int E, int k, const float* __restrict__ dl, const float* __restrict__ w_gate,
     const int32_t* __restrict__ row_of, const float* __restrict__ dx_rows,
-    const float* __restrict__ dx_shared, float* __restrict__ dx) {
+    const float* __restrict__ dx_shared, const float* __restrict__ dv,
+    const float* __restrict__ w_noise, float* __restrict__ dx) {
   __shared__ __align__(16) float dls[kDxTokens][256];
+  __shared__ __align__(16) float dvs[kDxTokens][256];
   const int t0 = blockIdx.x * kDxTokens, c = blockIdx.y * kThreads + threadIdx.x;
   const int nt = min(kDxTokens, N - t0);
   const int E4 = (E + 3) & ~3;  // dl columns past E are zero
   for (int i = threadIdx.x; i < kDxTokens * E4; i += kThreads) {
     const int tt = i / E4, e = i - tt * E4;
     dls[tt][e] = (tt < nt && e < E) ? dl[(size_t)(t0 + tt) * E + e] : 0.f;
+    if (dv) dvs[tt][e] = (tt < nt && e < E) ? dv[(size_t)(t0 + tt) * E + e] : 0.f;
   }
   __syncthreads();
   if (c >= d) return;
@@ -131,6 +146,18 @@ __global__ __launch_bounds__(kThreads) void router_bwd_dx_kernel(
       for (int i = 0; i < 4; ++i) acc[tt] = __builtin_fmaf(v[i], w[i], acc[tt]);
     }
   }
+  if (dv)
+    for (int e = 0; e < E4; e += 4) {
+      float w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = e + i < E ? w_noise[(size_t)(e + i) * d + c] : 0.f;
+#pragma unroll
+      for (int tt = 0; tt < kDxTokens; ++tt) {
+        const f32x4_t v = *(const f32x4_t*)&dvs[tt][e];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[tt] = __builtin_fmaf(v[i], w[i], acc[tt]);
+      }
+    }
 #pragma unroll
   for (int tt = 0; tt < kDxTokens; ++tt)
     if (tt < nt) dx[(size_t)(t0 + tt) * d + c] = acc[tt];
@@ -204,9 +231,10 @@ __global__ __launch_bounds__(kThreads) void router_bwd_bias_kernel(int N, int E,
 
 namespace moe_host {
 
+// workspace: dW partials [chunks][E][d] | dv [N][E]
 size_t router_backward_workspace_bytes(int N, int d, int E) {
   const int chunks = (N + kChunkTokens - 1) / kChunkTokens;
-  return align256((size_t)chunks * E * d * 4);
+  return align256((size_t)chunks * E * d * 4) + align256((size_t)N * E * 4);
 }
 
 moe_status router_backward_launch(int N, int d, int E, int k, int C, int renormalize,
@@ -215,34 +243,41 @@ moe_status router_backward_launch(int N, int d, int E, int k, int C, int renorma
                                   const int32_t* expert_of, const int32_t* row_of,
                                   const float* dgates, const int32_t* counts_routed, float alpha,
                                   float beta, const float* dx_rows, const float* dx_shared,
-                                  float* dlogits, float* dw_gate, float* dlogit_bias, float* dx,
-                                  void* workspace, hipStream_t st) {
+                                  const float* w_noise, const float* noise_v, uint64_t seed,
+                                  float* dlogits, float* dw_gate, float* dlogit_bias,
+                                  float* dw_noise, float* dx, void* workspace, hipStream_t st) {
+  const int chunks = (N + kChunkTokens - 1) / kChunkTokens;
+  float* partial = (float*)workspace;
+  float* dv = w_noise ? (float*)((char*)workspace + align256((size_t)chunks * E * d * 4)) : nullptr;
   const int per_block = kThreads / 64;
   router_bwd_token_kernel<<<(N + per_block - 1) / per_block, kThreads, 0, st>>>(
       N, E, k, C, renormalize, logits, cand_ids, expert_of, row_of, dgates, counts_routed, alpha,
-      beta, dlogits);
+      beta, dlogits, w_noise ? noise_v : nullptr, seed, dv);
   moe_status s = launch_status("router backward (scores)");
   if (s != MOE_OK) return s;
   dim3 gdx((N + kDxTokens - 1) / kDxTokens, (d + kThreads - 1) / kThreads);
   router_bwd_dx_kernel<<<gdx, kThreads, 0, st>>>(N, d, E, k, dlogits, w_gate, row_of, dx_rows,
-                                                 dx_shared, dx);
+                                                 dx_shared, dv, w_noise, dx);
   s = launch_status("router backward (dx)");
   if (s != MOE_OK) return s;
-  const int chunks = (N + kChunkTokens - 1) / kChunkTokens;
-  float* partial = (float*)workspace;
-  dim3 grid((d + kThreads - 1) / kThreads, (E + kWgExperts - 1) / kWgExperts, chunks);
-  if (x_dt == MOE_BF16)
-    router_bwd_wg_partial_kernel<uint16_t><<<grid, kThreads, 0, st>>>(
-        N, d, E, dlogits, (const uint16_t*)x, partial);
-  else
-    router_bwd_wg_partial_kernel<float><<<grid, kThreads, 0, st>>>(N, d, E, dlogits,
-                                                                   (const float*)x, partial);
-  s = launch_status("router backward (dW_g partials)");
-  if (s != MOE_OK) return s;
-  router_bwd_wg_reduce_kernel<<<(int)(((size_t)E * d + kThreads - 1) / kThreads), kThreads, 0,
-                                st>>>(d, E, chunks, partial, dw_gate);
-  s = launch_status("router backward (dW_g)");
-  if (s != MOE_OK) return s;
+  // dW = g^T x for g = dl (-> dW_g) and, with noise, g = dv (-> dW_noise)
+  for (int pass = 0; pass < (w_noise ? 2 : 1); ++pass) {
+    const float* gsrc = pass == 0 ? dlogits : dv;
+    float* out = pass == 0 ? dw_gate : dw_noise;
+    dim3 grid((d + kThreads - 1) / kThreads, (E + kWgExperts - 1) / kWgExperts, chunks);
+    if (x_dt == MOE_BF16)
+      router_bwd_wg_partial_kernel<uint16_t><<<grid, kThreads, 0, st>>>(
+          N, d, E, gsrc, (const uint16_t*)x, partial);
+    else
+      router_bwd_wg_partial_kernel<float><<<grid, kThreads, 0, st>>>(N, d, E, gsrc,
+                                                                     (const float*)x, partial);
+    s = launch_status("router backward (weight gradient partials)");
+    if (s != MOE_OK) return s;
+    router_bwd_wg_reduce_kernel<<<(int)(((size_t)E * d + kThreads - 1) / kThreads), kThreads, 0,
+                                  st>>>(d, E, chunks, partial, out);
+    s = launch_status("router backward (weight gradient)");
+    if (s != MOE_OK) return s;
+  }
   if (dlogit_bias) {
     router_bwd_bias_kernel<<<E, kThreads, 0, st>>>(N, E, dlogits, dlogit_bias);
     s = launch_status("router backward (logit bias)");

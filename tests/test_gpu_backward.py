@@ -92,6 +92,8 @@ CASES = {
                                                   capacity_factor=1.0, n_tokens=512),
     # 64 experts, top-8 with a selection bias, plus a shared expert
     "deepseek_reduced": W.REDUCED["c3"],
+    # Switch top-1 with noisy gating, capacity, reroute then drop; GELU experts
+    "switch_gelu_noise_reduced": W.REDUCED["c4"],
 }
 
 
@@ -113,12 +115,20 @@ def test_layer_backward_matches_oracle(moe, key):
     dy = _dy(cfg)
     ref = OB.layer_backward(cfg, host["x"], cfg.x_dtype, host["w_gate"], experts, fwd,
                             dy.numpy().astype(np.float64), ALPHA, BETA, shared=shared,
-                            logit_bias=host["logit_bias"], keep_terms=True)
+                            logit_bias=host["logit_bias"], w_noise=host["w_noise"],
+                            keep_terms=True)
     dev = to_device(inp)
-    layer = moe.MoELayer(moe.spec_from_config(cfg), dev, x_dtype=torch.bfloat16, train=True)
-    layer_eval = moe.MoELayer(moe.spec_from_config(cfg), dev, x_dtype=torch.bfloat16)
+    spec = moe.spec_from_config(cfg)
+    spec.h_fp32 = False  # training keeps h in bf16
+    layer = moe.MoELayer(spec, dev, x_dtype=torch.bfloat16, train=True)
+    layer_eval = moe.MoELayer(spec, dev, x_dtype=torch.bfloat16)
     logits = torch.from_numpy(fwd["logits"]).cuda()
-    y = layer.forward(dev["x"], logits_in=logits).clone()
+    noise_in = None
+    if host["w_noise"] is not None:  # the pre-activations that produced the oracle's logits
+        X = oracle.decode_rows(host["x"], cfg.x_dtype)
+        noise_in = torch.from_numpy((X @ host["w_noise"].astype(np.float64).T)
+                                    .astype(np.float32)).cuda()
+    y = layer.forward(dev["x"], logits_in=logits, noise_in=noise_in).clone()
     y_eval = layer_eval.forward(dev["x"], logits_in=logits)
     torch.cuda.synchronize()
     # the training forward computes the same layer output bit for bit
@@ -130,6 +140,38 @@ def test_layer_backward_matches_oracle(moe, key):
     torch.cuda.synchronize()
     _check_bounds(g, ref, fwd, dy.numpy().astype(np.float64), host, cfg)
     _check_router_statistical(g, ref, fwd, dy.numpy().astype(np.float64), host, cfg)
+
+
+def _first_order_terms(T, act):
+    """First-order rounding-error terms (in units of u) of da and du per row
+    and feature (du's None without SwiGLU): the roundings of a (and u), of
+    dO through dh = dO W2 (absolute terms A), and of da (du) itself."""
+    a, dh = T["a"], T["dh"]
+    A = np.abs(T["dO"]) @ np.abs(T["w2"])
+    if act == W.ACT_SWIGLU:
+        uu = T["u"]
+        sig = 1.0 / (1.0 + np.exp(-a))
+        silu, dsilu = a * sig, sig * (1.0 + a * (1.0 - sig))
+        Ma = np.abs(uu * dsilu) * A + np.abs(dh * uu) * (np.abs(dsilu) + np.abs(a)) + np.abs(T["da"])
+        Mu = np.abs(silu) * A + np.abs(dh) * (np.abs(dsilu * a) + np.abs(silu)) + np.abs(T["du"])
+        return Ma, Mu
+    if act == W.ACT_GELU:
+        phi = np.exp(-0.5 * a * a) / np.sqrt(2.0 * np.pi)
+        from scipy.special import erf
+        dact = 0.5 * (1.0 + erf(a / np.sqrt(2.0))) + a * phi
+        d2 = phi * (2.0 - a * a)  # GELU''
+    else:
+        dact = (a > 0).astype(np.float64)
+        d2 = np.zeros_like(a)
+    return np.abs(dact) * A + np.abs(dh * d2 * a) + np.abs(T["da"]), None
+
+
+def _noise_factor(cfg, host):
+    """z sigmoid(v) of the noisy gating, per token and expert (fp64)."""
+    X = oracle.decode_rows(host["x"], cfg.x_dtype)
+    v = X @ host["w_noise"].astype(np.float64).T
+    z = oracle.hash_normal_grid(cfg.noise_seed, cfg.n_tokens, cfg.n_experts).astype(np.float64)
+    return z / (1.0 + np.exp(-v))
 
 
 def _check_router_statistical(g, ref, fwd, dy, host, cfg):
@@ -188,6 +230,10 @@ def _check_router_statistical(g, ref, fwd, dy, host, cfg):
     if g["dlogit_bias"] is not None:
         checks["dlogit_bias"] = (ref["dlogit_bias"], 7 * np.sqrt((sl ** 2).sum(axis=0))
                                  + (Fdl + 1e-5 * np.abs(ref["dl"])).sum(axis=0))
+    if host["w_noise"] is not None:
+        zs = np.abs(_noise_factor(cfg, host))
+        checks["dw_noise"] = (ref["dw_noise"], 7 * np.sqrt(((sl * zs) ** 2).T @ X ** 2)
+                              + ((Fdl + 1e-5 * np.abs(ref["dl"])) * zs).T @ np.abs(X))
     worst = {}
     for name, (R, B) in checks.items():
         G = to_np(g[name]).astype(np.float64)
@@ -214,27 +260,25 @@ def _check_bounds(g, ref, fwd, dy, host, cfg):
         blocks.append(("shared", ref["shared_terms"]))
     for e, T in blocks:
         tt = T["tokens"]
-        a, uu, dh = T["a"], T["u"], T["dh"]
-        sig = 1.0 / (1.0 + np.exp(-a))
-        silu, dsilu = a * sig, sig * (1.0 + a * (1.0 - sig))
-        A = np.abs(T["dO"]) @ np.abs(T["w2"])
-        Ma = np.abs(uu * dsilu) * A + np.abs(dh * uu) * (np.abs(dsilu) + np.abs(a)) + np.abs(T["da"])
-        Mu = np.abs(silu) * A + np.abs(dh) * (np.abs(dsilu * a) + np.abs(silu)) + np.abs(T["du"])
+        Ma, Mu = _first_order_terms(T, cfg.act)
         X = np.abs(T["X"])
         pre, idx = ("shared_", 0) if e == "shared" else ("", e)
-        for name, B, R in (("dw2", np.abs(T["dO"]).T @ np.abs(T["h"]), ref[pre + "dW2"]),
-                           ("dw1", Ma.T @ X, ref[pre + "dW1"]), ("dw3", Mu.T @ X, ref[pre + "dW3"])):
+        cases = [("dw2", np.abs(T["dO"]).T @ np.abs(T["h"]), ref[pre + "dW2"]),
+                 ("dw1", Ma.T @ X, ref[pre + "dW1"])]
+        if Mu is not None:
+            cases.append(("dw3", Mu.T @ X, ref[pre + "dW3"]))
+        for name, B, R in cases:
             bounds.setdefault(pre + name, []).append(3 * u * B)
             refs.setdefault(pre + name, []).append(R if e == "shared" else R[e])
             gots.setdefault(pre + name, []).append(to_np(g[pre + name][idx]))
-        Brow = 3 * u * (Ma @ np.abs(T["w1"]) + Mu @ np.abs(T["w3"]))
+        Brow = 3 * u * (Ma @ np.abs(T["w1"]) + (Mu @ np.abs(T["w3"]) if Mu is not None else 0.0))
         np.add.at(Bdx, tt, Brow)
         if e == "shared":
             continue
         # expert part of dx: per packed row (rows are identical: row_of is bit-exact)
         jj = T["slots"]
         rows = dsp["row_of"][tt, jj]
-        ref_rows = T["da"] @ T["w1"] + T["du"] @ T["w3"]
+        ref_rows = T["da"] @ T["w1"] + (T["du"] @ T["w3"] if Mu is not None else 0.0)
         bounds.setdefault("dx_rows", []).append(Brow)
         refs.setdefault("dx_rows", []).append(ref_rows)
         gots.setdefault("dx_rows", []).append(dx_rows_gpu[rows])
@@ -256,8 +300,16 @@ def _check_bounds(g, ref, fwd, dy, host, cfg):
     xa = np.abs(oracle.decode_rows(host["x"], cfg.x_dtype))
     wga = np.abs(host["w_gate"].astype(np.float64))
     one = {"dgates": (Bg, ref["dg"]), "dlogits": (Bl, ref["dl"]),
-           "dw_gate": (Bl.T @ xa + 1e-5 * np.abs(ref["dl"]).T @ xa, ref["dw_gate"]),
-           "dx": (Bdx + Bl @ wga + 1e-5 * np.abs(ref["dl"]) @ wga, ref["dx"])}
+           "dw_gate": (Bl.T @ xa + 1e-5 * np.abs(ref["dl"]).T @ xa, ref["dw_gate"])}
+    Bx = Bdx + Bl @ wga + 1e-5 * np.abs(ref["dl"]) @ wga
+    if host["w_noise"] is not None:
+        # dv = dl z sigmoid(v): its error follows dl's
+        zs = np.abs(_noise_factor(cfg, host))
+        wna = np.abs(host["w_noise"].astype(np.float64))
+        Bv = Bl * zs + 1e-5 * np.abs(ref["dl"]) * zs
+        one["dw_noise"] = (Bv.T @ xa, ref["dw_noise"])
+        Bx = Bx + Bv @ wna
+    one["dx"] = (Bx, ref["dx"])
     if g["dlogit_bias"] is not None:
         one["dlogit_bias"] = (Bl.sum(axis=0), ref["dlogit_bias"])
     for name, (B, R) in one.items():
@@ -266,7 +318,9 @@ def _check_bounds(g, ref, fwd, dy, host, cfg):
     for name in bounds:
         for B, R, G in zip(bounds[name], refs[name], gots[name]):
             err = np.abs(np.asarray(G, np.float64) - R)
-            assert np.all(err <= B), (name, float(np.max(err - B)))
+            if not np.all(err <= B):
+                i = np.unravel_index(np.argmax(err - B), err.shape)
+                raise AssertionError((name, i, float(np.asarray(G)[i]), float(R[i]), float(B[i])))
             if B.size:
                 worst[name] = max(worst.get(name, 0.0), float(np.max(err / np.maximum(B, 1e-300))))
     print("  max error / bound:", {kk: round(v, 3) for kk, v in worst.items()}, flush=True)
@@ -277,6 +331,7 @@ ROUTER_CASES = {
     "c2": W.REDUCED["c2"],                                   # renormalised top-2
     "c3": W.REDUCED["c3"],                                   # E = 64, top-8, selection bias
     "c4_no_noise": W.REDUCED["c4"].with_(name="c4_reduced_no_noise", noisy=False),  # reroute
+    "c4": W.REDUCED["c4"],                                   # reroute + noisy gating
 }
 
 
@@ -296,17 +351,24 @@ def test_router_backward_fp32_against_oracle(moe, key):
     dsp = fwd["dispatch"]
     dg = np.where(dsp["row_of"] >= 0, rng.standard_normal((N, k)), 0.0).astype(np.float32)
     X = oracle.decode_rows(host["x"], cfg.x_dtype)
-    ref = OB.router_backward(cfg, X, host["w_gate"], fwd, dg, 0.3, 0.05, host["logit_bias"])
+    wn = host["w_noise"]
+    ref = OB.router_backward(cfg, X, host["w_gate"], fwd, dg, 0.3, 0.05, host["logit_bias"], wn)
     c = lambda a, dt=None: torch.from_numpy(np.ascontiguousarray(a if dt is None else a.astype(dt))).cuda()
     f32 = dict(dtype=torch.float32, device="cuda")
     out = dict(dlogits=torch.full((N, E), 7.0, **f32), dw_gate=torch.full((E, d), 7.0, **f32),
                dx=torch.full((N, d), 7.0, **f32),
-               dlogit_bias=None if host["logit_bias"] is None else torch.full((E,), 7.0, **f32))
+               dlogit_bias=None if host["logit_bias"] is None else torch.full((E,), 7.0, **f32),
+               dw_noise=None if wn is None else torch.full((E, d), 7.0, **f32))
+    noise = {}
+    if wn is not None:  # the noise pre-activations behind the oracle's logits
+        noise = dict(w_noise=c(wn), noise_seed=cfg.noise_seed,
+                     noise_v=c((X @ wn.astype(np.float64).T).astype(np.float32)))
     moe.moe_router_backward(dev_x(inp), c(host["w_gate"]), c(fwd["logits"]),
                             c(fwd["route"]["cand_ids"]), c(dsp["expert_of"]), c(dsp["row_of"]),
                             c(dg), c(dsp["counts_routed"]), out["dlogits"], out["dw_gate"],
                             out["dx"], top_k=k, renormalize=cfg.renormalize, alpha=0.3,
-                            beta=0.05, dlogit_bias=out["dlogit_bias"])
+                            beta=0.05, dlogit_bias=out["dlogit_bias"], dw_noise=out["dw_noise"],
+                            **noise)
     torch.cuda.synchronize()
     dl = ref["dl"]
     got = to_np(out["dlogits"])
@@ -319,6 +381,14 @@ def test_router_backward_fp32_against_oracle(moe, key):
               "dx": (ref["dx"], e_l * wga.sum(axis=0)[None, :] + 1e-5 * (adl @ wga))}
     if out["dlogit_bias"] is not None:
         checks["dlogit_bias"] = (ref["dlogit_bias"], e_l * N + 1e-5 * adl.sum(axis=0))
+    if wn is not None:
+        # dv = dl z sigmoid(v): within (e_l + 1e-5 |dl|) |z sigmoid(v)| plus its own rounding
+        zs = np.abs(_noise_factor(cfg, host))
+        ev = (e_l + 1e-5 * adl) * zs + 1e-5 * np.abs(ref["dl"]) * zs
+        wna = np.abs(wn.astype(np.float64))
+        checks["dw_noise"] = (ref["dw_noise"], ev.T @ ax + 1e-5 * (adl * zs).T @ ax)
+        R, B = checks["dx"]
+        checks["dx"] = (R, B + ev @ wna + 1e-5 * (adl * zs) @ wna)
     for name, (R, B) in checks.items():
         err = np.abs(to_np(out[name]).astype(np.float64) - R)
         assert np.all(err <= B), (name, float(np.max(err / B)))
