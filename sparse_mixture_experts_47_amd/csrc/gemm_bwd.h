@@ -302,50 +302,83 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bwd_kernel(BwdArgs g) {
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- epilogue
+  // ---- epilogue, staged through LDS: each 32 x 32 accumulator block goes
+  // to a wave-private LDS patch (rows padded to 36 floats: 16-byte aligned,
+  // and the two row halves a store instruction touches fall on different
+  // banks), and comes back as 4 consecutive columns per lane, so every
+  // global access is 16 bytes of fp32 (8 of bf16) and a store instruction
+  // covers 8 full 128-byte row segments instead of 2.
+  __syncthreads();  // every wave is done with the operand stages
+  constexpr int SP = 36;
+  float* stage = (float*)smem + wave * 32 * SP;
+  const int rq = lane >> 3, c4 = (lane & 7) * 4;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int col = n0 + wn * WN + j * 32 + (lane & 31);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int lr = wm * WM + i * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
-        const float v = acc[i][j][r];
+      for (int r = 0; r < 16; ++r)
+        stage[((r & 3) + 4 * (lane >> 5) + 8 * (r >> 2)) * SP + (lane & 31)] = acc[i][j][r];
+      const int col = n0 + wn * WN + j * 32 + c4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int br = rq + 8 * q;
+        const f32x4_t v = *(const f32x4_t*)(stage + br * SP + c4);
+        const int lr = wm * WM + i * 32 + br;
         if constexpr (MODE == MODE_ROWS) {
           const int row = row0 + lr;
           if (row >= row_end) continue;
           if constexpr (BEPI == BEPI_DACT) {
             // h = act(a): da = v act'(a); ReLU' = [a > 0], GELU' = Phi(a) + a phi(a)
             const size_t o = (size_t)row * g.N + col;
-            const float a = moe::bf16_bits_to_f32(g.pre[o]);
-            float dact;
-            if (g.act == MOE_RELU) {
-              dact = a > 0.f ? 1.f : 0.f;
-            } else {
-              const float Phi = 0.5f * (1.f + erff(a * 0.70710678118654752f));
-              dact = Phi + a * 0.39894228040143268f * __expf(-0.5f * a * a);
+            const u32x2_t ab = *(const u32x2_t*)(g.pre + o);
+            float da[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const float a = moe::bf16_bits_to_f32((uint16_t)(ab[t >> 1] >> (16 * (t & 1))));
+              float dact;
+              if (g.act == MOE_RELU) {
+                dact = a > 0.f ? 1.f : 0.f;
+              } else {
+                const float Phi = 0.5f * (1.f + erff(a * 0.70710678118654752f));
+                dact = Phi + a * 0.39894228040143268f * __expf(-0.5f * a * a);
+              }
+              da[t] = v[t] * dact;
             }
-            g.dpre[o] = moe::f32_to_bf16_bits(v * dact);
+            *(u32x2_t*)(g.dpre + o) = u32x2_t{moe::pack_bf16x2(da[0], da[1]),
+                                              moe::pack_bf16x2(da[2], da[3])};
           } else if constexpr (BEPI == BEPI_DSWIGLU) {
             // h = silu(a) * u; dh = v: da = v u silu'(a), du = v silu(a),
             // silu'(a) = sig (1 + a (1 - sig))
             const size_t o = (size_t)row * 2 * g.N + col;
-            const float a = moe::bf16_bits_to_f32(g.pre[o]);
-            const float u = moe::bf16_bits_to_f32(g.pre[o + g.N]);
-            const float sig = __builtin_amdgcn_rcpf(1.f + __expf(-a));
-            g.dpre[o] = moe::f32_to_bf16_bits(v * u * sig * (1.f + a * (1.f - sig)));
-            g.dpre[o + g.N] = moe::f32_to_bf16_bits(v * a * sig);
+            const u32x2_t ab = *(const u32x2_t*)(g.pre + o);
+            const u32x2_t ub = *(const u32x2_t*)(g.pre + o + g.N);
+            float da[4], du[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const float a = moe::bf16_bits_to_f32((uint16_t)(ab[t >> 1] >> (16 * (t & 1))));
+              const float u = moe::bf16_bits_to_f32((uint16_t)(ub[t >> 1] >> (16 * (t & 1))));
+              const float sig = __builtin_amdgcn_rcpf(1.f + __expf(-a));
+              da[t] = v[t] * u * sig * (1.f + a * (1.f - sig));
+              du[t] = v[t] * a * sig;
+            }
+            *(u32x2_t*)(g.dpre + o) = u32x2_t{moe::pack_bf16x2(da[0], da[1]),
+                                              moe::pack_bf16x2(da[2], da[3])};
+            *(u32x2_t*)(g.dpre + o + g.N) = u32x2_t{moe::pack_bf16x2(du[0], du[1]),
+                                                    moe::pack_bf16x2(du[2], du[3])};
           } else {
-            ((float*)g.C0)[(size_t)row * g.ldc + col] = v;
+            *(f32x4_t*)((float*)g.C0 + (size_t)row * g.ldc + col) = v;
           }
         } else {
           const int m = m0 + lr;
           const size_t o = m < g.mseg ? ((size_t)e * g.mseg + m) * g.ldc + col
                                       : ((size_t)e * (g.M - g.mseg) + (m - g.mseg)) * g.ldc + col;
           void* C = m < g.mseg ? g.C0 : g.C1;
-          if (g.c_bf16) ((uint16_t*)C)[o] = moe::f32_to_bf16_bits(v);
-          else ((float*)C)[o] = v;
+          if (g.c_bf16)
+            *(u32x2_t*)((uint16_t*)C + o) = u32x2_t{moe::pack_bf16x2(v[0], v[1]),
+                                                    moe::pack_bf16x2(v[2], v[3])};
+          else
+            *(f32x4_t*)((float*)C + o) = v;
         }
       }
     }
