@@ -431,41 +431,83 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
 
   constexpr int OB = OUTK == OUT_F32 ? 4 : 2;
   char* Cb = (char*)g.C + (size_t)blockIdx.y * g.c_split * OB;
+  // Epilogue, staged through LDS: each 32 x 32 block of results goes to a
+  // wave-private patch (rows padded to 36 floats: 16-byte aligned, and the
+  // row halves of one write fall on different banks) and comes back as 4
+  // consecutive columns per lane, so the global stores are 16 bytes (fp32)
+  // or 8 (bf16) a lane and one instruction covers 8 whole row segments.
+  static_assert(NS * STAGE * 2 >= NW * 32 * 36 * 4, "LDS for the staged epilogue");
+  __syncthreads();  // every wave is done with the operand stages
+  constexpr int SP = 36;
+  float* stage = (float*)smem + wave * 32 * SP;
+  const int rq = lane >> 3, c4 = (lane & 7) * 4;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int col = n0 + wn * WN + j * 32 + (lane & 31);
-      if (col >= g.n_valid) continue;
-      const float bv = ((EPI == EPI_ACT || EPI == EPI_OUT) && g.bias)
-                           ? g.bias[(size_t)e * g.Nrows + col] : 0.f;
+      const int colv = n0 + wn * WN + j * 32 + (lane & 31);
+      const float bv = ((EPI == EPI_ACT || EPI == EPI_OUT) && g.bias && colv < g.n_valid)
+                           ? g.bias[(size_t)e * g.Nrows + colv] : 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = row0 + wm * WM + i * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
-        if (row >= row_end) continue;
+        const int br = (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
         float v;
         if (EPI == EPI_GLU) {
           v = silu(acc[0][i][j][r]) * acc[NACC - 1][i][j][r];
-          if (g.pre) {
-            const size_t po = (size_t)row * 2 * g.Nrows + col;
+          const int row = row0 + wm * WM + i * 32 + br;
+          if (g.pre && row < row_end && colv < g.n_valid) {
+            const size_t po = (size_t)row * 2 * g.Nrows + colv;
             g.pre[po] = moe::f32_to_bf16_bits(acc[0][i][j][r]);
             g.pre[po + g.Nrows] = moe::f32_to_bf16_bits(acc[NACC - 1][i][j][r]);
           }
-        }
-        else if (EPI == EPI_ACT) {
+        } else if (EPI == EPI_ACT) {
           v = act_fn(g.act, acc[0][i][j][r] + bv);
-          if (g.pre) g.pre[(size_t)row * g.Nrows + col] = moe::f32_to_bf16_bits(acc[0][i][j][r] + bv);
-        }
-        else
-          v = acc[0][i][j][r] + bv;
-        const size_t o = (size_t)row * g.ldc + col;
-        if (OUTK == OUT_F32) {
-          ((float*)Cb)[o] = v;
+          const int row = row0 + wm * WM + i * 32 + br;
+          if (g.pre && row < row_end && colv < g.n_valid)
+            g.pre[(size_t)row * g.Nrows + colv] = moe::f32_to_bf16_bits(acc[0][i][j][r] + bv);
         } else {
-          const uint16_t hi = moe::f32_to_bf16_bits(v);
-          ((uint16_t*)Cb)[o] = hi;
-          if (OUTK == OUT_BF16_PAIR)
-            ((uint16_t*)Cb)[g.c_plane + o] = moe::f32_to_bf16_bits(v - moe::bf16_bits_to_f32(hi));
+          v = acc[0][i][j][r] + bv;
+        }
+        stage[br * SP + (lane & 31)] = v;
+      }
+      const int col = n0 + wn * WN + j * 32 + c4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int br = rq + 8 * q;
+        const int row = row0 + wm * WM + i * 32 + br;
+        if (row >= row_end || col >= g.n_valid) continue;
+        const f32x4_t v = *(const f32x4_t*)(stage + br * SP + c4);
+        const size_t o = (size_t)row * g.ldc + col;
+        if (col + 4 <= g.n_valid) {
+          if (OUTK == OUT_F32) {
+            *(f32x4_t*)((float*)Cb + o) = v;
+          } else {
+            uint16_t hb[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) hb[t] = moe::f32_to_bf16_bits(v[t]);
+            *(u32x2_t*)((uint16_t*)Cb + o) =
+                u32x2_t{(uint32_t)hb[0] | ((uint32_t)hb[1] << 16),
+                        (uint32_t)hb[2] | ((uint32_t)hb[3] << 16)};
+            if (OUTK == OUT_BF16_PAIR) {
+              float lo[4];
+#pragma unroll
+              for (int t = 0; t < 4; ++t) lo[t] = v[t] - moe::bf16_bits_to_f32(hb[t]);
+              *(u32x2_t*)((uint16_t*)Cb + g.c_plane + o) =
+                  u32x2_t{moe::pack_bf16x2(lo[0], lo[1]), moe::pack_bf16x2(lo[2], lo[3])};
+            }
+          }
+        } else {
+          for (int t = 0; t < 4 && col + t < g.n_valid; ++t) {
+            if (OUTK == OUT_F32) {
+              ((float*)Cb)[o + t] = v[t];
+            } else {
+              const uint16_t hi = moe::f32_to_bf16_bits(v[t]);
+              ((uint16_t*)Cb)[o + t] = hi;
+              if (OUTK == OUT_BF16_PAIR)
+                ((uint16_t*)Cb)[g.c_plane + o + t] =
+                    moe::f32_to_bf16_bits(v[t] - moe::bf16_bits_to_f32(hi));
+            }
+          }
         }
       }
     }
