@@ -1,6 +1,6 @@
 """Benchmark: one MoE FFN layer forward per step on one MI355X, through libmoe.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4|c5|c6]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4|c5|c6|c7]
                 [--backward]
 
 A step is one pass of the whole layer: router GEMM + fp32 softmax + top-k,
@@ -14,7 +14,10 @@ roofline: the grouped expert FFN (moe_grouped_ffn: tile table + GEMM 1
 gate/up with fused SwiGLU + GEMM 2 down) is the dominant kernel group; its
 duration is measured with HIP events on the launch stream inside the timed
 region. cpu_baseline: the CPU oracle (fp64 FFNs) timed on a bounded sample of
-the same workload on this host's cores.
+the same workload on this host's cores (for the tiny Switch layer also on one
+pinned core, in a child process). clocks: GFX and memory clocks and socket
+power read with amd-smi while the same step runs back to back, after the
+timed region.
 
 --backward: a step is one training pass of the layer instead: the training
 forward (which keeps the experts' pre-activations) and the backward pass of
@@ -42,7 +45,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "c6"])
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "c6", "c7"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0,
                     help="tokens in the oracle's timed sample (0: choose by workload)")
@@ -53,6 +56,10 @@ def parse():
                     help="time a training step (forward + backward) instead of the forward")
     ap.add_argument("--dw-bf16", action="store_true",
                     help="with --backward: expert weight gradients in bf16 instead of fp32")
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="skip the amd-smi clock and power sample after the timed region")
+    ap.add_argument("--oracle-single-core", action="store_true",
+                    help=argparse.SUPPRESS)  # child process: time the oracle on one core
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB read + 1 GiB write streaming kernel (torch.neg) "
                          "to calibrate the HBM byte counters")
@@ -167,6 +174,126 @@ def cpu_model():
     except OSError:
         pass
     return "unknown"
+
+
+def oracle_single_core_child(args):
+    """Child-process entry (no GPU use): pin this process to one core, draw the
+    workload's inputs by the same recipe with the CPU generator, and time the
+    oracle's layer forward on them; prints one JSON object."""
+    import workloads as W
+    core = sorted(os.sched_getaffinity(0))[0]
+    os.sched_setaffinity(0, {core})
+    cfg = W.CONFIGS[args.workload]
+    host = W.make_inputs(cfg, "cpu")
+    S = args.cpu_sample or cfg.n_tokens
+    runs, t0 = [], time.perf_counter()
+    while len(runs) < 3 or (time.perf_counter() - t0 < 2.0 and len(runs) < 200):
+        runs.append(cpu_baseline(cfg, host, S))
+    vals = sorted(r["value"] for r in runs)
+    r = runs[0]
+    r["value"] = vals[len(vals) // 2]
+    r["cores"] = 1
+    r["sample"] = ("oracle layer forward (fp32 routing, fp64 FFN/combine) on the first %d "
+                   "tokens of the workload as one batch, median of %d runs; one pinned core; "
+                   "inputs drawn by the same recipe with the CPU generator; CPU: %s"
+                   % (S, len(runs), cpu_model()))
+    print(json.dumps(r), flush=True)
+
+
+def cpu_baseline_single_core(workload, sample_tokens):
+    """The oracle on one core: a child process with every thread pool at one
+    thread (OpenMP, BLAS) and its affinity pinned to one core."""
+    import subprocess
+    env = dict(os.environ)
+    for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        env[k] = "1"
+    cmd = [sys.executable, os.path.abspath(__file__), "--workload", workload,
+           "--oracle-single-core", "--cpu-sample", str(sample_tokens)]
+    try:
+        r = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=600)
+        lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+        if r.returncode != 0 or not lines:
+            return {"error": "child exited with %d: %s" % (r.returncode, r.stderr[-300:])}
+        return json.loads(lines[-1])
+    except (OSError, subprocess.SubprocessError, ValueError) as e:
+        return {"error": repr(e)}
+
+
+def sample_clocks(run_step, cap_s=20.0):
+    """GFX and memory clocks and socket power while `run_step` (one step of
+    the workload) runs back to back: `amd-smi metric -c -p` is read from a
+    side thread while the main thread keeps the GPU busy. Returns the
+    per-domain clocks in MHz, or an error string if amd-smi is unavailable."""
+    import shutil
+    import subprocess
+    import threading
+
+    import torch
+
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return {"error": "amd-smi not found"}
+    res = {}
+
+    def probe():
+        # let the clock settle under the load first; the second of two reads
+        # is the one reported (the first can return the idle values of the
+        # firmware's previous metrics update)
+        time.sleep(1.0)
+        try:
+            for _ in range(2):
+                r = subprocess.run([exe, "metric", "-c", "-p"], capture_output=True, text=True,
+                                   timeout=60)
+                res["text"], res["rc"] = r.stdout, r.returncode
+        except (OSError, subprocess.SubprocessError) as e:
+            res["error"] = repr(e)
+
+    th = threading.Thread(target=probe)
+    th.start()
+    t0 = time.perf_counter()
+    n = 0
+    while th.is_alive() and time.perf_counter() - t0 < cap_s:
+        for _ in range(4):
+            run_step()
+        torch.cuda.synchronize()
+        n += 4
+    th.join()
+    if "text" not in res:
+        return {"error": res.get("error", "amd-smi did not finish")}
+    out = parse_amd_smi_clocks(res["text"])
+    if "error" in out:
+        out["error"] += " (rc %s)" % res.get("rc")
+        return out
+    out.update(steps_during_sample=n,
+               source="amd-smi metric -c -p, second of two reads taken while the step ran "
+                      "back to back (after 1 s of it) following the timed region")
+    return out
+
+
+def parse_amd_smi_clocks(text):
+    """Clocks from amd-smi's text report: each domain is a header line
+    ("GFX_0:", "MEM_0:", ...) followed by its "CLK: <n> MHz" line; the socket
+    power is a "SOCKET_POWER: <w> W" line."""
+    clocks, power, header = {}, None, None
+    for line in text.splitlines():
+        t = line.strip()
+        if t.endswith(":") and " " not in t:
+            header = t[:-1]
+        elif t.startswith("CLK:") and header and header not in clocks:
+            v = t[4:].split()
+            if v and v[0].isdigit():
+                clocks[header] = int(v[0])
+        elif t.startswith("SOCKET_POWER:"):
+            v = t.split(":", 1)[1].split()
+            if v and v[0].replace(".", "", 1).isdigit():
+                power = float(v[0])
+    gfx = [v for k, v in clocks.items() if k.upper().startswith("GFX")]
+    mem = [v for k, v in clocks.items() if k.upper().startswith("MEM")]
+    if not gfx:
+        return {"error": "no GFX clock in amd-smi output"}
+    return {"sclk_mhz_min": min(gfx), "sclk_mhz_max": max(gfx),
+            "mclk_mhz": max(mem) if mem else None, "socket_power_w": power,
+            "clocks_mhz": clocks}
 
 
 def cpu_baseline_backward(cfg, dev, sample_tokens, alpha, beta):
@@ -334,6 +461,8 @@ def bench_backward(args):
         "per_call_ms_median": {k: round(float(np.median(v)), 4) for k, v in samples.items()},
         "per_call_ms_min": {k: round(float(np.min(v)), 4) for k, v in samples.items()},
     }
+    if not args.no_clocks:
+        out["clocks"] = sample_clocks(step)
     if not args.no_cpu_baseline:
         S = args.cpu_sample or 256
         out["cpu_baseline"] = cpu_baseline_backward(cfg, dev, S, alpha, beta)
@@ -342,6 +471,8 @@ def bench_backward(args):
 
 def main():
     args = parse()
+    if args.oracle_single_core:
+        return oracle_single_core_child(args)
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -488,10 +619,14 @@ def main():
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = 4 * n
         del a, b
+    if not args.no_clocks:
+        out["clocks"] = sample_clocks(lambda: layer.forward(x))
     if not args.no_cpu_baseline:
         S = args.cpu_sample or {"c1": 256, "c2": 1024, "c3": 64, "c4": 4096, "c5": 64,
-                                  "c6": 1024}[args.workload]
+                                  "c6": 1024, "c7": 64}[args.workload]
         out["cpu_baseline"] = cpu_baseline(cfg, dev, S)
+        if args.workload == "c1":
+            out["cpu_baseline"]["single_core"] = cpu_baseline_single_core("c1", S)
     print(json.dumps(out), flush=True)
 
 

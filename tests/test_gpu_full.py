@@ -14,7 +14,7 @@ from parity_utils import (MARGIN, TOL_REL, DeviceExperts, host_view, margins, or
 
 pytestmark = pytest.mark.gpu
 
-SAMPLES = {"c1": 256, "c2": 12, "c3": 4, "c4": 24, "c5": 4}
+SAMPLES = {"c1": 256, "c2": 12, "c3": 4, "c4": 24, "c5": 4, "c7": 4}
 
 
 @pytest.fixture(scope="module")
@@ -24,7 +24,7 @@ def moe():
     return m
 
 
-@pytest.mark.parametrize("key", ["c1", "c2", "c3", "c4", "c5"])
+@pytest.mark.parametrize("key", ["c1", "c2", "c3", "c4", "c5", "c7"])
 def test_full_size_parity(moe, key):
     cfg = W.CONFIGS[key]
     print("full-size", key, cfg.name, flush=True)

@@ -108,7 +108,15 @@ C5 = MoEConfig("deepseek_decode_fp8", 64, 7168, 256, 2048, 8, ACT_SWIGLU, BF16, 
 # expert takes N * 2 / 8 = 1024 tokens.
 C6 = C2.with_(name="mixtral_prefill_expert_choice", expert_choice=True, seed=6)
 
-CONFIGS = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5, "c6": C6}
+# One GPU's share of the DeepSeek-shaped layer under 8-way expert parallelism:
+# 32 of the 256 experts live on the GPU, and the tokens of all eight GPUs that
+# route there arrive packed, about 8192 * 8 / 32 = 2048 rows per expert. Here
+# the GPU's own 8192 tokens route top-8 over its 32 experts, which gives the
+# grouped FFN that same shape (the exchange itself is not modelled); the
+# shared expert runs on the local tokens as in the full layer.
+C7 = C3.with_(name="deepseek_ep8_local_share", n_experts=32, seed=7)
+
+CONFIGS = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5, "c6": C6, "c7": C7}
 
 # Reduced shapes of the same recipes: small enough for the fp64 oracle to run
 # in seconds, large enough to span several GEMM tiles with ragged tails.
