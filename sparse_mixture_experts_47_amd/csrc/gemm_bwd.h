@@ -62,29 +62,75 @@ struct BwdArgs {
 
 __device__ __forceinline__ int ks_phys(int row, int chunk) { return chunk ^ ((row & 3) << 2); }
 
-// MFMA fragment (32 columns x 16 K) of a K-slow LDS tile [BK][BC] at column
-// block cb and K step kk. kvalid < BK zeroes the K values past it.
+// Element offset in a K-slow LDS tile [BK][BC] of the first of the two
+// transposing reads that give this lane its MFMA fragment (32 columns x 16 K)
+// at column block cb and K step kk; the second read is 4 rows further.
 template <int BC>
-__device__ __forceinline__ bf16x8_t frag_kslow(const uint16_t* tile, int cb, int kk, int lane,
-                                               int kvalid) {
+__device__ __forceinline__ int kslow_off(int cb, int kk, int lane) {
   const int G = lane >> 4, s = lane & 15, p = s >> 2, c4 = s & 3;
   const int row = kk * 16 + 8 * (G >> 1) + p;
   const int col = cb + 16 * (G & 1) + 4 * c4;
-  const int off0 = row * BC + (ks_phys(row, col >> 3) << 3) + (col & 7);
-  const int off1 = off0 + 4 * BC;  // row + 4: same (row & 3), same swizzle
-  s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4_t*)(tile + off0));
-  s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4_t*)(tile + off1));
-  if (kvalid < 64) {
-    // this lane holds K = kk*16 + 8*(lane>>5) + 0..7 of column (lane & 31)
-    const int k0 = kk * 16 + 8 * (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (k0 + i >= kvalid) lo[i] = 0;
-      if (k0 + 4 + i >= kvalid) hi[i] = 0;
-    }
-  }
+  return row * BC + (ks_phys(row, col >> 3) << 3) + (col & 7);  // row + 4: same swizzle
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
+}
+
+// N K-slow fragments of 256-column tiles (second read 4 rows = 2048 bytes
+// further), read with ds_read_b64_tr_b16 from one asm block that ends with
+// s_waitcnt lgkmcnt(0), so every output is in its register when the block
+// ends. (Written through the compiler's builtin instead, each transposing
+// read is preceded by a vmcnt(0) wait: the compiler cannot tell it from a
+// read of LDS that the in-flight global_load_lds transfers are still
+// writing, and so waits for the next stages' operand loads at every K step.)
+template <int N>
+__device__ __forceinline__ void kslow_read(s16x4_t (&lo)[N], s16x4_t (&hi)[N],
+                                           const uint32_t (&a)[N]);
+
+template <>
+__device__ __forceinline__ void kslow_read<4>(s16x4_t (&lo)[4], s16x4_t (&hi)[4],
+                                              const uint32_t (&a)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %2, %9\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %4, %10\n\t"
+      "ds_read_b64_tr_b16 %5, %10 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %6, %11\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:2048\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]),
+        "=&v"(lo[3]), "=&v"(hi[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void kslow_read<6>(s16x4_t (&lo)[6], s16x4_t (&hi)[6],
+                                              const uint32_t (&a)[6]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %12\n\t"
+      "ds_read_b64_tr_b16 %1, %12 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %2, %13\n\t"
+      "ds_read_b64_tr_b16 %3, %13 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %4, %14\n\t"
+      "ds_read_b64_tr_b16 %5, %14 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %6, %15\n\t"
+      "ds_read_b64_tr_b16 %7, %15 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %8, %16\n\t"
+      "ds_read_b64_tr_b16 %9, %16 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %10, %17\n\t"
+      "ds_read_b64_tr_b16 %11, %17 offset:2048\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]),
+        "=&v"(lo[3]), "=&v"(hi[3]), "=&v"(lo[4]), "=&v"(hi[4]), "=&v"(lo[5]), "=&v"(hi[5])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5])
+      : "memory");
+}
+
+__device__ __forceinline__ bf16x8_t kslow_join(s16x4_t lo, s16x4_t hi) {
   union {
     s16x4_t h[2];
     bf16x8_t v;
@@ -239,19 +285,45 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bwd_kernel(BwdArgs g) {
     bf16x8_t a[FM];
     bf16x8_t b[FN];
   };
+  static_assert(BN == 256 && (MODE == MODE_ROWS || BM == 256),
+                "the transposing-read block assumes 256-column K-slow tiles");
+  constexpr int NKS = (MODE == MODE_DENSE ? FM : 0) + FN;  // K-slow fragments per K step
   auto read_frags = [&](Frags& f, int stage, int kk, int kvalid) {
     const uint16_t* cur = smem + stage * STAGE;
+    uint32_t addr[NKS];
+    if constexpr (MODE == MODE_ROWS) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      if constexpr (MODE == MODE_ROWS)
+      for (int i = 0; i < FM; ++i)
         f.a[i] = *(const bf16x8_t*)(cur + moe_gemm::dlds_off<64>(wm * WM + i * 32 + (lane & 31),
                                                                   kk * 2 + (lane >> 5)));
-      else
-        f.a[i] = frag_kslow<BM>(cur, wm * WM + i * 32, kk, lane, kvalid);
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        addr[i] = lds_addr(cur + kslow_off<BM>(wm * WM + i * 32, kk, lane));
     }
+    constexpr int B0 = MODE == MODE_DENSE ? FM : 0;
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-      f.b[j] = frag_kslow<BN>(cur + A_ELEMS, wn * WN + j * 32, kk, lane, 64);
+      addr[B0 + j] = lds_addr(cur + A_ELEMS + kslow_off<BN>(wn * WN + j * 32, kk, lane));
+    s16x4_t lo[NKS], hi[NKS];
+    kslow_read<NKS>(lo, hi, addr);
+    if constexpr (MODE == MODE_DENSE) {
+      if (kvalid < BK) {
+        // this lane holds K = kk*16 + 8*(lane>>5) + 0..7 of its column
+        const int k0 = kk * 16 + 8 * (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            if (k0 + t >= kvalid) lo[i][t] = 0;
+            if (k0 + 4 + t >= kvalid) hi[i][t] = 0;
+          }
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) f.a[i] = kslow_join(lo[i], hi[i]);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) f.b[j] = kslow_join(lo[B0 + j], hi[B0 + j]);
   };
   auto mfma = [&](const Frags& f) {
 #pragma unroll
