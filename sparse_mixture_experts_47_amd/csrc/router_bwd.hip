@@ -26,7 +26,6 @@
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChunkTokens = 256;  // tokens per partial sum of dW_g
 
 // one wave per token
 __global__ __launch_bounds__(kThreads) void router_bwd_token_kernel(
@@ -97,106 +96,220 @@ __global__ __launch_bounds__(kThreads) void router_bwd_token_kernel(
   }
 }
 
+// Four consecutive fp32 values of a row at column col (masked past d; as
+// one 16-byte access when rows are 16-byte aligned, i.e. d % 4 == 0).
+__device__ __forceinline__ f32x4_t load4(const float* __restrict__ row, int col, int d,
+                                         bool vec) {
+  if (vec && col + 3 < d) return *(const f32x4_t*)(row + col);
+  f32x4_t v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = col + q < d ? row[col + q] : 0.f;
+  return v;
+}
+
 // dx_t = sum_j dx_rows[row_of[t][j]] (kept slots in order) + dx_shared[t]
 //        + sum_e dl_te W_g[e] (e ascending) + sum_e dv_te W_noise[e] (with
-//        noise). A block takes kDxTokens tokens x
-// 256 columns: their dl rows sit in LDS and every W_g element read serves
-// all of the block's tokens.
-constexpr int kDxTokens = 16;
+//        noise). A block takes kDxT tokens x kDxC columns; each thread holds
+//        4 tokens x 16 columns (4 groups of 4 consecutive columns, 64 apart),
+//        and the product runs over LDS chunks of kDxE experts: the chunk's
+//        gradient columns (transposed, [e][token]) and weight rows
+//        ([e][column]), 64 FMAs per 5 LDS reads. (Loading the next chunk into
+//        registers during the products needs 200 VGPRs, and the halved
+//        occupancy slows the row gather more than the overlap gains.)
+constexpr int kDxT = 64, kDxC = 256, kDxE = 32;
 __global__ __launch_bounds__(kThreads) void router_bwd_dx_kernel(
     int N, int d, int E, int k, const float* __restrict__ dl, const float* __restrict__ w_gate,
     const int32_t* __restrict__ row_of, const float* __restrict__ dx_rows,
     const float* __restrict__ dx_shared, const float* __restrict__ dv,
     const float* __restrict__ w_noise, float* __restrict__ dx) {
-  __shared__ __align__(16) float dls[kDxTokens][256];
-  __shared__ __align__(16) float dvs[kDxTokens][256];
-  const int t0 = blockIdx.x * kDxTokens, c = blockIdx.y * kThreads + threadIdx.x;
-  const int nt = min(kDxTokens, N - t0);
-  const int E4 = (E + 3) & ~3;  // dl columns past E are zero
-  for (int i = threadIdx.x; i < kDxTokens * E4; i += kThreads) {
-    const int tt = i / E4, e = i - tt * E4;
-    dls[tt][e] = (tt < nt && e < E) ? dl[(size_t)(t0 + tt) * E + e] : 0.f;
-    if (dv) dvs[tt][e] = (tt < nt && e < E) ? dv[(size_t)(t0 + tt) * E + e] : 0.f;
-  }
-  __syncthreads();
-  if (c >= d) return;
-  float acc[kDxTokens];
+  __shared__ __align__(16) float gs[kDxE][kDxT];
+  __shared__ __align__(16) float ws[kDxE][kDxC];
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int t0 = blockIdx.x * kDxT, c0 = blockIdx.y * kDxC;
+  const bool vec = (d & 3) == 0;
+  f32x4_t acc[4][4];  // [token i][column group j]
 #pragma unroll
-  for (int tt = 0; tt < kDxTokens; ++tt) {
-    float a = 0.f;
-    if (tt < nt) {
-      const int t = t0 + tt;
-      if (dx_rows)
-        for (int j = 0; j < k; ++j) {
-          const int r = row_of[(size_t)t * k + j];
-          if (r >= 0) a += dx_rows[(size_t)r * d + c];
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + ty * 4 + i;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = c0 + 64 * j + tx * 4;
+      f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+      if (t < N && col < d) {
+        if (dx_rows)
+          for (int s = 0; s < k; ++s) {
+            const int r = row_of[(size_t)t * k + s];
+            if (r >= 0) a += load4(dx_rows + (size_t)r * d, col, d, vec);
+          }
+        if (dx_shared) a += load4(dx_shared + (size_t)t * d, col, d, vec);
+      }
+      acc[i][j] = a;
+    }
+  }
+  for (int pass = 0; pass < (dv ? 2 : 1); ++pass) {
+    const float* G = pass == 0 ? dl : dv;
+    const float* Wm = pass == 0 ? w_gate : w_noise;
+    for (int e0 = 0; e0 < E; e0 += kDxE) {
+      __syncthreads();  // the previous chunk is consumed
+      for (int i = tid; i < kDxE * kDxT; i += kThreads) {
+        const int tt = i / kDxE, ee = i - tt * kDxE;
+        const int t = t0 + tt, e = e0 + ee;
+        gs[ee][tt] = (t < N && e < E) ? G[(size_t)t * E + e] : 0.f;
+      }
+      for (int i = tid; i < kDxE * (kDxC / 4); i += kThreads) {
+        const int ee = i / (kDxC / 4), c4 = i - ee * (kDxC / 4);
+        const int e = e0 + ee;
+        *(f32x4_t*)&ws[ee][c4 * 4] =
+            e < E ? load4(Wm + (size_t)e * d, c0 + c4 * 4, d, vec) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+      __syncthreads();
+      const int ne = min(kDxE, E - e0);
+#pragma unroll 4
+      for (int ee = 0; ee < ne; ++ee) {
+        const f32x4_t g = *(const f32x4_t*)&gs[ee][ty * 4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4_t w = *(const f32x4_t*)&ws[ee][64 * j + tx * 4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(g[i], w[q], acc[i][j][q]);
         }
-      if (dx_shared) a += dx_shared[(size_t)t * d + c];
-    }
-    acc[tt] = a;
-  }
-  for (int e = 0; e < E4; e += 4) {
-    float w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = e + i < E ? w_gate[(size_t)(e + i) * d + c] : 0.f;
-#pragma unroll
-    for (int tt = 0; tt < kDxTokens; ++tt) {
-      const f32x4_t v = *(const f32x4_t*)&dls[tt][e];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[tt] = __builtin_fmaf(v[i], w[i], acc[tt]);
-    }
-  }
-  if (dv)
-    for (int e = 0; e < E4; e += 4) {
-      float w[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = e + i < E ? w_noise[(size_t)(e + i) * d + c] : 0.f;
-#pragma unroll
-      for (int tt = 0; tt < kDxTokens; ++tt) {
-        const f32x4_t v = *(const f32x4_t*)&dvs[tt][e];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[tt] = __builtin_fmaf(v[i], w[i], acc[tt]);
       }
     }
+  }
 #pragma unroll
-  for (int tt = 0; tt < kDxTokens; ++tt)
-    if (tt < nt) dx[(size_t)(t0 + tt) * d + c] = acc[tt];
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + ty * 4 + i;
+    if (t >= N) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = c0 + 64 * j + tx * 4;
+      float* out = dx + (size_t)t * d;
+      if (vec && col + 3 < d) {
+        *(f32x4_t*)(out + col) = acc[i][j];
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (col + q < d) out[col + q] = acc[i][j][q];
+      }
+    }
+  }
+}
+
+// Tokens per partial sum of a weight gradient: 256, halved (down to 128)
+// while the grid would have fewer than 2048 blocks.
+int wg_chunk_tokens(int N, int d, int E) {
+  const long long base = (long long)((d + 255) / 256) * ((E + 31) / 32);
+  int ch = 256;
+  while (ch > 128 && base * ((N + ch - 1) / ch) < 2048) ch >>= 1;
+  return ch;
 }
 
 // partial[chunk][e][c] = sum over the chunk's tokens (ascending) of
-// dl[t][e] x[t][c]; a block takes 256 columns x kWgExperts experts, with the
-// chunk's dl columns in LDS, so x is read once per expert group
-constexpr int kWgExperts = 32;
+// g[t][e] x[t][c]. A block takes 32 experts x 256 columns of one chunk; each
+// thread holds 4 experts x 8 columns (2 groups of 4, 128 apart). Tokens go
+// through LDS 32 at a time (g as [t][e], x converted to fp32 as [t][c]),
+// each group loaded into registers while the previous one is multiplied.
+constexpr int kWgE = 32, kWgC = 256, kWgT = 32;
 template <typename XT>
 __global__ __launch_bounds__(kThreads) void router_bwd_wg_partial_kernel(
-    int N, int d, int E, const float* __restrict__ dl, const XT* __restrict__ x,
-    float* __restrict__ partial) {
-  __shared__ __align__(16) float dls[kChunkTokens][kWgExperts];
-  const int c = blockIdx.x * kThreads + threadIdx.x;
-  const int e0 = blockIdx.y * kWgExperts, chunk = blockIdx.z;
-  const int t0 = chunk * kChunkTokens, t1 = min(N, t0 + kChunkTokens);
-  const int ne = min(kWgExperts, E - e0);
-  for (int i = threadIdx.x; i < kChunkTokens * kWgExperts; i += kThreads) {
-    const int tt = i / kWgExperts, ei = i - tt * kWgExperts;
-    dls[tt][ei] = (t0 + tt < t1 && ei < ne) ? dl[(size_t)(t0 + tt) * E + e0 + ei] : 0.f;
-  }
-  __syncthreads();
-  if (c >= d) return;
-  float acc[kWgExperts];
+    int N, int d, int E, int chunk_tokens, const float* __restrict__ gsrc,
+    const XT* __restrict__ x, float* __restrict__ partial) {
+  __shared__ __align__(16) float gs[kWgT][kWgE];
+  __shared__ __align__(16) float xs[kWgT][kWgC];
+  const int tid = threadIdx.x, eg = tid >> 5, cg = tid & 31;
+  const int c0 = blockIdx.x * kWgC, e0 = blockIdx.y * kWgE, chunk = blockIdx.z;
+  const int t0 = chunk * chunk_tokens, t1 = min(N, t0 + chunk_tokens);
+  // staging: 4 gradient values and 8 groups of 4 consecutive x values a thread
+  constexpr int GPT = kWgT * kWgE / kThreads, XPT = kWgT * (kWgC / 4) / kThreads;
+  const bool vec = (d & 3) == 0;
+  float gr[GPT];
+  f32x4_t xr[XPT];
+  auto fetch = [&](int ts) {
+    const int nt = min(kWgT, t1 - ts);
 #pragma unroll
-  for (int i = 0; i < kWgExperts; ++i) acc[i] = 0.f;
-  for (int t = t0; t < t1; ++t) {
-    float xv;
-    if constexpr (sizeof(XT) == 2) xv = moe::bf16_bits_to_f32(x[(size_t)t * d + c]);
-    else xv = x[(size_t)t * d + c];
+    for (int u = 0; u < GPT; ++u) {
+      const int i = tid + u * kThreads, tt = i / kWgE, ee = i - tt * kWgE;
+      const int e = e0 + ee;
+      gr[u] = (tt < nt && e < E) ? gsrc[(size_t)(ts + tt) * E + e] : 0.f;
+    }
 #pragma unroll
-    for (int i = 0; i < kWgExperts; i += 4) {
-      const f32x4_t v = *(const f32x4_t*)&dls[t - t0][i];
+    for (int u = 0; u < XPT; ++u) {
+      const int i = tid + u * kThreads, tt = i / (kWgC / 4), c4 = i - tt * (kWgC / 4);
+      const int c = c0 + c4 * 4;
+      f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+      if (tt < nt) {
+        const XT* row = x + (size_t)(ts + tt) * d;
+        if constexpr (sizeof(XT) == 2) {
+          if (vec && c + 3 < d) {
+            const u32x2_t b = *(const u32x2_t*)(row + c);
+            v = f32x4_t{moe::bf16_bits_to_f32((uint16_t)b[0]),
+                        moe::bf16_bits_to_f32((uint16_t)(b[0] >> 16)),
+                        moe::bf16_bits_to_f32((uint16_t)b[1]),
+                        moe::bf16_bits_to_f32((uint16_t)(b[1] >> 16))};
+          } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[i + q] = __builtin_fmaf(v[q], xv, acc[i + q]);
+            for (int q = 0; q < 4; ++q)
+              if (c + q < d) v[q] = moe::bf16_bits_to_f32(row[c + q]);
+          }
+        } else {
+          v = load4(row, c, d, vec);
+        }
+      }
+      xr[u] = v;
+    }
+  };
+  f32x4_t acc[4][2];  // [expert i][column group h]
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) acc[i][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (t0 < t1) fetch(t0);
+  for (int ts = t0; ts < t1; ts += kWgT) {
+    const int nt = min(kWgT, t1 - ts);
+    __syncthreads();  // the previous tokens are consumed
+#pragma unroll
+    for (int u = 0; u < GPT; ++u) {
+      const int i = tid + u * kThreads, tt = i / kWgE, ee = i - tt * kWgE;
+      gs[tt][ee] = gr[u];
+    }
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+      const int i = tid + u * kThreads, tt = i / (kWgC / 4), c4 = i - tt * (kWgC / 4);
+      *(f32x4_t*)&xs[tt][c4 * 4] = xr[u];
+    }
+    __syncthreads();
+    if (ts + kWgT < t1) fetch(ts + kWgT);
+    for (int tt = 0; tt < nt; ++tt) {
+      const f32x4_t g = *(const f32x4_t*)&gs[tt][eg * 4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const f32x4_t xv = *(const f32x4_t*)&xs[tt][128 * h + cg * 4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[i][h][q] = __builtin_fmaf(g[i], xv[q], acc[i][h][q]);
+      }
     }
   }
-  for (int i = 0; i < ne; ++i) partial[((size_t)chunk * E + e0 + i) * d + c] = acc[i];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = e0 + eg * 4 + i;
+    if (e >= E) continue;
+    float* out = partial + ((size_t)chunk * E + e) * d;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = c0 + 128 * h + cg * 4;
+      if (vec && c + 3 < d) {
+        *(f32x4_t*)(out + c) = acc[i][h];
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (c + q < d) out[c + q] = acc[i][h][q];
+      }
+    }
+  }
 }
 
 // dW_g[e][c] = sum of the partials in chunk order
@@ -205,6 +318,7 @@ __global__ __launch_bounds__(kThreads) void router_bwd_wg_reduce_kernel(
   const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
   if (i >= (size_t)E * d) return;
   float acc = 0.f;
+#pragma unroll 8
   for (int ch = 0; ch < chunks; ++ch) acc += partial[(size_t)ch * E * d + i];
   dw[i] = acc;
 }
@@ -233,7 +347,8 @@ namespace moe_host {
 
 // workspace: dW partials [chunks][E][d] | dv [N][E]
 size_t router_backward_workspace_bytes(int N, int d, int E) {
-  const int chunks = (N + kChunkTokens - 1) / kChunkTokens;
+  const int ch = wg_chunk_tokens(N, d, E);
+  const int chunks = (N + ch - 1) / ch;
   return align256((size_t)chunks * E * d * 4) + align256((size_t)N * E * 4);
 }
 
@@ -246,7 +361,8 @@ moe_status router_backward_launch(int N, int d, int E, int k, int C, int renorma
                                   const float* w_noise, const float* noise_v, uint64_t seed,
                                   float* dlogits, float* dw_gate, float* dlogit_bias,
                                   float* dw_noise, float* dx, void* workspace, hipStream_t st) {
-  const int chunks = (N + kChunkTokens - 1) / kChunkTokens;
+  const int ch = wg_chunk_tokens(N, d, E);
+  const int chunks = (N + ch - 1) / ch;
   float* partial = (float*)workspace;
   float* dv = w_noise ? (float*)((char*)workspace + align256((size_t)chunks * E * d * 4)) : nullptr;
   const int per_block = kThreads / 64;
@@ -255,7 +371,7 @@ moe_status router_backward_launch(int N, int d, int E, int k, int C, int renorma
       beta, dlogits, w_noise ? noise_v : nullptr, seed, dv);
   moe_status s = launch_status("router backward (scores)");
   if (s != MOE_OK) return s;
-  dim3 gdx((N + kDxTokens - 1) / kDxTokens, (d + kThreads - 1) / kThreads);
+  dim3 gdx((N + kDxT - 1) / kDxT, (d + kDxC - 1) / kDxC);
   router_bwd_dx_kernel<<<gdx, kThreads, 0, st>>>(N, d, E, k, dlogits, w_gate, row_of, dx_rows,
                                                  dx_shared, dv, w_noise, dx);
   s = launch_status("router backward (dx)");
@@ -264,13 +380,13 @@ moe_status router_backward_launch(int N, int d, int E, int k, int C, int renorma
   for (int pass = 0; pass < (w_noise ? 2 : 1); ++pass) {
     const float* gsrc = pass == 0 ? dlogits : dv;
     float* out = pass == 0 ? dw_gate : dw_noise;
-    dim3 grid((d + kThreads - 1) / kThreads, (E + kWgExperts - 1) / kWgExperts, chunks);
+    dim3 grid((d + kWgC - 1) / kWgC, (E + kWgE - 1) / kWgE, chunks);
     if (x_dt == MOE_BF16)
       router_bwd_wg_partial_kernel<uint16_t><<<grid, kThreads, 0, st>>>(
-          N, d, E, gsrc, (const uint16_t*)x, partial);
+          N, d, E, ch, gsrc, (const uint16_t*)x, partial);
     else
-      router_bwd_wg_partial_kernel<float><<<grid, kThreads, 0, st>>>(N, d, E, gsrc,
-                                                                     (const float*)x, partial);
+      router_bwd_wg_partial_kernel<float><<<grid, kThreads, 0, st>>>(
+          N, d, E, ch, gsrc, (const float*)x, partial);
     s = launch_status("router backward (weight gradient partials)");
     if (s != MOE_OK) return s;
     router_bwd_wg_reduce_kernel<<<(int)(((size_t)E * d + kThreads - 1) / kThreads), kThreads, 0,
