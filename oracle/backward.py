@@ -31,6 +31,13 @@ order the forward runs backwards:
   softmax -> logits, + z-loss term on the logits
   (noise: logits of the softmax -> raw logits and W_noise)
   router GEMM -> W_g, logit bias and the token rows.
+
+Expert choice (heavensheep "Routing Function"; CS336 notes section 3: the
+experts select tokens): the selections of every expert are held fixed, a
+chosen (token, expert) pair's gate is the score s_te itself, so the gate
+gradient is the score gradient of that pair; f_e = capacity / (N k) is the
+same for every expert, and the auxiliary term then adds the same amount to
+every score of a token, which the softmax Jacobian removes.
 """
 from __future__ import annotations
 
@@ -117,7 +124,8 @@ def layer_backward(cfg, x, x_dt, w_gate, experts, fwd, dy, alpha=0.0, beta=0.0,
     da, du): its rows' token and slot indices and fp64 intermediates (and
     `shared_terms` for the shared expert, every token with gate 1)."""
     if getattr(cfg, "expert_choice", False):
-        raise ValueError("the backward oracle covers token-choice routing")
+        return _expert_choice_backward(cfg, x, x_dt, w_gate, experts, fwd, dy, alpha, beta,
+                                       shared, logit_bias, w_noise, keep_terms)
     X = decode_rows(x, x_dt)
     N, d = X.shape
     E, k = cfg.n_experts, cfg.top_k
@@ -155,21 +163,71 @@ def layer_backward(cfg, x, x_dt, w_gate, experts, fwd, dy, alpha=0.0, beta=0.0,
     if keep_terms:
         out["terms"] = terms
 
-    # ---- shared expert: gate 1 on every token
     if shared is not None:
-        w = shared.get(0)
-        g = expert_backward(X, dy, cfg.act, decode_weight(w["w1"], cfg.w_dtype),
-                            decode_weight(w["w3"], cfg.w_dtype),
-                            decode_weight(w["w2"], cfg.w_dtype))
-        dX += g["dX"]
-        for n in ("dW1", "dW3", "dW2"):
-            out["shared_" + n] = g[n]
-        if keep_terms:
-            w1s, w3s, w2s = (decode_weight(w[n], cfg.w_dtype) for n in ("w1", "w3", "w2"))
-            out["shared_terms"] = dict(tokens=np.arange(N), X=X, dO=dy, w1=w1s, w3=w3s, w2=w2s,
-                                       **{n: g[n] for n in ("a", "u", "h", "dh", "da", "du")})
+        dX += _shared_backward(cfg, X, dy, shared, out, keep_terms)
 
     rb = router_backward(cfg, X, w_gate, fwd, dg, alpha, beta, logit_bias, w_noise)
+    dX += rb.pop("dx")
+    out.update(rb)
+    out["dx"] = dX
+    out["dg"] = dg
+    return out
+
+
+def _shared_backward(cfg, X, dy, shared, out, keep_terms):
+    """The shared expert (gate 1 on every token): stores its weight
+    gradients (and terms) in out, returns its token-row gradient."""
+    w = shared.get(0)
+    w1s, w3s, w2s = (decode_weight(w[n], cfg.w_dtype) for n in ("w1", "w3", "w2"))
+    g = expert_backward(X, dy, cfg.act, w1s, w3s, w2s)
+    for n in ("dW1", "dW3", "dW2"):
+        out["shared_" + n] = g[n]
+    if keep_terms:
+        out["shared_terms"] = dict(tokens=np.arange(X.shape[0]), X=X, dO=dy, w1=w1s, w3=w3s,
+                                   w2=w2s, **{n: g[n] for n in ("a", "u", "h", "dh", "da", "du")})
+    return g["dX"]
+
+
+def _expert_choice_backward(cfg, x, x_dt, w_gate, experts, fwd, dy, alpha, beta, shared,
+                            logit_bias, w_noise, keep_terms):
+    """layer_backward for expert-choice routing (see the module docstring).
+    fwd["ec"] holds row_of and gates [N][E] of the chosen pairs; dg is then
+    [N][E] (0 where expert e did not choose token t) and the terms' slots
+    are expert indices."""
+    X = decode_rows(x, x_dt)
+    N, d = X.shape
+    E = cfg.n_experts
+    dy = np.asarray(dy, np.float64)
+    ec = fwd["ec"]
+    row_of, gates = ec["row_of"], ec["gates"]
+    kept = row_of >= 0
+    dg = np.where(kept, np.einsum("td,ted->te", dy, fwd["Yexp"]), 0.0)
+    dX = np.zeros((N, d))
+    grads = {n: [] for n in ("dW1", "dW3", "dW2", "db1", "db2")}
+    terms = []
+    for e in range(E):
+        tt = np.nonzero(kept[:, e])[0]  # an expert's rows list its tokens in token order
+        w = experts.get(e)
+        w1, w3, w2 = (decode_weight(w[n], cfg.w_dtype) for n in ("w1", "w3", "w2"))
+        b1 = None if w["b1"] is None else np.asarray(w["b1"], np.float64)
+        b2 = None if w["b2"] is None else np.asarray(w["b2"], np.float64)
+        dO = gates[tt, e].astype(np.float64)[:, None] * dy[tt]
+        g = expert_backward(X[tt], dO, cfg.act, w1, w3, w2, b1, b2)
+        np.add.at(dX, tt, g["dX"])
+        for n in grads:
+            grads[n].append(g[n])
+        if keep_terms:
+            terms.append(dict(tokens=tt, slots=np.full(len(tt), e), X=X[tt], dO=dO, w1=w1,
+                              w3=w3, w2=w2, **{n: g[n] for n in ("a", "u", "h", "dh", "da", "du")}))
+    out = {n: (None if grads[n][0] is None else np.stack(grads[n])) for n in grads}
+    if keep_terms:
+        out["terms"] = terms
+    if shared is not None:
+        dX += _shared_backward(cfg, X, dy, shared, out, keep_terms)
+    # gate of a chosen pair = s_te: dL/ds_te = dg_te
+    f = np.full(E, ec["capacity"] / (N * cfg.top_k))
+    rb = _logits_backward(cfg, X, w_gate, fwd["route"], dg.copy(), f, alpha, beta, logit_bias,
+                          w_noise, np.arange(N), N)
     dX += rb.pop("dx")
     out.update(rb)
     out["dx"] = dX
@@ -233,9 +291,19 @@ def router_backward(cfg, X, w_gate, fwd, dg, alpha=0.0, beta=0.0, logit_bias=Non
         # Switch gate: g = s of the expert actually used (after a reroute)
         for j in range(k):
             np.add.at(ds, (np.arange(n), np.maximum(exp_of[:, j], 0)), dg[:, j])
-    # auxiliary loss: d(alpha E sum_e f_e P_e)/ds_te = alpha E f_e / N
     f = dsp["counts_routed"].astype(np.float64) / (N * k)
-    ds += alpha * E * f[None, :] / N
+    return _logits_backward(cfg, X, w_gate, r, ds, f, alpha, beta, logit_bias, w_noise, rows, N)
+
+
+def _logits_backward(cfg, X, w_gate, r, ds, f, alpha, beta, logit_bias, w_noise, rows, N):
+    """From score gradients ds [n][E] (the tokens `rows` of a batch of N):
+    + the auxiliary-loss term (f_e the routed fractions), softmax -> logits,
+    + z-loss, (noise), router GEMM. Returns dict(ds, dl, dw_gate,
+    dlogit_bias, dw_noise, dx)."""
+    E = cfg.n_experts
+    s = r["s"][rows].astype(np.float64)
+    # auxiliary loss: d(alpha E sum_e f_e P_e)/ds_te = alpha E f_e / N
+    ds = ds + alpha * E * np.asarray(f, np.float64)[None, :] / N
 
     # softmax -> logits (+ z-loss: d(lse_t^2 / N)/dl_te = 2 lse_t s_te / N)
     dl = s * (ds - (s * ds).sum(axis=1, keepdims=True))

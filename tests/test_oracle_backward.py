@@ -14,11 +14,11 @@ from oracle import backward as B
 
 
 def _tiny(act=W.ACT_SWIGLU, w_dt=W.F32, renorm=True, k=2, E=4, overflow=W.DROPLESS, cf=None,
-          noise=False, N=24, d=16, F=12, seed=7, shared=False):
+          noise=False, N=24, d=16, F=12, seed=7, shared=False, ec=False):
     cfg = W.C2.with_(name="bwd_tiny", n_tokens=N, d_model=d, n_experts=E, d_ff=F, top_k=k,
                      act=act, w_dtype=w_dt, x_dtype=W.F32 if w_dt == W.F32 else W.BF16,
-                     renormalize=renorm, overflow=overflow, capacity_factor=cf, seed=seed,
-                     noise_seed=44 if noise else 0)
+                     renormalize=renorm and not ec, overflow=overflow, capacity_factor=cf,
+                     seed=seed, noise_seed=44 if noise else 0, expert_choice=ec)
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((N, d)).astype(np.float32)
     w = dict(w1=(rng.standard_normal((E, F, d)) / np.sqrt(d)).astype(np.float32),
@@ -57,18 +57,30 @@ def _autograd(cfg, x, w, wg, lb, wn, fwd, dy, alpha, beta):
         l = l + z * torch.nn.functional.softplus(X @ Wn.T)
     s = torch.softmax(l, dim=1)
     lse = torch.logsumexp(l, dim=1)
-    r, dsp = fwd["route"], fwd["dispatch"]
-    cand = torch.tensor(r["cand_ids"][:, :k].astype(np.int64))
-    exp_of = dsp["expert_of"]
-    row_of = dsp["row_of"]
-    if cfg.renormalize:
-        sel = torch.gather(s, 1, cand)
-        g = sel / sel.sum(dim=1, keepdim=True)
+    r = fwd["route"]
+    if cfg.expert_choice:
+        # every expert's chosen tokens fixed; a chosen pair's gate is s_te
+        ec = fwd["ec"]
+        row_of = ec["row_of"]
+        exp_of = np.tile(np.arange(E, dtype=np.int64), (N, 1))
+        g = s
+        counts = np.full(E, ec["capacity"])
+        slots = E
     else:
-        g = torch.gather(s, 1, torch.tensor(np.maximum(exp_of, 0).astype(np.int64)))
+        dsp = fwd["dispatch"]
+        cand = torch.tensor(r["cand_ids"][:, :k].astype(np.int64))
+        exp_of = dsp["expert_of"]
+        row_of = dsp["row_of"]
+        if cfg.renormalize:
+            sel = torch.gather(s, 1, cand)
+            g = sel / sel.sum(dim=1, keepdim=True)
+        else:
+            g = torch.gather(s, 1, torch.tensor(np.maximum(exp_of, 0).astype(np.int64)))
+        counts = dsp["counts_routed"]
+        slots = k
     y = torch.zeros((N, cfg.d_model), dtype=torch.float64)
     for t in range(N):
-        for j in range(k):
+        for j in range(slots):
             if row_of[t, j] < 0:
                 continue
             e = int(exp_of[t, j])
@@ -84,7 +96,7 @@ def _autograd(cfg, x, w, wg, lb, wn, fwd, dy, alpha, beta):
     if "shared" in w:
         S1, S3, S2 = (T(w["shared"][n][0]) for n in ("w1", "w3", "w2"))
         y = y + (torch.nn.functional.silu(X @ S1.T) * (X @ S3.T)) @ S2.T
-    f = torch.tensor(dsp["counts_routed"].astype(np.float64) / (N * k))
+    f = torch.tensor(counts.astype(np.float64) / (N * k))
     aux = E * (f * s.mean(dim=0)).sum()
     zl = (lse ** 2).mean()
     L = (torch.tensor(dy) * y).sum() + alpha * aux + beta * zl
@@ -134,6 +146,28 @@ def test_backward_matches_autograd(case):
         # the oracle's softmax scores are the fp32 values of the forward,
         # torch's are fp64: agreement to a few fp32 ulps
         assert _rel(got[n], v) < 2e-6, (n, _rel(got[n], v))
+
+
+@pytest.mark.parametrize("case", ["swiglu_shared", "relu_bias_logit_bias", "gelu_noise"])
+def test_expert_choice_backward_matches_autograd(case):
+    """Expert-choice routing: the experts' selections held fixed, a chosen
+    pair's gate is its score."""
+    kw = dict(swiglu_shared=dict(shared=True), relu_bias_logit_bias=dict(act=W.ACT_RELU),
+              gelu_noise=dict(act=W.ACT_GELU, noise=True))[case]
+    cfg, x, w, wg, lb, wn, dy = _tiny(ec=True, E=5, k=2, N=30, **kw)
+    alpha, beta = 0.3, 0.05
+    fwd, got = _run(cfg, x, w, wg, lb, wn, dy, alpha, beta)
+    row_of = fwd["ec"]["row_of"]
+    assert ((row_of >= 0).sum(axis=0) == fwd["ec"]["capacity"]).all()
+    assert ((row_of >= 0).sum(axis=1) != cfg.top_k).any()  # tokens get uneven expert counts
+    ref = _autograd(cfg, x, w, wg, lb, wn, fwd, dy, alpha, beta)
+    for n, v in ref.items():
+        assert _rel(got[n], v) < 2e-6, (n, _rel(got[n], v))
+    # the auxiliary term is the same for every score of a token (f_e is
+    # uniform), so the logit gradients do not depend on alpha -- up to the
+    # fp32 scores summing to 1 within ~1e-7
+    _, got0 = _run(cfg, x, w, wg, lb, wn, dy, 0.0, beta)
+    assert _rel(got0["dl"], got["dl"]) < 1e-8
 
 
 def test_expert_backward_matches_finite_differences():
