@@ -361,7 +361,8 @@ def bench_backward(args):
             e[1].record(stream)
         b = layer._bwd
         sh = layer.shared is not None
-        moe.moe_combine_backward(dy, layer.y_rows, layer.row_of, layer.gates, b[0]["d_rows"],
+        gates, cand, expert_of, routed, k, renorm = moe._routing_for_backward(layer)
+        moe.moe_combine_backward(dy, layer.y_rows, layer.row_of, gates, b[0]["d_rows"],
                                  b[0]["dgates"], d_shared=b[0]["d_shared"] if sh else None)
         if e is not None:
             e[2].record(stream)
@@ -376,10 +377,10 @@ def bench_backward(args):
                                          b[0]["shared_dw2"], max_rows=cfg.n_tokens, ws=b[1])
         if e is not None:
             e[3].record(stream)
-        moe.moe_router_backward(x, dev["w_gate"], layer.logits, layer.cand_ids, layer.expert_of,
-                                layer.row_of, b[0]["dgates"], layer.counts_routed,
+        moe.moe_router_backward(x, dev["w_gate"], layer.logits, cand, expert_of,
+                                layer.row_of, b[0]["dgates"], routed,
                                 b[0]["dlogits"], b[0]["dw_gate"], b[0]["dx"],
-                                top_k=cfg.top_k, renormalize=cfg.renormalize, alpha=alpha,
+                                top_k=k, renormalize=renorm, alpha=alpha,
                                 beta=beta, dx_rows=b[0]["dx_rows"],
                                 dx_shared=b[0]["dx_shared"] if sh else None,
                                 dlogit_bias=b[0]["dlogit_bias"], w_noise=dev.get("w_noise"),

@@ -419,8 +419,6 @@ class MoELayer:
         # training: the experts' forward keeps its pre-activations and h
         self.train = bool(train)
         if self.train:
-            if self.ec:
-                raise ValueError("the backward pass covers token-choice routing")
             if s.h_fp32:
                 raise ValueError("training keeps h in bf16 (build the spec with h_fp32=False)")
             bf = dict(dtype=torch.bfloat16, device=dev)
@@ -429,6 +427,9 @@ class MoELayer:
             self.noise_v = (torch.empty((N, E), **f32) if weights.get("w_noise") is not None
                             else None)
             self.h = torch.empty((R, s.d_ff), **bf)
+            # expert choice: slot j of a token is expert j in the backward's router step
+            self.ec_expert_of = (torch.arange(E, **i32).repeat(N, 1).contiguous()
+                                 if self.ec else None)
             if self.shared is not None:
                 self.preact_sh = torch.empty((N, (2 if glu else 1) * s.shared_d_ff), **bf)
                 self.h_sh = torch.empty((N, s.shared_d_ff), **bf)
@@ -537,7 +538,8 @@ def _backward_buffers(layer, dw_dtype=torch.float32):
     f32 = dict(dtype=torch.float32, device=dev)
     wdt = dict(dtype=dw_dtype, device=dev)
     b = dict(d_rows=torch.empty((R, d), dtype=torch.bfloat16, device=dev),
-             dgates=torch.empty((N, s.top_k), **f32), dx_rows=torch.empty((R, d), **f32),
+             dgates=torch.empty((N, E if layer.ec else s.top_k), **f32),
+             dx_rows=torch.empty((R, d), **f32),
              dw1=torch.empty((E, F, d), **wdt),
              dw3=torch.empty((E, F, d), **wdt) if s.act == SWIGLU else None,
              dw2=torch.empty((E, d, F), **wdt), dlogits=torch.empty((N, E), **f32),
@@ -559,14 +561,29 @@ def _backward_buffers(layer, dw_dtype=torch.float32):
     return b, ws_f, ws_r
 
 
+def _routing_for_backward(layer):
+    """(gates, candidate ids, expert of each slot, routed counts, slots per
+    token, renormalised) as the backward's combine and router steps see the
+    forward's routing. Expert choice: a token's slots are all E experts
+    (slot j = expert j, kept where expert j chose the token), its gates the
+    chosen scores, not renormalised, and every expert routed its capacity."""
+    s = layer.spec
+    if layer.ec:
+        return (layer.ec_gates, layer.ec_expert_of, layer.ec_expert_of, layer.counts_kept,
+                s.n_experts, False)
+    return (layer.gates, layer.cand_ids, layer.expert_of, layer.counts_routed, s.top_k,
+            s.renormalize)
+
+
 def layer_backward(layer, x, dy, alpha=0.0, beta=0.0, dw_dtype=torch.float32, stream=None):
     """Backward of the last `layer.forward` (the layer built with train=True):
     L = <dy, y> + alpha * Switch aux + beta * z-loss. Returns a dict of fp32
     device tensors: dx, dw_gate, dlogit_bias (or None), dw_noise (or None),
     dw1, dw3 (None unless SwiGLU), dw2,
-    dlogits, dgates, and with a shared expert shared_dw1/3/2 [1][...] (buffers
-    reused by the next call). dw_dtype: float32, or bfloat16 for the expert
-    weight gradients."""
+    dlogits, dgates ([N][top_k], or [N][E] with expert choice: the gradient
+    of each chosen pair's gate, 0 elsewhere), and with a shared expert
+    shared_dw1/3/2 [1][...] (buffers reused by the next call). dw_dtype:
+    float32, or bfloat16 for the expert weight gradients."""
     if not layer.train:
         raise ValueError("build the layer with train=True to run its backward pass")
     if not layer._forward_done:
@@ -577,7 +594,8 @@ def layer_backward(layer, x, dy, alpha=0.0, beta=0.0, dw_dtype=torch.float32, st
     b, ws_f, ws_r = layer._bwd
     s, w = layer.spec, layer.w
     sh = layer.shared is not None
-    moe_combine_backward(dy, layer.y_rows, layer.row_of, layer.gates, b["d_rows"], b["dgates"],
+    gates, cand, expert_of, routed, k, renorm = _routing_for_backward(layer)
+    moe_combine_backward(dy, layer.y_rows, layer.row_of, gates, b["d_rows"], b["dgates"],
                          d_shared=b["d_shared"] if sh else None, stream=stream)
     rows, index = layer._packed_rows(x)
     moe_grouped_ffn_backward(layer.ffn, rows, layer.offsets, layer.preact, layer.h, b["d_rows"],
@@ -589,10 +607,9 @@ def layer_backward(layer, x, dy, alpha=0.0, beta=0.0, dw_dtype=torch.float32, st
                                  b["d_shared"], b["dx_shared"], b["shared_dw1"],
                                  b["shared_dw3"], b["shared_dw2"], max_rows=s.n_tokens, ws=ws_f,
                                  stream=stream)
-    moe_router_backward(x, w["w_gate"], layer.logits, layer.cand_ids, layer.expert_of,
-                        layer.row_of, b["dgates"], layer.counts_routed, b["dlogits"],
-                        b["dw_gate"], b["dx"], top_k=s.top_k, renormalize=s.renormalize,
-                        alpha=alpha, beta=beta, dx_rows=b["dx_rows"],
+    moe_router_backward(x, w["w_gate"], layer.logits, cand, expert_of, layer.row_of,
+                        b["dgates"], routed, b["dlogits"], b["dw_gate"], b["dx"], top_k=k,
+                        renormalize=renorm, alpha=alpha, beta=beta, dx_rows=b["dx_rows"],
                         dx_shared=b["dx_shared"] if sh else None,
                         dlogit_bias=b["dlogit_bias"], w_noise=w.get("w_noise"),
                         noise_seed=s.noise_seed, noise_v=layer.noise_v, dw_noise=b["dw_noise"],

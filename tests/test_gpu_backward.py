@@ -142,6 +142,64 @@ def test_layer_backward_matches_oracle(moe, key):
     _check_router_statistical(g, ref, fwd, dy.numpy().astype(np.float64), host, cfg)
 
 
+EC_CASES = {
+    # Mixtral-shaped experts, every expert takes its 150 top tokens (N 600, E 8)
+    "expert_choice_reduced": W.REDUCED["c6"],
+    # 64 fine-grained experts taking 40 tokens each, plus a shared expert
+    "deepseek_expert_choice_reduced": W.REDUCED["c3"].with_(
+        name="deepseek_expert_choice_reduced", expert_choice=True, select_bias=False),
+}
+
+
+def _ec_view(cfg, fwd):
+    """Expert choice seen as E slots per token (slot j = expert j, kept where
+    expert j chose the token, gate = its score, not renormalised): the form
+    the error bounds below take their slots and routing from."""
+    ec = fwd["ec"]
+    N, E = ec["row_of"].shape
+    disp = dict(row_of=ec["row_of"], expert_of=np.tile(np.arange(E, dtype=np.int32), (N, 1)),
+                gates=ec["gates"], counts_routed=np.full(E, ec["capacity"], np.int32),
+                offsets=ec["offsets"])
+    return cfg.with_(top_k=E, renormalize=False, expert_choice=False), dict(fwd, dispatch=disp)
+
+
+@pytest.mark.parametrize("key", list(EC_CASES))
+def test_expert_choice_layer_backward_matches_oracle(moe, key):
+    cfg = EC_CASES[key]
+    print("expert-choice backward", key, cfg, flush=True)
+    inp = W.make_inputs(cfg, "cpu")
+    host = host_inputs(inp)
+    experts = experts_of(host)
+    shared = experts_of(host, "shared_") if cfg.shared_d_ff else None
+    fwd = oracle.layer_forward(cfg, host["x"], cfg.x_dtype, host["w_gate"], experts, shared,
+                               host["logit_bias"], host["select_bias"], host["w_noise"])
+    dy = _dy(cfg)
+    ref = OB.layer_backward(cfg, host["x"], cfg.x_dtype, host["w_gate"], experts, fwd,
+                            dy.numpy().astype(np.float64), ALPHA, BETA, shared=shared,
+                            logit_bias=host["logit_bias"], w_noise=host["w_noise"],
+                            keep_terms=True)
+    dev = to_device(inp)
+    spec = moe.spec_from_config(cfg)
+    spec.h_fp32 = False
+    layer = moe.MoELayer(spec, dev, x_dtype=torch.bfloat16, train=True)
+    layer_eval = moe.MoELayer(spec, dev, x_dtype=torch.bfloat16)
+    logits = torch.from_numpy(fwd["logits"]).cuda()
+    y = layer.forward(dev["x"], logits_in=logits).clone()
+    y_eval = layer_eval.forward(dev["x"], logits_in=logits)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_eval)
+    ec = fwd["ec"]
+    for name in ("row_of", "offsets", "perm_token"):
+        assert np.array_equal(to_np(getattr(layer, name)), ec[name]), name
+    assert np.array_equal(to_np(layer.ec_gates).view(np.uint32), ec["gates"].view(np.uint32))
+    g = moe.layer_backward(layer, dev["x"], dy.cuda(), ALPHA, BETA)
+    torch.cuda.synchronize()
+    assert np.all(to_np(g["dgates"])[ec["row_of"] < 0] == 0.0)
+    cfg_v, fwd_v = _ec_view(cfg, fwd)
+    _check_bounds(g, ref, fwd_v, dy.numpy().astype(np.float64), host, cfg_v)
+    _check_router_statistical(g, ref, fwd_v, dy.numpy().astype(np.float64), host, cfg_v)
+
+
 def _first_order_terms(T, act):
     """First-order rounding-error terms (in units of u) of da and du per row
     and feature (du's None without SwiGLU): the roundings of a (and u), of
