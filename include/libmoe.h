@@ -305,9 +305,14 @@ moe_status moe_balance_stats(int32_t n_tokens, int32_t n_experts, int32_t top_k,
  * routing path. Order of the calls: moe_combine_backward ->
  * moe_grouped_ffn_backward (routed experts, and the shared expert if any) ->
  * moe_router_backward. Scope: token-choice routing (with or without noisy
- * gating, capacity and reroute); bf16 SwiGLU, ReLU or
+ * gating, capacity and reroute) and expert choice; bf16 SwiGLU, ReLU or
  * GELU experts without biases (h kept in bf16); d_model and d_ff multiples
- * of 256.
+ * of 256. Expert choice runs as E slots per token: row_of [N][E] and the
+ * gates [N][E] of moe_expert_choice go to moe_combine_backward with
+ * top_k = E, and moe_router_backward takes top_k = n_cand = E,
+ * renormalize = 0, cand_ids = expert_of = [N][E] with column j holding j
+ * (slot j is expert j; a chosen pair's gate is its score) and
+ * counts_routed = the capacity of every expert.
  * Gradients come out in fp32 (expert weight gradients optionally bf16) and
  * overwrite their buffers (no accumulation). */
 
