@@ -13,7 +13,9 @@ Prints one JSON line. The default workload is the Mixtral-shaped prefill
 roofline: the grouped expert FFN (moe_grouped_ffn: tile table + GEMM 1
 gate/up with fused SwiGLU + GEMM 2 down) is the dominant kernel group; its
 duration is measured with HIP events on the launch stream inside the timed
-region. cpu_baseline: the CPU oracle (fp64 FFNs) timed on a bounded sample of
+region. graph_replay: the same step replayed as one HIP graph (reported
+beside the eager figure, which stays the metric). cpu_baseline: the CPU
+oracle (fp64 FFNs) timed on a bounded sample of
 the same workload on this host's cores (for the tiny Switch layer also on one
 pinned core, in a child process). clocks: GFX and memory clocks and socket
 power read with amd-smi while the same step runs back to back, after the
@@ -620,6 +622,23 @@ def main():
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = 4 * n
         del a, b
+    # the same step as one HIP graph replay (every kernel of the layer in one
+    # launch): reported beside the eager figure, which stays the metric
+    try:
+        g = layer.capture(x)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        gms = (time.perf_counter() - t0) * 1e3 / args.steps
+        out["graph_replay"] = {"ms_per_step": round(gms, 4),
+                               "tokens_per_s": round(cfg.n_tokens / (gms * 1e-3), 1),
+                               "steps": args.steps}
+        del g
+    except Exception as e:  # reported, never fatal to the measurement
+        out["graph_replay"] = {"error": repr(e)[:300]}
     if not args.no_clocks:
         out["clocks"] = sample_clocks(lambda: layer.forward(x))
     if not args.no_cpu_baseline:

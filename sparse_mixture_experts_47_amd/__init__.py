@@ -519,6 +519,24 @@ class MoELayer:
                           select_bias=self.w.get("select_bias") if update_bias else None,
                           bias_rate=s.bias_rate, stream=stream)
 
+    def capture(self, x, stats=True):
+        """A HIP graph of one whole forward on x (torch.cuda.CUDAGraph): one
+        replay relaunches every kernel of the layer (router, dispatch,
+        grouped FFN, shared expert on its side stream, combine, statistics)
+        with a single call, for launch-bound small batches. The graph reads x
+        and writes self.y (and the other buffers) in place; the library
+        makes no allocation, memset or host synchronisation inside a forward,
+        so the captured work is exactly the eager one."""
+        warm = torch.cuda.Stream(device=self.dev)
+        warm.wait_stream(torch.cuda.current_stream(self.dev))
+        with torch.cuda.stream(warm):
+            self.forward(x, stats=stats)  # first launches set kernel attributes
+        torch.cuda.current_stream(self.dev).wait_stream(warm)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.forward(x, stats=stats)
+        return g
+
     def forward(self, x, logits_in=None, stats=True, update_bias=False, stream=None,
                 noise_in=None):
         self.start_shared(x, stream)
