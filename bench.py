@@ -58,6 +58,8 @@ def parse():
                     help="time a training step (forward + backward) instead of the forward")
     ap.add_argument("--dw-bf16", action="store_true",
                     help="with --backward: expert weight gradients in bf16 instead of fp32")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay of the step after the timed region")
     ap.add_argument("--no-clocks", action="store_true",
                     help="skip the amd-smi clock and power sample after the timed region")
     ap.add_argument("--oracle-single-core", action="store_true",
@@ -625,6 +627,8 @@ def main():
     # the same step as one HIP graph replay (every kernel of the layer in one
     # launch): reported beside the eager figure, which stays the metric
     try:
+        if args.no_graph:
+            raise RuntimeError("skipped (--no-graph)")
         g = layer.capture(x)
         g.replay()
         torch.cuda.synchronize()
