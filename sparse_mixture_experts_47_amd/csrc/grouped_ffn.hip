@@ -144,21 +144,44 @@ __global__ __launch_bounds__(256) void ggemm_f32_kernel(GemmArgs g) {
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[b][i][j] = 0.f;
+  // Each thread stages 4 consecutive K values of one A row and of one B row
+  // per plane (BM x BK = BN x BK = 4 x 256), loaded one K step ahead into
+  // registers; rows past the tile and K past the end load zeros.
+  static_assert(BM * BK == 4 * 256 && BN * BK == 4 * 256, "one 4-vector per thread");
+  const int lm = tid >> 2, lk = (tid & 3) * 4;
+  const bool vec = (K & 3) == 0;
+  const int arow_l = row0 + lm;
+  const float* arow_p =
+      arow_l < row_end ? A + (size_t)(g.a_rows ? g.a_rows[arow_l] : arow_l) * K : nullptr;
+  const float* brow_p[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    brow_p[b] = n0 + lm < Nout ? Bp[b] + (size_t)(n0 + lm) * K : nullptr;
+  auto load4 = [&](const float* row, int k) {
+    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+    if (!row) return v;
+    if (vec && k + 3 < K) return *(const f32x4_t*)(row + k);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (k + q < K) v[q] = row[k + q];
+    return v;
+  };
+  f32x4_t ar = load4(arow_p, lk), br[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) br[b] = load4(brow_p[b], lk);
   for (int k0 = 0; k0 < K; k0 += BK) {
-    for (int i = tid; i < BM * BK; i += 256) {
-      const int m = i / BK, kk = i % BK;
-      const int row = row0 + m, k = k0 + kk;
-      const int arow = (row < row_end && g.a_rows) ? g.a_rows[row] : row;
-      As[kk][m] = (row < row_end && k < K) ? A[(size_t)arow * K + k] : 0.f;
-    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) As[lk + q][lm] = ar[q];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
-      for (int i = tid; i < BN * BK; i += 256) {
-        const int n = i / BK, kk = i % BK;
-        const int col = n0 + n, k = k0 + kk;
-        Bs[b][kk][n] = (col < Nout && k < K) ? Bp[b][(size_t)col * K + k] : 0.f;
-      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Bs[b][lk + q][lm] = br[b][q];
     __syncthreads();
+    if (k0 + BK < K) {
+      ar = load4(arow_p, k0 + BK + lk);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) br[b] = load4(brow_p[b], k0 + BK + lk);
+    }
 #pragma unroll
     for (int kk = 0; kk < BK; ++kk) {
       float a[TM];

@@ -47,25 +47,65 @@ __global__ __launch_bounds__(kThreads) void router_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = 0.f;
 
-  for (int k0 = 0; k0 < d; k0 += BK) {
-    for (int i = tid; i < BM * BK; i += kThreads) {
-      int m = i / BK, kk = i % BK;
-      int t = t0 + m, k = k0 + kk;
-      float v = 0.f;
-      if (t < N && k < d) {
-        size_t off = (size_t)t * d + k;
-        v = XBF16 ? moe::bf16_bits_to_f32(((const uint16_t*)xv)[off]) : ((const float*)xv)[off];
-      }
-      As[kk][m] = v;
+  // staging: each thread loads groups of 4 consecutive K values (one A row
+  // segment and, while there are B rows left, one B row segment per group),
+  // one K step ahead into registers; past-the-end rows and K load zeros
+  constexpr int AG = BM * BK / 4 / kThreads, BG = (BN * BK / 4 + kThreads - 1) / kThreads;
+  static_assert(AG >= 1 && AG * kThreads * 4 == BM * BK, "A staging");
+  const bool vec = (d & 3) == 0;
+  auto ldx = [&](int t, int k) {
+    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+    if (t >= N) return v;
+    const size_t off = (size_t)t * d + k;
+    if constexpr (XBF16) {
+      for (int q = 0; q < 4; ++q)
+        if (k + q < d) v[q] = moe::bf16_bits_to_f32(((const uint16_t*)xv)[off + q]);
+    } else {
+      if (vec && k + 3 < d) return *(const f32x4_t*)((const float*)xv + off);
+      for (int q = 0; q < 4; ++q)
+        if (k + q < d) v[q] = ((const float*)xv)[off + q];
     }
-    for (int i = tid; i < BN * BK; i += kThreads) {
-      int n = i / BK, kk = i % BK;
-      int c = c0 + n, k = k0 + kk;
-      float v = 0.f;
-      if (c < E2 && k < d) v = (c < E) ? wg[(size_t)c * d + k] : wn[(size_t)(c - E) * d + k];
-      Bs[kk][n] = v;
+    return v;
+  };
+  auto ldw = [&](int c, int k) {
+    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+    if (c >= E2) return v;
+    const float* row = c < E ? wg + (size_t)c * d : wn + (size_t)(c - E) * d;
+    if (vec && k + 3 < d) return *(const f32x4_t*)(row + k);
+    for (int q = 0; q < 4; ++q)
+      if (k + q < d) v[q] = row[k + q];
+    return v;
+  };
+  f32x4_t ar[AG], br[BG];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < AG; ++u) {
+      const int i = tid + u * kThreads, m = i / (BK / 4), kq = (i % (BK / 4)) * 4;
+      ar[u] = ldx(t0 + m, k0 + kq);
+    }
+#pragma unroll
+    for (int u = 0; u < BG; ++u) {
+      const int i = tid + u * kThreads, n = i / (BK / 4), kq = (i % (BK / 4)) * 4;
+      br[u] = i < BN * BK / 4 ? ldw(c0 + n, k0 + kq) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  fetch(0);
+  for (int k0 = 0; k0 < d; k0 += BK) {
+#pragma unroll
+    for (int u = 0; u < AG; ++u) {
+      const int i = tid + u * kThreads, m = i / (BK / 4), kq = (i % (BK / 4)) * 4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) As[kq + q][m] = ar[u][q];
+    }
+#pragma unroll
+    for (int u = 0; u < BG; ++u) {
+      const int i = tid + u * kThreads, n = i / (BK / 4), kq = (i % (BK / 4)) * 4;
+      if (i < BN * BK / 4)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) Bs[kq + q][n] = br[u][q];
     }
     __syncthreads();
+    if (k0 + BK < d) fetch(k0 + BK);
 #pragma unroll
     for (int kk = 0; kk < BK; ++kk) {
       float a[TM], b[TN];
