@@ -43,8 +43,9 @@ struct Vec8<uint16_t> {
   }
 };
 
-// One block per token; each thread owns 8 consecutive features per pass
-// (k <= 8: the token's rows and gates sit in registers).
+// One block per token and column slice (blockIdx.y of gridDim.y: a few
+// tokens, as in decode, still fill the chip); each thread owns 8 consecutive
+// features per pass (k <= 8: the token's rows and gates sit in registers).
 template <typename YT, typename ST, typename OT>
 __global__ __launch_bounds__(kThreads) void combine_kernel(int d, int k,
                                                            const YT* __restrict__ y_rows,
@@ -60,7 +61,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(int d, int k,
     rows[j] = j < k ? row_of[(size_t)t * k + j] : -1;
     g[j] = j < k ? gates[(size_t)t * k + j] : 0.f;
   }
-  for (int c = threadIdx.x * 8; c < d; c += kThreads * 8) {
+  for (int c = (blockIdx.y * kThreads + threadIdx.x) * 8; c < d; c += gridDim.y * kThreads * 8) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void combine_wide_kernel(int d, int k,
     s_g[pos] = gj;
   }
   __syncthreads();
-  for (int c = threadIdx.x * 8; c < d; c += kThreads * 8) {
+  for (int c = (blockIdx.y * kThreads + threadIdx.x) * 8; c < d; c += gridDim.y * kThreads * 8) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int q = 0; q < n; ++q) {
       float v[8];
@@ -133,12 +134,18 @@ __global__ __launch_bounds__(kThreads) void combine_wide_kernel(int d, int k,
 template <typename YT, typename ST, typename OT>
 void launch_combine(int N, int d, int k, const void* yr, const int32_t* row_of,
                     const float* gates, const void* ysh, void* y, hipStream_t st) {
+  // column slices per token: enough blocks for the chip when tokens are few
+  const int chunks = (d + kThreads * 8 - 1) / (kThreads * 8);
+  int slices = 1;
+  while (slices < chunks && (long long)N * slices < 1024) slices *= 2;
+  if (slices > chunks) slices = chunks;
+  const dim3 grid(N, slices);
   if (k <= 8)
-    combine_kernel<YT, ST, OT><<<N, kThreads, 0, st>>>(d, k, (const YT*)yr, row_of, gates,
-                                                       (const ST*)ysh, (OT*)y);
+    combine_kernel<YT, ST, OT><<<grid, kThreads, 0, st>>>(d, k, (const YT*)yr, row_of, gates,
+                                                          (const ST*)ysh, (OT*)y);
   else
-    combine_wide_kernel<YT, ST, OT><<<N, kThreads, 0, st>>>(d, k, (const YT*)yr, row_of, gates,
-                                                            (const ST*)ysh, (OT*)y);
+    combine_wide_kernel<YT, ST, OT><<<grid, kThreads, 0, st>>>(d, k, (const YT*)yr, row_of,
+                                                               gates, (const ST*)ysh, (OT*)y);
 }
 
 template <typename YT, typename ST>
