@@ -40,6 +40,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/sec + grouped-GEMM % MFMA peak / decode % HBM peak, 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector (published, with packed fp32 FMA)
 
 
 def parse():
@@ -571,6 +572,11 @@ def main():
     if cfg.w_dtype == 2 or args.workload in ("c3", "c4"):
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
+    elif cfg.x_dtype == W.F32:
+        # fp32 experts run on the vector ALU (fp32 FMA), not on MFMA
+        roof = {"bound": "alu", "achieved": round(tflops, 3), "peak": PEAK_FP32_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP32_TFLOPS, 6),
+                "traffic": traffic}
     else:
         roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
