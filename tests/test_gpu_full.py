@@ -86,6 +86,53 @@ def test_full_size_parity(moe, key):
         assert rel_err(to_np(y2)[sample][alike], ref["y"][alike]) <= out_tol(cfg)
 
 
+def test_rows_beyond_int32_elements(moe):
+    """The DeepSeek-shaped prefill at 40000 tokens over 64 experts: 320000
+    packed rows of 7168, so the packed rows hold more than 2^31 elements and
+    every row offset past the 299593rd needs 64-bit arithmetic. Routing and
+    dispatch bit-exact from the oracle's logits; the sampled tokens are those
+    whose rows sit highest in the packed layout."""
+    cfg = W.C3.with_(name="deepseek_prefill_40k_tokens_64_experts", n_tokens=40000,
+                     n_experts=64, seed=31)
+    print("large rows", cfg.name, flush=True)
+    torch.manual_seed(0)
+    dev = W.make_inputs(cfg, "cuda")
+    torch.cuda.synchronize()
+    hx = host_view(dev["x"])
+    hwg = host_view(dev["w_gate"])
+    hb = {k: host_view(dev[k]) for k in ("logit_bias", "select_bias", "w_noise")}
+    H, _ = oracle.router_logits(hx, cfg.x_dtype, hwg, hb["logit_bias"], hb["w_noise"],
+                                cfg.noise_seed)
+    r0 = oracle.route(H, cfg.top_k, cfg.n_cand, cfg.renormalize, hb["select_bias"])
+    d0 = oracle.dispatch(r0["cand_ids"], r0["cand_scores"], r0["gates"], cfg.n_experts,
+                         cfg.top_k, cfg.overflow, cfg.capacity)
+    assert (int(d0["R"]) - 1) * cfg.d_model >= 2 ** 31
+    top = d0["row_of"].max(axis=1)
+    sample = np.sort(np.argsort(top, kind="stable")[-4:])
+    assert int(top[sample].min()) * cfg.d_model >= 2 ** 31
+    print("  oracle routing done, R =", d0["R"], " sample rows", top[sample], flush=True)
+    layer = moe.MoELayer(moe.spec_from_config(cfg), dev, x_dtype=torch.bfloat16)
+    y = layer.forward(dev["x"], logits_in=torch.from_numpy(H).cuda()).clone()
+    torch.cuda.synchronize()
+    shared = DeviceExperts(dev, "shared_")
+    ref = oracle.layer_forward(cfg, hx, cfg.x_dtype, hwg, DeviceExperts(dev), shared,
+                               hb["logit_bias"], hb["select_bias"], hb["w_noise"], logits=H,
+                               tokens=sample)
+    d = ref["dispatch"]
+    assert np.array_equal(to_np(layer.cand_ids), ref["route"]["cand_ids"])
+    assert np.array_equal(to_np(layer.gates).view(np.uint32), d["gates"].view(np.uint32))
+    for name in ("counts_routed", "offsets", "row_of", "expert_of"):
+        assert np.array_equal(to_np(getattr(layer, name)), d[name]), name
+    assert np.array_equal(to_np(layer.perm_token)[:d["R"]], d["perm_token"])
+    err = rel_err(to_np(y)[sample], ref["y"])
+    print("  sampled max|dy|/rms =", err, flush=True)
+    assert err <= out_tol(cfg)
+    # the packed rows behind the sample, read back directly: the last rows of
+    # the layout hold finite expert outputs of the right scale
+    yr = layer.y_rows[d["R"] - 16:d["R"]].float().cpu().numpy()
+    assert np.all(np.isfinite(yr)) and np.abs(yr).max() > 0
+
+
 def test_full_size_expert_choice(moe):
     """Mixtral-shaped prefill with expert-choice routing: selection bit-exact
     over all tokens from the oracle's logits, sampled outputs, statistics."""
