@@ -23,7 +23,10 @@
 // remapped to a logical tile such that each XCD walks one contiguous range
 // of logical tiles; logical tiles run GN N-tiles fastest, then M tiles, then
 // the next group of GN N-tiles, so the blocks resident on one XCD at a time
-// share a few A row panels and B weight panels in that XCD's L2.
+// share a few A row panels and B weight panels in that XCD's L2. The grid
+// is sized for the most M tiles the row counts could need; the ranges are
+// cut from the tiles that exist (read from the tile table), an equal share
+// per XCD, and the spare blocks exit at once.
 #pragma once
 
 #include <type_traits>
@@ -114,6 +117,12 @@ __device__ __forceinline__ int tile_expert(const int32_t* ts, int E, int mt) {
 #define MOE_PINGPONG 0
 #endif
 // LDS bytes the stages of one tile may take
+// 1: the XCDs split the M tiles that exist (tile_start[E]) rather than the
+// grid's max_mt slots per N group (DeepSeek prefill 3% faster, one GPU's
+// EP-8 share 1%, the rest unchanged)
+#ifndef MOE_XCD_QUOTA
+#define MOE_XCD_QUOTA 1
+#endif
 #ifndef MOE_LDS_BUDGET
 #define MOE_LDS_BUDGET 147456
 #endif
@@ -166,9 +175,22 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
+#if MOE_XCD_QUOTA
+  // the grid is sized for max_mt M tiles; the XCDs split the tiles that
+  // exist (tile_start[E] of them) evenly instead, each walking a contiguous
+  // range, and the surplus blocks of every XCD exit
+  const int n_real = g.tile_start[g.E];
+  const int total = ((g.n_tiles_n + g.group_n - 1) / g.group_n) * n_real * g.group_n;
+  const int quota = (total + 7) >> 3;
+  if ((int)(blockIdx.x >> 3) >= quota) return;
+  const int logical = (blockIdx.x & 7) * quota + (blockIdx.x >> 3);
+  if (logical >= total) return;
+  const int span = n_real * g.group_n;
+#else
   const int per_xcd = gridDim.x >> 3;
   const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   const int span = g.max_mt * g.group_n;
+#endif
   const int ng = logical / span, rem = logical - ng * span;
   const int mt = rem / g.group_n;
   const int nt = ng * g.group_n + (rem - mt * g.group_n);
@@ -527,6 +549,7 @@ inline hipError_t launch_dlds(Args g, int k_splits, hipStream_t st) {
     configured = true;
   }
   g.n_tiles_n = g.Nrows / BN;
+  if (g.group_n > g.n_tiles_n) g.group_n = g.n_tiles_n;
   const int n_groups = (g.n_tiles_n + g.group_n - 1) / g.group_n;
   const long long tiles = (long long)g.max_mt * n_groups * g.group_n;
   const int grid_x = (int)((tiles + 7) / 8 * 8);

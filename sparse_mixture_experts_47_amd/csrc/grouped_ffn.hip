@@ -613,6 +613,21 @@ __global__ __launch_bounds__(NW * 64) void ffn_fp8_stream_kernel(Fp8Args g,
 #ifndef MOE_G2_PAIR_BN
 #define MOE_G2_PAIR_BN 64
 #endif
+// N-group size of each expert GEMM launch (the pair GEMM 2 of fp32 h has
+// its own); with the quota split, groups of 8 in GEMM 1 measured 1-1.5%
+// faster on the Mixtral shapes and 3% slower on one GPU's EP-8 DeepSeek
+// share, groups of 4 or 8 everywhere no better overall, and GEMM 2 of the
+// Switch shape with all 16 N tiles per group (each XCD reading only its own
+// rows of h) 4% slower
+#ifndef MOE_G1_GN
+#define MOE_G1_GN MOE_GROUP_N
+#endif
+#ifndef MOE_G2_GN
+#define MOE_G2_GN MOE_GROUP_N
+#endif
+#ifndef MOE_G2_PAIR_GN
+#define MOE_G2_PAIR_GN MOE_GROUP_N
+#endif
 #ifndef MOE_G2_PAIR_WGN
 #define MOE_G2_PAIR_WGN 2
 #endif
@@ -749,11 +764,13 @@ hipError_t launch_g2(bool pair, bool ybf, const moe_gemm::Args& g2, hipStream_t 
   using namespace moe_gemm;
   const bool n2 = g2.Nrows % 128 == 0;
   if (pair) {
+    moe_gemm::Args gp = g2;
+    gp.group_n = MOE_G2_PAIR_GN;
     if (n2 && MOE_G2_PAIR_BN == 128)
-      return ybf ? run_gemm<BM, 128, 2, 1, EPI_OUT, OUT_BF16, MOE_G2_PAIR_WGN>(g2, 1, st)
-                 : run_gemm<BM, 128, 2, 1, EPI_OUT, OUT_F32, MOE_G2_PAIR_WGN>(g2, 1, st);
-    return ybf ? run_gemm<BM, 64, 2, 1, EPI_OUT, OUT_BF16, 2, MOE_GEMM_BK, MOE_G2_PAIR_WGM>(g2, 1, st)
-               : run_gemm<BM, 64, 2, 1, EPI_OUT, OUT_F32, 2, MOE_GEMM_BK, MOE_G2_PAIR_WGM>(g2, 1, st);
+      return ybf ? run_gemm<BM, 128, 2, 1, EPI_OUT, OUT_BF16, MOE_G2_PAIR_WGN>(gp, 1, st)
+                 : run_gemm<BM, 128, 2, 1, EPI_OUT, OUT_F32, MOE_G2_PAIR_WGN>(gp, 1, st);
+    return ybf ? run_gemm<BM, 64, 2, 1, EPI_OUT, OUT_BF16, 2, MOE_GEMM_BK, MOE_G2_PAIR_WGM>(gp, 1, st)
+               : run_gemm<BM, 64, 2, 1, EPI_OUT, OUT_F32, 2, MOE_GEMM_BK, MOE_G2_PAIR_WGM>(gp, 1, st);
   }
   if (MOE_G2_WIDE && BM == 256 && g2.Nrows % 256 == 0)
     return ybf ? run_gemm<BM, 256, 1, 1, EPI_OUT, OUT_BF16, MOE_G2_WIDE_WGN, MOE_GEMM_BK,
@@ -915,6 +932,7 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
   const bool ybf = y_dt == MOE_BF16;
   Args g1 = base_args(x_rows, w->w1, w->w3, w->b1, h, d, F, E, max_mt, (int)w->act, offsets,
                       tt.ts);
+  g1.group_n = MOE_G1_GN;
   g1.a_rows = row_index;
   g1.pre = preact;
   g1.seg_begin = tt.sb;
@@ -922,6 +940,7 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
   g1.tile_e = tt.te;
   Args g2 = base_args(h, w->w2, nullptr, w->b2, y_rows, F, d, E, max_mt, (int)w->act, offsets,
                       tt.ts);
+  g2.group_n = MOE_G2_GN;
   g2.seg_begin = tt.sb;
   g2.seg_end = tt.se;
   g2.tile_e = tt.te;
