@@ -166,11 +166,23 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bwd_kernel(BwdArgs g) {
   const int wm = wave / WGN, wn = wave % WGN;
 
   // ---- tile -> (expert, M tile, N tile); XCD-aware as in the forward GEMM
-  const int per_xcd = gridDim.x >> 3;
-  const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  [[maybe_unused]] const int per_xcd = gridDim.x >> 3;
   int e, mt, nt, row0 = 0, row_end = 0, kbeg = 0, kcount = 0;
   if constexpr (MODE == MODE_ROWS) {
+#if MOE_XCD_QUOTA
+    // an equal share of the M tiles that exist per XCD (the grid is sized
+    // for max_mt); spare blocks exit
+    const int n_real = g.tile_start[g.E];
+    const int total = ((g.n_tiles_n + g.group_n - 1) / g.group_n) * n_real * g.group_n;
+    const int quota = (total + 7) >> 3;
+    if ((int)(blockIdx.x >> 3) >= quota) return;
+    const int logical = (blockIdx.x & 7) * quota + (blockIdx.x >> 3);
+    if (logical >= total) return;
+    const int span = n_real * g.group_n;
+#else
+    const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
     const int span = g.max_mt * g.group_n;
+#endif
     const int ng = logical / span, rem = logical - ng * span;
     mt = rem / g.group_n;
     nt = ng * g.group_n + (rem - mt * g.group_n);
@@ -180,6 +192,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bwd_kernel(BwdArgs g) {
     row_end = g.offsets[e + 1];
     kcount = g.K;
   } else {
+    const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
     const int mtiles = g.M / BM;
     const int span = mtiles * g.group_n;
     const int per_e = span * ((g.n_tiles_n + g.group_n - 1) / g.group_n);
