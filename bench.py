@@ -480,7 +480,7 @@ def main():
     if args.oracle_single_core:
         return oracle_single_core_child(args)
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: libmoe has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     if args.backward:
