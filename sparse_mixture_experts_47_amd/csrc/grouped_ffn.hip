@@ -607,11 +607,14 @@ __global__ __launch_bounds__(NW * 64) void ffn_fp8_stream_kernel(Fp8Args g,
 // fragment reads per MFMA than 256x128, faster than 4 waves of 128x128
 // GEMM 2 with a bf16 hi/lo pair h (two A planes) and GEMM 1 with an
 // activation epilogue (the Switch/GELU shape: ~86 rows per expert, d_model
-// 1024): 64-column GEMM 2 tiles on 4x2 waves double the tile count of a
-// launch that otherwise leaves CUs idle, and 8-wave GEMM 1 tiles; together
-// 27% faster than 128-column tiles on 2x2 waves
+// 1024): GEMM 2 runs 128x256 tiles on 2x4 waves with two 64-wide K stages.
+// Its A operand is two planes of h, so a narrow tile re-streams them for
+// every N tile: against 64-column tiles on 4x2 waves (twice the tiles,
+// fewer idle CUs) the wide tile is 10% faster for the launch pair, with
+// four 32-wide stages 6%; 128-column tiles on 4x2 or 2x2 waves are slower
+// than either. GEMM 1 uses 8-wave tiles (9% faster than 2x2 waves).
 #ifndef MOE_G2_PAIR_BN
-#define MOE_G2_PAIR_BN 64
+#define MOE_G2_PAIR_BN 256
 #endif
 // N-group size of each expert GEMM launch (the pair GEMM 2 of fp32 h has
 // its own); with the quota split, groups of 8 in GEMM 1 measured 1-1.5%
@@ -627,6 +630,9 @@ __global__ __launch_bounds__(NW * 64) void ffn_fp8_stream_kernel(Fp8Args g,
 #endif
 #ifndef MOE_G2_PAIR_GN
 #define MOE_G2_PAIR_GN MOE_GROUP_N
+#endif
+#ifndef MOE_G2_PAIR256_BK
+#define MOE_G2_PAIR256_BK 64
 #endif
 #ifndef MOE_G2_PAIR_WGN
 #define MOE_G2_PAIR_WGN 2
@@ -766,6 +772,9 @@ hipError_t launch_g2(bool pair, bool ybf, const moe_gemm::Args& g2, hipStream_t 
   if (pair) {
     moe_gemm::Args gp = g2;
     gp.group_n = MOE_G2_PAIR_GN;
+    if (BM == 128 && MOE_G2_PAIR_BN == 256 && g2.Nrows % 256 == 0)
+      return ybf ? run_gemm<BM, 256, 2, 1, EPI_OUT, OUT_BF16, 4, MOE_G2_PAIR256_BK, 2>(gp, 1, st)
+                 : run_gemm<BM, 256, 2, 1, EPI_OUT, OUT_F32, 4, MOE_G2_PAIR256_BK, 2>(gp, 1, st);
     if (n2 && MOE_G2_PAIR_BN == 128)
       return ybf ? run_gemm<BM, 128, 2, 1, EPI_OUT, OUT_BF16, MOE_G2_PAIR_WGN>(gp, 1, st)
                  : run_gemm<BM, 128, 2, 1, EPI_OUT, OUT_F32, MOE_G2_PAIR_WGN>(gp, 1, st);
