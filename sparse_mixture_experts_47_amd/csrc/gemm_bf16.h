@@ -562,29 +562,30 @@ inline hipError_t launch_dlds(Args g, int k_splits, hipStream_t st) {
 #define MOE_GEMM_BK 64
 #endif
 
-// LDS stages for a tile: as many as fit in 144 KB (at most 8), bounded so
-// that (stages - 1) x loads-per-stage fits the 6-bit vmcnt (4 waves).
-template <int BM, int BN, int BK, int NA, int NB>
+// LDS stages for a tile: as many as fit in the budget (144 KB unless a
+// launch asks for less, at most 8), bounded so that (stages - 1) x
+// loads-per-stage fits the 6-bit vmcnt (4 waves).
+template <int BM, int BN, int BK, int NA, int NB, int BUDGET = MOE_LDS_BUDGET>
 constexpr int pick_stages() {
   constexpr int stage_bytes = (NA * BM + NB * BN) * BK * 2;
   constexpr int lpt = (NA * BM + NB * BN) * BK * 2 / 1024 / 4;  // with 4 waves
-  int ns = MOE_LDS_BUDGET / stage_bytes;
+  int ns = BUDGET / stage_bytes;
   if (ns > 8) ns = 8;
   while (ns > 2 && (ns - 1) * lpt >= 64) --ns;
   return ns;
 }
 
 // K width of a stage: the preferred one if two stages of it fit, else 32.
-template <int BM, int BN, int NA, int NB, int BKP>
+template <int BM, int BN, int NA, int NB, int BKP, int BUDGET = MOE_LDS_BUDGET>
 constexpr int pick_bk() {
-  return pick_stages<BM, BN, BKP, NA, NB>() >= 2 ? BKP : 32;
+  return pick_stages<BM, BN, BKP, NA, NB, BUDGET>() >= 2 ? BKP : 32;
 }
 
 template <int BM, int BN, int NA, int NB, int EPI, int OUTK, int WGN = 2, int BKP = MOE_GEMM_BK,
-          int WGM = 2>
+          int WGM = 2, int BUDGET = MOE_LDS_BUDGET>
 inline hipError_t run_gemm(const Args& g, int k_splits, hipStream_t st) {
-  constexpr int bk = pick_bk<BM, BN, NA, NB, BKP>();
-  constexpr int ns = pick_stages<BM, BN, bk, NA, NB>();
+  constexpr int bk = pick_bk<BM, BN, NA, NB, BKP, BUDGET>();
+  constexpr int ns = pick_stages<BM, BN, bk, NA, NB, BUDGET>();
   static_assert(ns >= 2, "tile too large for two LDS stages");
   return launch_dlds<BM, BN, bk, ns, WGM, WGN, NA, NB, EPI, OUTK>(g, k_splits, st);
 }

@@ -631,6 +631,19 @@ __global__ __launch_bounds__(NW * 64) void ffn_fp8_stream_kernel(Fp8Args g,
 #ifndef MOE_G2_PAIR_GN
 #define MOE_G2_PAIR_GN MOE_GROUP_N
 #endif
+#ifndef MOE_G2_PAIR_LDS
+#define MOE_G2_PAIR_LDS MOE_LDS_BUDGET
+#endif
+// LDS for GEMM 1 with an activation epilogue and 128-row tiles: three
+// 32-wide stages (48 KB, 74 VGPRs) let three blocks share a CU, so one
+// block's fill and epilogue overlap the others' K loops (K = d_model is
+// short on the Switch shape: 1024). Switch-shaped layer: GEMM 1 246 ->
+// ~190 us, grouped FFN -12% against one block per CU with four 64-wide
+// stages; two blocks (two 64-wide stages) -8%. The pair GEMM 2 needs 136
+// VGPRs, so a smaller budget cannot add a block there.
+#ifndef MOE_G1_ACT_LDS
+#define MOE_G1_ACT_LDS 49152
+#endif
 #ifndef MOE_G2_PAIR256_BK
 #define MOE_G2_PAIR256_BK 64
 #endif
@@ -759,8 +772,10 @@ hipError_t launch_g1(bool glu, bool pair, const moe_gemm::Args& g1, hipStream_t 
                 : run_gemm<BM, 64, 1, 2, EPI_GLU, OUT_BF16>(g1, 1, st);
   }
   if (n1)
-    return pair ? run_gemm<BM, 128, 1, 1, EPI_ACT, OUT_BF16_PAIR, MOE_G1_ACT_WGN>(g1, 1, st)
-                : run_gemm<BM, 128, 1, 1, EPI_ACT, OUT_BF16, MOE_G1_ACT_WGN>(g1, 1, st);
+    return pair ? run_gemm<BM, 128, 1, 1, EPI_ACT, OUT_BF16_PAIR, MOE_G1_ACT_WGN, MOE_GEMM_BK, 2,
+                           BM == 128 ? MOE_G1_ACT_LDS : MOE_LDS_BUDGET>(g1, 1, st)
+                : run_gemm<BM, 128, 1, 1, EPI_ACT, OUT_BF16, MOE_G1_ACT_WGN, MOE_GEMM_BK, 2,
+                           BM == 128 ? MOE_G1_ACT_LDS : MOE_LDS_BUDGET>(g1, 1, st);
   return pair ? run_gemm<BM, 64, 1, 1, EPI_ACT, OUT_BF16_PAIR>(g1, 1, st)
               : run_gemm<BM, 64, 1, 1, EPI_ACT, OUT_BF16>(g1, 1, st);
 }
@@ -772,12 +787,18 @@ hipError_t launch_g2(bool pair, bool ybf, const moe_gemm::Args& g2, hipStream_t 
   if (pair) {
     moe_gemm::Args gp = g2;
     gp.group_n = MOE_G2_PAIR_GN;
-    if (BM == 128 && MOE_G2_PAIR_BN == 256 && g2.Nrows % 256 == 0)
-      return ybf ? run_gemm<BM, 256, 2, 1, EPI_OUT, OUT_BF16, 4, MOE_G2_PAIR256_BK, 2>(gp, 1, st)
-                 : run_gemm<BM, 256, 2, 1, EPI_OUT, OUT_F32, 4, MOE_G2_PAIR256_BK, 2>(gp, 1, st);
-    if (n2 && MOE_G2_PAIR_BN == 128)
-      return ybf ? run_gemm<BM, 128, 2, 1, EPI_OUT, OUT_BF16, MOE_G2_PAIR_WGN>(gp, 1, st)
-                 : run_gemm<BM, 128, 2, 1, EPI_OUT, OUT_F32, MOE_G2_PAIR_WGN>(gp, 1, st);
+    if constexpr (BM == 128 && MOE_G2_PAIR_BN == 256) {
+      if (g2.Nrows % 256 == 0)
+        return ybf ? run_gemm<BM, 256, 2, 1, EPI_OUT, OUT_BF16, 4, MOE_G2_PAIR256_BK, 2,
+                              MOE_G2_PAIR_LDS>(gp, 1, st)
+                   : run_gemm<BM, 256, 2, 1, EPI_OUT, OUT_F32, 4, MOE_G2_PAIR256_BK, 2,
+                              MOE_G2_PAIR_LDS>(gp, 1, st);
+    }
+    if constexpr (MOE_G2_PAIR_BN == 128) {
+      if (n2)
+        return ybf ? run_gemm<BM, 128, 2, 1, EPI_OUT, OUT_BF16, MOE_G2_PAIR_WGN>(gp, 1, st)
+                   : run_gemm<BM, 128, 2, 1, EPI_OUT, OUT_F32, MOE_G2_PAIR_WGN>(gp, 1, st);
+    }
     return ybf ? run_gemm<BM, 64, 2, 1, EPI_OUT, OUT_BF16, 2, MOE_GEMM_BK, MOE_G2_PAIR_WGM>(gp, 1, st)
                : run_gemm<BM, 64, 2, 1, EPI_OUT, OUT_F32, 2, MOE_GEMM_BK, MOE_G2_PAIR_WGM>(gp, 1, st);
   }
