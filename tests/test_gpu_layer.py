@@ -358,6 +358,41 @@ def test_grouped_ffn_fp32_intermediate_is_tighter(moe):
     assert errs[True] <= 1e-3 and errs[True] < errs[False] / 8
 
 
+@pytest.mark.parametrize("d_model", [192, 256, 320, 512])
+def test_grouped_ffn_fp32_h_column_tilings(moe, d_model):
+    """GEMM 2 with fp32 h (hi + lo bf16 planes) on 128-row tiles runs
+    256-column tiles when d_model is a multiple of 256 (256, 512) and
+    64-column tiles otherwise (192, 320). Ragged experts (empty ones, a
+    single row, one past a tile), rows gathered through a row index; both
+    tilings reach the fp32-h bar, and rows past offsets[E] stay untouched."""
+    cfg = W.REDUCED["c4"].with_(name="switch_fp32h_d%d" % d_model, d_model=d_model)
+    print("fp32 h, d_model", d_model, flush=True)
+    inp = W.make_inputs(cfg, "cpu")
+    host = host_inputs(inp)
+    dev = to_device(inp)
+    E = cfg.n_experts
+    rng = np.random.default_rng(d_model)
+    counts = rng.integers(0, 60, size=E)
+    counts[0] = 0
+    counts[3] = 1
+    counts[5] = 200
+    counts[-1] = 0
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offs[-1])
+    tok = rng.integers(0, cfg.n_tokens, size=R)
+    y = torch.full((R + 3, d_model), 7.0, dtype=torch.float32, device="cuda")
+    w, keep = moe.ffn_weights(dev["w1"], dev["w2"], dev["w3"], cfg.act, h_fp32=True)
+    moe.moe_grouped_ffn(w, dev["x"], torch.from_numpy(offs).cuda(), y,
+                        row_index=torch.from_numpy(tok.astype(np.int32)).cuda(), max_rows=R)
+    torch.cuda.synchronize()
+    X64 = oracle.decode_rows(host["x"][tok], cfg.x_dtype)
+    ref = oracle.ffn_for_assignments(np.arange(R), np.repeat(np.arange(E), counts), X64,
+                                     cfg.act, cfg.w_dtype, experts_of(host))
+    got = to_np(y)
+    assert rel_err(got[:R], ref) <= 1e-3
+    assert np.all(got[R:] == 7.0)
+
+
 @pytest.mark.parametrize("key", ["c2", "c4", "c5", "c1"])
 def test_fused_gather_matches_explicit_gather(moe, key):
     """GEMM 1 reading token rows through perm_token gives bit-identical
