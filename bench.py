@@ -602,7 +602,7 @@ def main():
         "config": {"workload": cfg.name, "n_tokens": cfg.n_tokens, "d_model": cfg.d_model,
                    "n_experts": cfg.n_experts, "d_ff": cfg.d_ff, "top_k": cfg.top_k,
                    "act": ["relu", "gelu", "swiglu"][cfg.act],
-                   "shared_d_ff": cfg.shared_d_ff, "capacity": cfg.capacity,
+                   "shared_d_ff": cfg.shared_d_ff, "capacity": layer.spec.capacity,
                    "routing": "expert_choice" if cfg.expert_choice else "token_choice",
                    "parallelism": "single-gpu"},
         "roofline": roof,

@@ -167,8 +167,14 @@ size_t moe_dispatch_workspace_bytes(int32_t n_tokens, int32_t n_experts, int32_t
 
 /* capacity = ceil(n_tokens / n_experts * capacity_factor) (chiang97912
  * "专家容量": tokens per batch / number of experts x capacity factor; the
- * rounding up is this library's choice). Host function. */
-int32_t moe_capacity(int32_t n_tokens, int32_t n_experts, double capacity_factor);
+ * rounding up is this library's choice). The factor is the exact fraction
+ * cf_num / cf_den (1.25 = 5/4, 1.1 = 11/10), so a decimal factor is never
+ * replaced by its nearest binary value; the result is exact integer
+ * arithmetic, clamped to INT32_MAX. Expert-choice routing takes
+ * moe_capacity(N, E, top_k, 1) = ceil(N * top_k / E) tokens per expert.
+ * Returns -1 if n_tokens <= 0, n_experts <= 0, cf_num < 0 or cf_den <= 0.
+ * Host function, no GPU work. */
+int32_t moe_capacity(int32_t n_tokens, int32_t n_experts, int32_t cf_num, int32_t cf_den);
 
 /* ---------------------------------------------------------------------- */
 /* moe_expert_choice                                                       */

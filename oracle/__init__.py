@@ -17,6 +17,7 @@ import ctypes
 import os
 import subprocess
 import threading
+from fractions import Fraction
 
 import numpy as np
 
@@ -170,6 +171,28 @@ def route(logits, top_k, n_cand, renormalize, select_bias=None):
     return dict(s=s, cand_ids=cand, cand_scores=cand_s, gates=gates, lse=lse)
 
 
+def capacity(n_tokens, n_experts, capacity_factor):
+    """Expert capacity: (tokens per batch / number of experts) x capacity
+    factor, rounded up (chiang97912 MoE notes, section "专家容量"; the page
+    gives no rounding, the upward one is this library's reading). Exact
+    rational arithmetic: a float factor is taken as the decimal it prints as
+    (1.25 is 5/4, 1.1 is 11/10), never as its binary approximation, so the
+    one rounding is the ceiling itself. None means dropless: -1."""
+    if capacity_factor is None:
+        return -1
+    f = Fraction(repr(capacity_factor)) if isinstance(capacity_factor, float) else \
+        Fraction(capacity_factor)
+    q = Fraction(int(n_tokens)) / int(n_experts) * f
+    return -((-q.numerator) // q.denominator)  # ceiling of a fraction
+
+
+def expert_choice_capacity(n_tokens, n_experts, top_k):
+    """Tokens per expert under expert-choice routing: the number that gives
+    every expert the average load of top-k token choice, N*k/E, rounded up
+    (the rounding is this library's reading)."""
+    return capacity(n_tokens, n_experts, int(top_k))
+
+
 def expert_choice(s, capacity):
     """Expert-choice routing (heavensheep "Routing Function": experts choose
     tokens, which balances the load by construction; "[CS336-04] Mixture of
@@ -319,8 +342,10 @@ def layer_forward(cfg, x, x_dt, w_gate, experts: ExpertSource, shared: ExpertSou
     if getattr(cfg, "expert_choice", False):
         return _expert_choice_forward(cfg, x, x_dt, H, raw, experts, shared, tokens)
     r = route(H, cfg.top_k, cfg.n_cand, cfg.renormalize, select_bias)
+    cap = -1 if cfg.overflow == DROPLESS else capacity(H.shape[0], cfg.n_experts,
+                                                        cfg.capacity_factor)
     dsp = dispatch(r["cand_ids"], r["cand_scores"], r["gates"], cfg.n_experts, cfg.top_k,
-                   cfg.overflow, cfg.capacity)
+                   cfg.overflow, cap)
     st = balance_stats(cfg.top_k, dsp["counts_routed"], dsp["counts_kept"], r["s"], r["lse"])
     N = H.shape[0]
     rows = np.arange(N) if tokens is None else np.asarray(tokens)
@@ -346,11 +371,11 @@ def layer_forward(cfg, x, x_dt, w_gate, experts: ExpertSource, shared: ExpertSou
 
 def _expert_choice_forward(cfg, x, x_dt, H, raw, experts, shared, tokens):
     """Layer forward with expert-choice routing: softmax scores as for token
-    choice, every expert takes its `cfg.ec_capacity` top tokens, the FFNs run
+    choice, every expert takes its ceil(N*top_k/E) top tokens, the FFNs run
     on those rows, and a token's output sums gate x expert output over the
     experts that chose it (in expert order), plus the shared expert."""
     r = route(H, 1, 1, False)  # the full score matrix s; its top-1 is unused
-    ec = expert_choice(r["s"], cfg.ec_capacity)
+    ec = expert_choice(r["s"], expert_choice_capacity(H.shape[0], cfg.n_experts, cfg.top_k))
     E = cfg.n_experts
     N = H.shape[0]
     rows = np.arange(N) if tokens is None else np.asarray(tokens)

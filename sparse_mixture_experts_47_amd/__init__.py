@@ -15,6 +15,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+from fractions import Fraction
 from dataclasses import dataclass
 from typing import Optional
 
@@ -70,7 +71,7 @@ def _load():
     L.moe_dispatch.restype = i32
     L.moe_dispatch_workspace_bytes.argtypes = [i32, i32, i32]
     L.moe_dispatch_workspace_bytes.restype = sz
-    L.moe_capacity.argtypes = [i32, i32, ctypes.c_double]
+    L.moe_capacity.argtypes = [i32, i32, i32, i32]
     L.moe_capacity.restype = i32
     L.moe_grouped_ffn.argtypes = [ctypes.POINTER(FFNWeights), P, i32, P, P, i32, P, i32, P, sz,
                                   P]
@@ -147,8 +148,19 @@ def _dev_check(*ts):
             raise ValueError("libmoe tensors must live on the GPU")
 
 
-def capacity(n_tokens: int, n_experts: int, capacity_factor: float) -> int:
-    return int(lib.moe_capacity(n_tokens, n_experts, capacity_factor))
+def capacity(n_tokens: int, n_experts: int, capacity_factor) -> int:
+    """moe_capacity: ceil(n_tokens / n_experts * capacity_factor). A float
+    factor is passed as the decimal it prints as (1.1 -> 11/10); an int or a
+    fractions.Fraction as itself."""
+    f = Fraction(repr(capacity_factor)) if isinstance(capacity_factor, float) else \
+        Fraction(capacity_factor)
+    if f.numerator > 2**31 - 1 or f.denominator > 2**31 - 1:
+        raise ValueError("capacity factor %r needs a fraction of 31-bit integers" %
+                         (capacity_factor,))
+    c = int(lib.moe_capacity(n_tokens, n_experts, f.numerator, f.denominator))
+    if c < 0:
+        raise MoEError(1, "moe_capacity(%d, %d, %s) out of range" % (n_tokens, n_experts, f))
+    return c
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:
@@ -636,9 +648,17 @@ def layer_backward(layer, x, dy, alpha=0.0, beta=0.0, dw_dtype=torch.float32, st
 
 
 def spec_from_config(cfg) -> LayerSpec:
-    """LayerSpec from a workload config object (duck-typed)."""
-    return LayerSpec(cfg.n_tokens, cfg.d_model, cfg.n_experts, cfg.d_ff, cfg.top_k, cfg.act,
-                     cfg.renormalize, cfg.overflow, cfg.capacity, cfg.n_cand, cfg.noise_seed,
-                     1e-3, cfg.shared_d_ff, bool(getattr(cfg, "h_fp32", False)),
-                     bool(getattr(cfg, "expert_choice", False)),
-                     int(cfg.ec_capacity) if getattr(cfg, "expert_choice", False) else 0)
+    """LayerSpec from a workload config object (duck-typed). Capacities come
+    from moe_capacity: ceil(N * capacity_factor / E) under a dropping policy,
+    ceil(N * top_k / E) tokens per expert under expert choice."""
+    N, E = cfg.n_tokens, cfg.n_experts
+    ec = bool(getattr(cfg, "expert_choice", False))
+    cap = -1
+    if cfg.overflow != DROPLESS:
+        if cfg.capacity_factor is None:
+            raise ValueError("a dropping policy needs a capacity factor")
+        cap = capacity(N, E, cfg.capacity_factor)
+    return LayerSpec(N, cfg.d_model, E, cfg.d_ff, cfg.top_k, cfg.act,
+                     cfg.renormalize, cfg.overflow, cap, cfg.n_cand, cfg.noise_seed,
+                     1e-3, cfg.shared_d_ff, bool(getattr(cfg, "h_fp32", False)), ec,
+                     capacity(N, E, cfg.top_k) if ec else 0)

@@ -112,10 +112,13 @@ const char* moe_status_string(moe_status s) {
   return "MOE_UNKNOWN";
 }
 
-int32_t moe_capacity(int32_t n_tokens, int32_t n_experts, double capacity_factor) {
-  if (n_tokens <= 0 || n_experts <= 0 || !(capacity_factor >= 0.0)) return -1;
-  const double c = (double)n_tokens / (double)n_experts * capacity_factor;
-  return (int32_t)ceil(c - 1e-9);
+int32_t moe_capacity(int32_t n_tokens, int32_t n_experts, int32_t cf_num, int32_t cf_den) {
+  if (n_tokens <= 0 || n_experts <= 0 || cf_num < 0 || cf_den <= 0) return -1;
+  // ceil(N * num / (E * den)) in exact integer arithmetic: both products fit
+  // in 62 bits, so no rounding enters before the one ceiling
+  const int64_t p = (int64_t)n_tokens * cf_num, q = (int64_t)n_experts * cf_den;
+  const int64_t c = (p + q - 1) / q;
+  return c > INT32_MAX ? INT32_MAX : (int32_t)c;
 }
 
 size_t moe_router_workspace_bytes(int32_t n_tokens, int32_t d_model, int32_t n_experts,

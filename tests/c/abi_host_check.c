@@ -18,9 +18,12 @@
 
 int main(void) {
   /* capacity = ceil(N * CF / E) */
-  EXPECT(moe_capacity(256, 4, 1.25) == 80);
-  EXPECT(moe_capacity(16384, 64, 1.0) == 256);
-  EXPECT(moe_capacity(10, 3, 1.0) == 4);
+  EXPECT(moe_capacity(256, 4, 5, 4) == 80);
+  EXPECT(moe_capacity(16384, 64, 1, 1) == 256);
+  EXPECT(moe_capacity(10, 3, 1, 1) == 4);
+  EXPECT(moe_capacity(257, 4, 5, 4) == 81);
+  EXPECT(moe_capacity(100, 10, 11, 10) == 11);
+  EXPECT(moe_capacity(10, 3, 1, 0) == -1);
   EXPECT(moe_router_workspace_bytes(4096, 4096, 8, 0) > 0);
   EXPECT(moe_dispatch_workspace_bytes(8192, 256, 8) > 0);
   EXPECT(moe_router_backward_workspace_bytes(4096, 4096, 8) > 0);

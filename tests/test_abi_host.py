@@ -33,9 +33,25 @@ def test_capacity_and_workspace_queries(lib):
     assert lib.capacity(256, 4, 1.25) == 80
     assert lib.capacity(16384, 64, 1.0) == 256
     assert lib.capacity(10, 3, 1.0) == 4
+    assert lib.capacity(257, 4, 1.25) == 81
+    assert lib.capacity(100, 10, 1.1) == 11
     assert lib.lib.moe_router_workspace_bytes(4096, 4096, 8, 0) > 4096 * 8 * 4
     assert lib.lib.moe_dispatch_workspace_bytes(8192, 256, 8) > 0
     assert lib.lib.moe_workspace_bytes(4096, 8, 2, 4096, 14336) >= 8192 * 14336 * 2
+
+
+def test_capacity_matches_oracle(lib):
+    # libmoe's host capacity against the oracle's exact rational one; neither
+    # feeds the other
+    import random
+    import oracle
+    rnd = random.Random(7)
+    factors = [0, 0.1, 0.25, 0.5, 1.0, 1.1, 1.2, 1.25, 1.5, 2.0, 3.0, 0.3, 1.05]
+    for _ in range(2000):
+        N, E, cf = rnd.randint(1, 70000), rnd.randint(1, 256), rnd.choice(factors)
+        assert lib.capacity(N, E, cf) == oracle.capacity(N, E, cf), (N, E, cf)
+    for N, E, k in ((4096, 8, 2), (600, 8, 2), (10, 4, 3), (1, 256, 8), (777, 7, 5)):
+        assert lib.capacity(N, E, k) == oracle.expert_choice_capacity(N, E, k)
 
 
 def test_validation_errors_before_any_launch(lib):

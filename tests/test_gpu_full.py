@@ -105,7 +105,8 @@ def test_rows_beyond_int32_elements(moe):
                                 cfg.noise_seed)
     r0 = oracle.route(H, cfg.top_k, cfg.n_cand, cfg.renormalize, hb["select_bias"])
     d0 = oracle.dispatch(r0["cand_ids"], r0["cand_scores"], r0["gates"], cfg.n_experts,
-                         cfg.top_k, cfg.overflow, cfg.capacity)
+                         cfg.top_k, cfg.overflow,
+                         oracle.capacity(cfg.n_tokens, cfg.n_experts, cfg.capacity_factor))
     assert (int(d0["R"]) - 1) * cfg.d_model >= 2 ** 31
     top = d0["row_of"].max(axis=1)
     sample = np.sort(np.argsort(top, kind="stable")[-4:])

@@ -176,8 +176,10 @@ def test_dispatch_bit_exact(moe, N, E, k, policy, cf):
     logits = torch.randn((N, E), generator=g) + skew
     C = k + 1 if policy == W.REROUTE_THEN_DROP else k
     r = oracle.route(logits.numpy(), k, C, policy == W.DROPLESS)
+    cap_ref = oracle.capacity(N, E, cf)
     cap = -1 if cf is None else moe.capacity(N, E, cf)
-    ref = oracle.dispatch(r["cand_ids"], r["cand_scores"], r["gates"], E, k, policy, cap)
+    assert cap == cap_ref
+    ref = oracle.dispatch(r["cand_ids"], r["cand_scores"], r["gates"], E, k, policy, cap_ref)
     got = _dispatch_gpu(moe, r["cand_ids"], r["cand_scores"], r["gates"], E, k, policy, cap)
     for name in ("counts_routed", "counts_kept", "offsets", "row_of", "expert_of"):
         assert np.array_equal(got[name], ref[name]), name
@@ -189,6 +191,7 @@ def test_dispatch_forced_collapse(moe):
     # every token to expert 0: kept = capacity, kept tokens are exactly 0..cap-1
     N, E = 256, 4
     cap = moe.capacity(N, E, 1.25)
+    assert cap == 80  # 256 / 4 x 1.25
     cand = np.zeros((N, 1), np.int32)
     cs = np.ones((N, 1), np.float32)
     got = _dispatch_gpu(moe, cand, cs, cs.copy(), E, 1, W.DROP, cap)

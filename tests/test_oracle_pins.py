@@ -158,11 +158,26 @@ def test_renormalised_gates_sum_to_one():
 
 # ------------------------------------------------------------------ P4 capacity
 def test_capacity_closed_forms():
-    # chiang97912 notes, "专家容量": capacity = tokens/experts x factor
-    assert W.C1.capacity == 80    # 256/4 * 1.25
-    assert W.C4.capacity == 256   # 16384/64 * 1.0
-    assert W.C2.capacity == -1 and W.C3.capacity == -1 and W.C5.capacity == -1
-    assert W.C1.with_(n_tokens=257).capacity == math.ceil(257 / 4 * 1.25)
+    # chiang97912 notes, "专家容量": capacity = tokens/experts x factor, read
+    # as rounded up. Literal values worked by hand; the non-integer cases are
+    # the ones where floor, round and ceil disagree.
+    assert oracle.capacity(256, 4, 1.25) == 80       # tiny Switch: exactly 80
+    assert oracle.capacity(16384, 64, 1.0) == 256    # skewed Switch: exactly 256
+    assert oracle.capacity(257, 4, 1.25) == 81       # 80.3125: floor 80, round 80
+    assert oracle.capacity(10, 3, 1.0) == 4          # 3.333: floor 3, round 3
+    assert oracle.capacity(11, 4, 1.5) == 5          # 4.125
+    assert oracle.capacity(7, 2, 0.5) == 2           # 1.75: floor 1
+    assert oracle.capacity(30, 4, 1.1) == 9          # 8.25 (1.1 read as 11/10)
+    assert oracle.capacity(100, 10, 1.1) == 11       # exactly 11, not the 12 that
+    #                                                  the binary 1.1 (> 11/10) gives
+    assert oracle.capacity(30, 3, 0.1) == 1          # exactly 1
+    assert oracle.capacity(1, 64, 1.0) == 1          # 1/64 rounds up to one slot
+    assert oracle.capacity(64, 4, 0) == 0            # zero factor: every token drops
+    assert oracle.capacity(256, 4, None) == -1       # dropless
+    # expert choice: N*k/E rounded up
+    assert oracle.expert_choice_capacity(4096, 8, 2) == 1024
+    assert oracle.expert_choice_capacity(600, 8, 2) == 150
+    assert oracle.expert_choice_capacity(10, 4, 3) == 8  # 7.5
 
 
 def test_collapse_onto_one_expert_keeps_first_cap_tokens():
@@ -530,7 +545,7 @@ def test_expert_choice_layer_equals_dense_masked_formula():
     inp, a = _small_layer(cfg)
     out = oracle.layer_forward(cfg, a["x"], cfg.x_dtype, a["w_gate"], oracle.ExpertSource(a))
     s = out["route"]["s"].astype(np.float64)
-    cap = cfg.ec_capacity
+    cap = 12  # 48 tokens x top-2 / 8 experts
     X = oracle.decode_rows(a["x"], cfg.x_dtype)
     f = lambda w: oracle.bf16_to_f32(w).astype(np.float64)
     ref = np.zeros_like(X)

@@ -50,7 +50,7 @@ class MoEConfig:
     w_dtype: int                   # F32, BF16 or FP8_E4M3 (expert weights)
     renormalize: bool              # True: gates = top-k scores / their sum
     overflow: int = DROPLESS       # DROPLESS, DROP, REROUTE_THEN_DROP
-    capacity_factor: Optional[float] = None
+    capacity_factor: Optional[float] = None  # None = dropless; read as the decimal it prints as
     ffn_bias: bool = False         # b1/b2 present (C1)
     shared_d_ff: int = 0           # 0 = no shared expert
     select_bias: bool = False      # per-expert selection bias (loss-free balancing)
@@ -63,28 +63,13 @@ class MoEConfig:
     # keep the FFN intermediate h in fp32 (GEMM 2 as hi+lo bf16 passes); used
     # where the layer is bound by weight reads and MFMA time is spare
     h_fp32: bool = False
-    # expert-choice routing: every expert takes its top ec_capacity tokens
-    # (top_k then only sets the average, N * top_k = E * ec_capacity)
+    # expert-choice routing: every expert takes a fixed number of its top
+    # tokens (top_k then only sets the average load per expert)
     expert_choice: bool = False
 
     @property
     def n_cand(self) -> int:
         return self.top_k + 1 if self.overflow == REROUTE_THEN_DROP else self.top_k
-
-    @property
-    def capacity(self) -> int:
-        """Expert capacity = ceil(tokens / experts * capacity factor), or -1
-        when dropless. The closed form (tokens per batch / number of experts)
-        x capacity factor is given on the chiang97912 MoE notes, section
-        "专家容量"; rounding up is this library's reading."""
-        if self.overflow == DROPLESS or self.capacity_factor is None:
-            return -1
-        return int(math.ceil(self.n_tokens * self.capacity_factor / self.n_experts - 1e-9))
-
-    @property
-    def ec_capacity(self) -> int:
-        """Tokens per expert under expert choice: ceil(N * top_k / E)."""
-        return -(-self.n_tokens * self.top_k // self.n_experts)
 
     def with_(self, **kw) -> "MoEConfig":
         return dataclasses.replace(self, **kw)
