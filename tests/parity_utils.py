@@ -74,12 +74,14 @@ class DeviceExperts(oracle.ExpertSource):
         self.cache = {}
 
     def get(self, e):
+        # only the latest expert stays on the host: the oracle walks experts
+        # one at a time, and a full-size layer's weights run to 22 GB
         if e not in self.cache:
             out = {}
             for k in ("w1", "w3", "w2", "b1", "b2", "s1", "s3", "s2"):
                 v = self.d.get(self.prefix + k)
                 out[k] = None if v is None else host_view(v[e])
-            self.cache[e] = out
+            self.cache = {e: out}
         return self.cache[e]
 
 
@@ -99,3 +101,49 @@ def margins(keys, k):
 def oracle_keys(route, select_bias):
     s = route["s"]
     return s + select_bias[None, :] if select_bias is not None else s
+
+
+def tile_cover_sample(row_of, offsets, block=128, max_tokens=None):
+    """Tokens whose packed rows touch every `block`-row slice of every
+    expert's rows (slices start at the expert's first row, so every tile of
+    any row tiling in multiples of `block` -- full tiles, the ragged last
+    tile, a separate tail launch -- holds a sampled row) and every expert's
+    last row. Greedy set cover: repeatedly take the token that covers the most
+    targets not yet covered (ties to the lower token). row_of [N][slots]
+    (-1 = not kept), offsets [E+1] from the oracle's dispatch. Returns
+    (sorted token array, coverage dict)."""
+    row_of = np.asarray(row_of)
+    off = np.asarray(offsets, np.int64)
+    E = len(off) - 1
+    M = np.diff(off)
+    nblk = (M + block - 1) // block
+    blk_base = np.concatenate([[0], np.cumsum(nblk)])
+    n_targets = int(blk_base[-1]) + E
+    N, S = row_of.shape
+    rows = row_of.astype(np.int64)
+    kept = rows >= 0
+    e_of = np.clip(np.searchsorted(off, np.maximum(rows, 0), side="right") - 1, 0, E - 1)
+    t_blk = np.where(kept, blk_base[e_of] + (rows - off[e_of]) // block, -1)
+    t_last = np.where(kept & (rows == off[e_of + 1] - 1), blk_base[-1] + e_of, -1)
+    targets = np.concatenate([t_blk, t_last], axis=1)  # [N][2*slots], -1 = none
+    covered = np.zeros(n_targets + 1, bool)
+    covered[-1] = True  # the -1 slot
+    exists = np.zeros(n_targets, bool)
+    exists[targets[targets >= 0]] = True
+    covered[:-1] = ~exists
+    chosen = []
+    while not covered[:-1].all():
+        gain = np.zeros(N, np.int64)
+        for c in range(targets.shape[1]):
+            gain += ~covered[targets[:, c]]
+        t = int(np.argmax(gain))
+        if gain[t] == 0:
+            break
+        chosen.append(t)
+        covered[targets[t]] = True
+        if max_tokens is not None and len(chosen) >= max_tokens:
+            break
+    cov = dict(tokens=len(chosen), blocks=int(covered[:int(blk_base[-1])].sum()),
+               blocks_total=int(blk_base[-1]), last_rows=int(covered[int(blk_base[-1]):-1].sum()),
+               experts_with_rows=int((M > 0).sum()))
+    return np.array(sorted(chosen), np.int64), cov

@@ -302,6 +302,16 @@ def _check_router_statistical(g, ref, fwd, dy, host, cfg):
         worst[name] = float(ratio[i])
     print("  router-side error / (7 sigma + fp32):", {kk: round(v, 3) for kk, v in worst.items()},
           flush=True)
+    # the forward's normwise measure, max|g - ref| / RMS(ref), reported (not
+    # a bar here: with top-8 of 64 experts most logit gradients are tiny, so
+    # the RMS is small beside the largest entries' rounding error)
+    normwise = {}
+    for name in ("dgates", "dlogits", "dw_gate"):
+        R = checks[name][0]
+        G = to_np(g[name]).astype(np.float64)
+        normwise[name] = float(np.max(np.abs(G - R)) / np.sqrt(np.mean(R ** 2)))
+    print("  router-side max|err|/rms:", {kk: "%.2e" % v for kk, v in normwise.items()},
+          flush=True)
 
 
 def _check_bounds(g, ref, fwd, dy, host, cfg):

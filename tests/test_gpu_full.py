@@ -10,11 +10,13 @@ import torch
 import oracle
 import workloads as W
 from parity_utils import (MARGIN, TOL_REL, DeviceExperts, host_view, margins, oracle_keys,
-                          out_tol, rel_err, require_gpu, to_np)
+                          out_tol, rel_err, require_gpu, tile_cover_sample, to_np)
 
 pytestmark = pytest.mark.gpu
 
-SAMPLES = {"c1": 256, "c2": 12, "c3": 4, "c4": 24, "c5": 4, "c7": 4}
+# Tokens drawn at random on top of the tile-covering sample (the C1 and C5
+# batches are small enough to check every token).
+SAMPLES = {"c1": 256, "c2": 4, "c3": 2, "c4": 8, "c5": 64, "c7": 2}
 
 
 @pytest.fixture(scope="module")
@@ -45,8 +47,19 @@ def test_full_size_parity(moe, key):
     torch.cuda.synchronize()
     rng = np.random.default_rng(len(key))
     N = cfg.n_tokens
-    sample = np.arange(N) if SAMPLES[key] >= N else np.sort(
-        rng.choice(N, SAMPLES[key], replace=False))
+    r0 = oracle.route(H, cfg.top_k, cfg.n_cand, cfg.renormalize, hb["select_bias"])
+    d0 = oracle.dispatch(r0["cand_ids"], r0["cand_scores"], r0["gates"], cfg.n_experts,
+                         cfg.top_k, cfg.overflow,
+                         oracle.capacity(N, cfg.n_experts, cfg.capacity_factor))
+    if SAMPLES[key] >= N:
+        sample = np.arange(N)
+    else:
+        cover, cov = tile_cover_sample(d0["row_of"], d0["offsets"])
+        sample = np.union1d(cover, rng.choice(N, SAMPLES[key], replace=False))
+        print("  tile coverage:", cov, flush=True)
+        assert cov["blocks"] == cov["blocks_total"]
+        assert cov["last_rows"] == cov["experts_with_rows"]
+    print("  sampled tokens:", len(sample), flush=True)
     shared = DeviceExperts(dev, "shared_") if cfg.shared_d_ff else None
     ref = oracle.layer_forward(cfg, hx, cfg.x_dtype, hwg, DeviceExperts(dev), shared,
                                hb["logit_bias"], hb["select_bias"], hb["w_noise"], logits=H,
@@ -151,7 +164,13 @@ def test_full_size_expert_choice(moe):
     y = layer.forward(dev["x"], logits_in=torch.from_numpy(H).cuda()).clone()
     torch.cuda.synchronize()
     rng = np.random.default_rng(6)
-    sample = np.sort(rng.choice(cfg.n_tokens, 12, replace=False))
+    r0 = oracle.route(H, 1, 1, False)
+    ec0 = oracle.expert_choice(r0["s"], oracle.expert_choice_capacity(
+        cfg.n_tokens, cfg.n_experts, cfg.top_k))
+    cover, cov = tile_cover_sample(ec0["row_of"], ec0["offsets"])
+    print("  tile coverage:", cov, flush=True)
+    assert cov["blocks"] == cov["blocks_total"]
+    sample = np.union1d(cover, rng.choice(cfg.n_tokens, 4, replace=False))
     ref = oracle.layer_forward(cfg, hx, cfg.x_dtype, hwg, DeviceExperts(dev), None,
                                hb["logit_bias"], hb["select_bias"], hb["w_noise"], logits=H,
                                tokens=sample)

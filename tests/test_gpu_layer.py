@@ -118,6 +118,42 @@ def test_level2_router_gemm(moe, key):
     assert err <= out_tol(cfg), err
 
 
+@pytest.mark.parametrize("N,d,E,seed", [(300, 64, 64, 44), (130, 128, 16, 0xDEADBEEFCAFEBABE),
+                                         (65, 64, 256, 7)])
+def test_noisy_logits_bit_exact(moe, N, d, E, seed):
+    """Noisy gating H = l + z*softplus(v) (chiang97912 notes, "KeepTopK 策略"),
+    bit for bit against the oracle. x, W_g and W_noise hold small integers,
+    so both router GEMMs are exact in fp32 on either side (every partial sum
+    is an integer below 2^24) and any difference in H can only come from the
+    noise draw z, the softplus or the final fused multiply-add. v spans both
+    branches of the softplus (above 20: v itself; else log1p(exp(v)))."""
+    g = torch.Generator().manual_seed(N * 31 + E)
+    x = torch.randint(-2, 3, (N, d), generator=g).to(torch.bfloat16)
+    wg = torch.randint(-3, 4, (E, d), generator=g).float()
+    wn = torch.randint(-1, 2, (E, d), generator=g).float()
+    lb = (-1.1 * torch.log(torch.arange(E, dtype=torch.float64) + 1.0)).float()
+    H_ref, raw_ref = oracle.router_logits(W.bits_u16(x), W.BF16, wg.numpy(), lb.numpy(),
+                                          wn.numpy(), seed)
+    v_ref = (x.double() @ wn.double().T).numpy()
+    assert np.any(v_ref > 20) and np.any(np.abs(v_ref) <= 20)
+    C = 2
+    i32 = dict(dtype=torch.int32, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    cand, cs = torch.empty((N, C), **i32), torch.empty((N, C), **f32)
+    gates = torch.empty((N, 1), **f32)
+    H, v = torch.empty((N, E), **f32), torch.empty((N, E), **f32)
+    moe.moe_router_topk(x.cuda(), wg.cuda(), top_k=1, n_cand=C, renormalize=False,
+                        logit_bias=lb.cuda(), w_noise=wn.cuda(), noise_seed=seed,
+                        cand_ids=cand, cand_scores=cs, gates=gates, logits_out=H,
+                        noise_out=v)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(v), v_ref.astype(np.float32))
+    assert np.array_equal(to_np(H).view(np.uint32), H_ref.view(np.uint32))
+    # selection on top of the identical H is the oracle's too
+    r = oracle.route(H_ref, 1, C, False)
+    assert np.array_equal(to_np(cand), r["cand_ids"])
+
+
 @pytest.mark.parametrize("E,k,C,N,scale", [(5, 2, 3, 37, 1.0), (100, 8, 8, 70, 1.5),
                                            (256, 8, 9, 65, 2.0), (64, 1, 2, 1, 1.0),
                                            (3, 3, 3, 8, 0.0), (256, 1, 1, 130, 30.0)])

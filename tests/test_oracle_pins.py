@@ -460,6 +460,13 @@ def test_bf16_decode_is_exact():
 def test_splitmix64_published_vector():
     # First output of SplitMix64 seeded with 0 (Steele, Lea & Flood 2014).
     assert oracle.splitmix64(0) == 0xE220A8397B1DCDAF
+    # The generator's state advances by the golden-ratio increment between
+    # outputs; the first five outputs for seed 1234567 of the published
+    # reference generator.
+    G = 0x9E3779B97F4A7C15
+    seq = [oracle.splitmix64((1234567 + i * G) % 2**64) for i in range(5)]
+    assert seq == [6457827717110365317, 3203168211198807973, 9817491932198370423,
+                   4593380528125082431, 16408922859458223821]
 
 
 def test_hash_normal_moments_and_determinism():
