@@ -22,8 +22,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# LIBMOE_PATH selects another build of the same sources (tile-tuning builds)
-LIB_PATH = os.environ.get("LIBMOE_PATH") or os.path.join(_HERE, "libmoe.so")
+# the in-tree build, always (no environment override)
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 RELU, GELU, SWIGLU = 0, 1, 2

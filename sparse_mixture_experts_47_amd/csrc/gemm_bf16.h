@@ -101,28 +101,7 @@ __device__ __forceinline__ int tile_expert(const int32_t* ts, int E, int mt) {
 // 16-byte LDS read serves 16 lanes (16 consecutive rows, one logical chunk)
 // per cycle over 64 four-byte banks; rows r, r+4, r+8, r+12 share bank
 // group r%4, and the swizzle gives them four different chunks.
-#ifndef MOE_MFMA_PRIO
-#define MOE_MFMA_PRIO 0
-#endif
-#ifndef MOE_SCHED_GROUPS
-#define MOE_SCHED_GROUPS 0
-#endif
-#ifndef MOE_MFMA_ORDER
-#define MOE_MFMA_ORDER 0
-#endif
-#ifndef MOE_SKIP_EMPTY
-#define MOE_SKIP_EMPTY 1
-#endif
-#ifndef MOE_PINGPONG
-#define MOE_PINGPONG 0
-#endif
 // LDS bytes the stages of one tile may take
-// 1: the XCDs split the M tiles that exist (tile_start[E]) rather than the
-// grid's max_mt slots per N group (DeepSeek prefill 3% faster, one GPU's
-// EP-8 share 1%, the rest unchanged)
-#ifndef MOE_XCD_QUOTA
-#define MOE_XCD_QUOTA 1
-#endif
 #ifndef MOE_LDS_BUDGET
 #define MOE_LDS_BUDGET 147456
 #endif
@@ -175,7 +154,6 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
-#if MOE_XCD_QUOTA
   // the grid is sized for max_mt M tiles; the XCDs split the tiles that
   // exist (tile_start[E] of them) evenly instead, each walking a contiguous
   // range, and the surplus blocks of every XCD exit
@@ -186,11 +164,6 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
   const int logical = (blockIdx.x & 7) * quota + (blockIdx.x >> 3);
   if (logical >= total) return;
   const int span = n_real * g.group_n;
-#else
-  const int per_xcd = gridDim.x >> 3;
-  const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  const int span = g.max_mt * g.group_n;
-#endif
   const int ng = logical / span, rem = logical - ng * span;
   const int mt = rem / g.group_n;
   const int nt = ng * g.group_n + (rem - mt * g.group_n);
@@ -206,7 +179,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
   // (256-row tiles only: with 128-row tiles the checked loop measured slower
   // than computing the padding)
   int nfm = FM;
-  if constexpr (MOE_SKIP_EMPTY && BM == 256)
+  if constexpr (BM == 256)
     nfm = __builtin_amdgcn_readfirstlane(
         max(0, min(FM, (row_end - row0 - wm * WM + 31) / 32)));
   const int k_begin = blockIdx.y * g.k_chunk;
@@ -296,24 +269,6 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
                                        dlds_off<BK>(wn * WN + j * 32 + (lane & 31), c));
   };
   auto mfma = [&](const Frags& f, auto full) {
-#if MOE_MFMA_PRIO
-    __builtin_amdgcn_s_setprio(1);
-#endif
-#if MOE_MFMA_ORDER
-    // A-fragment major: consecutive MFMAs share their A operand
-#pragma unroll
-    for (int p = 0; p < NA; ++p)
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            if (!decltype(full)::value && i >= nfm) continue;
-            f32x16_t& d = acc[EPI == EPI_GLU ? b : 0][i][j];
-            d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[p][i], f.b[b][j], d, 0, 0, 0);
-          }
-#else
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -326,74 +281,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
             f32x16_t& d = acc[EPI == EPI_GLU ? b : 0][i][j];
             d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[p][i], f.b[b][j], d, 0, 0, 0);
           }
-#endif
-#if MOE_MFMA_PRIO
-    __builtin_amdgcn_s_setprio(0);
-#endif
   };
 
-  if constexpr (MOE_PINGPONG && NW == 8) {
-    if (KT > 0) {
-    // Ping-pong schedule. The 8 waves form two groups of four (one wave of
-    // each per SIMD) that run one phase apart: while one group issues the
-    // MFMAs of a cluster (CS K steps), the other reads the fragments of its
-    // next cluster from LDS and issues global loads, and every phase ends
-    // with a workgroup barrier. A SIMD's MFMA pipe is thus fed by one of its
-    // two waves in every phase, and a barrier costs only its own latency.
-    // Group 1 starts with an idle phase; cluster c of group q is read in
-    // phase 2c+q and multiplied in phase 2c+q+1.
-    // Stage rules: tile t+NS-1 is loaded into stage (t-1)%NS at the first
-    // read phase of tile t (every wave finished reading tile t-1 one phase
-    // earlier: reads end with lgkmcnt(0) before their phase barrier); each
-    // wave waits for its own loads of tile t+1 at the end of the phase just
-    // before group 0 first reads tile t+1 (group 0: its last multiply phase
-    // of tile t, group 1: its last read phase of tile t).
-    constexpr int CS = 2;                // K steps per cluster
-    static_assert(KK % CS == 0, "clusters per tile");
-    constexpr int CPT = KK / CS;
-    const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
-    Frags cf[CS];
-#pragma unroll
-    for (int j = 0; j < NS - 1; ++j)
-      if (j < KT) issue(j, j);
-    if (KT > NS - 2) wait_vmcnt<(NS - 2) * LPT>();
-    else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    if (grp == 1) __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    const int NC = KT * CPT;
-    for (int c = 0; c < NC; ++c) {
-      const int t = c / CPT, h = c - t * CPT;
-      // ---- read phase
-      if (h == 0 && t + NS - 1 < KT) issue(t + NS - 1, (t + NS - 1) % NS);
-#pragma unroll
-      for (int s = 0; s < CS; ++s) read_frags(cf[s], t % NS, h * CS + s, std::true_type{});
-      __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
-      if (grp == 1 && h == CPT - 1 && t + 1 < KT) {
-        if (t + NS - 1 < KT) wait_vmcnt<(NS - 2) * LPT>();
-        else wait_vmcnt<0>();
-      }
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      // ---- multiply phase
-#if MOE_MFMA_PRIO
-      __builtin_amdgcn_s_setprio(1);
-#endif
-#pragma unroll
-      for (int s = 0; s < CS; ++s) mfma(cf[s], std::true_type{});
-#if MOE_MFMA_PRIO
-      __builtin_amdgcn_s_setprio(0);
-#endif
-      __builtin_amdgcn_sched_barrier(0);
-      if (grp == 0 && h == CPT - 1 && t + 1 < KT) {
-        if (t + NS - 1 < KT) wait_vmcnt<(NS - 2) * LPT>();
-        else wait_vmcnt<0>();
-      }
-      if (grp == 0 || c + 1 < NC) __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    }
-  } else {
+  {
     // Schedule per K tile kt (stage kt % NS), in two 16-wide halves:
     //   read half 1 of tile kt; MFMAs on half 0;
     //   wait for this wave's LDS reads and for tile kt+1's loads; barrier
@@ -422,11 +312,6 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
         for (int kk = 0; kk + 1 < KK; ++kk) {
           read_frags(fr[(kk + 1) & 1], kt % NS, kk + 1, full);
           mfma(fr[kk & 1], full);
-#if MOE_SCHED_GROUPS
-          // all LDS reads of the next step go out before this step's MFMAs
-          __builtin_amdgcn_sched_group_barrier(0x100, NA * FM + NB * FN, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, NA * NB * FM * FN, 0);
-#endif
           __builtin_amdgcn_sched_barrier(0);
         }
         // this wave's LDS reads of tile kt are done; tile kt+1 may still be
@@ -439,11 +324,6 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
         if (kt + NS < KT) issue(kt + NS, kt % NS);
         if (kt + 1 < KT) read_frags(fr[KK & 1], (kt + 1) % NS, 0, full);
         mfma(fr[(KK - 1) & 1], full);
-#if MOE_SCHED_GROUPS
-        __builtin_amdgcn_sched_group_barrier(0x020, LPT, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, NA * FM + NB * FN, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, NA * NB * FM * FN, 0);
-#endif
         __builtin_amdgcn_sched_barrier(0);
       }
     };

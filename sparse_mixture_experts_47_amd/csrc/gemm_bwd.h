@@ -169,7 +169,6 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bwd_kernel(BwdArgs g) {
   [[maybe_unused]] const int per_xcd = gridDim.x >> 3;
   int e, mt, nt, row0 = 0, row_end = 0, kbeg = 0, kcount = 0;
   if constexpr (MODE == MODE_ROWS) {
-#if MOE_XCD_QUOTA
     // an equal share of the M tiles that exist per XCD (the grid is sized
     // for max_mt); spare blocks exit
     const int n_real = g.tile_start[g.E];
@@ -179,10 +178,6 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bwd_kernel(BwdArgs g) {
     const int logical = (blockIdx.x & 7) * quota + (blockIdx.x >> 3);
     if (logical >= total) return;
     const int span = n_real * g.group_n;
-#else
-    const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-    const int span = g.max_mt * g.group_n;
-#endif
     const int ng = logical / span, rem = logical - ng * span;
     mt = rem / g.group_n;
     nt = ng * g.group_n + (rem - mt * g.group_n);
