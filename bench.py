@@ -10,6 +10,12 @@ synthetic (seeded, drawn on the GPU) and resident in HBM before timing.
 Prints one JSON line. The default workload is the Mixtral-shaped prefill
 (4096 tokens, d_model 4096, 8 experts of d_ff 14336 SwiGLU, top-2, bf16).
 
+decode: with the default workload, a sub-record for the decode-shaped layer
+(64 tokens against the DeepSeek-shaped layer, fp8 e4m3 expert weights):
+whole-layer and grouped-FFN bandwidth on the touched experts' weights against
+the HBM peak. per_call_gbs: algorithmic bytes and achieved GB/s (fraction of
+the HBM peak) of the router, dispatch and combine calls.
+
 roofline: the grouped expert FFN (moe_grouped_ffn: tile table + GEMM 1
 gate/up with fused SwiGLU + GEMM 2 down) is the dominant kernel group; its
 duration is measured with HIP events on the launch stream inside the timed
@@ -50,6 +56,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "c6", "c7"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="with the default Mixtral workload: skip the decode-shaped sub-record")
     ap.add_argument("--cpu-sample", type=int, default=0,
                     help="tokens in the oracle's timed sample (0: choose by workload)")
     ap.add_argument("--cold-steps", type=int, default=10,
@@ -71,13 +79,15 @@ def parse():
     return ap.parse_args()
 
 
-def ffn_work(cfg, counts_kept, touched):
+def ffn_work(cfg, counts_kept, touched, fused_combine=False):
     """Algorithmic work of one routed moe_grouped_ffn launch (the dominant
     kernel pair): FLOPs = 2 d F per weight matrix per kept assignment (3
     matrices for SwiGLU, 2 otherwise); weight bytes = every touched expert's
     weights once (+ fp32 per-channel scales for fp8); activation bytes = the
     packed rows read (bf16) and expert outputs written (fp32), h written and
-    read once (bf16, or a bf16 pair with h_fp32)."""
+    read once (bf16, or a bf16 pair with h_fp32). With the top-1 combine in
+    GEMM 2's epilogue the outputs go to all N token rows instead (dropped
+    tokens' rows zeroed)."""
     d, F = cfg.d_model, cfg.d_ff
     nmat = 3 if cfg.act == 2 else 2
     R = int(sum(counts_kept))
@@ -88,7 +98,8 @@ def ffn_work(cfg, counts_kept, touched):
     wbytes = touched * nmat * d * F * wbytes_el
     if cfg.w_dtype == 2:
         wbytes += touched * 4 * ((nmat - 1) * F + d)
-    act_bytes = R * d * xbytes + R * d * 4 + R * F * hbytes * 2
+    out_rows = cfg.n_tokens if fused_combine else R
+    act_bytes = R * d * xbytes + out_rows * d * 4 + R * F * hbytes * 2
     return flops, wbytes, act_bytes
 
 
@@ -475,6 +486,148 @@ def bench_backward(args):
     print(json.dumps(out), flush=True)
 
 
+def call_bytes(cfg, layer, counts):
+    """Algorithmic bytes of the memory-bound calls of one forward, in the
+    formats this library moves: router (x and router weights read once,
+    candidates, gates and logits written), dispatch (candidates and gates
+    read, per-assignment rows and counts written), combine (each kept fp32
+    expert row and the shared expert's row read once, the output written)."""
+    N, d, E = cfg.n_tokens, cfg.d_model, cfg.n_experts
+    k, C = layer.gates.shape[1], layer.C
+    xb = 4 if cfg.x_dtype == 0 else 2
+    R = int(sum(counts))
+    router = N * d * xb + E * d * 4 * (2 if cfg.noisy else 1) + N * E * 4 + N * (2 * C + k) * 4
+    if layer.scores is not None:
+        router += N * E * 4
+    if layer.ec:
+        dispatch = N * E * 4 + E * 4 + layer.R * 4 + N * E * 8
+    else:
+        dispatch = N * C * 8 + N * k * 4 * 5 + E * 12
+    slots = layer.row_of.shape[1]
+    combine = R * d * 4 + N * slots * 8 + N * d * layer.y.element_size()
+    if layer.shared is not None:
+        combine += N * d * 4
+    return {"router": router, "dispatch": dispatch, "combine": combine}
+
+
+def time_forward(cfg, steps, warmup, cold_steps):
+    """Build the layer for `cfg` on resident synthetic inputs, run `warmup`
+    forwards, then time `steps` back-to-back forwards with HIP events around
+    every call on the launch stream (and `cold_steps` more, each after a
+    512 MiB write that evicts the 256 MB Infinity Cache)."""
+    import numpy as np
+    import torch
+
+    import sparse_mixture_experts_47_amd as moe
+    import workloads as W
+
+    dev = W.make_inputs(cfg, "cuda")
+    xdt = torch.float32 if cfg.x_dtype == W.F32 else torch.bfloat16
+    layer = moe.MoELayer(moe.spec_from_config(cfg), dev, x_dtype=xdt)
+    x = dev["x"]
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        layer.forward(x)
+    torch.cuda.synchronize()
+    counts = layer.counts_kept.cpu().numpy()
+    names = ["router", "dispatch", "grouped_ffn", "combine", "stats"]
+
+    def one_step(e):
+        e[0].record(stream)
+        layer.start_shared(x)
+        layer.route(x)
+        e[1].record(stream)
+        layer.dispatch(x)
+        e[2].record(stream)
+        layer.experts(x)
+        e[3].record(stream)
+        layer.combine()
+        e[4].record(stream)
+        layer.stats()
+        e[5].record(stream)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for st in range(steps):
+        one_step(ev[st])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    samples = {n: [ev[st][i].elapsed_time(ev[st][i + 1]) for st in range(steps)]
+               for i, n in enumerate(names)}
+    layer_ev = [ev[st][0].elapsed_time(ev[st][len(names)]) for st in range(steps)]
+    cold = None
+    if cold_steps > 0:
+        evict = torch.empty(1 << 27, dtype=torch.float32, device="cuda")
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+               for _ in range(cold_steps)]
+        for st in range(cold_steps):
+            evict.fill_(float(st))
+            one_step(cev[st])
+            torch.cuda.synchronize()
+        csamp = {n: [cev[st][i].elapsed_time(cev[st][i + 1]) for st in range(cold_steps)]
+                 for i, n in enumerate(names)}
+        clayer = [cev[st][0].elapsed_time(cev[st][len(names)]) for st in range(cold_steps)]
+        cold = {"steps": cold_steps, "evict_bytes": 4 << 27,
+                "ms_per_step_median": round(float(np.median(clayer)), 4),
+                "ms_per_step_min": round(float(np.min(clayer)), 4),
+                "per_call_ms_median": {kk: round(float(np.median(v)), 4)
+                                       for kk, v in csamp.items()}}
+        del evict
+    return dict(dev=dev, layer=layer, x=x, counts=counts, samples=samples, layer_ev=layer_ev,
+                ms_step=elapsed * 1e3 / steps, cold=cold)
+
+
+def per_call_gbs(cfg, layer, counts, samples):
+    """Achieved algorithmic GB/s and fraction of HBM peak of the router,
+    dispatch and combine calls (median call time)."""
+    import numpy as np
+    out = {}
+    for name, nbytes in call_bytes(cfg, layer, counts).items():
+        ms = float(np.median(samples[name]))
+        if name == "combine" and layer.fused_combine:
+            out[name] = {"fused_into": "grouped_ffn", "ms_median": round(ms, 4)}
+            continue
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"bytes": int(nbytes), "ms_median": round(ms, 4), "gbs": round(gbs, 1),
+                     "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    return out
+
+
+def decode_record(steps, warmup):
+    """The decode-shaped layer (64 tokens against the DeepSeek-shaped layer,
+    fp8 e4m3 expert weights): whole-layer and grouped-FFN bandwidth against
+    the HBM peak, on the touched experts' weights."""
+    import numpy as np
+    import workloads as W
+    cfg = W.CONFIGS["c5"]
+    r = time_forward(cfg, steps, warmup, 0)
+    layer, counts = r["layer"], r["counts"]
+    touched = int((counts > 0).sum())
+    flops, wbytes, act_bytes = ffn_work(cfg, counts, touched, layer.fused_combine)
+    ffn_ms = float(np.median(r["samples"]["grouped_ffn"]))
+    lw = layer_weight_bytes(cfg, touched)
+    lay_ms = float(np.median(r["layer_ev"]))
+    rec = {"workload": cfg.name, "n_tokens": cfg.n_tokens, "steps": steps,
+           "ms_per_step": round(r["ms_step"], 4),
+           "layer_ms_events_median": round(lay_ms, 4),
+           "touched_experts": touched, "layer_weight_bytes": int(lw),
+           "layer_weight_gbs": round(lw / (r["ms_step"] * 1e-3) / 1e9, 1),
+           "layer_weight_frac_hbm": round(lw / (r["ms_step"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+           "grouped_ffn_ms_median": round(ffn_ms, 4),
+           "grouped_ffn_bytes": int(wbytes + act_bytes),
+           "grouped_ffn_gbs": round((wbytes + act_bytes) / (ffn_ms * 1e-3) / 1e9, 1),
+           "grouped_ffn_frac_hbm": round((wbytes + act_bytes) / (ffn_ms * 1e-3) / 1e9
+                                         / PEAK_HBM_GBS, 4),
+           "per_call_ms_median": {kk: round(float(np.median(v)), 4)
+                                  for kk, v in r["samples"].items()},
+           "per_call_gbs": per_call_gbs(cfg, layer, counts, r["samples"]),
+           "tokens_per_s": round(cfg.n_tokens / (r["ms_step"] * 1e-3), 1)}
+    del r
+    return rec
+
+
 def main():
     args = parse()
     if args.oracle_single_core:
@@ -493,78 +646,13 @@ def main():
 
     cfg = W.CONFIGS[args.workload]
     torch.cuda.set_device(0)
-    dev = W.make_inputs(cfg, "cuda")
-    xdt = torch.float32 if cfg.x_dtype == W.F32 else torch.bfloat16
-    layer = moe.MoELayer(moe.spec_from_config(cfg), dev, x_dtype=xdt)
-    x = dev["x"]
-    stream = torch.cuda.current_stream()
-
-    for _ in range(args.warmup):
-        layer.forward(x)
-    torch.cuda.synchronize()
-    counts = layer.counts_kept.cpu().numpy()
+    r = time_forward(cfg, args.steps, args.warmup, args.cold_steps)
+    dev, layer, x, counts = r["dev"], r["layer"], r["x"], r["counts"]
     touched = int((counts > 0).sum())
-
-    names = ["router", "dispatch", "grouped_ffn", "combine", "stats"]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        e = ev[s]
-        e[0].record(stream)
-        layer.start_shared(x)
-        layer.route(x)
-        e[1].record(stream)
-        layer.dispatch(x)
-        e[2].record(stream)
-        layer.experts(x)
-        e[3].record(stream)
-        layer.combine()
-        e[4].record(stream)
-        layer.stats()
-        e[5].record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-
-    samples = {n: [ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]
-               for i, n in enumerate(names)}
+    samples, layer_ev, cold = r["samples"], r["layer_ev"], r["cold"]
     per = {n: float(np.mean(v)) for n, v in samples.items()}
-    layer_ev = [ev[s][0].elapsed_time(ev[s][len(names)]) for s in range(args.steps)]
-
-    # cold-cache steps: a 512 MiB write before each step evicts the 256 MB
-    # Infinity Cache; each step is timed on its own with events
-    cold = None
-    if args.cold_steps > 0:
-        evict = torch.empty(1 << 27, dtype=torch.float32, device="cuda")
-        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-               for _ in range(args.cold_steps)]
-        for s in range(args.cold_steps):
-            evict.fill_(float(s))
-            e = cev[s]
-            e[0].record(stream)
-            layer.start_shared(x)
-            layer.route(x)
-            e[1].record(stream)
-            layer.dispatch(x)
-            e[2].record(stream)
-            layer.experts(x)
-            e[3].record(stream)
-            layer.combine()
-            e[4].record(stream)
-            layer.stats()
-            e[5].record(stream)
-            torch.cuda.synchronize()
-        csamp = {n: [cev[s][i].elapsed_time(cev[s][i + 1]) for s in range(args.cold_steps)]
-                 for i, n in enumerate(names)}
-        clayer = [cev[s][0].elapsed_time(cev[s][len(names)]) for s in range(args.cold_steps)]
-        cold = {"steps": args.cold_steps, "evict_bytes": 4 << 27,
-                "ms_per_step_median": round(float(np.median(clayer)), 4),
-                "ms_per_step_min": round(float(np.min(clayer)), 4),
-                "per_call_ms_median": {k: round(float(np.median(v)), 4) for k, v in csamp.items()}}
-        del evict
-    ms_step = elapsed * 1e3 / args.steps
-    flops, wbytes, act_bytes = ffn_work(cfg, counts, touched)
+    ms_step = r["ms_step"]
+    flops, wbytes, act_bytes = ffn_work(cfg, counts, touched, layer.fused_combine)
     ffn_ms = per["grouped_ffn"]
     tflops = flops / (ffn_ms * 1e-3) / 1e12
     gbs = (wbytes + act_bytes) / (ffn_ms * 1e-3) / 1e9
@@ -582,7 +670,8 @@ def main():
                 "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic}
     roof["kernel"] = ("moe_grouped_ffn, routed experts (tile table + GEMM 1 gate/up with "
-                      "fused activation + GEMM 2 down)")
+                      "fused activation + GEMM 2 down" +
+                      (" with the top-1 combine in its epilogue)" if layer.fused_combine else ")"))
     roof["per_launch"] = {"flops": flops, "weight_bytes": wbytes, "activation_bytes": act_bytes,
                           "avg_ms": round(ffn_ms, 4)}
 
@@ -618,6 +707,7 @@ def main():
                                        / PEAK_HBM_GBS, 4),
         "touched_experts": touched,
         "kept_assignments": int(counts.sum()),
+        "per_call_gbs": per_call_gbs(cfg, layer, counts, samples),
     }
     if args.copy_calibration:
         # a plain streaming kernel of known size for HBM counter calibration:
@@ -651,12 +741,18 @@ def main():
         out["graph_replay"] = {"error": repr(e)[:300]}
     if not args.no_clocks:
         out["clocks"] = sample_clocks(lambda: layer.forward(x))
+
     if not args.no_cpu_baseline:
         S = args.cpu_sample or {"c1": 256, "c2": 1024, "c3": 64, "c4": 4096, "c5": 64,
                                   "c6": 1024, "c7": 64}[args.workload]
         out["cpu_baseline"] = cpu_baseline(cfg, dev, S)
         if args.workload == "c1":
             out["cpu_baseline"]["single_core"] = cpu_baseline_single_core("c1", S)
+    if args.workload == "c2" and not args.no_decode:
+        # the second target: the decode-shaped layer against the HBM peak
+        del layer, dev, r
+        torch.cuda.empty_cache()
+        out["decode"] = decode_record(args.steps, args.warmup)
     print(json.dumps(out), flush=True)
 
 

@@ -110,6 +110,13 @@ typedef struct {
                                before the softplus (the backward pass's
                                input), or NULL. Not written when logits_in
                                is given (the router computes no logits) */
+  const void* w_planes;     /* w_gate (and w_noise) as three bf16 planes from
+                               moe_router_prepare, or NULL: then every call
+                               splits them into the workspace first. Used
+                               when x is bf16 and d % 64 == 0 (the matrix-
+                               core router), ignored otherwise; must match
+                               w_gate / w_noise (the caller re-prepares after
+                               changing them) */
 } moe_router_params;
 
 /*  x          [N][d] activations, x_dt = MOE_F32 or MOE_BF16
@@ -130,6 +137,23 @@ moe_status moe_router_topk(const moe_router_params* p, const void* x, moe_dtype 
                            void* hip_stream);
 size_t moe_router_workspace_bytes(int32_t n_tokens, int32_t d_model, int32_t n_experts,
                                   int32_t with_noise);
+
+/* The router weights w_gate (rows 0..E-1) and w_noise (rows E..2E-1, if
+ * given) as three bf16 planes whose sum is the fp32 weight exactly:
+ * hi = bf16(w), mid = bf16(w - hi), lo = bf16(w - hi - mid), so that the
+ * router GEMM with bf16 x runs on bf16 matrix cores with every product
+ * exact (the fp32 router of heavensheep "Training": the scores must not be
+ * computed in bf16). Layout [3][E2pad][d], E2pad = E (2E with w_noise)
+ * rounded up to a multiple of 64, zero rows past the weights; size from
+ * moe_router_planes_bytes. The caller owns `planes` and passes it as
+ * moe_router_params.w_planes on later calls; libmoe keeps no state.
+ * Needs d_model % 64 == 0 and 1 <= n_experts <= 256 (else EINVAL /
+ * EUNSUPPORTED), planes_bytes >= moe_router_planes_bytes (else
+ * EWORKSPACE), 16-byte aligned planes. Asynchronous on hip_stream. */
+size_t moe_router_planes_bytes(int32_t n_experts, int32_t d_model, int32_t with_noise);
+moe_status moe_router_prepare(const float* w_gate, const float* w_noise, int32_t n_experts,
+                              int32_t d_model, void* planes, size_t planes_bytes,
+                              void* hip_stream);
 
 /* ---------------------------------------------------------------------- */
 /* moe_dispatch                                                            */
@@ -164,6 +188,7 @@ moe_status moe_dispatch(int32_t n_tokens, int32_t n_experts, int32_t top_k, int3
                         int32_t* perm_token, void* x_perm, void* workspace, size_t ws_bytes,
                         void* hip_stream);
 size_t moe_dispatch_workspace_bytes(int32_t n_tokens, int32_t n_experts, int32_t top_k);
+
 
 /* capacity = ceil(n_tokens / n_experts * capacity_factor) (chiang97912
  * "专家容量": tokens per batch / number of experts x capacity factor; the
@@ -254,6 +279,30 @@ moe_status moe_grouped_ffn(const moe_ffn_weights* w, const void* x_rows, moe_dty
                            void* hip_stream);
 size_t moe_grouped_ffn_workspace_bytes(const moe_ffn_weights* w, moe_dtype act_dt,
                                        int32_t max_rows);
+
+/* moe_grouped_ffn followed by moe_combine for top-1 routing without a
+ * shared expert, in one call: the combine is done where the expert outputs
+ * are made (mkbk-pku.cn "MOE的优化", Fused MoE kernel: no round trip of the
+ * expert outputs through memory). With one assignment per token, GEMM 2's
+ * epilogue writes fmaf(gates[t], value, 0) straight to y[t] for the token
+ * t = perm_token[r] of each packed row r, and the rows of tokens whose
+ * assignment was dropped (row_of[t] < 0) are set to 0 -- the same bits
+ * moe_combine would produce from y_rows. A first small kernel zeroes the
+ * dropped rows and puts each kept gate at its packed row (in the
+ * workspace), so the epilogue's gate and token loads do not depend on each
+ * other. Arguments as moe_grouped_ffn,
+ * plus n_tokens, perm_token [max_rows], row_of [N][1] and gates [N][1]
+ * from moe_dispatch (top_k = 1), y [N][d_model] fp32 out instead of
+ * y_rows. Needs max_rows <= n_tokens (EINVAL), no fp8 weights and
+ * d_model % 4 == 0 (EUNSUPPORTED); perm_token's first offsets[E] entries
+ * must be distinct tokens (dispatch's output is). Workspace: as
+ * moe_grouped_ffn. */
+moe_status moe_grouped_ffn_combine_top1(const moe_ffn_weights* w, const void* x_rows,
+                                        moe_dtype act_dt, const int32_t* row_index,
+                                        const int32_t* offsets, int32_t max_rows,
+                                        int32_t n_tokens, const int32_t* perm_token,
+                                        const int32_t* row_of, const float* gates, float* y,
+                                        void* workspace, size_t ws_bytes, void* hip_stream);
 
 /* ---------------------------------------------------------------------- */
 /* moe_combine                                                             */

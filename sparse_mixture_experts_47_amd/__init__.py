@@ -44,7 +44,8 @@ class RouterParams(ctypes.Structure):
                 ("n_cand", ctypes.c_int32), ("renormalize", ctypes.c_int32),
                 ("logit_bias", ctypes.c_void_p), ("select_bias", ctypes.c_void_p),
                 ("w_noise", ctypes.c_void_p), ("noise_seed", ctypes.c_uint64),
-                ("scores_out", ctypes.c_void_p), ("noise_out", ctypes.c_void_p)]
+                ("scores_out", ctypes.c_void_p), ("noise_out", ctypes.c_void_p),
+                ("w_planes", ctypes.c_void_p)]
 
 
 class FFNWeights(ctypes.Structure):
@@ -66,6 +67,10 @@ def _load():
     L.moe_router_topk.restype = i32
     L.moe_router_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.moe_router_workspace_bytes.restype = sz
+    L.moe_router_planes_bytes.argtypes = [i32, i32, i32]
+    L.moe_router_planes_bytes.restype = sz
+    L.moe_router_prepare.argtypes = [P, P, i32, i32, P, sz, P]
+    L.moe_router_prepare.restype = i32
     L.moe_dispatch.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, i32, i32, P, P, P, P,
                                P, P, P, P, sz, P]
     L.moe_dispatch.restype = i32
@@ -76,6 +81,9 @@ def _load():
     L.moe_grouped_ffn.argtypes = [ctypes.POINTER(FFNWeights), P, i32, P, P, i32, P, i32, P, sz,
                                   P]
     L.moe_grouped_ffn.restype = i32
+    L.moe_grouped_ffn_combine_top1.argtypes = [ctypes.POINTER(FFNWeights), P, i32, P, P, i32,
+                                               i32, P, P, P, P, P, sz, P]
+    L.moe_grouped_ffn_combine_top1.restype = i32
     L.moe_grouped_ffn_workspace_bytes.argtypes = [ctypes.POINTER(FFNWeights), i32, i32]
     L.moe_grouped_ffn_workspace_bytes.restype = sz
     L.moe_combine.argtypes = [i32, i32, i32, P, i32, P, P, P, i32, P, i32, P]
@@ -168,12 +176,26 @@ def workspace(nbytes: int, device) -> torch.Tensor:
 
 
 # --------------------------------------------------------------------- calls
+def moe_router_prepare(w_gate, w_noise=None, planes=None, stream=None):
+    """The router weights as three exact bf16 planes for later router calls
+    (w_planes=); returns the (new or given) uint8 device buffer."""
+    E, d = w_gate.shape
+    nb = lib.moe_router_planes_bytes(E, d, int(w_noise is not None))
+    if planes is None:
+        planes = workspace(nb, w_gate.device)
+    _dev_check(w_gate, w_noise, planes)
+    _check(lib.moe_router_prepare(_ptr(w_gate), _ptr(w_noise), E, d, _ptr(planes), planes.numel(),
+                                  _stream(stream)))
+    return planes
+
+
 def moe_router_topk(x, w_gate, *, top_k, n_cand=None, renormalize=True, logit_bias=None,
                     select_bias=None, w_noise=None, noise_seed=0, logits_in=None, cand_ids,
                     cand_scores, gates, logits_out=None, score_sums=None, scores_out=None,
-                    noise_out=None, ws=None, stream=None):
+                    noise_out=None, w_planes=None, ws=None, stream=None):
     """Router GEMM + fp32 softmax + top-k. Outputs are written in place;
-    scores_out [N][E] fp32 (optional) receives every softmax score."""
+    scores_out [N][E] fp32 (optional) receives every softmax score; w_planes
+    (from moe_router_prepare) skips the per-call weight split."""
     N, E = cand_ids.shape[0], (w_gate.shape[0] if logits_in is None else logits_in.shape[1])
     d = x.shape[1] if x is not None else 0
     n_cand = n_cand or top_k
@@ -181,7 +203,7 @@ def moe_router_topk(x, w_gate, *, top_k, n_cand=None, renormalize=True, logit_bi
                scores_out, noise_out)
     p = RouterParams(N, d, E, top_k, n_cand, int(bool(renormalize)),
                      _ptr(logit_bias), _ptr(select_bias), _ptr(w_noise), int(noise_seed),
-                     _ptr(scores_out), _ptr(noise_out))
+                     _ptr(scores_out), _ptr(noise_out), _ptr(w_planes))
     if ws is None:
         ws = workspace(lib.moe_router_workspace_bytes(N, d, E, int(w_noise is not None)),
                        cand_ids.device)
@@ -239,6 +261,22 @@ def moe_grouped_ffn(weights: FFNWeights, x_rows, offsets, y_rows, *, row_index=N
     _check(lib.moe_grouped_ffn(ctypes.byref(weights), _ptr(x_rows), _dt(x_rows),
                                _ptr(row_index), _ptr(offsets), max_rows, _ptr(y_rows),
                                _dt(y_rows), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def moe_grouped_ffn_combine_top1(weights: FFNWeights, x_rows, offsets, perm_token, row_of, gates,
+                                 y, *, row_index=None, max_rows=None, ws=None, stream=None):
+    """Grouped expert FFN with the top-1 gate-weighted combine in GEMM 2's
+    epilogue: writes y [N][d] (fp32) in token order directly."""
+    _dev_check(x_rows, offsets, perm_token, row_of, gates, y, row_index)
+    N = row_of.shape[0]
+    max_rows = max_rows or perm_token.shape[0]
+    if ws is None:
+        ws = workspace(lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(weights), _dt(x_rows),
+                                                           max_rows), x_rows.device)
+    _check(lib.moe_grouped_ffn_combine_top1(ctypes.byref(weights), _ptr(x_rows), _dt(x_rows),
+                                            _ptr(row_index), _ptr(offsets), max_rows, N,
+                                            _ptr(perm_token), _ptr(row_of), _ptr(gates), _ptr(y),
+                                            _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def moe_combine(y_rows, row_of, gates, y, *, y_shared=None, stream=None):
@@ -354,7 +392,7 @@ class MoELayer:
     """
 
     def __init__(self, spec: LayerSpec, weights: dict, x_dtype=torch.bfloat16, device="cuda",
-                 out_dtype=None, fused_gather=True, train=False):
+                 out_dtype=None, fused_gather=True, train=False, fuse_combine=True):
         self.spec = s = spec
         self.w = weights
         self.dev = torch.device(device)
@@ -421,6 +459,11 @@ class MoELayer:
             self._shared_pending = False
         xdt = _dt(torch.empty(0, dtype=x_dtype))
         noise = int(weights.get("w_noise") is not None)
+        # router weights as exact bf16 planes, split once (bf16 x, matrix-
+        # core router); prepare_router() redoes it after the weights change
+        self.router_planes = None
+        if xdt == BF16 and s.d_model % 64 == 0:
+            self.prepare_router()
         self.ws_router = workspace(lib.moe_router_workspace_bytes(N, s.d_model, E, noise), dev)
         self.ws_dispatch = workspace(lib.moe_dispatch_workspace_bytes(N, E, k), dev)
         self.ws_ffn = workspace(lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(self.ffn), xdt,
@@ -446,7 +489,18 @@ class MoELayer:
                 self.preact_sh = torch.empty((N, (2 if glu else 1) * s.shared_d_ff), **bf)
                 self.h_sh = torch.empty((N, s.shared_d_ff), **bf)
             self._bwd = None
+        # top-1 routing without a shared expert: the combine runs in GEMM 2's
+        # epilogue (moe_grouped_ffn_combine_top1), y_rows is not written
+        self.fused_combine = bool(fuse_combine and not self.ec and k == 1 and
+                                  self.shared is None and not self.train and
+                                  weights["w1"].dtype != torch.uint8 and
+                                  self.out_dtype == torch.float32 and s.d_model % 4 == 0)
         self._forward_done = False
+
+    def prepare_router(self, stream=None):
+        """(Re)split w_gate / w_noise into the router's bf16 weight planes."""
+        self.router_planes = moe_router_prepare(self.w["w_gate"], self.w.get("w_noise"),
+                                                planes=self.router_planes, stream=stream)
 
     def route(self, x, logits_in=None, stream=None, noise_in=None):
         """noise_in (training with noisy gating and logits_in only): the noise
@@ -466,8 +520,8 @@ class MoELayer:
                         cand_ids=self.cand_ids, cand_scores=self.cand_scores, gates=self.gates,
                         logits_out=self.logits, score_sums=self.score_sums,
                         scores_out=self.scores,
-                        noise_out=self.noise_v if self.train else None, ws=self.ws_router,
-                        stream=stream)
+                        noise_out=self.noise_v if self.train else None,
+                        w_planes=self.router_planes, ws=self.ws_router, stream=stream)
 
     def dispatch(self, x, stream=None):
         s = self.spec
@@ -510,12 +564,18 @@ class MoELayer:
             moe_grouped_ffn_train(self.ffn, rows, self.offsets, self.y_rows, self.preact, self.h,
                                   row_index=index, max_rows=self.R, ws=self.ws_ffn,
                                   stream=stream)
+        elif self.fused_combine:
+            moe_grouped_ffn_combine_top1(self.ffn, rows, self.offsets, self.perm_token,
+                                         self.row_of, self.gates, self.y, row_index=index,
+                                         max_rows=self.R, ws=self.ws_ffn, stream=stream)
         else:
             moe_grouped_ffn(self.ffn, rows, self.offsets, self.y_rows, row_index=index,
                             max_rows=self.R, ws=self.ws_ffn, stream=stream)
         self.start_shared(x, stream)
 
     def combine(self, stream=None):
+        if self.fused_combine:
+            return  # done in the experts' GEMM 2 epilogue
         if self.shared is not None:
             (stream or torch.cuda.current_stream()).wait_event(self.ev_shared)
             self._shared_pending = False

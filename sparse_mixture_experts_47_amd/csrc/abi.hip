@@ -9,6 +9,9 @@
 namespace moe_host {
 
 size_t router_workspace_bytes(int N, int d, int E, int with_noise);
+size_t router_planes_bytes(int E, int d, int with_noise);
+moe_status router_prepare_launch(const float* w_gate, const float* w_noise, int E, int d,
+                                 uint16_t* planes, hipStream_t st);
 moe_status router_launch(const moe_router_params* p, const void* x, moe_dtype x_dt,
                          const float* w_gate, const float* logits_in, int32_t* cand_ids,
                          float* cand_scores, float* gates, float* logits_out,
@@ -24,7 +27,12 @@ size_t grouped_ffn_workspace_bytes(const moe_ffn_weights* w, moe_dtype act_dt, i
 moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_dtype act_dt,
                               const int32_t* row_index, const int32_t* offsets, int max_rows,
                               void* y_rows, moe_dtype y_dt, void* workspace, hipStream_t st,
-                              uint16_t* preact = nullptr, uint16_t* h_out = nullptr);
+                              uint16_t* preact = nullptr, uint16_t* h_out = nullptr,
+                              const int32_t* out_token = nullptr,
+                              const float* out_gate = nullptr);
+moe_status combine_dropped_launch(int N, int d, const int32_t* row_of, const float* gates,
+                                  float* gate_row, float* y, hipStream_t st);
+float* row_gates_ws(const moe_ffn_weights* w, moe_dtype act_dt, int max_rows, void* ws);
 size_t grouped_ffn_backward_workspace_bytes(const moe_ffn_weights* w, int max_rows,
                                             bool gather);
 moe_status grouped_ffn_backward_launch(const moe_ffn_weights* w, const void* x_rows,
@@ -152,6 +160,29 @@ size_t moe_workspace_bytes(int32_t n_tokens, int32_t n_experts, int32_t top_k, i
   return m > c ? m : c;
 }
 
+size_t moe_router_planes_bytes(int32_t n_experts, int32_t d_model, int32_t with_noise) {
+  if (n_experts <= 0 || d_model <= 0) return 0;
+  return router_planes_bytes(n_experts, d_model, with_noise ? 1 : 0);
+}
+
+moe_status moe_router_prepare(const float* w_gate, const float* w_noise, int32_t n_experts,
+                              int32_t d_model, void* planes, size_t planes_bytes,
+                              void* hip_stream) {
+  CHECK(w_gate && planes, MOE_EINVAL, "moe_router_prepare: NULL w_gate or planes");
+  CHECK(n_experts >= 1 && d_model >= 1, MOE_EINVAL, "moe_router_prepare: E=%d d=%d", n_experts,
+        d_model);
+  CHECK(n_experts <= 256, MOE_EUNSUPPORTED, "moe_router_prepare: n_experts %d > 256",
+        n_experts);
+  CHECK(d_model % 64 == 0, MOE_EINVAL, "moe_router_prepare: d_model %d %% 64 != 0", d_model);
+  const size_t need = router_planes_bytes(n_experts, d_model, w_noise ? 1 : 0);
+  CHECK(planes_bytes >= need, MOE_EWORKSPACE,
+        "moe_router_prepare: %zu bytes of planes needed, %zu given", need, planes_bytes);
+  CHECK(((uintptr_t)planes & 15) == 0, MOE_EINVAL,
+        "moe_router_prepare: planes not 16-byte aligned");
+  return router_prepare_launch(w_gate, w_noise, n_experts, d_model, (uint16_t*)planes,
+                               (hipStream_t)hip_stream);
+}
+
 moe_status moe_router_topk(const moe_router_params* p, const void* x, moe_dtype x_dt,
                            const float* w_gate, const float* logits_in, int32_t* cand_ids,
                            float* cand_scores, float* gates, float* logits_out,
@@ -174,12 +205,47 @@ moe_status moe_router_topk(const moe_router_params* p, const void* x, moe_dtype 
     CHECK(x_dt == MOE_F32 || x_dt == MOE_BF16, MOE_EUNSUPPORTED,
           "moe_router_topk: x dtype must be F32 or BF16");
   }
+  CHECK(((uintptr_t)p->w_planes & 15) == 0, MOE_EINVAL,
+        "moe_router_topk: w_planes not 16-byte aligned");
   const int noise = (!logits_in && p->w_noise) ? 1 : 0;
   moe_status s = check_ws(workspace, ws_bytes, router_workspace_bytes(N, logits_in ? 0 : d, E, noise),
                           "moe_router_topk");
   if (s != MOE_OK) return s;
   return router_launch(p, x, x_dt, w_gate, logits_in, cand_ids, cand_scores, gates, logits_out,
                        score_sums, workspace, (hipStream_t)hip_stream);
+}
+
+static moe_status check_dispatch(const char* who, int32_t n_tokens, int32_t n_experts,
+                                 int32_t top_k, int32_t n_cand, moe_overflow policy,
+                                 int32_t capacity, const int32_t* cand_ids,
+                                 const float* cand_scores, const float* gates, const void* x,
+                                 moe_dtype x_dt, int32_t d_model, const int32_t* counts_routed,
+                                 const int32_t* counts_kept, const int32_t* offsets,
+                                 const int32_t* row_of, const int32_t* expert_of,
+                                 const int32_t* perm_token, const void* x_perm) {
+  const int N = n_tokens, E = n_experts, k = top_k, C = n_cand;
+  CHECK(N >= 1 && E >= 1 && k >= 1 && k <= E, MOE_EINVAL,
+        "%s: N=%d E=%d k=%d out of range", who, N, E, k);
+  CHECK(C == k || C == k + 1, MOE_EINVAL, "%s: n_cand %d must be k or k+1", who, C);
+  CHECK((long long)N * C < (1ll << 31), MOE_EINVAL, "%s: N*n_cand too large", who);
+  CHECK(policy == MOE_DROPLESS || policy == MOE_DROP || policy == MOE_REROUTE_THEN_DROP,
+        MOE_EINVAL, "%s: unknown overflow policy %d", who, (int)policy);
+  CHECK(policy == MOE_DROPLESS || capacity >= 0, MOE_EINVAL,
+        "%s: capacity %d must be >= 0 with a dropping policy", who, capacity);
+  CHECK(capacity >= -1, MOE_EINVAL, "%s: capacity %d < -1", who, capacity);
+  CHECK(cand_ids && cand_scores && gates && counts_routed && counts_kept && offsets && row_of &&
+            expert_of && perm_token,
+        MOE_EINVAL, "%s: NULL argument", who);
+  CHECK(E <= 256, MOE_EUNSUPPORTED, "%s: n_experts %d > 256", who, E);
+  CHECK(policy != MOE_REROUTE_THEN_DROP || (k == 1 && C == 2), MOE_EUNSUPPORTED,
+        "%s: reroute needs top_k == 1 and n_cand == 2", who);
+  if (x_perm) {
+    CHECK(x, MOE_EINVAL, "%s: x_perm given without x", who);
+    CHECK(x_dt == MOE_F32 || x_dt == MOE_BF16, MOE_EUNSUPPORTED, "%s: x dtype", who);
+    CHECK(d_model >= 8 && d_model % 8 == 0, MOE_EUNSUPPORTED,
+          "%s: d_model %d must be a multiple of 8", who, d_model);
+  }
+  return MOE_OK;
 }
 
 moe_status moe_dispatch(int32_t n_tokens, int32_t n_experts, int32_t top_k, int32_t n_cand,
@@ -189,39 +255,24 @@ moe_status moe_dispatch(int32_t n_tokens, int32_t n_experts, int32_t top_k, int3
                         int32_t* offsets, int32_t* row_of, int32_t* expert_of,
                         int32_t* perm_token, void* x_perm, void* workspace, size_t ws_bytes,
                         void* hip_stream) {
-  const int N = n_tokens, E = n_experts, k = top_k, C = n_cand;
-  CHECK(N >= 1 && E >= 1 && k >= 1 && k <= E, MOE_EINVAL,
-        "moe_dispatch: N=%d E=%d k=%d out of range", N, E, k);
-  CHECK(C == k || C == k + 1, MOE_EINVAL, "moe_dispatch: n_cand %d must be k or k+1", C);
-  CHECK((long long)N * C < (1ll << 31), MOE_EINVAL, "moe_dispatch: N*n_cand too large");
-  CHECK(policy == MOE_DROPLESS || policy == MOE_DROP || policy == MOE_REROUTE_THEN_DROP,
-        MOE_EINVAL, "moe_dispatch: unknown overflow policy %d", (int)policy);
-  CHECK(policy == MOE_DROPLESS || capacity >= 0, MOE_EINVAL,
-        "moe_dispatch: capacity %d must be >= 0 with a dropping policy", capacity);
-  CHECK(capacity >= -1, MOE_EINVAL, "moe_dispatch: capacity %d < -1", capacity);
-  CHECK(cand_ids && cand_scores && gates && counts_routed && counts_kept && offsets && row_of &&
-            expert_of && perm_token,
-        MOE_EINVAL, "moe_dispatch: NULL argument");
-  CHECK(E <= 256, MOE_EUNSUPPORTED, "moe_dispatch: n_experts %d > 256", E);
-  CHECK(policy != MOE_REROUTE_THEN_DROP || (k == 1 && C == 2), MOE_EUNSUPPORTED,
-        "moe_dispatch: reroute needs top_k == 1 and n_cand == 2");
-  if (x_perm) {
-    CHECK(x, MOE_EINVAL, "moe_dispatch: x_perm given without x");
-    CHECK(x_dt == MOE_F32 || x_dt == MOE_BF16, MOE_EUNSUPPORTED, "moe_dispatch: x dtype");
-    CHECK(d_model >= 8 && d_model % 8 == 0, MOE_EUNSUPPORTED,
-          "moe_dispatch: d_model %d must be a multiple of 8", d_model);
-  }
-  moe_status s = check_ws(workspace, ws_bytes, dispatch_workspace_bytes(N, E, k), "moe_dispatch");
+  moe_status s = check_dispatch("moe_dispatch", n_tokens, n_experts, top_k, n_cand, policy,
+                                capacity, cand_ids, cand_scores, gates, x, x_dt, d_model,
+                                counts_routed, counts_kept, offsets, row_of, expert_of,
+                                perm_token, x_perm);
   if (s != MOE_OK) return s;
-  return dispatch_launch(N, E, k, C, policy, capacity, cand_ids, cand_scores, gates, x, x_dt,
-                         d_model, counts_routed, counts_kept, offsets, row_of, expert_of,
-                         perm_token, x_perm, workspace, (hipStream_t)hip_stream);
+  s = check_ws(workspace, ws_bytes, dispatch_workspace_bytes(n_tokens, n_experts, top_k),
+               "moe_dispatch");
+  if (s != MOE_OK) return s;
+  return dispatch_launch(n_tokens, n_experts, top_k, n_cand, policy, capacity, cand_ids,
+                         cand_scores, gates, x, x_dt, d_model, counts_routed, counts_kept,
+                         offsets, row_of, expert_of, perm_token, x_perm, workspace,
+                         (hipStream_t)hip_stream);
 }
 
-moe_status moe_grouped_ffn(const moe_ffn_weights* w, const void* x_rows, moe_dtype act_dt,
-                           const int32_t* row_index, const int32_t* offsets, int32_t max_rows,
-                           void* y_rows, moe_dtype y_dt, void* workspace, size_t ws_bytes,
-                           void* hip_stream) {
+
+static moe_status check_ffn(const moe_ffn_weights* w, const void* x_rows, moe_dtype act_dt,
+                            const int32_t* offsets, int32_t max_rows, const void* y_rows,
+                            moe_dtype y_dt, void* workspace, size_t ws_bytes) {
   CHECK(w, MOE_EINVAL, "moe_grouped_ffn: weights is NULL");
   const int E = w->n_experts, d = w->d_model, F = w->d_ff;
   CHECK(E >= 1 && d >= 1 && F >= 1 && max_rows >= 1, MOE_EINVAL,
@@ -251,11 +302,45 @@ moe_status moe_grouped_ffn(const moe_ffn_weights* w, const void* x_rows, moe_dty
   } else {
     CHECK(0, MOE_EUNSUPPORTED, "moe_grouped_ffn: activation dtype %d", (int)act_dt);
   }
-  moe_status s = check_ws(workspace, ws_bytes, grouped_ffn_workspace_bytes(w, act_dt, max_rows),
-                          "moe_grouped_ffn");
+  return check_ws(workspace, ws_bytes, grouped_ffn_workspace_bytes(w, act_dt, max_rows),
+                  "moe_grouped_ffn");
+}
+
+moe_status moe_grouped_ffn(const moe_ffn_weights* w, const void* x_rows, moe_dtype act_dt,
+                           const int32_t* row_index, const int32_t* offsets, int32_t max_rows,
+                           void* y_rows, moe_dtype y_dt, void* workspace, size_t ws_bytes,
+                           void* hip_stream) {
+  const moe_status s = check_ffn(w, x_rows, act_dt, offsets, max_rows, y_rows, y_dt, workspace,
+                                 ws_bytes);
   if (s != MOE_OK) return s;
   return grouped_ffn_launch(w, x_rows, act_dt, row_index, offsets, max_rows, y_rows, y_dt,
                             workspace, (hipStream_t)hip_stream);
+}
+
+moe_status moe_grouped_ffn_combine_top1(const moe_ffn_weights* w, const void* x_rows,
+                                        moe_dtype act_dt, const int32_t* row_index,
+                                        const int32_t* offsets, int32_t max_rows,
+                                        int32_t n_tokens, const int32_t* perm_token,
+                                        const int32_t* row_of, const float* gates, float* y,
+                                        void* workspace, size_t ws_bytes, void* hip_stream) {
+  moe_status s = check_ffn(w, x_rows, act_dt, offsets, max_rows, y, MOE_F32, workspace,
+                           ws_bytes);
+  if (s != MOE_OK) return s;
+  CHECK(n_tokens >= 1 && perm_token && row_of && gates, MOE_EINVAL,
+        "moe_grouped_ffn_combine_top1: n_tokens %d, NULL perm_token/row_of/gates", n_tokens);
+  CHECK(max_rows <= n_tokens, MOE_EINVAL,
+        "moe_grouped_ffn_combine_top1: %d packed rows for %d tokens (top-1: at most one each)",
+        max_rows, n_tokens);
+  CHECK(w->w_dt != MOE_FP8_E4M3, MOE_EUNSUPPORTED,
+        "moe_grouped_ffn_combine_top1: fp8 experts take moe_grouped_ffn + moe_combine");
+  CHECK(w->d_model % 4 == 0, MOE_EUNSUPPORTED,
+        "moe_grouped_ffn_combine_top1: d_model %d %% 4 != 0", w->d_model);
+  const hipStream_t st = (hipStream_t)hip_stream;
+  float* gate_row = row_gates_ws(w, act_dt, max_rows, workspace);
+  s = combine_dropped_launch(n_tokens, w->d_model, row_of, gates, gate_row, y, st);
+  if (s != MOE_OK) return s;
+  return grouped_ffn_launch(w, x_rows, act_dt, row_index, offsets, max_rows, y, MOE_F32,
+                            workspace, st, nullptr, nullptr, perm_token, gate_row);
 }
 
 // ------------------------------------------------------------ training

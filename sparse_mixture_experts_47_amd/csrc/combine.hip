@@ -228,6 +228,34 @@ moe_status combine_backward_launch(int N, int d, int k, const float* dy, const v
 }
 
 
+// Top-1 combine done in the expert GEMM's epilogue, the part before it:
+// rows of tokens whose one assignment was dropped get zero output (the
+// residual is the caller's), and each kept token's gate goes to its packed
+// row (gate_row), where the epilogue that writes the token's row reads it.
+__global__ __launch_bounds__(kThreads) void combine_dropped_kernel(int d,
+                                                                   const int32_t* __restrict__ row_of,
+                                                                   const float* __restrict__ gates,
+                                                                   float* __restrict__ gate_row,
+                                                                   float* __restrict__ y) {
+  const int t = blockIdx.x;
+  const int r = row_of[t];
+  if (r >= 0) {
+    if (blockIdx.y == 0 && threadIdx.x == 0) gate_row[r] = gates[t];
+    return;
+  }
+  for (int c = (blockIdx.y * kThreads + threadIdx.x) * 4; c < d; c += gridDim.y * kThreads * 4)
+    *(f32x4_t*)(y + (size_t)t * d + c) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+}
+
+moe_status combine_dropped_launch(int N, int d, const int32_t* row_of, const float* gates,
+                                  float* gate_row, float* y, hipStream_t st) {
+  const int per = kThreads * 4;
+  int slices = (d + per - 1) / per;
+  slices = slices < 1 ? 1 : (slices > 8 ? 8 : slices);
+  combine_dropped_kernel<<<dim3(N, slices), kThreads, 0, st>>>(d, row_of, gates, gate_row, y);
+  return launch_status("combine (dropped tokens)");
+}
+
 moe_status combine_launch(int N, int d, int k, const void* y_rows, moe_dtype y_dt,
                           const int32_t* row_of, const float* gates, const void* y_shared,
                           moe_dtype sh_dt, void* y, moe_dtype out_dt, hipStream_t st) {

@@ -66,6 +66,13 @@ struct Args {
   // of 2 * Nrows (gate | up) or Nrows -- the state the backward pass
   // differentiates
   uint16_t* pre;
+  // OUT with fp32 output, or null: product row r is the only kept
+  // assignment of token c_rows[r] (top-1 routing), and the epilogue writes
+  // fmaf(c_gate[r], value, 0) to row c_rows[r] of C -- the gate-weighted
+  // combine, done where the expert output is made (c_gate: the gates in
+  // packed row order)
+  const int32_t* c_rows;
+  const float* c_gate;
 };
 
 __device__ __forceinline__ float act_fn(int act, float v) {
@@ -173,6 +180,23 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
   const int row_end = g.seg_end ? g.seg_end[e] : g.offsets[e + 1];
   const int n0 = nt * BN;
   const int K = g.K;
+  // top-1 combine: the token and gate of every row this lane will store,
+  // loaded now so that their latency hides behind the K loop
+  constexpr bool SCATTER = EPI == EPI_OUT && OUTK == OUT_F32;
+  int tokv[SCATTER ? FM : 1][4];
+  float gatev[SCATTER ? FM : 1][4];
+  if constexpr (SCATTER) {
+    if (g.c_rows) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = min(row0 + wm * WM + i * 32 + (lane >> 3) + 8 * q, row_end - 1);
+          tokv[i][q] = g.c_rows[row];
+          gatev[i][q] = g.c_gate[row];
+        }
+    }
+  }
   // 32-row blocks of this wave's rows that hold at least one row of the
   // group: the rest of a partly filled M tile needs no fragment reads and
   // no MFMAs (uniform per wave)
@@ -339,10 +363,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
   // consecutive columns per lane, so the global stores are 16 bytes (fp32)
   // or 8 (bf16) a lane and one instruction covers 8 whole row segments.
   static_assert(NS * STAGE * 2 >= NW * 32 * 36 * 4, "LDS for the staged epilogue");
+  const int rq = lane >> 3, c4 = (lane & 7) * 4;
   __syncthreads();  // every wave is done with the operand stages
   constexpr int SP = 36;
   float* stage = (float*)smem + wave * 32 * SP;
-  const int rq = lane >> 3, c4 = (lane & 7) * 4;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -378,8 +402,16 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
         const int br = rq + 8 * q;
         const int row = row0 + wm * WM + i * 32 + br;
         if (row >= row_end || col >= g.n_valid) continue;
-        const f32x4_t v = *(const f32x4_t*)(stage + br * SP + c4);
-        const size_t o = (size_t)row * g.ldc + col;
+        f32x4_t v = *(const f32x4_t*)(stage + br * SP + c4);
+        size_t o = (size_t)row * g.ldc + col;
+        if constexpr (SCATTER) {
+          if (g.c_rows) {
+            const float gt = gatev[i][q];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) v[t] = __builtin_fmaf(gt, v[t], 0.f);
+            o = (size_t)tokv[i][q] * g.ldc + col;
+          }
+        }
         if (col + 4 <= g.n_valid) {
           if (OUTK == OUT_F32) {
             *(f32x4_t*)((float*)Cb + o) = v;

@@ -106,6 +106,10 @@ struct GemmArgs {
   const int32_t* offsets;
   const int32_t* tile_start;
   const int32_t* a_rows;  // product row r reads A row a_rows[r], or r if null
+  // MODE_OUT, or null: write fmaf(c_gate[r], value, 0) to row c_rows[r]
+  // of C (top-1 combine in the epilogue; c_gate in packed row order)
+  const int32_t* c_rows;
+  const float* c_gate;
 };
 
 // Expert of M tile `mt`: tile_start[e] <= mt < tile_start[e+1].
@@ -214,7 +218,12 @@ __global__ __launch_bounds__(256) void ggemm_f32_kernel(GemmArgs g) {
         v = acc[0][i][j] + bv;
         if (MODE == MODE_ACT) v = act_fn(g.act, v);
       }
-      ((float*)g.C)[(size_t)row * Nout + col] = v;
+      size_t orow = row;
+      if (MODE == MODE_OUT && g.c_rows) {
+        orow = g.c_rows[row];
+        v = __builtin_fmaf(g.c_gate[row], v, 0.f);
+      }
+      ((float*)g.C)[orow * Nout + col] = v;
     }
   }
 }
@@ -871,15 +880,24 @@ static TileTables tile_tables(char* base, int E, int max_rows) {
   return t;
 }
 
+// After the tile tables: the gates in packed row order [max_rows] fp32 (top-1
+// combine in GEMM 2's epilogue).
 size_t grouped_ffn_workspace_bytes(const moe_ffn_weights* w, moe_dtype act_dt, int max_rows) {
   return h_bytes(w, act_dt, max_rows) +
-         align256(table_ints(w->n_experts, max_rows) * sizeof(int32_t));
+         align256(table_ints(w->n_experts, max_rows) * sizeof(int32_t)) +
+         align256((size_t)max_rows * sizeof(float));
+}
+
+float* row_gates_ws(const moe_ffn_weights* w, moe_dtype act_dt, int max_rows, void* ws) {
+  return (float*)((char*)ws + h_bytes(w, act_dt, max_rows) +
+                  align256(table_ints(w->n_experts, max_rows) * sizeof(int32_t)));
 }
 
 moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_dtype act_dt,
                               const int32_t* row_index, const int32_t* offsets, int max_rows,
                               void* y_rows, moe_dtype y_dt, void* workspace, hipStream_t st,
-                              uint16_t* preact, uint16_t* h_out) {
+                              uint16_t* preact, uint16_t* h_out, const int32_t* out_token,
+                              const float* out_gate) {
   const int E = w->n_experts, d = w->d_model, F = w->d_ff;
   char* ws = (char*)workspace;
   // training: h goes to the caller's buffer (it is an operand of the weight
@@ -945,9 +963,9 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
 
   if (act_dt == MOE_F32) {
     GemmArgs a1{x_rows, w->w1, w->w3, w->b1, h, d, F, E, max_mt, (int)w->act, offsets,
-                tile_start, row_index};
+                tile_start, row_index, nullptr, nullptr};
     GemmArgs a2{h, w->w2, nullptr, w->b2, y_rows, F, d, E, max_mt, (int)w->act, offsets,
-                tile_start, nullptr};
+                tile_start, nullptr, out_token, out_gate};
     const int g1 = max_mt * ((F + 63) / 64), g2 = max_mt * ((d + 63) / 64);
     if (glu)
       ggemm_f32_kernel<MODE_GLU><<<g1, 256, 0, st>>>(a1);
@@ -971,6 +989,8 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
   Args g2 = base_args(h, w->w2, nullptr, w->b2, y_rows, F, d, E, max_mt, (int)w->act, offsets,
                       tt.ts);
   g2.group_n = MOE_G2_GN;
+  g2.c_rows = out_token;
+  g2.c_gate = out_gate;
   g2.seg_begin = tt.sb;
   g2.seg_end = tt.se;
   g2.tile_e = tt.te;

@@ -49,6 +49,14 @@ int main(void) {
                       (float*)fake, NULL, MOE_BF16, 0, (int32_t*)fake, (int32_t*)fake,
                       (int32_t*)fake, (int32_t*)fake, (int32_t*)fake, (int32_t*)fake, NULL,
                       fake, (size_t)1 << 30, NULL) == MOE_EINVAL);
+  /* router weight planes: 3 planes of E (or 2E) rows padded to 64 */
+  EXPECT(moe_router_planes_bytes(8, 4096, 0) == (size_t)3 * 64 * 4096 * 2);
+  EXPECT(moe_router_planes_bytes(64, 1024, 1) == (size_t)3 * 128 * 1024 * 2);
+  EXPECT(moe_router_prepare((const float*)fake, NULL, 8, 100, fake, (size_t)1 << 30, NULL) ==
+         MOE_EINVAL);
+  EXPECT(moe_router_prepare((const float*)fake, NULL, 8, 64, fake, 16, NULL) == MOE_EWORKSPACE);
+  EXPECT(moe_router_prepare((const float*)fake, NULL, 300, 64, fake, (size_t)1 << 30, NULL) ==
+         MOE_EUNSUPPORTED);
   EXPECT(strlen(moe_status_string(MOE_EWORKSPACE)) > 0);
   EXPECT(strlen(moe_version()) > 0);
   printf("ok %s\n", moe_version());

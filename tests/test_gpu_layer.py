@@ -119,7 +119,8 @@ def test_level2_router_gemm(moe, key):
 
 
 @pytest.mark.parametrize("N,d,E,seed", [(300, 64, 64, 44), (130, 128, 16, 0xDEADBEEFCAFEBABE),
-                                         (65, 64, 256, 7)])
+                                         (65, 64, 256, 7), (300, 256, 64, 44),
+                                         (16400, 256, 32, 5), (17, 512, 8, 3)])
 def test_noisy_logits_bit_exact(moe, N, d, E, seed):
     """Noisy gating H = l + z*softplus(v) (chiang97912 notes, "KeepTopK 策略"),
     bit for bit against the oracle. x, W_g and W_noise hold small integers,
@@ -152,6 +153,62 @@ def test_noisy_logits_bit_exact(moe, N, d, E, seed):
     # selection on top of the identical H is the oracle's too
     r = oracle.route(H_ref, 1, C, False)
     assert np.array_equal(to_np(cand), r["cand_ids"])
+
+
+@pytest.mark.parametrize("key,n", [("c1", 256), ("c4", 2000), ("c4", 37), ("c2", 600)])
+def test_top1_combine_in_epilogue_matches_combine(moe, key, n):
+    """Top-1 routing: the combine done in GEMM 2's epilogue gives the same
+    bits as the grouped FFN into packed rows followed by moe_combine (fp32
+    SIMT path for the tiny Switch layer, the bf16-pair GEMM 2 for the skewed
+    one with 53% of its tokens dropped, a top-1 variant of the Mixtral
+    shape on the plain bf16 GEMM 2)."""
+    cfg = W.REDUCED[key].with_(n_tokens=n)
+    if cfg.top_k != 1:
+        cfg = cfg.with_(top_k=1, renormalize=False, overflow=W.DROP, capacity_factor=1.0)
+    inp = W.make_inputs(cfg, "cpu")
+    dev = to_device(inp)
+    spec = moe.spec_from_config(cfg)
+    xdt = torch.float32 if cfg.x_dtype == W.F32 else torch.bfloat16
+    fused = moe.MoELayer(spec, dev, x_dtype=xdt)
+    plain = moe.MoELayer(spec, dev, x_dtype=xdt, fuse_combine=False)
+    assert fused.fused_combine and not plain.fused_combine
+    fused.y.fill_(float("nan"))
+    y1 = fused.forward(dev["x"]).clone()
+    y2 = plain.forward(dev["x"])
+    torch.cuda.synchronize()
+    dropped = int((to_np(plain.row_of) < 0).sum())
+    print("  tokens", n, "dropped", dropped, flush=True)
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
+@pytest.mark.parametrize("N,d,E,noise", [(600, 512, 8, False), (16400, 256, 64, True),
+                                          (333, 1024, 64, False), (257, 512, 256, False),
+                                          (100, 192, 16, True)])
+def test_router_prepared_planes_match_per_call_split(moe, N, d, E, noise):
+    """The router with weight planes from moe_router_prepare gives the same
+    bits as the router that splits the weights itself on every call (fused
+    kernel for up to 64 experts, split-K GEMM and select kernel beyond)."""
+    g = torch.Generator().manual_seed(N + d + E)
+    x = torch.randn((N, d), generator=g).to(torch.bfloat16).cuda()
+    wg = (torch.randn((E, d), generator=g) * 0.02).cuda()
+    wn = (torch.randn((E, d), generator=g) * 0.02).cuda() if noise else None
+    k = 2 if E >= 2 else 1
+    outs = []
+    for planes in (None, moe.moe_router_prepare(wg, wn)):
+        o = dict(cand_ids=torch.empty((N, k), dtype=torch.int32, device="cuda"),
+                 cand_scores=torch.empty((N, k), device="cuda"),
+                 gates=torch.empty((N, k), device="cuda"),
+                 logits_out=torch.empty((N, E), device="cuda"),
+                 score_sums=torch.empty(E + 1, dtype=torch.float64, device="cuda"))
+        moe.moe_router_topk(x, wg, top_k=k, w_noise=wn, noise_seed=9, w_planes=planes, **o)
+        torch.cuda.synchronize()
+        outs.append({kk: v.cpu() for kk, v in o.items()})
+    for kk in outs[0]:
+        assert torch.equal(outs[0][kk], outs[1][kk]), kk
+    # and the logits are the oracle's within the fp32 accumulation bar
+    H, _ = oracle.router_logits(W.bits_u16(x.cpu()), W.BF16, wg.cpu().numpy(), None,
+                                None if wn is None else wn.cpu().numpy(), 9)
+    assert rel_err(outs[0]["logits_out"].numpy(), H) <= TOL_REL
 
 
 @pytest.mark.parametrize("E,k,C,N,scale", [(5, 2, 3, 37, 1.0), (100, 8, 8, 70, 1.5),
