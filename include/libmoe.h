@@ -189,6 +189,25 @@ moe_status moe_dispatch(int32_t n_tokens, int32_t n_experts, int32_t top_k, int3
                         void* hip_stream);
 size_t moe_dispatch_workspace_bytes(int32_t n_tokens, int32_t n_experts, int32_t top_k);
 
+/* moe_dispatch for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and errors as moe_dispatch, without the
+ * workspace: its scratch is a fixed device array inside libmoe, one per GPU,
+ * MOE_DISPATCH_NOALLOC_SCRATCH_BYTES long and held until the process ends;
+ * no call allocates. Sizes whose moe_dispatch_workspace_bytes exceed it are
+ * rejected with MOE_EWORKSPACE before any launch (4 MiB covers, e.g., the
+ * DeepSeek-shaped 8192 tokens x top-8 over 256 experts, 0.8 MB). Every call
+ * on one GPU shares that GPU's array: calls that overlap on the same GPU
+ * (other streams, other threads) race; calls in stream order do not (no
+ * part of the array has to start at zero). */
+#define MOE_DISPATCH_NOALLOC_SCRATCH_BYTES (4u << 20)
+moe_status moe_dispatch_noalloc(int32_t n_tokens, int32_t n_experts, int32_t top_k,
+                                int32_t n_cand, moe_overflow policy, int32_t capacity,
+                                const int32_t* cand_ids, const float* cand_scores, float* gates,
+                                const void* x, moe_dtype x_dt, int32_t d_model,
+                                int32_t* counts_routed, int32_t* counts_kept, int32_t* offsets,
+                                int32_t* row_of, int32_t* expert_of, int32_t* perm_token,
+                                void* x_perm, void* hip_stream);
 
 /* capacity = ceil(n_tokens / n_experts * capacity_factor) (chiang97912
  * "专家容量": tokens per batch / number of experts x capacity factor; the

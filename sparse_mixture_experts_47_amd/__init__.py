@@ -74,6 +74,9 @@ def _load():
     L.moe_dispatch.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, i32, i32, P, P, P, P,
                                P, P, P, P, sz, P]
     L.moe_dispatch.restype = i32
+    L.moe_dispatch_noalloc.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, i32, i32, P, P,
+                                       P, P, P, P, P, P]
+    L.moe_dispatch_noalloc.restype = i32
     L.moe_dispatch_workspace_bytes.argtypes = [i32, i32, i32]
     L.moe_dispatch_workspace_bytes.restype = sz
     L.moe_capacity.argtypes = [i32, i32, i32, i32]
@@ -228,6 +231,23 @@ def moe_dispatch(cand_ids, cand_scores, gates, *, n_experts, top_k, policy=DROPL
                             _ptr(counts_kept), _ptr(offsets), _ptr(row_of), _ptr(expert_of),
                             _ptr(perm_token), _ptr(x_perm), _ptr(ws), ws.numel(),
                             _stream(stream)))
+
+
+def moe_dispatch_noalloc(cand_ids, cand_scores, gates, *, n_experts, top_k, policy=DROPLESS,
+                         capacity=-1, x=None, counts_routed, counts_kept, offsets, row_of,
+                         expert_of, perm_token, x_perm=None, stream=None):
+    """moe_dispatch with the library's fixed scratch instead of a workspace
+    (no device allocation anywhere in the call)."""
+    N, C = cand_ids.shape
+    _dev_check(cand_ids, cand_scores, gates, x, counts_routed, counts_kept, offsets, row_of,
+               expert_of, perm_token, x_perm)
+    d = x.shape[1] if x is not None else 0
+    _check(lib.moe_dispatch_noalloc(N, n_experts, top_k, C, policy, capacity, _ptr(cand_ids),
+                                    _ptr(cand_scores), _ptr(gates), _ptr(x),
+                                    _dt(x) if x is not None else F32, d, _ptr(counts_routed),
+                                    _ptr(counts_kept), _ptr(offsets), _ptr(row_of),
+                                    _ptr(expert_of), _ptr(perm_token), _ptr(x_perm),
+                                    _stream(stream)))
 
 
 def moe_expert_choice(scores, capacity, *, offsets, perm_token, row_of, gates, counts=None,

@@ -17,6 +17,7 @@ moe_status router_launch(const moe_router_params* p, const void* x, moe_dtype x_
                          float* cand_scores, float* gates, float* logits_out,
                          double* score_sums, void* workspace, hipStream_t st);
 size_t dispatch_workspace_bytes(int N, int E, int k);
+moe_status dispatch_scratch_ptr(void** out);
 moe_status dispatch_launch(int N, int E, int k, int C, moe_overflow policy, int cap,
                            const int32_t* cand, const float* cand_s, float* gates,
                            const void* x, moe_dtype x_dt, int d, int32_t* counts_routed,
@@ -269,6 +270,31 @@ moe_status moe_dispatch(int32_t n_tokens, int32_t n_experts, int32_t top_k, int3
                          (hipStream_t)hip_stream);
 }
 
+moe_status moe_dispatch_noalloc(int32_t n_tokens, int32_t n_experts, int32_t top_k,
+                                int32_t n_cand, moe_overflow policy, int32_t capacity,
+                                const int32_t* cand_ids, const float* cand_scores, float* gates,
+                                const void* x, moe_dtype x_dt, int32_t d_model,
+                                int32_t* counts_routed, int32_t* counts_kept, int32_t* offsets,
+                                int32_t* row_of, int32_t* expert_of, int32_t* perm_token,
+                                void* x_perm, void* hip_stream) {
+  moe_status s = check_dispatch("moe_dispatch_noalloc", n_tokens, n_experts, top_k, n_cand,
+                                policy, capacity, cand_ids, cand_scores, gates, x, x_dt,
+                                d_model, counts_routed, counts_kept, offsets, row_of,
+                                expert_of, perm_token, x_perm);
+  if (s != MOE_OK) return s;
+  const size_t need = dispatch_workspace_bytes(n_tokens, n_experts, top_k);
+  CHECK(need <= (size_t)MOE_DISPATCH_NOALLOC_SCRATCH_BYTES, MOE_EWORKSPACE,
+        "moe_dispatch_noalloc: N=%d E=%d k=%d needs %zu bytes of scratch, more than the "
+        "library's fixed %zu (use moe_dispatch with a workspace)",
+        n_tokens, n_experts, top_k, need, (size_t)MOE_DISPATCH_NOALLOC_SCRATCH_BYTES);
+  void* scratch = nullptr;
+  s = dispatch_scratch_ptr(&scratch);
+  if (s != MOE_OK) return s;
+  return dispatch_launch(n_tokens, n_experts, top_k, n_cand, policy, capacity, cand_ids,
+                         cand_scores, gates, x, x_dt, d_model, counts_routed, counts_kept,
+                         offsets, row_of, expert_of, perm_token, x_perm, scratch,
+                         (hipStream_t)hip_stream);
+}
 
 static moe_status check_ffn(const moe_ffn_weights* w, const void* x_rows, moe_dtype act_dt,
                             const int32_t* offsets, int32_t max_rows, const void* y_rows,

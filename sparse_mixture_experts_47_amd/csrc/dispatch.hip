@@ -10,6 +10,8 @@
 // (every first choice in ascending token order, then every second choice,
 // ...): per-block histograms, an ordered scan over blocks, and in-wave ranks
 // from ballots over the expert id's bits. No atomic decides any position.
+#include <mutex>
+
 #include "moe_device.h"
 
 namespace {
@@ -271,6 +273,49 @@ moe_status dispatch_launch(int N, int E, int k, int C, moe_overflow policy, int 
   gather_rows_kernel<<<grid, kThreads, 0, st>>>((const u32x4_t*)x, perm_token, offsets, E,
                                                 chunks, (u32x4_t*)x_perm);
   return launch_status("dispatch gather");
+}
+
+// ---------------------------------------------------------------- no-alloc
+// Scratch for moe_dispatch_noalloc: a file-scope device array, one copy per
+// GPU the library runs on, held until the process ends. Host code never
+// passes the array's name to a kernel (on the host it is a stand-in, not a
+// device address): the address comes from hipGetSymbolAddress, once per
+// device with that device current, and is kept per device. Every
+// dispatch kernel writes each scratch word it later reads, so nothing needs
+// clearing between calls; calls that overlap on one GPU share the array and
+// race.
+static __device__ __align__(256) char dispatch_scratch[MOE_DISPATCH_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+moe_status dispatch_scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    set_error("moe_dispatch_noalloc: hipGetDevice failed: %s", hipGetErrorString(e));
+    return MOE_EHIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    set_error("moe_dispatch_noalloc: device %d beyond the %d supported", dev, kMaxDevices);
+    return MOE_EUNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(dispatch_scratch));
+    if (e != hipSuccess || !p) {
+      set_error("moe_dispatch_noalloc: hipGetSymbolAddress of the scratch array failed: %s",
+                hipGetErrorString(e));
+      return MOE_EHIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
 }
 
 }  // namespace moe_host
