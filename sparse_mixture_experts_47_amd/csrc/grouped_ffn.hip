@@ -980,7 +980,13 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
   const bool ybf = y_dt == MOE_BF16;
   Args g1 = base_args(x_rows, w->w1, w->w3, w->b1, h, d, F, E, max_mt, (int)w->act, offsets,
                       tt.ts);
-  g1.group_n = MOE_G1_GN;
+  // N tiles per group of the XCD-aware order. 256-row tiles (the prefill
+  // shapes): 8 for a few large experts, 4 for many (GEMM pair on the
+  // Mixtral shape 2.91 -> 2.86 ms and 2.77 -> 2.68 ms with expert choice,
+  // groups of 2; one GPU's EP-8 DeepSeek share 6.09 ms with 2 or 4, 6.26
+  // with 8; the DeepSeek-shaped layer 7.98 -> 7.86 ms with 4)
+  const int gn256 = E <= 16 ? 8 : 4;
+  g1.group_n = bm == 256 ? gn256 : MOE_G1_GN;
   g1.a_rows = row_index;
   g1.pre = preact;
   g1.seg_begin = tt.sb;
@@ -988,7 +994,7 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
   g1.tile_e = tt.te;
   Args g2 = base_args(h, w->w2, nullptr, w->b2, y_rows, F, d, E, max_mt, (int)w->act, offsets,
                       tt.ts);
-  g2.group_n = MOE_G2_GN;
+  g2.group_n = bm == 256 ? gn256 : MOE_G2_GN;
   g2.c_rows = out_token;
   g2.c_gate = out_gate;
   g2.seg_begin = tt.sb;
