@@ -133,7 +133,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Output kinds of the direct-LDS kernel.
-enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_BF16_PAIR = 2 };
+// OUT_F32_SCATTER: fp32, each product row to the token row c_rows[r], times
+// its gate (the top-1 combine; its own instance so that the plain fp32 GEMM
+// keeps no registers for the tokens and gates)
+enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_BF16_PAIR = 2, OUT_F32_SCATTER = 3 };
 
 // NA A planes (bf16, plane p at A + p * a_plane elements): NA = 2 is an fp32
 // operand kept as hi + lo bf16 parts. OUT_BF16_PAIR writes the result the
@@ -182,11 +185,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
   const int K = g.K;
   // top-1 combine: the token and gate of every row this lane will store,
   // loaded now so that their latency hides behind the K loop
-  constexpr bool SCATTER = EPI == EPI_OUT && OUTK == OUT_F32;
+  constexpr bool SCATTER = EPI == EPI_OUT && OUTK == OUT_F32_SCATTER;
+  static_assert(OUTK != OUT_F32_SCATTER || EPI == EPI_OUT, "scatter is the output GEMM's");
   int tokv[SCATTER ? FM : 1][4];
   float gatev[SCATTER ? FM : 1][4];
   if constexpr (SCATTER) {
-    if (g.c_rows) {
+    {
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -355,7 +359,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
     else k_loop(std::false_type{});
   }
 
-  constexpr int OB = OUTK == OUT_F32 ? 4 : 2;
+  constexpr bool F32OUT = OUTK == OUT_F32 || OUTK == OUT_F32_SCATTER;
+  constexpr int OB = F32OUT ? 4 : 2;
   char* Cb = (char*)g.C + (size_t)blockIdx.y * g.c_split * OB;
   // Epilogue, staged through LDS: each 32 x 32 block of results goes to a
   // wave-private patch (rows padded to 36 floats: 16-byte aligned, and the
@@ -405,15 +410,13 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
         f32x4_t v = *(const f32x4_t*)(stage + br * SP + c4);
         size_t o = (size_t)row * g.ldc + col;
         if constexpr (SCATTER) {
-          if (g.c_rows) {
-            const float gt = gatev[i][q];
+          const float gt = gatev[i][q];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) v[t] = __builtin_fmaf(gt, v[t], 0.f);
-            o = (size_t)tokv[i][q] * g.ldc + col;
-          }
+          for (int t = 0; t < 4; ++t) v[t] = __builtin_fmaf(gt, v[t], 0.f);
+          o = (size_t)tokv[i][q] * g.ldc + col;
         }
         if (col + 4 <= g.n_valid) {
-          if (OUTK == OUT_F32) {
+          if (F32OUT) {
             *(f32x4_t*)((float*)Cb + o) = v;
           } else {
             uint16_t hb[4];
@@ -432,7 +435,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
           }
         } else {
           for (int t = 0; t < 4 && col + t < g.n_valid; ++t) {
-            if (OUTK == OUT_F32) {
+            if (F32OUT) {
               ((float*)Cb)[o + t] = v[t];
             } else {
               const uint16_t hi = moe::f32_to_bf16_bits(v[t]);

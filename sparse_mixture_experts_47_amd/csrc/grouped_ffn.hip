@@ -789,8 +789,8 @@ hipError_t launch_g1(bool glu, bool pair, const moe_gemm::Args& g1, hipStream_t 
               : run_gemm<BM, 64, 1, 1, EPI_ACT, OUT_BF16>(g1, 1, st);
 }
 
-template <int BM>
-hipError_t launch_g2(bool pair, bool ybf, const moe_gemm::Args& g2, hipStream_t st) {
+template <int BM, int OF32>
+hipError_t launch_g2_k(bool pair, bool ybf, const moe_gemm::Args& g2, hipStream_t st) {
   using namespace moe_gemm;
   const bool n2 = g2.Nrows % 128 == 0;
   if (pair) {
@@ -800,27 +800,36 @@ hipError_t launch_g2(bool pair, bool ybf, const moe_gemm::Args& g2, hipStream_t 
       if (g2.Nrows % 256 == 0)
         return ybf ? run_gemm<BM, 256, 2, 1, EPI_OUT, OUT_BF16, 4, MOE_G2_PAIR256_BK, 2,
                               MOE_G2_PAIR_LDS>(gp, 1, st)
-                   : run_gemm<BM, 256, 2, 1, EPI_OUT, OUT_F32, 4, MOE_G2_PAIR256_BK, 2,
+                   : run_gemm<BM, 256, 2, 1, EPI_OUT, OF32, 4, MOE_G2_PAIR256_BK, 2,
                               MOE_G2_PAIR_LDS>(gp, 1, st);
     }
     if constexpr (MOE_G2_PAIR_BN == 128) {
       if (n2)
         return ybf ? run_gemm<BM, 128, 2, 1, EPI_OUT, OUT_BF16, MOE_G2_PAIR_WGN>(gp, 1, st)
-                   : run_gemm<BM, 128, 2, 1, EPI_OUT, OUT_F32, MOE_G2_PAIR_WGN>(gp, 1, st);
+                   : run_gemm<BM, 128, 2, 1, EPI_OUT, OF32, MOE_G2_PAIR_WGN>(gp, 1, st);
     }
     return ybf ? run_gemm<BM, 64, 2, 1, EPI_OUT, OUT_BF16, 2, MOE_GEMM_BK, MOE_G2_PAIR_WGM>(gp, 1, st)
-               : run_gemm<BM, 64, 2, 1, EPI_OUT, OUT_F32, 2, MOE_GEMM_BK, MOE_G2_PAIR_WGM>(gp, 1, st);
+               : run_gemm<BM, 64, 2, 1, EPI_OUT, OF32, 2, MOE_GEMM_BK, MOE_G2_PAIR_WGM>(gp, 1, st);
   }
   if (MOE_G2_WIDE && BM == 256 && g2.Nrows % 256 == 0)
     return ybf ? run_gemm<BM, 256, 1, 1, EPI_OUT, OUT_BF16, MOE_G2_WIDE_WGN, MOE_GEMM_BK,
                           MOE_G2_WIDE_WGM>(g2, 1, st)
-               : run_gemm<BM, 256, 1, 1, EPI_OUT, OUT_F32, MOE_G2_WIDE_WGN, MOE_GEMM_BK,
+               : run_gemm<BM, 256, 1, 1, EPI_OUT, OF32, MOE_G2_WIDE_WGN, MOE_GEMM_BK,
                           MOE_G2_WIDE_WGM>(g2, 1, st);
   if (n2)
     return ybf ? run_gemm<BM, 128, 1, 1, EPI_OUT, OUT_BF16, MOE_G2_WGN>(g2, 1, st)
-               : run_gemm<BM, 128, 1, 1, EPI_OUT, OUT_F32, MOE_G2_WGN>(g2, 1, st);
+               : run_gemm<BM, 128, 1, 1, EPI_OUT, OF32, MOE_G2_WGN>(g2, 1, st);
   return ybf ? run_gemm<BM, 64, 1, 1, EPI_OUT, OUT_BF16>(g2, 1, st)
              : run_gemm<BM, 64, 1, 1, EPI_OUT, OUT_F32>(g2, 1, st);
+}
+
+// GEMM 2 with fp32 output into packed rows, or (c_rows set) scattered to
+// token rows with the gate applied
+template <int BM>
+hipError_t launch_g2(bool pair, bool ybf, const moe_gemm::Args& g2, hipStream_t st) {
+  using namespace moe_gemm;
+  if (g2.c_rows) return launch_g2_k<BM, OUT_F32_SCATTER>(pair, false, g2, st);
+  return launch_g2_k<BM, OUT_F32>(pair, ybf, g2, st);
 }
 
 moe_gemm::Args base_args(const void* A, const void* B0, const void* B1, const float* bias,
