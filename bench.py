@@ -708,6 +708,7 @@ def main():
         "touched_experts": touched,
         "kept_assignments": int(counts.sum()),
         "per_call_gbs": per_call_gbs(cfg, layer, counts, samples),
+        "library": os.path.relpath(moe.LIB_PATH, ROOT),
     }
     if args.copy_calibration:
         # a plain streaming kernel of known size for HBM counter calibration:

@@ -489,6 +489,40 @@ def test_grouped_ffn_fp32_h_column_tilings(moe, d_model):
     assert np.all(got[R:] == 7.0)
 
 
+@pytest.mark.parametrize("act", [W.ACT_SWIGLU, W.ACT_GELU])
+def test_grouped_ffn_fp32_h_256_row_tiles(moe, act):
+    """fp32 h (hi + lo bf16 planes) when experts average 512 rows or more:
+    256-row tiles with the gated (SwiGLU) or plain activation epilogue
+    writing the bf16 pair, the pair GEMM 2 on 256-row tiles, and the 128-row
+    tail launches of both GEMMs. Experts: empty, one partly filled 256-row
+    tile (700 rows), a 66-row tail (1090) and a one-row tail (513); rows
+    gathered through a row index."""
+    base = W.REDUCED["c2"]
+    cfg = base.with_(name="fp32h_256_rows", n_tokens=1200, n_experts=4, act=act)
+    print("fp32 h, 256-row tiles, act", act, flush=True)
+    inp = W.make_inputs(cfg, "cpu")
+    host = host_inputs(inp)
+    dev = to_device(inp)
+    counts = np.array([0, 700, 1090, 513])
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offs[-1])
+    assert R // cfg.n_experts >= 512
+    tok = np.random.default_rng(act).integers(0, cfg.n_tokens, size=R)
+    y = torch.full((R + 5, cfg.d_model), 7.0, dtype=torch.float32, device="cuda")
+    w, keep = moe.ffn_weights(dev["w1"], dev["w2"], dev["w3"], cfg.act, h_fp32=True)
+    moe.moe_grouped_ffn(w, dev["x"], torch.from_numpy(offs).cuda(), y,
+                        row_index=torch.from_numpy(tok.astype(np.int32)).cuda(), max_rows=R)
+    torch.cuda.synchronize()
+    X64 = oracle.decode_rows(host["x"][tok], cfg.x_dtype)
+    ref = oracle.ffn_for_assignments(np.arange(R), np.repeat(np.arange(cfg.n_experts), counts),
+                                     X64, cfg.act, cfg.w_dtype, experts_of(host))
+    got = to_np(y)
+    err = rel_err(got[:R], ref)
+    print("  max|dy|/rms =", err, flush=True)
+    assert err <= 1e-3
+    assert np.all(got[R:] == 7.0)
+
+
 @pytest.mark.parametrize("key", ["c2", "c4", "c5", "c1"])
 def test_fused_gather_matches_explicit_gather(moe, key):
     """GEMM 1 reading token rows through perm_token gives bit-identical
