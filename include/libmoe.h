@@ -19,8 +19,9 @@
  *    and owns (e.g. torch tensors' data_ptr()). libmoe allocates no device
  *    memory and keeps no state between calls; scratch space comes from the
  *    caller's `workspace` (size from the matching *_workspace_bytes query,
- *    alignment 256 bytes). Parameter structs are HOST memory, read during
- *    the call only.
+ *    alignment 256 bytes) -- except moe_dispatch_noalloc, whose scratch is a
+ *    fixed array inside the library (see there). Parameter structs are HOST
+ *    memory, read during the call only.
  *  - Layouts are row-major and dense. bf16 is the upper half of an IEEE
  *    binary32; fp8 is OCP E4M3FN (bias 7, max 448, no infinities).
  *  - Every call enqueues its kernels on `hip_stream` (a hipStream_t; NULL is
