@@ -134,11 +134,11 @@ __global__ __launch_bounds__(kThreads) void combine_wide_kernel(int d, int k,
 template <typename YT, typename ST, typename OT>
 void launch_combine(int N, int d, int k, const void* yr, const int32_t* row_of,
                     const float* gates, const void* ysh, void* y, hipStream_t st) {
-  // column slices per token: enough blocks for the chip when tokens are few
-  const int chunks = (d + kThreads * 8 - 1) / (kThreads * 8);
-  int slices = 1;
-  while (slices < chunks && (long long)N * slices < 1024) slices *= 2;
-  if (slices > chunks) slices = chunks;
+  // one column slice per 2048 features: each thread combines one 8-feature
+  // chunk of one token (more blocks in flight than looping over the slices:
+  // DeepSeek-shaped combine 0.448 -> 0.431 ms, Mixtral 0.037 -> 0.035 ms),
+  // and a few tokens (decode) still fill the chip
+  const int slices = (d + kThreads * 8 - 1) / (kThreads * 8);
   const dim3 grid(N, slices);
   if (k <= 8)
     combine_kernel<YT, ST, OT><<<grid, kThreads, 0, st>>>(d, k, (const YT*)yr, row_of, gates,
