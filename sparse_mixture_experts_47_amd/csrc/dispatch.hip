@@ -188,6 +188,119 @@ __global__ __launch_bounds__(kThreads) void disp_scatter_kernel(ScatterArgs s) {
   }
 }
 
+// The whole dispatch in one workgroup for small problems (N*k <= 8192, no
+// reroute): the same stable counting sort in rank-major item order. Every
+// key is loaded up front (8 per thread, rank-major item a = c*1024 + tid);
+// then the items are taken 1024 at a time in order: ranks inside a wave
+// from ballots over the key bits, each wave's per-expert count in LDS, and
+// per expert an exclusive prefix over the waves plus the count carried from
+// the earlier chunks. Capacity, kept counts, offsets and the scatter follow
+// in the same workgroup, without the five launches of the general path
+// (decode and small batches are launch-bound).
+constexpr int kSmallThreads = 1024, kSmallWaves = kSmallThreads / MOE_WAVE;
+constexpr int kSmallMaxItems = 8192, kSmallChunks = kSmallMaxItems / kSmallThreads;
+
+__global__ __launch_bounds__(kSmallThreads) void disp_small_kernel(
+    int N, int E, int k, int C, int policy, int cap, const int32_t* __restrict__ cand,
+    float* __restrict__ gates, int32_t* __restrict__ counts_routed,
+    int32_t* __restrict__ counts_kept, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ row_of, int32_t* __restrict__ expert_of,
+    int32_t* __restrict__ perm_token) {
+  __shared__ int key_s[kSmallMaxItems];   // rank-major keys
+  __shared__ int slot_s[kSmallMaxItems];  // rank-major slots (-1: dropped / no key)
+  __shared__ int wcnt[kSmallWaves][256];  // this chunk's count per wave and expert
+  __shared__ int wpre[kSmallWaves][256];  // items of the expert before this wave
+  __shared__ int off_s[256];              // inclusive scan of the kept counts
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int A = N * k;
+  int bits = 1;
+  while ((1 << bits) < E) ++bits;
+  int key[kSmallChunks];
+#pragma unroll
+  for (int c = 0; c < kSmallChunks; ++c) {
+    const int a = c * kSmallThreads + tid;
+    key[c] = -1;
+    if (a < A) {
+      const int j = a / N, t = a - j * N;
+      key[c] = cand[(size_t)t * C + j];
+    }
+  }
+  for (int i = tid; i < kSmallWaves * 256; i += kSmallThreads) (&wcnt[0][0])[i] = 0;
+  int running = 0;  // thread e < E: items of expert e in the chunks so far
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < kSmallChunks; ++c) {
+    if (c * kSmallThreads >= A) break;  // uniform
+    const int a = c * kSmallThreads + tid;
+    const int kc = key[c];
+    const bool valid = kc >= 0;
+    uint64_t m = __ballot(valid);
+    for (int b = 0; b < bits; ++b) {
+      const bool bit = (kc >> b) & 1;
+      const uint64_t bal = __ballot(bit);
+      m &= bit ? bal : ~bal;
+    }
+    const int rank = __popcll(m & moe::lanemask_lt());
+    if (valid && rank == 0) wcnt[wave][kc] = __popcll(m);
+    __syncthreads();
+    if (tid < E) {
+      int v[kSmallWaves];
+#pragma unroll
+      for (int w = 0; w < kSmallWaves; ++w) v[w] = wcnt[w][tid];
+#pragma unroll
+      for (int w = 0; w < kSmallWaves; ++w) {
+        wpre[w][tid] = running;
+        running += v[w];
+        wcnt[w][tid] = 0;
+      }
+    }
+    __syncthreads();
+    if (a < A) {
+      key_s[a] = kc;
+      int slot = -1;
+      if (valid) {
+        const int pos = wpre[wave][kc] + rank;
+        slot = (cap < 0 || pos < cap) ? pos : -1;
+      }
+      slot_s[a] = slot;
+    }
+  }
+  // kept counts and offsets (Hillis-Steele scan over at most 256 experts)
+  int kept = 0;
+  if (tid < E) {
+    kept = cap < 0 ? running : min(running, cap);
+    counts_routed[tid] = running;
+    counts_kept[tid] = kept;
+  }
+  if (tid < 256) off_s[tid] = kept;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const int v = (tid < 256 && tid >= o) ? off_s[tid - o] : 0;
+    __syncthreads();
+    if (tid < 256) off_s[tid] += v;
+    __syncthreads();
+  }
+  if (tid < E) offsets[tid] = off_s[tid] - kept;
+  if (tid == E - 1) offsets[E] = off_s[tid];
+  // scatter, token-major output index a = t*k + j (reads only LDS written
+  // before the scan's barriers)
+  for (int a = tid; a < A; a += kSmallThreads) {
+    const int t = a / k, j = a - t * k;
+    const int e = key_s[j * N + t];
+    const int slot = slot_s[j * N + t];
+    if (slot < 0) {
+      row_of[a] = -1;
+      expert_of[a] = -1;
+      if (policy != MOE_DROPLESS) gates[a] = 0.f;
+    } else {
+      const int row = (e == 0 ? 0 : off_s[e - 1]) + slot;  // off_s is inclusive
+      row_of[a] = row;
+      expert_of[a] = e;
+      perm_token[row] = t;
+    }
+  }
+}
+
 // x_perm[r] = x[perm_token[r]] for r < offsets[E]; 16-byte lanes.
 __global__ __launch_bounds__(kThreads) void gather_rows_kernel(
     const u32x4_t* __restrict__ x, const int32_t* __restrict__ perm_token,
@@ -205,6 +318,18 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(
 namespace moe_host {
 
 static size_t disp_nblk(int A) { return (size_t)(A + kThreads - 1) / kThreads; }
+
+static moe_status gather_launch(int N, int E, int k, const void* x, moe_dtype x_dt, int d,
+                                const int32_t* perm_token, const int32_t* offsets, void* x_perm,
+                                hipStream_t st) {
+  const int A = N * k;
+  const int esz = x_dt == MOE_BF16 ? 2 : 4;
+  const int chunks = d * esz / 16;
+  const int grid = A < 4096 ? A : 4096;
+  gather_rows_kernel<<<grid, kThreads, 0, st>>>((const u32x4_t*)x, perm_token, offsets, E,
+                                                chunks, (u32x4_t*)x_perm);
+  return launch_status("dispatch gather");
+}
 
 size_t dispatch_workspace_bytes(int N, int E, int k) {
   const size_t A = (size_t)N * k;
@@ -243,11 +368,21 @@ moe_status dispatch_launch(int N, int E, int k, int C, moe_overflow policy, int 
   const int ecap = (policy == MOE_DROPLESS) ? -1 : cap;
   const bool reroute = policy == MOE_REROUTE_THEN_DROP;
 
+  moe_status s;
+  if (!reroute && A <= kSmallMaxItems) {
+    disp_small_kernel<<<1, kSmallThreads, 0, st>>>(N, E, k, C, (int)policy, ecap, cand, gates,
+                                                   counts_routed, counts_kept, offsets, row_of,
+                                                   expert_of, perm_token);
+    s = launch_status("dispatch (one workgroup)");
+    if (s != MOE_OK || !x_perm) return s;
+    return gather_launch(N, E, k, x, x_dt, d, perm_token, offsets, x_perm, st);
+  }
+
   KeyArgs g1{N, k, C, 0, cand, nullptr, A};
   disp_count_kernel<<<nb, kThreads, 0, st>>>(g1, E, blockcnt);
   disp_scan_kernel<<<E, kThreads, 0, st>>>(nb, E, blockcnt, blockbase, routed);
   disp_rank_kernel<<<nb, kThreads, 0, st>>>(g1, E, ecap, blockbase, nullptr, slot1);
-  moe_status s = launch_status("dispatch phase 1");
+  s = launch_status("dispatch phase 1");
   if (s != MOE_OK) return s;
 
   if (reroute) {
@@ -267,12 +402,7 @@ moe_status dispatch_launch(int N, int E, int k, int C, moe_overflow policy, int 
   disp_scatter_kernel<<<(A + kThreads - 1) / kThreads, kThreads, 0, st>>>(sa);
   s = launch_status("dispatch scatter");
   if (s != MOE_OK || !x_perm) return s;
-  const int esz = x_dt == MOE_BF16 ? 2 : 4;
-  const int chunks = d * esz / 16;
-  const int grid = A < 4096 ? A : 4096;
-  gather_rows_kernel<<<grid, kThreads, 0, st>>>((const u32x4_t*)x, perm_token, offsets, E,
-                                                chunks, (u32x4_t*)x_perm);
-  return launch_status("dispatch gather");
+  return gather_launch(N, E, k, x, x_dt, d, perm_token, offsets, x_perm, st);
 }
 
 // ---------------------------------------------------------------- no-alloc

@@ -262,7 +262,9 @@ def _dispatch_gpu(moe, cand, cs, gates, E, k, policy, cap, x=None):
                                              (16384, 64, 1, W.REROUTE_THEN_DROP, 1.0),
                                              (777, 256, 8, W.DROPLESS, None),
                                              (1, 4, 1, W.DROP, 1.0),
-                                             (513, 7, 3, W.DROP, 0.5)])
+                                             (513, 7, 3, W.DROP, 0.5),
+                                             (1025, 32, 4, W.DROP, 0.75),
+                                             (4097, 8, 2, W.DROP, 1.0)])
 def test_dispatch_bit_exact(moe, N, E, k, policy, cf):
     g = torch.Generator().manual_seed(N + E)
     skew = torch.tensor([-1.1 * np.log(e + 1) for e in range(E)], dtype=torch.float32)
