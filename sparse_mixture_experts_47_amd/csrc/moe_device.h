@@ -90,36 +90,64 @@ __device__ __forceinline__ float noise_normal(uint64_t seed, uint32_t t, uint32_
 }
 
 // ---------------------------------------------------------------- wave ops
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, MOE_WAVE));
+// Butterfly over the 64 lanes (call with every lane active): level o
+// combines lane i with lane i ^ o, o = 32, 16, 8, 4, 2, 1, without the LDS
+// crossbar. gfx950's permlane swaps hand every lane the pair of values
+// (lane & ~o, lane | o) for o = 32 and 16; inside a row of 16 lanes a
+// rotation by 8 is xor 8, and after that level lanes i and i ^ 8 hold equal
+// values, so the rotation by 4 (lane i receives lane i - 4 mod 16) brings
+// the value of lane i ^ 4; quad permutations give xor 2 and xor 1. Each
+// level applies op to the lane's own value and its partner's (at o = 32
+// and 16 in lane order, which a commutative op does not see).
+namespace detail {
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+}  // namespace detail
+
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_butterfly(uint32_t v, Op op) {
+  const auto p32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = op(p32[0], p32[1]);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = op(p16[0], p16[1]);
+  v = op(v, detail::dpp<0x128>(v));  // row_ror:8
+  v = op(v, detail::dpp<0x124>(v));  // row_ror:4
+  v = op(v, detail::dpp<0x4e>(v));   // quad_perm [2,3,0,1]
+  v = op(v, detail::dpp<0xb1>(v));   // quad_perm [1,0,3,2]
   return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  return __uint_as_float(wave_butterfly(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
 }
 
 // Sum over the wave pairing lane i with lane i^o for o = 32..1: lane 0's
 // value is the halving tree a_i + a_{i+h}, h = 32, 16, ..., 1, and every
-// lane ends with that same value.
+// lane ends with that same value (one rounded addition per level, and an
+// addition does not depend on the order of its operands).
 __device__ __forceinline__ float wave_tree_sum(float v) {
+  return __uint_as_float(wave_butterfly(__float_as_uint(v), [](uint32_t a, uint32_t b) {
 #pragma clang fp contract(off)
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = v + __shfl_xor(v, o, MOE_WAVE);
-  return v;
+    const float r = __uint_as_float(a) + __uint_as_float(b);
+    return __float_as_uint(r);
+  }));
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
-  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  lo = (uint32_t)__shfl_xor((int)lo, o, MOE_WAVE);
-  hi = (uint32_t)__shfl_xor((int)hi, o, MOE_WAVE);
-  return ((uint64_t)hi << 32) | lo;
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return wave_butterfly(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
 }
 
+// 64-bit maximum: the largest high word, then the largest low word among
+// the lanes that hold it.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    uint64_t w = shfl_xor_u64(v, o);
-    v = w > v ? w : v;
-  }
-  return v;
+  const uint32_t hi = (uint32_t)(v >> 32);
+  const uint32_t mh = wave_max_u32(hi);
+  const uint32_t ml = wave_max_u32(hi == mh ? (uint32_t)v : 0u);
+  return ((uint64_t)mh << 32) | ml;
 }
 
 // fp32 -> uint32 whose unsigned order is the float order (finite values).

@@ -20,7 +20,10 @@ constexpr int kWaves = kThreads / MOE_WAVE;
 // short of waves (few tokens: the kernel is latency bound), four for large
 // batches (fewer per-block score partials to sum afterwards).
 inline int select_tok_per_wave(int N) { return N >= 2048 ? 4 : 1; }
-constexpr int kMaxSplits = 8;  // K splits of the router GEMM (partials summed in order)
+// K splits of the router GEMM (partials summed in split order); many for a
+// few tokens, where the GEMM has few tiles and the weight planes dominate
+constexpr int kMaxSplits = 8;
+constexpr int kSplitChunk = 8;  // partials loaded together by the select kernel
 inline int select_blocks(int N) {
   const int per_block = select_tok_per_wave(N) * kWaves;
   return (N + per_block - 1) / per_block;
@@ -243,7 +246,8 @@ __device__ __forceinline__ void finish_token(const SelectArgs& a, int t, int lan
     const uint64_t w = moe::wave_max_u64(best);
     const int ew = (int)(0xFFFFu - (uint32_t)(w & 0xFFFFu));
     const int owner = ew & 63, slot = ew >> 6;
-    const float sw = __shfl(pick(sc, slot, SLOTS), owner, MOE_WAVE);
+    const float sw = __int_as_float(
+        __builtin_amdgcn_readlane(__float_as_int(pick(sc, slot, SLOTS)), owner));
     if (lane == j) {
       my_c = ew;
       my_cs = sw;
@@ -261,10 +265,10 @@ __device__ __forceinline__ void finish_token(const SelectArgs& a, int t, int lan
     a.cand[(size_t)t * a.C + lane] = my_c;
     a.cand_s[(size_t)t * a.C + lane] = my_cs;
   }
-  float Sk = __shfl(my_cs, 0, MOE_WAVE);
+  float Sk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_cs), 0));
   for (int j = 1; j < a.k; ++j) {
 #pragma clang fp contract(off)
-    Sk = Sk + __shfl(my_cs, j, MOE_WAVE);
+    Sk = Sk + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_cs), j));
   }
   if (lane < a.k) a.gates[(size_t)t * a.k + lane] = a.renorm ? my_cs / Sk : my_cs;
 }
@@ -289,6 +293,26 @@ __device__ __forceinline__ void write_partials(const SelectArgs& a, int lane, in
     for (int w = 1; w < kThreads / MOE_WAVE; ++w) v += red[w][e];
     a.partials[(size_t)blockIdx.x * (E + 1) + e] = v;
   }
+}
+
+// The split partials of one logit added in split order, loaded kSplitChunk
+// at a time ahead of their additions.
+__device__ __forceinline__ float split_sum(const SelectArgs& a, const float* p) {
+  const int ns = a.nsplit;
+  float v = 0.f;
+  for (int q0 = 0; q0 < ns; q0 += kSplitChunk) {
+    float pv[kSplitChunk];
+#pragma unroll
+    for (int q = 0; q < kSplitChunk; ++q)
+      pv[q] = q0 + q < ns ? p[(size_t)(q0 + q) * a.split_stride] : 0.f;
+#pragma unroll
+    for (int q = 0; q < kSplitChunk; ++q) {
+#pragma clang fp contract(off)
+      if (q0 + q == 0) v = pv[0];
+      else if (q0 + q < ns) v = v + pv[q];
+    }
+  }
+  return v;
 }
 
 // One wave per token (tok_per_wave tokens in turn) over logits that come in
@@ -316,25 +340,8 @@ __global__ __launch_bounds__(kThreads) void router_select_kernel(SelectArgs a) {
       valid[s] = e < E;
       float v = -INFINITY;
       if (valid[s]) {
-        // all split partials are loaded before the in-order sum
-        float pv[kMaxSplits];
-#pragma unroll
-        for (int q = 0; q < kMaxSplits; ++q)
-          pv[q] = q < a.nsplit ? row[q * a.split_stride + e] : 0.f;
-        v = pv[0];
-#pragma unroll
-        for (int q = 1; q < kMaxSplits; ++q)
-          if (q < a.nsplit) v = v + pv[q];
-        float nv = 0.f;
-        if (a.from_gemm && a.noise) {
-#pragma unroll
-          for (int q = 0; q < kMaxSplits; ++q)
-            pv[q] = q < a.nsplit ? row[q * a.split_stride + E + e] : 0.f;
-          nv = pv[0];
-#pragma unroll
-          for (int q = 1; q < kMaxSplits; ++q)
-            if (q < a.nsplit) nv = nv + pv[q];
-        }
+        v = split_sum(a, row + e);
+        const float nv = (a.from_gemm && a.noise) ? split_sum(a, row + E + e) : 0.f;
         v = token_logit(a, t, e, v, nv);
       }
       l[s] = v;
@@ -371,9 +378,20 @@ struct FusedArgs {
 
 constexpr int kFusedWaves = 16;
 
-template <int RB, int NCB>
+__device__ __forceinline__ float add_nc(float a, float b) {
+#pragma clang fp contract(off)
+  return a + b;
+}
+
+// PACK (at most 8 GEMM columns, NCB = 1): the 16 MFMA columns carry the hi
+// plane in columns 0-7 and the mid plane in 8-15, and a second operand the
+// lo plane in 0-7 (zero in 8-15), so each K step takes two products and two
+// thirds of the plane bytes; a K slice's logit is then (hi + mid) + lo.
+template <int RB, int NCB, bool PACK>
 __global__ __launch_bounds__(kFusedWaves * 64) void router_fused_kernel(FusedArgs f,
                                                                         SelectArgs a) {
+  static_assert(!PACK || NCB == 1, "packed planes: one column block");
+  constexpr int NP = PACK ? 2 : 3;  // B operands per K step
   constexpr int TM = 16 * RB, W = NCB * 16;
   constexpr int KW = kFusedWaves / NCB;  // K slices; wave = (column block, K slice)
   __shared__ float part[KW][TM][W + 1];
@@ -390,12 +408,24 @@ __global__ __launch_bounds__(kFusedWaves * 64) void router_fused_kernel(FusedArg
     const int t = min(t0 + rb * 16 + r16, a.N - 1);  // rows past N read row N-1
     xr[rb] = f.x + (size_t)t * d + grp * 16;
   }
-  const uint16_t* wr = f.planes + (size_t)(cb * 16 + r16) * d + grp * 16;
-  // one 64-wide K step: x (two 8-value halves per row block) and the three
-  // weight planes
+  // B operand p of this lane: plane p, row cb * 16 + r16; packed: hi or mid
+  // (r16 < 8 or not) row r16 % 8, then lo row r16 (lanes with r16 >= 8 load
+  // nothing and supply zeros)
+  const uint16_t* wr[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    if (PACK)
+      wr[p] = f.planes + (p == 0 ? (r16 < 8 ? 0 : f.plane_stride) : 2 * f.plane_stride) +
+              (size_t)(r16 & 7) * d + grp * 16;
+    else
+      wr[p] = f.planes + p * f.plane_stride + (size_t)(cb * 16 + r16) * d + grp * 16;
+  }
+  const bool wlive1 = !PACK || r16 < 8;
+  // one 64-wide K step: x (two 8-value halves per row block) and the weight
+  // operands
   struct Step {
     u32x4_t x[RB][2];
-    u32x4_t w[3][2];
+    u32x4_t w[NP][2];
   };
   auto load = [&](Step& o, int st) {
     const int k = st * 64;
@@ -405,25 +435,36 @@ __global__ __launch_bounds__(kFusedWaves * 64) void router_fused_kernel(FusedArg
       o.x[rb][1] = *(const u32x4_t*)(xr[rb] + k + 8);
     }
 #pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      const uint16_t* w = wr + p * f.plane_stride + k;
-      o.w[p][0] = *(const u32x4_t*)w;
-      o.w[p][1] = *(const u32x4_t*)(w + 8);
+    for (int p = 0; p < NP; ++p) {
+      const uint16_t* w = wr[p] + k;
+      if (p == 0 || wlive1) {
+        o.w[p][0] = *(const u32x4_t*)w;
+        o.w[p][1] = *(const u32x4_t*)(w + 8);
+      } else {
+        o.w[p][0] = u32x4_t{0u, 0u, 0u, 0u};
+        o.w[p][1] = u32x4_t{0u, 0u, 0u, 0u};
+      }
     }
   };
-  f32x4_t acc[RB];
+  // packed: acc[.][0] sums hi | mid, acc[.][1] sums lo; else one sum
+  constexpr int NA = PACK ? 2 : 1;
+  f32x4_t acc[RB][NA];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int q = 0; q < NA; ++q) acc[rb][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   auto mult = [&](const Step& o) {
 #pragma unroll
-    for (int p = 0; p < 3; ++p)
+    for (int p = 0; p < NP; ++p)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+        for (int rb = 0; rb < RB; ++rb) {
+          const int q = PACK ? p : 0;
+          acc[rb][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               __builtin_bit_cast(bf16x8_t, o.x[rb][h]), __builtin_bit_cast(bf16x8_t, o.w[p][h]),
-              acc[rb], 0, 0, 0);
+              acc[rb][q], 0, 0, 0);
+        }
   };
   // Slice ks holds steps ks, ks + KW, ...; blocks start their walk at
   // different steps of the slice so that they do not all read the same
@@ -456,7 +497,15 @@ __global__ __launch_bounds__(kFusedWaves * 64) void router_fused_kernel(FusedArg
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) part[ks][rb * 16 + 4 * grp + r][cb * 16 + r16] = acc[rb][r];
+    for (int r = 0; r < 4; ++r) {
+      float v = acc[rb][0][r];
+      if (PACK) {
+        // column r16 < 8: its hi sum here, its mid sum 8 lanes on (row_ror:8)
+        const float mid = __uint_as_float(moe::detail::dpp<0x128>(__float_as_uint(v)));
+        v = add_nc(add_nc(v, mid), acc[rb][1][r]);
+      }
+      if (!PACK || r16 < 8) part[ks][rb * 16 + 4 * grp + r][cb * 16 + r16] = v;
+    }
   __syncthreads();
   // the K slices, added in slice order
   for (int i = threadIdx.x; i < TM * W; i += kFusedWaves * 64) {
@@ -656,10 +705,12 @@ bool fused_router(const RouterPlan& pl, int E) { return pl.mfma && E <= 32 && pl
 hipError_t launch_fused(int ncb, int nblk, const FusedArgs& f, const SelectArgs& a,
                         hipStream_t st) {
   constexpr int th = kFusedWaves * 64;
-  if (ncb == 1)
-    router_fused_kernel<1, 1><<<nblk, th, 0, st>>>(f, a);
+  if (ncb == 0)
+    router_fused_kernel<1, 1, true><<<nblk, th, 0, st>>>(f, a);
+  else if (ncb == 1)
+    router_fused_kernel<1, 1, false><<<nblk, th, 0, st>>>(f, a);
   else
-    router_fused_kernel<1, 2><<<nblk, th, 0, st>>>(f, a);
+    router_fused_kernel<1, 2, false><<<nblk, th, 0, st>>>(f, a);
   return hipGetLastError();
 }
 }  // namespace
@@ -729,7 +780,8 @@ moe_status router_launch(const moe_router_params* p, const void* x, moe_dtype x_
       }
       if (fused) {
         FusedArgs f{(const uint16_t*)x, planes, (long long)n, d};
-        const int ncb = E2 <= 16 ? 1 : 2;
+        // 0: hi and mid planes packed into one operand (at most 8 columns)
+        const int ncb = E2 <= 8 ? 0 : E2 <= 16 ? 1 : 2;
         nblk = (N + 15) / 16;
         const hipError_t err = launch_fused(ncb, nblk, f, a, st);
         if (err != hipSuccess) {
