@@ -120,7 +120,8 @@ def test_level2_router_gemm(moe, key):
 
 @pytest.mark.parametrize("N,d,E,seed", [(300, 64, 64, 44), (130, 128, 16, 0xDEADBEEFCAFEBABE),
                                          (65, 64, 256, 7), (300, 256, 64, 44),
-                                         (16400, 256, 32, 5), (17, 512, 8, 3)])
+                                         (16400, 256, 32, 5), (17, 512, 8, 3),
+                                         (200, 128, 4, 11), (64, 256, 3, 12)])
 def test_noisy_logits_bit_exact(moe, N, d, E, seed):
     """Noisy gating H = l + z*softplus(v) (chiang97912 notes, "KeepTopK 策略"),
     bit for bit against the oracle. x, W_g and W_noise hold small integers,
@@ -183,7 +184,8 @@ def test_top1_combine_in_epilogue_matches_combine(moe, key, n):
 
 @pytest.mark.parametrize("N,d,E,noise", [(600, 512, 8, False), (16400, 256, 64, True),
                                           (333, 1024, 64, False), (257, 512, 256, False),
-                                          (100, 192, 16, True)])
+                                          (100, 192, 16, True), (300, 256, 4, True),
+                                          (129, 128, 5, False)])
 def test_router_prepared_planes_match_per_call_split(moe, N, d, E, noise):
     """The router with weight planes from moe_router_prepare gives the same
     bits as the router that splits the weights itself on every call (fused
