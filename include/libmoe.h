@@ -167,7 +167,9 @@ moe_status moe_router_prepare(const float* w_gate, const float* w_noise, int32_t
  * expert already holds `capacity` assignments overflows (policy above).
  * Rows: offsets = exclusive prefix sum of counts_kept; the assignment's row
  * is offsets[e] + its slot (its position among e's kept assignments).
- *  cand_ids, cand_scores [N][n_cand] from moe_router_topk
+ *  cand_ids, cand_scores [N][n_cand] from moe_router_topk; an id outside
+ *              [0, n_experts) is no candidate (its assignment, or its
+ *              reroute, is dropped; it takes no capacity)
  *  gates       [N][top_k] in/out: rerouted -> second candidate's score,
  *              dropped -> 0 (DROPLESS leaves it untouched)
  *  capacity    -1 for DROPLESS, else >= 0 (see moe_capacity)

@@ -23,15 +23,21 @@ struct KeyArgs {
   const int32_t* cand;      // mode 1: a = t, key = cand[t][1] if slot1[t] < 0
   const int32_t* slot1;
   int A;                    // number of items
+  int E;
 };
+
+// An id outside [0, E) is no candidate: its assignment is dropped.
+__device__ __forceinline__ int valid_key(int32_t id, int E) {
+  return (uint32_t)id < (uint32_t)E ? id : -1;
+}
 
 __device__ __forceinline__ int item_key(const KeyArgs& g, int a) {
   if (a >= g.A) return -1;
   if (g.mode == 0) {
     const int j = a / g.N, t = a - j * g.N;
-    return g.cand[(size_t)t * g.C + j];
+    return valid_key(g.cand[(size_t)t * g.C + j], g.E);
   }
-  return g.slot1[a] < 0 ? g.cand[(size_t)a * g.C + 1] : -1;
+  return g.slot1[a] < 0 ? valid_key(g.cand[(size_t)a * g.C + 1], g.E) : -1;
 }
 
 __global__ __launch_bounds__(kThreads) void disp_count_kernel(KeyArgs g, int E,
@@ -222,7 +228,7 @@ __global__ __launch_bounds__(kSmallThreads) void disp_small_kernel(
     key[c] = -1;
     if (a < A) {
       const int j = a / N, t = a - j * N;
-      key[c] = cand[(size_t)t * C + j];
+      key[c] = valid_key(cand[(size_t)t * C + j], E);
     }
   }
   for (int i = tid; i < kSmallWaves * 256; i += kSmallThreads) (&wcnt[0][0])[i] = 0;
@@ -378,7 +384,7 @@ moe_status dispatch_launch(int N, int E, int k, int C, moe_overflow policy, int 
     return gather_launch(N, E, k, x, x_dt, d, perm_token, offsets, x_perm, st);
   }
 
-  KeyArgs g1{N, k, C, 0, cand, nullptr, A};
+  KeyArgs g1{N, k, C, 0, cand, nullptr, A, E};
   disp_count_kernel<<<nb, kThreads, 0, st>>>(g1, E, blockcnt);
   disp_scan_kernel<<<E, kThreads, 0, st>>>(nb, E, blockcnt, blockbase, routed);
   disp_rank_kernel<<<nb, kThreads, 0, st>>>(g1, E, ecap, blockbase, nullptr, slot1);
@@ -387,7 +393,7 @@ moe_status dispatch_launch(int N, int E, int k, int C, moe_overflow policy, int 
 
   if (reroute) {
     const int nb2 = (int)disp_nblk(N);
-    KeyArgs g2{N, k, C, 1, cand, slot1, N};
+    KeyArgs g2{N, k, C, 1, cand, slot1, N, E};
     disp_kept1_kernel<<<1, kThreads, 0, st>>>(E, cap, routed, kept1);
     disp_count_kernel<<<nb2, kThreads, 0, st>>>(g2, E, blockcnt);
     disp_scan_kernel<<<E, kThreads, 0, st>>>(nb2, E, blockcnt, blockbase, demand2);

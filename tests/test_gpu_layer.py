@@ -284,6 +284,44 @@ def test_dispatch_bit_exact(moe, N, E, k, policy, cf):
     assert np.array_equal(got["gates"].view(np.uint32), ref["gates"].view(np.uint32))
 
 
+@pytest.mark.parametrize("N,E,k,policy,cf", [(500, 16, 4, W.DROPLESS, None),
+                                             (3000, 64, 4, W.DROP, 1.0),
+                                             (10000, 32, 1, W.REROUTE_THEN_DROP, 1.0)])
+def test_dispatch_ids_out_of_range_are_dropped(moe, N, E, k, policy, cf):
+    """Candidate ids outside [0, E) are no candidate: against the oracle on the
+    same candidates with those ids sent to an extra expert E placed last
+    (which takes no capacity from the others), every assignment to a real
+    expert gets the same row and the offsets of the real experts agree; the
+    GPU drops the rest. Reroute: only second candidates are made invalid."""
+    g = torch.Generator().manual_seed(N + E + k)
+    C = k + 1 if policy == W.REROUTE_THEN_DROP else k
+    logits = torch.randn((N, E), generator=g)
+    r = oracle.route(logits.numpy(), k, C, policy == W.DROPLESS)
+    cand = r["cand_ids"].copy()
+    bad = torch.rand((N, C), generator=g).numpy() < 0.07
+    if policy == W.REROUTE_THEN_DROP:
+        bad[:, 0] = False
+    pick = torch.randint(0, 3, (N, C), generator=g).numpy()
+    junk = np.choose(pick, [-3, E + 5, 1000]).astype(np.int32)
+    cand[bad] = junk[bad]
+    cap = -1 if cf is None else moe.capacity(N, E, cf)
+    got = _dispatch_gpu(moe, cand, r["cand_scores"], r["gates"], E, k, policy, cap)
+    dummy = np.where(bad, E, cand).astype(np.int32)
+    ref = oracle.dispatch(dummy, r["cand_scores"], r["gates"], E + 1, k, policy,
+                          -1 if cf is None else cap)
+    to_dummy = ref["expert_of"] == E  # kept by the oracle's extra expert
+    real = ~to_dummy
+    assert np.array_equal(got["row_of"][real], ref["row_of"][real])
+    assert np.array_equal(got["expert_of"][real], ref["expert_of"][real])
+    assert np.all(got["row_of"][to_dummy] == -1) and np.all(got["expert_of"][to_dummy] == -1)
+    assert np.array_equal(got["offsets"], ref["offsets"][:E + 1])
+    assert np.array_equal(got["counts_kept"], ref["counts_kept"][:E])
+    R = int(ref["offsets"][E])
+    assert np.array_equal(got["perm_token"][:R], ref["perm_token"][:R])
+    print("  invalid ids", int(bad.sum()), "of them kept by the extra expert",
+          int(to_dummy.sum()), flush=True)
+
+
 def test_dispatch_forced_collapse(moe):
     # every token to expert 0: kept = capacity, kept tokens are exactly 0..cap-1
     N, E = 256, 4
