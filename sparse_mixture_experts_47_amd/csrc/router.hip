@@ -20,10 +20,7 @@ constexpr int kWaves = kThreads / MOE_WAVE;
 // short of waves (few tokens: the kernel is latency bound), four for large
 // batches (fewer per-block score partials to sum afterwards).
 inline int select_tok_per_wave(int N) { return N >= 2048 ? 4 : 1; }
-// K splits of the router GEMM (partials summed in split order); many for a
-// few tokens, where the GEMM has few tiles and the weight planes dominate
-constexpr int kMaxSplits = 8;
-constexpr int kSplitChunk = 8;  // partials loaded together by the select kernel
+constexpr int kMaxSplits = 8;  // K splits of the router GEMM (partials summed in order)
 inline int select_blocks(int N) {
   const int per_block = select_tok_per_wave(N) * kWaves;
   return (N + per_block - 1) / per_block;
@@ -295,26 +292,6 @@ __device__ __forceinline__ void write_partials(const SelectArgs& a, int lane, in
   }
 }
 
-// The split partials of one logit added in split order, loaded kSplitChunk
-// at a time ahead of their additions.
-__device__ __forceinline__ float split_sum(const SelectArgs& a, const float* p) {
-  const int ns = a.nsplit;
-  float v = 0.f;
-  for (int q0 = 0; q0 < ns; q0 += kSplitChunk) {
-    float pv[kSplitChunk];
-#pragma unroll
-    for (int q = 0; q < kSplitChunk; ++q)
-      pv[q] = q0 + q < ns ? p[(size_t)(q0 + q) * a.split_stride] : 0.f;
-#pragma unroll
-    for (int q = 0; q < kSplitChunk; ++q) {
-#pragma clang fp contract(off)
-      if (q0 + q == 0) v = pv[0];
-      else if (q0 + q < ns) v = v + pv[q];
-    }
-  }
-  return v;
-}
-
 // One wave per token (tok_per_wave tokens in turn) over logits that come in
 // (logits_in) or as K-split GEMM partials (summed in split order).
 template <int SLOTS>
@@ -340,8 +317,26 @@ __global__ __launch_bounds__(kThreads) void router_select_kernel(SelectArgs a) {
       valid[s] = e < E;
       float v = -INFINITY;
       if (valid[s]) {
-        v = split_sum(a, row + e);
-        const float nv = (a.from_gemm && a.noise) ? split_sum(a, row + E + e) : 0.f;
+        // all split partials are loaded before the in-order sum (unrolled:
+        // the loads of every slot go out together)
+        float pv[kMaxSplits];
+#pragma unroll
+        for (int q = 0; q < kMaxSplits; ++q)
+          pv[q] = q < a.nsplit ? row[q * a.split_stride + e] : 0.f;
+        v = pv[0];
+#pragma unroll
+        for (int q = 1; q < kMaxSplits; ++q)
+          if (q < a.nsplit) v = v + pv[q];
+        float nv = 0.f;
+        if (a.from_gemm && a.noise) {
+#pragma unroll
+          for (int q = 0; q < kMaxSplits; ++q)
+            pv[q] = q < a.nsplit ? row[q * a.split_stride + E + e] : 0.f;
+          nv = pv[0];
+#pragma unroll
+          for (int q = 1; q < kMaxSplits; ++q)
+            if (q < a.nsplit) nv = nv + pv[q];
+        }
         v = token_logit(a, t, e, v, nv);
       }
       l[s] = v;
