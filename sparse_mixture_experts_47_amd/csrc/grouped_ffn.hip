@@ -789,10 +789,13 @@ hipError_t launch_g1(bool glu, bool pair, const moe_gemm::Args& g1, hipStream_t 
               : run_gemm<BM, 64, 1, 1, EPI_ACT, OUT_BF16>(g1, 1, st);
 }
 
+// narrow: 64-column tiles (the tail launch of a few experts' last rows: twice
+// the blocks to stream their W2 columns, Mixtral shape 128 -> 108 us)
 template <int BM, int OF32>
-hipError_t launch_g2_k(bool pair, bool ybf, const moe_gemm::Args& g2, hipStream_t st) {
+hipError_t launch_g2_k(bool pair, bool ybf, const moe_gemm::Args& g2, hipStream_t st,
+                       bool narrow) {
   using namespace moe_gemm;
-  const bool n2 = g2.Nrows % 128 == 0;
+  const bool n2 = g2.Nrows % 128 == 0 && !narrow;
   if (pair) {
     moe_gemm::Args gp = g2;
     gp.group_n = MOE_G2_PAIR_GN;
@@ -820,16 +823,17 @@ hipError_t launch_g2_k(bool pair, bool ybf, const moe_gemm::Args& g2, hipStream_
     return ybf ? run_gemm<BM, 128, 1, 1, EPI_OUT, OUT_BF16, MOE_G2_WGN>(g2, 1, st)
                : run_gemm<BM, 128, 1, 1, EPI_OUT, OF32, MOE_G2_WGN>(g2, 1, st);
   return ybf ? run_gemm<BM, 64, 1, 1, EPI_OUT, OUT_BF16>(g2, 1, st)
-             : run_gemm<BM, 64, 1, 1, EPI_OUT, OUT_F32>(g2, 1, st);
+             : run_gemm<BM, 64, 1, 1, EPI_OUT, OF32>(g2, 1, st);
 }
 
 // GEMM 2 with fp32 output into packed rows, or (c_rows set) scattered to
 // token rows with the gate applied
 template <int BM>
-hipError_t launch_g2(bool pair, bool ybf, const moe_gemm::Args& g2, hipStream_t st) {
+hipError_t launch_g2(bool pair, bool ybf, const moe_gemm::Args& g2, hipStream_t st,
+                     bool narrow = false) {
   using namespace moe_gemm;
-  if (g2.c_rows) return launch_g2_k<BM, OUT_F32_SCATTER>(pair, false, g2, st);
-  return launch_g2_k<BM, OUT_F32>(pair, ybf, g2, st);
+  if (g2.c_rows) return launch_g2_k<BM, OUT_F32_SCATTER>(pair, false, g2, st, narrow);
+  return launch_g2_k<BM, OUT_F32>(pair, ybf, g2, st, narrow);
 }
 
 moe_gemm::Args base_args(const void* A, const void* B0, const void* B1, const float* bias,
@@ -1023,7 +1027,7 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
     err = launch_g1<256>(glu, pair, g1, st);
     if (err == hipSuccess && split) err = launch_g1<128>(glu, pair, g1r, st);
     if (err == hipSuccess) err = launch_g2<256>(pair, ybf, g2, st);
-    if (err == hipSuccess && split) err = launch_g2<128>(pair, ybf, g2r, st);
+    if (err == hipSuccess && split) err = launch_g2<128>(pair, ybf, g2r, st, true);
   } else {
     err = launch_g1<128>(glu, pair, g1, st);
     if (err == hipSuccess) err = launch_g2<128>(pair, ybf, g2, st);

@@ -156,14 +156,19 @@ def test_noisy_logits_bit_exact(moe, N, d, E, seed):
     assert np.array_equal(to_np(cand), r["cand_ids"])
 
 
-@pytest.mark.parametrize("key,n", [("c1", 256), ("c4", 2000), ("c4", 37), ("c2", 600)])
-def test_top1_combine_in_epilogue_matches_combine(moe, key, n):
+@pytest.mark.parametrize("key,n,d", [("c1", 256, None), ("c4", 2000, None), ("c4", 37, None),
+                                     ("c2", 600, None), ("c2", 600, 192), ("c2", 5000, None)])
+def test_top1_combine_in_epilogue_matches_combine(moe, key, n, d):
     """Top-1 routing: the combine done in GEMM 2's epilogue gives the same
     bits as the grouped FFN into packed rows followed by moe_combine (fp32
     SIMT path for the tiny Switch layer, the bf16-pair GEMM 2 for the skewed
     one with 53% of its tokens dropped, a top-1 variant of the Mixtral
-    shape on the plain bf16 GEMM 2)."""
+    shape on the plain bf16 GEMM 2: 128-row tiles, 64-column tiles where
+    d_model is not a multiple of 128, and 256-row tiles with the short
+    tails in a second launch of 128-row x 64-column tiles)."""
     cfg = W.REDUCED[key].with_(n_tokens=n)
+    if d is not None:
+        cfg = cfg.with_(d_model=d)
     if cfg.top_k != 1:
         cfg = cfg.with_(top_k=1, renormalize=False, overflow=W.DROP, capacity_factor=1.0)
     inp = W.make_inputs(cfg, "cpu")
