@@ -512,9 +512,11 @@ def call_bytes(cfg, layer, counts):
 
 def time_forward(cfg, steps, warmup, cold_steps):
     """Build the layer for `cfg` on resident synthetic inputs, run `warmup`
-    forwards, then time `steps` back-to-back forwards with HIP events around
-    every call on the launch stream (and `cold_steps` more, each after a
-    512 MiB write that evicts the 256 MB Infinity Cache)."""
+    forwards, then time `steps` back-to-back forwards (wall clock between
+    two synchronisations; HIP events on the launch stream around the grouped
+    FFN), then as many more with events around every call for the per-call
+    breakdown (and `cold_steps` more, each after a 512 MiB write that evicts
+    the 256 MB Infinity Cache)."""
     import numpy as np
     import torch
 
@@ -546,16 +548,35 @@ def time_forward(cfg, steps, warmup, cold_steps):
         layer.stats()
         e[5].record(stream)
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-          for _ in range(steps)]
+    def timed_step(e):
+        # the timed steps carry events around the grouped FFN only: an event
+        # record between two calls costs the stream 1.5-5 us, which every
+        # per-call event would add to the step
+        layer.start_shared(x)
+        layer.route(x)
+        layer.dispatch(x)
+        e[0].record(stream)
+        layer.experts(x)
+        e[1].record(stream)
+        layer.combine()
+        layer.stats()
+
+    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for st in range(steps):
-        one_step(ev[st])
+        timed_step(fev[st])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    # per-call breakdown: as many steps again, with events around every call
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+          for _ in range(steps)]
+    for st in range(steps):
+        one_step(ev[st])
+    torch.cuda.synchronize()
     samples = {n: [ev[st][i].elapsed_time(ev[st][i + 1]) for st in range(steps)]
                for i, n in enumerate(names)}
+    samples["grouped_ffn"] = [fev[st][0].elapsed_time(fev[st][1]) for st in range(steps)]
     layer_ev = [ev[st][0].elapsed_time(ev[st][len(names)]) for st in range(steps)]
     cold = None
     if cold_steps > 0:
