@@ -54,7 +54,8 @@ struct Args {
   int n_tiles_n;         // Nrows / BN
   int group_n;           // GN
   const int32_t* offsets;     // [E+1]
-  const int32_t* tile_start;  // [E+1]
+  const int32_t* tile_start;  // [E+1], or null: one group of rows1 rows (no table)
+  int rows1;
   const int32_t* a_rows;      // row r of the product reads A row a_rows[r] (or r if null)
   // rows of group e covered by this launch: [seg_begin[e], seg_end[e]), or
   // [offsets[e], offsets[e+1]) when null; tile_e[mt] = group of M tile mt
@@ -167,7 +168,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
   // the grid is sized for max_mt M tiles; the XCDs split the tiles that
   // exist (tile_start[E] of them) evenly instead, each walking a contiguous
   // range, and the surplus blocks of every XCD exit
-  const int n_real = g.tile_start[g.E];
+  const bool one_group = g.tile_start == nullptr;
+  const int n_real = one_group ? (g.rows1 + BM - 1) / BM : g.tile_start[g.E];
   const int total = ((g.n_tiles_n + g.group_n - 1) / g.group_n) * n_real * g.group_n;
   const int quota = (total + 7) >> 3;
   if ((int)(blockIdx.x >> 3) >= quota) return;
@@ -177,10 +179,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
   const int ng = logical / span, rem = logical - ng * span;
   const int mt = rem / g.group_n;
   const int nt = ng * g.group_n + (rem - mt * g.group_n);
-  if (nt >= g.n_tiles_n || mt >= g.tile_start[g.E]) return;
-  const int e = g.tile_e ? g.tile_e[mt] : tile_expert(g.tile_start, g.E, mt);
-  const int row0 = (g.seg_begin ? g.seg_begin[e] : g.offsets[e]) + (mt - g.tile_start[e]) * BM;
-  const int row_end = g.seg_end ? g.seg_end[e] : g.offsets[e + 1];
+  if (nt >= g.n_tiles_n || mt >= n_real) return;
+  const int e = one_group ? 0 : g.tile_e ? g.tile_e[mt] : tile_expert(g.tile_start, g.E, mt);
+  const int row0 = one_group ? mt * BM
+                             : (g.seg_begin ? g.seg_begin[e] : g.offsets[e]) +
+                                   (mt - g.tile_start[e]) * BM;
+  const int row_end = one_group ? g.rows1 : g.seg_end ? g.seg_end[e] : g.offsets[e + 1];
   const int n0 = nt * BN;
   const int K = g.K;
   // top-1 combine: the token and gate of every row this lane will store,

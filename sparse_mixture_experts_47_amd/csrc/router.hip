@@ -20,7 +20,12 @@ constexpr int kWaves = kThreads / MOE_WAVE;
 // short of waves (few tokens: the kernel is latency bound), four for large
 // batches (fewer per-block score partials to sum afterwards).
 inline int select_tok_per_wave(int N) { return N >= 2048 ? 4 : 1; }
-constexpr int kMaxSplits = 8;  // K splits of the router GEMM (partials summed in order)
+// K splits of the router GEMM whose partials the select kernel adds itself
+// (loaded together, summed in order); up to kMaxGemmSplits (a few tokens:
+// few tiles, so the weight planes need many workgroups) a reduce kernel
+// adds them first
+constexpr int kMaxSplits = 8;
+constexpr int kMaxGemmSplits = 64;
 inline int select_blocks(int N) {
   const int per_block = select_tok_per_wave(N) * kWaves;
   return (N + per_block - 1) / per_block;
@@ -542,18 +547,10 @@ __global__ __launch_bounds__(kFusedWaves * 64) void router_fused_kernel(FusedArg
 // hi = bf16(w), mid = bf16(w - hi), lo = bf16(w - hi - mid) (each step
 // exact in fp32). Rows: w_gate 0..E-1, w_noise E..2E-1, zero padding.
 // x is bf16, so x . W runs on bf16 MFMA with every product exact. Four
-// consecutive k per thread (d is a multiple of 64 on this path). The first
-// thread also writes the one-group tile table of the GEMM over N token
-// rows: offsets = {0, N}, tile_start = {0, ceil(N / bm)}.
+// consecutive k per thread (d is a multiple of 64 on this path).
 __global__ __launch_bounds__(kThreads) void router_split_weights_kernel(
     const float* __restrict__ wg, const float* __restrict__ wn, int E, int E2, int E2pad, int d,
-    uint16_t* __restrict__ planes, int N, int bm, int32_t* __restrict__ table) {
-  if (table && blockIdx.x == 0 && threadIdx.x == 0) {
-    table[0] = 0;
-    table[1] = N;
-    table[2] = 0;
-    table[3] = (N + bm - 1) / bm;
-  }
+    uint16_t* __restrict__ planes) {
   const size_t n = (size_t)E2pad * d, n4 = n / 4;
   for (size_t i4 = (size_t)blockIdx.x * kThreads + threadIdx.x; i4 < n4;
        i4 += (size_t)gridDim.x * kThreads) {
@@ -580,14 +577,21 @@ __global__ __launch_bounds__(kThreads) void router_split_weights_kernel(
   }
 }
 
-// The one-group tile table of the router GEMM over N token rows (when the
-// weight planes come prepared, no split kernel writes it).
-__global__ void router_table_kernel(int N, int bm, int32_t* __restrict__ table) {
-  if (threadIdx.x == 0) {
-    table[0] = 0;
-    table[1] = N;
-    table[2] = 0;
-    table[3] = (N + bm - 1) / bm;
+// More K splits than the select kernel adds itself: every logit's split
+// partials added in split order (all loaded first) into split 0's slot.
+__global__ __launch_bounds__(kThreads) void router_split_reduce_kernel(float* __restrict__ raw,
+                                                                       int nsplit,
+                                                                       long long stride) {
+  for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < stride;
+       i += (long long)gridDim.x * kThreads) {
+    float pv[kMaxGemmSplits];
+#pragma unroll
+    for (int q = 0; q < kMaxGemmSplits; ++q) pv[q] = q < nsplit ? raw[q * stride + i] : 0.f;
+    float v = pv[0];
+#pragma unroll
+    for (int q = 1; q < kMaxGemmSplits; ++q)
+      if (q < nsplit) v = v + pv[q];
+    raw[i] = v;
   }
 }
 
@@ -626,7 +630,7 @@ struct RouterPlan {
   bool mfma;
   int bm;
   int E2, E2pad, bn, nsplit, k_chunk;
-  size_t planes_bytes, raw_bytes, table_bytes, stat_bytes;
+  size_t planes_bytes, raw_bytes, stat_bytes;
 };
 
 RouterPlan plan_router(int N, int d, int E, int with_noise, bool x_bf16) {
@@ -641,10 +645,9 @@ RouterPlan plan_router(int N, int d, int E, int with_noise, bool x_bf16) {
     p.E2pad = (p.E2 + p.bn - 1) / p.bn * p.bn;
     const int tiles = ((N + p.bm - 1) / p.bm) * (p.E2pad / p.bn);
     const int KT = d / 64;
-    // enough K splits for ~512 workgroups, at most 8 (the select kernel sums
-    // the split partials of every logit in order)
+    // enough K splits for ~512 workgroups
     int want = (512 + tiles - 1) / tiles;
-    want = want < 1 ? 1 : (want > kMaxSplits ? kMaxSplits : want);
+    want = want < 1 ? 1 : (want > kMaxGemmSplits ? kMaxGemmSplits : want);
     want = want > KT ? KT : want;
     const int steps = (KT + want - 1) / want;
     p.k_chunk = steps * 64;
@@ -655,7 +658,6 @@ RouterPlan plan_router(int N, int d, int E, int with_noise, bool x_bf16) {
     p.E2pad = p.E2;
   }
   p.raw_bytes = align256((size_t)p.nsplit * N * p.E2pad * sizeof(float));
-  p.table_bytes = 256;
   const size_t nblk = (size_t)select_blocks(N);
   p.stat_bytes = align256(nblk * (E + 1) * sizeof(double));
   return p;
@@ -666,8 +668,8 @@ size_t router_workspace_bytes(int N, int d, int E, int with_noise) {
   // the larger of the two plans (x dtype is not known at query time)
   RouterPlan a = plan_router(N, d, E, with_noise, true);
   RouterPlan b = plan_router(N, d, E, with_noise, false);
-  size_t sa = a.planes_bytes + a.raw_bytes + a.table_bytes + a.stat_bytes;
-  size_t sb = b.planes_bytes + b.raw_bytes + b.table_bytes + b.stat_bytes;
+  size_t sa = a.planes_bytes + a.raw_bytes + a.stat_bytes;
+  size_t sb = b.planes_bytes + b.raw_bytes + b.stat_bytes;
   return sa > sb ? sa : sb;
 }
 
@@ -685,7 +687,7 @@ moe_status router_prepare_launch(const float* w_gate, const float* w_noise, int 
   const size_t sblk = (n / 4 + kThreads - 1) / kThreads;
   const int sgrid = (int)(sblk < 2048 ? sblk : 2048);
   router_split_weights_kernel<<<sgrid, kThreads, 0, st>>>(w_gate, w_noise, E, E2, E2pad, d,
-                                                          planes, 0, 1, nullptr);
+                                                          planes);
   return launch_status("router weight planes");
 }
 
@@ -722,8 +724,7 @@ moe_status router_launch(const moe_router_params* p, const void* x, moe_dtype x_
   char* ws = (char*)workspace;
   uint16_t* planes = (uint16_t*)ws;
   float* raw = (float*)(ws + pl.planes_bytes);
-  int32_t* table = (int32_t*)(ws + pl.planes_bytes + pl.raw_bytes);
-  double* partials = (double*)(ws + pl.planes_bytes + pl.raw_bytes + pl.table_bytes);
+  double* partials = (double*)(ws + pl.planes_bytes + pl.raw_bytes);
 
   SelectArgs a;
   a.N = N;
@@ -756,22 +757,16 @@ moe_status router_launch(const moe_router_params* p, const void* x, moe_dtype x_
       const size_t n = (size_t)pl.E2pad * d;
       const bool fused = fused_router(pl, E);
       // weight planes: the caller's prepared ones, else split into the
-      // workspace now (the split kernel also writes the GEMM's tile table)
+      // workspace now
       if (!p->w_planes) {
         const size_t sblk = (n / 4 + kThreads - 1) / kThreads;
         const int sgrid = (int)(sblk < 2048 ? sblk : 2048);
         router_split_weights_kernel<<<sgrid, kThreads, 0, st>>>(w_gate, p->w_noise, E, E2,
-                                                                pl.E2pad, d, planes, N, pl.bm,
-                                                                fused ? nullptr : table);
+                                                                pl.E2pad, d, planes);
         moe_status s = launch_status("router weight split");
         if (s != MOE_OK) return s;
       } else {
         planes = (uint16_t*)p->w_planes;
-        if (!fused) {
-          router_table_kernel<<<1, 64, 0, st>>>(N, pl.bm, table);
-          moe_status s = launch_status("router tile table");
-          if (s != MOE_OK) return s;
-        }
       }
       if (fused) {
         FusedArgs f{(const uint16_t*)x, planes, (long long)n, d};
@@ -803,8 +798,9 @@ moe_status router_launch(const moe_router_params* p, const void* x, moe_dtype x_
       g.max_mt = (N + pl.bm - 1) / pl.bm;
       g.act = 0;
       g.group_n = 8;
-      g.offsets = table;
-      g.tile_start = table + 2;
+      g.offsets = nullptr;     // one group of N token rows, no tile table
+      g.tile_start = nullptr;
+      g.rows1 = N;
       const hipError_t err =
           launch_dlds<kRouterBM, 64, 64, 2, 2, 2, 1, 3, EPI_SUM, OUT_F32>(g, pl.nsplit, st);
       if (err != hipSuccess) {
@@ -813,6 +809,15 @@ moe_status router_launch(const moe_router_params* p, const void* x, moe_dtype x_
       }
       a.stride = pl.E2pad;
       a.nsplit = pl.nsplit;
+      if (pl.nsplit > kMaxSplits) {
+        const long long cnt = (long long)N * pl.E2pad;
+        const long long rblk = (cnt + kThreads - 1) / kThreads;
+        router_split_reduce_kernel<<<(int)(rblk < 4096 ? rblk : 4096), kThreads, 0, st>>>(
+            raw, pl.nsplit, cnt);
+        moe_status s = launch_status("router split reduce");
+        if (s != MOE_OK) return s;
+        a.nsplit = 1;
+      }
       }
     } else {
       if (E2 <= 16) {
