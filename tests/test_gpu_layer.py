@@ -327,6 +327,41 @@ def test_dispatch_ids_out_of_range_are_dropped(moe, N, E, k, policy, cf):
           int(to_dummy.sum()), flush=True)
 
 
+@pytest.mark.parametrize("N,E,k,policy", [(300, 8, 2, W.DROP), (9000, 4, 1, W.DROP),
+                                          (5000, 16, 1, W.REROUTE_THEN_DROP)])
+def test_dispatch_capacity_zero_drops_everything(moe, N, E, k, policy):
+    """Capacity factor 0: capacity 0 on both sides, every assignment (and
+    every reroute) dropped, no rows, every gate zeroed -- bit for bit the
+    oracle's dispatch, on the one-workgroup and the multi-block paths."""
+    cap_ref = oracle.capacity(N, E, 0.0)
+    cap = moe.capacity(N, E, 0.0)
+    assert cap == cap_ref == 0
+    g = torch.Generator().manual_seed(N + 3 * E)
+    C = k + 1 if policy == W.REROUTE_THEN_DROP else k
+    r = oracle.route(torch.randn((N, E), generator=g).numpy(), k, C, False)
+    ref = oracle.dispatch(r["cand_ids"], r["cand_scores"], r["gates"], E, k, policy, cap_ref)
+    got = _dispatch_gpu(moe, r["cand_ids"], r["cand_scores"], r["gates"], E, k, policy, cap)
+    for name in ("counts_routed", "counts_kept", "offsets", "row_of", "expert_of"):
+        assert np.array_equal(got[name], ref[name]), name
+    assert ref["R"] == 0 and np.all(got["row_of"] == -1) and np.all(got["gates"] == 0)
+    assert np.array_equal(got["gates"].view(np.uint32), ref["gates"].view(np.uint32))
+
+
+def test_layer_capacity_zero_outputs_zero(moe):
+    """The whole layer with capacity 0 (every token dropped, no shared
+    expert): the grouped FFN gets no rows and the output is exactly zero."""
+    cfg = W.REDUCED["c4"].with_(capacity_factor=0.0, n_tokens=700)
+    inp = W.make_inputs(cfg, "cpu")
+    dev = to_device(inp)
+    layer = moe.MoELayer(moe.spec_from_config(cfg), dev, x_dtype=torch.bfloat16)
+    assert layer.spec.capacity == 0
+    layer.y.fill_(float("nan"))
+    y = layer.forward(dev["x"])
+    torch.cuda.synchronize()
+    assert int(to_np(layer.offsets)[-1]) == 0
+    assert torch.count_nonzero(y).item() == 0 and not torch.isnan(y).any().item()
+
+
 def test_dispatch_forced_collapse(moe):
     # every token to expert 0: kept = capacity, kept tokens are exactly 0..cap-1
     N, E = 256, 4
