@@ -220,7 +220,8 @@ def test_router_prepared_planes_match_per_call_split(moe, N, d, E, noise):
 
 @pytest.mark.parametrize("E,k,C,N,scale", [(5, 2, 3, 37, 1.0), (100, 8, 8, 70, 1.5),
                                            (256, 8, 9, 65, 2.0), (64, 1, 2, 1, 1.0),
-                                           (3, 3, 3, 8, 0.0), (256, 1, 1, 130, 30.0)])
+                                           (3, 3, 3, 8, 0.0), (256, 1, 1, 130, 30.0),
+                                           (1, 1, 1, 50, 1.0), (2, 1, 2, 2049, 3.0)])
 def test_router_select_edge_shapes_bit_exact(moe, E, k, C, N, scale):
     g = torch.Generator().manual_seed(E * 1000 + N)
     logits = (torch.randn((N, E), generator=g) * scale)
