@@ -700,6 +700,40 @@ def test_grouped_ffn_256_row_tiles_with_tails(moe):
     assert np.all(got[R:] == 7.0)
 
 
+@pytest.mark.parametrize("h_fp32", [False, True])
+def test_grouped_ffn_whole_expert_gemm1(moe, h_fp32):
+    """Experts averaging 1536 rows or more: GEMM 1 runs each expert whole on
+    256-row tiles (its tail in a partly filled last tile), GEMM 2 sends tails
+    of at most 128 rows to the 128-row launch. Tails of 1, 100, 208 (kept in
+    the main GEMM 2 table) and 20 rows, and an empty expert; bf16 h and the
+    fp32 hi + lo pair."""
+    cfg = W.REDUCED["c2"].with_(name="whole_expert_g1", n_tokens=1000, d_model=256, d_ff=512,
+                                n_experts=5)
+    print("whole-expert GEMM 1, h_fp32", h_fp32, flush=True)
+    inp = W.make_inputs(cfg, "cpu")
+    host = host_inputs(inp)
+    dev = to_device(inp)
+    E = cfg.n_experts
+    counts = np.array([0, 2049, 2404, 2000, 1300])
+    assert counts.sum() // E >= 1536
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offs[-1])
+    tok = np.random.default_rng(13).integers(0, cfg.n_tokens, size=R)
+    w, keep = moe.ffn_weights(dev["w1"], dev["w2"], dev["w3"], cfg.act, h_fp32=h_fp32)
+    y = torch.full((R + 3, cfg.d_model), 7.0, dtype=torch.float32, device="cuda")
+    moe.moe_grouped_ffn(w, dev["x"], torch.from_numpy(offs).cuda(), y,
+                        row_index=torch.from_numpy(tok.astype(np.int32)).cuda(), max_rows=R)
+    torch.cuda.synchronize()
+    X64 = oracle.decode_rows(host["x"][tok], cfg.x_dtype)
+    ref = oracle.ffn_for_assignments(np.arange(R), np.repeat(np.arange(E), counts), X64,
+                                     cfg.act, cfg.w_dtype, experts_of(host))
+    got = to_np(y)
+    err = rel_err(got[:R], ref)
+    print("  max|dy|/rms =", err, flush=True)
+    assert err <= (1e-3 if h_fp32 else out_tol(cfg))
+    assert np.all(got[R:] == 7.0)
+
+
 def test_grouped_ffn_256_row_tiles_partial_blocks(moe):
     """Long-K experts averaging 256-511 rows run 256-row tiles without a
     tail launch; the last tile's unused 32-row blocks skip their MFMAs.
