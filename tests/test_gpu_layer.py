@@ -121,14 +121,19 @@ def test_level2_router_gemm(moe, key):
 @pytest.mark.parametrize("N,d,E,seed", [(300, 64, 64, 44), (130, 128, 16, 0xDEADBEEFCAFEBABE),
                                          (65, 64, 256, 7), (300, 256, 64, 44),
                                          (16400, 256, 32, 5), (17, 512, 8, 3),
-                                         (200, 128, 4, 11), (64, 256, 3, 12)])
+                                         (200, 128, 4, 11), (64, 256, 3, 12),
+                                         (8200, 64, 4, 31), (8197, 128, 16, 21),
+                                         (8300, 192, 8, 4)])
 def test_noisy_logits_bit_exact(moe, N, d, E, seed):
     """Noisy gating H = l + z*softplus(v) (chiang97912 notes, "KeepTopK 策略"),
     bit for bit against the oracle. x, W_g and W_noise hold small integers,
     so both router GEMMs are exact in fp32 on either side (every partial sum
     is an integer below 2^24) and any difference in H can only come from the
     noise draw z, the softplus or the final fused multiply-add. v spans both
-    branches of the softplus (above 20: v itself; else log1p(exp(v)))."""
+    branches of the softplus (above 20: v itself; else log1p(exp(v))). From
+    8192 tokens the fused router takes 32 tokens a block; the cases there
+    cover its packed (8 columns, one K step: 15 of 16 waves idle), 16- and
+    32-column kernels with ragged last blocks."""
     g = torch.Generator().manual_seed(N * 31 + E)
     x = torch.randint(-2, 3, (N, d), generator=g).to(torch.bfloat16)
     wg = torch.randint(-3, 4, (E, d), generator=g).float()
@@ -190,7 +195,8 @@ def test_top1_combine_in_epilogue_matches_combine(moe, key, n, d):
 @pytest.mark.parametrize("N,d,E,noise", [(600, 512, 8, False), (16400, 256, 64, True),
                                           (333, 1024, 64, False), (257, 512, 256, False),
                                           (100, 192, 16, True), (300, 256, 4, True),
-                                          (129, 128, 5, False)])
+                                          (129, 128, 5, False), (8197, 256, 32, False),
+                                          (9000, 512, 8, False)])
 def test_router_prepared_planes_match_per_call_split(moe, N, d, E, noise):
     """The router with weight planes from moe_router_prepare gives the same
     bits as the router that splits the weights itself on every call (fused
