@@ -61,15 +61,23 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(int d, int k,
     rows[j] = j < k ? row_of[(size_t)t * k + j] : -1;
     g[j] = j < k ? gates[(size_t)t * k + j] : 0.f;
   }
-  for (int c = (blockIdx.y * kThreads + threadIdx.x) * 8; c < d; c += gridDim.y * kThreads * 8) {
+  // the grid covers d in one pass (gridDim.y * kThreads * 8 >= d): one
+  // 8-feature chunk a thread
+  const int c = (blockIdx.y * kThreads + threadIdx.x) * 8;
+  if (c < d) {
+    // every kept row's chunk is requested before the first product (eight
+    // loads in flight a thread instead of one row at a time), then summed in
+    // slot order
+    float v[8][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (rows[j] >= 0) Vec8<YT>::load(y_rows + (size_t)rows[j] * d + c, v[j]);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (rows[j] < 0) continue;
-      float v[8];
-      Vec8<YT>::load(y_rows + (size_t)rows[j] * d + c, v);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(g[j], v[i], acc[i]);
+      for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(g[j], v[j][i], acc[i]);
     }
     if (ysh) {
       float v[8];
