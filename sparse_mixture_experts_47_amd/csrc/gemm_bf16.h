@@ -133,6 +133,33 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Issue order for the scheduler. ilv_reads: MF groups of one MFMA, the
+// first RD of them followed by one LDS read. ilv_tail: the first H = MF/2
+// MFMAs each followed by up to VPM global loads (LPT in all), the other H by
+// up to RPM LDS reads (RD in all) -- the reads come after the loads, which
+// write LDS.
+template <int I, int MF, int RD>
+__device__ __forceinline__ void ilv_reads() {
+  if constexpr (I < MF) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (I < RD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    ilv_reads<I + 1, MF, RD>();
+  }
+}
+template <int I, int MF, int RD, int LPT>
+__device__ __forceinline__ void ilv_tail() {
+  constexpr int H = MF / 2;
+  constexpr int VPM = (LPT + H - 1) / H, RPM = (RD + (MF - H) - 1) / (MF - H);
+  if constexpr (I < MF) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (I < H && I * VPM < LPT)
+      __builtin_amdgcn_sched_group_barrier(0x230, (VPM < LPT - I * VPM ? VPM : LPT - I * VPM), 0);
+    if constexpr (I >= H && (I - H) * RPM < RD)
+      __builtin_amdgcn_sched_group_barrier(0x100, (RPM < RD - (I - H) * RPM ? RPM : RD - (I - H) * RPM), 0);
+    ilv_tail<I + 1, MF, RD, LPT>();
+  }
+}
+
 // Output kinds of the direct-LDS kernel.
 // OUT_F32_SCATTER: fp32, each product row to the token row c_rows[r], times
 // its gate (the top-1 combine; its own instance so that the plain fp32 GEMM
@@ -325,6 +352,44 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
     // LDS reads always run under the previous half's MFMAs, and the global
     // loads run NS-1 to NS tiles ahead. sched_barrier keeps the compiler from
     // moving MFMAs across the waits.
+    // Interleaved schedule (full tiles, at least NS K tiles): the same
+    // stages and waits, but the region after the barrier has no branches --
+    // past the last tile the loads re-read tile KT-1 into the stage just
+    // released (no tile reads it again) and the fragment reads of tile KT
+    // go unused -- so the loads of tile kt+NS and the first fragment reads
+    // of tile kt+1 can be issued between the MFMAs of the last half of tile
+    // kt instead of ahead of them, and the matrix pipe does not drain while
+    // they issue. Every iteration issues LPT loads, so the wait for tile
+    // kt+1 is always vmcnt((NS-2) LPT).
+    // Measured against the plain loop (grouped FFN): Mixtral-shaped 2.81 ->
+    // 2.65 ms, DeepSeek-shaped 7.93 -> 7.35, one GPU's EP-8 DeepSeek share
+    // 6.47 -> 5.41; the Switch-shaped kernels (activation epilogue with three
+    // blocks per CU, and the two-plane h of GEMM 2) were 3% slower with it,
+    // so they keep the plain loop.
+    constexpr bool kInterleave = EPI != EPI_ACT && NA == 1;
+    constexpr int RD = NA * FM + NB * FN, MF = NA * FM * NB * FN;
+    auto k_loop_ilv = [&](Frags(&fr)[2], auto full) {
+      for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+        for (int kk = 0; kk + 1 < KK; ++kk) {
+          read_frags(fr[(kk + 1) & 1], kt % NS, kk + 1, full);
+          mfma(fr[kk & 1], full);
+          ilv_reads<0, MF, RD>();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+        wait_vmcnt<(NS - 2) * LPT>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue(min(kt + NS, KT - 1), kt % NS);
+        read_frags(fr[KK & 1], (kt + 1) % NS, 0, full);
+        mfma(fr[(KK - 1) & 1], full);
+        ilv_tail<0, MF, RD, LPT>();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // the loads past the last tile land in LDS the epilogue reuses
+      wait_vmcnt<0>();
+    };
     // one instance for waves whose 32-row blocks are all in use, one with
     // per-block checks (only the last M tile of a group can need it); both
     // run the same barriers
@@ -338,6 +403,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
         else wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
         read_frags(fr[0], 0, 0, full);
+      }
+      if constexpr (kInterleave && decltype(full)::value) {
+        if (KT >= NS) {
+          k_loop_ilv(fr, full);
+          return;
+        }
       }
       for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
