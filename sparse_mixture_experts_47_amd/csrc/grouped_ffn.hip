@@ -697,12 +697,6 @@ __global__ __launch_bounds__(NW * 64) void ffn_fp8_stream_kernel(Fp8Args g,
 #ifndef MOE_G2_WIDE_WGM
 #define MOE_G2_WIDE_WGM 2
 #endif
-#ifndef MOE_G1_BK
-#define MOE_G1_BK MOE_GEMM_BK
-#endif
-#ifndef MOE_G2_WIDE_BK
-#define MOE_G2_WIDE_BK MOE_GEMM_BK
-#endif
 #ifndef MOE_G1_WGM
 #define MOE_G1_WGM 2
 #endif
@@ -798,7 +792,7 @@ hipError_t launch_g1(bool glu, bool pair, const moe_gemm::Args& g1, hipStream_t 
   if (glu) {
     if (n1)
       return pair ? run_gemm<BM, 128, 1, 2, EPI_GLU, OUT_BF16_PAIR>(g1, 1, st)
-                  : run_gemm<BM, 128, 1, 2, EPI_GLU, OUT_BF16, MOE_G1_WGN, MOE_G1_BK,
+                  : run_gemm<BM, 128, 1, 2, EPI_GLU, OUT_BF16, MOE_G1_WGN, MOE_GEMM_BK,
                              MOE_G1_WGM>(g1, 1, st);
     return pair ? run_gemm<BM, 64, 1, 2, EPI_GLU, OUT_BF16_PAIR>(g1, 1, st)
                 : run_gemm<BM, 64, 1, 2, EPI_GLU, OUT_BF16>(g1, 1, st);
@@ -838,9 +832,9 @@ hipError_t launch_g2_k(bool pair, bool ybf, const moe_gemm::Args& g2, hipStream_
                : run_gemm<BM, 64, 2, 1, EPI_OUT, OF32, 2, MOE_GEMM_BK, MOE_G2_PAIR_WGM>(gp, 1, st);
   }
   if (MOE_G2_WIDE && BM == 256 && g2.Nrows % 256 == 0)
-    return ybf ? run_gemm<BM, 256, 1, 1, EPI_OUT, OUT_BF16, MOE_G2_WIDE_WGN, MOE_G2_WIDE_BK,
+    return ybf ? run_gemm<BM, 256, 1, 1, EPI_OUT, OUT_BF16, MOE_G2_WIDE_WGN, MOE_GEMM_BK,
                           MOE_G2_WIDE_WGM>(g2, 1, st)
-               : run_gemm<BM, 256, 1, 1, EPI_OUT, OF32, MOE_G2_WIDE_WGN, MOE_G2_WIDE_BK,
+               : run_gemm<BM, 256, 1, 1, EPI_OUT, OF32, MOE_G2_WIDE_WGN, MOE_GEMM_BK,
                           MOE_G2_WIDE_WGM>(g2, 1, st);
   if (n2)
     return ybf ? run_gemm<BM, 128, 1, 1, EPI_OUT, OUT_BF16, MOE_G2_WGN>(g2, 1, st)
