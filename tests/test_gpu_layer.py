@@ -768,3 +768,37 @@ def test_grouped_ffn_256_row_tiles_partial_blocks(moe):
     got = to_np(y)
     assert rel_err(got[:R], ref) <= out_tol(cfg)
     assert np.all(got[R:] == 7.0)
+
+
+@pytest.mark.parametrize("d_model,d_ff", [(64, 256), (128, 128), (192, 192), (256, 384),
+                                          (512, 448)])
+def test_grouped_ffn_short_k_pipeline_edges(moe, d_model, d_ff):
+    """K loops of 1, 2, 3, 4, 6 and 7 K tiles of 64: with two LDS stages
+    (256-row tiles) and three or six (128-row tail tiles), the K-loop
+    schedule that re-loads the last K tile past the end starts at exactly as
+    many tiles as stages; 128- and 64-column tiles (d_ff not a multiple of
+    128), full, partly filled and one-row tiles, an empty expert."""
+    cfg = W.REDUCED["c2"].with_(name="short_k", n_tokens=700, d_model=d_model, d_ff=d_ff)
+    print("short-K pipeline edges: d_model", d_model, "d_ff", d_ff, flush=True)
+    inp = W.make_inputs(cfg, "cpu")
+    host = host_inputs(inp)
+    dev = to_device(inp)
+    E = cfg.n_experts
+    counts = np.array([0, 768, 513, 1100, 700, 520, 1, 600])
+    assert len(counts) == E and counts.sum() >= 512 * E
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offs[-1])
+    tok = np.random.default_rng(17).integers(0, cfg.n_tokens, size=R)
+    w, keep = moe.ffn_weights(dev["w1"], dev["w2"], dev["w3"], cfg.act, None, None)
+    y = torch.full((R + 3, cfg.d_model), 7.0, dtype=torch.float32, device="cuda")
+    moe.moe_grouped_ffn(w, dev["x"], torch.from_numpy(offs).cuda(), y,
+                        row_index=torch.from_numpy(tok.astype(np.int32)).cuda(), max_rows=R)
+    torch.cuda.synchronize()
+    X64 = oracle.decode_rows(host["x"][tok], cfg.x_dtype)
+    ref = oracle.ffn_for_assignments(np.arange(R), np.repeat(np.arange(E), counts), X64,
+                                     cfg.act, cfg.w_dtype, experts_of(host))
+    got = to_np(y)
+    err = rel_err(got[:R], ref)
+    print("  max|dy|/rms =", err, flush=True)
+    assert err <= out_tol(cfg)
+    assert np.all(got[R:] == 7.0)
