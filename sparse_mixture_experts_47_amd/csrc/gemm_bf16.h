@@ -148,14 +148,16 @@ __device__ __forceinline__ void ilv_reads() {
 }
 template <int I, int MF, int RD, int LPT>
 __device__ __forceinline__ void ilv_tail() {
-  constexpr int H = MF / 2;
-  constexpr int VPM = (LPT + H - 1) / H, RPM = (RD + (MF - H) - 1) / (MF - H);
+  // a single MFMA (H = 1, nothing after it) takes the loads and the reads
+  constexpr int H = MF >= 2 ? MF / 2 : 1, NR = MF - H;
+  constexpr int VPM = (LPT + H - 1) / H, RPM = NR > 0 ? (RD + NR - 1) / NR : RD;
+  constexpr int RB = NR > 0 ? H : 0;  // first MFMA followed by reads
   if constexpr (I < MF) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     if constexpr (I < H && I * VPM < LPT)
       __builtin_amdgcn_sched_group_barrier(0x230, (VPM < LPT - I * VPM ? VPM : LPT - I * VPM), 0);
-    if constexpr (I >= H && (I - H) * RPM < RD)
-      __builtin_amdgcn_sched_group_barrier(0x100, (RPM < RD - (I - H) * RPM ? RPM : RD - (I - H) * RPM), 0);
+    if constexpr (I >= RB && (I - RB) * RPM < RD)
+      __builtin_amdgcn_sched_group_barrier(0x100, (RPM < RD - (I - RB) * RPM ? RPM : RD - (I - RB) * RPM), 0);
     ilv_tail<I + 1, MF, RD, LPT>();
   }
 }
@@ -308,16 +310,18 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
     bf16x8_t a[NA][FM];
     bf16x8_t b[NB][FN];
   };
-  // `full`: std::true_type when every 32-row block of the wave is in use
-  // (no per-block checks in the generated loop)
-  auto read_frags = [&](Frags& f, int stage, int kk, auto full) {
+  // `cnt`: std::integral_constant<int, M>; M >= 0: the wave's first M
+  // 32-row blocks are in use, known when the loop is compiled (no per-block
+  // checks in it); M < 0: the first nfm, checked at run time
+  auto read_frags = [&](Frags& f, int stage, int kk, auto cnt) {
+    constexpr int M = decltype(cnt)::value;
     const uint16_t* cur = smem + stage * STAGE;
     const int c = kk * 2 + (lane >> 5);  // chunk of this lane's 8 K values
 #pragma unroll
     for (int p = 0; p < NA; ++p)
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        if (decltype(full)::value || i < nfm)
+        if (M >= 0 ? i < M : i < nfm)
           f.a[p][i] = *(const bf16x8_t*)(cur + p * A_PLANE +
                                          dlds_off<BK>(wm * WM + i * 32 + (lane & 31), c));
 #pragma unroll
@@ -327,7 +331,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
         f.b[b][j] = *(const bf16x8_t*)(cur + NA * A_PLANE + b * B_PLANE +
                                        dlds_off<BK>(wn * WN + j * 32 + (lane & 31), c));
   };
-  auto mfma = [&](const Frags& f, auto full) {
+  auto mfma = [&](const Frags& f, auto cnt) {
+    constexpr int M = decltype(cnt)::value;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -336,7 +341,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
         for (int p = 0; p < NA; ++p)
 #pragma unroll
           for (int i = 0; i < FM; ++i) {
-            if (!decltype(full)::value && i >= nfm) continue;
+            if (M >= 0 ? i >= M : i >= nfm) continue;
             f32x16_t& d = acc[EPI == EPI_GLU ? b : 0][i][j];
             d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[p][i], f.b[b][j], d, 0, 0, 0);
           }
@@ -367,8 +372,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
     // blocks per CU, and the two-plane h of GEMM 2) were 3% slower with it,
     // so they keep the plain loop.
     constexpr bool kInterleave = EPI != EPI_ACT && NA == 1;
-    constexpr int RD = NA * FM + NB * FN, MF = NA * FM * NB * FN;
     auto k_loop_ilv = [&](Frags(&fr)[2], auto full) {
+      // MFMAs and fragment reads of one 16-wide step for the blocks in use
+      constexpr int M = decltype(full)::value;
+      constexpr int RD = NA * M + NB * FN, MF = NA * M * NB * FN;
       for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
         for (int kk = 0; kk + 1 < KK; ++kk) {
@@ -404,7 +411,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
         __builtin_amdgcn_s_barrier();
         read_frags(fr[0], 0, 0, full);
       }
-      if constexpr (kInterleave && decltype(full)::value) {
+      if constexpr (kInterleave && decltype(full)::value > 0) {
         if (KT >= NS) {
           k_loop_ilv(fr, full);
           return;
@@ -430,8 +437,19 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    if (nfm == FM) k_loop(std::true_type{});
-    else k_loop(std::false_type{});
+    // a partly filled last M tile: the waves with some blocks in use run the
+    // interleaved loop compiled for their block count (256-row tiles have 4
+    // blocks a wave); waves with none, and other shapes, check at run time
+    if (nfm == FM) {
+      k_loop(std::integral_constant<int, FM>{});
+    } else if constexpr (kInterleave && FM == 4) {
+      if (nfm == 3) k_loop(std::integral_constant<int, 3>{});
+      else if (nfm == 2) k_loop(std::integral_constant<int, 2>{});
+      else if (nfm == 1) k_loop(std::integral_constant<int, 1>{});
+      else k_loop(std::integral_constant<int, -1>{});
+    } else {
+      k_loop(std::integral_constant<int, -1>{});
+    }
   }
 
   constexpr bool F32OUT = OUTK == OUT_F32 || OUTK == OUT_F32_SCATTER;
