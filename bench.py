@@ -14,7 +14,9 @@ decode: with the default workload, a sub-record for the decode-shaped layer
 (64 tokens against the DeepSeek-shaped layer, fp8 e4m3 expert weights):
 whole-layer and grouped-FFN bandwidth on the touched experts' weights against
 the HBM peak. per_call_gbs: algorithmic bytes and achieved GB/s (fraction of
-the HBM peak) of the router, dispatch and combine calls.
+the HBM peak) of the router, dispatch and combine calls, and beside them
+x_read_reference: torch.sum over x timed the same way (warm and cold), the
+rate a plain read of the router's main input reaches at this size.
 
 roofline: the grouped expert FFN (moe_grouped_ffn: tile table + GEMM 1
 gate/up with fused SwiGLU + GEMM 2 down) is the dominant kernel group; its
@@ -578,6 +580,15 @@ def time_forward(cfg, steps, warmup, cold_steps):
                for i, n in enumerate(names)}
     samples["grouped_ffn"] = [fev[st][0].elapsed_time(fev[st][1]) for st in range(steps)]
     layer_ev = [ev[st][0].elapsed_time(ev[st][len(names)]) for st in range(steps)]
+    # yardstick for the router: torch's own reduction over x (a plain read of
+    # the router's main input), timed with the same events, warm and cold
+    xev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for st in range(steps):
+        xev[st][0].record(stream)
+        torch.sum(x, dtype=torch.float32)
+        xev[st][1].record(stream)
+    torch.cuda.synchronize()
+    x_read = {"warm": [xev[st][0].elapsed_time(xev[st][1]) for st in range(steps)], "cold": []}
     cold = None
     if cold_steps > 0:
         evict = torch.empty(1 << 27, dtype=torch.float32, device="cuda")
@@ -590,6 +601,14 @@ def time_forward(cfg, steps, warmup, cold_steps):
         csamp = {n: [cev[st][i].elapsed_time(cev[st][i + 1]) for st in range(cold_steps)]
                  for i, n in enumerate(names)}
         clayer = [cev[st][0].elapsed_time(cev[st][len(names)]) for st in range(cold_steps)]
+        xc = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(cold_steps)]
+        for st in range(cold_steps):
+            evict.fill_(float(st))
+            xc[st][0].record(stream)
+            torch.sum(x, dtype=torch.float32)
+            xc[st][1].record(stream)
+            torch.cuda.synchronize()
+        x_read["cold"] = [xc[st][0].elapsed_time(xc[st][1]) for st in range(cold_steps)]
         cold = {"steps": cold_steps, "evict_bytes": 4 << 27,
                 "ms_per_step_median": round(float(np.median(clayer)), 4),
                 "ms_per_step_min": round(float(np.min(clayer)), 4),
@@ -597,14 +616,26 @@ def time_forward(cfg, steps, warmup, cold_steps):
                                        for kk, v in csamp.items()}}
         del evict
     return dict(dev=dev, layer=layer, x=x, counts=counts, samples=samples, layer_ev=layer_ev,
-                ms_step=elapsed * 1e3 / steps, cold=cold)
+                ms_step=elapsed * 1e3 / steps, cold=cold, x_read=x_read)
 
 
-def per_call_gbs(cfg, layer, counts, samples):
+def per_call_gbs(cfg, layer, counts, samples, x_read=None):
     """Achieved algorithmic GB/s and fraction of HBM peak of the router,
-    dispatch and combine calls (median call time)."""
+    dispatch and combine calls (median call time); with x_read, the same
+    figures for torch.sum over x timed alike (warm, and cold after the
+    cache-evicting write), the rate a plain read of the router's main input
+    reaches at this size."""
     import numpy as np
     out = {}
+    if x_read:
+        xb = cfg.n_tokens * cfg.d_model * (4 if cfg.x_dtype == 0 else 2)
+        ref = {"bytes": int(xb), "what": "torch.sum over x, HIP events around the call"}
+        for kk, v in x_read.items():
+            if v:
+                ms = float(np.median(v))
+                ref[kk] = {"ms_median": round(ms, 4), "gbs": round(xb / (ms * 1e-3) / 1e9, 1),
+                           "frac_hbm": round(xb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        out["x_read_reference"] = ref
     for name, nbytes in call_bytes(cfg, layer, counts).items():
         ms = float(np.median(samples[name]))
         if name == "combine" and layer.fused_combine:
@@ -643,7 +674,7 @@ def decode_record(steps, warmup):
                                          / PEAK_HBM_GBS, 4),
            "per_call_ms_median": {kk: round(float(np.median(v)), 4)
                                   for kk, v in r["samples"].items()},
-           "per_call_gbs": per_call_gbs(cfg, layer, counts, r["samples"]),
+           "per_call_gbs": per_call_gbs(cfg, layer, counts, r["samples"], r.get("x_read")),
            "tokens_per_s": round(cfg.n_tokens / (r["ms_step"] * 1e-3), 1)}
     del r
     return rec
@@ -728,7 +759,7 @@ def main():
                                        / PEAK_HBM_GBS, 4),
         "touched_experts": touched,
         "kept_assignments": int(counts.sum()),
-        "per_call_gbs": per_call_gbs(cfg, layer, counts, samples),
+        "per_call_gbs": per_call_gbs(cfg, layer, counts, samples, r.get("x_read")),
         "library": os.path.relpath(moe.LIB_PATH, ROOT),
     }
     if args.copy_calibration:
