@@ -74,6 +74,9 @@ struct Args {
   // packed row order)
   const int32_t* c_rows;
   const float* c_gate;
+  // nonzero: the rows of group e are split evenly over its M tiles
+  // (tile_start[e+1] - tile_start[e] of them) instead of BM rows a tile
+  int even;
 };
 
 __device__ __forceinline__ float act_fn(int act, float v) {
@@ -210,10 +213,25 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
   const int nt = ng * g.group_n + (rem - mt * g.group_n);
   if (nt >= g.n_tiles_n || mt >= n_real) return;
   const int e = one_group ? 0 : g.tile_e ? g.tile_e[mt] : tile_expert(g.tile_start, g.E, mt);
-  const int row0 = one_group ? mt * BM
-                             : (g.seg_begin ? g.seg_begin[e] : g.offsets[e]) +
-                                   (mt - g.tile_start[e]) * BM;
-  const int row_end = one_group ? g.rows1 : g.seg_end ? g.seg_end[e] : g.offsets[e + 1];
+  int row0, row_end;
+  if (one_group) {
+    row0 = mt * BM;
+    row_end = g.rows1;
+  } else {
+    const int beg = g.seg_begin ? g.seg_begin[e] : g.offsets[e];
+    const int end = g.seg_end ? g.seg_end[e] : g.offsets[e + 1];
+    if (g.even) {
+      // the group's rows split evenly over its M tiles, heights a multiple
+      // of 32 (at most BM, as the tile count is ceil(rows / BM))
+      const int nte = g.tile_start[e + 1] - g.tile_start[e];
+      const int h = (((end - beg) + nte - 1) / nte + 31) & ~31;
+      row0 = beg + (mt - g.tile_start[e]) * h;
+      row_end = min(row0 + h, end);
+    } else {
+      row0 = beg + (mt - g.tile_start[e]) * BM;
+      row_end = end;
+    }
+  }
   const int n0 = nt * BN;
   const int K = g.K;
   // top-1 combine: the token and gate of every row this lane will store,

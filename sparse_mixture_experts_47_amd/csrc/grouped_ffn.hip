@@ -45,17 +45,15 @@ __device__ __forceinline__ float silu(float g) {
 // (split == 2), go to a second table of bm/2-row tiles, so that an expert
 // just over a multiple of bm does not pay for a nearly empty bm-row tile.
 // Optional outputs (null to skip): seg_* = row range of each expert per
-// table, te* = expert of each tile (saves the per-block search), ts_w/te_w =
-// a third table over whole experts (every row in bm-row tiles, as split == 0).
+// table, te* = expert of each tile (saves the per-block search).
 __global__ __launch_bounds__(256) void tile_table_kernel(
     const int32_t* __restrict__ offsets, int E, int bm, int split, int32_t* __restrict__ ts,
     int32_t* __restrict__ ts_r, int32_t* __restrict__ sb, int32_t* __restrict__ se,
     int32_t* __restrict__ sb_r, int32_t* __restrict__ se_r, int32_t* __restrict__ te,
-    int32_t* __restrict__ te_r, int32_t* __restrict__ ts_w = nullptr,
-    int32_t* __restrict__ te_w = nullptr) {
-  __shared__ int sc[3][256];
+    int32_t* __restrict__ te_r) {
+  __shared__ int sc[2][256];
   const int e = threadIdx.x;
-  int n = 0, nr = 0, nw = 0, beg = 0, mid = 0, end = 0;
+  int n = 0, nr = 0, beg = 0, mid = 0, end = 0;
   if (e < E) {
     beg = offsets[e];
     end = offsets[e + 1];
@@ -70,19 +68,15 @@ __global__ __launch_bounds__(256) void tile_table_kernel(
       n = (cnt + bm - 1) / bm;
       mid = end;
     }
-    nw = (cnt + bm - 1) / bm;  // whole-expert table: every row in bm-row tiles
   }
   sc[0][e] = n;
   sc[1][e] = nr;
-  sc[2][e] = nw;
   __syncthreads();
   for (int o = 1; o < 256; o <<= 1) {
     const int v0 = e >= o ? sc[0][e - o] : 0, v1 = e >= o ? sc[1][e - o] : 0;
-    const int v2 = e >= o ? sc[2][e - o] : 0;
     __syncthreads();
     sc[0][e] += v0;
     sc[1][e] += v1;
-    sc[2][e] += v2;
     __syncthreads();
   }
   if (e < E) {
@@ -99,12 +93,6 @@ __global__ __launch_bounds__(256) void tile_table_kernel(
       for (int t = 0; t < n; ++t) te[t0 + t] = e;
     if (te_r)
       for (int t = 0; t < nr; ++t) te_r[t1 + t] = e;
-    if (ts_w) {
-      const int t2 = sc[2][e] - nw;
-      ts_w[e] = t2;
-      if (e == E - 1) ts_w[E] = sc[2][e];
-      for (int t = 0; t < nw; ++t) te_w[t2 + t] = e;
-    }
   }
 }
 
@@ -623,10 +611,11 @@ __global__ __launch_bounds__(NW * 64) void ffn_fp8_stream_kernel(Fp8Args g,
 #ifndef MOE_SPLIT_TAIL
 #define MOE_SPLIT_TAIL 2
 #endif
-// GEMM 1 runs over whole experts (no tail launch) from this many rows per
-// expert on average
-#ifndef MOE_G1_WHOLE_ROWS
-#define MOE_G1_WHOLE_ROWS 1536
+// From this many rows per expert on average (six or more 256-row tiles),
+// each expert's rows are split evenly over its 256-row tiles and there is
+// no tail launch
+#ifndef MOE_EVEN_ROWS
+#define MOE_EVEN_ROWS 1536
 #endif
 // GEMM 1 (SwiGLU, 256-row tiles) runs 8 waves (2 per SIMD); GEMM 2 with
 // 256-row tiles uses 256x256 tiles on 8 waves (128x64 per wave): fewer LDS
@@ -889,14 +878,12 @@ static size_t h_bytes(const moe_ffn_weights* w, moe_dtype act_dt, int max_rows) 
 
 // Tile tables after h (int32): tile_start and split-remainder tile_start
 // [E+1] each, segment bounds of both [E] x 4, the tile -> expert maps (main:
-// at most max_rows/128 + E tiles, remainder: at most 2E), then the
-// whole-expert table's tile_start [E+1] and tile -> expert map.
+// at most max_rows/128 + E tiles, remainder: at most 2E).
 struct TileTables {
-  int32_t *ts, *ts_r, *sb, *se, *sb_r, *se_r, *te, *te_r, *ts_w, *te_w;
+  int32_t *ts, *ts_r, *sb, *se, *sb_r, *se_r, *te, *te_r;
 };
 static size_t table_ints(int E, int max_rows) {
-  return (size_t)6 * E + 2 + (size_t)(max_rows / 128 + E + 1) + 2 * (size_t)E +
-         (size_t)(E + 1) + (size_t)(max_rows / 128 + E + 1);
+  return (size_t)6 * E + 2 + (size_t)(max_rows / 128 + E + 1) + 2 * (size_t)E;
 }
 static TileTables tile_tables(char* base, int E, int max_rows) {
   int32_t* p = (int32_t*)base;
@@ -909,8 +896,6 @@ static TileTables tile_tables(char* base, int E, int max_rows) {
   t.se_r = t.sb_r + E;
   t.te = t.se_r + E;
   t.te_r = t.te + (max_rows / 128 + E + 1);
-  t.ts_w = t.te_r + 2 * E;
-  t.te_w = t.ts_w + (E + 1);
   return t;
 }
 
@@ -984,24 +969,24 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
   const int bm = act_dt == MOE_F32 ? 64
                  : (avg_rows >= MOE_BM256_ROWS || (avg_rows >= 256 && d >= 4096)) ? 256
                                                                                   : 128;
-  const bool split = bm == 256 && avg_rows >= MOE_BM256_ROWS && MOE_SPLIT_TAIL;
-  // With many tiles per expert the tail launch serves GEMM 2 only: GEMM 1
-  // keeps each expert's tail in a partly filled last 256-row tile (a third
-  // table, whole experts). An XCD runs 4 M x 8 N tiles at once (groups of 8
-  // N tiles), so an expert of 4 full tiles plus a tail spans two such
-  // windows and streams its weights twice (GEMM 1 fetch 2.8 -> 5.3 GB on the
-  // Mixtral shape, the same time), while 8 tiles plus a tail add half of
-  // that and save the tail launch's re-read of every expert's weights (one
-  // GPU's EP-8 DeepSeek share, 2048 rows per expert: GEMM pair 5.82 ->
-  // 5.66 ms).
-  const bool g1_whole = split && avg_rows >= MOE_G1_WHOLE_ROWS;
+  // With many tiles per expert there is no tail launch: each expert's rows
+  // are split evenly over its ceil(rows / 256) tiles (heights a multiple of
+  // 32), so its tiles run at one pace and the waves' unused 32-row blocks
+  // skip their MFMAs. One GPU's EP-8 DeepSeek share (2048 rows per expert):
+  // grouped FFN 5.53 -> 5.44 ms against a GEMM 1 over whole experts (tail in
+  // a partly filled last tile) plus a GEMM 2 tail launch. On the Mixtral
+  // shape (4 tiles and a tail per expert) the even split is 6% slower: GEMM
+  // 2's 512 main tiles are exactly two rounds of the 256 CUs, 640 even ones
+  // start a third; an XCD runs 4 M x 8 N tiles at once, so the fifth M tile
+  // of an expert also re-streams its weights. DeepSeek shape: 1% slower.
+  const bool even = bm == 256 && avg_rows >= MOE_EVEN_ROWS;
+  const bool split = bm == 256 && avg_rows >= MOE_BM256_ROWS && MOE_SPLIT_TAIL && !even;
   if (act_dt == MOE_F32)
     tile_table_kernel<<<1, 256, 0, st>>>(offsets, E, bm, 0, tt.ts, nullptr, nullptr, nullptr,
                                          nullptr, nullptr, nullptr, nullptr);
   else
     tile_table_kernel<<<1, 256, 0, st>>>(offsets, E, bm, split ? MOE_SPLIT_TAIL : 0, tt.ts, tt.ts_r, tt.sb,
-                                         tt.se, tt.sb_r, tt.se_r, tt.te, tt.te_r,
-                                         g1_whole ? tt.ts_w : nullptr, tt.te_w);
+                                         tt.se, tt.sb_r, tt.se_r, tt.te, tt.te_r);
   s = launch_status("tile table");
   if (s != MOE_OK) return s;
   const int max_mt = (max_rows + bm - 1) / bm + E;
@@ -1037,11 +1022,6 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
   g1.seg_begin = tt.sb;
   g1.seg_end = tt.se;
   g1.tile_e = tt.te;
-  if (g1_whole) {
-    g1.tile_start = tt.ts_w;
-    g1.seg_begin = g1.seg_end = nullptr;
-    g1.tile_e = tt.te_w;
-  }
   Args g2 = base_args(h, w->w2, nullptr, w->b2, y_rows, F, d, E, max_mt, (int)w->act, offsets,
                       tt.ts);
   g2.group_n = bm == 256 ? gn256 : MOE_G2_GN;
@@ -1050,6 +1030,7 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
   g2.seg_begin = tt.sb;
   g2.seg_end = tt.se;
   g2.tile_e = tt.te;
+  g1.even = g2.even = even ? 1 : 0;
   g1.c_plane = (long long)max_rows * F;  // lo plane of the bf16 pair h
   g2.a_plane = (long long)max_rows * F;
   // remainder launches: same operands, the second table, 128-row tiles
@@ -1062,7 +1043,7 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
   hipError_t err;
   if (bm == 256) {
     err = launch_g1<256>(glu, pair, g1, st);
-    if (err == hipSuccess && split && !g1_whole) err = launch_g1<128>(glu, pair, g1r, st);
+    if (err == hipSuccess && split) err = launch_g1<128>(glu, pair, g1r, st);
     if (err == hipSuccess) err = launch_g2<256>(pair, ybf, g2, st);
     if (err == hipSuccess && split) err = launch_g2<128>(pair, ybf, g2r, st, true);
   } else {

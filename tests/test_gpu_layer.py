@@ -707,15 +707,15 @@ def test_grouped_ffn_256_row_tiles_with_tails(moe):
 
 
 @pytest.mark.parametrize("h_fp32", [False, True])
-def test_grouped_ffn_whole_expert_gemm1(moe, h_fp32):
-    """Experts averaging 1536 rows or more: GEMM 1 runs each expert whole on
-    256-row tiles (its tail in a partly filled last tile), GEMM 2 sends tails
-    of at most 128 rows to the 128-row launch. Tails of 1, 100, 208 (kept in
-    the main GEMM 2 table) and 20 rows, and an empty expert; bf16 h and the
-    fp32 hi + lo pair."""
-    cfg = W.REDUCED["c2"].with_(name="whole_expert_g1", n_tokens=1000, d_model=256, d_ff=512,
+def test_grouped_ffn_even_split(moe, h_fp32):
+    """Experts averaging 1536 rows or more: both GEMMs split each expert's
+    rows evenly over its 256-row tiles (heights a multiple of 32, no tail
+    launch): 2049 rows (eight tiles and a one-row ninth), 2404 (ten of
+    256, last 100), 2000 (eight of 256, last 208), 1300 (six of 224, last
+    180), and an empty expert; bf16 h and the fp32 hi + lo pair."""
+    cfg = W.REDUCED["c2"].with_(name="even_split", n_tokens=1000, d_model=256, d_ff=512,
                                 n_experts=5)
-    print("whole-expert GEMM 1, h_fp32", h_fp32, flush=True)
+    print("even row split, h_fp32", h_fp32, flush=True)
     inp = W.make_inputs(cfg, "cpu")
     host = host_inputs(inp)
     dev = to_device(inp)
