@@ -123,9 +123,14 @@ __device__ __forceinline__ int tile_expert(const int32_t* ts, int E, int mt) {
 }
 
 // ---------------------------------------------------------------- fp32 SIMT
-template <int MODE>
+// BM x BM output tiles on a 16 x 16 thread grid (BM / 16 square register
+// blocks), 64-wide K steps. BM = 32 when 64-row tiles would leave the chip
+// short of blocks: the fp32 path serves small layers (the tiny Switch
+// layer's GEMM 2 ran 9 blocks of 64 x 64 with one wave per SIMD, 20 us of
+// dependent FMAs per thread).
+template <int MODE, int BM>
 __global__ __launch_bounds__(256) void ggemm_f32_kernel(GemmArgs g) {
-  constexpr int BM = 64, BN = 64, BK = 16, TM = 4, TN = 4;
+  constexpr int BN = BM, BK = 64, TM = BM / 16, TN = BN / 16;
   constexpr int NB = MODE == MODE_GLU ? 2 : 1;
   __shared__ float As[BK][BM + 4];
   __shared__ float Bs[NB][BK][BN + 4];
@@ -148,19 +153,28 @@ __global__ __launch_bounds__(256) void ggemm_f32_kernel(GemmArgs g) {
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[b][i][j] = 0.f;
-  // Each thread stages 4 consecutive K values of one A row and of one B row
-  // per plane (BM x BK = BN x BK = 4 x 256), loaded one K step ahead into
-  // registers; rows past the tile and K past the end load zeros.
-  static_assert(BM * BK == 4 * 256 && BN * BK == 4 * 256, "one 4-vector per thread");
-  const int lm = tid >> 2, lk = (tid & 3) * 4;
+  // Staging: BM rows x 16 groups of 4 consecutive K values per operand
+  // (plane), G groups a thread (row (tid + 256 u) / 16, group tid % 16),
+  // loaded one K step ahead into registers; rows past the tile and K past
+  // the end load zeros. 64-wide K steps: on the small shapes of this path
+  // each step's global-load round trip counts. The products of an output
+  // add in k order whatever the tiling.
+  constexpr int G = BM * BK / 4 / 256;
+  static_assert(G >= 1 && G * 256 * 4 == BM * BK, "whole 4-vectors per thread");
+  const int lk = (tid % (BK / 4)) * 4;
+  int lm[G];
+  const float* arow_p[G];
+  const float* brow_p[NB][G];
   const bool vec = (K & 3) == 0;
-  const int arow_l = row0 + lm;
-  const float* arow_p =
-      arow_l < row_end ? A + (size_t)(g.a_rows ? g.a_rows[arow_l] : arow_l) * K : nullptr;
-  const float* brow_p[NB];
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
-    brow_p[b] = n0 + lm < Nout ? Bp[b] + (size_t)(n0 + lm) * K : nullptr;
+  for (int u = 0; u < G; ++u) {
+    lm[u] = (tid + 256 * u) / (BK / 4);
+    const int ar = row0 + lm[u];
+    arow_p[u] = ar < row_end ? A + (size_t)(g.a_rows ? g.a_rows[ar] : ar) * K : nullptr;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      brow_p[b][u] = n0 + lm[u] < Nout ? Bp[b] + (size_t)(n0 + lm[u]) * K : nullptr;
+  }
   auto load4 = [&](const float* row, int k) {
     f32x4_t v = {0.f, 0.f, 0.f, 0.f};
     if (!row) return v;
@@ -170,22 +184,29 @@ __global__ __launch_bounds__(256) void ggemm_f32_kernel(GemmArgs g) {
       if (k + q < K) v[q] = row[k + q];
     return v;
   };
-  f32x4_t ar = load4(arow_p, lk), br[NB];
+  f32x4_t ar[G], br[NB][G];
+  auto fetch = [&](int k0) {
 #pragma unroll
-  for (int b = 0; b < NB; ++b) br[b] = load4(brow_p[b], lk);
+    for (int u = 0; u < G; ++u) {
+      ar[u] = load4(arow_p[u], k0 + lk);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) br[b][u] = load4(brow_p[b][u], k0 + lk);
+    }
+  };
+  fetch(0);
   for (int k0 = 0; k0 < K; k0 += BK) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) As[lk + q][lm] = ar[q];
+    for (int u = 0; u < G; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) As[lk + q][lm[u]] = ar[u][q];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) Bs[b][lk + q][lm] = br[b][q];
-    __syncthreads();
-    if (k0 + BK < K) {
-      ar = load4(arow_p, k0 + BK + lk);
+      for (int u = 0; u < G; ++u)
 #pragma unroll
-      for (int b = 0; b < NB; ++b) br[b] = load4(brow_p[b], k0 + BK + lk);
-    }
+        for (int q = 0; q < 4; ++q) Bs[b][lk + q][lm[u]] = br[b][u][q];
+    __syncthreads();
+    if (k0 + BK < K) fetch(k0 + BK);
 #pragma unroll
     for (int kk = 0; kk < BK; ++kk) {
       float a[TM];
@@ -966,7 +987,11 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
   // partly filled tiles; measured faster with d_model = 1024). With 256-row
   // tiles, short tails of the experts run as a second launch of 128-row tiles.
   const int avg_rows = max_rows / E;
-  const int bm = act_dt == MOE_F32 ? 64
+  // fp32: 32-row tiles while 64-row ones give fewer blocks than two per CU
+  const bool f32_small =
+      (size_t)(max_rows / 64 + E) * (size_t)((F > d ? F : d) + 63) / 64 <
+      (size_t)2 * device_cu_count();
+  const int bm = act_dt == MOE_F32 ? (f32_small ? 32 : 64)
                  : (avg_rows >= MOE_BM256_ROWS || (avg_rows >= 256 && d >= 4096)) ? 256
                                                                                   : 128;
   // With many tiles per expert there is no tail launch: each expert's rows
@@ -996,12 +1021,20 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
                 tile_start, row_index, nullptr, nullptr};
     GemmArgs a2{h, w->w2, nullptr, w->b2, y_rows, F, d, E, max_mt, (int)w->act, offsets,
                 tile_start, nullptr, out_token, out_gate};
-    const int g1 = max_mt * ((F + 63) / 64), g2 = max_mt * ((d + 63) / 64);
-    if (glu)
-      ggemm_f32_kernel<MODE_GLU><<<g1, 256, 0, st>>>(a1);
-    else
-      ggemm_f32_kernel<MODE_ACT><<<g1, 256, 0, st>>>(a1);
-    ggemm_f32_kernel<MODE_OUT><<<g2, 256, 0, st>>>(a2);
+    const int g1 = max_mt * ((F + bm - 1) / bm), g2 = max_mt * ((d + bm - 1) / bm);
+    if (bm == 32) {
+      if (glu)
+        ggemm_f32_kernel<MODE_GLU, 32><<<g1, 256, 0, st>>>(a1);
+      else
+        ggemm_f32_kernel<MODE_ACT, 32><<<g1, 256, 0, st>>>(a1);
+      ggemm_f32_kernel<MODE_OUT, 32><<<g2, 256, 0, st>>>(a2);
+    } else {
+      if (glu)
+        ggemm_f32_kernel<MODE_GLU, 64><<<g1, 256, 0, st>>>(a1);
+      else
+        ggemm_f32_kernel<MODE_ACT, 64><<<g1, 256, 0, st>>>(a1);
+      ggemm_f32_kernel<MODE_OUT, 64><<<g2, 256, 0, st>>>(a2);
+    }
     return launch_status("grouped FFN fp32");
   }
 

@@ -33,13 +33,12 @@ inline int select_blocks(int N) {
 
 // ---------------------------------------------------------------- GEMM
 // out[t][c] = sum_k x[t][k] * W[c][k] with W = [w_gate ; w_noise] (E or 2E
-// rows), fp32 accumulation. Tiles: BM tokens x BN router columns, BK = 16,
-// each thread a 4x4 register block. x is bf16 or fp32.
-template <int BM, int BN, bool XBF16>
+// rows), fp32 accumulation in k order. Tiles: BM tokens x BN router columns,
+// BK-wide K steps, each thread a TM x TN register block. x is bf16 or fp32.
+template <int BM, int BN, int BK, int TM, int TN, bool XBF16>
 __global__ __launch_bounds__(kThreads) void router_gemm_kernel(
     const void* __restrict__ xv, const float* __restrict__ wg, const float* __restrict__ wn,
     float* __restrict__ out, int N, int d, int E, int E2) {
-  constexpr int BK = 16, TM = 4, TN = 4;
   static_assert((BM / TM) * (BN / TN) == kThreads, "tile");
   __shared__ float As[BK][BM + 4];
   __shared__ float Bs[BK][BN + 4];
@@ -855,18 +854,21 @@ moe_status router_launch(const moe_router_params* p, const void* x, moe_dtype x_
       }
       }
     } else {
+      // a few columns: 64-token tiles with 64-wide K steps (the tiny Switch
+      // layer, 256 tokens x d 64 x 4 experts: one 256-token block walking
+      // four 16-wide steps, each a global-load round trip, took 9.1 us)
       if (E2 <= 16) {
-        dim3 grid((N + 255) / 256, 1);
+        dim3 grid((N + 63) / 64, 1);
         if (x_dt == MOE_BF16)
-          router_gemm_kernel<256, 16, true><<<grid, kThreads, 0, st>>>(x, w_gate, p->w_noise, raw, N, d, E, E2);
+          router_gemm_kernel<64, 16, 64, 2, 2, true><<<grid, kThreads, 0, st>>>(x, w_gate, p->w_noise, raw, N, d, E, E2);
         else
-          router_gemm_kernel<256, 16, false><<<grid, kThreads, 0, st>>>(x, w_gate, p->w_noise, raw, N, d, E, E2);
+          router_gemm_kernel<64, 16, 64, 2, 2, false><<<grid, kThreads, 0, st>>>(x, w_gate, p->w_noise, raw, N, d, E, E2);
       } else {
         dim3 grid((N + 63) / 64, (E2 + 63) / 64);
         if (x_dt == MOE_BF16)
-          router_gemm_kernel<64, 64, true><<<grid, kThreads, 0, st>>>(x, w_gate, p->w_noise, raw, N, d, E, E2);
+          router_gemm_kernel<64, 64, 16, 4, 4, true><<<grid, kThreads, 0, st>>>(x, w_gate, p->w_noise, raw, N, d, E, E2);
         else
-          router_gemm_kernel<64, 64, false><<<grid, kThreads, 0, st>>>(x, w_gate, p->w_noise, raw, N, d, E, E2);
+          router_gemm_kernel<64, 64, 16, 4, 4, false><<<grid, kThreads, 0, st>>>(x, w_gate, p->w_noise, raw, N, d, E, E2);
       }
       moe_status s = launch_status("router_gemm");
       if (s != MOE_OK) return s;

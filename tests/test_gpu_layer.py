@@ -802,3 +802,44 @@ def test_grouped_ffn_short_k_pipeline_edges(moe, d_model, d_ff):
     print("  max|dy|/rms =", err, flush=True)
     assert err <= out_tol(cfg)
     assert np.all(got[R:] == 7.0)
+
+
+@pytest.mark.parametrize("n_rows,d_model,d_ff,act", [(300, 64, 256, W.ACT_RELU),
+                                                     (5000, 128, 1024, W.ACT_RELU),
+                                                     (700, 64, 192, W.ACT_SWIGLU),
+                                                     (6000, 192, 512, W.ACT_GELU)])
+def test_grouped_ffn_fp32_tilings(moe, n_rows, d_model, d_ff, act):
+    """fp32 activations take 32-row tiles while 64-row ones would give fewer
+    blocks than two per CU, else 64-row tiles; 64-wide K steps with a ragged
+    last step (d_model 192, d_ff 192); ragged experts, an empty and a
+    one-row one; ReLU/GELU with biases and SwiGLU without."""
+    glu = act == W.ACT_SWIGLU
+    cfg = W.REDUCED["c1"].with_(name="fp32_tilings", n_tokens=max(n_rows // 2, 64),
+                                d_model=d_model, d_ff=d_ff, act=act, ffn_bias=not glu)
+    print("fp32 grouped FFN:", n_rows, "rows, d_model", d_model, "d_ff", d_ff, flush=True)
+    inp = W.make_inputs(cfg, "cpu")
+    host = host_inputs(inp)
+    dev = to_device(inp)
+    E = cfg.n_experts
+    rng = np.random.default_rng(21)
+    frac = rng.random(E)
+    frac[0] = 0.0
+    counts = np.floor(frac / frac.sum() * (n_rows - 1)).astype(np.int64)
+    counts[1] += 1
+    counts[-1] += n_rows - counts.sum()
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offs[-1])
+    tok = rng.integers(0, cfg.n_tokens, size=R)
+    x = dev["x"][torch.from_numpy(tok).cuda()].contiguous()
+    y = torch.full((R + 5, cfg.d_model), 7.0, dtype=torch.float32, device="cuda")
+    w, keep = moe.ffn_weights(dev["w1"], dev["w2"], dev["w3"], cfg.act, dev["b1"], dev["b2"])
+    moe.moe_grouped_ffn(w, x, torch.from_numpy(offs).cuda(), y, max_rows=R)
+    torch.cuda.synchronize()
+    X64 = oracle.decode_rows(host["x"][tok], cfg.x_dtype)
+    ref = oracle.ffn_for_assignments(np.arange(R), np.repeat(np.arange(E), counts), X64,
+                                     cfg.act, cfg.w_dtype, experts_of(host))
+    got = to_np(y)
+    err = rel_err(got[:R], ref)
+    print("  max|dy|/rms =", err, flush=True)
+    assert err <= out_tol(cfg)
+    assert np.all(got[R:] == 7.0)
