@@ -124,8 +124,8 @@ __device__ __forceinline__ int tile_expert(const int32_t* ts, int E, int mt) {
 
 // ---------------------------------------------------------------- fp32 SIMT
 // BM x BM output tiles on a 16 x 16 thread grid (BM / 16 square register
-// blocks), 64-wide K steps. BM = 32 when 64-row tiles would leave the chip
-// short of blocks: the fp32 path serves small layers (the tiny Switch
+// blocks), 64-wide K steps. BM = 32 or 16 when 64-row tiles would leave the
+// chip short of blocks: the fp32 path serves small layers (the tiny Switch
 // layer's GEMM 2 ran 9 blocks of 64 x 64 with one wave per SIMD, 20 us of
 // dependent FMAs per thread).
 template <int MODE, int BM>
@@ -987,11 +987,15 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
   // partly filled tiles; measured faster with d_model = 1024). With 256-row
   // tiles, short tails of the experts run as a second launch of 128-row tiles.
   const int avg_rows = max_rows / E;
-  // fp32: 32-row tiles while 64-row ones give fewer blocks than two per CU
-  const bool f32_small =
-      (size_t)(max_rows / 64 + E) * (size_t)((F > d ? F : d) + 63) / 64 <
-      (size_t)2 * device_cu_count();
-  const int bm = act_dt == MOE_F32 ? (f32_small ? 32 : 64)
+  // fp32: 64-row tiles, 32-row ones while those would give fewer blocks than
+  // two per CU, 16-row ones below half a block per CU (the tiny Switch
+  // layer: grouped FFN 39 -> 31 -> 26 us from 64 to 32 to 16 rows)
+  const size_t f32_blocks64 =
+      (size_t)(max_rows / 64 + E) * (size_t)(((F > d ? F : d) + 63) / 64);
+  const int f32_bm = f32_blocks64 < (size_t)device_cu_count() / 2   ? 16
+                     : f32_blocks64 < (size_t)2 * device_cu_count() ? 32
+                                                                    : 64;
+  const int bm = act_dt == MOE_F32 ? f32_bm
                  : (avg_rows >= MOE_BM256_ROWS || (avg_rows >= 256 && d >= 4096)) ? 256
                                                                                   : 128;
   // With many tiles per expert there is no tail launch: each expert's rows
@@ -1022,7 +1026,13 @@ moe_status grouped_ffn_launch(const moe_ffn_weights* w, const void* x_rows, moe_
     GemmArgs a2{h, w->w2, nullptr, w->b2, y_rows, F, d, E, max_mt, (int)w->act, offsets,
                 tile_start, nullptr, out_token, out_gate};
     const int g1 = max_mt * ((F + bm - 1) / bm), g2 = max_mt * ((d + bm - 1) / bm);
-    if (bm == 32) {
+    if (bm == 16) {
+      if (glu)
+        ggemm_f32_kernel<MODE_GLU, 16><<<g1, 256, 0, st>>>(a1);
+      else
+        ggemm_f32_kernel<MODE_ACT, 16><<<g1, 256, 0, st>>>(a1);
+      ggemm_f32_kernel<MODE_OUT, 16><<<g2, 256, 0, st>>>(a2);
+    } else if (bm == 32) {
       if (glu)
         ggemm_f32_kernel<MODE_GLU, 32><<<g1, 256, 0, st>>>(a1);
       else

@@ -805,14 +805,17 @@ def test_grouped_ffn_short_k_pipeline_edges(moe, d_model, d_ff):
 
 
 @pytest.mark.parametrize("n_rows,d_model,d_ff,act", [(300, 64, 256, W.ACT_RELU),
-                                                     (5000, 128, 1024, W.ACT_RELU),
                                                      (700, 64, 192, W.ACT_SWIGLU),
+                                                     (2000, 128, 512, W.ACT_RELU),
+                                                     (3000, 192, 320, W.ACT_SWIGLU),
+                                                     (5000, 128, 1024, W.ACT_RELU),
                                                      (6000, 192, 512, W.ACT_GELU)])
 def test_grouped_ffn_fp32_tilings(moe, n_rows, d_model, d_ff, act):
-    """fp32 activations take 32-row tiles while 64-row ones would give fewer
-    blocks than two per CU, else 64-row tiles; 64-wide K steps with a ragged
-    last step (d_model 192, d_ff 192); ragged experts, an empty and a
-    one-row one; ReLU/GELU with biases and SwiGLU without."""
+    """fp32 activations on 16-, 32- and 64-row tiles (two cases each on a
+    256-CU part: fewer 64-row blocks than half a CU, than two per CU, or
+    more); 64-wide K steps with a ragged last step (192, 320); ragged
+    experts, an empty and a one-row one; ReLU/GELU with biases and SwiGLU
+    without."""
     glu = act == W.ACT_SWIGLU
     cfg = W.REDUCED["c1"].with_(name="fp32_tilings", n_tokens=max(n_rows // 2, 64),
                                 d_model=d_model, d_ff=d_ff, act=act, ffn_bias=not glu)
