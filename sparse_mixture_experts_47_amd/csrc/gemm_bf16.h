@@ -140,7 +140,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 // first RD of them followed by one LDS read. ilv_tail: the first H = MF/2
 // MFMAs each followed by up to VPM global loads (LPT in all), the other H by
 // up to RPM LDS reads (RD in all) -- the reads come after the loads, which
-// write LDS.
+// write LDS. Group masks: 0x008 MFMA, 0x100 LDS read, 0x230 vector-memory
+// read or write and LDS write (a direct-to-LDS load matches as either).
 template <int I, int MF, int RD>
 __device__ __forceinline__ void ilv_reads() {
   if constexpr (I < MF) {
