@@ -529,7 +529,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_dlds_kernel(Args 
         }
         if (col + 4 <= g.n_valid) {
           if (F32OUT) {
-            *(f32x4_t*)((float*)Cb + o) = v;
+            // fp32 rows are read back only by a later call (combine or the
+            // caller): streaming stores (DeepSeek-shaped grouped FFN -0.8%,
+            // one GPU's EP-8 share -1.1%, Mixtral shape unchanged; with the
+            // backward's fp32 gradient stores, its expert backward -2.5%)
+            __builtin_nontemporal_store(v, (f32x4_t*)((float*)Cb + o));
           } else {
             uint16_t hb[4];
 #pragma unroll

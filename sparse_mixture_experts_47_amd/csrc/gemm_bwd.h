@@ -447,7 +447,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bwd_kernel(BwdArgs g) {
             *(u32x2_t*)(g.dpre + o + g.N) = u32x2_t{moe::pack_bf16x2(du[0], du[1]),
                                                     moe::pack_bf16x2(du[2], du[3])};
           } else {
-            *(f32x4_t*)((float*)g.C0 + (size_t)row * g.ldc + col) = v;
+            __builtin_nontemporal_store(v, (f32x4_t*)((float*)g.C0 + (size_t)row * g.ldc + col));
           }
         } else {
           const int m = m0 + lr;
@@ -457,8 +457,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bwd_kernel(BwdArgs g) {
           if (g.c_bf16)
             *(u32x2_t*)((uint16_t*)C + o) = u32x2_t{moe::pack_bf16x2(v[0], v[1]),
                                                     moe::pack_bf16x2(v[2], v[3])};
-          else
-            *(f32x4_t*)((float*)C + o) = v;
+          else  // written once, read by a later call: a streaming store
+            __builtin_nontemporal_store(v, (f32x4_t*)((float*)C + o));
         }
       }
     }
