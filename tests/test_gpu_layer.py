@@ -846,3 +846,127 @@ def test_grouped_ffn_fp32_tilings(moe, n_rows, d_model, d_ff, act):
     print("  max|dy|/rms =", err, flush=True)
     assert err <= out_tol(cfg)
     assert np.all(got[R:] == 7.0)
+
+
+# Row counts per expert (4 experts): 256-row tiles (average at least 512) with
+# an empty expert, a partly filled last tile (700), a 66-row tail launch
+# (1090) and a one-row tail (513); or 128-row tiles (an empty expert, one
+# row, a tile plus one row, a ragged 300).
+_COUNTS_256 = np.array([0, 700, 1090, 513])
+_COUNTS_128 = np.array([0, 1, 129, 300])
+
+
+def _ffn_case(moe, act, d_model, d_ff, big, n_tokens):
+    cfg = W.REDUCED["c2"].with_(name="ffn_variants", n_tokens=n_tokens, n_experts=4,
+                                d_model=d_model, d_ff=d_ff, act=act,
+                                ffn_bias=act != W.ACT_SWIGLU)
+    inp = W.make_inputs(cfg, "cpu")
+    counts = _COUNTS_256 if big else _COUNTS_128
+    assert (counts.sum() // 4 >= 512) == big
+    return cfg, host_inputs(inp), to_device(inp), counts
+
+
+def _bf16_y_tol(ref, base):
+    # bf16 output rows: round to nearest moves a value v by at most 2^-8 |v|
+    rms = np.sqrt(np.mean(np.asarray(ref, np.float64) ** 2))
+    return base + 2.0 ** -8 * (np.max(np.abs(ref)) / rms + base)
+
+
+@pytest.mark.parametrize("act,h32,ybf,d_model,d_ff,big", [
+    (W.ACT_SWIGLU, True, True, 256, 256, False),
+    (W.ACT_SWIGLU, True, True, 192, 192, False),
+    (W.ACT_RELU, False, True, 192, 192, False),
+    (W.ACT_GELU, True, False, 192, 320, False),
+    (W.ACT_RELU, False, True, 256, 256, True),
+    (W.ACT_SWIGLU, False, True, 384, 256, True),
+    (W.ACT_SWIGLU, True, True, 192, 192, True),
+    (W.ACT_RELU, False, True, 192, 320, True),
+    (W.ACT_GELU, True, False, 192, 320, True)])
+def test_grouped_ffn_epilogue_variants(moe, act, h32, ybf, d_model, d_ff, big):
+    """The GEMM instances each combination of options selects, on 256-row
+    tiles (with the 128-row tail launches) and on 128-row tiles: gated or
+    plain activation epilogue (with biases), bf16 h or fp32 h as a hi + lo
+    pair, fp32 or bf16 output rows, and 256-, 128- or 64-column tiles of
+    either GEMM (d_model a multiple of 256, of 128 only, or of 64 only;
+    d_ff likewise). Rows gathered through a row index; rows past offsets[E]
+    untouched."""
+    cfg, host, dev, counts = _ffn_case(moe, act, d_model, d_ff, big, n_tokens=1500)
+    print("grouped FFN variant: act", act, "h_fp32", h32, "bf16 y", ybf, "d_model", d_model,
+          "d_ff", d_ff, "256-row tiles" if big else "128-row tiles", flush=True)
+    E = cfg.n_experts
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offs[-1])
+    tok = np.random.default_rng(d_model + d_ff + int(big)).integers(0, cfg.n_tokens, size=R)
+    ydt = torch.bfloat16 if ybf else torch.float32
+    y = torch.full((R + 5, d_model), 7.0, dtype=ydt, device="cuda")
+    w, keep = moe.ffn_weights(dev["w1"], dev["w2"], dev["w3"], cfg.act, dev.get("b1"),
+                              dev.get("b2"), h_fp32=h32)
+    moe.moe_grouped_ffn(w, dev["x"], torch.from_numpy(offs).cuda(), y,
+                        row_index=torch.from_numpy(tok.astype(np.int32)).cuda(), max_rows=R)
+    torch.cuda.synchronize()
+    X64 = oracle.decode_rows(host["x"][tok], cfg.x_dtype)
+    ref = oracle.ffn_for_assignments(np.arange(R), np.repeat(np.arange(E), counts), X64,
+                                     cfg.act, cfg.w_dtype, experts_of(host))
+    got = to_np(y)
+    base = 1e-3 if h32 else out_tol(cfg)
+    tol = _bf16_y_tol(ref, base) if ybf else base
+    err = rel_err(got[:R], ref)
+    print("  max|dy|/rms =", err, "bar", tol, flush=True)
+    assert err <= tol
+    assert np.all(got[R:] == 7.0)
+
+
+@pytest.mark.parametrize("act,h32,d_model,d_ff,big", [
+    (W.ACT_SWIGLU, False, 384, 256, True),
+    (W.ACT_SWIGLU, False, 192, 192, True),
+    (W.ACT_SWIGLU, True, 192, 192, True),
+    (W.ACT_RELU, True, 192, 320, False),
+    (W.ACT_GELU, False, 256, 256, True)])
+def test_grouped_ffn_combine_top1_tilings(moe, act, h32, d_model, d_ff, big):
+    """The top-1 combine in GEMM 2's epilogue (each packed row's output,
+    times its token's gate, stored to the token's row) on the column tilings
+    and tile heights the plain grouped FFN uses, with bf16 or fp32 h:
+    y[t] = gate[t] * FFN_e(x[t]) for kept tokens, exactly 0 for tokens whose
+    assignment was dropped."""
+    cfg, host, dev, counts = _ffn_case(moe, act, d_model, d_ff, big, n_tokens=2600)
+    print("top-1 combine in GEMM 2: act", act, "h_fp32", h32, "d_model", d_model, "d_ff", d_ff,
+          "256-row tiles" if big else "128-row tiles", flush=True)
+    E, N = cfg.n_experts, cfg.n_tokens
+    rng = np.random.default_rng(d_model * 7 + d_ff + int(big))
+    R = int(counts.sum())
+    assert R <= N
+    perm = rng.permutation(N)[:R].astype(np.int32)        # kept tokens in packed order
+    expert = np.repeat(np.arange(E), counts)
+    row_of = np.full((N, 1), -1, np.int32)
+    row_of[perm, 0] = np.arange(R, dtype=np.int32)
+    gates = np.zeros((N, 1), np.float32)
+    gates[perm, 0] = rng.uniform(0.05, 1.0, size=R).astype(np.float32)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    y = torch.full((N, d_model), 7.0, dtype=torch.float32, device="cuda")
+    w, keep = moe.ffn_weights(dev["w1"], dev["w2"], dev["w3"], cfg.act, dev.get("b1"),
+                              dev.get("b2"), h_fp32=h32)
+    perm_d = torch.from_numpy(perm).cuda()
+    moe.moe_grouped_ffn_combine_top1(w, dev["x"], torch.from_numpy(offs).cuda(), perm_d,
+                                     torch.from_numpy(row_of).cuda(),
+                                     torch.from_numpy(gates).cuda(), y, row_index=perm_d,
+                                     max_rows=R)
+    torch.cuda.synchronize()
+    X64 = oracle.decode_rows(host["x"][perm], cfg.x_dtype)
+    ffn = oracle.ffn_for_assignments(np.arange(R), expert, X64, cfg.act, cfg.w_dtype,
+                                     experts_of(host))
+    ref = np.zeros((N, d_model))
+    ref[perm] = gates[perm].astype(np.float64) * ffn
+    got = to_np(y)
+    dropped = row_of[:, 0] < 0
+    assert dropped.sum() == N - R
+    assert np.all(got[dropped] == 0.0)
+    # the expert outputs' bar is normwise over the outputs themselves: the
+    # kept rows divided by their gates (one fp32 rounding each, from the
+    # product) against the oracle's ungated FFN rows; with the gated rows the
+    # rms shrinks by the gates' spread while the largest errors sit on rows
+    # of large gates
+    g = gates[perm].astype(np.float64)
+    err = rel_err(got[perm].astype(np.float64) / g, ffn)
+    err_gated = rel_err(got[perm], ref[perm])
+    print("  max|dy|/rms =", err, "(gated rows:", err_gated, ")", flush=True)
+    assert err <= (1e-3 if h32 else out_tol(cfg))
