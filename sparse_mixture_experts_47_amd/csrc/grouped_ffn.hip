@@ -841,11 +841,13 @@ hipError_t launch_g2_k(bool pair, bool ybf, const moe_gemm::Args& g2, hipStream_
     return ybf ? run_gemm<BM, 64, 2, 1, EPI_OUT, OUT_BF16, 2, MOE_GEMM_BK, MOE_G2_PAIR_WGM>(gp, 1, st)
                : run_gemm<BM, 64, 2, 1, EPI_OUT, OF32, 2, MOE_GEMM_BK, MOE_G2_PAIR_WGM>(gp, 1, st);
   }
-  if (MOE_G2_WIDE && BM == 256 && g2.Nrows % 256 == 0)
-    return ybf ? run_gemm<BM, 256, 1, 1, EPI_OUT, OUT_BF16, MOE_G2_WIDE_WGN, MOE_GEMM_BK,
-                          MOE_G2_WIDE_WGM>(g2, 1, st)
-               : run_gemm<BM, 256, 1, 1, EPI_OUT, OF32, MOE_G2_WIDE_WGN, MOE_GEMM_BK,
-                          MOE_G2_WIDE_WGM>(g2, 1, st);
+  if constexpr (MOE_G2_WIDE && BM == 256) {  // (no 128-row instances of the wide tiles)
+    if (g2.Nrows % 256 == 0)
+      return ybf ? run_gemm<BM, 256, 1, 1, EPI_OUT, OUT_BF16, MOE_G2_WIDE_WGN, MOE_GEMM_BK,
+                            MOE_G2_WIDE_WGM>(g2, 1, st)
+                 : run_gemm<BM, 256, 1, 1, EPI_OUT, OF32, MOE_G2_WIDE_WGN, MOE_GEMM_BK,
+                            MOE_G2_WIDE_WGM>(g2, 1, st);
+  }
   if (n2)
     return ybf ? run_gemm<BM, 128, 1, 1, EPI_OUT, OUT_BF16, MOE_G2_WGN>(g2, 1, st)
                : run_gemm<BM, 128, 1, 1, EPI_OUT, OF32, MOE_G2_WGN>(g2, 1, st);
