@@ -809,7 +809,8 @@ def test_grouped_ffn_short_k_pipeline_edges(moe, d_model, d_ff):
                                                      (2000, 128, 512, W.ACT_RELU),
                                                      (3000, 192, 320, W.ACT_SWIGLU),
                                                      (5000, 128, 1024, W.ACT_RELU),
-                                                     (6000, 192, 512, W.ACT_GELU)])
+                                                     (6000, 192, 512, W.ACT_GELU),
+                                                     (6000, 192, 512, W.ACT_SWIGLU)])
 def test_grouped_ffn_fp32_tilings(moe, n_rows, d_model, d_ff, act):
     """fp32 activations on 16-, 32- and 64-row tiles (two cases each on a
     256-CU part: fewer 64-row blocks than half a CU, than two per CU, or
@@ -970,3 +971,83 @@ def test_grouped_ffn_combine_top1_tilings(moe, act, h32, d_model, d_ff, big):
     err_gated = rel_err(got[perm], ref[perm])
     print("  max|dy|/rms =", err, "(gated rows:", err_gated, ")", flush=True)
     assert err <= (1e-3 if h32 else out_tol(cfg))
+
+
+@pytest.mark.parametrize("k", [3, 12])
+@pytest.mark.parametrize("yt,st,ot", [(a, b, c) for a in ("f32", "bf16")
+                                      for b in (None, "f32", "bf16") for c in ("f32", "bf16")])
+def test_combine_dtype_combinations(moe, yt, st, ot, k):
+    """moe_combine for every mix of fp32 / bf16 expert rows, shared-expert
+    rows (or none) and output, with k = 3 (one chunk a thread) and k = 12
+    (the wide form for k > 8): gate-weighted sums in slot order against the
+    oracle's combine, dropped slots and a token with every slot dropped
+    contributing nothing."""
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    rng = np.random.default_rng(k * 31 + len(yt + str(st) + ot))
+    N, d = 40, 320
+    R = N * k
+    row_of = rng.permutation(R).astype(np.int32).reshape(N, k).copy()
+    row_of[rng.random((N, k)) < 0.25] = -1
+    row_of[7] = -1
+    gates = rng.random((N, k)).astype(np.float32)
+    yr = torch.randn((R, d)).to(dt[yt])
+    ysh = None if st is None else torch.randn((N, d)).to(dt[st])
+    out = torch.empty((N, d), dtype=dt[ot], device="cuda")
+    moe.moe_combine(yr.cuda(), torch.from_numpy(row_of).cuda(), torch.from_numpy(gates).cuda(),
+                    out, y_shared=None if ysh is None else ysh.cuda())
+    torch.cuda.synchronize()
+    yr64 = yr.double().numpy()
+    Yexp = np.zeros((N, k, d))
+    for t in range(N):
+        for j in range(k):
+            if row_of[t, j] >= 0:
+                Yexp[t, j] = yr64[row_of[t, j]]
+    ref = oracle.combine(row_of, gates, Yexp, None if ysh is None else ysh.double().numpy())
+    got = to_np(out)
+    # inputs are exact in fp64: fp32 output carries only fp32 rounding, bf16
+    # output one more rounding of at most 2^-8 relative
+    assert rel_err(got, ref) <= (1e-6 if ot == "f32" else _bf16_y_tol(ref, 1e-6))
+    if st is None:
+        assert np.all(got[7] == 0.0)
+
+
+@pytest.mark.parametrize("act,ybf", [(W.ACT_GELU, False), (W.ACT_GELU, True),
+                                     (W.ACT_SWIGLU, True)])
+def test_fp8_plain_activation_and_bf16_rows(moe, act, ybf):
+    """fp8 weights with a plain (GELU) activation or SwiGLU, fp32 or bf16
+    output rows, on the streaming path (max_rows <= 8 per expert) and the
+    64-row-group path (larger max_rows): both match the oracle, rows past
+    offsets[E] untouched."""
+    cfg = W.REDUCED["c5"].with_(name="fp8_variants", act=act)
+    print("fp8 weights: act", act, "bf16 y", ybf, flush=True)
+    inp = W.make_inputs(cfg, "cpu")
+    host = host_inputs(inp)
+    dev = to_device(inp)
+    E, d = cfg.n_experts, cfg.d_model
+    rng = np.random.default_rng(13 + act)
+    counts = rng.integers(0, 9, size=E)
+    counts[0] = 0
+    counts[1], counts[2], counts[3] = 1, 16, 33
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offs[-1])
+    assert R <= 8 * E
+    tok = rng.integers(0, cfg.n_tokens, size=R)
+    w, keep = moe.ffn_weights(dev["w1"], dev["w2"], dev.get("w3"), cfg.act, None, None,
+                              dev["s1"], dev.get("s3"), dev["s2"])
+    X64 = oracle.decode_rows(host["x"][tok], cfg.x_dtype)
+    ref = oracle.ffn_for_assignments(np.arange(R), np.repeat(np.arange(E), counts), X64,
+                                     cfg.act, cfg.w_dtype, experts_of(host))
+    tol = _bf16_y_tol(ref, TOL_FP8) if ybf else TOL_FP8
+    for max_rows in (R, 8 * E + 1):
+        idx = np.zeros(max_rows, np.int32)
+        idx[:R] = tok
+        y = torch.full((max_rows + 2, d), 7.0, dtype=torch.bfloat16 if ybf else torch.float32,
+                       device="cuda")
+        moe.moe_grouped_ffn(w, dev["x"], torch.from_numpy(offs).cuda(), y,
+                            row_index=torch.from_numpy(idx).cuda(), max_rows=max_rows)
+        torch.cuda.synchronize()
+        got = to_np(y)
+        err = rel_err(got[:R], ref)
+        print("  max_rows", max_rows, "max|dy|/rms =", err, "bar", tol, flush=True)
+        assert err <= tol
+        assert np.all(got[R:] == 7.0)
