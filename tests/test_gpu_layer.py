@@ -1051,3 +1051,35 @@ def test_fp8_plain_activation_and_bf16_rows(moe, act, ybf):
         print("  max_rows", max_rows, "max|dy|/rms =", err, "bar", tol, flush=True)
         assert err <= tol
         assert np.all(got[R:] == 7.0)
+
+
+@pytest.mark.parametrize("xdt,d,E", [("bf16", 224, 8), ("bf16", 224, 32), ("f32", 256, 32)])
+def test_router_gemm_plain_tilings(moe, xdt, d, E):
+    """The router GEMM without matrix cores (bf16 x with d not a multiple of
+    64, or fp32 x), for at most 16 columns and for more: fp32 logits against
+    the fp64 product, and the top-2 experts of every token whose 2nd and 3rd
+    logits are apart by more than the logits' error bar."""
+    rng = np.random.default_rng(d + E)
+    N, k = 777, 2
+    x = torch.from_numpy(rng.standard_normal((N, d)).astype(np.float32))
+    if xdt == "bf16":
+        x = x.to(torch.bfloat16)
+    wg = torch.from_numpy((0.05 * rng.standard_normal((E, d))).astype(np.float32))
+    cand = torch.empty((N, k), dtype=torch.int32, device="cuda")
+    score = torch.empty((N, k), dtype=torch.float32, device="cuda")
+    gates = torch.empty((N, k), dtype=torch.float32, device="cuda")
+    logits = torch.empty((N, E), dtype=torch.float32, device="cuda")
+    moe.moe_router_topk(x.cuda(), wg.cuda(), top_k=k, cand_ids=cand, cand_scores=score,
+                        gates=gates, logits_out=logits)
+    torch.cuda.synchronize()
+    ref = x.double().numpy() @ wg.double().numpy().T
+    err = rel_err(to_np(logits), ref)
+    print("router GEMM", xdt, "d", d, "E", E, "max|dl|/rms =", err, flush=True)
+    assert err <= 1e-5
+    rms = np.sqrt(np.mean(ref * ref))
+    s = -np.sort(-ref, axis=1)
+    clear = (s[:, k - 1] - s[:, k]) > 1e-4 * rms
+    want = np.sort(np.argsort(-ref, axis=1)[:, :k], axis=1)
+    got = np.sort(to_np(cand), axis=1)
+    assert clear.mean() > 0.9
+    assert np.array_equal(got[clear], want[clear])
