@@ -56,7 +56,11 @@ def _bf16_bits(a):
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
 
 
-def test_combine_backward_matches_definition(moe):
+@pytest.mark.parametrize("ydt", ["f32", "bf16"])
+def test_combine_backward_matches_definition(moe, ydt):
+    """Combine backward: each kept slot's row gradient g * dy (one fp32
+    rounding, then bf16) bit for bit, and the gate gradients dy . y_row
+    against fp64, for fp32 or bf16 expert rows."""
     rng = np.random.default_rng(21)
     N, d, k = 70, 264, 3
     R = N * k
@@ -68,7 +72,11 @@ def test_combine_backward_matches_definition(moe):
     yr = rng.standard_normal((R, d)).astype(np.float32)
     d_rows = torch.full((R, d), 7, dtype=torch.bfloat16, device="cuda")
     dg = torch.full((N, k), 9.0, device="cuda")
-    moe.moe_combine_backward(torch.from_numpy(dy).cuda(), torch.from_numpy(yr).cuda(),
+    yr_t = torch.from_numpy(yr)
+    if ydt == "bf16":
+        yr_t = yr_t.to(torch.bfloat16)
+    yr = yr_t.double().numpy()  # the rows as the kernel reads them
+    moe.moe_combine_backward(torch.from_numpy(dy).cuda(), yr_t.cuda(),
                              torch.from_numpy(row_of).cuda(), torch.from_numpy(gates).cuda(),
                              d_rows, dg)
     torch.cuda.synchronize()
